@@ -1,0 +1,136 @@
+"""Pins for oracle.attention and oracle.pipeline (dequantization + fp64 decode)."""
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+import synth
+from oracle import attention, codebook, layout, pipeline
+
+
+def _softmax_attention(q, K, V):
+    """Independent reference: scipy's softmax over q.K^T/sqrt(d)."""
+    return softmax(q @ K.T / np.sqrt(q.shape[-1]), axis=-1) @ V
+
+
+def test_attend_matches_scipy_softmax():
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((4, 128)) * 3
+    K = rng.standard_normal((300, 128)); V = rng.standard_normal((300, 128))
+    np.testing.assert_allclose(attention.attend(q, K, V), _softmax_attention(q, K, V), rtol=1e-12, atol=1e-13)
+
+
+def test_invariants():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((2, 128)) * 2
+    K = rng.standard_normal((50, 128)); V = rng.standard_normal((50, 128))
+    o = attention.attend(q, K, V)
+    perm = rng.permutation(50)
+    np.testing.assert_allclose(attention.attend(q, K[perm], V[perm]), o, rtol=1e-12)  # A.V = A_P.V_P
+    np.testing.assert_allclose(attention.attend(q, K[:1], V[:1]), np.repeat(V[:1], 2, 0), rtol=1e-15)
+    np.testing.assert_allclose(attention.attend(np.zeros((1, 128)), K, V)[0], V.mean(0), rtol=1e-12)
+    assert np.all(o <= V.max(0) + 1e-12) and np.all(o >= V.min(0) - 1e-12)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 50])
+def test_split_merge_equals_single_pass(splits):
+    rng = np.random.default_rng(splits)
+    q = rng.standard_normal((3, 128)) * 4
+    K = rng.standard_normal((50, 128)); V = rng.standard_normal((50, 128))
+    parts = [attention.partial(q, K[s], V[s]) for s in np.array_split(np.arange(50), splits)]
+    np.testing.assert_allclose(attention.merge(parts), attention.attend(q, K, V), rtol=1e-12)
+
+
+def test_dequant_closed_forms():
+    b = 3
+    c = codebook.codebook(b)[0].astype(np.float64)
+    codes = np.tile(np.arange(8), 16)[None].repeat(2, 0)
+    S = np.float16([1.5, 0.25])
+    v = attention.dequant_codebook(codes, S, b)
+    np.testing.assert_array_equal(v[0], 1.5 * c[codes[0]])
+    bits = np.zeros(64, int); bits[3] = 3
+    sigma = np.ones(64, np.float32) * np.float32(0.3)
+    k = attention.dequant_k_gtq(codes, S, sigma, bits)
+    assert np.count_nonzero(k[0]) == 2
+    assert k[1, 6] == 0.25 * float(np.float32(0.3)) * c[codes[1, 6]]
+    xa = attention.dequant_affine(np.array([[0, 3, 15] + [0] * 125]), np.float16([[0.5]]), np.float16([[-1.0]]), 128)
+    np.testing.assert_array_equal(xa[0, :3], [-1.0, 0.5, 6.5])
+
+
+def _layer(w, n, meta, n_recent=0):
+    K = np.stack([synth.keys(w, 0, h, 0, n) for h in range(w.Hkv)])[None]
+    V = np.stack([synth.values(w, 0, h, 0, n) for h in range(w.Hkv)])[None]
+    q = np.concatenate([synth.queries(w, 0, h, 0, n) for h in range(w.Hkv)])[None]
+    c = pipeline.build_layer(K, V, k_mode="gtq", v_mode="codebook", v_bits=w.v_bits, n_cap=n,
+                             meta=meta, n_recent=n_recent)
+    return K, V, q, c
+
+
+def test_passthrough_width16_equals_unquantized_keys():
+    """All blocks at the oracle-only width 16 (fp16 passthrough): the full pipeline (quantize ->
+    pack -> unpack -> dequant -> attention) equals attention over fp16 keys and dequantized V."""
+    w = synth.reduced(synth.WORKLOADS[1], N=200)
+    meta = pipeline.LayerMeta(np.full((1, 64), 16), np.ones((1, 64), np.float32),
+                              np.ones((1, 64), np.float32), np.ones((1, 64)))
+    K, V, q, c = _layer(w, 200, meta)
+    o = pipeline.decode_layer(c, q)
+    vc, S = __import__("oracle").quantize.quantize_v(V[0, 0], w.v_bits)
+    Vh = attention.dequant_codebook(vc, S, w.v_bits)
+    ref = _softmax_attention(q[0].astype(np.float64), K[0, 0].astype(np.float16).astype(np.float64), Vh)
+    np.testing.assert_allclose(o[0], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_recent_buffer_concatenation_position_free():
+    w = synth.reduced(synth.WORKLOADS[5], N=300, L=1)
+    kc = [synth.calibration(w, 0, h) for h in range(w.Hkv)]
+    meta = pipeline.calibrate([a for a, _ in kc], [b for _, b in kc], w.k_budget_units)
+    K, V, q, c = _layer(w, 300, meta, n_recent=64)
+    assert c.n_packed == 236 and c.n_recent_valid == 64
+    # ring slots: position p lives at slot p % 64
+    np.testing.assert_array_equal(c.recent_k[0, 1, 299 % 64], K[0, 1, 299].astype(np.float16))
+    o = pipeline.decode_layer(c, q)
+    for h in range(w.Hkv):
+        Kh, Vh = pipeline.dequant_head(c, 0, h)
+        # recent tokens first instead of last: same result (A.V = A_P.V_P)
+        Kr = np.concatenate([Kh[236:], Kh[:236]]); Vr = np.concatenate([Vh[236:], Vh[:236]])
+        qh = q[0, h * w.g:(h + 1) * w.g].astype(np.float64)
+        np.testing.assert_allclose(_softmax_attention(qh, Kr, Vr), o[0, h * w.g:(h + 1) * w.g], rtol=1e-10, atol=1e-12)
+        # the recent part is the fp16 rows of positions 236..299, position p in ring slot p % 64
+        for p in range(236, 300):
+            np.testing.assert_array_equal(Kh[236 + p % 64], K[0, h, p].astype(np.float16).astype(np.float64))
+            np.testing.assert_array_equal(Vh[236 + p % 64], V[0, h, p].astype(np.float16).astype(np.float64))
+
+
+def test_block_gtq_beats_uniform_logit_mae():
+    """Direction of the abstract's per-layer comparison: at equal K budget, per-block widths give a
+    lower RoPE-logit MAE than uniform widths on heterogeneous synthetic heads (soft check)."""
+    from oracle import quantize
+    for wid in (1, 2):
+        w = synth.reduced(synth.WORKLOADS[wid], N=2048)
+        for h in range(w.Hkv):
+            kc, qc = synth.calibration(w, 0, h)
+            meta = pipeline.calibrate([kc], [qc], w.k_budget_units)
+            K = synth.keys(w, 0, h, 0, 2048)
+            q = synth.queries(w, 0, h, 0, 2048).astype(np.float64)
+            exact = q @ K.astype(np.float64).T
+            maes = []
+            for bits in (meta.bits[0], np.full(64, w.k_budget_units // 64)):
+                codes, S = quantize.quantize_k_gtq(K, meta.sigma[0], meta.r[0], bits)
+                Kh = attention.dequant_k_gtq(codes, S, meta.sigma[0], bits)
+                maes.append(np.abs(q @ Kh.T - exact).mean())
+            assert maes[0] < maes[1], (wid, h, maes)
+
+
+def test_affine_pipeline_matches_direct():
+    from oracle import quantize
+    w = synth.reduced(synth.WORKLOADS[4], N=130, Hkv=2, Hq=8)
+    K = np.stack([synth.keys(w, 0, h, 0, 130) for h in range(2)])[None]
+    V = np.stack([synth.values(w, 0, h, 0, 130) for h in range(2)])[None]
+    q = np.concatenate([synth.queries(w, 0, h, 0, 130) for h in range(2)])[None]
+    c = pipeline.build_layer(K, V, k_mode="affine", v_mode="affine", v_bits=2, n_cap=192, k_bits=4, k_group=32)
+    o = pipeline.decode_layer(c, q)
+    for h in range(2):
+        kc, ks, kz = quantize.quantize_affine(K[0, h], 4, 32)
+        vc, vs, vz = quantize.quantize_affine(V[0, h], 2, 128)
+        ref = _softmax_attention(q[0, 4 * h:4 * h + 4].astype(np.float64),
+                                 attention.dequant_affine(kc, ks, kz, 32), attention.dequant_affine(vc, vs, vz, 128))
+        np.testing.assert_allclose(o[0, 4 * h:4 * h + 4], ref, rtol=1e-12, atol=1e-12)
