@@ -1,0 +1,209 @@
+/*
+ * bgtq.h — C ABI of the packed-cache decode library for MI355X (gfx950).
+ *
+ * Decode attention served directly from a low-bit packed KV cache.  Keys carry per-RoPE-block
+ * integer bit widths chosen by Block-GTQ's greedy allocator; values carry one uniform width.
+ * Sources: "RoPE-Aware Bit Allocation for KV-Cache Quantization" (abstract; review §1 Key
+ * Terms, §3 Method & Key Results, Figures 1-2), "Quantize What Counts" technical summary
+ * (Results: group-size sensitivity, K4V2), "LogQuant" technical summary (Method 2 recent
+ * window, Method 4 position-agnostic concatenation).
+ *
+ * Conventions shared by every call:
+ *  - Every function returns an int status: BGTQ_OK (0) or a negative BGTQ_E_* code;
+ *    bgtq_last_error() returns a thread-local message for the last failure.
+ *  - Pointers named "device" are device memory the caller allocated (e.g. torch tensors) and
+ *    still owns; "host" pointers are ordinary host memory.  The library never allocates,
+ *    frees or synchronizes device memory, except where a call says it is synchronous.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device work is
+ *    enqueued on it and returns immediately.
+ *  - Arguments are validated on the host before anything is enqueued; a failed check
+ *    returns BGTQ_E_INVALID / BGTQ_E_UNSUPPORTED / BGTQ_E_BUDGET / BGTQ_E_CAPACITY and has no
+ *    side effect.  A failed launch returns BGTQ_E_HIP.  No C++ exception crosses the ABI.
+ *  - Head dimension d is 128 (64 RoPE blocks of 2 coordinates, interleaved pairs (2i, 2i+1)).
+ *  - Cached values must be finite with |x| <= 65504 and give finite fp16 scales; other
+ *    inputs give undefined codes (they cannot be checked without reading device memory).
+ */
+#ifndef BGTQ_H
+#define BGTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    BGTQ_OK = 0,
+    BGTQ_E_INVALID = -1,      /* bad pointer, shape, layer, size or workspace */
+    BGTQ_E_UNSUPPORTED = -2,  /* valid request outside what the kernels implement */
+    BGTQ_E_BUDGET = -3,       /* bit budget infeasible for the allocator */
+    BGTQ_E_CAPACITY = -4,     /* append would exceed the cache capacity */
+    BGTQ_E_HIP = -5           /* a HIP runtime call or kernel launch failed */
+};
+
+enum { BGTQ_F32 = 0, BGTQ_F16 = 1, BGTQ_BF16 = 2 };          /* activation dtypes */
+enum { BGTQ_SCORE_QK = 0, BGTQ_SCORE_K = 1 };               /* energy score modes */
+enum { BGTQ_K_BLOCKGTQ = 0, BGTQ_K_AFFINE = 1 };            /* key formats */
+enum { BGTQ_V_CODEBOOK = 0, BGTQ_V_AFFINE = 1 };            /* value formats */
+
+/* Buffer selectors for bgtq_cache_bytes. */
+enum {
+    BGTQ_BUF_K_CODES = 0, BGTQ_BUF_V_CODES = 1, BGTQ_BUF_K_SCALE = 2, BGTQ_BUF_K_ZERO = 3,
+    BGTQ_BUF_V_SCALE = 4, BGTQ_BUF_V_ZERO = 5, BGTQ_BUF_RECENT_K = 6, BGTQ_BUF_RECENT_V = 7,
+    BGTQ_BUF_META = 8         /* bits + sigma + inv_sigma, for reference */
+};
+
+#define BGTQ_HEAD_DIM 128
+#define BGTQ_N_BLOCKS 64
+#define BGTQ_TILE 64
+#define BGTQ_MAX_BATCH 64
+
+/*
+ * Packed KV cache descriptor (plain data; the caller fills it and owns every buffer).
+ *
+ * Geometry: L layers, B sequences, Hq query heads, Hkv KV heads (Hq % Hkv == 0, g = Hq/Hkv in
+ * {1, 2, 4, 8}), d = 128, n_cap = packed-token capacity per (layer, sequence), a multiple of 64.
+ *
+ * Key format (k_mode):
+ *   BGTQ_K_BLOCKGTQ — per-block widths bits[l][h][i] in 0..8 with sum == budget_units (a
+ *     multiple of 16); each token stores 2*budget_units bits plus one fp16 scale.
+ *   BGTQ_K_AFFINE — every coordinate k_bits (2, 4 or 8) bits; fp16 scale and zero per group
+ *     of k_group (8..128, divides 128) coordinates of one token.
+ * Value format (v_mode): v_bits in 1..4 per coordinate;
+ *   BGTQ_V_CODEBOOK — one fp16 scale per token (uniform TQ-MSE width);
+ *   BGTQ_V_AFFINE — fp16 scale and zero per token (group = 128).
+ * n_recent > 0 keeps the newest n_recent tokens of each (layer, sequence, kv head) in an fp16
+ *   ring (slot = position % n_recent) outside the packed cache; 0 disables it.
+ *
+ * Device buffers (per layer blocks, layer-major; sizes from bgtq_cache_bytes):
+ *   k_codes  uint8 [L][B][Hkv][n_cap/64][64 * K record bytes]   (tile layout, see below)
+ *   v_codes  uint8 [L][B][Hkv][n_cap/64][1024 * v_bits]
+ *   k_scale  fp16  [L][B][Hkv][n_cap]            (affine: [..][n_cap][128/k_group])
+ *   k_zero   fp16  affine keys only, same shape as k_scale; else NULL
+ *   v_scale  fp16  [L][B][Hkv][n_cap];  v_zero: affine values only, same shape; else NULL
+ *   recent_k, recent_v  fp16 [L][B][Hkv][n_recent][128] when n_recent > 0; else NULL
+ *   bits      uint8 [L][Hkv][64]   widths (BLOCKGTQ), from bgtq_allocate
+ *   sigma     fp32  [L][Hkv][64]   per-block key scale sigma_i = sqrt(E_k[i]/2)
+ *   inv_sigma fp32  [L][Hkv][64]   fp32(1/sigma_i), 0 for a dead block
+ * Host state:
+ *   n_tokens  int64 [L][B] host array: tokens appended so far per (layer, sequence) (packed +
+ *     recent).  bgtq_quantize_append advances it on success only.
+ *
+ * Tile layout (64 consecutive tokens of one (batch, kv head)):
+ *   K record = little-endian bit stream of R = 2U/32 dwords (affine: 4*k_bits dwords).  Block-GTQ
+ *   record: blocks by width descending (ties: lower index first), width-0 blocks omitted; block i
+ *   of width w holds code(2i) then code(2i+1), w bits each.  Affine: coordinate j at bits
+ *   [k_bits*j, +k_bits).  Tile = dword-major, token-minor: dword k of token t at byte (k*64+t)*4.
+ *   V tile = 16 token quads x 16 groups of 8 dims x v_bits dwords (quad-major).  The v_bits dwords
+ *   of (quad q, group G) hold 16 fields of 2*v_bits bits, field f at bit 2*v_bits*f: token pair
+ *   2q + f/8, dim 8G + f%8; low half = even token's code, high half = odd token's code.
+ */
+typedef struct bgtq_cache {
+    int32_t L, B, Hq, Hkv, d;
+    int64_t n_cap;
+    int32_t k_mode, budget_units, k_bits, k_group;
+    int32_t v_mode, v_bits;
+    int32_t n_recent;
+    void *k_codes, *v_codes, *k_scale, *k_zero, *v_scale, *v_zero, *recent_k, *recent_v;
+    const uint8_t *bits;
+    const float *sigma, *inv_sigma;
+    int64_t *n_tokens;
+} bgtq_cache;
+
+/* Thread-local text describing the last non-OK status of this thread ("" if none). */
+const char *bgtq_last_error(void);
+
+/* Library version string. */
+const char *bgtq_version(void);
+
+/*
+ * The library's frozen TQ-MSE scalar table for `bits` in 1..8 (host, synchronous).
+ * TQ-MSE (review §1; abstract) quantizes coordinates with an MSE-optimal scalar quantizer
+ * whose error falls as 4^-b.  Table: Lloyd-Max quantizer of N(0,1), centroids rounded to fp16,
+ * thresholds = exact midpoints of adjacent centroids.  centroids_f16 (host, 2^bits uint16 fp16
+ * bit patterns, ascending) and thresholds (host, 2^bits - 1 floats) may be NULL.
+ */
+int bgtq_codebook(int bits, uint16_t *centroids_f16, float *thresholds);
+
+/*
+ * Greedy integer bit allocation (host, synchronous).  Block-GTQ (abstract; review §3,
+ * Figure 1): per layer and KV head, widths by marginal gain under the 4^-b rate.  Starting from
+ * b_min on every block with a positive score (0 elsewhere), repeatedly add one bit to the block
+ * maximizing s_i * 4^-b_i among blocks with b_i < b_max and s_i > 0; ties go to the lowest
+ * index.  scores: host fp64 [n_heads][n_blk]; bits_out: host uint8 [n_heads][n_blk].
+ * Errors: BGTQ_E_INVALID (NULL, n_blk not in 1..256, b_max not in 1..8, b_min > b_max,
+ * negative or non-finite score), BGTQ_E_BUDGET (budget_units cannot be spent on any head).
+ */
+int bgtq_allocate(const double *scores, int n_heads, int n_blk, int budget_units,
+                  int b_min, int b_max, uint8_t *bits_out);
+
+/*
+ * Calibration energy (device reduction, then a synchronous copy to the host).  Block-GTQ
+ * (abstract; review §3) scores each RoPE block from calibration data per layer and KV head:
+ * E_k[i] = mean_t ||k_t,(2i,2i+1)||^2, E_q[i] = mean over t and the g query heads of the group of
+ * ||q||^2, score = E_q*E_k (BGTQ_SCORE_QK) or E_k (BGTQ_SCORE_K); sigma_i = fp32(sqrt(E_k[i]/2)),
+ * inv_sigma_i = fp32(1/sigma_i) (0 if sigma_i = 0).  Sums run in fp64 on the device.
+ * k_cal: device [T_cal][Hkv][128], q_cal: device [T_cal][Hkv*g][128], contiguous, dtype.
+ * Outputs (host, [Hkv][64]; any may be NULL): scores fp64, sigma fp32, inv_sigma fp32.
+ * Synchronizes `stream`.  Errors: BGTQ_E_INVALID (NULL inputs, T_cal < 1, d != 128, bad dtype).
+ */
+int bgtq_block_energy(const void *k_cal, const void *q_cal, int dtype, int64_t T_cal,
+                      int Hkv, int g, int d, int score_mode, double *scores, float *sigma,
+                      float *inv_sigma, void *stream);
+
+/* Bytes of one cache buffer (all L layers) for the descriptor's geometry; <0 on error. */
+int64_t bgtq_cache_bytes(const bgtq_cache *c, int which);
+
+/*
+ * Quantize-append (device, asynchronous).  The packed-cache path (review §1 Packed-Cache;
+ * abstract) writes each new K/V row as codes plus a per-token fp16 scale.  Per token:
+ * S = fp16_rne(sqrt_f32(sum_j (x_j * inv_sigma_i)^2 / 128)) with the sum in fp32, sequential
+ * over j, no FMA; code_j = number of thresholds tau_m with x_j >= fp32(fp32(S*sigma_i)*tau_m)
+ * (values: sigma = 1).  Affine groups: scale = fp16(fp32(max-min)/(2^b-1)), zero = fp16(min),
+ * code = clamp(rint((x-zero)/scale)).  With n_recent > 0, tokens that leave the fp16 window are
+ * quantized and new tokens enter the ring.
+ * k, v: device rows in `dtype`, element (b, t, h, j) at b*strides[0] + t*strides[1] +
+ * h*strides[2] + j (strides in elements; NULL = contiguous [B][n_new][Hkv][128]).
+ * Appends n_new tokens to every sequence of `layer`.  Errors: BGTQ_E_INVALID,
+ * BGTQ_E_UNSUPPORTED (format outside the kernels), BGTQ_E_CAPACITY (packed tokens > n_cap).
+ */
+int bgtq_quantize_append(bgtq_cache *c, int layer, const void *k, const void *v, int dtype,
+                         int64_t n_new, const int64_t *strides, void *stream);
+
+/* Workspace bytes bgtq_decode_attention needs for n_splits (0 = the library's choice). */
+int64_t bgtq_decode_workspace_bytes(const bgtq_cache *c, int n_splits);
+
+/*
+ * Decode attention from the packed cache (device, asynchronous).  Packed-cache serving
+ * (review §1 Packed-Cache, Figure 2; abstract): in one pass over the codes, without an fp16
+ * copy of K/V, compute z_t = q.k_hat_t/sqrt(128) with k_hat = S*sigma_i*c[code] (affine:
+ * scale*code+zero), an online softmax, and o = sum_t p_t v_hat_t / sum_t p_t over the packed
+ * tokens and the fp16 recent tokens (order-free concatenation, LogQuant summary Method 4).
+ * Split-K over context; partials merged by log-sum-exp.
+ * q: device [B][Hq][128] in dtype; out: device fp32 [B][Hq][128]; ws: device scratch of at
+ * least bgtq_decode_workspace_bytes(c, n_splits) bytes (256-byte aligned), contents undefined
+ * after the call.  Errors: BGTQ_E_INVALID (NULL, layer, empty context, small workspace),
+ * BGTQ_E_UNSUPPORTED.
+ */
+int bgtq_decode_attention(const bgtq_cache *c, int layer, const void *q, int dtype, float *out,
+                          void *ws, size_t ws_bytes, int n_splits, void *stream);
+
+/* Workspace bytes for bgtq_fp16_decode_attention. */
+int64_t bgtq_fp16_decode_workspace_bytes(int64_t N, int B, int Hq, int Hkv, int n_splits);
+
+/*
+ * Unquantized comparator (device, asynchronous): the same split-K decode attention over an fp16
+ * cache, the role fp16 FlashAttention-2 plays in the abstract's serving comparison.
+ * k16, v16: device fp16 [B][Hkv][N][128]; q: device [B][Hq][128] in dtype; out: fp32
+ * [B][Hq][128]; ws as above.  Errors: BGTQ_E_INVALID, BGTQ_E_UNSUPPORTED.
+ */
+int bgtq_fp16_decode_attention(const void *k16, const void *v16, int64_t N, int B, int Hq,
+                               int Hkv, int d, const void *q, int dtype, float *out, void *ws,
+                               size_t ws_bytes, int n_splits, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BGTQ_H */

@@ -11,14 +11,14 @@ p%32 of dword p/32).  Blocks appear in "block order": width descending, ties by 
 block index, width-0 blocks omitted; block i of width w puts code(2i) at the next w bits and
 code(2i+1) at the w bits after it.
 K record (affine, b bits): coordinate j at bits [b*j, b*j + b).
-Tile of K records: split each record into chunks of 4 dwords (the last may be shorter); chunk
-c of all 64 tokens occupies one region starting at byte c*1024, token t's chunk at
-t * (chunk dwords) * 4 inside the region.
+Tile of K records (R dwords per token): dword-major, token-minor — dword k of token t at byte
+(k*64 + t)*4, so the k-th dword of all 64 tokens is one contiguous 256-byte row.
 
-V tile (b bits, codebook or affine): 32 token pairs (2p, 2p+1) x 8 dim groups of 16 dims x
-b dwords, in that order (pair-major).  Within the b dwords of (pair p, group G), dim 16G+j
-has a 2b-bit field at bit 2b*j: low b bits = code of token 2p, high b bits = code of 2p+1.
-A token that does not exist contributes zero bits.
+V tile (b bits, codebook or affine): 16 token quads (4q .. 4q+3) x 16 dim groups of 8 dims x
+b dwords, in that order (quad-major).  The b dwords of (quad q, group G) hold 16 fields of 2b
+bits, field f at bit 2b*f: token pair 2q + f//8 (tokens 4q + 2(f//8) and the next one), dim
+8G + f%8; low b bits = code of the even token, high b bits = code of the odd token.  A token
+that does not exist contributes zero bits.
 
 Scales: fp16 arrays indexed [token] (codebook K/V) or [token][group] (affine), one per
 (batch, kv head), outside the tiles.
@@ -101,62 +101,47 @@ def k_affine_codes(words: np.ndarray, b: int, d: int = 128) -> np.ndarray:
     return np.stack([_get(words, b * j, b) for j in range(d)], axis=1)
 
 
-def _chunks(R: int):
-    return [(c * 1024, min(4, R - 4 * c)) for c in range((R + 3) // 4)]
-
-
 def tile_records(words: np.ndarray, n_tiles: int) -> np.ndarray:
-    """records [n, R] -> tiles uint8 [n_tiles, 64*R*4] in the chunked token-minor layout."""
+    """records [n, R] -> tiles uint8 [n_tiles, 64*R*4], dword-major token-minor."""
     n, R = words.shape
     padded = np.zeros((n_tiles * TILE, R), np.uint32)
     padded[:n] = words
-    padded = padded.reshape(n_tiles, TILE, R)
-    out = np.zeros((n_tiles, TILE * R), np.uint32)
-    for c, (off, cs) in enumerate(_chunks(R)):
-        base = off // 4
-        out[:, base:base + TILE * cs] = padded[:, :, 4 * c:4 * c + cs].reshape(n_tiles, TILE * cs)
+    out = padded.reshape(n_tiles, TILE, R).transpose(0, 2, 1).copy()  # [tile, k, t]
     return out.view(np.uint8).reshape(n_tiles, TILE * R * 4)
 
 
 def untile_records(tiles: np.ndarray, n: int, R: int) -> np.ndarray:
     n_tiles = tiles.shape[0]
-    t32 = np.ascontiguousarray(tiles).view(np.uint32).reshape(n_tiles, TILE * R)
-    words = np.zeros((n_tiles, TILE, R), np.uint32)
-    for c, (off, cs) in enumerate(_chunks(R)):
-        base = off // 4
-        words[:, :, 4 * c:4 * c + cs] = t32[:, base:base + TILE * cs].reshape(n_tiles, TILE, cs)
-    return words.reshape(n_tiles * TILE, R)[:n]
+    t32 = np.ascontiguousarray(tiles).view(np.uint32).reshape(n_tiles, R, TILE)
+    return t32.transpose(0, 2, 1).reshape(n_tiles * TILE, R)[:n]
 
 
 def v_tiles(codes: np.ndarray, b: int, n_tiles: int) -> np.ndarray:
-    """codes [n, 128] -> tiles uint8 [n_tiles, 1024*b] in the pair-major layout."""
+    """codes [n, 128] -> tiles uint8 [n_tiles, 1024*b] in the quad-major layout."""
     n, d = codes.shape
     assert d == 128
-    npairs = n_tiles * TILE // 2
-    even = np.zeros((npairs, d), np.int64)
-    odd = np.zeros((npairs, d), np.int64)
-    even[: (n + 1) // 2] = codes[0::2]
-    odd[: n // 2] = codes[1::2]
-    words = np.zeros((npairs * 8, b), np.uint32)  # rows = (pair, group)
-    for G in range(8):
-        rows = slice(G, None, 8)
-        sub = np.zeros((npairs, b), np.uint32)
-        for j in range(16):
-            dim = 16 * G + j
-            field = even[:, dim] | (odd[:, dim] << b)
-            _put(sub, 2 * b * j, 2 * b, field)
-        words[rows] = sub
-    return words.reshape(n_tiles, TILE // 2 * 8 * b).view(np.uint8).reshape(n_tiles, 1024 * b)
+    full = np.zeros((n_tiles * TILE, d), np.int64)
+    full[:n] = codes
+    quads = full.reshape(n_tiles * TILE // 4, 4, d)          # [quad, token in quad, dim]
+    rows = np.zeros((quads.shape[0], 16, b), np.uint32)       # [quad, group, dword]
+    for G in range(16):
+        sub = np.zeros((quads.shape[0], b), np.uint32)
+        for f in range(16):
+            pr, dim = f // 8, 8 * G + f % 8
+            field = quads[:, 2 * pr, dim] | (quads[:, 2 * pr + 1, dim] << b)
+            _put(sub, 2 * b * f, 2 * b, field)
+        rows[:, G] = sub
+    return rows.reshape(n_tiles, 1024 * b // 4).view(np.uint8).reshape(n_tiles, 1024 * b)
 
 
 def v_codes(tiles: np.ndarray, b: int, n: int) -> np.ndarray:
-    t32 = np.ascontiguousarray(tiles).view(np.uint32).reshape(-1, b)  # rows = (tile, pair, group)
-    npairs = tiles.shape[0] * TILE // 2
-    codes = np.zeros((2 * npairs, 128), np.int64)
-    for G in range(8):
-        sub = t32[G::8]
-        for j in range(16):
-            field = _get(sub, 2 * b * j, 2 * b)
-            codes[0::2, 16 * G + j] = field & ((1 << b) - 1)
-            codes[1::2, 16 * G + j] = field >> b
-    return codes[:n]
+    n_tiles = tiles.shape[0]
+    rows = np.ascontiguousarray(tiles).view(np.uint32).reshape(n_tiles * TILE // 4, 16, b)
+    quads = np.zeros((rows.shape[0], 4, 128), np.int64)
+    for G in range(16):
+        for f in range(16):
+            pr, dim = f // 8, 8 * G + f % 8
+            field = _get(rows[:, G], 2 * b * f, 2 * b)
+            quads[:, 2 * pr, dim] = field & ((1 << b) - 1)
+            quads[:, 2 * pr + 1, dim] = field >> b
+    return quads.reshape(-1, 128)[:n]

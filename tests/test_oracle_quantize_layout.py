@@ -161,32 +161,44 @@ def test_straddling_field_round_trip():
         np.testing.assert_array_equal(back, codes)
 
 
-def test_tile_chunk_positions():
-    """Token t's dword k lives at byte (k//4)*1024 + t*16 + (k%4)*4 for R = 12."""
-    words = np.arange(64 * 12, dtype=np.uint32).reshape(64, 12)
-    tiles = layout.tile_records(words, 1).view(np.uint32)[0]
-    for t in (0, 1, 37, 63):
-        for k in range(12):
-            assert tiles[((k // 4) * 1024 + t * 16 + (k % 4) * 4) // 4] == words[t, k]
-    # R = 6: chunks of 4 and 2 dwords
-    words = np.arange(64 * 6, dtype=np.uint32).reshape(64, 6)
-    tiles = layout.tile_records(words, 1).view(np.uint32)[0]
-    assert tiles[(1024 + 5 * 8 + 4) // 4] == words[5, 5]
+def test_tile_record_positions():
+    """Token t's dword k lives at byte (k*64 + t)*4 of its tile (dword-major, token-minor)."""
+    for R in (12, 6, 8):
+        words = np.arange(64 * R, dtype=np.uint32).reshape(64, R) * 7 + 1
+        tiles = layout.tile_records(words, 1).view(np.uint32)[0]
+        for t in (0, 1, 37, 63):
+            for k in range(R):
+                assert tiles[k * 64 + t] == words[t, k]
+    words = np.arange(100 * 8, dtype=np.uint32).reshape(100, 8)
+    tiles = layout.tile_records(words, 2)
+    np.testing.assert_array_equal(layout.untile_records(tiles, 100, 8), words)
+    assert tiles.view(np.uint32)[1, 3 * 64 + (70 - 64)] == words[70, 3]
 
 
-def test_v_pair_layout_hand_worked():
+def test_v_quad_layout_hand_worked():
     b = 3
-    codes = np.zeros((3, 128), int)
-    codes[0, 17] = 5   # token 0 (even), dim 17 = group 1, j = 1
+    codes = np.zeros((7, 128), int)
+    codes[0, 17] = 5   # token 0 (quad 0, pair 0, even), dim 17 = group 2, field f = 1
     codes[1, 17] = 2   # token 1 (odd)
-    codes[2, 0] = 7    # token 2: pair 1, group 0, j = 0, low half
+    codes[2, 3] = 6    # token 2 (quad 0, pair 1, even), dim 3 = group 0, field f = 8 + 3 = 11
+    codes[6, 0] = 7    # token 6 (quad 1, pair 1, even), dim 0: field f = 8
     tiles = layout.v_tiles(codes, b, 1).view(np.uint32)[0]
-    # pair 0, group 1 -> dwords [(0*8+1)*3, +3); field j=1 at bit 6: 5 | 2<<3
-    assert tiles[3] == (5 | (2 << 3)) << 6
-    # pair 1, group 0 -> dword (1*8+0)*3 = 24
-    assert tiles[24] == 7
-    assert np.count_nonzero(tiles) == 2
-    np.testing.assert_array_equal(layout.v_codes(layout.v_tiles(codes, b, 1), b, 3), codes)
+    # (quad 0, group 2) -> dwords [(0*16+2)*3, +3); field 1 at bit 6: 5 | 2<<3
+    assert tiles[6] == (5 | (2 << 3)) << 6
+    # (quad 0, group 0): field 11 at bit 66 -> dword 2 of the row, bit 2
+    assert tiles[2] == 6 << 2
+    # (quad 1, group 0) -> dword 16*3 = 48; field 8 at bit 48 -> dword 1, bit 16
+    assert tiles[49] == 7 << 16
+    assert np.count_nonzero(tiles) == 3
+    np.testing.assert_array_equal(layout.v_codes(layout.v_tiles(codes, b, 1), b, 7), codes)
+
+
+def test_v_straddling_field():
+    """b = 3: field 5 occupies bits 30..35 and straddles dwords 0 and 1 of the row."""
+    codes = np.zeros((2, 128), int)
+    codes[0, 5], codes[1, 5] = 7, 5   # field = 7 | 5 << 3 = 47 = 0b101111
+    tiles = layout.v_tiles(codes, 3, 1).view(np.uint32)[0]
+    assert tiles[0] == (47 & 0b11) << 30 and tiles[1] == 47 >> 2
 
 
 @pytest.mark.parametrize("b", [1, 2, 3, 4])
