@@ -146,11 +146,12 @@ int bgtq_allocate(const double *scores, int n_heads, int n_blk, int budget_units
  * inv_sigma_i = fp32(1/sigma_i) (0 if sigma_i = 0).  Sums run in fp64 on the device.
  * k_cal: device [T_cal][Hkv][128], q_cal: device [T_cal][Hkv*g][128], contiguous, dtype.
  * Outputs (host, [Hkv][64]; any may be NULL): scores fp64, sigma fp32, inv_sigma fp32.
- * Synchronizes `stream`.  Errors: BGTQ_E_INVALID (NULL inputs, T_cal < 1, d != 128, bad dtype).
+ * ws: device scratch of at least Hkv*64*16 bytes (caller-owned).  Synchronizes `stream`.
+ * Errors: BGTQ_E_INVALID (NULL inputs, T_cal < 1, bad dtype, small ws), BGTQ_E_UNSUPPORTED (d).
  */
 int bgtq_block_energy(const void *k_cal, const void *q_cal, int dtype, int64_t T_cal,
                       int Hkv, int g, int d, int score_mode, double *scores, float *sigma,
-                      float *inv_sigma, void *stream);
+                      float *inv_sigma, void *ws, size_t ws_bytes, void *stream);
 
 /* Bytes of one cache buffer (all L layers) for the descriptor's geometry; <0 on error. */
 int64_t bgtq_cache_bytes(const bgtq_cache *c, int which);

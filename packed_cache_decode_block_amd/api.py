@@ -1,0 +1,180 @@
+"""Thin wrappers over the C ABI: marshal torch tensors / numpy arrays into pointers and sizes."""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from . import _lib
+from ._lib import check, lib
+
+_DT = None
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: _lib.F32, torch.float16: _lib.F16, torch.bfloat16: _lib.BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensor must be on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+
+
+def bgtq_version() -> str:
+    return lib.bgtq_version().decode()
+
+
+def bgtq_codebook(bits: int):
+    """(centroids fp16 [2^bits], thresholds fp32 [2^bits - 1]) of the library's frozen table."""
+    n = 1 << bits if 1 <= bits <= 8 else 1
+    c = np.zeros(n, np.uint16)
+    t = np.zeros(max(n - 1, 1), np.float32)
+    check(lib.bgtq_codebook(bits, c.ctypes.data_as(C.POINTER(C.c_uint16)), t.ctypes.data_as(C.POINTER(C.c_float))))
+    return c.view(np.float16), t[: n - 1]
+
+
+def bgtq_allocate(scores, budget_units: int, b_min: int = 0, b_max: int = 8) -> np.ndarray:
+    """Greedy widths: scores [n_heads, n_blk] fp64 -> uint8 [n_heads, n_blk] (host)."""
+    s = np.ascontiguousarray(scores, dtype=np.float64)
+    if s.ndim == 1:
+        s = s[None]
+    out = np.zeros(s.shape, np.uint8)
+    check(lib.bgtq_allocate(s.ctypes.data_as(C.POINTER(C.c_double)), s.shape[0], s.shape[1], budget_units, b_min,
+                            b_max, out.ctypes.data_as(C.POINTER(C.c_uint8))))
+    return out
+
+
+def bgtq_block_energy(k_cal, q_cal, score_mode: int = _lib.SCORE_QK, stream=None):
+    """k_cal [T, Hkv, 128], q_cal [T, Hq, 128] device tensors -> (scores fp64, sigma fp32, inv_sigma fp32)
+    host arrays [Hkv, 64].  Synchronizes the stream."""
+    torch = _torch()
+    _require_cuda(k_cal, q_cal)
+    T, Hkv, d = k_cal.shape
+    g = q_cal.shape[1] // Hkv
+    ws = torch.empty(Hkv * 64 * 2, dtype=torch.float64, device=k_cal.device)
+    sc = np.zeros((Hkv, 64)); sg = np.zeros((Hkv, 64), np.float32); rs = np.zeros((Hkv, 64), np.float32)
+    check(lib.bgtq_block_energy(_ptr(k_cal), _ptr(q_cal), _dtype_code(k_cal), T, Hkv, g, d, score_mode,
+                                sc.ctypes.data_as(C.POINTER(C.c_double)), sg.ctypes.data_as(C.POINTER(C.c_float)),
+                                rs.ctypes.data_as(C.POINTER(C.c_float)), _ptr(ws), ws.numel() * 8, _stream(stream)))
+    return sc, sg, rs
+
+
+class PackedCache:
+    """Device buffers of a packed KV cache plus the descriptor the library reads.
+
+    All buffers are torch tensors owned by this object (layer-major, see include/bgtq.h).
+    """
+
+    def __init__(self, *, L, B, Hq, Hkv, n_cap, k_mode=_lib.K_BLOCKGTQ, budget_units=128, k_bits=4, k_group=32,
+                 v_mode=_lib.V_CODEBOOK, v_bits=2, n_recent=0, device="cuda", zero=True):
+        torch = _torch()
+        self.desc = _lib.CacheDesc()
+        d = self.desc
+        d.L, d.B, d.Hq, d.Hkv, d.d = L, B, Hq, Hkv, 128
+        d.n_cap = n_cap
+        d.k_mode, d.budget_units, d.k_bits, d.k_group = k_mode, budget_units, k_bits, k_group
+        d.v_mode, d.v_bits, d.n_recent = v_mode, v_bits, n_recent
+        self.n_tokens = np.zeros((L, B), np.int64)
+        d.n_tokens = self.n_tokens.ctypes.data_as(C.POINTER(C.c_int64))
+        alloc = torch.zeros if zero else torch.empty
+
+        def buf(which, dtype):
+            n = check(lib.bgtq_cache_bytes(C.byref(d), which))
+            if n == 0:
+                return None
+            return alloc(n // torch.tensor([], dtype=dtype).element_size(), dtype=dtype, device=device)
+
+        self.k_codes = buf(_lib.BUF_K_CODES, torch.uint8)
+        self.v_codes = buf(_lib.BUF_V_CODES, torch.uint8)
+        self.k_scale = buf(_lib.BUF_K_SCALE, torch.float16)
+        self.k_zero = buf(_lib.BUF_K_ZERO, torch.float16)
+        self.v_scale = buf(_lib.BUF_V_SCALE, torch.float16)
+        self.v_zero = buf(_lib.BUF_V_ZERO, torch.float16)
+        self.recent_k = buf(_lib.BUF_RECENT_K, torch.float16) if n_recent else None
+        self.recent_v = buf(_lib.BUF_RECENT_V, torch.float16) if n_recent else None
+        self.bits = torch.zeros((L, Hkv, 64), dtype=torch.uint8, device=device)
+        self.sigma = torch.zeros((L, Hkv, 64), dtype=torch.float32, device=device)
+        self.inv_sigma = torch.zeros((L, Hkv, 64), dtype=torch.float32, device=device)
+        for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "recent_k", "recent_v",
+                     "bits", "sigma", "inv_sigma"):
+            setattr(d, name, _ptr(getattr(self, name)))
+        self._ws = None
+
+    def set_metadata(self, layer: int, bits, sigma, inv_sigma):
+        """Upload per-(kv head, block) widths and key scales of one layer (host arrays [Hkv, 64])."""
+        torch = _torch()
+        self.bits[layer].copy_(torch.from_numpy(np.ascontiguousarray(bits, np.uint8)))
+        self.sigma[layer].copy_(torch.from_numpy(np.ascontiguousarray(sigma, np.float32)))
+        self.inv_sigma[layer].copy_(torch.from_numpy(np.ascontiguousarray(inv_sigma, np.float32)))
+
+    def quantize_append(self, layer: int, k, v, stream=None):
+        """Append rows k, v [B, n_new, Hkv, 128] (any strides in B/token/head, dim contiguous)."""
+        if not (k.is_cuda and v.is_cuda):
+            raise ValueError("k and v must be on the GPU")
+        if k.shape != v.shape or k.dtype != v.dtype or k.stride() != v.stride():
+            raise ValueError("k and v must have the same shape, dtype and strides")
+        if k.stride(-1) != 1:
+            raise ValueError("head_dim must be contiguous")
+        strides = (C.c_int64 * 3)(k.stride(0), k.stride(1), k.stride(2))
+        check(lib.bgtq_quantize_append(C.byref(self.desc), layer, _ptr(k), _ptr(v), _dtype_code(k), k.shape[1],
+                                       strides, _stream(stream)))
+
+    def workspace_bytes(self, n_splits: int = 0) -> int:
+        return check(lib.bgtq_decode_workspace_bytes(C.byref(self.desc), n_splits))
+
+    def workspace(self, n_splits: int = 0, device="cuda"):
+        torch = _torch()
+        n = self.workspace_bytes(n_splits)
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+        return self._ws
+
+    def decode_attention(self, layer: int, q, out=None, n_splits: int = 0, ws=None, stream=None):
+        """q [B, Hq, 128] -> out fp32 [B, Hq, 128]."""
+        torch = _torch()
+        _require_cuda(q)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if ws is None:
+            ws = self.workspace(n_splits, q.device)
+        check(lib.bgtq_decode_attention(C.byref(self.desc), layer, _ptr(q), _dtype_code(q), _ptr(out), _ptr(ws),
+                                        ws.numel(), n_splits, _stream(stream)))
+        return out
+
+
+def bgtq_fp16_decode_attention(k16, v16, q, out=None, n_splits: int = 0, ws=None, stream=None):
+    """Unquantized comparator: k16, v16 fp16 [B, Hkv, N, 128]; q [B, Hq, 128] -> fp32 [B, Hq, 128]."""
+    torch = _torch()
+    _require_cuda(k16, v16, q)
+    B, Hkv, N, d = k16.shape
+    Hq = q.shape[1]
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if ws is None:
+        n = check(lib.bgtq_fp16_decode_workspace_bytes(N, B, Hq, Hkv, n_splits))
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    check(lib.bgtq_fp16_decode_attention(_ptr(k16), _ptr(v16), N, B, Hq, Hkv, d, _ptr(q), _dtype_code(q), _ptr(out),
+                                         _ptr(ws), ws.numel(), n_splits, _stream(stream)))
+    return out

@@ -1,0 +1,515 @@
+// Host side of the C ABI declared in include/bgtq.h: argument validation, the greedy
+// allocator, cache geometry, workspace carving and kernel launches.  No device allocation,
+// no synchronization except in bgtq_block_energy (which returns host scores).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/bgtq.h"
+#include "bgtq_internal.h"
+#include "generated/bgtq_codebook_data.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return BGTQ_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(BGTQ_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int D = 128;
+constexpr int TILE = 64;
+constexpr int PART = 132;
+
+bool dtype_ok(int dt) { return dt == BGTQ_F32 || dt == BGTQ_F16 || dt == BGTQ_BF16; }
+
+// Validate the descriptor's geometry and format; fill g.  Pointers are checked by callers.
+int geometry(const bgtq_cache* c, bgtq::Geometry& g) {
+    if (!c) return fail(BGTQ_E_INVALID, "cache descriptor is NULL");
+    if (c->d != D) return fail(BGTQ_E_UNSUPPORTED, "head dim %d unsupported (only 128)", c->d);
+    if (c->L < 1 || c->B < 1 || c->Hq < 1 || c->Hkv < 1)
+        return fail(BGTQ_E_INVALID, "L, B, Hq, Hkv must be positive");
+    if (c->B > BGTQ_MAX_BATCH) return fail(BGTQ_E_UNSUPPORTED, "B=%d exceeds %d", c->B, BGTQ_MAX_BATCH);
+    if (c->Hq % c->Hkv) return fail(BGTQ_E_INVALID, "Hq %% Hkv != 0");
+    const int G = c->Hq / c->Hkv;
+    if (!(G == 1 || G == 2 || G == 4 || G == 8)) return fail(BGTQ_E_UNSUPPORTED, "group size %d unsupported", G);
+    if (c->n_cap < TILE || c->n_cap % TILE) return fail(BGTQ_E_INVALID, "n_cap must be a positive multiple of 64");
+    if (c->n_recent < 0) return fail(BGTQ_E_INVALID, "n_recent < 0");
+    g.B = c->B; g.Hq = c->Hq; g.Hkv = c->Hkv; g.G = G;
+    g.n_cap = c->n_cap;
+    g.n_tiles = c->n_cap / TILE;
+    g.k_mode = c->k_mode;
+    g.k_bits = c->k_bits;
+    g.k_group = c->k_group;
+    if (c->k_mode == BGTQ_K_BLOCKGTQ) {
+        if (c->budget_units < 16 || c->budget_units > 8 * 64 || c->budget_units % 16)
+            return fail(BGTQ_E_INVALID, "budget_units must be a multiple of 16 in [16, 512]");
+        g.R = 2 * c->budget_units / 32;
+    } else if (c->k_mode == BGTQ_K_AFFINE) {
+        if (!(c->k_bits == 2 || c->k_bits == 4 || c->k_bits == 8))
+            return fail(BGTQ_E_INVALID, "k_bits must be 2, 4 or 8");
+        if (c->k_group < 8 || c->k_group > D || D % c->k_group)
+            return fail(BGTQ_E_INVALID, "k_group must divide 128 and be >= 8");
+        g.R = c->k_bits * D / 32;
+    } else {
+        return fail(BGTQ_E_INVALID, "unknown k_mode %d", c->k_mode);
+    }
+    if (c->v_mode != BGTQ_V_CODEBOOK && c->v_mode != BGTQ_V_AFFINE) return fail(BGTQ_E_INVALID, "unknown v_mode");
+    if (c->v_bits < 1 || c->v_bits > 4) return fail(BGTQ_E_INVALID, "v_bits must be in 1..4");
+    g.v_mode = c->v_mode;
+    g.v_bits = c->v_bits;
+    g.n_recent = c->n_recent;
+    g.k_tile_bytes = (int64_t)TILE * g.R * 4;
+    g.v_tile_bytes = (int64_t)1024 * g.v_bits;
+    const int64_t bh = (int64_t)g.B * g.Hkv;
+    g.k_codes_layer = bh * g.n_tiles * g.k_tile_bytes;
+    g.v_codes_layer = bh * g.n_tiles * g.v_tile_bytes;
+    g.k_scale_layer = bh * g.n_cap * 2 * (c->k_mode == BGTQ_K_AFFINE ? D / c->k_group : 1);
+    g.v_scale_layer = bh * g.n_cap * 2;
+    g.recent_layer = bh * (int64_t)g.n_recent * D * 2;
+    return BGTQ_OK;
+}
+
+int64_t prep_bytes(const bgtq::Geometry& g) {
+    return (int64_t)g.B * g.Hkv * bgtq::prep_layout(g.G).stride * 4;
+}
+
+int default_splits(int64_t max_tiles, int bh, int n_cu) {
+    // Enough workgroups to cover every CU about twice, with at least 8 tiles (2 per wave) each.
+    int64_t target = (int64_t)2 * n_cu;
+    int64_t s = (target + bh - 1) / bh;
+    int64_t max_s = (max_tiles + 7) / 8;
+    if (s > max_s) s = max_s;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+int cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0;
+        hipDeviceProp_t p;
+        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess) n = p.multiProcessorCount;
+        if (n <= 0) n = 256;
+    }
+    return n;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* bgtq_last_error(void) { return g_err.c_str(); }
+
+const char* bgtq_version(void) { return "bgtq 0.1 (gfx950)"; }
+
+int bgtq_codebook(int bits, uint16_t* centroids_f16, float* thresholds) {
+    if (bits < 1 || bits > 8) return fail(BGTQ_E_INVALID, "bits must be in 1..8");
+    const int n = 1 << bits;
+    const int cb = n - 2, tb = n - bits - 1;
+    if (centroids_f16)
+        for (int m = 0; m < n; ++m) centroids_f16[m] = bgtq_cb_centroid_f16[cb + m];
+    if (thresholds)
+        for (int m = 0; m < n - 1; ++m) std::memcpy(&thresholds[m], &bgtq_cb_threshold_f32[tb + m], 4);
+    return ok();
+}
+
+int bgtq_allocate(const double* scores, int n_heads, int n_blk, int budget_units, int b_min, int b_max,
+                  uint8_t* bits_out) {
+    if (!scores || !bits_out) return fail(BGTQ_E_INVALID, "NULL pointer");
+    if (n_heads < 1 || n_blk < 1 || n_blk > 256) return fail(BGTQ_E_INVALID, "bad n_heads/n_blk");
+    if (b_max < 1 || b_max > 8 || b_min < 0 || b_min > b_max) return fail(BGTQ_E_INVALID, "bad b_min/b_max");
+    if (budget_units < 0) return fail(BGTQ_E_INVALID, "negative budget");
+    for (int64_t i = 0; i < (int64_t)n_heads * n_blk; ++i)
+        if (!(scores[i] >= 0.0) || !std::isfinite(scores[i]))
+            return fail(BGTQ_E_INVALID, "score %lld is negative or not finite", (long long)i);
+    std::vector<uint8_t> out((size_t)n_heads * n_blk);
+    for (int hd = 0; hd < n_heads; ++hd) {
+        const double* s = scores + (size_t)hd * n_blk;
+        uint8_t* b = out.data() + (size_t)hd * n_blk;
+        int spent = 0;
+        for (int i = 0; i < n_blk; ++i) {
+            b[i] = s[i] > 0.0 ? (uint8_t)b_min : 0;
+            spent += b[i];
+        }
+        if (spent > budget_units) return fail(BGTQ_E_BUDGET, "b_min exceeds the budget (head %d)", hd);
+        for (; spent < budget_units; ++spent) {
+            int best = -1;
+            double best_key = 0.0;
+            for (int i = 0; i < n_blk; ++i) {
+                if (b[i] >= b_max || !(s[i] > 0.0)) continue;
+                const double key = std::ldexp(s[i], -2 * (int)b[i]);  // exact: s * 4^-b
+                if (best < 0 || key > best_key) {
+                    best = i;
+                    best_key = key;
+                }
+            }
+            if (best < 0) return fail(BGTQ_E_BUDGET, "budget %d exceeds what head %d can hold", budget_units, hd);
+            ++b[best];
+        }
+    }
+    std::memcpy(bits_out, out.data(), out.size());
+    return ok();
+}
+
+int bgtq_block_energy(const void* k_cal, const void* q_cal, int dtype, int64_t T_cal, int Hkv, int g, int d,
+                      int score_mode, double* scores, float* sigma, float* inv_sigma, void* ws, size_t ws_bytes,
+                      void* stream) {
+    if (!k_cal || !q_cal || !ws) return fail(BGTQ_E_INVALID, "NULL pointer");
+    if (!dtype_ok(dtype)) return fail(BGTQ_E_INVALID, "bad dtype");
+    if (d != D) return fail(BGTQ_E_UNSUPPORTED, "head dim must be 128");
+    if (T_cal < 1 || Hkv < 1 || g < 1) return fail(BGTQ_E_INVALID, "bad sizes");
+    if (score_mode != BGTQ_SCORE_QK && score_mode != BGTQ_SCORE_K) return fail(BGTQ_E_INVALID, "bad score mode");
+    const size_t need = (size_t)Hkv * 64 * 2 * sizeof(double);
+    if (ws_bytes < need) return fail(BGTQ_E_INVALID, "workspace too small (%zu < %zu)", ws_bytes, need);
+    hipStream_t s = (hipStream_t)stream;
+    bgtq::EnergyArgs a{k_cal, q_cal, dtype, T_cal, Hkv, g, (double*)ws};
+    hipError_t e = bgtq::launch_energy(a, s);
+    if (e != hipSuccess) return hip_fail(e, "energy launch");
+    std::vector<double> host((size_t)Hkv * 128);
+    e = hipMemcpyAsync(host.data(), ws, need, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "energy copy");
+    for (int h = 0; h < Hkv; ++h)
+        for (int i = 0; i < 64; ++i) {
+            const double ek = host[(h * 64 + i) * 2] / (double)T_cal;
+            const double eq = host[(h * 64 + i) * 2 + 1] / ((double)T_cal * g);
+            const float sg = (float)std::sqrt(ek / 2.0);
+            if (scores) scores[h * 64 + i] = score_mode == BGTQ_SCORE_QK ? eq * ek : ek;
+            if (sigma) sigma[h * 64 + i] = sg;
+            if (inv_sigma) inv_sigma[h * 64 + i] = sg > 0.f ? 1.0f / sg : 0.f;
+        }
+    return ok();
+}
+
+int64_t bgtq_cache_bytes(const bgtq_cache* c, int which) {
+    bgtq::Geometry g;
+    int rc = geometry(c, g);
+    if (rc) return rc;
+    const int64_t L = c->L;
+    switch (which) {
+        case BGTQ_BUF_K_CODES: return L * g.k_codes_layer;
+        case BGTQ_BUF_V_CODES: return L * g.v_codes_layer;
+        case BGTQ_BUF_K_SCALE: return L * g.k_scale_layer;
+        case BGTQ_BUF_K_ZERO: return c->k_mode == BGTQ_K_AFFINE ? L * g.k_scale_layer : 0;
+        case BGTQ_BUF_V_SCALE: return L * g.v_scale_layer;
+        case BGTQ_BUF_V_ZERO: return c->v_mode == BGTQ_V_AFFINE ? L * g.v_scale_layer : 0;
+        case BGTQ_BUF_RECENT_K:
+        case BGTQ_BUF_RECENT_V: return L * g.recent_layer;
+        case BGTQ_BUF_META: return L * g.Hkv * 64 * (1 + 4 + 4);
+    }
+    return fail(BGTQ_E_INVALID, "unknown buffer selector %d", which);
+}
+
+int bgtq_quantize_append(bgtq_cache* c, int layer, const void* k, const void* v, int dtype, int64_t n_new,
+                         const int64_t* strides, void* stream) {
+    bgtq::Geometry g;
+    int rc = geometry(c, g);
+    if (rc) return rc;
+    if (layer < 0 || layer >= c->L) return fail(BGTQ_E_INVALID, "layer %d out of range", layer);
+    if (!k || !v) return fail(BGTQ_E_INVALID, "NULL k/v");
+    if (!dtype_ok(dtype)) return fail(BGTQ_E_INVALID, "bad dtype");
+    if (n_new < 0) return fail(BGTQ_E_INVALID, "n_new < 0");
+    if (!c->n_tokens) return fail(BGTQ_E_INVALID, "n_tokens is NULL");
+    if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale) return fail(BGTQ_E_INVALID, "NULL cache buffer");
+    if (c->k_mode == BGTQ_K_BLOCKGTQ && (!c->bits || !c->sigma || !c->inv_sigma))
+        return fail(BGTQ_E_INVALID, "Block-GTQ keys need bits, sigma and inv_sigma");
+    if (c->k_mode == BGTQ_K_AFFINE && !c->k_zero) return fail(BGTQ_E_INVALID, "affine keys need k_zero");
+    if (c->v_mode == BGTQ_V_AFFINE && !c->v_zero) return fail(BGTQ_E_INVALID, "affine values need v_zero");
+    if (c->n_recent > 0 && (!c->recent_k || !c->recent_v)) return fail(BGTQ_E_INVALID, "recent ring buffers are NULL");
+    int64_t sB, sT, sH;
+    if (strides) {
+        sB = strides[0]; sT = strides[1]; sH = strides[2];
+    } else {
+        sH = D; sT = (int64_t)g.Hkv * D; sB = n_new * sT;
+    }
+    int64_t* nt = c->n_tokens + (size_t)layer * c->B;
+    const int R = c->n_recent;
+    // Plan: positions [packed_old, packed_new) get quantized; the new fp16 window is written last.
+    std::vector<int64_t> packed_old(c->B), packed_new(c->B), total_old(c->B), total_new(c->B);
+    for (int b = 0; b < c->B; ++b) {
+        if (nt[b] < 0) return fail(BGTQ_E_INVALID, "n_tokens[%d] < 0", b);
+        total_old[b] = nt[b];
+        total_new[b] = nt[b] + n_new;
+        packed_old[b] = total_old[b] - (R > 0 ? std::min<int64_t>(total_old[b], R) : 0);
+        packed_new[b] = total_new[b] - (R > 0 ? std::min<int64_t>(total_new[b], R) : 0);
+        if (packed_new[b] > c->n_cap)
+            return fail(BGTQ_E_CAPACITY, "sequence %d: %lld packed tokens exceed n_cap %lld", b,
+                        (long long)packed_new[b], (long long)c->n_cap);
+    }
+    if (n_new == 0) return ok();
+    hipStream_t s = (hipStream_t)stream;
+    const size_t bh = (size_t)g.B * g.Hkv;
+    bgtq::QuantArgs q{};
+    q.dtype = dtype;
+    q.k_codes = (uint8_t*)c->k_codes + (size_t)layer * g.k_codes_layer;
+    q.v_codes = (uint8_t*)c->v_codes + (size_t)layer * g.v_codes_layer;
+    q.k_scale = (uint16_t*)((uint8_t*)c->k_scale + (size_t)layer * g.k_scale_layer);
+    q.k_zero = c->k_zero ? (uint16_t*)((uint8_t*)c->k_zero + (size_t)layer * g.k_scale_layer) : nullptr;
+    q.v_scale = (uint16_t*)((uint8_t*)c->v_scale + (size_t)layer * g.v_scale_layer);
+    q.v_zero = c->v_zero ? (uint16_t*)((uint8_t*)c->v_zero + (size_t)layer * g.v_scale_layer) : nullptr;
+    if (c->k_mode == BGTQ_K_BLOCKGTQ) {
+        q.bits = c->bits + (size_t)layer * g.Hkv * 64;
+        q.sigma = c->sigma + (size_t)layer * g.Hkv * 64;
+        q.inv_sigma = c->inv_sigma + (size_t)layer * g.Hkv * 64;
+    }
+    q.Hkv = g.Hkv;
+    q.n_cap = g.n_cap;
+    q.n_tiles = g.n_tiles;
+    q.k_tile_bytes = g.k_tile_bytes;
+    q.v_tile_bytes = g.v_tile_bytes;
+    q.k_mode = c->k_mode;
+    q.R = g.R;
+    q.k_bits = c->k_bits;
+    q.k_group = c->k_group;
+    q.v_mode = c->v_mode;
+    q.v_bits = c->v_bits;
+    q.which = 3;
+    hipError_t e;
+    auto run = [&](const void* sk, const void* sv, int dt, int64_t b_, int64_t t_, int64_t h_, int64_t mod_n,
+                   const std::vector<int64_t>& lo, const std::vector<int64_t>& hi,
+                   const std::vector<int64_t>& off) -> hipError_t {
+        q.src_k = sk;
+        q.src_v = sv;
+        q.dtype = dt;
+        q.sB = b_; q.sT = t_; q.sH = h_;
+        q.mod_n = mod_n;
+        int64_t max_tiles = 0;
+        for (int b = 0; b < c->B; ++b) {
+            q.pos_lo[b] = lo[b];
+            q.pos_hi[b] = hi[b];
+            q.off[b] = off[b];
+            q.tile0[b] = lo[b] / TILE;
+            if (hi[b] > lo[b]) max_tiles = std::max(max_tiles, (hi[b] - 1) / TILE - lo[b] / TILE + 1);
+        }
+        return bgtq::launch_quant(q, c->B, max_tiles, s);
+    };
+    std::vector<int64_t> lo(c->B), hi(c->B), off(c->B);
+    if (R > 0) {
+        // 1) tokens leaving the fp16 ring: positions [packed_old, min(packed_new, total_old)), from ring slots
+        const uint16_t* rk = (const uint16_t*)c->recent_k + (size_t)layer * bh * R * D;
+        const uint16_t* rv = (const uint16_t*)c->recent_v + (size_t)layer * bh * R * D;
+        for (int b = 0; b < c->B; ++b) {
+            lo[b] = packed_old[b];
+            hi[b] = std::min(packed_new[b], total_old[b]);
+            if (hi[b] < lo[b]) hi[b] = lo[b];
+            off[b] = 0;
+        }
+        e = run(rk, rv, BGTQ_F16, (int64_t)g.Hkv * R * D, D, (int64_t)R * D, R, lo, hi, off);
+        if (e != hipSuccess) return hip_fail(e, "quantize (ring eviction)");
+    }
+    // 2) new rows that go straight to the packed cache: positions [max(total_old, packed_old), packed_new)
+    for (int b = 0; b < c->B; ++b) {
+        lo[b] = std::max(total_old[b], packed_old[b]);
+        hi[b] = std::max(packed_new[b], lo[b]);
+        off[b] = total_old[b];
+    }
+    e = run(k, v, dtype, sB, sT, sH, 0, lo, hi, off);
+    if (e != hipSuccess) return hip_fail(e, "quantize (new rows)");
+    if (R > 0) {
+        // 3) new rows that stay in the fp16 window: positions [max(packed_new, total_old), total_new)
+        bgtq::RingArgs ra{};
+        ra.k = k;
+        ra.v = v;
+        ra.dtype = dtype;
+        ra.sB = sB; ra.sT = sT; ra.sH = sH;
+        ra.ring_k = (uint16_t*)c->recent_k + (size_t)layer * bh * R * D;
+        ra.ring_v = (uint16_t*)c->recent_v + (size_t)layer * bh * R * D;
+        ra.Hkv = g.Hkv;
+        ra.n_recent = R;
+        int64_t max_rows = 0;
+        for (int b = 0; b < c->B; ++b) {
+            ra.pos_lo[b] = std::max(packed_new[b], total_old[b]);
+            ra.pos_hi[b] = total_new[b];
+            ra.off[b] = total_old[b];
+            max_rows = std::max(max_rows, ra.pos_hi[b] - ra.pos_lo[b]);
+        }
+        e = bgtq::launch_ring(ra, c->B, max_rows, s);
+        if (e != hipSuccess) return hip_fail(e, "ring write");
+    }
+    for (int b = 0; b < c->B; ++b) nt[b] = total_new[b];
+    return ok();
+}
+
+int64_t bgtq_decode_workspace_bytes(const bgtq_cache* c, int n_splits) {
+    bgtq::Geometry g;
+    int rc = geometry(c, g);
+    if (rc) return rc;
+    if (n_splits < 0) return fail(BGTQ_E_INVALID, "n_splits < 0");
+    const int64_t max_tiles = g.n_tiles;
+    const int ns = n_splits ? n_splits : default_splits(max_tiles, g.B * g.Hkv, cu_count());
+    const int parts = ns + (g.n_recent > 0 ? 1 : 0);
+    return (int64_t)align256(prep_bytes(g)) + (int64_t)g.B * g.Hq * parts * PART * 4;
+}
+
+int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dtype, float* out, void* ws,
+                          size_t ws_bytes, int n_splits, void* stream) {
+    bgtq::Geometry g;
+    int rc = geometry(c, g);
+    if (rc) return rc;
+    if (layer < 0 || layer >= c->L) return fail(BGTQ_E_INVALID, "layer %d out of range", layer);
+    if (!q || !out || !ws) return fail(BGTQ_E_INVALID, "NULL q/out/ws");
+    if (((uintptr_t)ws) & 255) return fail(BGTQ_E_INVALID, "workspace must be 256-byte aligned");
+    if (!dtype_ok(dtype)) return fail(BGTQ_E_INVALID, "bad dtype");
+    if (!c->n_tokens) return fail(BGTQ_E_INVALID, "n_tokens is NULL");
+    if (n_splits < 0) return fail(BGTQ_E_INVALID, "n_splits < 0");
+    if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale) return fail(BGTQ_E_INVALID, "NULL cache buffer");
+    if (c->k_mode == BGTQ_K_BLOCKGTQ && (!c->bits || !c->sigma)) return fail(BGTQ_E_INVALID, "NULL key metadata");
+    if (c->k_mode == BGTQ_K_AFFINE && !c->k_zero) return fail(BGTQ_E_INVALID, "affine keys need k_zero");
+    if (c->v_mode == BGTQ_V_AFFINE && !c->v_zero) return fail(BGTQ_E_INVALID, "affine values need v_zero");
+    if (c->n_recent > 0 && (!c->recent_k || !c->recent_v)) return fail(BGTQ_E_INVALID, "recent ring buffers are NULL");
+    if (!bgtq::decode_supported(c->k_mode, g.R, c->k_bits, c->k_group, c->v_bits, g.G))
+        return fail(BGTQ_E_UNSUPPORTED, "no decode kernel for this format (k_mode %d, R %d, k_bits %d, k_group %d, "
+                    "v_bits %d, g %d)", c->k_mode, g.R, c->k_bits, c->k_group, c->v_bits, g.G);
+    const int64_t* nt = c->n_tokens + (size_t)layer * c->B;
+    bgtq::DecodeArgs a{};
+    int64_t max_tiles = 0;
+    bool any_recent = false;
+    for (int b = 0; b < c->B; ++b) {
+        if (nt[b] <= 0) return fail(BGTQ_E_INVALID, "sequence %d has an empty context", b);
+        const int64_t rec = c->n_recent > 0 ? std::min<int64_t>(nt[b], c->n_recent) : 0;
+        a.n_packed[b] = nt[b] - rec;
+        a.n_rec[b] = (int32_t)rec;
+        if (a.n_packed[b] > c->n_cap) return fail(BGTQ_E_INVALID, "sequence %d exceeds n_cap", b);
+        max_tiles = std::max(max_tiles, (a.n_packed[b] + TILE - 1) / TILE);
+        any_recent |= rec > 0;
+    }
+    const int ns = n_splits ? n_splits : default_splits(g.n_tiles, g.B * g.Hkv, cu_count());
+    const int parts = ns + (c->n_recent > 0 ? 1 : 0);
+    const size_t prep_sz = align256(prep_bytes(g));
+    const size_t need = prep_sz + (size_t)g.B * g.Hq * parts * PART * 4;
+    if (ws_bytes < need) return fail(BGTQ_E_INVALID, "workspace too small (%zu < %zu)", ws_bytes, need);
+    (void)any_recent;
+    hipStream_t s = (hipStream_t)stream;
+    const bgtq::PrepLayout PL = bgtq::prep_layout(g.G);
+    uint32_t* prep = (uint32_t*)ws;
+    float* part = (float*)((uint8_t*)ws + prep_sz);
+    bgtq::PrepArgs pa{};
+    pa.q = q;
+    pa.dtype = dtype;
+    pa.bits = c->k_mode == BGTQ_K_BLOCKGTQ ? c->bits + (size_t)layer * g.Hkv * 64 : nullptr;
+    pa.sigma = c->k_mode == BGTQ_K_BLOCKGTQ ? c->sigma + (size_t)layer * g.Hkv * 64 : nullptr;
+    pa.out = prep;
+    pa.Hkv = g.Hkv;
+    pa.G = g.G;
+    pa.k_mode = c->k_mode;
+    pa.k_group = c->k_mode == BGTQ_K_AFFINE ? c->k_group : 128;
+    pa.stride = PL.stride;
+    hipError_t e = bgtq::launch_prep(pa, g.B, s);
+    if (e != hipSuccess) return hip_fail(e, "prep launch");
+    const size_t bh = (size_t)g.B * g.Hkv;
+    a.k_codes = (const uint8_t*)c->k_codes + (size_t)layer * g.k_codes_layer;
+    a.v_codes = (const uint8_t*)c->v_codes + (size_t)layer * g.v_codes_layer;
+    a.k_scale = (const uint16_t*)((const uint8_t*)c->k_scale + (size_t)layer * g.k_scale_layer);
+    a.k_zero = c->k_zero ? (const uint16_t*)((const uint8_t*)c->k_zero + (size_t)layer * g.k_scale_layer) : nullptr;
+    a.v_scale = (const uint16_t*)((const uint8_t*)c->v_scale + (size_t)layer * g.v_scale_layer);
+    a.v_zero = c->v_zero ? (const uint16_t*)((const uint8_t*)c->v_zero + (size_t)layer * g.v_scale_layer) : nullptr;
+    if (c->n_recent > 0) {
+        a.recent_k = (const uint16_t*)c->recent_k + (size_t)layer * bh * c->n_recent * D;
+        a.recent_v = (const uint16_t*)c->recent_v + (size_t)layer * bh * c->n_recent * D;
+    }
+    a.prep = prep;
+    a.part = part;
+    a.Hkv = g.Hkv;
+    a.Hq = g.Hq;
+    a.G = g.G;
+    a.n_cap = g.n_cap;
+    a.n_tiles = g.n_tiles;
+    a.k_tile_bytes = g.k_tile_bytes;
+    a.v_tile_bytes = g.v_tile_bytes;
+    a.k_group = c->k_group;
+    a.n_recent = c->n_recent;
+    a.n_splits = ns;
+    a.n_parts = parts;
+    a.tiles_per_split = (int)((max_tiles + ns - 1) / ns);
+    if (a.tiles_per_split < 1) a.tiles_per_split = 1;
+    a.prep_stride = PL.stride;
+    a.v_affine = c->v_mode == BGTQ_V_AFFINE;
+    e = bgtq::launch_decode(a, g.B, c->k_mode, g.R, c->v_bits, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    bgtq::CombineArgs ca{part, out, parts};
+    e = bgtq::launch_combine(ca, g.B * g.Hq, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return ok();
+}
+
+int64_t bgtq_fp16_decode_workspace_bytes(int64_t N, int B, int Hq, int Hkv, int n_splits) {
+    if (N < 1 || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || n_splits < 0) return fail(BGTQ_E_INVALID, "bad sizes");
+    const int G = Hq / Hkv;
+    const int ns = n_splits ? n_splits : default_splits((N + TILE - 1) / TILE, B * Hkv, cu_count());
+    return (int64_t)align256((size_t)B * Hkv * bgtq::prep_layout(G).stride * 4) + (int64_t)B * Hq * ns * PART * 4;
+}
+
+int bgtq_fp16_decode_attention(const void* k16, const void* v16, int64_t N, int B, int Hq, int Hkv, int d,
+                               const void* q, int dtype, float* out, void* ws, size_t ws_bytes, int n_splits,
+                               void* stream) {
+    if (!k16 || !v16 || !q || !out || !ws) return fail(BGTQ_E_INVALID, "NULL pointer");
+    if (d != D) return fail(BGTQ_E_UNSUPPORTED, "head dim must be 128");
+    if (N < 1 || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(BGTQ_E_INVALID, "bad sizes");
+    if (!dtype_ok(dtype)) return fail(BGTQ_E_INVALID, "bad dtype");
+    if (n_splits < 0) return fail(BGTQ_E_INVALID, "n_splits < 0");
+    if (((uintptr_t)ws) & 255) return fail(BGTQ_E_INVALID, "workspace must be 256-byte aligned");
+    if (((uintptr_t)k16) & 15 || ((uintptr_t)v16) & 15) return fail(BGTQ_E_INVALID, "fp16 cache must be 16-byte aligned");
+    const int G = Hq / Hkv;
+    if (!(G == 1 || G == 2 || G == 4 || G == 8)) return fail(BGTQ_E_UNSUPPORTED, "group size %d unsupported", G);
+    const int64_t n_tiles = (N + TILE - 1) / TILE;
+    const int ns = n_splits ? n_splits : default_splits(n_tiles, B * Hkv, cu_count());
+    const bgtq::PrepLayout PL = bgtq::prep_layout(G);
+    const size_t prep_sz = align256((size_t)B * Hkv * PL.stride * 4);
+    const size_t need = prep_sz + (size_t)B * Hq * ns * PART * 4;
+    if (ws_bytes < need) return fail(BGTQ_E_INVALID, "workspace too small (%zu < %zu)", ws_bytes, need);
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t* prep = (uint32_t*)ws;
+    float* part = (float*)((uint8_t*)ws + prep_sz);
+    bgtq::PrepArgs pa{};
+    pa.q = q;
+    pa.dtype = dtype;
+    pa.out = prep;
+    pa.Hkv = Hkv;
+    pa.G = G;
+    pa.k_mode = BGTQ_K_AFFINE;  // natural-order query copy only
+    pa.k_group = 128;
+    pa.stride = PL.stride;
+    hipError_t e = bgtq::launch_prep(pa, B, s);
+    if (e != hipSuccess) return hip_fail(e, "prep launch");
+    bgtq::Fp16Args a{};
+    a.k16 = (const uint16_t*)k16;
+    a.v16 = (const uint16_t*)v16;
+    a.prep = prep;
+    a.part = part;
+    a.Hkv = Hkv;
+    a.Hq = Hq;
+    a.G = G;
+    a.N = N;
+    a.n_splits = ns;
+    a.tiles_per_split = (int)((n_tiles + ns - 1) / ns);
+    a.prep_stride = PL.stride;
+    e = bgtq::launch_fp16(a, B, s);
+    if (e != hipSuccess) return hip_fail(e, "fp16 decode launch");
+    bgtq::CombineArgs ca{part, out, ns};
+    e = bgtq::launch_combine(ca, B * Hq, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,979 @@
+// HIP kernels for packed-cache decode attention on CDNA4 (gfx950), wave64.
+//
+// Method: "RoPE-Aware Bit Allocation for KV-Cache Quantization" (Block-GTQ; abstract, review
+// §1/§3, Figures 1-2): keys quantized per RoPE block with greedy integer widths, values at one
+// width, attention computed directly from the packed codes.  Affine K4/V2 groups follow the
+// "Quantize What Counts" summary (Results: group-size sensitivity); the fp16 recent ring and the
+// order-free concatenation follow the "LogQuant" summary (Method 2 and Method 4).
+//
+// Decode mapping (one workgroup = 4 waves = one split of one (batch, kv head)):
+//  * q·k: lane = token.  The tile's K records are staged dword-major in LDS; each nonzero RoPE
+//    block (sorted by width) is one static "slot": a 64-bit LDS window, alignbit, two bit-field
+//    extracts, two centroid reads from an LDS table, then 2g FMAs whose query operand is
+//    broadcast from VGPRs with DPP row_newbcast (q' = q * sigma * log2(e)/sqrt(d), 16 values per
+//    VGPR, replicated in the 4 rows).  No MFMA: per (token, kv head) the work is a g-row GEMV.
+//  * online softmax in base 2, wave-uniform running max per head.
+//  * p·v: lane = (token quad slot, 8-dim group); the 2*v_bits-bit pair field indexes an LDS table
+//    of fp16 centroid pairs and v_dot2_f32_f16 accumulates w(t, t+1)·c(t, t+1) in fp32, with
+//    w = p * scale rounded to fp16 (as flash attention rounds P before P·V).
+//  * epilogue: cross-lane + cross-wave log-sum-exp merge, one (m, l, o) partial per split;
+//    a second kernel merges the splits.
+#include "bgtq_internal.h"
+
+#include "../../include/bgtq.h"
+#include "generated/bgtq_codebook_data.h"
+
+namespace bgtq {
+namespace {
+
+constexpr int TILE = 64;
+constexpr int D = 128;
+constexpr int PART = 132;                       // floats per partial record: o[128], m, l
+constexpr float kLog2eOverSqrtD = 0.12751743074233076f;  // log2(e) / sqrt(128)
+
+__constant__ uint32_t c_cent32[BGTQ_CB_CENTROIDS] = BGTQ_CB_CENTROID_F32_INIT;
+__constant__ uint16_t c_cent16[BGTQ_CB_CENTROIDS] = BGTQ_CB_CENTROID_F16_INIT;
+__constant__ uint32_t c_thr32[BGTQ_CB_THRESHOLDS] = BGTQ_CB_THRESHOLD_F32_INIT;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int cent_base(int w) { return (1 << w) - 2; }
+__device__ __forceinline__ int thr_base(int w) { return (1 << w) - w - 1; }
+__device__ __forceinline__ float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float bf2f(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
+
+__device__ __forceinline__ float load_act(const void* p, int64_t i, int dtype) {
+    if (dtype == BGTQ_F32) return ((const float*)p)[i];
+    const uint32_t u = ((const uint16_t*)p)[i];
+    return dtype == BGTQ_F16 ? h2f(u) : bf2f(u);
+}
+
+// Orders LDS traffic of one wave: lanes exchange data through LDS without a workgroup barrier.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------------------------------------
+// acc[h] += bcast(q, lane BASE + h) * va ; acc[h] += bcast(q, lane BASE + G + h) * vb
+// DPP row_newbcast reads lane n of each 16-lane row; s_nop 1 covers the VALU->DPP read hazard.
+template <int G, int BASE> struct SlotFma;
+
+#define BGTQ_F(A, L, SRC) "v_fmac_f32_dpp " A ", %[q], " SRC " row_newbcast:" #L " row_mask:0xf bank_mask:0xf\n"
+
+template <int BASE> struct SlotFma<8, BASE> {
+    static __device__ __forceinline__ void run(float* a, float q, float va, float vb) {
+        static_assert(BASE == 0, "g = 8 uses whole VGPRs");
+        asm volatile("s_nop 1\n"
+                     BGTQ_F("%0", 0, "%[va]") BGTQ_F("%1", 1, "%[va]") BGTQ_F("%2", 2, "%[va]")
+                     BGTQ_F("%3", 3, "%[va]") BGTQ_F("%4", 4, "%[va]") BGTQ_F("%5", 5, "%[va]")
+                     BGTQ_F("%6", 6, "%[va]") BGTQ_F("%7", 7, "%[va]")
+                     BGTQ_F("%0", 8, "%[vb]") BGTQ_F("%1", 9, "%[vb]") BGTQ_F("%2", 10, "%[vb]")
+                     BGTQ_F("%3", 11, "%[vb]") BGTQ_F("%4", 12, "%[vb]") BGTQ_F("%5", 13, "%[vb]")
+                     BGTQ_F("%6", 14, "%[vb]") BGTQ_F("%7", 15, "%[vb]")
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+                       "+v"(a[6]), "+v"(a[7])
+                     : [q] "v"(q), [va] "v"(va), [vb] "v"(vb));
+    }
+};
+
+#define BGTQ_FN(A, L, SRC) "v_fmac_f32_dpp " A ", %[q], " SRC " row_newbcast:%c[" L "] row_mask:0xf bank_mask:0xf\n"
+
+template <int BASE> struct SlotFma<4, BASE> {
+    static __device__ __forceinline__ void run(float* a, float q, float va, float vb) {
+        asm volatile("s_nop 1\n"
+                     BGTQ_FN("%0", "l0", "%[va]") BGTQ_FN("%1", "l1", "%[va]")
+                     BGTQ_FN("%2", "l2", "%[va]") BGTQ_FN("%3", "l3", "%[va]")
+                     BGTQ_FN("%0", "l4", "%[vb]") BGTQ_FN("%1", "l5", "%[vb]")
+                     BGTQ_FN("%2", "l6", "%[vb]") BGTQ_FN("%3", "l7", "%[vb]")
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+                     : [q] "v"(q), [va] "v"(va), [vb] "v"(vb), [l0] "n"(BASE), [l1] "n"(BASE + 1),
+                       [l2] "n"(BASE + 2), [l3] "n"(BASE + 3), [l4] "n"(BASE + 4), [l5] "n"(BASE + 5),
+                       [l6] "n"(BASE + 6), [l7] "n"(BASE + 7));
+    }
+};
+
+template <int BASE> struct SlotFma<2, BASE> {
+    static __device__ __forceinline__ void run(float* a, float q, float va, float vb) {
+        asm volatile("s_nop 1\n"
+                     BGTQ_FN("%0", "l0", "%[va]") BGTQ_FN("%1", "l1", "%[va]")
+                     BGTQ_FN("%0", "l2", "%[vb]") BGTQ_FN("%1", "l3", "%[vb]")
+                     : "+v"(a[0]), "+v"(a[1])
+                     : [q] "v"(q), [va] "v"(va), [vb] "v"(vb), [l0] "n"(BASE), [l1] "n"(BASE + 1),
+                       [l2] "n"(BASE + 2), [l3] "n"(BASE + 3));
+    }
+};
+
+template <int BASE> struct SlotFma<1, BASE> {
+    static __device__ __forceinline__ void run(float* a, float q, float va, float vb) {
+        asm volatile("s_nop 1\n"
+                     BGTQ_FN("%0", "l0", "%[va]") BGTQ_FN("%0", "l1", "%[vb]")
+                     : "+v"(a[0])
+                     : [q] "v"(q), [va] "v"(va), [vb] "v"(vb), [l0] "n"(BASE), [l1] "n"(BASE + 1));
+    }
+};
+
+// slot s (RoPE block in sorted or natural order) -> (q VGPR, first DPP lane)
+template <int G, int S> struct SlotPos {
+    static constexpr int vgpr = (S * 2 * G) / 16;
+    static constexpr int base = (S * 2 * G) % 16;
+};
+
+// ---------------------------------------------------------------------------------------------
+// Per-wave softmax / P·V state.
+template <int G> struct WaveState {
+    float m[G];        // running max (base-2 logits), wave-uniform
+    float l[G];        // per-lane partial sum of p
+    float zs[G];       // per-lane partial sum of p * zero (affine values)
+    float o[G][8];     // lane (quad slot, 8-dim group) accumulators
+};
+
+template <int G> __device__ __forceinline__ void state_init(WaveState<G>& st) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        st.m[h] = -INFINITY;
+        st.l[h] = 0.f;
+        st.zs[h] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.o[h][j] = 0.f;
+    }
+}
+
+// z: base-2 logits of this lane's token (-inf if invalid).  wscale multiplies p into the fp16
+// weight; zero (affine values) accumulates p * zero.  Writes fp16 weights to wbuf[pair*G + h].
+template <int G>
+__device__ __forceinline__ void softmax_tile(WaveState<G>& st, const float* z, bool valid, float wscale,
+                                             float zero, uint16_t* wbuf, int lane) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        if (__ballot(z[h] > st.m[h])) {
+            const float mn = fmaxf(st.m[h], wave_max(z[h]));
+            const float alpha = __builtin_amdgcn_exp2f(st.m[h] - mn);
+            st.m[h] = mn;
+            st.l[h] *= alpha;
+            st.zs[h] *= alpha;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) st.o[h][j] *= alpha;
+        }
+        const float p = valid ? __builtin_amdgcn_exp2f(z[h] - st.m[h]) : 0.f;
+        st.l[h] += p;
+        st.zs[h] += p * zero;
+        wbuf[((lane >> 1) * G + h) * 2 + (lane & 1)] = valid ? f2h(p * wscale) : (uint16_t)0;
+    }
+}
+
+// Extract the 2*VB-bit field f (static) from a VB-dword record.
+template <int VB, int F>
+__device__ __forceinline__ uint32_t vfield(const uint32_t* r) {
+    constexpr int bit = 2 * VB * F, w = bit / 32, sh = bit % 32, nb = 2 * VB;
+    if constexpr (sh + nb <= 32) {
+        return (r[w] >> sh) & ((1u << nb) - 1u);
+    } else {
+        return __builtin_amdgcn_alignbit(r[w + 1], r[w], sh) & ((1u << nb) - 1u);
+    }
+}
+
+template <int G, int VB, int F>
+__device__ __forceinline__ void pv_field(WaveState<G>& st, const uint32_t* r, const uint32_t (&w)[2][G],
+                                         const uint32_t* vlut) {
+    const uint32_t cp = vlut[vfield<VB, F>(r)];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+        st.o[h][F & 7] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[F >> 3][h]),
+                                                __builtin_bit_cast(half2_t, cp), st.o[h][F & 7], false);
+}
+
+template <int G, int VB, int F = 0>
+__device__ __forceinline__ void pv_fields(WaveState<G>& st, const uint32_t* r, const uint32_t (&w)[2][G],
+                                          const uint32_t* vlut) {
+    if constexpr (F < 16) {
+        pv_field<G, VB, F>(st, r, w, vlut);
+        pv_fields<G, VB, F + 1>(st, r, w, vlut);
+    }
+}
+
+// Load the fp16 weight pairs of quad `quad` (pairs 2quad, 2quad+1) for all heads.
+template <int G>
+__device__ __forceinline__ void load_w(uint32_t (&w)[2][G], const uint16_t* wbuf, int quad) {
+    const uint32_t* wb = (const uint32_t*)wbuf + 2 * quad * G;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int h = 0; h < G; ++h) w[p][h] = wb[p * G + h];
+}
+
+// Epilogue: merge lanes and waves, write one (o[128], m, l) partial per query head.
+template <int G>
+__device__ __forceinline__ void write_partial(WaveState<G>& st, float* red /*[4][G][PART]*/, float* part,
+                                              int n_parts, int split, int wave, int lane) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float v = st.o[h][j];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            st.o[h][j] = v;
+        }
+        st.l[h] = wave_sum(st.l[h]);
+        st.zs[h] = wave_sum(st.zs[h]);
+    }
+    float* r = red + wave * G * PART;
+    if (lane < 16) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r[h * PART + lane * 8 + j] = st.o[h][j];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            r[h * PART + 128] = st.m[h];
+            r[h * PART + 129] = st.l[h];
+            r[h * PART + 130] = st.zs[h];
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * 130; idx += blockDim.x) {
+        const int h = idx / 130, j = idx % 130;
+        float M = -INFINITY;
+        for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, red[(wv * G + h) * PART + 128]);
+        float acc = 0.f;
+        for (int wv = 0; wv < 4; ++wv) {
+            const float* rw = red + (wv * G + h) * PART;
+            const float sc = (rw[128] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rw[128] - M);
+            if (j < 128) acc += sc * (rw[j] + rw[130]);
+            else if (j == 129) acc += sc * rw[129];
+        }
+        float* dst = part + ((size_t)h * n_parts + split) * PART;
+        dst[j] = (j == 128) ? M : acc;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// q·k over one Block-GTQ slot (static S), record staged dword-major in LDS.
+template <int G, int S>
+__device__ __forceinline__ void gtq_slot(float* acc, const float* qv, uint32_t d16, const uint32_t* stg,
+                                         const float* klut) {
+    const uint32_t k = d16 & 31u, o = (d16 >> 5) & 31u, w = d16 >> 10;
+    const uint32_t lo = stg[k * TILE], hi = stg[(k + 1) * TILE];
+    const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, o);
+    const uint32_t ca = x & ((1u << w) - 1u);
+    const uint32_t cb = __builtin_amdgcn_ubfe(x, w, w);
+    const float* lut = klut + ((1 << w) - 2);
+    SlotFma<G, SlotPos<G, S>::base>::run(acc, qv[SlotPos<G, S>::vgpr], lut[ca], lut[cb]);
+}
+
+template <int G, int GR = 0>
+__device__ __forceinline__ void gtq_groups(float* acc, const float* qv, const uint32_t* dsc, int nnz_pad,
+                                           const uint32_t* stg, const float* klut) {
+    if constexpr (GR < 16) {
+        if (GR * 4 < nnz_pad) {
+            gtq_slot<G, 4 * GR + 0>(acc, qv, dsc[2 * GR] & 0xFFFFu, stg, klut);
+            gtq_slot<G, 4 * GR + 1>(acc, qv, dsc[2 * GR] >> 16, stg, klut);
+            gtq_slot<G, 4 * GR + 2>(acc, qv, dsc[2 * GR + 1] & 0xFFFFu, stg, klut);
+            gtq_slot<G, 4 * GR + 3>(acc, qv, dsc[2 * GR + 1] >> 16, stg, klut);
+            gtq_groups<G, GR + 1>(acc, qv, dsc, nnz_pad, stg, klut);
+        }
+    }
+}
+
+// q·k over natural-order blocks of an in-register fp16 row chunk (blocks B0..B0+15).
+template <int G, int B0, int I = 0>
+__device__ __forceinline__ void fp16_blocks(float* acc, const float* qv, const uint32_t* row16) {
+    if constexpr (I < 16) {
+        const uint32_t x = row16[I];
+        SlotFma<G, SlotPos<G, B0 + I>::base>::run(acc, qv[SlotPos<G, B0 + I>::vgpr], h2f(x & 0xFFFFu), h2f(x >> 16));
+        fp16_blocks<G, B0, I + 1>(acc, qv, row16);
+    }
+}
+
+template <int N> __device__ __forceinline__ float ubyte_f(uint32_t x) { return (float)((x >> (8 * N)) & 0xFFu); }
+
+// q·k over affine 4-bit keys: 16 dwords of nibbles (coordinate j at bits 4j).  Dword K holds
+// coordinates 8K..8K+7; masking even/odd nibbles into bytes gives blocks 4K..4K+3 as byte pairs.
+// Per group of KG coordinates: z += scale * sum_j q_j code_j + zero * sum_j q_j.
+template <int G, int KG, int K = 0>
+__device__ __forceinline__ void affine4_run(float* acc, float* gp, const float* qv, const uint32_t* rec,
+                                            const float* scl, const float* zer, const float* qs) {
+    if constexpr (K < 16) {
+        const uint32_t x = rec[K];
+        const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+        SlotFma<G, SlotPos<G, 4 * K + 0>::base>::run(gp, qv[SlotPos<G, 4 * K + 0>::vgpr],
+                                                       ubyte_f<0>(lo), ubyte_f<0>(hi));
+        SlotFma<G, SlotPos<G, 4 * K + 1>::base>::run(gp, qv[SlotPos<G, 4 * K + 1>::vgpr],
+                                                       ubyte_f<1>(lo), ubyte_f<1>(hi));
+        SlotFma<G, SlotPos<G, 4 * K + 2>::base>::run(gp, qv[SlotPos<G, 4 * K + 2>::vgpr],
+                                                       ubyte_f<2>(lo), ubyte_f<2>(hi));
+        SlotFma<G, SlotPos<G, 4 * K + 3>::base>::run(gp, qv[SlotPos<G, 4 * K + 3>::vgpr],
+                                                       ubyte_f<3>(lo), ubyte_f<3>(hi));
+        constexpr int DPG = KG / 8;
+        if constexpr ((K + 1) % DPG == 0) {
+            constexpr int gi = K / DPG;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                acc[h] += scl[gi] * gp[h] + zer[gi] * qs[gi * G + h];
+                gp[h] = 0.f;
+            }
+        }
+        affine4_run<G, KG, K + 1>(acc, gp, qv, rec, scl, zer, qs);
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void load_qv(float* qv, const uint32_t* src, int lane) {
+    const float* s = (const float*)src;
+#pragma unroll
+    for (int v = 0; v < 8 * G; ++v) qv[v] = s[v * 16 + (lane & 15)];
+}
+
+// fp16 tiles (recent ring or the unquantized comparator): rows [n][128] fp16 of one (b, h).
+template <int G>
+__device__ void fp16_tiles(WaveState<G>& st, const uint16_t* K16, const uint16_t* V16, int64_t n,
+                           int64_t t_lo, int64_t t_hi, int wave, const float* qv, uint16_t* wbuf, int lane) {
+    for (int64_t t = t_lo + wave; t < t_hi; t += 4) {
+        const int64_t pos = t * TILE + lane;
+        const bool valid = pos < n;
+        float acc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = 0.f;
+        const uint4* rowp = (const uint4*)(K16 + (valid ? pos : 0) * D);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint32_t r16[16];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint4 v = rowp[c * 4 + u];
+                r16[4 * u] = v.x; r16[4 * u + 1] = v.y; r16[4 * u + 2] = v.z; r16[4 * u + 3] = v.w;
+            }
+            if (c == 0) fp16_blocks<G, 0>(acc, qv, r16);
+            if (c == 1) fp16_blocks<G, 16>(acc, qv, r16);
+            if (c == 2) fp16_blocks<G, 32>(acc, qv, r16);
+            if (c == 3) fp16_blocks<G, 48>(acc, qv, r16);
+        }
+        float z[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) z[h] = valid ? acc[h] : -INFINITY;
+        wave_lds_fence();
+        softmax_tile<G>(st, z, valid, 1.0f, 0.f, wbuf, lane);
+        wave_lds_fence();
+        // P·V: lane = (quad slot, 8-dim group); tokens 4quad..4quad+3, dims 8dg..8dg+7
+        const int dg = lane & 15;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int quad = it * 4 + (lane >> 4);
+            uint32_t w[2][G];
+            load_w<G>(w, wbuf, quad);
+            uint4 vr[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t p = t * TILE + quad * 4 + u;
+                vr[u] = p < n ? *(const uint4*)(V16 + p * D + dg * 8) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const uint32_t a4[4] = {vr[2 * pr].x, vr[2 * pr].y, vr[2 * pr].z, vr[2 * pr].w};
+                const uint32_t b4[4] = {vr[2 * pr + 1].x, vr[2 * pr + 1].y, vr[2 * pr + 1].z, vr[2 * pr + 1].w};
+#pragma unroll
+                for (int m2 = 0; m2 < 4; ++m2) {
+                    const uint32_t lo = __builtin_amdgcn_perm(b4[m2], a4[m2], 0x05040100u);  // (a.lo, b.lo)
+                    const uint32_t hi = __builtin_amdgcn_perm(b4[m2], a4[m2], 0x07060302u);  // (a.hi, b.hi)
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        st.o[h][2 * m2] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[pr][h]),
+                                                                 __builtin_bit_cast(half2_t, lo), st.o[h][2 * m2], false);
+                        st.o[h][2 * m2 + 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[pr][h]),
+                                                                     __builtin_bit_cast(half2_t, hi), st.o[h][2 * m2 + 1], false);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// KG == 0: Block-GTQ keys (R record dwords); KG > 0: affine 4-bit keys with groups of KG.
+template <int G, int R, int VB, int KG>
+__global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
+    constexpr bool AFFINE_K = KG > 0;
+    constexpr int NG = AFFINE_K ? D / (KG > 0 ? KG : 1) : 1;
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __shared__ float s_klut[512];
+    __shared__ uint32_t s_vlut[1 << (2 * VB)];
+    __shared__ uint32_t s_stage[4][AFFINE_K ? 1 : (R + 1) * TILE];
+    __shared__ uint16_t s_w[4][64 * G];
+    __shared__ float s_red[4 * G * PART];
+
+    for (int i = threadIdx.x; i < BGTQ_CB_CENTROIDS; i += blockDim.x) s_klut[i] = __builtin_bit_cast(float, c_cent32[i]);
+    for (int i = threadIdx.x; i < (1 << (2 * VB)); i += blockDim.x) {
+        const uint32_t ca = i & ((1 << VB) - 1), cb = i >> VB;
+        uint32_t ha, hb;
+        if (a.v_affine) {
+            ha = f2h((float)ca);
+            hb = f2h((float)cb);
+        } else {
+            ha = c_cent16[cent_base(VB) + ca];
+            hb = c_cent16[cent_base(VB) + cb];
+        }
+        s_vlut[i] = ha | (hb << 16);
+    }
+    __syncthreads();
+
+    const size_t bh = (size_t)b * a.Hkv + h;
+    const uint32_t* prep = a.prep + bh * a.prep_stride;
+    const PrepLayout PL = prep_layout(G);
+    float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_parts * PART;
+    uint16_t* wbuf = s_w[wave];
+
+    WaveState<G> st;
+    state_init<G>(st);
+    float qv[8 * G];
+
+    if (split == a.n_splits) {  // fp16 recent ring, concatenated order-free with the packed tokens
+        load_qv<G>(qv, prep + PL.qn(), lane);
+        const int64_t n = a.n_rec[b];
+        const uint16_t* rk = a.recent_k + bh * (size_t)a.n_recent * D;
+        const uint16_t* rv = a.recent_v + bh * (size_t)a.n_recent * D;
+        fp16_tiles<G>(st, rk, rv, n, 0, (n + TILE - 1) / TILE, wave, qv, wbuf, lane);
+        write_partial<G>(st, s_red, part, a.n_parts, split, wave, lane);
+        return;
+    }
+
+    load_qv<G>(qv, prep + (AFFINE_K ? PL.qn() : PL.qp()), lane);
+    uint32_t dsc[32];
+    int nnz_pad = 0;
+    float qs[NG * G];
+    constexpr int ng = NG;
+    if constexpr (!AFFINE_K) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) dsc[i] = prep[PL.desc() + i];
+        nnz_pad = (int)prep[PL.desc() + 32];
+    } else {
+        const float* qsp = (const float*)(prep + PL.qs());
+#pragma unroll
+        for (int i = 0; i < NG * G; ++i) qs[i] = qsp[i];
+    }
+
+    const int64_t n_packed = a.n_packed[b];
+    const int64_t n_tiles_b = (n_packed + TILE - 1) / TILE;
+    const int64_t t_lo = (int64_t)split * a.tiles_per_split;
+    const int64_t t_hi = t_lo + a.tiles_per_split < n_tiles_b ? t_lo + a.tiles_per_split : n_tiles_b;
+
+    const uint32_t* kc = (const uint32_t*)(a.k_codes + bh * a.n_tiles * a.k_tile_bytes);
+    const uint32_t* vc = (const uint32_t*)(a.v_codes + bh * a.n_tiles * a.v_tile_bytes);
+    const uint16_t* ks = a.k_scale + bh * a.n_cap * ng;
+    const uint16_t* kz = AFFINE_K ? a.k_zero + bh * a.n_cap * ng : nullptr;
+    const uint16_t* vs = a.v_scale + bh * a.n_cap;
+    const uint16_t* vz = a.v_affine ? a.v_zero + bh * a.n_cap : nullptr;
+    uint32_t* stg = s_stage[wave] + lane;
+
+    for (int64_t t = t_lo + wave; t < t_hi; t += 4) {
+        const int64_t pos = t * TILE + lane;
+        const bool valid = pos < n_packed;
+        const uint32_t* kt = kc + t * (a.k_tile_bytes / 4);
+        const uint32_t* vt = vc + t * (a.v_tile_bytes / 4);
+        uint32_t vrec[4][VB];
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int c = 0; c < VB; ++c) vrec[it][c] = vt[(it * 64 + lane) * VB + c];
+        const float vsc = h2f(vs[valid ? pos : 0]);
+        const float vzr = vz ? h2f(vz[valid ? pos : 0]) : 0.f;
+
+        float acc[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) acc[hh] = 0.f;
+        if constexpr (!AFFINE_K) {
+            uint32_t krec[R];
+#pragma unroll
+            for (int k = 0; k < R; ++k) krec[k] = kt[k * TILE + lane];
+            const float ksc = h2f(ks[valid ? pos : 0]);
+            wave_lds_fence();
+#pragma unroll
+            for (int k = 0; k < R; ++k) stg[k * TILE] = krec[k];
+            wave_lds_fence();
+            gtq_groups<G>(acc, qv, dsc, nnz_pad, stg, s_klut);
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) acc[hh] *= ksc;
+        } else {
+            uint32_t krec[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) krec[k] = kt[k * TILE + lane];
+            float scl[NG], zer[NG], gp[G];
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                scl[gi] = h2f(ks[(valid ? pos : 0) * NG + gi]);
+                zer[gi] = h2f(kz[(valid ? pos : 0) * NG + gi]);
+            }
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) gp[hh] = 0.f;
+            affine4_run<G, KG>(acc, gp, qv, krec, scl, zer, qs);
+        }
+        float z[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) z[hh] = valid ? acc[hh] : -INFINITY;
+        wave_lds_fence();
+        softmax_tile<G>(st, z, valid, vsc, vzr, wbuf, lane);
+        wave_lds_fence();
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            uint32_t w[2][G];
+            load_w<G>(w, wbuf, it * 4 + (lane >> 4));
+            pv_fields<G, VB>(st, vrec[it], w, s_vlut);
+        }
+    }
+    __syncthreads();
+    write_partial<G>(st, s_red, part, a.n_parts, split, wave, lane);
+}
+
+
+// Unquantized comparator: the same split-K decode over an fp16 [B][Hkv][N][128] cache.
+template <int G>
+__global__ __launch_bounds__(256) void k_decode_fp16(const Fp16Args a) {
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __shared__ uint16_t s_w[4][64 * G];
+    __shared__ float s_red[4 * G * PART];
+    const size_t bh = (size_t)b * a.Hkv + h;
+    const PrepLayout PL = prep_layout(G);
+    float qv[8 * G];
+    load_qv<G>(qv, a.prep + bh * a.prep_stride + PL.qn(), lane);
+    WaveState<G> st;
+    state_init<G>(st);
+    const int64_t n_tiles = (a.N + TILE - 1) / TILE;
+    const int64_t t_lo = (int64_t)split * a.tiles_per_split;
+    const int64_t t_hi = t_lo + a.tiles_per_split < n_tiles ? t_lo + a.tiles_per_split : n_tiles;
+    fp16_tiles<G>(st, a.k16 + bh * a.N * D, a.v16 + bh * a.N * D, a.N, t_lo, t_hi, wave, qv, s_w[wave], lane);
+    __syncthreads();
+    float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_splits * PART;
+    write_partial<G>(st, s_red, part, a.n_splits, split, wave, lane);
+}
+
+// Merge split partials (o, m, l) of one (batch, query head) by log-sum-exp.
+__global__ __launch_bounds__(128) void k_combine(const CombineArgs a) {
+    const int row = blockIdx.x, j = threadIdx.x;
+    const float* pr = a.part + (size_t)row * a.n_parts * PART;
+    float M = -INFINITY;
+    for (int s = 0; s < a.n_parts; ++s) M = fmaxf(M, pr[s * PART + 128]);
+    float L = 0.f, O = 0.f;
+    for (int s = 0; s < a.n_parts; ++s) {
+        const float m = pr[s * PART + 128];
+        if (m == -INFINITY) continue;
+        const float sc = __builtin_amdgcn_exp2f(m - M);
+        L += sc * pr[s * PART + 129];
+        O += sc * pr[s * PART + j];
+    }
+    a.out[(size_t)row * D + j] = O / L;
+}
+
+// Per (batch, kv head): block order, slot descriptors and the scaled query copies.
+__global__ __launch_bounds__(64) void k_prep(const PrepArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;  // i = RoPE block
+    const int G = a.G, Hq = a.Hkv * G;
+    const PrepLayout L = prep_layout(G);
+    uint32_t* out = a.out + ((size_t)b * a.Hkv + h) * a.stride;
+    float* qp = (float*)(out + L.qp());
+    float* qn = (float*)(out + L.qn());
+    float* qs = (float*)(out + L.qs());
+    __shared__ float s_qn[D][8];
+    __shared__ int s_wid[64];
+    __shared__ uint32_t s_desc[64];
+    float q0[8], q1[8];
+    for (int hh = 0; hh < G; ++hh) {
+        const int64_t base = ((int64_t)b * Hq + (int64_t)h * G + hh) * D + 2 * i;
+        q0[hh] = load_act(a.q, base, a.dtype);
+        q1[hh] = load_act(a.q, base + 1, a.dtype);
+        const float n0 = q0[hh] * kLog2eOverSqrtD, n1 = q1[hh] * kLog2eOverSqrtD;
+        qn[i * 2 * G + hh] = n0;
+        qn[i * 2 * G + G + hh] = n1;
+        s_qn[2 * i][hh] = n0;
+        s_qn[2 * i + 1][hh] = n1;
+    }
+    if (a.k_mode == BGTQ_K_BLOCKGTQ) {
+        const int w = a.bits[h * 64 + i];
+        s_wid[i] = w;
+        __syncthreads();
+        int rank = 0, pos = 0, nnz = 0;
+        for (int j = 0; j < 64; ++j) {
+            const int wj = s_wid[j];
+            const bool before = wj > w || (wj == w && j < i);
+            rank += before;
+            pos += before ? 2 * wj : 0;
+            nnz += wj > 0;
+        }
+        if (w > 0) {
+            const float sg = a.sigma[h * 64 + i] * kLog2eOverSqrtD;
+            for (int hh = 0; hh < G; ++hh) {
+                qp[rank * 2 * G + hh] = q0[hh] * sg;
+                qp[rank * 2 * G + G + hh] = q1[hh] * sg;
+            }
+            s_desc[rank] = (uint32_t)(pos >> 5) | ((uint32_t)(pos & 31) << 5) | ((uint32_t)w << 10);
+        }
+        if (i >= nnz) {  // padding slot: reads dword 0, contributes q' = 0
+            for (int hh = 0; hh < 2 * G; ++hh) qp[i * 2 * G + hh] = 0.f;
+            s_desc[i] = 1u << 10;
+        }
+        __syncthreads();
+        uint32_t* desc = out + L.desc();
+        if (i < 32) desc[i] = s_desc[2 * i] | (s_desc[2 * i + 1] << 16);
+        if (i == 0) desc[32] = (uint32_t)((nnz + 3) & ~3);
+    } else {
+        __syncthreads();
+        const int ng = D / a.k_group;
+        if (i < ng * G) {
+            const int gi = i / G, hh = i % G;
+            float acc = 0.f;
+            for (int j = gi * a.k_group; j < (gi + 1) * a.k_group; ++j) acc += s_qn[j][hh];
+            qs[gi * G + hh] = acc;
+        }
+    }
+}
+
+// Calibration energy sums in fp64: out[h][i] = (sum_t |k_t,blk i|^2, sum_{t,g} |q_t,g,blk i|^2).
+__global__ __launch_bounds__(256) void k_energy(const EnergyArgs a) {
+    const int h = blockIdx.x, blk = threadIdx.x & 63, part = threadIdx.x >> 6;
+    const int Hq = a.Hkv * a.G;
+    double ek = 0.0, eq = 0.0;
+    for (int64_t t = part; t < a.T; t += 4) {
+        const int64_t kb = (t * a.Hkv + h) * D + 2 * blk;
+        const double k0 = load_act(a.k, kb, a.dtype), k1 = load_act(a.k, kb + 1, a.dtype);
+        ek += k0 * k0 + k1 * k1;
+        for (int g = 0; g < a.G; ++g) {
+            const int64_t qb = (t * Hq + (int64_t)h * a.G + g) * D + 2 * blk;
+            const double q0 = load_act(a.q, qb, a.dtype), q1 = load_act(a.q, qb + 1, a.dtype);
+            eq += q0 * q0 + q1 * q1;
+        }
+    }
+    __shared__ double s_e[4][64][2];
+    s_e[part][blk][0] = ek;
+    s_e[part][blk][1] = eq;
+    __syncthreads();
+    if (part == 0) {
+        double sk = 0.0, sq = 0.0;
+        for (int p = 0; p < 4; ++p) {
+            sk += s_e[p][blk][0];
+            sq += s_e[p][blk][1];
+        }
+        a.out[(h * 64 + blk) * 2 + 0] = sk;
+        a.out[(h * 64 + blk) * 2 + 1] = sq;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Quantize-append.  The float32 steps are spelled out one IEEE operation at a time (no
+// contraction) so the codes and fp16 scales are reproducible bit for bit.
+__device__ __forceinline__ uint32_t tq_code(float x, float t, int w, const float* thr) {
+#pragma clang fp contract(off)
+    uint32_t code = 0;
+    const float* tb = thr + thr_base(w);
+    for (int st = w - 1; st >= 0; --st) {
+        const uint32_t cand = code + (1u << st);
+        const float th = t * tb[cand - 1];
+        if (x >= th) code = cand;
+    }
+    return code;
+}
+
+__device__ __forceinline__ float rms_scale16(const float* x /*LDS row, stride 1*/, const float* r /*per block or null*/,
+                                             uint16_t* s16) {
+#pragma clang fp contract(off)
+    float acc = 0.f;
+    for (int j = 0; j < D; ++j) {
+        const float u = r ? x[j] * r[j >> 1] : x[j];
+        acc = acc + u * u;
+    }
+    const float ms = acc / 128.0f;
+    const uint16_t h = f2h(sqrtf(ms));
+    *s16 = h;
+    return h2f(h);
+}
+
+__device__ __forceinline__ void affine_group(const float* x, int n, int bits, uint16_t* sc16, uint16_t* z16,
+                                             uint32_t* codes) {
+#pragma clang fp contract(off)
+    float mn = x[0], mx = x[0];
+    for (int j = 1; j < n; ++j) {
+        mn = fminf(mn, x[j]);
+        mx = fmaxf(mx, x[j]);
+    }
+    const float range = mx - mn;
+    const float scale = range / (float)((1 << bits) - 1);
+    const uint16_t s16 = f2h(scale), zz = f2h(mn);
+    *sc16 = s16;
+    *z16 = zz;
+    const float s32 = h2f(s16), z32 = h2f(zz);
+    const float top = (float)((1 << bits) - 1);
+    for (int j = 0; j < n; ++j) {
+        float c = 0.f;
+        if (s32 != 0.f) {
+            const float q = (x[j] - z32) / s32;
+            c = fminf(fmaxf(rintf(q), 0.f), top);
+        }
+        codes[j] = (uint32_t)c;
+    }
+}
+
+__global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
+    const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const int64_t tile = a.tile0[b] + blockIdx.x;
+    if (tile * TILE >= a.pos_hi[b]) return;  // whole workgroup beyond this sequence's range
+    const int64_t pos = tile * TILE + lane;
+    const bool active = pos >= a.pos_lo[b] && pos < a.pos_hi[b];
+    __shared__ float s_thr[BGTQ_CB_THRESHOLDS];
+    __shared__ float s_x[64][D + 1];
+    __shared__ int s_order[64];
+    __shared__ int s_wid[64];
+    __shared__ float s_r[64], s_sig[64];
+    for (int i = lane; i < BGTQ_CB_THRESHOLDS; i += 64) s_thr[i] = __builtin_bit_cast(float, c_thr32[i]);
+    const size_t bh = (size_t)b * a.Hkv + h;
+    const bool do_k = a.which & 1, do_v = (a.which >> 1) & 1;
+    int nnz = 0;
+    if (do_k && a.k_mode == BGTQ_K_BLOCKGTQ) {
+        const int w = a.bits[h * 64 + lane];
+        s_wid[lane] = w;
+        s_r[lane] = a.inv_sigma[h * 64 + lane];
+        s_sig[lane] = a.sigma[h * 64 + lane];
+        __syncthreads();
+        int rank = 0;
+        for (int j = 0; j < 64; ++j) {
+            const int wj = s_wid[j];
+            rank += wj > w || (wj == w && j < lane);
+            nnz += wj > 0;
+        }
+        if (w > 0) s_order[rank] = lane;
+    }
+    __syncthreads();
+    int64_t row = 0;
+    if (active) {
+        row = pos - a.off[b];
+        if (a.mod_n) row %= a.mod_n;
+    }
+    const int64_t base = (int64_t)b * a.sB + row * a.sT + (int64_t)h * a.sH;
+    for (int pass = 0; pass < 2; ++pass) {
+        if ((pass == 0 && !do_k) || (pass == 1 && !do_v)) continue;
+        const void* src = pass == 0 ? a.src_k : a.src_v;
+        const int64_t off = base;
+        float* x = s_x[lane];
+        for (int j = 0; j < D; ++j) x[j] = active ? load_act(src, off + j, a.dtype) : 0.f;
+        if (pass == 0) {
+            // ---- keys
+            uint32_t* kt = (uint32_t*)(a.k_codes + (bh * a.n_tiles + tile) * a.k_tile_bytes);
+            if (a.k_mode == BGTQ_K_BLOCKGTQ) {
+                uint16_t s16;
+                const float S = rms_scale16(x, s_r, &s16);
+                uint64_t buf = 0;
+                int nb = 0, k = 0;
+                for (int s = 0; s < nnz; ++s) {
+                    const int i = s_order[s], w = s_wid[i];
+                    float t;
+                    {
+#pragma clang fp contract(off)
+                        t = S * s_sig[i];
+                    }
+                    const uint32_t ca = tq_code(x[2 * i], t, w, s_thr);
+                    const uint32_t cb = tq_code(x[2 * i + 1], t, w, s_thr);
+                    buf |= (uint64_t)(ca | (cb << w)) << nb;
+                    nb += 2 * w;
+                    if (nb >= 32) {
+                        if (active) kt[k * TILE + lane] = (uint32_t)buf;
+                        buf >>= 32;
+                        nb -= 32;
+                        ++k;
+                    }
+                }
+                if (active) a.k_scale[bh * a.n_cap + pos] = s16;
+            } else {
+                const int ng = D / a.k_group;
+                uint32_t codes[D];
+                for (int gi = 0; gi < ng; ++gi) {
+                    uint16_t sc, zz;
+                    affine_group(x + gi * a.k_group, a.k_group, a.k_bits, &sc, &zz, codes + gi * a.k_group);
+                    if (active) {
+                        a.k_scale[(bh * a.n_cap + pos) * ng + gi] = sc;
+                        a.k_zero[(bh * a.n_cap + pos) * ng + gi] = zz;
+                    }
+                }
+                const int per = 32 / a.k_bits;
+                for (int k = 0; k < a.R; ++k) {
+                    uint32_t wv = 0;
+                    for (int u = 0; u < per; ++u) wv |= codes[k * per + u] << (u * a.k_bits);
+                    if (active) kt[k * TILE + lane] = wv;
+                }
+            }
+        } else {
+            // ---- values: quad layout, 4 lanes share each record
+            const int vb = a.v_bits;
+            uint32_t codes[D];
+            uint16_t s16 = 0, z16 = 0;
+            if (a.v_mode == BGTQ_V_CODEBOOK) {
+                const float S = rms_scale16(x, nullptr, &s16);
+                for (int j = 0; j < D; ++j) codes[j] = tq_code(x[j], S, vb, s_thr);
+            } else {
+                affine_group(x, D, vb, &s16, &z16, codes);
+            }
+            if (active) {
+                a.v_scale[bh * a.n_cap + pos] = s16;
+                if (a.v_mode == BGTQ_V_AFFINE) a.v_zero[bh * a.n_cap + pos] = z16;
+            }
+            const int tq = lane & 3;                 // token within quad
+            const int pr = tq >> 1, odd = tq & 1;
+            const int quad = lane >> 2;
+            const int64_t quad_pos = tile * TILE + quad * 4;
+            bool any = false;
+            for (int u = 0; u < 4; ++u) {
+                const int64_t p = quad_pos + u;
+                any |= p >= a.pos_lo[b] && p < a.pos_hi[b];
+            }
+            const bool rmw = quad_pos < a.pos_lo[b];
+            uint32_t* vt = (uint32_t*)(a.v_codes + (bh * a.n_tiles + tile) * a.v_tile_bytes);
+            for (int G8 = 0; G8 < 16; ++G8) {
+                uint32_t rec[4] = {0, 0, 0, 0};
+                if (active) {
+                    for (int f8 = 0; f8 < 8; ++f8) {
+                        const int f = pr * 8 + f8;
+                        const int bit = 2 * vb * f + odd * vb;
+                        const uint64_t v = (uint64_t)codes[8 * G8 + f8] << (bit % 32);
+                        rec[bit / 32] |= (uint32_t)v;
+                        if (bit / 32 + 1 < 4) rec[bit / 32 + 1] |= (uint32_t)(v >> 32);
+                    }
+                }
+                for (int c = 0; c < vb; ++c) {
+                    uint32_t r = rec[c];
+                    r |= __shfl_xor(r, 1, 64);
+                    r |= __shfl_xor(r, 2, 64);
+                    rec[c] = r;
+                }
+                if (tq == 0 && any) {
+                    uint32_t* dst = vt + (quad * 16 + G8) * vb;
+                    for (int c = 0; c < vb; ++c) dst[c] = rmw ? (dst[c] | rec[c]) : rec[c];
+                }
+            }
+        }
+    }
+}
+
+// Copy rows into the fp16 ring (slot = position % n_recent).
+__global__ __launch_bounds__(128) void k_ring(const RingArgs a) {
+    const int h = blockIdx.y, b = blockIdx.z, j = threadIdx.x;
+    const int64_t pos = a.pos_lo[b] + blockIdx.x;
+    if (pos >= a.pos_hi[b]) return;
+    const int64_t row = pos - a.off[b];
+    const int64_t src = (int64_t)b * a.sB + row * a.sT + (int64_t)h * a.sH + j;
+    const size_t dst = (((size_t)b * a.Hkv + h) * a.n_recent + (size_t)(pos % a.n_recent)) * D + j;
+    a.ring_k[dst] = f2h(load_act(a.k, src, a.dtype));
+    a.ring_v[dst] = f2h(load_act(a.v, src, a.dtype));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// Launchers
+hipError_t launch_prep(const PrepArgs& a, int B, hipStream_t s) {
+    hipLaunchKernelGGL(k_prep, dim3(a.Hkv, B), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s) {
+    hipLaunchKernelGGL(k_combine, dim3(rows), dim3(D), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_energy(const EnergyArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(k_energy, dim3(a.Hkv), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_t s) {
+    if (max_tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_quant, dim3((unsigned)max_tiles, a.Hkv, B), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t s) {
+    if (max_rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_ring, dim3((unsigned)max_rows, a.Hkv, B), dim3(D), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_fp16_g(const Fp16Args& a, int B, hipStream_t s) {
+    hipLaunchKernelGGL(k_decode_fp16<G>, dim3(a.n_splits, a.Hkv, B), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t s) {
+    switch (a.G) {
+        case 1: return launch_fp16_g<1>(a, B, s);
+        case 2: return launch_fp16_g<2>(a, B, s);
+        case 4: return launch_fp16_g<4>(a, B, s);
+        case 8: return launch_fp16_g<8>(a, B, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int G, int R, int VB, int KG>
+static hipError_t launch_dec(const DecodeArgs& a, int B, hipStream_t s) {
+    hipLaunchKernelGGL((k_decode<G, R, VB, KG>), dim3(a.n_parts, a.Hkv, B), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int G, int VB>
+static hipError_t launch_dec_gv(const DecodeArgs& a, int B, int k_mode, int R, hipStream_t s) {
+    if (k_mode == BGTQ_K_AFFINE) {
+        switch (a.k_group) {
+            case 32: return launch_dec<G, 16, VB, 32>(a, B, s);
+            case 64: return launch_dec<G, 16, VB, 64>(a, B, s);
+            case 128: return launch_dec<G, 16, VB, 128>(a, B, s);
+        }
+        return hipErrorInvalidValue;
+    }
+    switch (R) {
+        case 8: return launch_dec<G, 8, VB, 0>(a, B, s);
+        case 12: return launch_dec<G, 12, VB, 0>(a, B, s);
+        case 16: return launch_dec<G, 16, VB, 0>(a, B, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int G>
+static hipError_t launch_dec_g(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t s) {
+    switch (v_bits) {
+        case 2: return launch_dec_gv<G, 2>(a, B, k_mode, R, s);
+        case 3: return launch_dec_gv<G, 3>(a, B, k_mode, R, s);
+        case 4: return launch_dec_gv<G, 4>(a, B, k_mode, R, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t s) {
+    switch (a.G) {
+        case 1: return launch_dec_g<1>(a, B, k_mode, R, v_bits, s);
+        case 2: return launch_dec_g<2>(a, B, k_mode, R, v_bits, s);
+        case 4: return launch_dec_g<4>(a, B, k_mode, R, v_bits, s);
+        case 8: return launch_dec_g<8>(a, B, k_mode, R, v_bits, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+bool decode_supported(int k_mode, int R, int k_bits, int k_group, int v_bits, int G) {
+    if (!(G == 1 || G == 2 || G == 4 || G == 8)) return false;
+    if (v_bits < 2 || v_bits > 4) return false;
+    if (k_mode == BGTQ_K_AFFINE) return k_bits == 4 && (k_group == 32 || k_group == 64 || k_group == 128);
+    return R == 8 || R == 12 || R == 16;
+}
+
+}  // namespace bgtq

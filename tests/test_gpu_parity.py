@@ -1,0 +1,153 @@
+"""GPU parity: HIP library vs the CPU oracle on the same seeded inputs (through the C ABI).
+
+Bit-exact: packed code bytes and fp16 scales (and the fp16 ring).  Outputs: |gpu - ref| <=
+2e-3 + 1e-3*|ref| elementwise, ref = float64 oracle attention over the oracle's own cache.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import pipeline
+from tests import _parity as T
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import packed_cache_decode_block_amd as P  # noqa: E402
+
+
+def _compare_cache(cache, oc, w, layer=0, L=1):
+    B, H = w.B, w.Hkv
+    kc = T.layer_view(cache.k_codes, L, layer, oc.k_codes.shape).cpu().numpy()
+    vc = T.layer_view(cache.v_codes, L, layer, oc.v_codes.shape).cpu().numpy()
+    ks = T.layer_view(cache.k_scale, L, layer, oc.k_scale.shape).cpu().numpy()
+    vs = T.layer_view(cache.v_scale, L, layer, oc.v_scale.shape).cpu().numpy()
+    np.testing.assert_array_equal(ks.view(np.uint16), oc.k_scale.view(np.uint16), "k scales")
+    np.testing.assert_array_equal(vs.view(np.uint16), oc.v_scale.view(np.uint16), "v scales")
+    np.testing.assert_array_equal(kc, oc.k_codes, "k codes")
+    np.testing.assert_array_equal(vc, oc.v_codes, "v codes")
+    if oc.k_zero is not None:
+        kz = T.layer_view(cache.k_zero, L, layer, oc.k_zero.shape).cpu().numpy()
+        np.testing.assert_array_equal(kz.view(np.uint16), oc.k_zero.view(np.uint16), "k zeros")
+    if oc.v_zero is not None:
+        vz = T.layer_view(cache.v_zero, L, layer, oc.v_zero.shape).cpu().numpy()
+        np.testing.assert_array_equal(vz.view(np.uint16), oc.v_zero.view(np.uint16), "v zeros")
+    if oc.recent_k is not None:
+        rk = T.layer_view(cache.recent_k, L, layer, oc.recent_k.shape).cpu().numpy()
+        rv = T.layer_view(cache.recent_v, L, layer, oc.recent_v.shape).cpu().numpy()
+        np.testing.assert_array_equal(rk.view(np.uint16), oc.recent_k.view(np.uint16), "recent k")
+        np.testing.assert_array_equal(rv.view(np.uint16), oc.recent_v.view(np.uint16), "recent v")
+
+
+CASES = {
+    # name: (workload id, overrides, N, chunks)
+    "w1_full": (1, {}, 4096, (None,)),
+    "w1_ragged_chunks": (1, {}, 1000, (1, 2, 61, 64, 129, None)),
+    "w2_reduced": (2, {"L": 1}, 4096 + 37, (None,)),
+    "w3_reduced": (3, {"L": 1, "B": 2}, 2048 + 5, (777, None)),
+    "w4_reduced": (4, {"L": 1, "B": 2}, 2048 + 13, (None,)),
+    "w5_reduced": (5, {}, 3000, (1000, 7, None)),
+    "w5_all_recent": (5, {}, 200, (None,)),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_quantize_and_decode(name):
+    wid, ov, N, chunks = CASES[name]
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
+    print(f"[case {name}] N={N} B={w.B} Hq={w.Hq} Hkv={w.Hkv}", flush=True)
+    n_cap = ((N + 63) // 64 + 1) * 64
+    m = T.meta(w, 0)
+    K, V, q = T.inputs(w, 0, N)
+    oc = T.oracle_layer(w, K, V, m, n_cap)
+    cache = T.gpu_cache(w, n_cap)
+    if m is not None:
+        cache.set_metadata(0, m.bits, m.sigma, m.r)
+    T.append_all(cache, 0, K, V, w.dtype, chunks)
+    _compare_cache(cache, oc, w)
+    ref = pipeline.decode_layer(oc, q)
+    qd = T.to_dev(q, w.dtype)
+    for ns in (0, 1, 3):
+        out = cache.decode_attention(0, qd, n_splits=ns)
+        torch.cuda.synchronize()
+        e = T.assert_close(out.cpu().numpy(), ref, f"{name} splits={ns}")
+        print(f"  splits={ns}: max abs err {e:.2e}", flush=True)
+
+
+def test_decode_deterministic_and_split_invariant():
+    w = synth.reduced(synth.WORKLOADS[2], L=1)
+    N = 5000
+    m = T.meta(w, 0)
+    K, V, q = T.inputs(w, 0, N)
+    cache = T.gpu_cache(w, 5120)
+    cache.set_metadata(0, m.bits, m.sigma, m.r)
+    T.append_all(cache, 0, K, V, w.dtype)
+    qd = T.to_dev(q, w.dtype)
+    a = cache.decode_attention(0, qd, n_splits=7).cpu().numpy()
+    b = cache.decode_attention(0, qd, n_splits=7).cpu().numpy()
+    np.testing.assert_array_equal(a, b)
+    c = cache.decode_attention(0, qd, n_splits=2).cpu().numpy()
+    assert np.max(np.abs(a - c)) < 1e-4
+
+
+def test_ragged_sequence_lengths():
+    """Sequences of one batch with different lengths (host n_tokens per sequence)."""
+    w = synth.reduced(synth.WORKLOADS[3], L=1, B=3)
+    N = 700
+    m = T.meta(w, 0)
+    K, V, q = T.inputs(w, 0, N)
+    cache = T.gpu_cache(w, 768)
+    cache.set_metadata(0, m.bits, m.sigma, m.r)
+    T.append_all(cache, 0, K, V, w.dtype)
+    lens = [700, 1, 333]
+    cache.n_tokens[0, :] = lens
+    out = cache.decode_attention(0, T.to_dev(q, w.dtype), n_splits=2).cpu().numpy()
+    for b, n in enumerate(lens):
+        wb = synth.reduced(w, B=1)
+        oc = T.oracle_layer(wb, K[b:b + 1, :, :n], V[b:b + 1, :, :n], m, 768)
+        ref = pipeline.decode_layer(oc, q[b:b + 1])
+        T.assert_close(out[b:b + 1], ref, f"ragged b={b} n={n}")
+
+
+def test_errors_on_device_paths():
+    w = synth.reduced(synth.WORKLOADS[1], N=64)
+    cache = T.gpu_cache(w, 64)
+    q = torch.zeros((1, 1, 128), device="cuda")
+    with pytest.raises(P.BgtqError) as e:
+        cache.decode_attention(0, q, n_splits=1)                  # empty context
+    assert e.value.code == P.E_INVALID
+    k = torch.zeros((1, 65, 1, 128), device="cuda")
+    with pytest.raises(P.BgtqError) as e:
+        cache.quantize_append(0, k, k)                             # capacity
+    assert e.value.code == P.E_CAPACITY
+    assert cache.n_tokens[0, 0] == 0
+
+
+def test_fp16_baseline_decode():
+    w = synth.reduced(synth.WORKLOADS[2], L=1, B=2)
+    N = 3000
+    K, V, q = T.inputs(w, 0, N)
+    k16 = K.astype(np.float16)
+    v16 = V.astype(np.float16)
+    ref = pipeline.fp16_decode(k16, v16, q)
+    out = P.bgtq_fp16_decode_attention(torch.from_numpy(k16).cuda(), torch.from_numpy(v16).cuda(),
+                                       T.to_dev(q, w.dtype), n_splits=5)
+    T.assert_close(out.cpu().numpy(), ref, "fp16 baseline")
+
+
+@pytest.mark.parametrize("wid", [1, 3])
+def test_block_energy(wid):
+    from oracle import energy
+    w = synth.WORKLOADS[wid]
+    cal = [synth.calibration(w, 0, h) for h in range(w.Hkv)]
+    kc = np.stack([c[0] for c in cal], axis=1)                    # [T, Hkv, d]
+    qc = np.concatenate([np.transpose(c[1], (1, 0, 2)) for c in cal], axis=1)  # [T, Hq, d]
+    sc, sg, rs = P.bgtq_block_energy(T.to_dev(kc, w.dtype), T.to_dev(qc, w.dtype))
+    for h in range(w.Hkv):
+        ek, eq = energy.block_energy(cal[h][0], cal[h][1])
+        np.testing.assert_allclose(sc[h], energy.scores(ek, eq), rtol=1e-12)
+        s_o, r_o = energy.sigma_hat(ek)
+        assert np.max(np.abs(sg[h].astype(np.float64) / s_o - 1)) <= 2 ** -23

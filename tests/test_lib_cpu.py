@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI that need no GPU: exports, tables, allocator, sizes, validation."""
+import ctypes as C
+import re
+import os
+
+import numpy as np
+import pytest
+
+import packed_cache_decode_block_amd as P
+from packed_cache_decode_block_amd import _lib
+from oracle import allocate as oalloc
+from oracle import codebook as ocb
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "bgtq.h")
+
+
+def test_exports_every_declared_symbol():
+    decl = set(re.findall(r"\b(bgtq_[a-z0-9_]+)\s*\(", open(HEADER).read()))
+    assert decl == set(P.SYMBOLS)
+    for name in decl:
+        assert hasattr(P.lib, name)
+    assert P.bgtq_version().startswith("bgtq")
+
+
+@pytest.mark.parametrize("b", range(1, 9))
+def test_codebook_tables_match_oracle(b):
+    c16, thr = P.bgtq_codebook(b)
+    oc, ot = ocb.codebook(b)
+    np.testing.assert_array_equal(c16.view(np.uint16), oc.view(np.uint16))
+    np.testing.assert_array_equal(thr.view(np.uint32), ot.view(np.uint32))
+
+
+def test_codebook_rejects_bad_width():
+    with pytest.raises(P.BgtqError) as e:
+        P.bgtq_codebook(9)
+    assert e.value.code == P.E_INVALID
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_allocate_bit_exact_vs_oracle(seed):
+    rng = np.random.default_rng(seed)
+    n_heads = int(rng.integers(1, 5))
+    s = np.exp(rng.uniform(-12, 12, (n_heads, 64)))
+    if seed % 3 == 0:
+        s[:, rng.integers(0, 64, 10)] = 0.0                      # dead blocks
+    if seed % 4 == 0:
+        s = np.round(s, 0) + 1.0                                 # ties
+    U = int(rng.choice([64, 128, 192, 256]))
+    got = P.bgtq_allocate(s, U)
+    for h in range(n_heads):
+        np.testing.assert_array_equal(got[h], oalloc.greedy(s[h], U, 8).astype(np.uint8))
+
+
+def test_allocate_b_min_and_errors():
+    s = np.array([[1.0, 2.0, 0.0, 4.0]])
+    got = P.bgtq_allocate(s, 9, b_min=2, b_max=4)
+    np.testing.assert_array_equal(got[0], oalloc.greedy(s[0], 9, 4, b_min=2))
+    with pytest.raises(P.BgtqError) as e:
+        P.bgtq_allocate(s, 13, b_max=4)                          # 3 live blocks x 4 bits = 12 < 13
+    assert e.value.code == P.E_BUDGET
+    with pytest.raises(P.BgtqError) as e:
+        P.bgtq_allocate(np.array([[1.0, -1.0]]), 2)
+    assert e.value.code == P.E_INVALID
+    with pytest.raises(P.BgtqError) as e:
+        P.bgtq_allocate(np.array([[1.0, np.nan]]), 2)
+    assert e.value.code == P.E_INVALID
+    with pytest.raises(P.BgtqError):
+        P.bgtq_allocate(s, 4, b_max=9)
+
+
+def _desc(**kw):
+    d = _lib.CacheDesc()
+    base = dict(L=2, B=3, Hq=16, Hkv=2, d=128, n_cap=4096, k_mode=0, budget_units=192, k_bits=4, k_group=32,
+                v_mode=0, v_bits=3, n_recent=0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_cache_bytes_geometry():
+    d = _desc()
+    nb = lambda w: P.lib.bgtq_cache_bytes(C.byref(d), w)
+    assert nb(_lib.BUF_K_CODES) == 2 * 3 * 2 * 4096 * 48          # 48 B per token (K3)
+    assert nb(_lib.BUF_V_CODES) == 2 * 3 * 2 * 4096 * 48          # 3 bits x 128
+    assert nb(_lib.BUF_K_SCALE) == 2 * 3 * 2 * 4096 * 2
+    assert nb(_lib.BUF_K_ZERO) == 0
+    d = _desc(k_mode=1, k_bits=4, k_group=32, v_mode=1, v_bits=2, n_recent=256)
+    assert nb(_lib.BUF_K_CODES) == 2 * 3 * 2 * 4096 * 64
+    assert nb(_lib.BUF_K_SCALE) == 2 * 3 * 2 * 4096 * 4 * 2
+    assert nb(_lib.BUF_K_ZERO) == nb(_lib.BUF_K_SCALE)
+    assert nb(_lib.BUF_V_ZERO) == 2 * 3 * 2 * 4096 * 2
+    assert nb(_lib.BUF_RECENT_K) == 2 * 3 * 2 * 256 * 128 * 2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), P.E_UNSUPPORTED), (dict(Hq=15), P.E_INVALID), (dict(Hq=32, Hkv=2), P.E_UNSUPPORTED),
+    (dict(n_cap=100), P.E_INVALID), (dict(budget_units=100), P.E_INVALID), (dict(v_bits=5), P.E_INVALID),
+    (dict(k_mode=1, k_bits=3), P.E_INVALID), (dict(k_mode=1, k_group=48), P.E_INVALID), (dict(B=65), P.E_UNSUPPORTED),
+    (dict(k_mode=7), P.E_INVALID), (dict(n_recent=-1), P.E_INVALID)])
+def test_descriptor_validation(kw, code):
+    d = _desc(**kw)
+    assert P.lib.bgtq_cache_bytes(C.byref(d), _lib.BUF_K_CODES) == code
+    assert P.lib.bgtq_last_error()
+
+
+def test_append_and_decode_validate_before_launch():
+    """Invalid calls return an error without touching the device (NULL device pointers are never used)."""
+    d = _desc()
+    nt = np.zeros((2, 3), np.int64)
+    d.n_tokens = nt.ctypes.data_as(C.POINTER(C.c_int64))
+    fake = C.c_void_p(0x1000)
+    # NULL cache buffers
+    assert P.lib.bgtq_quantize_append(C.byref(d), 0, fake, fake, 2, 10, None, None) == P.E_INVALID
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma"):
+        setattr(d, name, 0x1000)
+    assert P.lib.bgtq_quantize_append(C.byref(d), 5, fake, fake, 2, 10, None, None) == P.E_INVALID  # layer
+    assert P.lib.bgtq_quantize_append(C.byref(d), 0, fake, fake, 9, 10, None, None) == P.E_INVALID  # dtype
+    assert P.lib.bgtq_quantize_append(C.byref(d), 0, fake, fake, 2, 5000, None, None) == P.E_CAPACITY
+    assert (nt == 0).all()                                        # no side effect on failure
+    out = C.c_void_p(0x2000)
+    ws = C.c_void_p(0x10000)
+    # empty context
+    assert P.lib.bgtq_decode_attention(C.byref(d), 0, fake, 2, out, ws, 1 << 30, 4, None) == P.E_INVALID
+    nt[0] = 100
+    # misaligned / too small workspace
+    assert P.lib.bgtq_decode_attention(C.byref(d), 0, fake, 2, out, C.c_void_p(0x10010), 1 << 30, 4, None) == P.E_INVALID
+    assert P.lib.bgtq_decode_attention(C.byref(d), 0, fake, 2, out, ws, 16, 4, None) == P.E_INVALID
+    # unsupported decode format (budget 208 -> 13-dword records has no kernel)
+    d2 = _desc(budget_units=208)
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma"):
+        setattr(d2, name, 0x1000)
+    d2.n_tokens = nt.ctypes.data_as(C.POINTER(C.c_int64))
+    assert P.lib.bgtq_decode_attention(C.byref(d2), 0, fake, 2, out, ws, 1 << 30, 4, None) == P.E_UNSUPPORTED
+
+
+def test_energy_and_fp16_validation():
+    fake = C.c_void_p(0x1000)
+    nul = None
+    assert P.lib.bgtq_block_energy(nul, fake, 2, 10, 2, 8, 128, 0, None, None, None, fake, 4096, None) == P.E_INVALID
+    assert P.lib.bgtq_block_energy(fake, fake, 2, 10, 2, 8, 64, 0, None, None, None, fake, 4096, None) == P.E_UNSUPPORTED
+    assert P.lib.bgtq_block_energy(fake, fake, 2, 10, 2, 8, 128, 0, None, None, None, fake, 16, None) == P.E_INVALID
+    assert P.lib.bgtq_fp16_decode_attention(fake, fake, 100, 1, 16, 2, 128, fake, 2, fake, C.c_void_p(0x10000), 16, 4,
+                                            None) == P.E_INVALID
+    assert P.lib.bgtq_fp16_decode_attention(fake, fake, 100, 1, 48, 2, 128, fake, 2, fake, C.c_void_p(0x10000),
+                                            1 << 30, 4, None) == P.E_UNSUPPORTED
