@@ -1,0 +1,275 @@
+#!/usr/bin/env python
+"""Bench: packed-KV decode attention on one MI355X.
+
+One step = decode attention for every layer of the workload (prep + split-K decode + combine per
+layer, through the C ABI) with the packed cache, queries and outputs resident in HBM.  Prints one
+JSON line: effective HBM GB/s over algorithmic bytes (codes, scales/zeros, fp16 recent tokens, q,
+out), the decode kernel's roofline (HIP events around every decode-kernel launch in the timed
+region), the unquantized fp16 comparator, and the CPU oracle timed on a bounded sample.
+
+Default workload: Qwen2.5-3B-shaped decode, 36 layers, 16 query / 2 KV heads, 131072 tokens,
+batch 1, Block-GTQ K3 keys and 3-bit values, bf16 activations (synthetic inputs).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed-KV decode attention: effective HBM GB/s (% of peak) at 128K ctx"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bytes_per_token_head(w) -> float:
+    """Algorithmic bytes one packed (token, kv head) costs: codes + scales (+ zeros)."""
+    if w.k_mode == "gtq":
+        k = 2 * w.k_budget_units / 8 + 2
+    else:
+        k = w.k_bits * w.d / 8 + (w.d // w.k_group) * 4
+    v = w.v_bits * w.d / 8 + (2 if w.v_mode == "codebook" else 4)
+    return k + v
+
+
+def layer_bytes(w, N: int) -> float:
+    n_rec = min(N, w.n_recent)
+    act = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    return (w.B * w.Hkv * ((N - n_rec) * bytes_per_token_head(w) + n_rec * 2 * w.d * 2)
+            + w.B * w.Hq * w.d * (act + 4))
+
+
+def build_packed(w, device="cuda"):
+    import torch
+
+    import packed_cache_decode_block_amd as P
+    import synth
+    from synth import gpu as sg
+
+    n_cap = (w.N - min(w.N, w.n_recent) + 63) // 64 * 64
+    cache = P.PackedCache(L=w.L, B=w.B, Hq=w.Hq, Hkv=w.Hkv, n_cap=n_cap,
+                          k_mode=P.K_BLOCKGTQ if w.k_mode == "gtq" else P.K_AFFINE,
+                          budget_units=w.k_budget_units or 128, k_bits=w.k_bits or 4, k_group=w.k_group or 32,
+                          v_mode=P.V_CODEBOOK if w.v_mode == "codebook" else P.V_AFFINE, v_bits=w.v_bits,
+                          n_recent=w.n_recent, zero=False)
+    td = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    qs = []
+    for layer in range(w.L):
+        if w.k_mode == "gtq":
+            cal = [synth.calibration(w, layer, h) for h in range(w.Hkv)]
+            kc = torch.from_numpy(np.ascontiguousarray(np.stack([c[0] for c in cal], axis=1))).to(device).to(td)
+            qc = torch.from_numpy(np.ascontiguousarray(
+                np.concatenate([np.transpose(c[1], (1, 0, 2)) for c in cal], axis=1))).to(device).to(td)
+            scores, sigma, inv_sigma = P.bgtq_block_energy(kc, qc)
+            bits = P.bgtq_allocate(scores, w.k_budget_units)
+            cache.set_metadata(layer, bits, sigma, inv_sigma)
+        for b in range(w.B):
+            k = torch.stack([sg.keys(w, layer, h, b, w.N, device) for h in range(w.Hkv)], dim=1)[None]
+            v = torch.stack([sg.values(w, layer, h, b, w.N, device) for h in range(w.Hkv)], dim=1)[None]
+            if b == 0:
+                kk, vv = k, v
+            else:
+                kk, vv = torch.cat([kk, k]), torch.cat([vv, v])
+        cache.quantize_append(layer, kk, vv)
+        del kk, vv
+        q = torch.stack([torch.cat([sg.queries(w, layer, h, b, w.N, device) for h in range(w.Hkv)])
+                         for b in range(w.B)])
+        qs.append(q)
+    torch.cuda.synchronize()
+    return cache, qs
+
+
+def build_fp16(w, device="cuda"):
+    """Unquantized comparator cache: the same synthetic rows in fp16, [B, Hkv, N, 128] per layer."""
+    import torch
+
+    from synth import gpu as sg
+    ks, vs = [], []
+    for layer in range(w.L):
+        ks.append(torch.stack([torch.stack([sg.keys(w, layer, h, b, w.N, device) for h in range(w.Hkv)])
+                               for b in range(w.B)]).to(torch.float16))
+        vs.append(torch.stack([torch.stack([sg.values(w, layer, h, b, w.N, device) for h in range(w.Hkv)])
+                               for b in range(w.B)]).to(torch.float16))
+    torch.cuda.synchronize()
+    return ks, vs
+
+
+def timed(run_step, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        run_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run_step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The oracle (numpy, fp64) decoding a bounded sample: layer 0, the first N_s tokens of every
+    (batch, kv head) of the first sequence, all query heads; repeated until ~budget_s seconds."""
+    import synth
+    from oracle import pipeline
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing
+        blas = 1
+    Ns = min(w.N, 16384)
+    ws = synth.reduced(w, B=1, L=1, N=Ns, n_recent=min(w.n_recent, Ns // 2))
+    m = None
+    if ws.k_mode == "gtq":
+        cal = [synth.calibration(ws, 0, h) for h in range(ws.Hkv)]
+        m = pipeline.calibrate([c[0] for c in cal], [c[1] for c in cal], ws.k_budget_units)
+    K = np.stack([synth.keys(ws, 0, h, 0, Ns) for h in range(ws.Hkv)])[None]
+    V = np.stack([synth.values(ws, 0, h, 0, Ns) for h in range(ws.Hkv)])[None]
+    q = np.concatenate([synth.queries(ws, 0, h, 0, Ns) for h in range(ws.Hkv)])[None]
+    oc = pipeline.build_layer(K, V, k_mode=ws.k_mode, v_mode=ws.v_mode, v_bits=ws.v_bits,
+                              n_cap=(Ns + 63) // 64 * 64, meta=m, k_bits=ws.k_bits or 4, k_group=ws.k_group or 32,
+                              n_recent=ws.n_recent)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        pipeline.decode_layer(oc, q)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    gbs = reps * layer_bytes(ws, Ns) / el / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+            "blas_threads": blas, "kind": "oracle", "seconds": round(el, 2),
+            "sample": f"layer 0 of 1, batch 1 of {w.B}, {Ns} of {w.N} tokens per kv head"
+                      f" ({ws.n_recent} in the fp16 ring), all {w.Hq} query heads, {reps} decode repetitions"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (see synth.WORKLOADS); 2 = headline")
+    ap.add_argument("--n-splits", type=int, default=0, help="0 = the library's choice")
+    ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 comparator")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
+    ap.add_argument("--eager", action="store_true", help="time eager launches only (no HIP graph replay)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU part "
+              "in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import packed_cache_decode_block_amd as P
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if args.layers:
+        w = synth.reduced(w, L=args.layers)
+    log(f"[bench] workload {w.wid}: {w.name}")
+    t0 = time.perf_counter()
+    cache, qs = build_packed(w)
+    log(f"[bench] packed cache built in {time.perf_counter() - t0:.1f}s")
+    outs = [torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda") for _ in range(w.L)]
+    ws = cache.workspace(args.n_splits)
+
+    def step():
+        for layer in range(w.L):
+            cache.decode_attention(layer, qs[layer], outs[layer], n_splits=args.n_splits, ws=ws)
+
+    P.bgtq_profile_enable(w.L * (args.steps + 1))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    P.bgtq_profile_read(P.PROF_DECODE)                     # drop warm-up records
+    sec = timed(step, args.steps, 0)
+    n_k, tot_ms, min_ms, max_ms = P.bgtq_profile_read(P.PROF_DECODE)
+    P.bgtq_profile_enable(0)
+    kern_ms = tot_ms / max(n_k, 1)
+    sec_eager = sec
+    # Replay the whole step (every layer's prep + decode + combine) from a HIP graph: no host launch
+    # overhead between the 3*L kernels.  Falls back to eager timing if capture fails.
+    graph_ok = False
+    if not args.eager:
+        try:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            with torch.cuda.graph(g):
+                step()
+            sec = timed(g.replay, args.steps, args.warmup)
+            graph_ok = True
+        except Exception as e:  # capture unsupported: keep the eager number
+            log(f"[bench] graph capture failed ({e}); reporting eager launches")
+    lb = layer_bytes(w, w.N)
+    value = w.L * lb / sec / 1e9
+    achieved = lb / (kern_ms * 1e-3) / 1e9
+    log(f"[bench] step {sec * 1e3:.3f} ms ({'graph' if graph_ok else 'eager'}; eager {sec_eager * 1e3:.3f} ms) "
+        f"({w.L} layers), decode kernel avg {kern_ms * 1e3:.2f} us "
+        f"(min {min_ms * 1e3:.2f}, max {max_ms * 1e3:.2f}, n={n_k}) -> {achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.L, "batch": w.B, "context": w.N, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.d, "k_format": "blockgtq" if w.k_mode == "gtq" else "affine",
+                   "k_bits_per_dim": (w.k_budget_units / 64) if w.k_mode == "gtq" else w.k_bits,
+                   "v_bits": w.v_bits, "n_recent_fp16": w.n_recent, "activations": w.dtype,
+                   "n_splits": args.n_splits or "auto"},
+        "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "launch": "hipgraph" if graph_ok else "eager", "ms_per_step_eager": round(sec_eager * 1e3, 4),
+        "tokens_heads_per_s": round(w.B * w.N * w.Hq * w.L / sec, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "k_decode (split-K packed decode)", "kernel_avg_us": round(kern_ms * 1e3, 3),
+                     "bytes_per_launch": lb, "launches_timed": n_k},
+    }
+    del ws
+    if not args.no_fp16:
+        del cache
+        torch.cuda.empty_cache()
+        ks, vs = build_fp16(w)
+        ws16 = torch.empty(P.lib.bgtq_fp16_decode_workspace_bytes(w.N, w.B, w.Hq, w.Hkv, args.n_splits),
+                           dtype=torch.uint8, device="cuda")
+
+        def step16():
+            for layer in range(w.L):
+                P.bgtq_fp16_decode_attention(ks[layer], vs[layer], qs[layer], outs[layer], args.n_splits, ws16)
+
+        P.bgtq_profile_enable(w.L * (args.steps + 1))
+        for _ in range(args.warmup):
+            step16()
+        torch.cuda.synchronize()
+        P.bgtq_profile_read(P.PROF_FP16_DECODE)
+        sec16 = timed(step16, args.steps, 0)
+        n16, tot16, _, _ = P.bgtq_profile_read(P.PROF_FP16_DECODE)
+        P.bgtq_profile_enable(0)
+        b16 = w.B * w.Hkv * w.N * 512 + w.B * w.Hq * w.d * 6
+        result["fp16_baseline"] = {
+            "ms_per_step": round(sec16 * 1e3, 4), "value": round(w.L * b16 / sec16 / 1e9, 2), "unit": "GB/s",
+            "kernel_avg_us": round(tot16 / max(n16, 1) * 1e3, 3),
+            "speedup_packed_vs_fp16": round(sec16 / sec, 3)}
+        log(f"[bench] fp16 comparator step {sec16 * 1e3:.3f} ms, speedup {sec16 / sec:.2f}x")
+        del ks, vs
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -203,6 +203,18 @@ int bgtq_fp16_decode_attention(const void *k16, const void *v16, int64_t N, int 
                                int Hkv, int d, const void *q, int dtype, float *out, void *ws,
                                size_t ws_bytes, int n_splits, void *stream);
 
+/*
+ * Kernel tracing (host).  While enabled, every launch of a main kernel (packed decode, fp16
+ * decode, quantize-append) is bracketed by a pair of HIP events recorded on its stream, up to
+ * `max_launches` launches; bgtq_profile_enable(0) disables and releases the events.
+ * bgtq_profile_read waits for the recorded events of one kind (BGTQ_PROF_*), returns their
+ * count and the total / min / max duration in milliseconds (any output may be NULL), and clears
+ * that kind's records.  Not thread-safe against concurrent decode calls on other threads.
+ */
+enum { BGTQ_PROF_DECODE = 0, BGTQ_PROF_FP16_DECODE = 1, BGTQ_PROF_QUANTIZE = 2 };
+int bgtq_profile_enable(int max_launches);
+int bgtq_profile_read(int kind, int *n_launches, double *total_ms, double *min_ms, double *max_ms);
+
 #ifdef __cplusplus
 }
 #endif

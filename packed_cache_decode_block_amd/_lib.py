@@ -18,7 +18,9 @@ MAX_BATCH = 64
 
 SYMBOLS = ["bgtq_last_error", "bgtq_version", "bgtq_codebook", "bgtq_allocate", "bgtq_block_energy",
            "bgtq_cache_bytes", "bgtq_quantize_append", "bgtq_decode_workspace_bytes", "bgtq_decode_attention",
-           "bgtq_fp16_decode_workspace_bytes", "bgtq_fp16_decode_attention"]
+           "bgtq_fp16_decode_workspace_bytes", "bgtq_fp16_decode_attention", "bgtq_profile_enable",
+           "bgtq_profile_read"]
+PROF_DECODE, PROF_FP16_DECODE, PROF_QUANTIZE = 0, 1, 2
 
 
 class BgtqError(RuntimeError):
@@ -38,11 +40,9 @@ class CacheDesc(C.Structure):
                 ("n_tokens", C.POINTER(C.c_int64))]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                          "(python packed_cache_decode_block_amd/build_lib.py)")
-    lib = C.CDLL(LIB_PATH)
+def bind(path: str):
+    """Load a library exporting the C ABI of include/bgtq.h and declare its prototypes."""
+    lib = C.CDLL(path)
     P, I, I64, SZ, D = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.POINTER(C.c_double)
     F = C.POINTER(C.c_float)
     sig = {
@@ -57,11 +57,20 @@ def _load():
         "bgtq_decode_attention": (I, [C.POINTER(CacheDesc), I, P, I, P, P, SZ, I, P]),
         "bgtq_fp16_decode_workspace_bytes": (I64, [I64, I, I, I, I]),
         "bgtq_fp16_decode_attention": (I, [P, P, I64, I, I, I, I, P, I, P, P, SZ, I, P]),
+        "bgtq_profile_enable": (I, [I]),
+        "bgtq_profile_read": (I, [I, C.POINTER(C.c_int), D, D, D]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = res, args
     return lib
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(python packed_cache_decode_block_amd/build_lib.py)")
+    return bind(LIB_PATH)
 
 
 lib = _load()

@@ -178,3 +178,16 @@ def bgtq_fp16_decode_attention(k16, v16, q, out=None, n_splits: int = 0, ws=None
     check(lib.bgtq_fp16_decode_attention(_ptr(k16), _ptr(v16), N, B, Hq, Hkv, d, _ptr(q), _dtype_code(q), _ptr(out),
                                          _ptr(ws), ws.numel(), n_splits, _stream(stream)))
     return out
+
+
+def bgtq_profile_enable(max_launches: int) -> None:
+    """Bracket up to max_launches main-kernel launches with HIP events (0 disables)."""
+    check(lib.bgtq_profile_enable(max_launches))
+
+
+def bgtq_profile_read(kind: int):
+    """(count, total_ms, min_ms, max_ms) of the recorded launches of one kind; clears them."""
+    n = C.c_int(0)
+    tot, mn, mx = C.c_double(0), C.c_double(0), C.c_double(0)
+    check(lib.bgtq_profile_read(kind, C.byref(n), C.byref(tot), C.byref(mn), C.byref(mx)))
+    return n.value, tot.value, mn.value, mx.value

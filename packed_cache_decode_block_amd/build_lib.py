@@ -55,5 +55,28 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+MOCK = os.path.join(BUILD, "libbgtq_mock.so")
+
+
+def build_mock() -> str:
+    """Host C ABI linked against mock launchers (test-only; checks kernel arguments without a GPU)."""
+    os.makedirs(BUILD, exist_ok=True)
+    gen_dir = os.path.join(CSRC, "generated")
+    os.makedirs(gen_dir, exist_ok=True)
+    gen_exe = os.path.join(BUILD, "gen_codebook")
+    _run(["g++", "-O2", "-std=c++17", "-o", gen_exe, os.path.join(CSRC, "gen_codebook.cpp")])
+    _run([gen_exe, os.path.join(gen_dir, "bgtq_codebook_data.h")])
+    flags = ["-O1", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]
+    objs = []
+    for u in ("bgtq_host.cpp", "mock_launch.cpp"):
+        obj = os.path.join(BUILD, "mock_" + u + ".o")
+        _run(["g++", *flags, "-c", os.path.join(CSRC, u), "-o", obj])
+        objs.append(obj)
+    tmp = MOCK + ".tmp"
+    _run(["g++", "-shared", "-o", tmp, *objs, "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"])
+    os.replace(tmp, MOCK)
+    return MOCK
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

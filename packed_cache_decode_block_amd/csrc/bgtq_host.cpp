@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -52,6 +53,7 @@ int geometry(const bgtq_cache* c, bgtq::Geometry& g) {
     const int G = c->Hq / c->Hkv;
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return fail(BGTQ_E_UNSUPPORTED, "group size %d unsupported", G);
     if (c->n_cap < TILE || c->n_cap % TILE) return fail(BGTQ_E_INVALID, "n_cap must be a positive multiple of 64");
+    if (c->n_cap > INT32_MAX) return fail(BGTQ_E_UNSUPPORTED, "n_cap exceeds 2^31 - 1");
     if (c->n_recent < 0) return fail(BGTQ_E_INVALID, "n_recent < 0");
     g.B = c->B; g.Hq = c->Hq; g.Hkv = c->Hkv; g.G = G;
     g.n_cap = c->n_cap;
@@ -88,10 +90,6 @@ int geometry(const bgtq_cache* c, bgtq::Geometry& g) {
     return BGTQ_OK;
 }
 
-int64_t prep_bytes(const bgtq::Geometry& g) {
-    return (int64_t)g.B * g.Hkv * bgtq::prep_layout(g.G).stride * 4;
-}
-
 int default_splits(int64_t max_tiles, int bh, int n_cu) {
     // Enough workgroups to cover every CU about twice, with at least 8 tiles (2 per wave) each.
     int64_t target = (int64_t)2 * n_cu;
@@ -115,11 +113,88 @@ int cu_count() {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Event pairs around main-kernel launches (tracing aid, see bgtq_profile_enable).
+struct Profiler {
+    int cap = 0;
+    std::vector<hipEvent_t> ev;   // 2 per record
+    std::vector<int> kind;
+    int n = 0;
+};
+Profiler g_prof;
+
+struct ProfScope {
+    hipStream_t s;
+    int slot = -1;
+    ProfScope(int kind, hipStream_t st) : s(st) {
+        if (g_prof.cap > 0 && g_prof.n < g_prof.cap) {
+            slot = g_prof.n++;
+            g_prof.kind[slot] = kind;
+            (void)hipEventRecord(g_prof.ev[2 * slot], s);
+        }
+    }
+    ~ProfScope() {
+        if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
+    }
+};
+
 }  // namespace
 
 extern "C" {
 
 const char* bgtq_last_error(void) { return g_err.c_str(); }
+
+int bgtq_profile_enable(int max_launches) {
+    if (max_launches < 0) return fail(BGTQ_E_INVALID, "max_launches < 0");
+    for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+    g_prof = Profiler{};
+    if (max_launches == 0) return ok();
+    g_prof.ev.resize(2 * (size_t)max_launches);
+    g_prof.kind.resize(max_launches);
+    for (auto& e : g_prof.ev) {
+        hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) {
+            g_prof.ev.clear();
+            return hip_fail(r, "hipEventCreate");
+        }
+    }
+    g_prof.cap = max_launches;
+    return ok();
+}
+
+int bgtq_profile_read(int kind, int* n_launches, double* total_ms, double* min_ms, double* max_ms) {
+    int cnt = 0;
+    double tot = 0.0, mn = 0.0, mx = 0.0;
+    std::vector<int> keep;
+    for (int i = 0; i < g_prof.n; ++i) {
+        if (g_prof.kind[i] != kind) {
+            keep.push_back(i);
+            continue;
+        }
+        hipError_t r = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+        float ms = 0.f;
+        if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+        if (r != hipSuccess) return hip_fail(r, "profile event");
+        tot += ms;
+        mn = cnt ? std::min(mn, (double)ms) : ms;
+        mx = cnt ? std::max(mx, (double)ms) : ms;
+        ++cnt;
+    }
+    // compact the records of other kinds to the front (swap their event pairs)
+    for (size_t j = 0; j < keep.size(); ++j) {
+        const int i = keep[j];
+        if (i != (int)j) {
+            std::swap(g_prof.ev[2 * j], g_prof.ev[2 * i]);
+            std::swap(g_prof.ev[2 * j + 1], g_prof.ev[2 * i + 1]);
+            g_prof.kind[j] = g_prof.kind[i];
+        }
+    }
+    g_prof.n = (int)keep.size();
+    if (n_launches) *n_launches = cnt;
+    if (total_ms) *total_ms = tot;
+    if (min_ms) *min_ms = mn;
+    if (max_ms) *max_ms = mx;
+    return ok();
+}
 
 const char* bgtq_version(void) { return "bgtq 0.1 (gfx950)"; }
 
@@ -302,6 +377,7 @@ int bgtq_quantize_append(bgtq_cache* c, int layer, const void* k, const void* v,
             q.tile0[b] = lo[b] / TILE;
             if (hi[b] > lo[b]) max_tiles = std::max(max_tiles, (hi[b] - 1) / TILE - lo[b] / TILE + 1);
         }
+        ProfScope ps(BGTQ_PROF_QUANTIZE, s);
         return bgtq::launch_quant(q, c->B, max_tiles, s);
     };
     std::vector<int64_t> lo(c->B), hi(c->B), off(c->B);
@@ -359,7 +435,8 @@ int64_t bgtq_decode_workspace_bytes(const bgtq_cache* c, int n_splits) {
     const int64_t max_tiles = g.n_tiles;
     const int ns = n_splits ? n_splits : default_splits(max_tiles, g.B * g.Hkv, cu_count());
     const int parts = ns + (g.n_recent > 0 ? 1 : 0);
-    return (int64_t)align256(prep_bytes(g)) + (int64_t)g.B * g.Hq * parts * PART * 4;
+    if (parts > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS - 1);
+    return (int64_t)g.B * g.Hq * parts * PART * 4;
 }
 
 int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dtype, float* out, void* ws,
@@ -383,40 +460,27 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
                     "v_bits %d, g %d)", c->k_mode, g.R, c->k_bits, c->k_group, c->v_bits, g.G);
     const int64_t* nt = c->n_tokens + (size_t)layer * c->B;
     bgtq::DecodeArgs a{};
+    int32_t n_rec[BGTQ_MAX_BATCH] = {};
     int64_t max_tiles = 0;
     bool any_recent = false;
     for (int b = 0; b < c->B; ++b) {
         if (nt[b] <= 0) return fail(BGTQ_E_INVALID, "sequence %d has an empty context", b);
         const int64_t rec = c->n_recent > 0 ? std::min<int64_t>(nt[b], c->n_recent) : 0;
-        a.n_packed[b] = nt[b] - rec;
-        a.n_rec[b] = (int32_t)rec;
+        a.n_packed[b] = (int32_t)(nt[b] - rec);
+        n_rec[b] = (int32_t)rec;
         if (a.n_packed[b] > c->n_cap) return fail(BGTQ_E_INVALID, "sequence %d exceeds n_cap", b);
-        max_tiles = std::max(max_tiles, (a.n_packed[b] + TILE - 1) / TILE);
+        max_tiles = std::max<int64_t>(max_tiles, ((int64_t)a.n_packed[b] + TILE - 1) / TILE);
         any_recent |= rec > 0;
     }
     const int ns = n_splits ? n_splits : default_splits(g.n_tiles, g.B * g.Hkv, cu_count());
     const int parts = ns + (c->n_recent > 0 ? 1 : 0);
-    const size_t prep_sz = align256(prep_bytes(g));
-    const size_t need = prep_sz + (size_t)g.B * g.Hq * parts * PART * 4;
+    if (parts > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS - 1);
+    const size_t need = (size_t)g.B * g.Hq * parts * PART * 4;
     if (ws_bytes < need) return fail(BGTQ_E_INVALID, "workspace too small (%zu < %zu)", ws_bytes, need);
     (void)any_recent;
     hipStream_t s = (hipStream_t)stream;
-    const bgtq::PrepLayout PL = bgtq::prep_layout(g.G);
-    uint32_t* prep = (uint32_t*)ws;
-    float* part = (float*)((uint8_t*)ws + prep_sz);
-    bgtq::PrepArgs pa{};
-    pa.q = q;
-    pa.dtype = dtype;
-    pa.bits = c->k_mode == BGTQ_K_BLOCKGTQ ? c->bits + (size_t)layer * g.Hkv * 64 : nullptr;
-    pa.sigma = c->k_mode == BGTQ_K_BLOCKGTQ ? c->sigma + (size_t)layer * g.Hkv * 64 : nullptr;
-    pa.out = prep;
-    pa.Hkv = g.Hkv;
-    pa.G = g.G;
-    pa.k_mode = c->k_mode;
-    pa.k_group = c->k_mode == BGTQ_K_AFFINE ? c->k_group : 128;
-    pa.stride = PL.stride;
-    hipError_t e = bgtq::launch_prep(pa, g.B, s);
-    if (e != hipSuccess) return hip_fail(e, "prep launch");
+    float* part = (float*)ws;
+    hipError_t e;
     const size_t bh = (size_t)g.B * g.Hkv;
     a.k_codes = (const uint8_t*)c->k_codes + (size_t)layer * g.k_codes_layer;
     a.v_codes = (const uint8_t*)c->v_codes + (size_t)layer * g.v_codes_layer;
@@ -424,11 +488,27 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
     a.k_zero = c->k_zero ? (const uint16_t*)((const uint8_t*)c->k_zero + (size_t)layer * g.k_scale_layer) : nullptr;
     a.v_scale = (const uint16_t*)((const uint8_t*)c->v_scale + (size_t)layer * g.v_scale_layer);
     a.v_zero = c->v_zero ? (const uint16_t*)((const uint8_t*)c->v_zero + (size_t)layer * g.v_scale_layer) : nullptr;
+    a.q = q;
+    a.q_dtype = dtype;
+    a.bits = c->k_mode == BGTQ_K_BLOCKGTQ ? c->bits + (size_t)layer * g.Hkv * 64 : nullptr;
+    a.sigma = c->k_mode == BGTQ_K_BLOCKGTQ ? c->sigma + (size_t)layer * g.Hkv * 64 : nullptr;
+    bgtq::Fp16Args ra{};
     if (c->n_recent > 0) {
-        a.recent_k = (const uint16_t*)c->recent_k + (size_t)layer * bh * c->n_recent * D;
-        a.recent_v = (const uint16_t*)c->recent_v + (size_t)layer * bh * c->n_recent * D;
+        ra.k16 = (const uint16_t*)c->recent_k + (size_t)layer * bh * c->n_recent * D;
+        ra.v16 = (const uint16_t*)c->recent_v + (size_t)layer * bh * c->n_recent * D;
+        ra.q = q;
+        ra.q_dtype = dtype;
+        ra.part = part;
+        ra.Hkv = g.Hkv;
+        ra.Hq = g.Hq;
+        ra.G = g.G;
+        ra.rows = c->n_recent;
+        ra.n_splits = 1;
+        ra.tiles_per_split = (c->n_recent + TILE - 1) / TILE;
+        ra.split0 = ns;
+        ra.n_parts = parts;
+        for (int b = 0; b < c->B; ++b) ra.n_valid[b] = n_rec[b];
     }
-    a.prep = prep;
     a.part = part;
     a.Hkv = g.Hkv;
     a.Hq = g.Hq;
@@ -443,10 +523,16 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
     a.n_parts = parts;
     a.tiles_per_split = (int)((max_tiles + ns - 1) / ns);
     if (a.tiles_per_split < 1) a.tiles_per_split = 1;
-    a.prep_stride = PL.stride;
     a.v_affine = c->v_mode == BGTQ_V_AFFINE;
-    e = bgtq::launch_decode(a, g.B, c->k_mode, g.R, c->v_bits, s);
+    {
+        ProfScope ps(BGTQ_PROF_DECODE, s);
+        e = bgtq::launch_decode(a, g.B, c->k_mode, g.R, c->v_bits, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "decode launch");
+    if (c->n_recent > 0) {
+        e = bgtq::launch_fp16(ra, g.B, s);
+        if (e != hipSuccess) return hip_fail(e, "recent-ring decode launch");
+    }
     bgtq::CombineArgs ca{part, out, parts};
     e = bgtq::launch_combine(ca, g.B * g.Hq, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
@@ -457,7 +543,9 @@ int64_t bgtq_fp16_decode_workspace_bytes(int64_t N, int B, int Hq, int Hkv, int 
     if (N < 1 || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || n_splits < 0) return fail(BGTQ_E_INVALID, "bad sizes");
     const int G = Hq / Hkv;
     const int ns = n_splits ? n_splits : default_splits((N + TILE - 1) / TILE, B * Hkv, cu_count());
-    return (int64_t)align256((size_t)B * Hkv * bgtq::prep_layout(G).stride * 4) + (int64_t)B * Hq * ns * PART * 4;
+    if (ns > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS);
+    (void)G;
+    return (int64_t)B * Hq * ns * PART * 4;
 }
 
 int bgtq_fp16_decode_attention(const void* k16, const void* v16, int64_t N, int B, int Hq, int Hkv, int d,
@@ -466,6 +554,8 @@ int bgtq_fp16_decode_attention(const void* k16, const void* v16, int64_t N, int 
     if (!k16 || !v16 || !q || !out || !ws) return fail(BGTQ_E_INVALID, "NULL pointer");
     if (d != D) return fail(BGTQ_E_UNSUPPORTED, "head dim must be 128");
     if (N < 1 || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(BGTQ_E_INVALID, "bad sizes");
+    if (B > BGTQ_MAX_BATCH) return fail(BGTQ_E_UNSUPPORTED, "B=%d exceeds %d", B, BGTQ_MAX_BATCH);
+    if (N > INT32_MAX) return fail(BGTQ_E_UNSUPPORTED, "N too large");
     if (!dtype_ok(dtype)) return fail(BGTQ_E_INVALID, "bad dtype");
     if (n_splits < 0) return fail(BGTQ_E_INVALID, "n_splits < 0");
     if (((uintptr_t)ws) & 255) return fail(BGTQ_E_INVALID, "workspace must be 256-byte aligned");
@@ -474,37 +564,31 @@ int bgtq_fp16_decode_attention(const void* k16, const void* v16, int64_t N, int 
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return fail(BGTQ_E_UNSUPPORTED, "group size %d unsupported", G);
     const int64_t n_tiles = (N + TILE - 1) / TILE;
     const int ns = n_splits ? n_splits : default_splits(n_tiles, B * Hkv, cu_count());
-    const bgtq::PrepLayout PL = bgtq::prep_layout(G);
-    const size_t prep_sz = align256((size_t)B * Hkv * PL.stride * 4);
-    const size_t need = prep_sz + (size_t)B * Hq * ns * PART * 4;
+    if (ns > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS);
+    const size_t need = (size_t)B * Hq * ns * PART * 4;
     if (ws_bytes < need) return fail(BGTQ_E_INVALID, "workspace too small (%zu < %zu)", ws_bytes, need);
     hipStream_t s = (hipStream_t)stream;
-    uint32_t* prep = (uint32_t*)ws;
-    float* part = (float*)((uint8_t*)ws + prep_sz);
-    bgtq::PrepArgs pa{};
-    pa.q = q;
-    pa.dtype = dtype;
-    pa.out = prep;
-    pa.Hkv = Hkv;
-    pa.G = G;
-    pa.k_mode = BGTQ_K_AFFINE;  // natural-order query copy only
-    pa.k_group = 128;
-    pa.stride = PL.stride;
-    hipError_t e = bgtq::launch_prep(pa, B, s);
-    if (e != hipSuccess) return hip_fail(e, "prep launch");
+    float* part = (float*)ws;
+    hipError_t e;
     bgtq::Fp16Args a{};
     a.k16 = (const uint16_t*)k16;
     a.v16 = (const uint16_t*)v16;
-    a.prep = prep;
+    a.q = q;
+    a.q_dtype = dtype;
     a.part = part;
     a.Hkv = Hkv;
     a.Hq = Hq;
     a.G = G;
-    a.N = N;
+    a.rows = N;
     a.n_splits = ns;
     a.tiles_per_split = (int)((n_tiles + ns - 1) / ns);
-    a.prep_stride = PL.stride;
-    e = bgtq::launch_fp16(a, B, s);
+    a.split0 = 0;
+    a.n_parts = ns;
+    for (int b = 0; b < B; ++b) a.n_valid[b] = (int32_t)N;
+    {
+        ProfScope ps(BGTQ_PROF_FP16_DECODE, s);
+        e = bgtq::launch_fp16(a, B, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "fp16 decode launch");
     bgtq::CombineArgs ca{part, out, ns};
     e = bgtq::launch_combine(ca, B * Hq, s);

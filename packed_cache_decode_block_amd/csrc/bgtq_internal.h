@@ -6,36 +6,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#define BGTQ_MAXB 64  // sequences per call carried in kernel arguments
+#define BGTQ_MAXB 64         // sequences per call carried in kernel arguments
+#define BGTQ_MAX_PARTS 8192  // split partials per query head merged by the combine kernel
 
 namespace bgtq {
-
-// Per-(batch, kv head) prep record written by k_prep and read by the decode kernels.
-// Offsets in 32-bit words from the record start.
-struct PrepLayout {
-    int G;
-    int qp_words;     // 64 slots x 2 x G q' (sorted Block-GTQ order, sigma folded)
-    int qn_words;     // 64 blocks x 2 x G q'' (natural order, no sigma)
-    int qs_words;     // affine: 16 groups x G per-group query sums
-    int desc_words;   // 32 words: 64 x 16-bit slot descriptors; +1 word nnz_pad
-    int stride;       // record size in words (multiple of 64)
-    __host__ __device__ int qp() const { return 0; }
-    __host__ __device__ int qn() const { return qp_words; }
-    __host__ __device__ int qs() const { return qp_words + qn_words; }
-    __host__ __device__ int desc() const { return qp_words + qn_words + qs_words; }
-};
-
-__host__ __device__ inline PrepLayout prep_layout(int G) {
-    PrepLayout p;
-    p.G = G;
-    p.qp_words = 128 * G;
-    p.qn_words = 128 * G;
-    p.qs_words = 16 * G;
-    p.desc_words = 64;
-    int total = p.qp_words + p.qn_words + p.qs_words + p.desc_words;
-    p.stride = (total + 63) / 64 * 64;
-    return p;
-}
 
 // Byte geometry of one layer's buffers.
 struct Geometry {
@@ -51,16 +25,6 @@ struct Geometry {
     int64_t recent_layer;                     // bytes per layer per ring (K or V)
 };
 
-struct PrepArgs {
-    const void* q;              // [B][Hq][128] dtype
-    int dtype;
-    const uint8_t* bits;        // [Hkv][64] for this layer (BLOCKGTQ) or NULL
-    const float* sigma;         // [Hkv][64] or NULL
-    uint32_t* out;              // ws prep region [B][Hkv][stride]
-    int Hkv, G, k_mode, k_group;
-    int stride;
-};
-
 struct DecodeArgs {
     // layer buffers
     const uint8_t* k_codes;     // [B][Hkv][n_tiles][k_tile_bytes]
@@ -69,22 +33,21 @@ struct DecodeArgs {
     const uint16_t* k_zero;
     const uint16_t* v_scale;
     const uint16_t* v_zero;
-    const uint16_t* recent_k;   // fp16 [B][Hkv][n_recent][128]
-    const uint16_t* recent_v;
-    const uint32_t* prep;       // [B][Hkv][prep stride]
+    const void* q;              // [B][Hq][128] in q_dtype
+    const uint8_t* bits;        // [Hkv][64] this layer's widths (Block-GTQ)
+    const float* sigma;         // [Hkv][64]
     float* part;                // [B][Hq][n_parts][132]
+    int q_dtype;
     int Hkv, Hq, G;
     int64_t n_cap, n_tiles;
     int64_t k_tile_bytes, v_tile_bytes;
     int k_group;
     int n_recent;
-    int n_splits;               // packed splits; split index n_splits = recent split
+    int n_splits;               // packed splits (the fp16 ring, if any, is partial n_splits)
     int n_parts;                // n_splits + (recent ? 1 : 0)
     int tiles_per_split;
-    int prep_stride;
     int v_affine;
-    int64_t n_packed[BGTQ_MAXB];
-    int32_t n_rec[BGTQ_MAXB];
+    int32_t n_packed[BGTQ_MAXB];
 };
 
 struct CombineArgs {
@@ -93,14 +56,19 @@ struct CombineArgs {
     int n_parts;
 };
 
+// fp16 tiles: rows [B][Hkv][rows][128] fp16.  Used for the unquantized comparator (all splits)
+// and for the fp16 recent ring of a packed cache (one extra split written at part index split0).
 struct Fp16Args {
-    const uint16_t* k16;        // [B][Hkv][N][128]
+    const uint16_t* k16;
     const uint16_t* v16;
-    const uint32_t* prep;
+    const void* q;              // [B][Hq][128] in q_dtype
     float* part;
+    int q_dtype;
     int Hkv, Hq, G;
-    int64_t N;
-    int n_splits, tiles_per_split, prep_stride;
+    int64_t rows;               // rows per (b, h) in memory
+    int n_splits, tiles_per_split;
+    int split0, n_parts;        // partial index of split 0; partial records per query head
+    int32_t n_valid[BGTQ_MAXB]; // valid rows per sequence
 };
 
 struct EnergyArgs {
@@ -153,7 +121,6 @@ struct RingArgs {
 };
 
 // Launchers (bgtq_kernels.hip).  Return hipSuccess or the launch error.
-hipError_t launch_prep(const PrepArgs& a, int B, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s);
 hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t s);

@@ -186,23 +186,24 @@ __device__ __forceinline__ uint32_t vfield(const uint32_t* r) {
     }
 }
 
-template <int G, int VB, int F>
-__device__ __forceinline__ void pv_field(WaveState<G>& st, const uint32_t* r, const uint32_t (&w)[2][G],
-                                         const uint32_t* vlut) {
-    const uint32_t cp = vlut[vfield<VB, F>(r)];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-        st.o[h][F & 7] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[F >> 3][h]),
-                                                __builtin_bit_cast(half2_t, cp), st.o[h][F & 7], false);
+// One P·V iteration of a lane: quad `quad` (tokens 4quad..4quad+3), 8 dims.  All 16 centroid-pair
+// reads and the 2G weight reads are issued before the 16*G v_dot2 so one LDS wait covers them.
+template <int VB, int F = 0>
+__device__ __forceinline__ void vfields_read(uint32_t* cp, const uint32_t* r, const uint32_t* vlut) {
+    if constexpr (F < 16) {
+        cp[F] = vlut[vfield<VB, F>(r)];
+        vfields_read<VB, F + 1>(cp, r, vlut);
+    }
 }
 
-template <int G, int VB, int F = 0>
-__device__ __forceinline__ void pv_fields(WaveState<G>& st, const uint32_t* r, const uint32_t (&w)[2][G],
-                                          const uint32_t* vlut) {
-    if constexpr (F < 16) {
-        pv_field<G, VB, F>(st, r, w, vlut);
-        pv_fields<G, VB, F + 1>(st, r, w, vlut);
-    }
+template <int G>
+__device__ __forceinline__ void pv_dot(WaveState<G>& st, const uint32_t* cp, const uint32_t (&w)[2][G]) {
+#pragma unroll
+    for (int f = 0; f < 16; ++f)
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+            st.o[h][f & 7] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[f >> 3][h]),
+                                                    __builtin_bit_cast(half2_t, cp[f]), st.o[h][f & 7], false);
 }
 
 // Load the fp16 weight pairs of quad `quad` (pairs 2quad, 2quad+1) for all heads.
@@ -264,29 +265,48 @@ __device__ __forceinline__ void write_partial(WaveState<G>& st, float* red /*[4]
 }
 
 // ---------------------------------------------------------------------------------------------
-// q·k over one Block-GTQ slot (static S), record staged dword-major in LDS.
-template <int G, int S>
-__device__ __forceinline__ void gtq_slot(float* acc, const float* qv, uint32_t d16, const uint32_t* stg,
-                                         const float* klut) {
-    const uint32_t k = d16 & 31u, o = (d16 >> 5) & 31u, w = d16 >> 10;
-    const uint32_t lo = stg[k * TILE], hi = stg[(k + 1) * TILE];
-    const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, o);
-    const uint32_t ca = x & ((1u << w) - 1u);
-    const uint32_t cb = __builtin_amdgcn_ubfe(x, w, w);
+// q·k over Block-GTQ slots, records staged dword-major in LDS.  Three stages per slot:
+// window read (two dwords around the slot's bit offset), centroid reads (two table lookups),
+// DPP-broadcast FMAs.  Groups of four slots are software-pipelined: the next group's window reads
+// are issued before this group's FMAs so their LDS latency hides behind the arithmetic.
+struct Win {
+    uint32_t lo, hi;
+};
+
+__device__ __forceinline__ uint32_t dsc16(const uint32_t* dsc, int s) {
+    return (dsc[s >> 1] >> (16 * (s & 1))) & 0xFFFFu;
+}
+
+__device__ __forceinline__ Win win_read(const uint32_t* stage, uint32_t li, uint32_t d16) {
+    const uint32_t k = d16 & 31u;
+    return Win{stage[k * TILE + li], stage[(k + 1) * TILE + li]};
+}
+
+__device__ __forceinline__ void lut_read(float& va, float& vb, const Win& wn, uint32_t d16, const float* klut) {
+    const uint32_t o = (d16 >> 5) & 31u, w = d16 >> 10;
+    const uint32_t x = __builtin_amdgcn_alignbit(wn.hi, wn.lo, o);
     const float* lut = klut + ((1 << w) - 2);
-    SlotFma<G, SlotPos<G, S>::base>::run(acc, qv[SlotPos<G, S>::vgpr], lut[ca], lut[cb]);
+    va = lut[x & ((1u << w) - 1u)];
+    vb = lut[__builtin_amdgcn_ubfe(x, w, w)];
 }
 
 template <int G, int GR = 0>
-__device__ __forceinline__ void gtq_groups(float* acc, const float* qv, const uint32_t* dsc, int nnz_pad,
-                                           const uint32_t* stg, const float* klut) {
+__device__ __forceinline__ void gtq_pipe(float* acc, const float* qv, const uint32_t* dsc, int nnz_pad,
+                                         const uint32_t* stage, uint32_t li, const float* klut, Win* wn) {
     if constexpr (GR < 16) {
         if (GR * 4 < nnz_pad) {
-            gtq_slot<G, 4 * GR + 0>(acc, qv, dsc[2 * GR] & 0xFFFFu, stg, klut);
-            gtq_slot<G, 4 * GR + 1>(acc, qv, dsc[2 * GR] >> 16, stg, klut);
-            gtq_slot<G, 4 * GR + 2>(acc, qv, dsc[2 * GR + 1] & 0xFFFFu, stg, klut);
-            gtq_slot<G, 4 * GR + 3>(acc, qv, dsc[2 * GR + 1] >> 16, stg, klut);
-            gtq_groups<G, GR + 1>(acc, qv, dsc, nnz_pad, stg, klut);
+            float va[4], vb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) lut_read(va[j], vb[j], wn[j], dsc16(dsc, 4 * GR + j), klut);
+            if constexpr (GR + 1 < 16) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wn[j] = win_read(stage, li, dsc16(dsc, 4 * (GR + 1) + j));
+            }
+            SlotFma<G, SlotPos<G, 4 * GR + 0>::base>::run(acc, qv[SlotPos<G, 4 * GR + 0>::vgpr], va[0], vb[0]);
+            SlotFma<G, SlotPos<G, 4 * GR + 1>::base>::run(acc, qv[SlotPos<G, 4 * GR + 1>::vgpr], va[1], vb[1]);
+            SlotFma<G, SlotPos<G, 4 * GR + 2>::base>::run(acc, qv[SlotPos<G, 4 * GR + 2>::vgpr], va[2], vb[2]);
+            SlotFma<G, SlotPos<G, 4 * GR + 3>::base>::run(acc, qv[SlotPos<G, 4 * GR + 3>::vgpr], va[3], vb[3]);
+            gtq_pipe<G, GR + 1>(acc, qv, dsc, nnz_pad, stage, li, klut, wn);
         }
     }
 }
@@ -333,13 +353,6 @@ __device__ __forceinline__ void affine4_run(float* acc, float* gp, const float* 
     }
 }
 
-template <int G>
-__device__ __forceinline__ void load_qv(float* qv, const uint32_t* src, int lane) {
-    const float* s = (const float*)src;
-#pragma unroll
-    for (int v = 0; v < 8 * G; ++v) qv[v] = s[v * 16 + (lane & 15)];
-}
-
 // fp16 tiles (recent ring or the unquantized comparator): rows [n][128] fp16 of one (b, h).
 template <int G>
 __device__ void fp16_tiles(WaveState<G>& st, const uint16_t* K16, const uint16_t* V16, int64_t n,
@@ -351,18 +364,30 @@ __device__ void fp16_tiles(WaveState<G>& st, const uint16_t* K16, const uint16_t
 #pragma unroll
         for (int h = 0; h < G; ++h) acc[h] = 0.f;
         const uint4* rowp = (const uint4*)(K16 + (valid ? pos : 0) * D);
+        // 256-byte row in four 64-byte chunks; the next chunk is in flight while one is consumed.
+        uint32_t cur[16], nxt[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint4 v = rowp[u];
+            cur[4 * u] = v.x; cur[4 * u + 1] = v.y; cur[4 * u + 2] = v.z; cur[4 * u + 3] = v.w;
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            uint32_t r16[16];
+            if (c < 3) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint4 v = rowp[c * 4 + u];
-                r16[4 * u] = v.x; r16[4 * u + 1] = v.y; r16[4 * u + 2] = v.z; r16[4 * u + 3] = v.w;
+                for (int u = 0; u < 4; ++u) {
+                    const uint4 v = rowp[(c + 1) * 4 + u];
+                    nxt[4 * u] = v.x; nxt[4 * u + 1] = v.y; nxt[4 * u + 2] = v.z; nxt[4 * u + 3] = v.w;
+                }
             }
-            if (c == 0) fp16_blocks<G, 0>(acc, qv, r16);
-            if (c == 1) fp16_blocks<G, 16>(acc, qv, r16);
-            if (c == 2) fp16_blocks<G, 32>(acc, qv, r16);
-            if (c == 3) fp16_blocks<G, 48>(acc, qv, r16);
+            asm volatile("" ::: "memory");
+            if (c == 0) fp16_blocks<G, 0>(acc, qv, cur);
+            if (c == 1) fp16_blocks<G, 16>(acc, qv, cur);
+            if (c == 2) fp16_blocks<G, 32>(acc, qv, cur);
+            if (c == 3) fp16_blocks<G, 48>(acc, qv, cur);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int u = 0; u < 16; ++u) cur[u] = nxt[u];
         }
         float z[G];
 #pragma unroll
@@ -405,9 +430,85 @@ __device__ void fp16_tiles(WaveState<G>& st, const uint16_t* K16, const uint16_t
 }
 
 // ---------------------------------------------------------------------------------------------
+// ---------------------------------------------------------------------------------------------
+// Per-workgroup query preparation (wave 0, lane = RoPE block i).  Writes, in LDS:
+//  qp[s*2G + e*G + h]: query coordinate (block s, half e) of head h times log2(e)/sqrt(d), with
+//    Block-GTQ keys in slot order (width descending, ties by block index) and sigma folded in;
+//    natural block order otherwise; zero for padding slots.
+//  dsc16[s]: slot descriptor (start dword | bit offset << 5 | width << 10); padding = width 1 at 0.
+//  qs[g*G + h]: per-key-group sums of the natural scaled query (affine keys).
+// The block order comes from nine wave ballots (one per width) instead of a sort.
+template <int G, bool SORTED, int KG>
+__device__ void prep_wave(const void* q, int dtype, const uint8_t* bits, const float* sigma, int b, int h,
+                          int Hq, int lane, float* qp, uint16_t* dsc16, uint32_t* nnz_pad, float* qs) {
+    float q0[G], q1[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        const int64_t base = ((int64_t)b * Hq + (int64_t)h * G + hh) * D + 2 * lane;
+        q0[hh] = load_act(q, base, dtype) * kLog2eOverSqrtD;
+        q1[hh] = load_act(q, base + 1, dtype) * kLog2eOverSqrtD;
+    }
+    if constexpr (SORTED) {
+        const int w = bits[h * 64 + lane];
+        const float sg = sigma[h * 64 + lane];
+        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        int rank = 0, pos = 0, nnz = 0;
+#pragma unroll
+        for (int v = 0; v <= 8; ++v) {
+            const uint64_t mk = __ballot(w == v);
+            const int c = __popcll(mk);
+            if (v == 0) nnz = 64 - c;
+            if (v > w) {
+                rank += c;
+                pos += 2 * v * c;
+            } else if (v == w) {
+                const int cl = __popcll(mk & lt);
+                rank += cl;
+                pos += 2 * v * cl;
+            }
+        }
+        if (w > 0) {
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                qp[rank * 2 * G + hh] = q0[hh] * sg;
+                qp[rank * 2 * G + G + hh] = q1[hh] * sg;
+            }
+            dsc16[rank] = (uint16_t)((pos >> 5) | ((pos & 31) << 5) | (w << 10));
+        }
+        if (lane >= nnz) {
+#pragma unroll
+            for (int hh = 0; hh < 2 * G; ++hh) qp[lane * 2 * G + hh] = 0.f;
+            dsc16[lane] = (uint16_t)(1u << 10);
+        }
+        if (lane == 0) *nnz_pad = (uint32_t)((nnz + 3) & ~3);
+    } else {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            qp[lane * 2 * G + hh] = q0[hh];
+            qp[lane * 2 * G + G + hh] = q1[hh];
+        }
+        if constexpr (KG > 0) {
+            wave_lds_fence();
+            constexpr int NG = D / KG;
+            if (lane < NG * G) {
+                const int gi = lane / G, hh = lane % G;
+                float acc = 0.f;
+                for (int j = gi * KG; j < (gi + 1) * KG; ++j) acc += qp[(j >> 1) * 2 * G + (j & 1) * G + hh];
+                qs[gi * G + hh] = acc;
+            }
+        }
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void load_qv_lds(float* qv, const float* qp, int lane) {
+#pragma unroll
+    for (int v = 0; v < 8 * G; ++v) qv[v] = qp[v * 16 + (lane & 15)];
+}
+
 // KG == 0: Block-GTQ keys (R record dwords); KG > 0: affine 4-bit keys with groups of KG.
 template <int G, int R, int VB, int KG>
-__global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
     constexpr bool AFFINE_K = KG > 0;
     constexpr int NG = AFFINE_K ? D / (KG > 0 ? KG : 1) : 1;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -417,6 +518,49 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
     __shared__ uint32_t s_stage[4][AFFINE_K ? 1 : (R + 1) * TILE];
     __shared__ uint16_t s_w[4][64 * G];
     __shared__ float s_red[4 * G * PART];
+    __shared__ float s_qp[128 * G];
+    __shared__ uint16_t s_dsc[64];
+    __shared__ uint32_t s_nnz;
+    __shared__ float s_qs[AFFINE_K ? NG * G : 1];
+
+    const size_t bh = (size_t)b * a.Hkv + h;
+    constexpr int ng = NG;
+    const int64_t n_packed = a.n_packed[b];
+    const int64_t n_tiles_b = (n_packed + TILE - 1) / TILE;
+    const int64_t t_lo = (int64_t)split * a.tiles_per_split;
+    const int64_t t_hi = t_lo + a.tiles_per_split < n_tiles_b ? t_lo + a.tiles_per_split : n_tiles_b;
+
+    const uint32_t* kc = (const uint32_t*)(a.k_codes + bh * a.n_tiles * a.k_tile_bytes);
+    const uint32_t* vc = (const uint32_t*)(a.v_codes + bh * a.n_tiles * a.v_tile_bytes);
+    const uint16_t* ks = a.k_scale + bh * a.n_cap * ng;
+    const uint16_t* kz = AFFINE_K ? a.k_zero + bh * a.n_cap * ng : nullptr;
+    const uint16_t* vs = a.v_scale + bh * a.n_cap;
+    const uint16_t* vz = a.v_affine ? a.v_zero + bh * a.n_cap : nullptr;
+    uint32_t* stage = s_stage[wave];
+    constexpr int RK = AFFINE_K ? 16 : R;
+
+    // Registers of the tile in flight (prefetched one tile ahead).
+    uint32_t kn[RK], vn[4][VB];
+    uint16_t ksn[NG], kzn[NG], vsn, vzn;
+    auto fetch = [&](int64_t t) {
+        const uint32_t* kt = kc + t * (a.k_tile_bytes / 4);
+        const uint32_t* vt = vc + t * (a.v_tile_bytes / 4);
+#pragma unroll
+        for (int k = 0; k < RK; ++k) kn[k] = kt[k * TILE + lane];
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int c = 0; c < VB; ++c) vn[it][c] = vt[(it * 64 + lane) * VB + c];
+        const int64_t p = t * TILE + lane < n_packed ? t * TILE + lane : 0;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            ksn[gi] = ks[p * NG + gi];
+            kzn[gi] = AFFINE_K ? kz[p * NG + gi] : (uint16_t)0;
+        }
+        vsn = vs[p];
+        vzn = vz ? vz[p] : (uint16_t)0;
+    };
+    if (t_lo + wave < t_hi) fetch(t_lo + wave);
 
     for (int i = threadIdx.x; i < BGTQ_CB_CENTROIDS; i += blockDim.x) s_klut[i] = __builtin_bit_cast(float, c_cent32[i]);
     for (int i = threadIdx.x; i < (1 << (2 * VB)); i += blockDim.x) {
@@ -431,97 +575,74 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
         }
         s_vlut[i] = ha | (hb << 16);
     }
+    if (wave == 0)
+        prep_wave<G, !AFFINE_K, KG>(a.q, a.q_dtype, a.bits, a.sigma, b, h, a.Hq, lane, s_qp, s_dsc, &s_nnz, s_qs);
     __syncthreads();
 
-    const size_t bh = (size_t)b * a.Hkv + h;
-    const uint32_t* prep = a.prep + bh * a.prep_stride;
-    const PrepLayout PL = prep_layout(G);
     float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_parts * PART;
     uint16_t* wbuf = s_w[wave];
 
     WaveState<G> st;
     state_init<G>(st);
     float qv[8 * G];
-
-    if (split == a.n_splits) {  // fp16 recent ring, concatenated order-free with the packed tokens
-        load_qv<G>(qv, prep + PL.qn(), lane);
-        const int64_t n = a.n_rec[b];
-        const uint16_t* rk = a.recent_k + bh * (size_t)a.n_recent * D;
-        const uint16_t* rv = a.recent_v + bh * (size_t)a.n_recent * D;
-        fp16_tiles<G>(st, rk, rv, n, 0, (n + TILE - 1) / TILE, wave, qv, wbuf, lane);
-        write_partial<G>(st, s_red, part, a.n_parts, split, wave, lane);
-        return;
-    }
-
-    load_qv<G>(qv, prep + (AFFINE_K ? PL.qn() : PL.qp()), lane);
+    load_qv_lds<G>(qv, s_qp, lane);
     uint32_t dsc[32];
     int nnz_pad = 0;
     float qs[NG * G];
-    constexpr int ng = NG;
     if constexpr (!AFFINE_K) {
+        const uint32_t* d32 = (const uint32_t*)s_dsc;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) dsc[i] = prep[PL.desc() + i];
-        nnz_pad = (int)prep[PL.desc() + 32];
+        for (int i = 0; i < 32; ++i) dsc[i] = __builtin_amdgcn_readfirstlane(d32[i]);
+        nnz_pad = (int)__builtin_amdgcn_readfirstlane(s_nnz);
     } else {
-        const float* qsp = (const float*)(prep + PL.qs());
 #pragma unroll
-        for (int i = 0; i < NG * G; ++i) qs[i] = qsp[i];
+        for (int i = 0; i < NG * G; ++i) qs[i] = s_qs[i];
     }
 
-    const int64_t n_packed = a.n_packed[b];
-    const int64_t n_tiles_b = (n_packed + TILE - 1) / TILE;
-    const int64_t t_lo = (int64_t)split * a.tiles_per_split;
-    const int64_t t_hi = t_lo + a.tiles_per_split < n_tiles_b ? t_lo + a.tiles_per_split : n_tiles_b;
-
-    const uint32_t* kc = (const uint32_t*)(a.k_codes + bh * a.n_tiles * a.k_tile_bytes);
-    const uint32_t* vc = (const uint32_t*)(a.v_codes + bh * a.n_tiles * a.v_tile_bytes);
-    const uint16_t* ks = a.k_scale + bh * a.n_cap * ng;
-    const uint16_t* kz = AFFINE_K ? a.k_zero + bh * a.n_cap * ng : nullptr;
-    const uint16_t* vs = a.v_scale + bh * a.n_cap;
-    const uint16_t* vz = a.v_affine ? a.v_zero + bh * a.n_cap : nullptr;
-    uint32_t* stg = s_stage[wave] + lane;
 
     for (int64_t t = t_lo + wave; t < t_hi; t += 4) {
         const int64_t pos = t * TILE + lane;
         const bool valid = pos < n_packed;
-        const uint32_t* kt = kc + t * (a.k_tile_bytes / 4);
-        const uint32_t* vt = vc + t * (a.v_tile_bytes / 4);
-        uint32_t vrec[4][VB];
+        uint32_t kr[RK], vr[4][VB];
+#pragma unroll
+        for (int k = 0; k < RK; ++k) kr[k] = kn[k];
 #pragma unroll
         for (int it = 0; it < 4; ++it)
 #pragma unroll
-            for (int c = 0; c < VB; ++c) vrec[it][c] = vt[(it * 64 + lane) * VB + c];
-        const float vsc = h2f(vs[valid ? pos : 0]);
-        const float vzr = vz ? h2f(vz[valid ? pos : 0]) : 0.f;
+            for (int c = 0; c < VB; ++c) vr[it][c] = vn[it][c];
+        float scl[NG], zer[NG];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            scl[gi] = h2f(ksn[gi]);
+            zer[gi] = h2f(kzn[gi]);
+        }
+        const float vsc = h2f(vsn), vzr = h2f(vzn);
+        if (t + 4 < t_hi) fetch(t + 4);
 
         float acc[G];
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) acc[hh] = 0.f;
         if constexpr (!AFFINE_K) {
-            uint32_t krec[R];
+            // Per-slot scalar values and lane addresses are recomputed each tile (not hoisted).
 #pragma unroll
-            for (int k = 0; k < R; ++k) krec[k] = kt[k * TILE + lane];
-            const float ksc = h2f(ks[valid ? pos : 0]);
+            for (int i = 0; i < 32; ++i) asm volatile("" : "+s"(dsc[i]));
+            uint32_t li = lane;
+            asm volatile("" : "+v"(li));
             wave_lds_fence();
 #pragma unroll
-            for (int k = 0; k < R; ++k) stg[k * TILE] = krec[k];
+            for (int k = 0; k < R; ++k) stage[k * TILE + li] = kr[k];
             wave_lds_fence();
-            gtq_groups<G>(acc, qv, dsc, nnz_pad, stg, s_klut);
+            Win wn[4];
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) acc[hh] *= ksc;
+            for (int j = 0; j < 4; ++j) wn[j] = win_read(stage, li, dsc16(dsc, j));
+            gtq_pipe<G>(acc, qv, dsc, nnz_pad, stage, li, s_klut, wn);
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) acc[hh] *= scl[0];
         } else {
-            uint32_t krec[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) krec[k] = kt[k * TILE + lane];
-            float scl[NG], zer[NG], gp[G];
-#pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-                scl[gi] = h2f(ks[(valid ? pos : 0) * NG + gi]);
-                zer[gi] = h2f(kz[(valid ? pos : 0) * NG + gi]);
-            }
+            float gp[G];
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) gp[hh] = 0.f;
-            affine4_run<G, KG>(acc, gp, qv, krec, scl, zer, qs);
+            affine4_run<G, KG>(acc, gp, qv, kr, scl, zer, qs);
         }
         float z[G];
 #pragma unroll
@@ -531,9 +652,10 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
         wave_lds_fence();
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            uint32_t w[2][G];
+            uint32_t w[2][G], cp[16];
             load_w<G>(w, wbuf, it * 4 + (lane >> 4));
-            pv_fields<G, VB>(st, vrec[it], w, s_vlut);
+            vfields_read<VB>(cp, vr[it], s_vlut);
+            pv_dot<G>(st, cp, w);
         }
     }
     __syncthreads();
@@ -541,106 +663,71 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
 }
 
 
-// Unquantized comparator: the same split-K decode over an fp16 [B][Hkv][N][128] cache.
+// fp16 tiles: the unquantized comparator over [B][Hkv][N][128], and the fp16 recent ring of a packed
+// cache (one split, concatenated order-free with the packed tokens).
 template <int G>
-__global__ __launch_bounds__(256) void k_decode_fp16(const Fp16Args a) {
+__global__ __launch_bounds__(256, 2) void k_decode_fp16(const Fp16Args a) {
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     __shared__ uint16_t s_w[4][64 * G];
     __shared__ float s_red[4 * G * PART];
     const size_t bh = (size_t)b * a.Hkv + h;
-    const PrepLayout PL = prep_layout(G);
+    __shared__ float s_qp[128 * G];
+    if (wave == 0)
+        prep_wave<G, false, 0>(a.q, a.q_dtype, nullptr, nullptr, b, h, a.Hq, lane, s_qp, nullptr, nullptr, nullptr);
+    __syncthreads();
     float qv[8 * G];
-    load_qv<G>(qv, a.prep + bh * a.prep_stride + PL.qn(), lane);
+    load_qv_lds<G>(qv, s_qp, lane);
     WaveState<G> st;
     state_init<G>(st);
-    const int64_t n_tiles = (a.N + TILE - 1) / TILE;
+    const int64_t n = a.n_valid[b];
+    const int64_t n_tiles = (n + TILE - 1) / TILE;
     const int64_t t_lo = (int64_t)split * a.tiles_per_split;
     const int64_t t_hi = t_lo + a.tiles_per_split < n_tiles ? t_lo + a.tiles_per_split : n_tiles;
-    fp16_tiles<G>(st, a.k16 + bh * a.N * D, a.v16 + bh * a.N * D, a.N, t_lo, t_hi, wave, qv, s_w[wave], lane);
+    fp16_tiles<G>(st, a.k16 + bh * a.rows * D, a.v16 + bh * a.rows * D, n, t_lo, t_hi, wave, qv, s_w[wave], lane);
     __syncthreads();
-    float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_splits * PART;
-    write_partial<G>(st, s_red, part, a.n_splits, split, wave, lane);
+    float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_parts * PART;
+    write_partial<G>(st, s_red, part, a.n_parts, a.split0 + split, wave, lane);
 }
 
-// Merge split partials (o, m, l) of one (batch, query head) by log-sum-exp.
-__global__ __launch_bounds__(128) void k_combine(const CombineArgs a) {
-    const int row = blockIdx.x, j = threadIdx.x;
+// Merge split partials (o, m, l) of one (batch, query head) by log-sum-exp: block-wide max, then
+// per-split scale factors in LDS, then each of 256 threads sums one dim over half of the splits.
+__global__ __launch_bounds__(256) void k_combine(const CombineArgs a) {
+    __shared__ float s_sc[BGTQ_MAX_PARTS];
+    __shared__ float s_r[8];
+    __shared__ float s_o[128];
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* pr = a.part + (size_t)row * a.n_parts * PART;
-    float M = -INFINITY;
-    for (int s = 0; s < a.n_parts; ++s) M = fmaxf(M, pr[s * PART + 128]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < a.n_parts; ++s) {
+    float mloc = -INFINITY;
+    for (int s = tid; s < a.n_parts; s += 256) mloc = fmaxf(mloc, pr[s * PART + 128]);
+    mloc = wave_max(mloc);
+    if (lane == 0) s_r[wave] = mloc;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_r[0], s_r[1]), fmaxf(s_r[2], s_r[3]));
+    float lloc = 0.f;
+    for (int s = tid; s < a.n_parts; s += 256) {
         const float m = pr[s * PART + 128];
-        if (m == -INFINITY) continue;
-        const float sc = __builtin_amdgcn_exp2f(m - M);
-        L += sc * pr[s * PART + 129];
-        O += sc * pr[s * PART + j];
+        const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        s_sc[s] = sc;
+        lloc += sc * pr[s * PART + 129];
     }
-    a.out[(size_t)row * D + j] = O / L;
-}
-
-// Per (batch, kv head): block order, slot descriptors and the scaled query copies.
-__global__ __launch_bounds__(64) void k_prep(const PrepArgs a) {
-    const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;  // i = RoPE block
-    const int G = a.G, Hq = a.Hkv * G;
-    const PrepLayout L = prep_layout(G);
-    uint32_t* out = a.out + ((size_t)b * a.Hkv + h) * a.stride;
-    float* qp = (float*)(out + L.qp());
-    float* qn = (float*)(out + L.qn());
-    float* qs = (float*)(out + L.qs());
-    __shared__ float s_qn[D][8];
-    __shared__ int s_wid[64];
-    __shared__ uint32_t s_desc[64];
-    float q0[8], q1[8];
-    for (int hh = 0; hh < G; ++hh) {
-        const int64_t base = ((int64_t)b * Hq + (int64_t)h * G + hh) * D + 2 * i;
-        q0[hh] = load_act(a.q, base, a.dtype);
-        q1[hh] = load_act(a.q, base + 1, a.dtype);
-        const float n0 = q0[hh] * kLog2eOverSqrtD, n1 = q1[hh] * kLog2eOverSqrtD;
-        qn[i * 2 * G + hh] = n0;
-        qn[i * 2 * G + G + hh] = n1;
-        s_qn[2 * i][hh] = n0;
-        s_qn[2 * i + 1][hh] = n1;
+    lloc = wave_sum(lloc);
+    __syncthreads();
+    if (lane == 0) s_r[4 + wave] = lloc;
+    __syncthreads();
+    const float L = (s_r[4] + s_r[5]) + (s_r[6] + s_r[7]);
+    const int j = tid & 127, half = tid >> 7;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int s = half;
+    for (; s + 6 < a.n_parts; s += 8) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] += s_sc[s + 2 * u] * pr[(size_t)(s + 2 * u) * PART + j];
     }
-    if (a.k_mode == BGTQ_K_BLOCKGTQ) {
-        const int w = a.bits[h * 64 + i];
-        s_wid[i] = w;
-        __syncthreads();
-        int rank = 0, pos = 0, nnz = 0;
-        for (int j = 0; j < 64; ++j) {
-            const int wj = s_wid[j];
-            const bool before = wj > w || (wj == w && j < i);
-            rank += before;
-            pos += before ? 2 * wj : 0;
-            nnz += wj > 0;
-        }
-        if (w > 0) {
-            const float sg = a.sigma[h * 64 + i] * kLog2eOverSqrtD;
-            for (int hh = 0; hh < G; ++hh) {
-                qp[rank * 2 * G + hh] = q0[hh] * sg;
-                qp[rank * 2 * G + G + hh] = q1[hh] * sg;
-            }
-            s_desc[rank] = (uint32_t)(pos >> 5) | ((uint32_t)(pos & 31) << 5) | ((uint32_t)w << 10);
-        }
-        if (i >= nnz) {  // padding slot: reads dword 0, contributes q' = 0
-            for (int hh = 0; hh < 2 * G; ++hh) qp[i * 2 * G + hh] = 0.f;
-            s_desc[i] = 1u << 10;
-        }
-        __syncthreads();
-        uint32_t* desc = out + L.desc();
-        if (i < 32) desc[i] = s_desc[2 * i] | (s_desc[2 * i + 1] << 16);
-        if (i == 0) desc[32] = (uint32_t)((nnz + 3) & ~3);
-    } else {
-        __syncthreads();
-        const int ng = D / a.k_group;
-        if (i < ng * G) {
-            const int gi = i / G, hh = i % G;
-            float acc = 0.f;
-            for (int j = gi * a.k_group; j < (gi + 1) * a.k_group; ++j) acc += s_qn[j][hh];
-            qs[gi * G + hh] = acc;
-        }
-    }
+    for (; s < a.n_parts; s += 2) acc[0] += s_sc[s] * pr[(size_t)s * PART + j];
+    const float o = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    if (half == 1) s_o[j] = o;
+    __syncthreads();
+    if (half == 0) a.out[(size_t)row * D + j] = (o + s_o[j]) / L;
 }
 
 // Calibration energy sums in fp64: out[h][i] = (sum_t |k_t,blk i|^2, sum_{t,g} |q_t,g,blk i|^2).
@@ -882,13 +969,9 @@ __global__ __launch_bounds__(128) void k_ring(const RingArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // Launchers
-hipError_t launch_prep(const PrepArgs& a, int B, hipStream_t s) {
-    hipLaunchKernelGGL(k_prep, dim3(a.Hkv, B), dim3(64), 0, s, a);
-    return hipGetLastError();
-}
-
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s) {
-    hipLaunchKernelGGL(k_combine, dim3(rows), dim3(D), 0, s, a);
+    if (!a.part || !a.out || a.n_parts < 1 || a.n_parts > BGTQ_MAX_PARTS) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_combine, dim3(rows), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -916,6 +999,7 @@ static hipError_t launch_fp16_g(const Fp16Args& a, int B, hipStream_t s) {
 }
 
 hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t s) {
+    if (!a.k16 || !a.v16 || !a.q || !a.part || B < 1 || B > BGTQ_MAXB) return hipErrorInvalidValue;
     switch (a.G) {
         case 1: return launch_fp16_g<1>(a, B, s);
         case 2: return launch_fp16_g<2>(a, B, s);
@@ -927,7 +1011,7 @@ hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t s) {
 
 template <int G, int R, int VB, int KG>
 static hipError_t launch_dec(const DecodeArgs& a, int B, hipStream_t s) {
-    hipLaunchKernelGGL((k_decode<G, R, VB, KG>), dim3(a.n_parts, a.Hkv, B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_decode<G, R, VB, KG>), dim3(a.n_splits, a.Hkv, B), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -960,6 +1044,11 @@ static hipError_t launch_dec_g(const DecodeArgs& a, int B, int k_mode, int R, in
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t s) {
+    if (!a.k_codes || !a.v_codes || !a.k_scale || !a.v_scale || !a.q || !a.part || B < 1 || B > BGTQ_MAXB)
+        return hipErrorInvalidValue;
+    if (k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma)) return hipErrorInvalidValue;
+    if (k_mode == BGTQ_K_AFFINE && !a.k_zero) return hipErrorInvalidValue;
+    if (a.v_affine && !a.v_zero) return hipErrorInvalidValue;
     switch (a.G) {
         case 1: return launch_dec_g<1>(a, B, k_mode, R, v_bits, s);
         case 2: return launch_dec_g<2>(a, B, k_mode, R, v_bits, s);

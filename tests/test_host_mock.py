@@ -1,0 +1,103 @@
+"""Host logic of the C ABI without a GPU: the real bgtq_host.cpp linked against mock launchers
+that check every kernel argument block (pointers set, ranges consistent) and record launches."""
+import ctypes as C
+
+import numpy as np
+import pytest
+
+from packed_cache_decode_block_amd import _lib, build_lib
+
+FAKE = 0x7F0000000000  # never dereferenced: the mocks only inspect argument blocks
+
+
+@pytest.fixture(scope="module")
+def mock():
+    lib = _lib.bind(build_lib.build_mock())
+    lib.bgtq_mock_log.restype = C.c_char_p
+    return lib
+
+
+def _desc(nt, **kw):
+    d = _lib.CacheDesc()
+    base = dict(L=2, B=2, Hq=16, Hkv=2, d=128, n_cap=4096, k_mode=0, budget_units=192, k_bits=4, k_group=32,
+                v_mode=0, v_bits=3, n_recent=0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    ptrs = ["k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma"]
+    if base["k_mode"] == 1:
+        ptrs.append("k_zero")
+    if base["v_mode"] == 1:
+        ptrs.append("v_zero")
+    if base["n_recent"]:
+        ptrs += ["recent_k", "recent_v"]
+    for i, name in enumerate(ptrs):
+        setattr(d, name, FAKE + i * 0x1000000)
+    d.n_tokens = nt.ctypes.data_as(C.POINTER(C.c_int64))
+    return d
+
+
+def _call_ok(mock, rc):
+    log = mock.bgtq_mock_log().decode()
+    assert rc == 0 and "BAD" not in log, (rc, mock.bgtq_last_error(), log)
+    return log
+
+
+FORMATS = [dict(), dict(budget_units=128, v_bits=2), dict(k_mode=1, k_bits=4, k_group=32, v_mode=1, v_bits=2),
+           dict(budget_units=192, v_bits=2, n_recent=256), dict(budget_units=256, v_bits=4, Hq=8, Hkv=8),
+           dict(k_mode=1, k_group=128, v_bits=4, Hq=4, Hkv=2, n_recent=64)]
+
+
+@pytest.mark.parametrize("fmt", range(len(FORMATS)))
+def test_append_then_decode_arguments(mock, fmt):
+    nt = np.zeros((2, 2), np.int64)
+    d = _desc(nt, **FORMATS[fmt])
+    q = C.c_void_p(FAKE + 0x50000000)
+    ws = C.c_void_p(FAKE + 0x60000000)
+    for n_new in (1, 63, 64, 200, 1000):
+        mock.bgtq_mock_reset()
+        _call_ok(mock, mock.bgtq_quantize_append(C.byref(d), 1, q, q, 2, n_new, None, None))
+        for ns in (0, 1, 3, 40):
+            mock.bgtq_mock_reset()
+            need = mock.bgtq_decode_workspace_bytes(C.byref(d), ns)
+            assert need > 0
+            log = _call_ok(mock, mock.bgtq_decode_attention(C.byref(d), 1, q, 2, q, ws, need, ns, None))
+            assert log.count("decode") == 1 and log.count("combine") == 1
+            assert log.count("fp16") == (1 if d.n_recent else 0)
+    assert (nt[1] == 1 + 63 + 64 + 200 + 1000).all() and (nt[0] == 0).all()
+
+
+def test_ring_eviction_plan(mock):
+    """With a 256-token fp16 window, appends quantize exactly the tokens that leave the window."""
+    nt = np.zeros((1, 1), np.int64)
+    d = _desc(nt, L=1, B=1, n_recent=256, budget_units=192, v_bits=2)
+    q = C.c_void_p(FAKE + 0x50000000)
+    mock.bgtq_mock_reset()
+    _call_ok(mock, mock.bgtq_quantize_append(C.byref(d), 0, q, q, 2, 100, None, None))
+    assert "quant" not in mock.bgtq_mock_log().decode()          # everything still fits the ring
+    mock.bgtq_mock_reset()
+    _call_ok(mock, mock.bgtq_quantize_append(C.byref(d), 0, q, q, 2, 300, None, None))
+    log = mock.bgtq_mock_log().decode()
+    assert "quant" in log and "ring" in log
+    assert nt[0, 0] == 400
+
+
+def test_capacity_and_failure_leave_state(mock):
+    nt = np.zeros((2, 2), np.int64)
+    d = _desc(nt, n_cap=128)
+    q = C.c_void_p(FAKE + 0x50000000)
+    assert mock.bgtq_quantize_append(C.byref(d), 0, q, q, 2, 129, None, None) == _lib.E_CAPACITY
+    assert (nt == 0).all()
+    _call_ok(mock, mock.bgtq_quantize_append(C.byref(d), 0, q, q, 2, 128, None, None))
+    assert mock.bgtq_quantize_append(C.byref(d), 0, q, q, 2, 1, None, None) == _lib.E_CAPACITY
+    assert (nt[0] == 128).all()
+
+
+def test_fp16_comparator_arguments(mock):
+    q = C.c_void_p(FAKE + 0x50000000)
+    ws = C.c_void_p(FAKE + 0x60000000)
+    for (N, B, Hq, Hkv, ns) in ((1, 1, 1, 1, 0), (3000, 2, 16, 2, 5), (131072, 1, 16, 2, 0), (777, 3, 32, 8, 0)):
+        mock.bgtq_mock_reset()
+        need = mock.bgtq_fp16_decode_workspace_bytes(N, B, Hq, Hkv, ns)
+        _call_ok(mock, mock.bgtq_fp16_decode_attention(q, q, N, B, Hq, Hkv, 128, q, 2, q, ws, need, ns, None))
+        assert mock.bgtq_mock_launches() == 2
