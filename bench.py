@@ -48,6 +48,25 @@ def layer_bytes(w, N: int) -> float:
             + w.B * w.Hq * w.d * (act + 4))
 
 
+def measured_traffic(wid: int):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary of this workload
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None when there is none or
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", {2: "k_decode_qwen2.5-3b_128k_hbm_counters.md"}.get(wid, "-"))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"sha256\s+`([0-9a-f]{64})`", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    src = os.path.join(ROOT, "packed_cache_decode_block_amd", "csrc", "bgtq_kernels.hip")
+    cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if not h or not t or h.group(1) != cur:
+        return None
+    return int(t.group(1))
+
+
 def build_packed(w, device="cuda"):
     import torch
 
@@ -162,6 +181,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU part "
@@ -172,6 +193,17 @@ def main():
 
     import packed_cache_decode_block_amd as P
     import synth
+
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 5 copies of {args.copy_probe} MiB (read {args.copy_probe} MiB, write "
+            f"{args.copy_probe} MiB each)")
+        return
 
     w = synth.WORKLOADS[args.workload]
     if args.layers:
@@ -234,7 +266,7 @@ def main():
         "launch": "hipgraph" if graph_ok else "eager", "ms_per_step_eager": round(sec_eager * 1e3, 4),
         "tokens_heads_per_s": round(w.B * w.N * w.Hq * w.L / sec, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.wid),
                      "kernel": "k_decode (split-K packed decode)", "kernel_avg_us": round(kern_ms * 1e3, 3),
                      "bytes_per_launch": lb, "launches_timed": n_k},
     }
