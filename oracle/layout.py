@@ -14,11 +14,12 @@ K record (affine, b bits): coordinate j at bits [b*j, b*j + b).
 Tile of K records (R dwords per token): dword-major, token-minor — dword k of token t at byte
 (k*64 + t)*4, so the k-th dword of all 64 tokens is one contiguous 256-byte row.
 
-V tile (b bits, codebook or affine): 16 token quads (4q .. 4q+3) x 16 dim groups of 8 dims x
-b dwords, in that order (quad-major).  The b dwords of (quad q, group G) hold 16 fields of 2b
-bits, field f at bit 2b*f: token pair 2q + f//8 (tokens 4q + 2(f//8) and the next one), dim
-8G + f%8; low b bits = code of the even token, high b bits = code of the odd token.  A token
-that does not exist contributes zero bits.
+V tile (b bits, codebook or affine), "lane-stream" order: the tile is split into 64 streams of
+4*b dwords, one per lane L = dd + 16*j (dd in 0..15, j in 0..3).  Stream L holds 64 fields of 2b
+bits, field phi = (s*8 + db)*4 + m (s in 0..1, db in 0..7, m in 0..3) at bit 2b*phi: the codes
+of dim 16*db + dd for the token pair (p, p + 32), p = 16*s + 4*j + m, code of p in the low b
+bits.  Stream dword c sits at tile dword ((c // 4)*64 + L)*4 + c % 4, so a wave reads the tile
+with b loads of 16 bytes per lane.
 
 Scales: fp16 arrays indexed [token] (codebook K/V) or [token][group] (affine), one per
 (batch, kv head), outside the tiles.
@@ -116,32 +117,41 @@ def untile_records(tiles: np.ndarray, n: int, R: int) -> np.ndarray:
     return t32.transpose(0, 2, 1).reshape(n_tiles * TILE, R)[:n]
 
 
+def _v_lane_fields(L: int):
+    """(field index, token p, dim) of every field in lane L's stream."""
+    dd, j = L % 16, L // 16
+    out = []
+    for s_ in range(2):
+        for db in range(8):
+            for m in range(4):
+                out.append(((s_ * 8 + db) * 4 + m, 16 * s_ + 4 * j + m, 16 * db + dd))
+    return out
+
+
 def v_tiles(codes: np.ndarray, b: int, n_tiles: int) -> np.ndarray:
-    """codes [n, 128] -> tiles uint8 [n_tiles, 1024*b] in the quad-major layout."""
+    """codes [n, 128] -> tiles uint8 [n_tiles, 1024*b] in the lane-stream layout."""
     n, d = codes.shape
     assert d == 128
     full = np.zeros((n_tiles * TILE, d), np.int64)
     full[:n] = codes
-    quads = full.reshape(n_tiles * TILE // 4, 4, d)          # [quad, token in quad, dim]
-    rows = np.zeros((quads.shape[0], 16, b), np.uint32)       # [quad, group, dword]
-    for G in range(16):
-        sub = np.zeros((quads.shape[0], b), np.uint32)
-        for f in range(16):
-            pr, dim = f // 8, 8 * G + f % 8
-            field = quads[:, 2 * pr, dim] | (quads[:, 2 * pr + 1, dim] << b)
-            _put(sub, 2 * b * f, 2 * b, field)
-        rows[:, G] = sub
-    return rows.reshape(n_tiles, 1024 * b // 4).view(np.uint8).reshape(n_tiles, 1024 * b)
+    tok = full.reshape(n_tiles, TILE, d)
+    streams = np.zeros((n_tiles, 64, 4 * b), np.uint32)       # [tile, lane, stream dword]
+    for L in range(64):
+        for phi, p, dim in _v_lane_fields(L):
+            field = tok[:, p, dim] | (tok[:, p + 32, dim] << b)
+            _put(streams[:, L], 2 * b * phi, 2 * b, field)
+    out = streams.reshape(n_tiles, 64, b, 4).transpose(0, 2, 1, 3)  # [tile, c // 4, lane, c % 4]
+    return np.ascontiguousarray(out).view(np.uint8).reshape(n_tiles, 1024 * b)
 
 
 def v_codes(tiles: np.ndarray, b: int, n: int) -> np.ndarray:
     n_tiles = tiles.shape[0]
-    rows = np.ascontiguousarray(tiles).view(np.uint32).reshape(n_tiles * TILE // 4, 16, b)
-    quads = np.zeros((rows.shape[0], 4, 128), np.int64)
-    for G in range(16):
-        for f in range(16):
-            pr, dim = f // 8, 8 * G + f % 8
-            field = _get(rows[:, G], 2 * b * f, 2 * b)
-            quads[:, 2 * pr, dim] = field & ((1 << b) - 1)
-            quads[:, 2 * pr + 1, dim] = field >> b
-    return quads.reshape(-1, 128)[:n]
+    t32 = np.ascontiguousarray(tiles).view(np.uint32).reshape(n_tiles, b, 64, 4)
+    streams = np.ascontiguousarray(t32.transpose(0, 2, 1, 3)).reshape(n_tiles, 64, 4 * b)
+    tok = np.zeros((n_tiles, TILE, 128), np.int64)
+    for L in range(64):
+        for phi, p, dim in _v_lane_fields(L):
+            field = _get(streams[:, L], 2 * b * phi, 2 * b)
+            tok[:, p, dim] = field & ((1 << b) - 1)
+            tok[:, p + 32, dim] = field >> b
+    return tok.reshape(-1, 128)[:n]

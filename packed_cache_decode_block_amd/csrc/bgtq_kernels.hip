@@ -153,8 +153,9 @@ template <int G> __device__ __forceinline__ void state_init(WaveState<G>& st) {
 }
 
 // z: base-2 logits of this lane's token (-inf if invalid).  wscale multiplies p into the fp16
-// weight; zero (affine values) accumulates p * zero.  Writes fp16 weights to wbuf[pair*G + h].
-template <int G>
+// weight; zero (affine values) accumulates p * zero.  Writes the fp16 weights to wbuf, as pairs
+// (2t, 2t+1) per head, [t/2][h][2] (PAIR32 false), or as pairs (t, t+32), [h][t%32][2] (PAIR32 true).
+template <int G, bool PAIR32 = false>
 __device__ __forceinline__ void softmax_tile(WaveState<G>& st, const float* z, bool valid, float wscale,
                                              float zero, uint16_t* wbuf, int lane) {
 #pragma unroll
@@ -171,7 +172,8 @@ __device__ __forceinline__ void softmax_tile(WaveState<G>& st, const float* z, b
         const float p = valid ? __builtin_amdgcn_exp2f(z[h] - st.m[h]) : 0.f;
         st.l[h] += p;
         st.zs[h] += p * zero;
-        wbuf[((lane >> 1) * G + h) * 2 + (lane & 1)] = valid ? f2h(p * wscale) : (uint16_t)0;
+        const int wi = PAIR32 ? (h * 32 + (lane & 31)) * 2 + (lane >> 5) : ((lane >> 1) * G + h) * 2 + (lane & 1);
+        wbuf[wi] = valid ? f2h(p * wscale) : (uint16_t)0;
     }
 }
 
@@ -186,24 +188,41 @@ __device__ __forceinline__ uint32_t vfield(const uint32_t* r) {
     }
 }
 
-// One P·V iteration of a lane: quad `quad` (tokens 4quad..4quad+3), 8 dims.  All 16 centroid-pair
-// reads and the 2G weight reads are issued before the 16*G v_dot2 so one LDS wait covers them.
-template <int VB, int F = 0>
-__device__ __forceinline__ void vfields_read(uint32_t* cp, const uint32_t* r, const uint32_t* vlut) {
-    if constexpr (F < 16) {
-        cp[F] = vlut[vfield<VB, F>(r)];
-        vfields_read<VB, F + 1>(cp, r, vlut);
-    }
-}
-
-template <int G>
-__device__ __forceinline__ void pv_dot(WaveState<G>& st, const uint32_t* cp, const uint32_t (&w)[2][G]) {
+// P·V of one tile for lane L = dd + 16j over its value stream (lane-stream layout): field
+// (s, db, m) holds the codes of dim 16db + dd for the token pair (p, p + 32), p = 16s + 4j + m;
+// the pair table turns it into two fp16 centroids and v_dot2 multiplies them by the fp16 weights
+// (w_p, w_p+32) of each head.  o[h][db] accumulates dim 16db + dd.
+template <int G, int VB, int SDB>
+__device__ __forceinline__ void pv_block(WaveState<G>& st, const uint32_t* vs, const uint32_t* vlut,
+                                         const uint32_t (&w)[G][4]) {
+    constexpr int db = SDB % 8;
+    const uint32_t cp[4] = {vlut[vfield<VB, 4 * SDB>(vs)], vlut[vfield<VB, 4 * SDB + 1>(vs)],
+                            vlut[vfield<VB, 4 * SDB + 2>(vs)], vlut[vfield<VB, 4 * SDB + 3>(vs)]};
 #pragma unroll
-    for (int f = 0; f < 16; ++f)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int h = 0; h < G; ++h)
-            st.o[h][f & 7] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[f >> 3][h]),
-                                                    __builtin_bit_cast(half2_t, cp[f]), st.o[h][f & 7], false);
+            st.o[h][db] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[h][m]),
+                                                 __builtin_bit_cast(half2_t, cp[m]), st.o[h][db], false);
+}
+
+template <int G, int VB, int S>
+__device__ __forceinline__ void pv_half(WaveState<G>& st, const uint32_t* vs, const uint32_t* vlut,
+                                        const uint32_t* wb32, int j) {
+    uint32_t w[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const uint4 q = *(const uint4*)(wb32 + h * 32 + 16 * S + 4 * j);
+        w[h][0] = q.x; w[h][1] = q.y; w[h][2] = q.z; w[h][3] = q.w;
+    }
+    pv_block<G, VB, S * 8 + 0>(st, vs, vlut, w);
+    pv_block<G, VB, S * 8 + 1>(st, vs, vlut, w);
+    pv_block<G, VB, S * 8 + 2>(st, vs, vlut, w);
+    pv_block<G, VB, S * 8 + 3>(st, vs, vlut, w);
+    pv_block<G, VB, S * 8 + 4>(st, vs, vlut, w);
+    pv_block<G, VB, S * 8 + 5>(st, vs, vlut, w);
+    pv_block<G, VB, S * 8 + 6>(st, vs, vlut, w);
+    pv_block<G, VB, S * 8 + 7>(st, vs, vlut, w);
 }
 
 // Load the fp16 weight pairs of quad `quad` (pairs 2quad, 2quad+1) for all heads.
@@ -217,7 +236,8 @@ __device__ __forceinline__ void load_w(uint32_t (&w)[2][G], const uint16_t* wbuf
 }
 
 // Epilogue: merge lanes and waves, write one (o[128], m, l) partial per query head.
-template <int G>
+// STRIDE16: o[h][j] holds dim 16j + lane (lanes 0..15 after the merge); else dim 8*lane + j.
+template <int G, bool STRIDE16 = false>
 __device__ __forceinline__ void write_partial(WaveState<G>& st, float* red /*[4][G][PART]*/, float* part,
                                               int n_parts, int split, int wave, int lane) {
 #pragma unroll
@@ -237,7 +257,7 @@ __device__ __forceinline__ void write_partial(WaveState<G>& st, float* red /*[4]
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) r[h * PART + lane * 8 + j] = st.o[h][j];
+            for (int j = 0; j < 8; ++j) r[h * PART + (STRIDE16 ? 16 * j + lane : lane * 8 + j)] = st.o[h][j];
     }
     if (lane == 0) {
 #pragma unroll
@@ -516,7 +536,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
     __shared__ float s_klut[512];
     __shared__ uint32_t s_vlut[1 << (2 * VB)];
     __shared__ uint32_t s_stage[4][AFFINE_K ? 1 : (R + 1) * TILE];
-    __shared__ uint16_t s_w[4][64 * G];
+    __shared__ __attribute__((aligned(16))) uint16_t s_w[4][64 * G];
     __shared__ float s_red[4 * G * PART];
     __shared__ float s_qp[128 * G];
     __shared__ uint16_t s_dsc[64];
@@ -540,7 +560,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
     constexpr int RK = AFFINE_K ? 16 : R;
 
     // Registers of the tile in flight (prefetched one tile ahead).
-    uint32_t kn[RK], vn[4][VB];
+    uint32_t kn[RK], vn[4 * VB];
     uint16_t ksn[NG], kzn[NG], vsn, vzn;
     auto fetch = [&](int64_t t) {
         const uint32_t* kt = kc + t * (a.k_tile_bytes / 4);
@@ -548,9 +568,10 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < RK; ++k) kn[k] = kt[k * TILE + lane];
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-#pragma unroll
-            for (int c = 0; c < VB; ++c) vn[it][c] = vt[(it * 64 + lane) * VB + c];
+        for (int c4 = 0; c4 < VB; ++c4) {
+            const uint4 v = ((const uint4*)vt)[c4 * 64 + lane];
+            vn[4 * c4] = v.x; vn[4 * c4 + 1] = v.y; vn[4 * c4 + 2] = v.z; vn[4 * c4 + 3] = v.w;
+        }
         const int64_t p = t * TILE + lane < n_packed ? t * TILE + lane : 0;
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
@@ -603,13 +624,11 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
     for (int64_t t = t_lo + wave; t < t_hi; t += 4) {
         const int64_t pos = t * TILE + lane;
         const bool valid = pos < n_packed;
-        uint32_t kr[RK], vr[4][VB];
+        uint32_t kr[RK], vr[4 * VB];
 #pragma unroll
         for (int k = 0; k < RK; ++k) kr[k] = kn[k];
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-#pragma unroll
-            for (int c = 0; c < VB; ++c) vr[it][c] = vn[it][c];
+        for (int c = 0; c < 4 * VB; ++c) vr[c] = vn[c];
         float scl[NG], zer[NG];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
@@ -648,18 +667,13 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) z[hh] = valid ? acc[hh] : -INFINITY;
         wave_lds_fence();
-        softmax_tile<G>(st, z, valid, vsc, vzr, wbuf, lane);
+        softmax_tile<G, true>(st, z, valid, vsc, vzr, wbuf, lane);
         wave_lds_fence();
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            uint32_t w[2][G], cp[16];
-            load_w<G>(w, wbuf, it * 4 + (lane >> 4));
-            vfields_read<VB>(cp, vr[it], s_vlut);
-            pv_dot<G>(st, cp, w);
-        }
+        pv_half<G, VB, 0>(st, vr, s_vlut, (const uint32_t*)wbuf, lane >> 4);
+        pv_half<G, VB, 1>(st, vr, s_vlut, (const uint32_t*)wbuf, lane >> 4);
     }
     __syncthreads();
-    write_partial<G>(st, s_red, part, a.n_parts, split, wave, lane);
+    write_partial<G, true>(st, s_red, part, a.n_parts, split, wave, lane);
 }
 
 
@@ -690,44 +704,72 @@ __global__ __launch_bounds__(256, 2) void k_decode_fp16(const Fp16Args a) {
     write_partial<G>(st, s_red, part, a.n_parts, a.split0 + split, wave, lane);
 }
 
-// Merge split partials (o, m, l) of one (batch, query head) by log-sum-exp: block-wide max, then
-// per-split scale factors in LDS, then each of 256 threads sums one dim over half of the splits.
+// Merge split partials (o, m, l) of one (batch, query head) by log-sum-exp.  Grid: (row, slice of
+// 16 dims); thread s takes splits s, s + 256, ...  The first split's record is loaded together with
+// the maxima so one memory round trip covers the common case (at most 256 splits).
+constexpr int CMB_DIMS = 16;
 __global__ __launch_bounds__(256) void k_combine(const CombineArgs a) {
-    __shared__ float s_sc[BGTQ_MAX_PARTS];
-    __shared__ float s_r[8];
-    __shared__ float s_o[128];
-    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ float s_r[4];
+    __shared__ float s_acc[4][CMB_DIMS + 1];
+    const int row = blockIdx.x, d0 = blockIdx.y * CMB_DIMS, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* pr = a.part + (size_t)row * a.n_parts * PART;
-    float mloc = -INFINITY;
-    for (int s = tid; s < a.n_parts; s += 256) mloc = fmaxf(mloc, pr[s * PART + 128]);
+    const bool has0 = tid < a.n_parts;
+    float4 o0[CMB_DIMS / 4];
+    float m0 = -INFINITY, l0 = 0.f;
+    if (has0) {
+        const float* r = pr + (size_t)tid * PART;
+        m0 = r[128];
+        l0 = r[129];
+#pragma unroll
+        for (int u = 0; u < CMB_DIMS / 4; ++u) o0[u] = *(const float4*)(r + d0 + 4 * u);
+    }
+    float mloc = m0;
+    for (int s = tid + 256; s < a.n_parts; s += 256) mloc = fmaxf(mloc, pr[(size_t)s * PART + 128]);
     mloc = wave_max(mloc);
     if (lane == 0) s_r[wave] = mloc;
     __syncthreads();
     const float M = fmaxf(fmaxf(s_r[0], s_r[1]), fmaxf(s_r[2], s_r[3]));
-    float lloc = 0.f;
-    for (int s = tid; s < a.n_parts; s += 256) {
-        const float m = pr[s * PART + 128];
-        const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-        s_sc[s] = sc;
-        lloc += sc * pr[s * PART + 129];
-    }
-    lloc = wave_sum(lloc);
-    __syncthreads();
-    if (lane == 0) s_r[4 + wave] = lloc;
-    __syncthreads();
-    const float L = (s_r[4] + s_r[5]) + (s_r[6] + s_r[7]);
-    const int j = tid & 127, half = tid >> 7;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    int s = half;
-    for (; s + 6 < a.n_parts; s += 8) {
+    float acc[CMB_DIMS + 1];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] += s_sc[s + 2 * u] * pr[(size_t)(s + 2 * u) * PART + j];
+    for (int j = 0; j <= CMB_DIMS; ++j) acc[j] = 0.f;
+    if (has0 && m0 != -INFINITY) {
+        const float sc = __builtin_amdgcn_exp2f(m0 - M);
+#pragma unroll
+        for (int u = 0; u < CMB_DIMS / 4; ++u) {
+            acc[4 * u] = sc * o0[u].x;
+            acc[4 * u + 1] = sc * o0[u].y;
+            acc[4 * u + 2] = sc * o0[u].z;
+            acc[4 * u + 3] = sc * o0[u].w;
+        }
+        acc[CMB_DIMS] = sc * l0;
     }
-    for (; s < a.n_parts; s += 2) acc[0] += s_sc[s] * pr[(size_t)s * PART + j];
-    const float o = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    if (half == 1) s_o[j] = o;
+    for (int s = tid + 256; s < a.n_parts; s += 256) {
+        const float* r = pr + (size_t)s * PART;
+        const float m = r[128];
+        if (m == -INFINITY) continue;
+        const float sc = __builtin_amdgcn_exp2f(m - M);
+#pragma unroll
+        for (int u = 0; u < CMB_DIMS / 4; ++u) {
+            const float4 o = *(const float4*)(r + d0 + 4 * u);
+            acc[4 * u] += sc * o.x;
+            acc[4 * u + 1] += sc * o.y;
+            acc[4 * u + 2] += sc * o.z;
+            acc[4 * u + 3] += sc * o.w;
+        }
+        acc[CMB_DIMS] += sc * r[129];
+    }
+#pragma unroll
+    for (int j = 0; j <= CMB_DIMS; ++j) acc[j] = wave_sum(acc[j]);
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j <= CMB_DIMS; ++j) s_acc[wave][j] = acc[j];
+    }
     __syncthreads();
-    if (half == 0) a.out[(size_t)row * D + j] = (o + s_o[j]) / L;
+    if (tid < CMB_DIMS) {
+        const float L = (s_acc[0][CMB_DIMS] + s_acc[1][CMB_DIMS]) + (s_acc[2][CMB_DIMS] + s_acc[3][CMB_DIMS]);
+        const float o = (s_acc[0][tid] + s_acc[1][tid]) + (s_acc[2][tid] + s_acc[3][tid]);
+        a.out[(size_t)row * D + d0 + tid] = o / L;
+    }
 }
 
 // Calibration energy sums in fp64: out[h][i] = (sum_t |k_t,blk i|^2, sum_{t,g} |q_t,g,blk i|^2).
@@ -825,6 +867,7 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
     __shared__ int s_order[64];
     __shared__ int s_wid[64];
     __shared__ float s_r[64], s_sig[64];
+    __shared__ uint8_t s_code[64][D];
     for (int i = lane; i < BGTQ_CB_THRESHOLDS; i += 64) s_thr[i] = __builtin_bit_cast(float, c_thr32[i]);
     const size_t bh = (size_t)b * a.Hkv + h;
     const bool do_k = a.which & 1, do_v = (a.which >> 1) & 1;
@@ -902,52 +945,52 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
                 }
             }
         } else {
-            // ---- values: quad layout, 4 lanes share each record
+            // ---- values: lane-stream layout.  Codes of the 64 tokens go through LDS; thread L then
+            // assembles stream L (4*vb dwords).  Bits of tokens before pos_lo are kept (read-modify-
+            // write); tokens at or past pos_hi get zero codes (never written before, appends are
+            // in order).
             const int vb = a.v_bits;
-            uint32_t codes[D];
             uint16_t s16 = 0, z16 = 0;
+            uint8_t* cr = s_code[lane];
             if (a.v_mode == BGTQ_V_CODEBOOK) {
                 const float S = rms_scale16(x, nullptr, &s16);
-                for (int j = 0; j < D; ++j) codes[j] = tq_code(x[j], S, vb, s_thr);
+                for (int j = 0; j < D; ++j) cr[j] = active ? (uint8_t)tq_code(x[j], S, vb, s_thr) : (uint8_t)0;
             } else {
+                uint32_t codes[D];
                 affine_group(x, D, vb, &s16, &z16, codes);
+                for (int j = 0; j < D; ++j) cr[j] = active ? (uint8_t)codes[j] : (uint8_t)0;
             }
             if (active) {
                 a.v_scale[bh * a.n_cap + pos] = s16;
                 if (a.v_mode == BGTQ_V_AFFINE) a.v_zero[bh * a.n_cap + pos] = z16;
             }
-            const int tq = lane & 3;                 // token within quad
-            const int pr = tq >> 1, odd = tq & 1;
-            const int quad = lane >> 2;
-            const int64_t quad_pos = tile * TILE + quad * 4;
-            bool any = false;
-            for (int u = 0; u < 4; ++u) {
-                const int64_t p = quad_pos + u;
-                any |= p >= a.pos_lo[b] && p < a.pos_hi[b];
-            }
-            const bool rmw = quad_pos < a.pos_lo[b];
+            __syncthreads();
+            const int64_t t0 = tile * TILE;
+            const int lo = a.pos_lo[b] > t0 ? (int)(a.pos_lo[b] - t0) : 0;
+            const int dd = lane & 15, jj = lane >> 4;
+            const uint32_t cm = (1u << vb) - 1u;
             uint32_t* vt = (uint32_t*)(a.v_codes + (bh * a.n_tiles + tile) * a.v_tile_bytes);
-            for (int G8 = 0; G8 < 16; ++G8) {
-                uint32_t rec[4] = {0, 0, 0, 0};
-                if (active) {
-                    for (int f8 = 0; f8 < 8; ++f8) {
-                        const int f = pr * 8 + f8;
-                        const int bit = 2 * vb * f + odd * vb;
-                        const uint64_t v = (uint64_t)codes[8 * G8 + f8] << (bit % 32);
-                        rec[bit / 32] |= (uint32_t)v;
-                        if (bit / 32 + 1 < 4) rec[bit / 32 + 1] |= (uint32_t)(v >> 32);
+            for (int c = 0; c < 4 * vb; ++c) {
+                uint64_t val = 0, msk = 0;
+                const int phi0 = (32 * c) / (2 * vb), phi1 = (32 * c + 31) / (2 * vb);
+                for (int phi = phi0; phi <= phi1 && phi < 64; ++phi) {
+                    const int m = phi & 3, db = (phi >> 2) & 7, sh = phi >> 5;
+                    const int p = 16 * sh + 4 * jj + m, dim = 16 * db + dd;
+                    const uint64_t f = (uint64_t)(s_code[p][dim] | ((uint32_t)s_code[p + 32][dim] << vb));
+                    const uint64_t fm = (uint64_t)((p >= lo ? cm : 0u) | (p + 32 >= lo ? cm << vb : 0u));
+                    const int bit = 2 * vb * phi - 32 * c;   // field position relative to dword c
+                    if (bit >= 0) {
+                        val |= f << bit;
+                        msk |= fm << bit;
+                    } else {
+                        val |= f >> -bit;
+                        msk |= fm >> -bit;
                     }
                 }
-                for (int c = 0; c < vb; ++c) {
-                    uint32_t r = rec[c];
-                    r |= __shfl_xor(r, 1, 64);
-                    r |= __shfl_xor(r, 2, 64);
-                    rec[c] = r;
-                }
-                if (tq == 0 && any) {
-                    uint32_t* dst = vt + (quad * 16 + G8) * vb;
-                    for (int c = 0; c < vb; ++c) dst[c] = rmw ? (dst[c] | rec[c]) : rec[c];
-                }
+                const uint32_t v32 = (uint32_t)val, m32 = (uint32_t)msk;
+                uint32_t* dst = vt + ((c >> 2) * 64 + lane) * 4 + (c & 3);
+                if (m32 == 0xFFFFFFFFu) *dst = v32;
+                else if (m32) *dst = (*dst & ~m32) | (v32 & m32);
             }
         }
     }
@@ -971,7 +1014,7 @@ __global__ __launch_bounds__(128) void k_ring(const RingArgs a) {
 // Launchers
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s) {
     if (!a.part || !a.out || a.n_parts < 1 || a.n_parts > BGTQ_MAX_PARTS) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_combine, dim3(rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_combine, dim3(rows, D / CMB_DIMS), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -175,30 +175,37 @@ def test_tile_record_positions():
     assert tiles.view(np.uint32)[1, 3 * 64 + (70 - 64)] == words[70, 3]
 
 
-def test_v_quad_layout_hand_worked():
+def test_v_lane_stream_layout_hand_worked():
+    """Positions worked out by hand from the layout rule (b = 3, 2b = 6-bit fields)."""
     b = 3
-    codes = np.zeros((7, 128), int)
-    codes[0, 17] = 5   # token 0 (quad 0, pair 0, even), dim 17 = group 2, field f = 1
-    codes[1, 17] = 2   # token 1 (odd)
-    codes[2, 3] = 6    # token 2 (quad 0, pair 1, even), dim 3 = group 0, field f = 8 + 3 = 11
-    codes[6, 0] = 7    # token 6 (quad 1, pair 1, even), dim 0: field f = 8
+    codes = np.zeros((60, 128), int)
+    # token 5 = pair p 5 (s 0, j 1, m 1), low half; dim 17 = (db 1, dd 1): lane 17, field 5 at
+    # bit 30 -> straddles stream dwords 0 and 1 -> tile dwords 68 and 69
+    codes[5, 17] = 5
+    # token 40 = p 8 + 32 (s 0, j 2, m 0), high half; dim 127 = (db 7, dd 15): lane 47, field 28
+    # at bit 168 -> stream dword 5 bit 8 -> tile dword (64 + 47)*4 + 1 = 445
+    codes[40, 127] = 6
+    # tokens 20 and 52 = p 20 (s 1, j 1, m 0), both halves; dim 0: lane 16, field 32 at bit 192
+    # -> stream dword 6 bit 0 -> tile dword (64 + 16)*4 + 2 = 322
+    codes[20, 0], codes[52, 0] = 7, 3
     tiles = layout.v_tiles(codes, b, 1).view(np.uint32)[0]
-    # (quad 0, group 2) -> dwords [(0*16+2)*3, +3); field 1 at bit 6: 5 | 2<<3
-    assert tiles[6] == (5 | (2 << 3)) << 6
-    # (quad 0, group 0): field 11 at bit 66 -> dword 2 of the row, bit 2
-    assert tiles[2] == 6 << 2
-    # (quad 1, group 0) -> dword 16*3 = 48; field 8 at bit 48 -> dword 1, bit 16
-    assert tiles[49] == 7 << 16
-    assert np.count_nonzero(tiles) == 3
-    np.testing.assert_array_equal(layout.v_codes(layout.v_tiles(codes, b, 1), b, 7), codes)
+    assert tiles[68] == 1 << 30 and tiles[69] == 1
+    assert tiles[445] == 48 << 8
+    assert tiles[322] == 7 | (3 << 3)
+    assert np.count_nonzero(tiles) == 4
+    np.testing.assert_array_equal(layout.v_codes(layout.v_tiles(codes, b, 1), b, 60), codes)
 
 
-def test_v_straddling_field():
-    """b = 3: field 5 occupies bits 30..35 and straddles dwords 0 and 1 of the row."""
-    codes = np.zeros((2, 128), int)
-    codes[0, 5], codes[1, 5] = 7, 5   # field = 7 | 5 << 3 = 47 = 0b101111
-    tiles = layout.v_tiles(codes, 3, 1).view(np.uint32)[0]
-    assert tiles[0] == (47 & 0b11) << 30 and tiles[1] == 47 >> 2
+def test_v_lane_fields_cover_tile_once():
+    """Every (token, dim) of a tile appears in exactly one field of exactly one lane stream."""
+    seen = np.zeros((64, 128), int)
+    for L in range(64):
+        phis = [phi for phi, _, _ in layout._v_lane_fields(L)]
+        assert sorted(phis) == list(range(64))
+        for _, p, dim in layout._v_lane_fields(L):
+            seen[p, dim] += 1
+            seen[p + 32, dim] += 1
+    assert (seen == 1).all()
 
 
 @pytest.mark.parametrize("b", [1, 2, 3, 4])
