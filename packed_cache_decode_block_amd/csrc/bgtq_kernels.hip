@@ -34,6 +34,8 @@ constexpr float kLog2eOverSqrtD = 0.12751743074233076f;  // log2(e) / sqrt(128)
 __constant__ uint32_t c_cent32[BGTQ_CB_CENTROIDS] = BGTQ_CB_CENTROID_F32_INIT;
 __constant__ uint16_t c_cent16[BGTQ_CB_CENTROIDS] = BGTQ_CB_CENTROID_F16_INIT;
 __constant__ uint32_t c_thr32[BGTQ_CB_THRESHOLDS] = BGTQ_CB_THRESHOLD_F32_INIT;
+// Decode tables for the matrix-core kernel: pair tables of widths 1..5, then the fp16 centroids.
+__constant__ __attribute__((aligned(16))) uint32_t c_mxtab[BGTQ_CB_MX_WORDS] = BGTQ_CB_MX_INIT;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -235,6 +237,26 @@ __device__ __forceinline__ void load_w(uint32_t (&w)[2][G], const uint16_t* wbuf
         for (int h = 0; h < G; ++h) w[p][h] = wb[p * G + h];
 }
 
+// Merge the four waves' (o, m, l, zero term) records in red[wave][h] into one partial per head:
+// part[h][split] = (sum_w e^(m_w - M) (o_w + zs_w), M, sum_w e^(m_w - M) l_w).
+template <int G>
+__device__ __forceinline__ void merge_waves(const float* red, float* part, int n_parts, int split) {
+    for (int idx = threadIdx.x; idx < G * 130; idx += blockDim.x) {
+        const int h = idx / 130, j = idx % 130;
+        float M = -INFINITY;
+        for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, red[(wv * G + h) * PART + 128]);
+        float acc = 0.f;
+        for (int wv = 0; wv < 4; ++wv) {
+            const float* rw = red + (wv * G + h) * PART;
+            const float sc = (rw[128] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rw[128] - M);
+            if (j < 128) acc += sc * (rw[j] + rw[130]);
+            else if (j == 129) acc += sc * rw[129];
+        }
+        float* dst = part + ((size_t)h * n_parts + split) * PART;
+        dst[j] = (j == 128) ? M : acc;
+    }
+}
+
 // Epilogue: merge lanes and waves, write one (o[128], m, l) partial per query head.
 // STRIDE16: o[h][j] holds dim 16j + lane (lanes 0..15 after the merge); else dim 8*lane + j.
 template <int G, bool STRIDE16 = false>
@@ -268,20 +290,7 @@ __device__ __forceinline__ void write_partial(WaveState<G>& st, float* red /*[4]
         }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < G * 130; idx += blockDim.x) {
-        const int h = idx / 130, j = idx % 130;
-        float M = -INFINITY;
-        for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, red[(wv * G + h) * PART + 128]);
-        float acc = 0.f;
-        for (int wv = 0; wv < 4; ++wv) {
-            const float* rw = red + (wv * G + h) * PART;
-            const float sc = (rw[128] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rw[128] - M);
-            if (j < 128) acc += sc * (rw[j] + rw[130]);
-            else if (j == 129) acc += sc * rw[129];
-        }
-        float* dst = part + ((size_t)h * n_parts + split) * PART;
-        dst[j] = (j == 128) ? M : acc;
-    }
+    merge_waves<G>(red, part, n_parts, split);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -458,19 +467,75 @@ __device__ void fp16_tiles(WaveState<G>& st, const uint16_t* K16, const uint16_t
 //  dsc16[s]: slot descriptor (start dword | bit offset << 5 | width << 10); padding = width 1 at 0.
 //  qs[g*G + h]: per-key-group sums of the natural scaled query (affine keys).
 // The block order comes from nine wave ballots (one per width) instead of a sort.
+// Global inputs of the preparation (lane = RoPE block), loaded raw and converted later so a kernel
+// can issue them, then its tile prefetch, before anything waits on them.
+template <int G> struct PrepIn {
+    uint32_t r0[G], r1[G];  // fp32 bits of (q_2i, q_2i+1), or the packed 16-bit pair in r0
+    float sg;
+    uint32_t w4;  // the dword of the width array holding this block's width (byte lane & 3)
+    int dtype;
+};
+
+template <int G, bool SORTED>
+__device__ __forceinline__ PrepIn<G> prep_load(const void* q, int dtype, const uint8_t* bits, const float* sigma, int b,
+                                               int h, int Hq, int lane) {
+    PrepIn<G> in;
+    in.dtype = dtype;
+    in.w4 = 0u;
+    in.sg = 0.f;
+    if constexpr (SORTED) {
+        in.w4 = ((const uint32_t*)(bits + h * 64))[lane >> 2];
+        in.sg = sigma[h * 64 + lane];
+    }
+    const int64_t row0 = ((int64_t)b * Hq + (int64_t)h * G) * D + 2 * lane;
+    if (dtype == BGTQ_F32) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            const uint2 v = *(const uint2*)((const float*)q + row0 + (int64_t)hh * D);
+            in.r0[hh] = v.x;
+            in.r1[hh] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            in.r0[hh] = *(const uint32_t*)((const uint16_t*)q + row0 + (int64_t)hh * D);
+            in.r1[hh] = 0u;
+        }
+    }
+    return in;
+}
+
 template <int G, bool SORTED, int KG>
-__device__ void prep_wave(const void* q, int dtype, const uint8_t* bits, const float* sigma, int b, int h,
-                          int Hq, int lane, float* qp, uint16_t* dsc16, uint32_t* nnz_pad, float* qs) {
+__device__ void prep_store(const PrepIn<G>& in, int lane, float* qp, uint16_t* dsc16, uint32_t* nnz_pad, float* qs) {
     float q0[G], q1[G];
+    if (in.dtype == BGTQ_F32) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            q0[hh] = __builtin_bit_cast(float, in.r0[hh]);
+            q1[hh] = __builtin_bit_cast(float, in.r1[hh]);
+        }
+    } else if (in.dtype == BGTQ_F16) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            q0[hh] = h2f(in.r0[hh] & 0xFFFFu);
+            q1[hh] = h2f(in.r0[hh] >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            q0[hh] = bf2f(in.r0[hh] & 0xFFFFu);
+            q1[hh] = bf2f(in.r0[hh] >> 16);
+        }
+    }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-        const int64_t base = ((int64_t)b * Hq + (int64_t)h * G + hh) * D + 2 * lane;
-        q0[hh] = load_act(q, base, dtype) * kLog2eOverSqrtD;
-        q1[hh] = load_act(q, base + 1, dtype) * kLog2eOverSqrtD;
+        q0[hh] *= kLog2eOverSqrtD;
+        q1[hh] *= kLog2eOverSqrtD;
     }
     if constexpr (SORTED) {
-        const int w = bits[h * 64 + lane];
-        const float sg = sigma[h * 64 + lane];
+        const int bw = (int)((in.w4 >> (8 * (lane & 3))) & 0xFFu);
+        const int w = bw < 8 ? bw : 8;  // widths above 8 are invalid; clamp
+        const float sg = in.sg;
         const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
         int rank = 0, pos = 0, nnz = 0;
 #pragma unroll
@@ -518,6 +583,12 @@ __device__ void prep_wave(const void* q, int dtype, const uint8_t* bits, const f
             }
         }
     }
+}
+
+template <int G, bool SORTED, int KG>
+__device__ void prep_wave(const void* q, int dtype, const uint8_t* bits, const float* sigma, int b, int h,
+                          int Hq, int lane, float* qp, uint16_t* dsc16, uint32_t* nnz_pad, float* qs) {
+    prep_store<G, SORTED, KG>(prep_load<G, SORTED>(q, dtype, bits, sigma, b, h, Hq, lane), lane, qp, dsc16, nnz_pad, qs);
 }
 
 template <int G>
@@ -676,6 +747,372 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
     write_partial<G, true>(st, s_red, part, a.n_parts, split, wave, lane);
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Matrix-core decode for g >= 4 query heads per kv head.  The g heads share every dequantized key
+// and value, so per 64-token tile q·K^T is a (g x 128) x (128 x 64) product and P·V a
+// (g x 64) x (64 x 128) product: v_mfma_f32_16x16x32_f16 takes both and the vector ALUs only
+// unpack codes and run the softmax.
+//  * A = Q' (16 rows x 32 K): row 4u + e is head 2u + e/2, with e even the fp16 high part and e odd
+//    the fp16 low part of q' = q * sigma * log2(e)/sqrt(d) (hi + lo carries ~22 bits).  Centroids
+//    are fp16 values exactly, so the products lose nothing and the MFMA sums in fp32.
+//  * B = K^ (32 K x 16 tokens): lane = token extracts 16 slots per k-step as fp16 centroid pairs
+//    (wave-uniform slot offsets, pair tables for widths <= 5, per-coordinate tables above), then
+//    two permlane swaps transpose the 4 x 4 blocks (token group x slot group) into operand order.
+//  * C (16 x 16 tokens): lane (token 16g + r, row group u) holds heads 2u, 2u + 1 as (hi, lo).
+//  * P·V: A = V^T (16 dims x 32 tokens) straight from the lane-stream value fields, B = W (32 tokens
+//    x 16 heads) through LDS in pair order (t, t + 32); O^T accumulates per 16-dim block.
+//  * online softmax with the exact running max per head (a wave-uniform branch raises it), so the
+//    largest weight of a split is fp16(scale) exactly, whatever the split boundaries.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+
+__device__ __forceinline__ half8_t as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const u32x4_t v = {a, b, c, d};
+    return __builtin_bit_cast(half8_t, v);
+}
+__device__ __forceinline__ f32x4_t mfma16(half8_t a, half8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// x.rows{2,3} <-> y.rows{0,1} (lanes 32..63 of x with lanes 0..31 of y)
+__device__ __forceinline__ void swap32(uint32_t& x, uint32_t& y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+}
+// x.rows{1,3} <-> y.rows{0,2}
+__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+}
+
+// 16 slots 16*KS + i of this lane's token as fp16 centroid pairs, transposed into B operands:
+// P[4g .. 4g+3] = slot group (lane row) of token group g.  A slot descriptor is start dword | bit
+// offset << 5 | width << 10.  All window reads are issued first, then all table reads (pair tables
+// for groups of four slots whose widest slot is <= 5, two per-coordinate reads otherwise), so one
+// LDS wait covers the k-step.
+template <int KS>
+__device__ __forceinline__ void mx_slots(uint32_t (&P)[16], const uint32_t* dsc, const uint32_t* stage, uint32_t li,
+                                         const uint32_t* pairs, const _Float16* c16) {
+    uint32_t x[16];
+    {
+        uint32_t lo[16], hi[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t k = dsc16(dsc, 16 * KS + i) & 31u;
+            lo[i] = stage[k * TILE + li];
+            hi[i] = stage[(k + 1) * TILE + li];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_alignbit(hi[i], lo[i], (dsc16(dsc, 16 * KS + i) >> 5) & 31u);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if ((dsc16(dsc, 16 * KS + 4 * q) >> 10) <= 5u) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w = dsc16(dsc, 16 * KS + 4 * q + i) >> 10;
+                P[4 * q + i] = pairs[((1u << (2 * w)) - 4u) / 3u + (x[4 * q + i] & ((1u << (2 * w)) - 1u))];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w = dsc16(dsc, 16 * KS + 4 * q + i) >> 10, m = (1u << w) - 1u;
+                const _Float16* t = c16 + ((1u << w) - 2u);
+                half2_t v;
+                v[0] = t[x[4 * q + i] & m];
+                v[1] = t[__builtin_amdgcn_ubfe(x[4 * q + i], w, w)];
+                P[4 * q + i] = __builtin_bit_cast(uint32_t, v);
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        swap32(P[m], P[8 + m]);
+        swap32(P[4 + m], P[12 + m]);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        swap16(P[m], P[4 + m]);
+        swap16(P[8 + m], P[12 + m]);
+    }
+}
+
+template <int KS>
+__device__ __forceinline__ void mx_qk(f32x4_t (&c)[4], const half8_t (&qa)[4], const uint32_t* dsc, const uint32_t* stage,
+                                      uint32_t li, const uint32_t* pairs, const _Float16* c16) {
+    uint32_t P[16];
+    mx_slots<KS>(P, dsc, stage, li, pairs, c16);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) c[g] = mfma16(qa[KS], as_h8(P[4 * g], P[4 * g + 1], P[4 * g + 2], P[4 * g + 3]), c[g]);
+}
+
+// P·V of one 32-token half S: B = W rows of this lane's head column, A = value fields (S, db, m).
+template <int VB, int S>
+__device__ __forceinline__ void mx_pv(f32x4_t (&o)[8], const uint32_t* vs, const uint32_t* vlut, const uint32_t* wx,
+                                      int lane) {
+    const u32x4_t wq = *(const u32x4_t*)(wx + (lane & 15) * 32 + 16 * S + 4 * (lane >> 4));
+    const half8_t wb = __builtin_bit_cast(half8_t, wq);
+    o[0] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 0) * 4>(vs)], vlut[vfield<VB, (S * 8 + 0) * 4 + 1>(vs)],
+                        vlut[vfield<VB, (S * 8 + 0) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 0) * 4 + 3>(vs)]), wb, o[0]);
+    o[1] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 1) * 4>(vs)], vlut[vfield<VB, (S * 8 + 1) * 4 + 1>(vs)],
+                        vlut[vfield<VB, (S * 8 + 1) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 1) * 4 + 3>(vs)]), wb, o[1]);
+    o[2] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 2) * 4>(vs)], vlut[vfield<VB, (S * 8 + 2) * 4 + 1>(vs)],
+                        vlut[vfield<VB, (S * 8 + 2) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 2) * 4 + 3>(vs)]), wb, o[2]);
+    o[3] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 3) * 4>(vs)], vlut[vfield<VB, (S * 8 + 3) * 4 + 1>(vs)],
+                        vlut[vfield<VB, (S * 8 + 3) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 3) * 4 + 3>(vs)]), wb, o[3]);
+    o[4] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 4) * 4>(vs)], vlut[vfield<VB, (S * 8 + 4) * 4 + 1>(vs)],
+                        vlut[vfield<VB, (S * 8 + 4) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 4) * 4 + 3>(vs)]), wb, o[4]);
+    o[5] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 5) * 4>(vs)], vlut[vfield<VB, (S * 8 + 5) * 4 + 1>(vs)],
+                        vlut[vfield<VB, (S * 8 + 5) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 5) * 4 + 3>(vs)]), wb, o[5]);
+    o[6] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 6) * 4>(vs)], vlut[vfield<VB, (S * 8 + 6) * 4 + 1>(vs)],
+                        vlut[vfield<VB, (S * 8 + 6) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 6) * 4 + 3>(vs)]), wb, o[6]);
+    o[7] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 7) * 4>(vs)], vlut[vfield<VB, (S * 8 + 7) * 4 + 1>(vs)],
+                        vlut[vfield<VB, (S * 8 + 7) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 7) * 4 + 3>(vs)]), wb, o[7]);
+}
+
+// Max over the 16 lanes of a row (DPP row rotations).
+__device__ __forceinline__ float row_max16(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false)));
+    return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false));
+    return v;
+}
+
+template <int G, int R, int VB>
+__global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
+    static_assert(G == 4 || G == 8, "matrix-core decode serves 4 or 8 query heads per kv head");
+    static_assert(R % 4 == 0, "K records are staged in 16-byte chunks");
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row = lane >> 4, col = lane & 15;
+    __shared__ __attribute__((aligned(16))) uint32_t s_tab[BGTQ_CB_MX_WORDS];
+    __shared__ uint32_t s_vlut[1 << (2 * VB)];
+    __shared__ __attribute__((aligned(16))) uint32_t s_stage[4][(R + 1) * TILE];
+    __shared__ __attribute__((aligned(16))) uint32_t s_wx[4][16 * 32];
+    __shared__ float s_alpha[4][16];
+    __shared__ float s_red[4 * G * PART];
+    __shared__ float s_qp[128 * G];
+    __shared__ uint16_t s_dsc[64];
+    __shared__ uint32_t s_nnz;
+    const uint32_t* s_pair = s_tab;
+    const _Float16* s_c16 = (const _Float16*)(s_tab + BGTQ_CB_PAIR_ENTRIES);
+
+    const size_t bh = (size_t)b * a.Hkv + h;
+    const int64_t n_packed = a.n_packed[b];
+    const int64_t n_tiles_b = (n_packed + TILE - 1) / TILE;
+    const int64_t t_lo = (int64_t)split * a.tiles_per_split;
+    const int64_t t_hi = t_lo + a.tiles_per_split < n_tiles_b ? t_lo + a.tiles_per_split : n_tiles_b;
+    const uint32_t* kc = (const uint32_t*)(a.k_codes + bh * a.n_tiles * a.k_tile_bytes);
+    const uint32_t* vc = (const uint32_t*)(a.v_codes + bh * a.n_tiles * a.v_tile_bytes);
+    const uint16_t* ksc = a.k_scale + bh * a.n_cap;
+    const uint16_t* vsc = a.v_scale + bh * a.n_cap;
+    const uint16_t* vzr = a.v_affine ? a.v_zero + bh * a.n_cap : nullptr;
+    uint32_t* stage = s_stage[wave];
+    uint32_t* wx = s_wx[wave];
+
+    // Prologue.  Global loads of the tables and of the query go out first, then the first tile's
+    // prefetch; loads retire in order, so the table and query writes below do not wait for HBM.
+    constexpr int TAB4 = BGTQ_CB_MX_WORDS / 4;
+    const u32x4_t* tab4 = (const u32x4_t*)c_mxtab;
+    // Loads are unconditional (clamped indices) so that no branch forces an early wait.
+    u32x4_t tv[(TAB4 + 255) / 256];
+#pragma unroll
+    for (int k = 0; k < (TAB4 + 255) / 256; ++k)
+        tv[k] = tab4[threadIdx.x + 256 * k < TAB4 ? threadIdx.x + 256 * k : 0];
+    const uint32_t vca = threadIdx.x & ((1 << VB) - 1), vcb = (threadIdx.x >> VB) & ((1 << VB) - 1);
+    const uint32_t vla = c_cent16[cent_base(VB) + vca], vlb = c_cent16[cent_base(VB) + vcb];
+    const PrepIn<G> pin = prep_load<G, true>(a.q, a.q_dtype, a.bits, a.sigma, b, h, a.Hq, lane);
+
+    // Tile in flight: K chunks (staged to LDS on arrival), value stream, scales of the four tokens
+    // 16g + col this lane owns in the softmax.
+    u32x4_t kn[R / 4], vn[VB];
+    uint16_t skn[4], svn[4], szn[4];
+    auto fetch = [&](int64_t t) {
+        const u32x4_t* kt = (const u32x4_t*)(kc + t * (a.k_tile_bytes / 4));
+        const u32x4_t* vt = (const u32x4_t*)(vc + t * (a.v_tile_bytes / 4));
+#pragma unroll
+        for (int c = 0; c < R / 4; ++c) kn[c] = kt[c * 64 + lane];
+#pragma unroll
+        for (int c = 0; c < VB; ++c) vn[c] = vt[c * 64 + lane];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int64_t p = t * TILE + 16 * g + col < n_packed ? t * TILE + 16 * g + col : 0;
+            skn[g] = ksc[p];
+            svn[g] = vsc[p];
+            szn[g] = vzr ? vzr[p] : (uint16_t)0;
+        }
+    };
+    // Unconditional (branch-free prologue); a wave without tiles reads a tile inside the allocation
+    // and never uses it.
+    fetch(t_lo + wave < t_hi ? t_lo + wave : (t_lo < a.n_tiles ? t_lo : 0));
+
+#pragma unroll
+    for (int k = 0; k < (TAB4 + 255) / 256; ++k)
+        if (threadIdx.x + 256 * k < TAB4) ((u32x4_t*)s_tab)[threadIdx.x + 256 * k] = tv[k];
+    if (threadIdx.x < (1 << (2 * VB)))
+        s_vlut[threadIdx.x] = a.v_affine ? (uint32_t)f2h((float)vca) | ((uint32_t)f2h((float)vcb) << 16) : vla | (vlb << 16);
+    for (int i = threadIdx.x; i < 4 * 16 * 32; i += blockDim.x) (&s_wx[0][0])[i] = 0u;
+    for (int i = threadIdx.x; i < 4 * TILE; i += blockDim.x) s_stage[i >> 6][R * TILE + (i & 63)] = 0u;
+    if (wave == 0) prep_store<G, true, 0>(pin, lane, s_qp, s_dsc, &s_nnz, nullptr);
+    __syncthreads();
+
+    uint32_t dsc[32];
+    {
+        const uint32_t* d32 = (const uint32_t*)s_dsc;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) dsc[i] = __builtin_amdgcn_readfirstlane(d32[i]);
+    }
+    const int nks = (int)((__builtin_amdgcn_readfirstlane(s_nnz) + 15u) >> 4);  // s_nnz: nonzero slots rounded up to 4
+
+    // Query operands: lane (row col = head part, K group row): slot 16ks + 4row + e/2, coord e%2.
+    half8_t qa[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int sl = 16 * ks + 4 * row + (e >> 1), hd = col >> 1;
+            const float qv = hd < G ? s_qp[sl * 2 * G + (e & 1) * G + hd] : 0.f;
+            const _Float16 hi = (_Float16)qv;
+            const _Float16 lo = (_Float16)(qv - (float)hi);
+            qa[ks][e] = (col & 1) ? lo : hi;
+        }
+    }
+
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, zs[2] = {0.f, 0.f};
+    f32x4_t o[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t t = t_lo + wave; t < t_hi; t += 4) {
+        wave_lds_fence();
+#pragma unroll
+        for (int c = 0; c < R / 4; ++c) ((u32x4_t*)stage)[c * 64 + lane] = kn[c];
+        wave_lds_fence();
+        u32x4_t vr[VB];
+#pragma unroll
+        for (int c = 0; c < VB; ++c) vr[c] = vn[c];
+        float sk[4], sv[4], sz[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            sk[g] = h2f(skn[g]);
+            sv[g] = h2f(svn[g]);
+            sz[g] = h2f(szn[g]);
+        }
+        asm volatile("" ::: "memory");
+        if (t + 4 < t_hi) fetch(t + 4);
+
+        // q·k on the matrix cores
+        f32x4_t c[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) c[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // Slot descriptors are re-read each tile so their scalar decode is not hoisted (it would
+        // not fit in SGPRs for 64 slots).
+#pragma unroll
+        for (int i = 0; i < 32; ++i) asm volatile("" : "+s"(dsc[i]));
+        uint32_t li = lane;
+        asm volatile("" : "+v"(li));
+        if (nks > 0) mx_qk<0>(c, qa, dsc, stage, li, s_pair, s_c16);
+        if (nks > 1) mx_qk<1>(c, qa, dsc, stage, li, s_pair, s_c16);
+        if (nks > 2) mx_qk<2>(c, qa, dsc, stage, li, s_pair, s_c16);
+        if (nks > 3) mx_qk<3>(c, qa, dsc, stage, li, s_pair, s_c16);
+
+        // softmax over the tile: lane holds tokens 16g + col, heads 2row, 2row + 1
+        float z[4][2], tmax[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const bool valid = t * TILE + 16 * g + col < n_packed;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                z[g][hh] = valid ? sk[g] * (c[g][2 * hh] + c[g][2 * hh + 1]) : -INFINITY;
+                tmax[hh] = fmaxf(tmax[hh], z[g][hh]);
+            }
+        }
+        if (__ballot(tmax[0] > m[0] || tmax[1] > m[1])) {
+            float alpha[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const float mn = fmaxf(m[hh], row_max16(tmax[hh]));
+                alpha[hh] = __builtin_amdgcn_exp2f(m[hh] - mn);
+                m[hh] = mn;
+                l[hh] *= alpha[hh];
+                zs[hh] *= alpha[hh];
+            }
+            wave_lds_fence();
+            if (col == 0) {
+                s_alpha[wave][2 * row] = alpha[0];
+                s_alpha[wave][2 * row + 1] = alpha[1];
+            }
+            wave_lds_fence();
+            const float al = s_alpha[wave][col];
+#pragma unroll
+            for (int db = 0; db < 8; ++db) o[db] *= al;
+        }
+        uint16_t wh[4][2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const float p = __builtin_amdgcn_exp2f(z[g][hh] - m[hh]);
+                l[hh] += p;
+                zs[hh] += p * sz[g];
+                wh[g][hh] = f2h(p * sv[g]);
+            }
+        }
+        wave_lds_fence();
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            uint32_t* wr = wx + (2 * row + hh) * 32 + col;
+            wr[0] = (uint32_t)wh[0][hh] | ((uint32_t)wh[2][hh] << 16);
+            wr[16] = (uint32_t)wh[1][hh] | ((uint32_t)wh[3][hh] << 16);
+        }
+        wave_lds_fence();
+
+        // P·V on the matrix cores
+        const uint32_t* vs = (const uint32_t*)vr;
+        mx_pv<VB, 0>(o, vs, s_vlut, wx, lane);
+        mx_pv<VB, 1>(o, vs, s_vlut, wx, lane);
+    }
+
+    // Epilogue: row sums of l and the zero term, O^T to LDS, merge the four waves.
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        l[hh] = row_sum16(l[hh]);
+        zs[hh] = row_sum16(zs[hh]);
+    }
+    float* r = s_red + wave * G * PART;
+    if (col < G) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[col * PART + 16 * db + 4 * row + e] = o[db][e];
+    }
+    if (col == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int hd = 2 * row + hh;
+            if (hd < G) {
+                r[hd * PART + 128] = m[hh];
+                r[hd * PART + 129] = l[hh];
+                r[hd * PART + 130] = zs[hh];
+            }
+        }
+    }
+    __syncthreads();
+    float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_parts * PART;
+    merge_waves<G>(s_red, part, a.n_parts, split);
+}
 
 // fp16 tiles: the unquantized comparator over [B][Hkv][N][128], and the fp16 recent ring of a packed
 // cache (one split, concatenated order-free with the packed tokens).
@@ -873,7 +1310,7 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
     const bool do_k = a.which & 1, do_v = (a.which >> 1) & 1;
     int nnz = 0;
     if (do_k && a.k_mode == BGTQ_K_BLOCKGTQ) {
-        const int w = a.bits[h * 64 + lane];
+        const int w = a.bits[h * 64 + lane] < 8 ? a.bits[h * 64 + lane] : 8;  // widths above 8 are invalid; clamp
         s_wid[lane] = w;
         s_r[lane] = a.inv_sigma[h * 64 + lane];
         s_sig[lane] = a.sigma[h * 64 + lane];
@@ -1058,6 +1495,12 @@ static hipError_t launch_dec(const DecodeArgs& a, int B, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int G, int R, int VB>
+static hipError_t launch_dec_mx(const DecodeArgs& a, int B, hipStream_t s) {
+    hipLaunchKernelGGL((k_decode_mx<G, R, VB>), dim3(a.n_splits, a.Hkv, B), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int G, int VB>
 static hipError_t launch_dec_gv(const DecodeArgs& a, int B, int k_mode, int R, hipStream_t s) {
     if (k_mode == BGTQ_K_AFFINE) {
@@ -1065,6 +1508,14 @@ static hipError_t launch_dec_gv(const DecodeArgs& a, int B, int k_mode, int R, h
             case 32: return launch_dec<G, 16, VB, 32>(a, B, s);
             case 64: return launch_dec<G, 16, VB, 64>(a, B, s);
             case 128: return launch_dec<G, 16, VB, 128>(a, B, s);
+        }
+        return hipErrorInvalidValue;
+    }
+    if constexpr (G >= 4) {
+        switch (R) {
+            case 8: return launch_dec_mx<G, 8, VB>(a, B, s);
+            case 12: return launch_dec_mx<G, 12, VB>(a, B, s);
+            case 16: return launch_dec_mx<G, 16, VB>(a, B, s);
         }
         return hipErrorInvalidValue;
     }

@@ -172,6 +172,24 @@ int main(int argc, char** argv) {
     std::fprintf(f, "}\n#define BGTQ_CB_THRESHOLD_F32_INIT {");
     for (size_t i = 0; i < thr.size(); ++i) std::fprintf(f, "%s0x%08" PRIx32 "u", i ? "," : "", thr[i]);
     std::fprintf(f, "}\n");
+    // Decode-side LDS image: pair tables for widths 1..5 (entry a | b << w = fp16 c[a] | fp16 c[b] << 16,
+    // table of width w at entry (4^w - 4) / 3), then every fp16 centroid, two per dword.
+    std::vector<uint32_t> img;
+    for (int w = 1; w <= 5; ++w) {
+        const int cb = (1 << w) - 2;
+        for (int idx = 0; idx < (1 << (2 * w)); ++idx)
+            img.push_back((uint32_t)cent[cb + (idx & ((1 << w) - 1))] | ((uint32_t)cent[cb + (idx >> w)] << 16));
+    }
+    const size_t n_pair = img.size();
+    for (size_t i = 0; i < 512; i += 2) {
+        const uint32_t lo = i < cent.size() ? cent[i] : 0u, hi = i + 1 < cent.size() ? cent[i + 1] : 0u;
+        img.push_back(lo | (hi << 16));
+    }
+    while (img.size() % 4) img.push_back(0u);
+    std::fprintf(f, "#define BGTQ_CB_PAIR_ENTRIES %zu\n#define BGTQ_CB_MX_WORDS %zu\n#define BGTQ_CB_MX_INIT {", n_pair,
+                 img.size());
+    for (size_t i = 0; i < img.size(); ++i) std::fprintf(f, "%s0x%08" PRIx32 "u", i ? "," : "", img[i]);
+    std::fprintf(f, "}\n");
     std::fclose(f);
     return 0;
 }
