@@ -51,7 +51,8 @@ enum { BGTQ_V_CODEBOOK = 0, BGTQ_V_AFFINE = 1 };            /* value formats */
 enum {
     BGTQ_BUF_K_CODES = 0, BGTQ_BUF_V_CODES = 1, BGTQ_BUF_K_SCALE = 2, BGTQ_BUF_K_ZERO = 3,
     BGTQ_BUF_V_SCALE = 4, BGTQ_BUF_V_ZERO = 5, BGTQ_BUF_RECENT_K = 6, BGTQ_BUF_RECENT_V = 7,
-    BGTQ_BUF_META = 8         /* bits + sigma + inv_sigma, for reference */
+    BGTQ_BUF_META = 8,        /* bits + sigma + inv_sigma, for reference */
+    BGTQ_BUF_SLOTS = 9        /* slot table (Block-GTQ keys; 0 bytes otherwise) */
 };
 
 #define BGTQ_HEAD_DIM 128
@@ -86,6 +87,10 @@ enum {
  *   bits      uint8 [L][Hkv][64]   widths (BLOCKGTQ), from bgtq_allocate
  *   sigma     fp32  [L][Hkv][64]   per-block key scale sigma_i = sqrt(E_k[i]/2)
  *   inv_sigma fp32  [L][Hkv][64]   fp32(1/sigma_i), 0 for a dead block
+ *   slots     uint32 [L][Hkv][64]  Block-GTQ only, else NULL: the record position of each
+ *     nonzero block in width order, derived from bits.  bgtq_quantize_append writes it (every
+ *     call, for the layer it appends to); bgtq_decode_attention reads it.  Contents are private
+ *     to the library; changing bits after an append requires appending again before decoding.
  * Host state:
  *   n_tokens  int64 [L][B] host array: tokens appended so far per (layer, sequence) (packed +
  *     recent).  bgtq_quantize_append advances it on success only.
@@ -95,9 +100,11 @@ enum {
  *   record: blocks by width descending (ties: lower index first), width-0 blocks omitted; block i
  *   of width w holds code(2i) then code(2i+1), w bits each.  Affine: coordinate j at bits
  *   [k_bits*j, +k_bits).  Tile = dword-major, token-minor: dword k of token t at byte (k*64+t)*4.
- *   V tile = 16 token quads x 16 groups of 8 dims x v_bits dwords (quad-major).  The v_bits dwords
- *   of (quad q, group G) hold 16 fields of 2*v_bits bits, field f at bit 2*v_bits*f: token pair
- *   2q + f/8, dim 8G + f%8; low half = even token's code, high half = odd token's code.
+ *   V tile ("lane streams"): 64 streams of 4*v_bits dwords, stream L = dd + 16j (dd 0..15,
+ *   j 0..3) holding 64 fields of 2*v_bits bits, field phi = (s*8 + db)*4 + m (s 0..1, db 0..7,
+ *   m 0..3) at bit 2*v_bits*phi: the codes of dim 16db + dd for tokens p and p + 32,
+ *   p = 16s + 4j + m, token p in the low half.  Stream dword c is tile dword
+ *   ((c/4)*64 + L)*4 + c%4.
  */
 typedef struct bgtq_cache {
     int32_t L, B, Hq, Hkv, d;
@@ -108,6 +115,7 @@ typedef struct bgtq_cache {
     void *k_codes, *v_codes, *k_scale, *k_zero, *v_scale, *v_zero, *recent_k, *recent_v;
     const uint8_t *bits;
     const float *sigma, *inv_sigma;
+    uint32_t *slots;
     int64_t *n_tokens;
 } bgtq_cache;
 

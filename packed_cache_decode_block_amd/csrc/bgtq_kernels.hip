@@ -36,6 +36,7 @@ __constant__ uint16_t c_cent16[BGTQ_CB_CENTROIDS] = BGTQ_CB_CENTROID_F16_INIT;
 __constant__ uint32_t c_thr32[BGTQ_CB_THRESHOLDS] = BGTQ_CB_THRESHOLD_F32_INIT;
 // Decode tables for the matrix-core kernel: pair tables of widths 1..5, then the fp16 centroids.
 __constant__ __attribute__((aligned(16))) uint32_t c_mxtab[BGTQ_CB_MX_WORDS] = BGTQ_CB_MX_INIT;
+constexpr uint32_t SLOT_COORD0 = 4u * BGTQ_CB_PAIR_ENTRIES;  // byte offset of the fp16 centroids in that image
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -765,6 +766,9 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
 //  * online softmax with the exact running max per head (a wave-uniform branch raises it), so the
 //    largest weight of a split is fp16(scale) exactly, whatever the split boundaries.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+// Read-only global data the kernel never writes, read through the constant address space so
+// uniform loads become scalar loads.
+typedef __attribute__((address_space(4))) uint32_t cu32_t;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -790,41 +794,42 @@ __device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
 }
 
 // 16 slots 16*KS + i of this lane's token as fp16 centroid pairs, transposed into B operands:
-// P[4g .. 4g+3] = slot group (lane row) of token group g.  A slot descriptor is start dword | bit
-// offset << 5 | width << 10.  All window reads are issued first, then all table reads (pair tables
-// for groups of four slots whose widest slot is <= 5, two per-coordinate reads otherwise), so one
-// LDS wait covers the k-step.
+// P[4g .. 4g+3] = slot group (lane row) of token group g.  Slot entries {row offset, bit offset,
+// W, B} come from the slot table in scalar registers.  All window reads are issued first, then
+// all table reads, so one LDS wait covers the k-step.
 template <int KS>
-__device__ __forceinline__ void mx_slots(uint32_t (&P)[16], const uint32_t* dsc, const uint32_t* stage, uint32_t li,
-                                         const uint32_t* pairs, const _Float16* c16) {
+__device__ __forceinline__ void mx_slots(uint32_t (&P)[16], const cu32_t* sd, const uint8_t* stage, uint32_t li4,
+                                         const uint8_t* tab) {
+    uint32_t D[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) D[i] = sd[16 * KS + i];  // one scalar load of the k-step's entries
     uint32_t x[16];
     {
         uint32_t lo[16], hi[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const uint32_t k = dsc16(dsc, 16 * KS + i) & 31u;
-            lo[i] = stage[k * TILE + li];
-            hi[i] = stage[(k + 1) * TILE + li];
+            const uint8_t* rp = stage + (D[i] & 0xF00u) + li4;
+            lo[i] = *(const uint32_t*)rp;
+            hi[i] = *(const uint32_t*)(rp + 4 * TILE);
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_alignbit(hi[i], lo[i], (dsc16(dsc, 16 * KS + i) >> 5) & 31u);
+        for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_alignbit(hi[i], lo[i], D[i]);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        if ((dsc16(dsc, 16 * KS + 4 * q) >> 10) <= 5u) {
+        if ((D[4 * q] >> 16) < SLOT_COORD0) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t w = dsc16(dsc, 16 * KS + 4 * q + i) >> 10;
-                P[4 * q + i] = pairs[((1u << (2 * w)) - 4u) / 3u + (x[4 * q + i] & ((1u << (2 * w)) - 1u))];
+                const uint32_t d = D[4 * q + i];
+                P[4 * q + i] = *(const uint32_t*)(tab + (d >> 16) + 4u * __builtin_amdgcn_ubfe(x[4 * q + i], 0, (d >> 12) & 15u));
             }
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t w = dsc16(dsc, 16 * KS + 4 * q + i) >> 10, m = (1u << w) - 1u;
-                const _Float16* t = c16 + ((1u << w) - 2u);
+                const uint32_t d = D[4 * q + i], W = (d >> 12) & 15u;
                 half2_t v;
-                v[0] = t[x[4 * q + i] & m];
-                v[1] = t[__builtin_amdgcn_ubfe(x[4 * q + i], w, w)];
+                v[0] = *(const _Float16*)(tab + (d >> 16) + 2u * __builtin_amdgcn_ubfe(x[4 * q + i], 0, W));
+                v[1] = *(const _Float16*)(tab + (d >> 16) + 2u * __builtin_amdgcn_ubfe(x[4 * q + i], W, W));
                 P[4 * q + i] = __builtin_bit_cast(uint32_t, v);
             }
         }
@@ -842,10 +847,10 @@ __device__ __forceinline__ void mx_slots(uint32_t (&P)[16], const uint32_t* dsc,
 }
 
 template <int KS>
-__device__ __forceinline__ void mx_qk(f32x4_t (&c)[4], const half8_t (&qa)[4], const uint32_t* dsc, const uint32_t* stage,
-                                      uint32_t li, const uint32_t* pairs, const _Float16* c16) {
+__device__ __forceinline__ void mx_qk(f32x4_t (&c)[4], const half8_t (&qa)[4], const cu32_t* sd, const uint8_t* stage,
+                                      uint32_t li4, const uint8_t* tab) {
     uint32_t P[16];
-    mx_slots<KS>(P, dsc, stage, li, pairs, c16);
+    mx_slots<KS>(P, sd, stage, li4, tab);
 #pragma unroll
     for (int g = 0; g < 4; ++g) c[g] = mfma16(qa[KS], as_h8(P[4 * g], P[4 * g + 1], P[4 * g + 2], P[4 * g + 3]), c[g]);
 }
@@ -906,8 +911,6 @@ __global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
     __shared__ float s_qp[128 * G];
     __shared__ uint16_t s_dsc[64];
     __shared__ uint32_t s_nnz;
-    const uint32_t* s_pair = s_tab;
-    const _Float16* s_c16 = (const _Float16*)(s_tab + BGTQ_CB_PAIR_ENTRIES);
 
     const size_t bh = (size_t)b * a.Hkv + h;
     const int64_t n_packed = a.n_packed[b];
@@ -968,12 +971,6 @@ __global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
     if (wave == 0) prep_store<G, true, 0>(pin, lane, s_qp, s_dsc, &s_nnz, nullptr);
     __syncthreads();
 
-    uint32_t dsc[32];
-    {
-        const uint32_t* d32 = (const uint32_t*)s_dsc;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) dsc[i] = __builtin_amdgcn_readfirstlane(d32[i]);
-    }
     const int nks = (int)((__builtin_amdgcn_readfirstlane(s_nnz) + 15u) >> 4);  // s_nnz: nonzero slots rounded up to 4
 
     // Query operands: lane (row col = head part, K group row): slot 16ks + 4row + e/2, coord e%2.
@@ -1017,16 +1014,19 @@ __global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
         f32x4_t c[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) c[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // Slot descriptors are re-read each tile so their scalar decode is not hoisted (it would
-        // not fit in SGPRs for 64 slots).
-#pragma unroll
-        for (int i = 0; i < 32; ++i) asm volatile("" : "+s"(dsc[i]));
-        uint32_t li = lane;
-        asm volatile("" : "+v"(li));
-        if (nks > 0) mx_qk<0>(c, qa, dsc, stage, li, s_pair, s_c16);
-        if (nks > 1) mx_qk<1>(c, qa, dsc, stage, li, s_pair, s_c16);
-        if (nks > 2) mx_qk<2>(c, qa, dsc, stage, li, s_pair, s_c16);
-        if (nks > 3) mx_qk<3>(c, qa, dsc, stage, li, s_pair, s_c16);
+        // Slot entries are loaded (scalar, cached) per k-step, not hoisted out of the tile loop:
+        // 64 entries would not fit in scalar registers.
+        uint32_t sdo = (uint32_t)h * 64 * BGTQ_SLOT_WORDS;
+        asm volatile("" : "+s"(sdo));
+        const cu32_t* sd = (const cu32_t*)(a.slots + sdo);
+        uint32_t li4 = 4 * lane;
+        asm volatile("" : "+v"(li4));
+        const uint8_t* stg = (const uint8_t*)stage;
+        const uint8_t* tab = (const uint8_t*)s_tab;
+        if (nks > 0) mx_qk<0>(c, qa, sd, stg, li4, tab);
+        if (nks > 1) mx_qk<1>(c, qa, sd, stg, li4, tab);
+        if (nks > 2) mx_qk<2>(c, qa, sd, stg, li4, tab);
+        if (nks > 3) mx_qk<3>(c, qa, sd, stg, li4, tab);
 
         // softmax over the tile: lane holds tokens 16g + col, heads 2row, 2row + 1
         float z[4][2], tmax[2] = {-INFINITY, -INFINITY};
@@ -1240,6 +1240,55 @@ __global__ __launch_bounds__(256) void k_energy(const EnergyArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Slot table of one (layer, kv head) for the matrix-core decode: entry r (r-th nonzero block in
+// width order, ties by block index; padding entries past the last one are width 1 at bit 0) is
+// one dword  pos%32 | (pos/32) << 8 | W << 12 | B << 16:  the bit offset in the low five bits
+// (an alignbit shift as is), the record dword times 256 (the stage row's byte offset) after a
+// mask, the extract width W and the table byte offset B.  The pair path (W = 2w, B = the pair
+// table of width w) serves groups of four entries whose widest member is <= 5 wide; the other
+// groups take two per-coordinate reads (W = w, B = the fp16 centroid table of width w, at byte
+// SLOT_COORD0 and up).  Offsets match the decode LDS image.
+__device__ void write_slot_table(const uint8_t* bits, uint32_t* slots, int lane, int* s_w, int* s_p) {
+    const int bw = bits[lane];
+    const int w = bw < 8 ? bw : 8;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int rank = 0, pos = 0, nnz = 0;
+#pragma unroll
+    for (int v = 0; v <= 8; ++v) {
+        const uint64_t mk = __ballot(w == v);
+        const int c = __popcll(mk);
+        if (v == 0) nnz = 64 - c;
+        if (v > w) {
+            rank += c;
+            pos += 2 * v * c;
+        } else if (v == w) {
+            const int cl = __popcll(mk & lt);
+            rank += cl;
+            pos += 2 * v * cl;
+        }
+    }
+    if (w > 0) {
+        s_w[rank] = w;
+        s_p[rank] = pos;
+    }
+    if (lane >= nnz) {
+        s_w[lane] = 1;
+        s_p[lane] = 0;
+    }
+    __syncthreads();
+    const int r = lane, wr = s_w[r], pr = s_p[r], lead = s_w[r & ~3];
+    uint32_t W, B;
+    if (lead <= 5) {
+        W = 2u * wr;
+        B = 4u * (((1u << (2 * wr)) - 4u) / 3u);
+    } else {
+        W = wr;
+        B = SLOT_COORD0 + 2u * ((1u << wr) - 2u);
+    }
+    slots[r] = (uint32_t)(pr & 31) | ((uint32_t)(pr >> 5) << 8) | (W << 12) | (B << 16);
+}
+
+// ---------------------------------------------------------------------------------------------
 // Quantize-append.  The float32 steps are spelled out one IEEE operation at a time (no
 // contraction) so the codes and fp16 scales are reproducible bit for bit.
 __device__ __forceinline__ uint32_t tq_code(float x, float t, int w, const float* thr) {
@@ -1295,6 +1344,10 @@ __device__ __forceinline__ void affine_group(const float* x, int n, int bits, ui
 
 __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
     const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    if (blockIdx.x == 0 && b == 0 && (a.which & 1) && a.k_mode == BGTQ_K_BLOCKGTQ) {
+        __shared__ int s_tw[64], s_tp[64];
+        write_slot_table(a.bits + h * 64, a.slots + (size_t)h * 64 * BGTQ_SLOT_WORDS, lane, s_tw, s_tp);
+    }
     const int64_t tile = a.tile0[b] + blockIdx.x;
     if (tile * TILE >= a.pos_hi[b]) return;  // whole workgroup beyond this sequence's range
     const int64_t pos = tile * TILE + lane;
@@ -1462,6 +1515,8 @@ hipError_t launch_energy(const EnergyArgs& a, hipStream_t s) {
 
 hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_t s) {
     if (max_tiles <= 0) return hipSuccess;
+    if ((a.which & 1) && a.k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma || !a.inv_sigma || !a.slots))
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_quant, dim3((unsigned)max_tiles, a.Hkv, B), dim3(64), 0, s, a);
     return hipGetLastError();
 }
@@ -1540,7 +1595,7 @@ static hipError_t launch_dec_g(const DecodeArgs& a, int B, int k_mode, int R, in
 hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t s) {
     if (!a.k_codes || !a.v_codes || !a.k_scale || !a.v_scale || !a.q || !a.part || B < 1 || B > BGTQ_MAXB)
         return hipErrorInvalidValue;
-    if (k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma)) return hipErrorInvalidValue;
+    if (k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma || !a.slots)) return hipErrorInvalidValue;
     if (k_mode == BGTQ_K_AFFINE && !a.k_zero) return hipErrorInvalidValue;
     if (a.v_affine && !a.v_zero) return hipErrorInvalidValue;
     switch (a.G) {
