@@ -90,14 +90,17 @@ int geometry(const bgtq_cache* c, bgtq::Geometry& g) {
     return BGTQ_OK;
 }
 
-int default_splits(int64_t max_tiles, int bh, int n_cu) {
-    // Enough workgroups to cover every CU about twice, with at least 8 tiles (2 per wave) each.
-    int64_t target = (int64_t)2 * n_cu;
+int default_splits(int64_t max_tiles, int bh, int n_cu, int per_cu) {
+    // One round of workgroups (per_cu resident per CU), each with a whole number of tiles per wave
+    // (a multiple of 4, at least 8) so that the waves of a split finish together.
+    const int64_t target = (int64_t)per_cu * n_cu;
     int64_t s = (target + bh - 1) / bh;
-    int64_t max_s = (max_tiles + 7) / 8;
-    if (s > max_s) s = max_s;
     if (s < 1) s = 1;
-    return (int)s;
+    int64_t tps = (max_tiles + s - 1) / s;
+    tps = (tps + 3) / 4 * 4;
+    if (tps < 8) tps = 8;
+    s = (max_tiles + tps - 1) / tps;
+    return (int)(s < 1 ? 1 : s);
 }
 
 int cu_count() {
@@ -435,7 +438,8 @@ int64_t bgtq_decode_workspace_bytes(const bgtq_cache* c, int n_splits) {
     if (rc) return rc;
     if (n_splits < 0) return fail(BGTQ_E_INVALID, "n_splits < 0");
     const int64_t max_tiles = g.n_tiles;
-    const int ns = n_splits ? n_splits : default_splits(max_tiles, g.B * g.Hkv, cu_count());
+    const int ns = n_splits ? n_splits
+                            : default_splits(max_tiles, g.B * g.Hkv, cu_count(), bgtq::decode_wgs_per_cu(c->k_mode, g.G));
     const int parts = ns + (g.n_recent > 0 ? 1 : 0);
     if (parts > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS - 1);
     return (int64_t)g.B * g.Hq * parts * PART * 4;
@@ -475,7 +479,11 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
         max_tiles = std::max<int64_t>(max_tiles, ((int64_t)a.n_packed[b] + TILE - 1) / TILE);
         any_recent |= rec > 0;
     }
-    const int ns = n_splits ? n_splits : default_splits(g.n_tiles, g.B * g.Hkv, cu_count());
+    // Default splits follow the current length; never more than the capacity-sized workspace holds.
+    const int per_cu = bgtq::decode_wgs_per_cu(c->k_mode, g.G);
+    const int ns = n_splits ? n_splits
+                            : std::min(default_splits(std::max<int64_t>(max_tiles, 1), g.B * g.Hkv, cu_count(), per_cu),
+                                       default_splits(g.n_tiles, g.B * g.Hkv, cu_count(), per_cu));
     const int parts = ns + (c->n_recent > 0 ? 1 : 0);
     if (parts > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS - 1);
     const size_t need = (size_t)g.B * g.Hq * parts * PART * 4;
@@ -546,7 +554,7 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
 int64_t bgtq_fp16_decode_workspace_bytes(int64_t N, int B, int Hq, int Hkv, int n_splits) {
     if (N < 1 || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || n_splits < 0) return fail(BGTQ_E_INVALID, "bad sizes");
     const int G = Hq / Hkv;
-    const int ns = n_splits ? n_splits : default_splits((N + TILE - 1) / TILE, B * Hkv, cu_count());
+    const int ns = n_splits ? n_splits : default_splits((N + TILE - 1) / TILE, B * Hkv, cu_count(), 2);
     if (ns > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS);
     (void)G;
     return (int64_t)B * Hq * ns * PART * 4;
@@ -567,7 +575,7 @@ int bgtq_fp16_decode_attention(const void* k16, const void* v16, int64_t N, int 
     const int G = Hq / Hkv;
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return fail(BGTQ_E_UNSUPPORTED, "group size %d unsupported", G);
     const int64_t n_tiles = (N + TILE - 1) / TILE;
-    const int ns = n_splits ? n_splits : default_splits(n_tiles, B * Hkv, cu_count());
+    const int ns = n_splits ? n_splits : default_splits(n_tiles, B * Hkv, cu_count(), 2);
     if (ns > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS);
     const size_t need = (size_t)B * Hq * ns * PART * 4;
     if (ws_bytes < need) return fail(BGTQ_E_INVALID, "workspace too small (%zu < %zu)", ws_bytes, need);

@@ -238,23 +238,33 @@ __device__ __forceinline__ void load_w(uint32_t (&w)[2][G], const uint16_t* wbuf
         for (int h = 0; h < G; ++h) w[p][h] = wb[p * G + h];
 }
 
-// Merge the four waves' (o, m, l, zero term) records in red[wave][h] into one partial per head:
-// part[h][split] = (sum_w e^(m_w - M) (o_w + zs_w), M, sum_w e^(m_w - M) l_w).
-template <int G>
-__device__ __forceinline__ void merge_waves(const float* red, float* part, int n_parts, int split) {
-    for (int idx = threadIdx.x; idx < G * 130; idx += blockDim.x) {
-        const int h = idx / 130, j = idx % 130;
+// Merge the NW waves' (o, m, l, zero term) records in red[wave][h] into one partial per head:
+// part[h][split] = (sum_w e^(m_w - M) (o_w + zs_w), M, sum_w e^(m_w - M) l_w).  The scale factors
+// are computed once per (wave, head) into sc (LDS, NW * G floats) before the element loop.
+template <int G, int NW = 4>
+__device__ __forceinline__ void merge_waves(const float* red, float* sc, float* part, int n_parts, int split) {
+    if (threadIdx.x < G) {
+        const int h = threadIdx.x;
         float M = -INFINITY;
-        for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, red[(wv * G + h) * PART + 128]);
-        float acc = 0.f;
-        for (int wv = 0; wv < 4; ++wv) {
-            const float* rw = red + (wv * G + h) * PART;
-            const float sc = (rw[128] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rw[128] - M);
-            if (j < 128) acc += sc * (rw[j] + rw[130]);
-            else if (j == 129) acc += sc * rw[129];
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, red[(wv * G + h) * PART + 128]);
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) {
+            const float m = red[(wv * G + h) * PART + 128];
+            sc[wv * G + h] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
         }
-        float* dst = part + ((size_t)h * n_parts + split) * PART;
-        dst[j] = (j == 128) ? M : acc;
+        part[((size_t)h * n_parts + split) * PART + 128] = M;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * 129; idx += blockDim.x) {
+        const int h = idx / 129, jj = idx % 129, j = jj < 128 ? jj : 129;
+        float acc = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) {
+            const float* rw = red + (wv * G + h) * PART;
+            acc += sc[wv * G + h] * (j < 128 ? rw[j] + rw[130] : rw[129]);
+        }
+        part[((size_t)h * n_parts + split) * PART + j] = acc;
     }
 }
 
@@ -291,7 +301,7 @@ __device__ __forceinline__ void write_partial(WaveState<G>& st, float* red /*[4]
         }
     }
     __syncthreads();
-    merge_waves<G>(red, part, n_parts, split);
+    merge_waves<G>(red, red + 4 * G * PART, part, n_parts, split);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -609,7 +619,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
     __shared__ uint32_t s_vlut[1 << (2 * VB)];
     __shared__ uint32_t s_stage[4][AFFINE_K ? 1 : (R + 1) * TILE];
     __shared__ __attribute__((aligned(16))) uint16_t s_w[4][64 * G];
-    __shared__ float s_red[4 * G * PART];
+    __shared__ float s_red[4 * G * PART + 4 * G];  // wave records, then merge scale factors
     __shared__ float s_qp[128 * G];
     __shared__ uint16_t s_dsc[64];
     __shared__ uint32_t s_nnz;
@@ -847,12 +857,13 @@ __device__ __forceinline__ void mx_slots(uint32_t (&P)[16], const cu32_t* sd, co
 }
 
 template <int KS>
-__device__ __forceinline__ void mx_qk(f32x4_t (&c)[4], const half8_t (&qa)[4], const cu32_t* sd, const uint8_t* stage,
+__device__ __forceinline__ void mx_qk(f32x4_t (&c)[4], const u32x4_t* qa, int lane, const cu32_t* sd, const uint8_t* stage,
                                       uint32_t li4, const uint8_t* tab) {
     uint32_t P[16];
     mx_slots<KS>(P, sd, stage, li4, tab);
+    const half8_t q = __builtin_bit_cast(half8_t, qa[KS * 64 + lane]);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) c[g] = mfma16(qa[KS], as_h8(P[4 * g], P[4 * g + 1], P[4 * g + 2], P[4 * g + 3]), c[g]);
+    for (int g = 0; g < 4; ++g) c[g] = mfma16(q, as_h8(P[4 * g], P[4 * g + 1], P[4 * g + 2], P[4 * g + 3]), c[g]);
 }
 
 // P·V of one 32-token half S: B = W rows of this lane's head column, A = value fields (S, db, m).
@@ -895,22 +906,48 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
+// LDS arena of the matrix-core decode (byte offsets).  Loop-time regions: tables, query operands,
+// weight exchange, softmax rescale factors, and per wave the stages of the tile in flight (K
+// records, value streams, scales).  The query-prep output and the epilogue records alias the stages.
+constexpr int a16(int x) { return (x + 15) & ~15; }
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
+template <int G, int R, int VB> struct MxLds {
+    static constexpr int TAB = 0;                                     // u32 [BGTQ_CB_MX_WORDS]
+    static constexpr int VLUT = a16(TAB + 4 * BGTQ_CB_MX_WORDS);      // u32 [4^VB]
+    static constexpr int QA = a16(VLUT + 4 * (1 << (2 * VB)));        // u32x4 [4 k-steps][64 lanes]
+    static constexpr int WX = QA + 4 * 64 * 16;                       // u32 [4 waves][16 heads][32 pairs]
+    static constexpr int ALPHA = WX + 4 * 16 * 32 * 4;                // f32 [4 waves][16]
+    static constexpr int NNZ = ALPHA + 4 * 16 * 4;                    // u32
+    static constexpr int DSC = NNZ + 16;                              // u16 [64] (prep output, unused)
+    static constexpr int KST = a16(DSC + 128);                        // per wave: R + 1 rows of 256 B
+    static constexpr int KST_W = (R + 1) * 256;
+    static constexpr int VST = KST + 4 * KST_W;                       // per wave: value streams
+    static constexpr int VST_W = VB * 1024;
+    static constexpr int SST = VST + 4 * VST_W;                       // per wave: K scales, V scales, V zeros
+    static constexpr int SST_W = 3 * 64 * 2;
+    static constexpr int QP = KST;                                    // prologue: f32 [128 G]
+    static constexpr int RED = KST;                                   // epilogue: f32 [4 G PART + 4 G]
+    static constexpr int SIZE = cmax(cmax(SST + 4 * SST_W, QP + 512 * G), RED + 4 * (4 * G * PART + 4 * G));
+};
+
 template <int G, int R, int VB>
-__global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
+__global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     static_assert(G == 4 || G == 8, "matrix-core decode serves 4 or 8 query heads per kv head");
     static_assert(R % 4 == 0, "K records are staged in 16-byte chunks");
+    using LD = MxLds<G, R, VB>;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = lane >> 4, col = lane & 15;
-    __shared__ __attribute__((aligned(16))) uint32_t s_tab[BGTQ_CB_MX_WORDS];
-    __shared__ uint32_t s_vlut[1 << (2 * VB)];
-    __shared__ __attribute__((aligned(16))) uint32_t s_stage[4][(R + 1) * TILE];
-    __shared__ __attribute__((aligned(16))) uint32_t s_wx[4][16 * 32];
-    __shared__ float s_alpha[4][16];
-    __shared__ float s_red[4 * G * PART];
-    __shared__ float s_qp[128 * G];
-    __shared__ uint16_t s_dsc[64];
-    __shared__ uint32_t s_nnz;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LD::SIZE];
+    uint32_t* s_tab = (uint32_t*)(lds + LD::TAB);
+    uint32_t* s_vlut = (uint32_t*)(lds + LD::VLUT);
+    u32x4_t* s_qa = (u32x4_t*)(lds + LD::QA);
+    float* s_alpha = (float*)(lds + LD::ALPHA) + wave * 16;
+    uint32_t* s_nnz = (uint32_t*)(lds + LD::NNZ);
+    uint8_t* kst = lds + LD::KST + wave * LD::KST_W;
+    uint8_t* vst = lds + LD::VST + wave * LD::VST_W;
+    uint16_t* sst = (uint16_t*)(lds + LD::SST + wave * LD::SST_W);
+    uint32_t* wx = (uint32_t*)(lds + LD::WX) + wave * 16 * 32;
 
     const size_t bh = (size_t)b * a.Hkv + h;
     const int64_t n_packed = a.n_packed[b];
@@ -919,11 +956,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
     const int64_t t_hi = t_lo + a.tiles_per_split < n_tiles_b ? t_lo + a.tiles_per_split : n_tiles_b;
     const uint32_t* kc = (const uint32_t*)(a.k_codes + bh * a.n_tiles * a.k_tile_bytes);
     const uint32_t* vc = (const uint32_t*)(a.v_codes + bh * a.n_tiles * a.v_tile_bytes);
-    const uint16_t* ksc = a.k_scale + bh * a.n_cap;
-    const uint16_t* vsc = a.v_scale + bh * a.n_cap;
-    const uint16_t* vzr = a.v_affine ? a.v_zero + bh * a.n_cap : nullptr;
-    uint32_t* stage = s_stage[wave];
-    uint32_t* wx = s_wx[wave];
+    const uint32_t* ks32 = (const uint32_t*)(a.k_scale + bh * a.n_cap);  // fp16 pairs (token 2i, 2i + 1)
+    const uint32_t* vs32 = (const uint32_t*)(a.v_scale + bh * a.n_cap);
+    const uint32_t* vz32 = a.v_affine ? (const uint32_t*)(a.v_zero + bh * a.n_cap) : nullptr;
 
     // Prologue.  Global loads of the tables and of the query go out first, then the first tile's
     // prefetch; loads retire in order, so the table and query writes below do not wait for HBM.
@@ -938,10 +973,11 @@ __global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
     const uint32_t vla = c_cent16[cent_base(VB) + vca], vlb = c_cent16[cent_base(VB) + vcb];
     const PrepIn<G> pin = prep_load<G, true>(a.q, a.q_dtype, a.bits, a.sigma, b, h, a.Hq, lane);
 
-    // Tile in flight: K chunks (staged to LDS on arrival), value stream, scales of the four tokens
-    // 16g + col this lane owns in the softmax.
+    // Tile in flight, staged to LDS when the next tile starts: K chunks, value streams, and one
+    // dword of scales per lane (lanes 0..31: K scales of tokens 2l, 2l+1; lanes 32..63: V scales;
+    // V zeros in a second dword for affine values).
     u32x4_t kn[R / 4], vn[VB];
-    uint16_t skn[4], svn[4], szn[4];
+    uint32_t sn, zn;
     auto fetch = [&](int64_t t) {
         const u32x4_t* kt = (const u32x4_t*)(kc + t * (a.k_tile_bytes / 4));
         const u32x4_t* vt = (const u32x4_t*)(vc + t * (a.v_tile_bytes / 4));
@@ -949,13 +985,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
         for (int c = 0; c < R / 4; ++c) kn[c] = kt[c * 64 + lane];
 #pragma unroll
         for (int c = 0; c < VB; ++c) vn[c] = vt[c * 64 + lane];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int64_t p = t * TILE + 16 * g + col < n_packed ? t * TILE + 16 * g + col : 0;
-            skn[g] = ksc[p];
-            svn[g] = vsc[p];
-            szn[g] = vzr ? vzr[p] : (uint16_t)0;
-        }
+        sn = (lane < 32 ? ks32 : vs32)[t * (TILE / 2) + (lane & 31)];
+        zn = vz32 ? vz32[t * (TILE / 2) + (lane & 31)] : 0u;
     };
     // Unconditional (branch-free prologue); a wave without tiles reads a tile inside the allocation
     // and never uses it.
@@ -966,26 +997,31 @@ __global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
         if (threadIdx.x + 256 * k < TAB4) ((u32x4_t*)s_tab)[threadIdx.x + 256 * k] = tv[k];
     if (threadIdx.x < (1 << (2 * VB)))
         s_vlut[threadIdx.x] = a.v_affine ? (uint32_t)f2h((float)vca) | ((uint32_t)f2h((float)vcb) << 16) : vla | (vlb << 16);
-    for (int i = threadIdx.x; i < 4 * 16 * 32; i += blockDim.x) (&s_wx[0][0])[i] = 0u;
-    for (int i = threadIdx.x; i < 4 * TILE; i += blockDim.x) s_stage[i >> 6][R * TILE + (i & 63)] = 0u;
-    if (wave == 0) prep_store<G, true, 0>(pin, lane, s_qp, s_dsc, &s_nnz, nullptr);
+    for (int i = threadIdx.x; i < 4 * 16 * 32; i += blockDim.x) ((uint32_t*)(lds + LD::WX))[i] = 0u;
+    float* s_qp = (float*)(lds + LD::QP);
+    if (wave == 0) prep_store<G, true, 0>(pin, lane, s_qp, (uint16_t*)(lds + LD::DSC), s_nnz, nullptr);
     __syncthreads();
 
-    const int nks = (int)((__builtin_amdgcn_readfirstlane(s_nnz) + 15u) >> 4);  // s_nnz: nonzero slots rounded up to 4
+    const int nks = (int)((__builtin_amdgcn_readfirstlane(*s_nnz) + 15u) >> 4);  // nonzero slots rounded up to 4
 
-    // Query operands: lane (row col = head part, K group row): slot 16ks + 4row + e/2, coord e%2.
-    half8_t qa[4];
+    // Query operands: lane (row col = head part, K group row): slot 16ks + 4row + e/2, coord e%2,
+    // head col/2, fp16 high part (col even) or low part (col odd).  Each lane keeps its own in LDS.
+    if (wave == 0) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 4; ++ks) {
+            half8_t qa;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int sl = 16 * ks + 4 * row + (e >> 1), hd = col >> 1;
-            const float qv = hd < G ? s_qp[sl * 2 * G + (e & 1) * G + hd] : 0.f;
-            const _Float16 hi = (_Float16)qv;
-            const _Float16 lo = (_Float16)(qv - (float)hi);
-            qa[ks][e] = (col & 1) ? lo : hi;
+            for (int e = 0; e < 8; ++e) {
+                const int sl = 16 * ks + 4 * row + (e >> 1), hd = col >> 1;
+                const float qv = hd < G ? s_qp[sl * 2 * G + (e & 1) * G + hd] : 0.f;
+                const _Float16 hi = (_Float16)qv;
+                const _Float16 lo = (_Float16)(qv - (float)hi);
+                qa[e] = (col & 1) ? lo : hi;
+            }
+            s_qa[ks * 64 + lane] = __builtin_bit_cast(u32x4_t, qa);
         }
     }
+    __syncthreads();  // the query prep area is reused as the tile stages below
 
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, zs[2] = {0.f, 0.f};
     f32x4_t o[8];
@@ -993,20 +1029,22 @@ __global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
     for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     for (int64_t t = t_lo + wave; t < t_hi; t += 4) {
+        // Stage the tile: K records, value streams, scales (transposed: token u at (u%16)*4 + u/16).
         wave_lds_fence();
 #pragma unroll
-        for (int c = 0; c < R / 4; ++c) ((u32x4_t*)stage)[c * 64 + lane] = kn[c];
-        wave_lds_fence();
-        u32x4_t vr[VB];
+        for (int c = 0; c < R / 4; ++c) ((u32x4_t*)kst)[c * 64 + lane] = kn[c];
 #pragma unroll
-        for (int c = 0; c < VB; ++c) vr[c] = vn[c];
-        float sk[4], sv[4], sz[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            sk[g] = h2f(skn[g]);
-            sv[g] = h2f(svn[g]);
-            sz[g] = h2f(szn[g]);
+        for (int c = 0; c < VB; ++c) ((u32x4_t*)vst)[c * 64 + lane] = vn[c];
+        {
+            const int u0 = 2 * (lane & 31), reg = lane < 32 ? 0 : 64;
+            sst[reg + (u0 & 15) * 4 + (u0 >> 4)] = (uint16_t)(sn & 0xFFFFu);
+            sst[reg + ((u0 + 1) & 15) * 4 + ((u0 + 1) >> 4)] = (uint16_t)(sn >> 16);
+            if (lane < 32) {
+                sst[128 + (u0 & 15) * 4 + (u0 >> 4)] = (uint16_t)(zn & 0xFFFFu);
+                sst[128 + ((u0 + 1) & 15) * 4 + ((u0 + 1) >> 4)] = (uint16_t)(zn >> 16);
+            }
         }
+        wave_lds_fence();
         asm volatile("" ::: "memory");
         if (t + 4 < t_hi) fetch(t + 4);
 
@@ -1021,18 +1059,28 @@ __global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
         const cu32_t* sd = (const cu32_t*)(a.slots + sdo);
         uint32_t li4 = 4 * lane;
         asm volatile("" : "+v"(li4));
-        const uint8_t* stg = (const uint8_t*)stage;
         const uint8_t* tab = (const uint8_t*)s_tab;
-        if (nks > 0) mx_qk<0>(c, qa, sd, stg, li4, tab);
-        if (nks > 1) mx_qk<1>(c, qa, sd, stg, li4, tab);
-        if (nks > 2) mx_qk<2>(c, qa, sd, stg, li4, tab);
-        if (nks > 3) mx_qk<3>(c, qa, sd, stg, li4, tab);
+        if (nks > 0) mx_qk<0>(c, s_qa, lane, sd, kst, li4, tab);
+        if (nks > 1) mx_qk<1>(c, s_qa, lane, sd, kst, li4, tab);
+        if (nks > 2) mx_qk<2>(c, s_qa, lane, sd, kst, li4, tab);
+        if (nks > 3) mx_qk<3>(c, s_qa, lane, sd, kst, li4, tab);
 
         // softmax over the tile: lane holds tokens 16g + col, heads 2row, 2row + 1
+        float sk[4], sv[4], sz[4];
+        {
+            const uint2 k2 = *(const uint2*)(sst + col * 4), v2 = *(const uint2*)(sst + 64 + col * 4);
+            const uint2 z2 = *(const uint2*)(sst + 128 + col * 4);
+            sk[0] = h2f(k2.x & 0xFFFFu); sk[1] = h2f(k2.x >> 16); sk[2] = h2f(k2.y & 0xFFFFu); sk[3] = h2f(k2.y >> 16);
+            sv[0] = h2f(v2.x & 0xFFFFu); sv[1] = h2f(v2.x >> 16); sv[2] = h2f(v2.y & 0xFFFFu); sv[3] = h2f(v2.y >> 16);
+            sz[0] = h2f(z2.x & 0xFFFFu); sz[1] = h2f(z2.x >> 16); sz[2] = h2f(z2.y & 0xFFFFu); sz[3] = h2f(z2.y >> 16);
+        }
         float z[4][2], tmax[2] = {-INFINITY, -INFINITY};
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const bool valid = t * TILE + 16 * g + col < n_packed;
+            // scales of tokens past the end are never written: keep them out of the arithmetic
+            sv[g] = valid ? sv[g] : 0.f;
+            sz[g] = valid ? sz[g] : 0.f;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 z[g][hh] = valid ? sk[g] * (c[g][2 * hh] + c[g][2 * hh + 1]) : -INFINITY;
@@ -1051,11 +1099,11 @@ __global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
             }
             wave_lds_fence();
             if (col == 0) {
-                s_alpha[wave][2 * row] = alpha[0];
-                s_alpha[wave][2 * row + 1] = alpha[1];
+                s_alpha[2 * row] = alpha[0];
+                s_alpha[2 * row + 1] = alpha[1];
             }
             wave_lds_fence();
-            const float al = s_alpha[wave][col];
+            const float al = s_alpha[col];
 #pragma unroll
             for (int db = 0; db < 8; ++db) o[db] *= al;
         }
@@ -1079,18 +1127,25 @@ __global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
         }
         wave_lds_fence();
 
-        // P·V on the matrix cores
-        const uint32_t* vs = (const uint32_t*)vr;
+        // P·V on the matrix cores; this lane's value stream comes back from the stage
+        uint32_t vs[4 * VB];
+#pragma unroll
+        for (int c = 0; c < VB; ++c) {
+            const u32x4_t v = ((const u32x4_t*)vst)[c * 64 + lane];
+            vs[4 * c] = v[0]; vs[4 * c + 1] = v[1]; vs[4 * c + 2] = v[2]; vs[4 * c + 3] = v[3];
+        }
         mx_pv<VB, 0>(o, vs, s_vlut, wx, lane);
         mx_pv<VB, 1>(o, vs, s_vlut, wx, lane);
     }
 
-    // Epilogue: row sums of l and the zero term, O^T to LDS, merge the four waves.
+    // Epilogue: row sums of l and the zero term, O^T to LDS (over the stages), merge the waves.
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         l[hh] = row_sum16(l[hh]);
         zs[hh] = row_sum16(zs[hh]);
     }
+    __syncthreads();  // every wave is done with its stages
+    float* s_red = (float*)(lds + LD::RED);
     float* r = s_red + wave * G * PART;
     if (col < G) {
 #pragma unroll
@@ -1111,7 +1166,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mx(const DecodeArgs a) {
     }
     __syncthreads();
     float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_parts * PART;
-    merge_waves<G>(s_red, part, a.n_parts, split);
+    merge_waves<G>(s_red, s_red + 4 * G * PART, part, a.n_parts, split);
 }
 
 // fp16 tiles: the unquantized comparator over [B][Hkv][N][128], and the fp16 recent ring of a packed
@@ -1121,7 +1176,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_fp16(const Fp16Args a) {
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     __shared__ uint16_t s_w[4][64 * G];
-    __shared__ float s_red[4 * G * PART];
+    __shared__ float s_red[4 * G * PART + 4 * G];  // wave records, then merge scale factors
     const size_t bh = (size_t)b * a.Hkv + h;
     __shared__ float s_qp[128 * G];
     if (wave == 0)
@@ -1606,6 +1661,8 @@ hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bi
     }
     return hipErrorInvalidValue;
 }
+
+int decode_wgs_per_cu(int k_mode, int G) { return (k_mode == BGTQ_K_BLOCKGTQ && G >= 4) ? 3 : 2; }
 
 bool decode_supported(int k_mode, int R, int k_bits, int k_group, int v_bits, int G) {
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return false;

@@ -101,6 +101,8 @@ hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t) 
     return hipSuccess;
 }
 
+int decode_wgs_per_cu(int k_mode, int G) { return (k_mode == BGTQ_K_BLOCKGTQ && G >= 4) ? 3 : 2; }
+
 bool decode_supported(int k_mode, int R, int k_bits, int k_group, int v_bits, int G) {
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return false;
     if (v_bits < 2 || v_bits > 4) return false;
