@@ -39,6 +39,12 @@ __constant__ __attribute__((aligned(16))) uint32_t c_mxtab[BGTQ_CB_MX_WORDS] = B
 constexpr uint32_t SLOT_COORD0 = 4u * BGTQ_CB_PAIR_ENTRIES;  // byte offset of the fp16 centroids in that image
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+// Read-only global data the kernel never writes, read through the constant address space so
+// uniform loads become scalar loads.
+typedef __attribute__((address_space(4))) uint32_t cu32_t;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int cent_base(int w) { return (1 << w) - 2; }
 __device__ __forceinline__ int thr_base(int w) { return (1 << w) - w - 1; }
@@ -265,6 +271,40 @@ __device__ __forceinline__ void merge_waves(const float* red, float* sc, float* 
             acc += sc[wv * G + h] * (j < 128 ? rw[j] + rw[130] : rw[129]);
         }
         part[((size_t)h * n_parts + split) * PART + j] = acc;
+    }
+}
+
+// merge_waves for four waves with 16-byte accesses: thread (h, quad of dims) handles 4 dims.
+template <int G>
+__device__ __forceinline__ void merge_waves4(const float* red, float* sc, float* part, int n_parts, int split) {
+    if (threadIdx.x < G) {
+        const int h = threadIdx.x;
+        float M = -INFINITY;
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, red[(wv * G + h) * PART + 128]);
+        float L = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv) {
+            const float m = red[(wv * G + h) * PART + 128];
+            const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+            sc[wv * G + h] = f;
+            L += f * red[(wv * G + h) * PART + 129];
+        }
+        float* dst = part + ((size_t)h * n_parts + split) * PART;
+        dst[128] = M;
+        dst[129] = L;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * 32; idx += blockDim.x) {
+        const int h = idx >> 5, j = 4 * (idx & 31);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv) {
+            const float* rw = red + (wv * G + h) * PART;
+            const float f = sc[wv * G + h];
+            acc += f * (*(const f32x4_t*)(rw + j) + rw[130]);
+        }
+        *(f32x4_t*)(part + ((size_t)h * n_parts + split) * PART + j) = acc;
     }
 }
 
@@ -775,12 +815,6 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
 //    x 16 heads) through LDS in pair order (t, t + 32); O^T accumulates per 16-dim block.
 //  * online softmax with the exact running max per head (a wave-uniform branch raises it), so the
 //    largest weight of a split is fp16(scale) exactly, whatever the split boundaries.
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-// Read-only global data the kernel never writes, read through the constant address space so
-// uniform loads become scalar loads.
-typedef __attribute__((address_space(4))) uint32_t cu32_t;
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 
 __device__ __forceinline__ half8_t as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -1005,21 +1039,19 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     const int nks = (int)((__builtin_amdgcn_readfirstlane(*s_nnz) + 15u) >> 4);  // nonzero slots rounded up to 4
 
     // Query operands: lane (row col = head part, K group row): slot 16ks + 4row + e/2, coord e%2,
-    // head col/2, fp16 high part (col even) or low part (col odd).  Each lane keeps its own in LDS.
-    if (wave == 0) {
+    // head col/2, fp16 high part (col even) or low part (col odd).  Wave w builds k-step w.
+    {
+        const int ks = wave;
+        half8_t qa;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            half8_t qa;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sl = 16 * ks + 4 * row + (e >> 1), hd = col >> 1;
-                const float qv = hd < G ? s_qp[sl * 2 * G + (e & 1) * G + hd] : 0.f;
-                const _Float16 hi = (_Float16)qv;
-                const _Float16 lo = (_Float16)(qv - (float)hi);
-                qa[e] = (col & 1) ? lo : hi;
-            }
-            s_qa[ks * 64 + lane] = __builtin_bit_cast(u32x4_t, qa);
+        for (int e = 0; e < 8; ++e) {
+            const int sl = 16 * ks + 4 * row + (e >> 1), hd = col >> 1;
+            const float qv = hd < G ? s_qp[sl * 2 * G + (e & 1) * G + hd] : 0.f;
+            const _Float16 hi = (_Float16)qv;
+            const _Float16 lo = (_Float16)(qv - (float)hi);
+            qa[e] = (col & 1) ? lo : hi;
         }
+        s_qa[ks * 64 + lane] = __builtin_bit_cast(u32x4_t, qa);
     }
     __syncthreads();  // the query prep area is reused as the tile stages below
 
@@ -1149,9 +1181,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     float* r = s_red + wave * G * PART;
     if (col < G) {
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) r[col * PART + 16 * db + 4 * row + e] = o[db][e];
+        for (int db = 0; db < 8; ++db) *(f32x4_t*)(r + col * PART + 16 * db + 4 * row) = o[db];
     }
     if (col == 0) {
 #pragma unroll
@@ -1166,7 +1196,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     }
     __syncthreads();
     float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_parts * PART;
-    merge_waves<G>(s_red, s_red + 4 * G * PART, part, a.n_parts, split);
+    merge_waves4<G>(s_red, s_red + 4 * G * PART, part, a.n_parts, split);
 }
 
 // fp16 tiles: the unquantized comparator over [B][Hkv][N][128], and the fp16 recent ring of a packed
