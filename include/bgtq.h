@@ -213,7 +213,8 @@ int bgtq_fp16_decode_attention(const void *k16, const void *v16, int64_t N, int 
 
 /*
  * Kernel tracing (host).  While enabled, every launch of a main kernel (packed decode, fp16
- * decode, quantize-append) is bracketed by a pair of HIP events recorded on its stream, up to
+ * decode, quantize-append) records a pair of HIP events around the kernel's own execution
+ * (hipExtLaunchKernelGGL; the dispatch gap before the kernel is not included), up to
  * `max_launches` launches; bgtq_profile_enable(0) disables and releases the events.
  * bgtq_profile_read waits for the recorded events of one kind (BGTQ_PROF_*), returns their
  * count and the total / min / max duration in milliseconds (any output may be NULL), and clears

@@ -125,19 +125,17 @@ struct Profiler {
 };
 Profiler g_prof;
 
+// Arms the slot's events for the next main-kernel launch, which records them around the kernel
+// itself; an unused pair is disarmed when the scope ends.
 struct ProfScope {
-    hipStream_t s;
-    int slot = -1;
-    ProfScope(int kind, hipStream_t st) : s(st) {
+    ProfScope(int kind, hipStream_t) {
         if (g_prof.cap > 0 && g_prof.n < g_prof.cap) {
-            slot = g_prof.n++;
+            const int slot = g_prof.n++;
             g_prof.kind[slot] = kind;
-            (void)hipEventRecord(g_prof.ev[2 * slot], s);
+            bgtq::arm_launch_events(g_prof.ev[2 * slot], g_prof.ev[2 * slot + 1]);
         }
     }
-    ~ProfScope() {
-        if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
-    }
+    ~ProfScope() { bgtq::disarm_launch_events(); }
 };
 
 }  // namespace

@@ -131,6 +131,10 @@ hipError_t launch_energy(const EnergyArgs& a, hipStream_t s);
 hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_t s);
 hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t s);
 bool decode_supported(int k_mode, int R, int k_bits, int k_group, int v_bits, int G);
+// Tracing aid: the next decode, fp16-decode or quantize kernel launch on this thread records
+// `start` and `stop` around the kernel itself (hipExtLaunchKernelGGL); disarm drops an unused pair.
+void arm_launch_events(hipEvent_t start, hipEvent_t stop);
+void disarm_launch_events();
 int decode_wgs_per_cu(int k_mode, int G);  // resident decode workgroups per CU the split heuristic aims for
 
 }  // namespace bgtq

@@ -20,6 +20,8 @@
 //    a second kernel merges the splits.
 #include "bgtq_internal.h"
 
+#include <hip/hip_ext.h>
+
 #include "../../include/bgtq.h"
 #include "generated/bgtq_codebook_data.h"
 
@@ -1587,6 +1589,21 @@ __global__ __launch_bounds__(128) void k_ring(const RingArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // Launchers
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+// Launch with the armed event pair, if any (consumed), else plainly.
+template <typename K, typename A>
+static hipError_t launch_main(K kernel, dim3 grid, dim3 block, hipStream_t s, const A& a) {
+    if (t_ev_start) {
+        hipEvent_t e0 = t_ev_start, e1 = t_ev_stop;
+        t_ev_start = t_ev_stop = nullptr;
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, a);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s) {
     if (!a.part || !a.out || a.n_parts < 1 || a.n_parts > BGTQ_MAX_PARTS) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_combine, dim3(rows, D / CMB_DIMS), dim3(256), 0, s, a);
@@ -1602,8 +1619,7 @@ hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_
     if (max_tiles <= 0) return hipSuccess;
     if ((a.which & 1) && a.k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma || !a.inv_sigma || !a.slots))
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_quant, dim3((unsigned)max_tiles, a.Hkv, B), dim3(64), 0, s, a);
-    return hipGetLastError();
+    return launch_main(k_quant, dim3((unsigned)max_tiles, a.Hkv, B), dim3(64), s, a);
 }
 
 hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t s) {
@@ -1614,8 +1630,7 @@ hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t s
 
 template <int G>
 static hipError_t launch_fp16_g(const Fp16Args& a, int B, hipStream_t s) {
-    hipLaunchKernelGGL(k_decode_fp16<G>, dim3(a.n_splits, a.Hkv, B), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_main(k_decode_fp16<G>, dim3(a.n_splits, a.Hkv, B), dim3(256), s, a);
 }
 
 hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t s) {
@@ -1631,14 +1646,12 @@ hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t s) {
 
 template <int G, int R, int VB, int KG>
 static hipError_t launch_dec(const DecodeArgs& a, int B, hipStream_t s) {
-    hipLaunchKernelGGL((k_decode<G, R, VB, KG>), dim3(a.n_splits, a.Hkv, B), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_main(k_decode<G, R, VB, KG>, dim3(a.n_splits, a.Hkv, B), dim3(256), s, a);
 }
 
 template <int G, int R, int VB>
 static hipError_t launch_dec_mx(const DecodeArgs& a, int B, hipStream_t s) {
-    hipLaunchKernelGGL((k_decode_mx<G, R, VB>), dim3(a.n_splits, a.Hkv, B), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_main(k_decode_mx<G, R, VB>, dim3(a.n_splits, a.Hkv, B), dim3(256), s, a);
 }
 
 template <int G, int VB>
@@ -1691,6 +1704,12 @@ hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bi
     }
     return hipErrorInvalidValue;
 }
+
+void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
+    t_ev_start = start;
+    t_ev_stop = stop;
+}
+void disarm_launch_events() { t_ev_start = t_ev_stop = nullptr; }
 
 int decode_wgs_per_cu(int k_mode, int G) { return (k_mode == BGTQ_K_BLOCKGTQ && G >= 4) ? 3 : 2; }
 

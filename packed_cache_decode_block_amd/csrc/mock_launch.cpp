@@ -101,6 +101,9 @@ hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t) 
     return hipSuccess;
 }
 
+void arm_launch_events(hipEvent_t, hipEvent_t) {}
+void disarm_launch_events() {}
+
 int decode_wgs_per_cu(int k_mode, int G) { return (k_mode == BGTQ_K_BLOCKGTQ && G >= 4) ? 3 : 2; }
 
 bool decode_supported(int k_mode, int R, int k_bits, int k_group, int v_bits, int G) {
