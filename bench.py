@@ -49,13 +49,19 @@ def layer_bytes(w, N: int) -> float:
             + w.B * w.Hq * w.d * (act + 4))
 
 
+def decode_kernel_name(w) -> str:
+    """The decode kernel a workload dispatches to: Block-GTQ keys with at least four query heads
+    per kv head take the matrix-core kernel, everything else the vector-ALU one."""
+    return "k_decode_mx" if (w.k_mode == "gtq" and w.Hq // w.Hkv >= 4) else "k_decode"
+
+
 def measured_traffic(wid: int):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary of this workload
     (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None when there is none or
     the kernel source has changed since the counters were taken."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", {2: "k_decode_qwen2.5-3b_128k_hbm_counters.md"}.get(wid, "-"))
+    path = os.path.join(ROOT, "profiles", {2: "k_decode_mx_qwen2.5-3b_128k_hbm_counters.md"}.get(wid, "-"))
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -266,7 +272,7 @@ def main():
         "tokens_heads_per_s": round(w.B * w.N * w.Hq * w.L / sec, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.wid),
-                     "kernel": "k_decode (split-K packed decode)", "kernel_avg_us": round(kern_ms * 1e3, 3),
+                     "kernel": decode_kernel_name(w), "kernel_avg_us": round(kern_ms * 1e3, 3),
                      "bytes_per_launch": lb, "launches_timed": n_k},
     }
     del ws
