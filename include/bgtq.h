@@ -51,8 +51,7 @@ enum { BGTQ_V_CODEBOOK = 0, BGTQ_V_AFFINE = 1 };            /* value formats */
 enum {
     BGTQ_BUF_K_CODES = 0, BGTQ_BUF_V_CODES = 1, BGTQ_BUF_K_SCALE = 2, BGTQ_BUF_K_ZERO = 3,
     BGTQ_BUF_V_SCALE = 4, BGTQ_BUF_V_ZERO = 5, BGTQ_BUF_RECENT_K = 6, BGTQ_BUF_RECENT_V = 7,
-    BGTQ_BUF_META = 8,        /* bits + sigma + inv_sigma, for reference */
-    BGTQ_BUF_SLOTS = 9        /* slot table (Block-GTQ keys; 0 bytes otherwise) */
+    BGTQ_BUF_META = 8         /* bits + sigma + inv_sigma, for reference */
 };
 
 #define BGTQ_HEAD_DIM 128
@@ -87,10 +86,6 @@ enum {
  *   bits      uint8 [L][Hkv][64]   widths (BLOCKGTQ), from bgtq_allocate
  *   sigma     fp32  [L][Hkv][64]   per-block key scale sigma_i = sqrt(E_k[i]/2)
  *   inv_sigma fp32  [L][Hkv][64]   fp32(1/sigma_i), 0 for a dead block
- *   slots     uint32 [L][Hkv][64]  Block-GTQ only, else NULL: the record position of each
- *     nonzero block in width order, derived from bits.  bgtq_quantize_append writes it (every
- *     call, for the layer it appends to); bgtq_decode_attention reads it.  Contents are private
- *     to the library; changing bits after an append requires appending again before decoding.
  * Host state:
  *   n_tokens  int64 [L][B] host array: tokens appended so far per (layer, sequence) (packed +
  *     recent).  bgtq_quantize_append advances it on success only.
@@ -115,7 +110,6 @@ typedef struct bgtq_cache {
     void *k_codes, *v_codes, *k_scale, *k_zero, *v_scale, *v_zero, *recent_k, *recent_v;
     const uint8_t *bits;
     const float *sigma, *inv_sigma;
-    uint32_t *slots;
     int64_t *n_tokens;
 } bgtq_cache;
 

@@ -13,7 +13,7 @@ SCORE_QK, SCORE_K = 0, 1
 K_BLOCKGTQ, K_AFFINE = 0, 1
 V_CODEBOOK, V_AFFINE = 0, 1
 (BUF_K_CODES, BUF_V_CODES, BUF_K_SCALE, BUF_K_ZERO, BUF_V_SCALE, BUF_V_ZERO, BUF_RECENT_K,
- BUF_RECENT_V, BUF_META, BUF_SLOTS) = range(10)
+ BUF_RECENT_V, BUF_META) = range(9)
 MAX_BATCH = 64
 
 SYMBOLS = ["bgtq_last_error", "bgtq_version", "bgtq_codebook", "bgtq_allocate", "bgtq_block_energy",
@@ -36,7 +36,7 @@ class CacheDesc(C.Structure):
                 ("v_mode", C.c_int32), ("v_bits", C.c_int32), ("n_recent", C.c_int32),
                 ("k_codes", C.c_void_p), ("v_codes", C.c_void_p), ("k_scale", C.c_void_p), ("k_zero", C.c_void_p),
                 ("v_scale", C.c_void_p), ("v_zero", C.c_void_p), ("recent_k", C.c_void_p), ("recent_v", C.c_void_p),
-                ("bits", C.c_void_p), ("sigma", C.c_void_p), ("inv_sigma", C.c_void_p), ("slots", C.c_void_p),
+                ("bits", C.c_void_p), ("sigma", C.c_void_p), ("inv_sigma", C.c_void_p),
                 ("n_tokens", C.POINTER(C.c_int64))]
 
 

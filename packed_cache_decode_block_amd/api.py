@@ -117,9 +117,8 @@ class PackedCache:
         self.bits = torch.zeros((L, Hkv, 64), dtype=torch.uint8, device=device)
         self.sigma = torch.zeros((L, Hkv, 64), dtype=torch.float32, device=device)
         self.inv_sigma = torch.zeros((L, Hkv, 64), dtype=torch.float32, device=device)
-        self.slots = buf(_lib.BUF_SLOTS, torch.int32)
         for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "recent_k", "recent_v",
-                     "bits", "sigma", "inv_sigma", "slots"):
+                     "bits", "sigma", "inv_sigma"):
             setattr(d, name, _ptr(getattr(self, name)))
         self._ws = None
 

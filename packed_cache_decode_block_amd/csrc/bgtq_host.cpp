@@ -293,7 +293,6 @@ int64_t bgtq_cache_bytes(const bgtq_cache* c, int which) {
         case BGTQ_BUF_RECENT_K:
         case BGTQ_BUF_RECENT_V: return L * g.recent_layer;
         case BGTQ_BUF_META: return L * g.Hkv * 64 * (1 + 4 + 4);
-        case BGTQ_BUF_SLOTS: return c->k_mode == BGTQ_K_BLOCKGTQ ? L * g.Hkv * 64 * BGTQ_SLOT_WORDS * 4 : 0;
     }
     return fail(BGTQ_E_INVALID, "unknown buffer selector %d", which);
 }
@@ -309,8 +308,8 @@ int bgtq_quantize_append(bgtq_cache* c, int layer, const void* k, const void* v,
     if (n_new < 0) return fail(BGTQ_E_INVALID, "n_new < 0");
     if (!c->n_tokens) return fail(BGTQ_E_INVALID, "n_tokens is NULL");
     if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale) return fail(BGTQ_E_INVALID, "NULL cache buffer");
-    if (c->k_mode == BGTQ_K_BLOCKGTQ && (!c->bits || !c->sigma || !c->inv_sigma || !c->slots))
-        return fail(BGTQ_E_INVALID, "Block-GTQ keys need bits, sigma, inv_sigma and slots");
+    if (c->k_mode == BGTQ_K_BLOCKGTQ && (!c->bits || !c->sigma || !c->inv_sigma))
+        return fail(BGTQ_E_INVALID, "Block-GTQ keys need bits, sigma and inv_sigma");
     if (c->k_mode == BGTQ_K_AFFINE && !c->k_zero) return fail(BGTQ_E_INVALID, "affine keys need k_zero");
     if (c->v_mode == BGTQ_V_AFFINE && !c->v_zero) return fail(BGTQ_E_INVALID, "affine values need v_zero");
     if (c->n_recent > 0 && (!c->recent_k || !c->recent_v)) return fail(BGTQ_E_INVALID, "recent ring buffers are NULL");
@@ -349,7 +348,6 @@ int bgtq_quantize_append(bgtq_cache* c, int layer, const void* k, const void* v,
         q.bits = c->bits + (size_t)layer * g.Hkv * 64;
         q.sigma = c->sigma + (size_t)layer * g.Hkv * 64;
         q.inv_sigma = c->inv_sigma + (size_t)layer * g.Hkv * 64;
-        q.slots = c->slots + (size_t)layer * g.Hkv * 64 * BGTQ_SLOT_WORDS;
     }
     q.Hkv = g.Hkv;
     q.n_cap = g.n_cap;
@@ -455,7 +453,7 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
     if (!c->n_tokens) return fail(BGTQ_E_INVALID, "n_tokens is NULL");
     if (n_splits < 0) return fail(BGTQ_E_INVALID, "n_splits < 0");
     if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale) return fail(BGTQ_E_INVALID, "NULL cache buffer");
-    if (c->k_mode == BGTQ_K_BLOCKGTQ && (!c->bits || !c->sigma || !c->slots))
+    if (c->k_mode == BGTQ_K_BLOCKGTQ && (!c->bits || !c->sigma))
         return fail(BGTQ_E_INVALID, "NULL key metadata");
     if (c->k_mode == BGTQ_K_AFFINE && !c->k_zero) return fail(BGTQ_E_INVALID, "affine keys need k_zero");
     if (c->v_mode == BGTQ_V_AFFINE && !c->v_zero) return fail(BGTQ_E_INVALID, "affine values need v_zero");
@@ -501,7 +499,6 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
     a.q_dtype = dtype;
     a.bits = c->k_mode == BGTQ_K_BLOCKGTQ ? c->bits + (size_t)layer * g.Hkv * 64 : nullptr;
     a.sigma = c->k_mode == BGTQ_K_BLOCKGTQ ? c->sigma + (size_t)layer * g.Hkv * 64 : nullptr;
-    a.slots = c->k_mode == BGTQ_K_BLOCKGTQ ? c->slots + (size_t)layer * g.Hkv * 64 * BGTQ_SLOT_WORDS : nullptr;
     bgtq::Fp16Args ra{};
     if (c->n_recent > 0) {
         ra.k16 = (const uint16_t*)c->recent_k + (size_t)layer * bh * c->n_recent * D;

@@ -8,7 +8,7 @@
 
 #define BGTQ_MAXB 64         // sequences per call carried in kernel arguments
 #define BGTQ_MAX_PARTS 8192  // split partials per query head merged by the combine kernel
-#define BGTQ_SLOT_WORDS 1    // dwords per slot-table entry
+#define BGTQ_KST_ROW_BYTES 320  // stride of the K-record rows staged in LDS by the matrix-core decode
 
 namespace bgtq {
 
@@ -37,7 +37,6 @@ struct DecodeArgs {
     const void* q;              // [B][Hq][128] in q_dtype
     const uint8_t* bits;        // [Hkv][64] this layer's widths (Block-GTQ)
     const float* sigma;         // [Hkv][64]
-    const uint32_t* slots;      // [Hkv][64][BGTQ_SLOT_WORDS] slot table (Block-GTQ)
     float* part;                // [B][Hq][n_parts][132]
     int q_dtype;
     int Hkv, Hq, G;
@@ -101,7 +100,6 @@ struct QuantArgs {
     const uint8_t* bits;        // [Hkv][64]
     const float* sigma;
     const float* inv_sigma;
-    uint32_t* slots;            // [Hkv][64][BGTQ_SLOT_WORDS] slot table written for decode (Block-GTQ)
     int Hkv;
     int64_t n_cap, n_tiles, k_tile_bytes, v_tile_bytes;
     int k_mode, R, k_bits, k_group;

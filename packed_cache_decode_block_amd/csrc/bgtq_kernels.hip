@@ -36,9 +36,9 @@ constexpr float kLog2eOverSqrtD = 0.12751743074233076f;  // log2(e) / sqrt(128)
 __constant__ uint32_t c_cent32[BGTQ_CB_CENTROIDS] = BGTQ_CB_CENTROID_F32_INIT;
 __constant__ uint16_t c_cent16[BGTQ_CB_CENTROIDS] = BGTQ_CB_CENTROID_F16_INIT;
 __constant__ uint32_t c_thr32[BGTQ_CB_THRESHOLDS] = BGTQ_CB_THRESHOLD_F32_INIT;
-// Decode tables for the matrix-core kernel: pair tables of widths 1..5, then the fp16 centroids.
+// LDS image of the matrix-core decode's tables: pair tables of widths 5..1, then the fp16
+// centroid tables of widths 8..1, each at a multiple of its size (offsets BGTQ_CB_MX_*_OFFSETS).
 __constant__ __attribute__((aligned(16))) uint32_t c_mxtab[BGTQ_CB_MX_WORDS] = BGTQ_CB_MX_INIT;
-constexpr uint32_t SLOT_COORD0 = 4u * BGTQ_CB_PAIR_ENTRIES;  // byte offset of the fp16 centroids in that image
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -520,6 +520,30 @@ __device__ void fp16_tiles(WaveState<G>& st, const uint16_t* K16, const uint16_t
 //  dsc16[s]: slot descriptor (start dword | bit offset << 5 | width << 10); padding = width 1 at 0.
 //  qs[g*G + h]: per-key-group sums of the natural scaled query (affine keys).
 // The block order comes from nine wave ballots (one per width) instead of a sort.
+// Stream order of the RoPE blocks (lane = block, w = its width): rank among the nonzero blocks by
+// width descending (ties: lower block first), bit position of its 2w-bit field in the K record,
+// and the number of nonzero blocks.  Nine wave ballots, one per width.
+__device__ __forceinline__ void block_order(int w, int lane, int& rank, int& pos, int& nnz) {
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    rank = 0;
+    pos = 0;
+    nnz = 0;
+#pragma unroll
+    for (int v = 0; v <= 8; ++v) {
+        const uint64_t mk = __ballot(w == v);
+        const int c = __popcll(mk);
+        if (v == 0) nnz = 64 - c;
+        if (v > w) {
+            rank += c;
+            pos += 2 * v * c;
+        } else if (v == w) {
+            const int cl = __popcll(mk & lt);
+            rank += cl;
+            pos += 2 * v * cl;
+        }
+    }
+}
+
 // Global inputs of the preparation (lane = RoPE block), loaded raw and converted later so a kernel
 // can issue them, then its tile prefetch, before anything waits on them.
 template <int G> struct PrepIn {
@@ -589,22 +613,8 @@ __device__ void prep_store(const PrepIn<G>& in, int lane, float* qp, uint16_t* d
         const int bw = (int)((in.w4 >> (8 * (lane & 3))) & 0xFFu);
         const int w = bw < 8 ? bw : 8;  // widths above 8 are invalid; clamp
         const float sg = in.sg;
-        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        int rank = 0, pos = 0, nnz = 0;
-#pragma unroll
-        for (int v = 0; v <= 8; ++v) {
-            const uint64_t mk = __ballot(w == v);
-            const int c = __popcll(mk);
-            if (v == 0) nnz = 64 - c;
-            if (v > w) {
-                rank += c;
-                pos += 2 * v * c;
-            } else if (v == w) {
-                const int cl = __popcll(mk & lt);
-                rank += cl;
-                pos += 2 * v * cl;
-            }
-        }
+        int rank, pos, nnz;
+        block_order(w, lane, rank, pos, nnz);
         if (w > 0) {
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
@@ -809,9 +819,12 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
 //  * A = Q' (16 rows x 32 K): row 4u + e is head 2u + e/2, with e even the fp16 high part and e odd
 //    the fp16 low part of q' = q * sigma * log2(e)/sqrt(d) (hi + lo carries ~22 bits).  Centroids
 //    are fp16 values exactly, so the products lose nothing and the MFMA sums in fp32.
-//  * B = K^ (32 K x 16 tokens): lane = token extracts 16 slots per k-step as fp16 centroid pairs
-//    (wave-uniform slot offsets, pair tables for widths <= 5, per-coordinate tables above), then
-//    two permlane swaps transpose the 4 x 4 blocks (token group x slot group) into operand order.
+//  * B = K^ (32 K x 16 tokens): lane (token j, row u) builds its own operand: K index 8u + e is
+//    coordinate e % 2 of stream slot 16 ks + 4 (e / 2) + u, so the four slots of a column (one
+//    per lane row) are consecutive in the record.  Per column and token group the lane reads a
+//    64-bit window of the staged record at its own slot's row, shifts it and ANDs/ORs it into a
+//    table address (pair tables for widths <= 5, fp16 coordinate tables for wider columns).  The
+//    one-dword column descriptors are built once per workgroup; no transposes.
 //  * C (16 x 16 tokens): lane (token 16g + r, row group u) holds heads 2u, 2u + 1 as (hi, lo).
 //  * P·V: A = V^T (16 dims x 32 tokens) straight from the lane-stream value fields, B = W (32 tokens
 //    x 16 heads) through LDS in pair order (t, t + 32); O^T accumulates per 16-dim block.
@@ -826,80 +839,88 @@ __device__ __forceinline__ half8_t as_h8(uint32_t a, uint32_t b, uint32_t c, uin
 __device__ __forceinline__ f32x4_t mfma16(half8_t a, half8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-// x.rows{2,3} <-> y.rows{0,1} (lanes 32..63 of x with lanes 0..31 of y)
-__device__ __forceinline__ void swap32(uint32_t& x, uint32_t& y) {
-    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
-    x = r[0];
-    y = r[1];
-}
-// x.rows{1,3} <-> y.rows{0,2}
-__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
-    x = r[0];
-    y = r[1];
+// Column descriptor of one stream slot (one dword, built in the prologue; a lane reads the four of
+// its k-step with one 16-byte LDS read):
+//   bits 0..4   alignbit shift that moves the field (pair) or the first code (coordinates) to bit
+//               2 (pair) or bit 1 (coordinates) of the 64-bit window
+//   bits 5..9   field width: 2w for a pair column, w for a coordinate column (0: empty slot)
+//   bits 10..15 64-bit shift that moves the second code to bit 1 (coordinate columns)
+//   bits 16..31 byte offset of the window's first stage row
+__device__ __forceinline__ uint32_t mx_desc(int pos, int w, bool coord) {
+    const int k = coord ? 1 : 2;
+    const int u = pos - k;                       // >= -2
+    const int rr = u >= 0 ? u >> 5 : -1;         // window row (-1: the spare row)
+    const uint32_t sh = (uint32_t)(u - 32 * rr);
+    const uint32_t fw = (uint32_t)(w == 0 ? 0 : (coord ? w : 2 * w));
+    const uint32_t sh1 = coord ? sh + (uint32_t)w : 0u;
+    return sh | (fw << 5) | (sh1 << 10) | ((uint32_t)(rr + 1) * BGTQ_KST_ROW_BYTES << 16);
 }
 
-// 16 slots 16*KS + i of this lane's token as fp16 centroid pairs, transposed into B operands:
-// P[4g .. 4g+3] = slot group (lane row) of token group g.  Slot entries {row offset, bit offset,
-// W, B} come from the slot table in scalar registers.  All window reads are issued first, then
-// all table reads, so one LDS wait covers the k-step.
-template <int KS>
-__device__ __forceinline__ void mx_slots(uint32_t (&P)[16], const cu32_t* sd, const uint8_t* stage, uint32_t li4,
-                                         const uint8_t* tab) {
-    uint32_t D[16];
+// One column of a k-step read as coordinate pairs: per token group g a 64-bit window of two stage
+// rows, alignbit, and_or into the pair table of the slot's width, one 4-byte read.  lb: this lane's
+// token column in the wave's K stage.
+template <int M>
+__device__ __forceinline__ void col_pair(uint32_t (&P)[16], const uint8_t* lds, uint32_t dsc, uint32_t lb) {
+    const uint32_t ad = (dsc >> 16) + lb;
+    const uint32_t mask = ((1u << ((dsc >> 5) & 31u)) - 1u) << 2;
+    const uint32_t base = mask + BGTQ_CB_MX_PAIR_BIAS;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) D[i] = sd[16 * KS + i];  // one scalar load of the k-step's entries
-    uint32_t x[16];
-    {
-        uint32_t lo[16], hi[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint8_t* rp = stage + (D[i] & 0xF00u) + li4;
-            lo[i] = *(const uint32_t*)rp;
-            hi[i] = *(const uint32_t*)(rp + 4 * TILE);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_alignbit(hi[i], lo[i], D[i]);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if ((D[4 * q] >> 16) < SLOT_COORD0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t d = D[4 * q + i];
-                P[4 * q + i] = *(const uint32_t*)(tab + (d >> 16) + 4u * __builtin_amdgcn_ubfe(x[4 * q + i], 0, (d >> 12) & 15u));
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t d = D[4 * q + i], W = (d >> 12) & 15u;
-                half2_t v;
-                v[0] = *(const _Float16*)(tab + (d >> 16) + 2u * __builtin_amdgcn_ubfe(x[4 * q + i], 0, W));
-                v[1] = *(const _Float16*)(tab + (d >> 16) + 2u * __builtin_amdgcn_ubfe(x[4 * q + i], W, W));
-                P[4 * q + i] = __builtin_bit_cast(uint32_t, v);
-            }
-        }
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        swap32(P[m], P[8 + m]);
-        swap32(P[4 + m], P[12 + m]);
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        swap16(P[m], P[4 + m]);
-        swap16(P[8 + m], P[12 + m]);
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t lo = *(const uint32_t*)(lds + ad + 64 * g);
+        const uint32_t hi = *(const uint32_t*)(lds + ad + 64 * g + BGTQ_KST_ROW_BYTES);
+        const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, dsc);
+        P[4 * g + M] = *(const uint32_t*)(lds + ((x & mask) | base));
     }
 }
 
-template <int KS>
-__device__ __forceinline__ void mx_qk(f32x4_t (&c)[4], const u32x4_t* qa, int lane, const cu32_t* sd, const uint8_t* stage,
-                                      uint32_t li4, const uint8_t* tab) {
+// One column read per coordinate (its first slot is wider than 5 bits): one window, the first code
+// by alignbit and the second by a 64-bit shift, two 2-byte reads from the fp16 centroid table.
+template <int M>
+__device__ __forceinline__ void col_coord(uint32_t (&P)[16], const uint8_t* lds, uint32_t dsc, uint32_t lb) {
+    const uint32_t ad = (dsc >> 16) + lb;
+    const uint32_t mask = ((1u << ((dsc >> 5) & 31u)) - 1u) << 1;
+    const uint32_t base = mask + BGTQ_CB_MX_COORD_BIAS;
+    const uint32_t sh1 = (dsc >> 10) & 63u;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t lo = *(const uint32_t*)(lds + ad + 64 * g);
+        const uint32_t hi = *(const uint32_t*)(lds + ad + 64 * g + BGTQ_KST_ROW_BYTES);
+        const uint32_t x0 = __builtin_amdgcn_alignbit(hi, lo, dsc);
+        const uint32_t x1 = (uint32_t)((((uint64_t)hi << 32) | lo) >> sh1);
+        const uint32_t c0 = *(const uint16_t*)(lds + ((x0 & mask) | base));
+        const uint32_t c1 = *(const uint16_t*)(lds + ((x1 & mask) | base));
+        P[4 * g + M] = c0 | (c1 << 16);
+    }
+}
+
+// k-step KS with its first A columns read per coordinate and the rest as pairs.
+template <int KS, int A>
+__device__ __forceinline__ void mx_kstep(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
+                                         const u32x4_t* sd, uint32_t lb) {
     uint32_t P[16];
-    mx_slots<KS>(P, sd, stage, li4, tab);
+    const u32x4_t dk = sd[KS];
+    if constexpr (A > 0) col_coord<0>(P, lds, dk[0], lb); else col_pair<0>(P, lds, dk[0], lb);
+    if constexpr (A > 1) col_coord<1>(P, lds, dk[1], lb); else col_pair<1>(P, lds, dk[1], lb);
+    if constexpr (A > 2) col_coord<2>(P, lds, dk[2], lb); else col_pair<2>(P, lds, dk[2], lb);
+    if constexpr (A > 3) col_coord<3>(P, lds, dk[3], lb); else col_pair<3>(P, lds, dk[3], lb);
     const half8_t q = __builtin_bit_cast(half8_t, qa[KS * 64 + lane]);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) c[g] = mfma16(q, as_h8(P[4 * g], P[4 * g + 1], P[4 * g + 2], P[4 * g + 3]), c[g]);
+    for (int g = 0; g < 4; ++g) {
+        const half8_t kb = as_h8(P[4 * g], P[4 * g + 1], P[4 * g + 2], P[4 * g + 3]);
+        c[g] = KS == 0 ? mfma16(q, kb, f32x4_t{0.f, 0.f, 0.f, 0.f}) : mfma16(q, kb, c[g]);
+    }
+}
+
+// k-step KS of a tile; ncc (wave-uniform) = number of coordinate columns of the whole record.
+template <int KS>
+__device__ __forceinline__ void mx_kstep_any(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
+                                             const u32x4_t* sd, uint32_t lb, int ncc) {
+    const int a = ncc - 4 * KS;
+    if (a <= 0) mx_kstep<KS, 0>(c, lds, qa, lane, sd, lb);
+    else if (a == 1) mx_kstep<KS, 1>(c, lds, qa, lane, sd, lb);
+    else if (a == 2) mx_kstep<KS, 2>(c, lds, qa, lane, sd, lb);
+    else if (a == 3) mx_kstep<KS, 3>(c, lds, qa, lane, sd, lb);
+    else mx_kstep<KS, 4>(c, lds, qa, lane, sd, lb);
 }
 
 // P·V of one 32-token half S: B = W rows of this lane's head column, A = value fields (S, db, m).
@@ -942,24 +963,25 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
-// LDS arena of the matrix-core decode (byte offsets).  Loop-time regions: tables, query operands,
-// weight exchange, softmax rescale factors, and per wave the stages of the tile in flight (K
-// records, value streams, scales).  The query-prep output and the epilogue records alias the stages.
+// LDS arena of the matrix-core decode (byte offsets).  Loop-time regions: tables (at offset 0,
+// the arena being 8192-aligned, so table offsets are LDS addresses), column descriptors, value
+// centroid pairs, query operands, weight exchange, softmax rescale factors, and per wave the stage
+// of the tile in flight (K record rows -1 .. R at BGTQ_KST_ROW_BYTES stride, scales).  The query
+// prep output and the epilogue records alias the stages.
 constexpr int a16(int x) { return (x + 15) & ~15; }
 constexpr int cmax(int x, int y) { return x > y ? x : y; }
 template <int G, int R, int VB> struct MxLds {
-    static constexpr int TAB = 0;                                     // u32 [BGTQ_CB_MX_WORDS]
-    static constexpr int VLUT = a16(TAB + 4 * BGTQ_CB_MX_WORDS);      // u32 [4^VB]
+    static constexpr int TAB = 0;                                     // BGTQ_CB_MX_BYTES
+    static constexpr int DESC = a16(TAB + BGTQ_CB_MX_BYTES);          // u32 [4 lane rows][16 columns]
+    static constexpr int VLUT = DESC + 64 * 4;                        // u32 [4^VB]
     static constexpr int QA = a16(VLUT + 4 * (1 << (2 * VB)));        // u32x4 [4 k-steps][64 lanes]
     static constexpr int WX = QA + 4 * 64 * 16;                       // u32 [4 waves][16 heads][32 pairs]
     static constexpr int ALPHA = WX + 4 * 16 * 32 * 4;                // f32 [4 waves][16]
-    static constexpr int NNZ = ALPHA + 4 * 16 * 4;                    // u32
+    static constexpr int NNZ = ALPHA + 4 * 16 * 4;                    // u32 [4]: padded nonzero slots, wide slots
     static constexpr int DSC = NNZ + 16;                              // u16 [64] (prep output, unused)
-    static constexpr int KST = a16(DSC + 128);                        // per wave: R + 1 rows of 256 B
-    static constexpr int KST_W = (R + 1) * 256;
-    static constexpr int VST = KST + 4 * KST_W;                       // per wave: value streams
-    static constexpr int VST_W = VB * 1024;
-    static constexpr int SST = VST + 4 * VST_W;                       // per wave: K scales, V scales, V zeros
+    static constexpr int KST = a16(DSC + 128);                        // per wave: R + 2 rows
+    static constexpr int KST_W = (R + 2) * BGTQ_KST_ROW_BYTES;
+    static constexpr int SST = KST + 4 * KST_W;                       // per wave: K scales, V scales, V zeros
     static constexpr int SST_W = 3 * 64 * 2;
     static constexpr int QP = KST;                                    // prologue: f32 [128 G]
     static constexpr int RED = KST;                                   // epilogue: f32 [4 G PART + 4 G]
@@ -972,16 +994,14 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     static_assert(R % 4 == 0, "K records are staged in 16-byte chunks");
     using LD = MxLds<G, R, VB>;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int row = lane >> 4, col = lane & 15;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[LD::SIZE];
-    uint32_t* s_tab = (uint32_t*)(lds + LD::TAB);
+    __shared__ __attribute__((aligned(8192))) uint8_t lds[LD::SIZE];
     uint32_t* s_vlut = (uint32_t*)(lds + LD::VLUT);
     u32x4_t* s_qa = (u32x4_t*)(lds + LD::QA);
     float* s_alpha = (float*)(lds + LD::ALPHA) + wave * 16;
     uint32_t* s_nnz = (uint32_t*)(lds + LD::NNZ);
     uint8_t* kst = lds + LD::KST + wave * LD::KST_W;
-    uint8_t* vst = lds + LD::VST + wave * LD::VST_W;
     uint16_t* sst = (uint16_t*)(lds + LD::SST + wave * LD::SST_W);
     uint32_t* wx = (uint32_t*)(lds + LD::WX) + wave * 16 * 32;
 
@@ -996,11 +1016,11 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     const uint32_t* vs32 = (const uint32_t*)(a.v_scale + bh * a.n_cap);
     const uint32_t* vz32 = a.v_affine ? (const uint32_t*)(a.v_zero + bh * a.n_cap) : nullptr;
 
-    // Prologue.  Global loads of the tables and of the query go out first, then the first tile's
-    // prefetch; loads retire in order, so the table and query writes below do not wait for HBM.
+    // Prologue.  Global loads of the tables, slot descriptors and query go out first, then the
+    // first tile's prefetch; loads retire in order, so the LDS writes below do not wait for HBM.
+    // Loads are unconditional (clamped indices) so that no branch forces an early wait.
     constexpr int TAB4 = BGTQ_CB_MX_WORDS / 4;
     const u32x4_t* tab4 = (const u32x4_t*)c_mxtab;
-    // Loads are unconditional (clamped indices) so that no branch forces an early wait.
     u32x4_t tv[(TAB4 + 255) / 256];
 #pragma unroll
     for (int k = 0; k < (TAB4 + 255) / 256; ++k)
@@ -1009,45 +1029,69 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     const uint32_t vla = c_cent16[cent_base(VB) + vca], vlb = c_cent16[cent_base(VB) + vcb];
     const PrepIn<G> pin = prep_load<G, true>(a.q, a.q_dtype, a.bits, a.sigma, b, h, a.Hq, lane);
 
-    // Tile in flight, staged to LDS when the next tile starts: K chunks, value streams, and one
-    // dword of scales per lane (lanes 0..31: K scales of tokens 2l, 2l+1; lanes 32..63: V scales;
-    // V zeros in a second dword for affine values).
+    // Tile data: K chunks and one dword of scales per lane (lanes 0..31: K scales of tokens 2l,
+    // 2l+1; lanes 32..63: V scales; V zeros in a second dword for affine values) are prefetched one
+    // tile ahead and staged to LDS when their tile starts; the value streams stay in registers
+    // (each lane reads its own stream) and are loaded once the previous tile's P·V is done.
     u32x4_t kn[R / 4], vn[VB];
     uint32_t sn, zn;
-    auto fetch = [&](int64_t t) {
+    auto fetch_k = [&](int64_t t) {
         const u32x4_t* kt = (const u32x4_t*)(kc + t * (a.k_tile_bytes / 4));
-        const u32x4_t* vt = (const u32x4_t*)(vc + t * (a.v_tile_bytes / 4));
 #pragma unroll
         for (int c = 0; c < R / 4; ++c) kn[c] = kt[c * 64 + lane];
-#pragma unroll
-        for (int c = 0; c < VB; ++c) vn[c] = vt[c * 64 + lane];
         sn = (lane < 32 ? ks32 : vs32)[t * (TILE / 2) + (lane & 31)];
         zn = vz32 ? vz32[t * (TILE / 2) + (lane & 31)] : 0u;
     };
+    auto fetch_v = [&](int64_t t) {
+        const u32x4_t* vt = (const u32x4_t*)(vc + t * (a.v_tile_bytes / 4));
+#pragma unroll
+        for (int c = 0; c < VB; ++c) vn[c] = vt[c * 64 + lane];
+    };
     // Unconditional (branch-free prologue); a wave without tiles reads a tile inside the allocation
     // and never uses it.
-    fetch(t_lo + wave < t_hi ? t_lo + wave : (t_lo < a.n_tiles ? t_lo : 0));
+    {
+        const int64_t t0 = t_lo + wave < t_hi ? t_lo + wave : (t_lo < a.n_tiles ? t_lo : 0);
+        fetch_k(t0);
+        fetch_v(t0);
+    }
 
 #pragma unroll
     for (int k = 0; k < (TAB4 + 255) / 256; ++k)
-        if (threadIdx.x + 256 * k < TAB4) ((u32x4_t*)s_tab)[threadIdx.x + 256 * k] = tv[k];
+        if (threadIdx.x + 256 * k < TAB4) ((u32x4_t*)(lds + LD::TAB))[threadIdx.x + 256 * k] = tv[k];
     if (threadIdx.x < (1 << (2 * VB)))
         s_vlut[threadIdx.x] = a.v_affine ? (uint32_t)f2h((float)vca) | ((uint32_t)f2h((float)vcb) << 16) : vla | (vlb << 16);
     for (int i = threadIdx.x; i < 4 * 16 * 32; i += blockDim.x) ((uint32_t*)(lds + LD::WX))[i] = 0u;
     float* s_qp = (float*)(lds + LD::QP);
-    if (wave == 0) prep_store<G, true, 0>(pin, lane, s_qp, (uint16_t*)(lds + LD::DSC), s_nnz, nullptr);
+    if (wave == 0) {
+        prep_store<G, true, 0>(pin, lane, s_qp, (uint16_t*)(lds + LD::DSC), s_nnz, nullptr);
+        // Column descriptors: stream slot r sits in column r / 4, lane row r % 4; a column is read
+        // per coordinate when its first slot is wider than 5 bits (slots are in width order).
+        const int bw = (int)((pin.w4 >> (8 * (lane & 3))) & 0xFFu);
+        const int w = bw < 8 ? bw : 8;
+        int rank, pos, nnz;
+        block_order(w, lane, rank, pos, nnz);
+        const int ncc_w = (__popcll(__ballot(w > 5)) + 3) >> 2;
+        uint32_t* s_desc = (uint32_t*)(lds + LD::DESC);
+        if (w > 0) s_desc[(rank & 3) * 16 + (rank >> 2)] = mx_desc(pos, w, (rank >> 2) < ncc_w);
+        if (lane >= nnz) s_desc[(lane & 3) * 16 + (lane >> 2)] = mx_desc(0, 0, (lane >> 2) < ncc_w);
+        if (lane == 0) s_nnz[1] = (uint32_t)ncc_w;
+    }
     __syncthreads();
 
-    const int nks = (int)((__builtin_amdgcn_readfirstlane(*s_nnz) + 15u) >> 4);  // nonzero slots rounded up to 4
+    const int nnz_pad = (int)__builtin_amdgcn_readfirstlane(s_nnz[0]);  // nonzero slots rounded up to 4
+    const int nks = (nnz_pad + 15) >> 4;
+    const int ncc = (int)__builtin_amdgcn_readfirstlane(s_nnz[1]);      // coordinate columns
+    const u32x4_t* sd = (const u32x4_t*)(lds + LD::DESC) + 4 * row;  // this lane row's descriptors
 
-    // Query operands: lane (row col = head part, K group row): slot 16ks + 4row + e/2, coord e%2,
-    // head col/2, fp16 high part (col even) or low part (col odd).  Wave w builds k-step w.
+    // Query operands: lane (col = head part, row u), element e: coordinate e % 2 of stream slot
+    // 16 ks + 4 (e / 2) + u, head col / 2, fp16 high part (col even) or low part (col odd).  Wave w
+    // builds k-step w.
     {
         const int ks = wave;
         half8_t qa;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int sl = 16 * ks + 4 * row + (e >> 1), hd = col >> 1;
+            const int sl = 16 * ks + 4 * (e >> 1) + row, hd = col >> 1;
             const float qv = hd < G ? s_qp[sl * 2 * G + (e & 1) * G + hd] : 0.f;
             const _Float16 hi = (_Float16)qv;
             const _Float16 lo = (_Float16)(qv - (float)hi);
@@ -1061,14 +1105,16 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     f32x4_t o[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint32_t lb = (uint32_t)(LD::KST + wave * LD::KST_W) + 4u * (uint32_t)col;
+    asm volatile("" : "+v"(lb));  // keep the stage base inside lb: one add per column address
 
     for (int64_t t = t_lo + wave; t < t_hi; t += 4) {
-        // Stage the tile: K records, value streams, scales (transposed: token u at (u%16)*4 + u/16).
+        // Stage the tile: K rows (row rho of the record at stage row rho + 1), scales (transposed:
+        // token u at (u%16)*4 + u/16).
         wave_lds_fence();
 #pragma unroll
-        for (int c = 0; c < R / 4; ++c) ((u32x4_t*)kst)[c * 64 + lane] = kn[c];
-#pragma unroll
-        for (int c = 0; c < VB; ++c) ((u32x4_t*)vst)[c * 64 + lane] = vn[c];
+        for (int c = 0; c < R / 4; ++c)
+            *(u32x4_t*)(kst + (4 * c + row + 1) * BGTQ_KST_ROW_BYTES + 16 * col) = kn[c];
         {
             const int u0 = 2 * (lane & 31), reg = lane < 32 ? 0 : 64;
             sst[reg + (u0 & 15) * 4 + (u0 >> 4)] = (uint16_t)(sn & 0xFFFFu);
@@ -1080,24 +1126,18 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         }
         wave_lds_fence();
         asm volatile("" ::: "memory");
-        if (t + 4 < t_hi) fetch(t + 4);
+        if (t + 4 < t_hi) fetch_k(t + 4);
 
         // q·k on the matrix cores
         f32x4_t c[4];
+        if (nks == 0) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) c[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // Slot entries are loaded (scalar, cached) per k-step, not hoisted out of the tile loop:
-        // 64 entries would not fit in scalar registers.
-        uint32_t sdo = (uint32_t)h * 64 * BGTQ_SLOT_WORDS;
-        asm volatile("" : "+s"(sdo));
-        const cu32_t* sd = (const cu32_t*)(a.slots + sdo);
-        uint32_t li4 = 4 * lane;
-        asm volatile("" : "+v"(li4));
-        const uint8_t* tab = (const uint8_t*)s_tab;
-        if (nks > 0) mx_qk<0>(c, s_qa, lane, sd, kst, li4, tab);
-        if (nks > 1) mx_qk<1>(c, s_qa, lane, sd, kst, li4, tab);
-        if (nks > 2) mx_qk<2>(c, s_qa, lane, sd, kst, li4, tab);
-        if (nks > 3) mx_qk<3>(c, s_qa, lane, sd, kst, li4, tab);
+            for (int g = 0; g < 4; ++g) c[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        if (nks > 0) mx_kstep_any<0>(c, lds, s_qa, lane, sd, lb, ncc);
+        if (nks > 1) mx_kstep_any<1>(c, lds, s_qa, lane, sd, lb, ncc);
+        if (nks > 2) mx_kstep_any<2>(c, lds, s_qa, lane, sd, lb, ncc);
+        if (nks > 3) mx_kstep_any<3>(c, lds, s_qa, lane, sd, lb, ncc);
 
         // softmax over the tile: lane holds tokens 16g + col, heads 2row, 2row + 1
         float sk[4], sv[4], sz[4];
@@ -1161,15 +1201,15 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         }
         wave_lds_fence();
 
-        // P·V on the matrix cores; this lane's value stream comes back from the stage
+        // P·V on the matrix cores from this lane's value stream, then the next tile's streams
         uint32_t vs[4 * VB];
 #pragma unroll
         for (int c = 0; c < VB; ++c) {
-            const u32x4_t v = ((const u32x4_t*)vst)[c * 64 + lane];
-            vs[4 * c] = v[0]; vs[4 * c + 1] = v[1]; vs[4 * c + 2] = v[2]; vs[4 * c + 3] = v[3];
+            vs[4 * c] = vn[c][0]; vs[4 * c + 1] = vn[c][1]; vs[4 * c + 2] = vn[c][2]; vs[4 * c + 3] = vn[c][3];
         }
         mx_pv<VB, 0>(o, vs, s_vlut, wx, lane);
         mx_pv<VB, 1>(o, vs, s_vlut, wx, lane);
+        if (t + 4 < t_hi) fetch_v(t + 4);
     }
 
     // Epilogue: row sums of l and the zero term, O^T to LDS (over the stages), merge the waves.
@@ -1327,54 +1367,6 @@ __global__ __launch_bounds__(256) void k_energy(const EnergyArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Slot table of one (layer, kv head) for the matrix-core decode: entry r (r-th nonzero block in
-// width order, ties by block index; padding entries past the last one are width 1 at bit 0) is
-// one dword  pos%32 | (pos/32) << 8 | W << 12 | B << 16:  the bit offset in the low five bits
-// (an alignbit shift as is), the record dword times 256 (the stage row's byte offset) after a
-// mask, the extract width W and the table byte offset B.  The pair path (W = 2w, B = the pair
-// table of width w) serves groups of four entries whose widest member is <= 5 wide; the other
-// groups take two per-coordinate reads (W = w, B = the fp16 centroid table of width w, at byte
-// SLOT_COORD0 and up).  Offsets match the decode LDS image.
-__device__ void write_slot_table(const uint8_t* bits, uint32_t* slots, int lane, int* s_w, int* s_p) {
-    const int bw = bits[lane];
-    const int w = bw < 8 ? bw : 8;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int rank = 0, pos = 0, nnz = 0;
-#pragma unroll
-    for (int v = 0; v <= 8; ++v) {
-        const uint64_t mk = __ballot(w == v);
-        const int c = __popcll(mk);
-        if (v == 0) nnz = 64 - c;
-        if (v > w) {
-            rank += c;
-            pos += 2 * v * c;
-        } else if (v == w) {
-            const int cl = __popcll(mk & lt);
-            rank += cl;
-            pos += 2 * v * cl;
-        }
-    }
-    if (w > 0) {
-        s_w[rank] = w;
-        s_p[rank] = pos;
-    }
-    if (lane >= nnz) {
-        s_w[lane] = 1;
-        s_p[lane] = 0;
-    }
-    __syncthreads();
-    const int r = lane, wr = s_w[r], pr = s_p[r], lead = s_w[r & ~3];
-    uint32_t W, B;
-    if (lead <= 5) {
-        W = 2u * wr;
-        B = 4u * (((1u << (2 * wr)) - 4u) / 3u);
-    } else {
-        W = wr;
-        B = SLOT_COORD0 + 2u * ((1u << wr) - 2u);
-    }
-    slots[r] = (uint32_t)(pr & 31) | ((uint32_t)(pr >> 5) << 8) | (W << 12) | (B << 16);
-}
-
 // ---------------------------------------------------------------------------------------------
 // Quantize-append.  The float32 steps are spelled out one IEEE operation at a time (no
 // contraction) so the codes and fp16 scales are reproducible bit for bit.
@@ -1431,10 +1423,6 @@ __device__ __forceinline__ void affine_group(const float* x, int n, int bits, ui
 
 __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
     const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-    if (blockIdx.x == 0 && b == 0 && (a.which & 1) && a.k_mode == BGTQ_K_BLOCKGTQ) {
-        __shared__ int s_tw[64], s_tp[64];
-        write_slot_table(a.bits + h * 64, a.slots + (size_t)h * 64 * BGTQ_SLOT_WORDS, lane, s_tw, s_tp);
-    }
     const int64_t tile = a.tile0[b] + blockIdx.x;
     if (tile * TILE >= a.pos_hi[b]) return;  // whole workgroup beyond this sequence's range
     const int64_t pos = tile * TILE + lane;
@@ -1617,7 +1605,7 @@ hipError_t launch_energy(const EnergyArgs& a, hipStream_t s) {
 
 hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_t s) {
     if (max_tiles <= 0) return hipSuccess;
-    if ((a.which & 1) && a.k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma || !a.inv_sigma || !a.slots))
+    if ((a.which & 1) && a.k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma || !a.inv_sigma))
         return hipErrorInvalidValue;
     return launch_main(k_quant, dim3((unsigned)max_tiles, a.Hkv, B), dim3(64), s, a);
 }
@@ -1693,7 +1681,7 @@ static hipError_t launch_dec_g(const DecodeArgs& a, int B, int k_mode, int R, in
 hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t s) {
     if (!a.k_codes || !a.v_codes || !a.k_scale || !a.v_scale || !a.q || !a.part || B < 1 || B > BGTQ_MAXB)
         return hipErrorInvalidValue;
-    if (k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma || !a.slots)) return hipErrorInvalidValue;
+    if (k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma)) return hipErrorInvalidValue;
     if (k_mode == BGTQ_K_AFFINE && !a.k_zero) return hipErrorInvalidValue;
     if (a.v_affine && !a.v_zero) return hipErrorInvalidValue;
     switch (a.G) {

@@ -172,23 +172,46 @@ int main(int argc, char** argv) {
     std::fprintf(f, "}\n#define BGTQ_CB_THRESHOLD_F32_INIT {");
     for (size_t i = 0; i < thr.size(); ++i) std::fprintf(f, "%s0x%08" PRIx32 "u", i ? "," : "", thr[i]);
     std::fprintf(f, "}\n");
-    // Decode-side LDS image: pair tables for widths 1..5 (entry a | b << w = fp16 c[a] | fp16 c[b] << 16,
-    // table of width w at entry (4^w - 4) / 3), then every fp16 centroid, two per dword.
-    std::vector<uint32_t> img;
+    // Decode-side LDS image (8 KiB).  Pair table of width w (entry a | b << w = fp16 c[a] | fp16 c[b] << 16,
+    // 4 bytes) at byte 4 * 4^w; fp16 coordinate table of width w (entry a = c[a], 2 bytes) at byte
+    // 2048 + 2^(w+1).  Each table starts at a multiple of its size and its offset is the index mask
+    // plus a constant (4 for pairs, 2050 for coordinates), so an entry address is (bits & mask) | base
+    // with base = mask + constant; a zero entry sits at 4 and at 2050 for empty slots (mask 0).
+    const size_t img_bytes = 8192;
+    std::vector<uint8_t> img(img_bytes, 0);
+    auto put16 = [&](size_t at, uint16_t v) { img[at] = (uint8_t)(v & 0xFF); img[at + 1] = (uint8_t)(v >> 8); };
+    std::vector<int> owner(img_bytes, 0);
+    auto claim = [&](size_t at, size_t n, int id) {
+        for (size_t i = at; i < at + n; ++i) {
+            if (i >= img_bytes || owner[i]) return false;
+            owner[i] = id;
+        }
+        return true;
+    };
+    if (!claim(4, 4, 1) || !claim(2050, 2, 2)) { std::fprintf(stderr, "zero entries collide\n"); return 1; }
     for (int w = 1; w <= 5; ++w) {
         const int cb = (1 << w) - 2;
-        for (int idx = 0; idx < (1 << (2 * w)); ++idx)
-            img.push_back((uint32_t)cent[cb + (idx & ((1 << w) - 1))] | ((uint32_t)cent[cb + (idx >> w)] << 16));
+        const size_t n = (size_t)1 << (2 * w), at = 4 * n;
+        if (!claim(at, 4 * n, 10 + w)) { std::fprintf(stderr, "pair table %d collides\n", w); return 1; }
+        for (size_t idx = 0; idx < n; ++idx) {
+            put16(at + 4 * idx, cent[cb + (idx & ((1u << w) - 1))]);
+            put16(at + 4 * idx + 2, cent[cb + (idx >> w)]);
+        }
     }
-    const size_t n_pair = img.size();
-    for (size_t i = 0; i < 512; i += 2) {
-        const uint32_t lo = i < cent.size() ? cent[i] : 0u, hi = i + 1 < cent.size() ? cent[i + 1] : 0u;
-        img.push_back(lo | (hi << 16));
+    for (int w = 1; w <= 8; ++w) {
+        const int cb = (1 << w) - 2;
+        const size_t n = (size_t)1 << w, at = 2048 + 2 * n;
+        if (!claim(at, 2 * n, 20 + w)) { std::fprintf(stderr, "coordinate table %d collides\n", w); return 1; }
+        for (size_t idx = 0; idx < n; ++idx) put16(at + 2 * idx, cent[cb + idx]);
     }
-    while (img.size() % 4) img.push_back(0u);
-    std::fprintf(f, "#define BGTQ_CB_PAIR_ENTRIES %zu\n#define BGTQ_CB_MX_WORDS %zu\n#define BGTQ_CB_MX_INIT {", n_pair,
-                 img.size());
-    for (size_t i = 0; i < img.size(); ++i) std::fprintf(f, "%s0x%08" PRIx32 "u", i ? "," : "", img[i]);
+    std::fprintf(f, "#define BGTQ_CB_MX_BYTES %zu\n#define BGTQ_CB_MX_WORDS %zu\n", img.size(), img.size() / 4);
+    std::fprintf(f, "#define BGTQ_CB_MX_PAIR_BIAS 4u\n#define BGTQ_CB_MX_COORD_BIAS 2050u\n");
+    std::fprintf(f, "#define BGTQ_CB_MX_INIT {");
+    for (size_t i = 0; i < img.size(); i += 4) {
+        const uint32_t v = (uint32_t)img[i] | ((uint32_t)img[i + 1] << 8) | ((uint32_t)img[i + 2] << 16) |
+                           ((uint32_t)img[i + 3] << 24);
+        std::fprintf(f, "%s0x%08" PRIx32 "u", i ? "," : "", v);
+    }
     std::fprintf(f, "}\n");
     std::fclose(f);
     return 0;

@@ -33,7 +33,7 @@ namespace bgtq {
 
 hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t) {
     if (!a.k_codes || !a.v_codes || !a.k_scale || !a.v_scale || !a.q || !a.part) return bad("decode: null pointer");
-    if (k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma || !a.slots)) return bad("decode: null key metadata");
+    if (k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma)) return bad("decode: null key metadata");
     if (k_mode == BGTQ_K_AFFINE && !a.k_zero) return bad("decode: null k_zero");
     if (a.v_affine && !a.v_zero) return bad("decode: null v_zero");
     if (B < 1 || B > BGTQ_MAXB || a.Hkv < 1 || a.Hq != a.Hkv * a.G) return bad("decode: geometry");
@@ -79,7 +79,7 @@ hipError_t launch_energy(const EnergyArgs& a, hipStream_t) {
 hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_t) {
     if (max_tiles <= 0) return hipSuccess;
     if (!a.src_k || !a.src_v || !a.k_codes || !a.v_codes || !a.k_scale || !a.v_scale) return bad("quant: null");
-    if (a.k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma || !a.inv_sigma || !a.slots)) return bad("quant: null metadata");
+    if (a.k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma || !a.inv_sigma)) return bad("quant: null metadata");
     if (a.k_mode == BGTQ_K_AFFINE && !a.k_zero) return bad("quant: null k_zero");
     if (a.v_mode == BGTQ_V_AFFINE && !a.v_zero) return bad("quant: null v_zero");
     for (int b = 0; b < B; ++b) {

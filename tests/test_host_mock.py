@@ -24,7 +24,7 @@ def _desc(nt, **kw):
     base.update(kw)
     for k, v in base.items():
         setattr(d, k, v)
-    ptrs = ["k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma", "slots"]
+    ptrs = ["k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma"]
     if base["k_mode"] == 1:
         ptrs.append("k_zero")
     if base["v_mode"] == 1:

@@ -85,14 +85,12 @@ def test_cache_bytes_geometry():
     assert nb(_lib.BUF_V_CODES) == 2 * 3 * 2 * 4096 * 48          # 3 bits x 128
     assert nb(_lib.BUF_K_SCALE) == 2 * 3 * 2 * 4096 * 2
     assert nb(_lib.BUF_K_ZERO) == 0
-    assert nb(_lib.BUF_SLOTS) == 2 * 2 * 64 * 4                   # slot table, [L][Hkv][64] uint32
     d = _desc(k_mode=1, k_bits=4, k_group=32, v_mode=1, v_bits=2, n_recent=256)
     assert nb(_lib.BUF_K_CODES) == 2 * 3 * 2 * 4096 * 64
     assert nb(_lib.BUF_K_SCALE) == 2 * 3 * 2 * 4096 * 4 * 2
     assert nb(_lib.BUF_K_ZERO) == nb(_lib.BUF_K_SCALE)
     assert nb(_lib.BUF_V_ZERO) == 2 * 3 * 2 * 4096 * 2
     assert nb(_lib.BUF_RECENT_K) == 2 * 3 * 2 * 256 * 128 * 2
-    assert nb(_lib.BUF_SLOTS) == 0                                # affine keys have no slot table
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -112,13 +110,13 @@ def test_append_and_decode_validate_before_launch():
     nt = np.zeros((2, 3), np.int64)
     d.n_tokens = nt.ctypes.data_as(C.POINTER(C.c_int64))
     fake = C.c_void_p(0x1000)
-    # NULL cache buffers; then everything but the slot table
+    # NULL cache buffers; then everything but the inverse key scales
     assert P.lib.bgtq_quantize_append(C.byref(d), 0, fake, fake, 2, 10, None, None) == P.E_INVALID
-    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma"):
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma"):
         setattr(d, name, 0x1000)
     assert P.lib.bgtq_quantize_append(C.byref(d), 0, fake, fake, 2, 10, None, None) == P.E_INVALID
-    assert b"slots" in P.lib.bgtq_last_error()
-    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma", "slots"):
+    assert b"inv_sigma" in P.lib.bgtq_last_error()
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma"):
         setattr(d, name, 0x1000)
     assert P.lib.bgtq_quantize_append(C.byref(d), 5, fake, fake, 2, 10, None, None) == P.E_INVALID  # layer
     assert P.lib.bgtq_quantize_append(C.byref(d), 0, fake, fake, 9, 10, None, None) == P.E_INVALID  # dtype
@@ -134,7 +132,7 @@ def test_append_and_decode_validate_before_launch():
     assert P.lib.bgtq_decode_attention(C.byref(d), 0, fake, 2, out, ws, 16, 4, None) == P.E_INVALID
     # unsupported decode format (budget 208 -> 13-dword records has no kernel)
     d2 = _desc(budget_units=208)
-    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma", "slots"):
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma"):
         setattr(d2, name, 0x1000)
     d2.n_tokens = nt.ctypes.data_as(C.POINTER(C.c_int64))
     assert P.lib.bgtq_decode_attention(C.byref(d2), 0, fake, 2, out, ws, 1 << 30, 4, None) == P.E_UNSUPPORTED
