@@ -198,6 +198,15 @@ __device__ __forceinline__ uint32_t vfield(const uint32_t* r) {
         return __builtin_amdgcn_alignbit(r[w + 1], r[w], sh) & ((1u << nb) - 1u);
     }
 }
+// The same field times 4 (a byte offset into a table of dwords), one shift and one AND.
+template <int VB, int F>
+__device__ __forceinline__ uint32_t vfield4(const uint32_t* r) {
+    constexpr int bit = 2 * VB * F, w = bit / 32, sh = bit % 32, nb = 2 * VB;
+    constexpr uint32_t m4 = ((1u << nb) - 1u) << 2;
+    if constexpr (sh + nb > 32) return __builtin_amdgcn_alignbit(r[w + 1], r[w], sh - 2) & m4;
+    else if constexpr (sh >= 2) return (r[w] >> (sh - 2)) & m4;
+    else return (r[w] << (2 - sh)) & m4;
+}
 
 // P·V of one tile for lane L = dd + 16j over its value stream (lane-stream layout): field
 // (s, db, m) holds the codes of dim 16db + dd for the token pair (p, p + 32), p = 16s + 4j + m;
@@ -856,13 +865,21 @@ __device__ __forceinline__ uint32_t mx_desc(int pos, int w, bool coord) {
     return sh | (fw << 5) | (sh1 << 10) | ((uint32_t)(rr + 1) * BGTQ_KST_ROW_BYTES << 16);
 }
 
+// ((1 << (width & 31)) - 1) << OFF in one v_bfm_b32.
+template <int OFF>
+__device__ __forceinline__ uint32_t bfm(uint32_t width) {
+    uint32_t r;
+    asm("v_bfm_b32 %0, %1, %2" : "=v"(r) : "v"(width), "n"(OFF));
+    return r;
+}
+
 // One column of a k-step read as coordinate pairs: per token group g a 64-bit window of two stage
 // rows, alignbit, and_or into the pair table of the slot's width, one 4-byte read.  lb: this lane's
 // token column in the wave's K stage.
 template <int M>
 __device__ __forceinline__ void col_pair(uint32_t (&P)[16], const uint8_t* lds, uint32_t dsc, uint32_t lb) {
     const uint32_t ad = (dsc >> 16) + lb;
-    const uint32_t mask = ((1u << ((dsc >> 5) & 31u)) - 1u) << 2;
+    const uint32_t mask = bfm<2>(dsc >> 5);
     const uint32_t base = mask + BGTQ_CB_MX_PAIR_BIAS;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -878,7 +895,7 @@ __device__ __forceinline__ void col_pair(uint32_t (&P)[16], const uint8_t* lds, 
 template <int M>
 __device__ __forceinline__ void col_coord(uint32_t (&P)[16], const uint8_t* lds, uint32_t dsc, uint32_t lb) {
     const uint32_t ad = (dsc >> 16) + lb;
-    const uint32_t mask = ((1u << ((dsc >> 5) & 31u)) - 1u) << 1;
+    const uint32_t mask = bfm<1>(dsc >> 5);
     const uint32_t base = mask + BGTQ_CB_MX_COORD_BIAS;
     const uint32_t sh1 = (dsc >> 10) & 63u;
 #pragma unroll
@@ -924,27 +941,21 @@ __device__ __forceinline__ void mx_kstep_any(f32x4_t (&c)[4], const uint8_t* lds
 }
 
 // P·V of one 32-token half S: B = W rows of this lane's head column, A = value fields (S, db, m).
+template <int VB, int F>
+__device__ __forceinline__ uint32_t vpair(const uint32_t* vs, const uint32_t* vlut) {
+    return *(const uint32_t*)((const uint8_t*)vlut + vfield4<VB, F>(vs));
+}
 template <int VB, int S>
 __device__ __forceinline__ void mx_pv(f32x4_t (&o)[8], const uint32_t* vs, const uint32_t* vlut, const uint32_t* wx,
                                       int lane) {
     const u32x4_t wq = *(const u32x4_t*)(wx + (lane & 15) * 32 + 16 * S + 4 * (lane >> 4));
     const half8_t wb = __builtin_bit_cast(half8_t, wq);
-    o[0] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 0) * 4>(vs)], vlut[vfield<VB, (S * 8 + 0) * 4 + 1>(vs)],
-                        vlut[vfield<VB, (S * 8 + 0) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 0) * 4 + 3>(vs)]), wb, o[0]);
-    o[1] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 1) * 4>(vs)], vlut[vfield<VB, (S * 8 + 1) * 4 + 1>(vs)],
-                        vlut[vfield<VB, (S * 8 + 1) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 1) * 4 + 3>(vs)]), wb, o[1]);
-    o[2] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 2) * 4>(vs)], vlut[vfield<VB, (S * 8 + 2) * 4 + 1>(vs)],
-                        vlut[vfield<VB, (S * 8 + 2) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 2) * 4 + 3>(vs)]), wb, o[2]);
-    o[3] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 3) * 4>(vs)], vlut[vfield<VB, (S * 8 + 3) * 4 + 1>(vs)],
-                        vlut[vfield<VB, (S * 8 + 3) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 3) * 4 + 3>(vs)]), wb, o[3]);
-    o[4] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 4) * 4>(vs)], vlut[vfield<VB, (S * 8 + 4) * 4 + 1>(vs)],
-                        vlut[vfield<VB, (S * 8 + 4) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 4) * 4 + 3>(vs)]), wb, o[4]);
-    o[5] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 5) * 4>(vs)], vlut[vfield<VB, (S * 8 + 5) * 4 + 1>(vs)],
-                        vlut[vfield<VB, (S * 8 + 5) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 5) * 4 + 3>(vs)]), wb, o[5]);
-    o[6] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 6) * 4>(vs)], vlut[vfield<VB, (S * 8 + 6) * 4 + 1>(vs)],
-                        vlut[vfield<VB, (S * 8 + 6) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 6) * 4 + 3>(vs)]), wb, o[6]);
-    o[7] = mfma16(as_h8(vlut[vfield<VB, (S * 8 + 7) * 4>(vs)], vlut[vfield<VB, (S * 8 + 7) * 4 + 1>(vs)],
-                        vlut[vfield<VB, (S * 8 + 7) * 4 + 2>(vs)], vlut[vfield<VB, (S * 8 + 7) * 4 + 3>(vs)]), wb, o[7]);
+#define BGTQ_PV(DB)                                                                                          \
+    o[DB] = mfma16(as_h8(vpair<VB, (S * 8 + DB) * 4>(vs, vlut), vpair<VB, (S * 8 + DB) * 4 + 1>(vs, vlut),      \
+                         vpair<VB, (S * 8 + DB) * 4 + 2>(vs, vlut), vpair<VB, (S * 8 + DB) * 4 + 3>(vs, vlut)), \
+                   wb, o[DB])
+    BGTQ_PV(0); BGTQ_PV(1); BGTQ_PV(2); BGTQ_PV(3); BGTQ_PV(4); BGTQ_PV(5); BGTQ_PV(6); BGTQ_PV(7);
+#undef BGTQ_PV
 }
 
 // Max over the 16 lanes of a row (DPP row rotations).
@@ -1015,8 +1026,9 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     const uint32_t* ks32 = (const uint32_t*)(a.k_scale + bh * a.n_cap);  // fp16 pairs (token 2i, 2i + 1)
     const uint32_t* vs32 = (const uint32_t*)(a.v_scale + bh * a.n_cap);
     const uint32_t* vz32 = a.v_affine ? (const uint32_t*)(a.v_zero + bh * a.n_cap) : nullptr;
+    const bool vaff = a.v_affine != 0;
 
-    // Prologue.  Global loads of the tables, slot descriptors and query go out first, then the
+    // Prologue.  Global loads of the tables and the query go out first, then the
     // first tile's prefetch; loads retire in order, so the LDS writes below do not wait for HBM.
     // Loads are unconditional (clamped indices) so that no branch forces an early wait.
     constexpr int TAB4 = BGTQ_CB_MX_WORDS / 4;
@@ -1060,7 +1072,8 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         if (threadIdx.x + 256 * k < TAB4) ((u32x4_t*)(lds + LD::TAB))[threadIdx.x + 256 * k] = tv[k];
     if (threadIdx.x < (1 << (2 * VB)))
         s_vlut[threadIdx.x] = a.v_affine ? (uint32_t)f2h((float)vca) | ((uint32_t)f2h((float)vcb) << 16) : vla | (vlb << 16);
-    for (int i = threadIdx.x; i < 4 * 16 * 32; i += blockDim.x) ((uint32_t*)(lds + LD::WX))[i] = 0u;
+#pragma unroll
+    for (int i = threadIdx.x; i < 4 * 16 * 32 / 4; i += 256) ((u32x4_t*)(lds + LD::WX))[i] = u32x4_t{0u, 0u, 0u, 0u};
     float* s_qp = (float*)(lds + LD::QP);
     if (wave == 0) {
         prep_store<G, true, 0>(pin, lane, s_qp, (uint16_t*)(lds + LD::DSC), s_nnz, nullptr);
@@ -1140,27 +1153,35 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         if (nks > 3) mx_kstep_any<3>(c, lds, s_qa, lane, sd, lb, ncc);
 
         // softmax over the tile: lane holds tokens 16g + col, heads 2row, 2row + 1
-        float sk[4], sv[4], sz[4];
+        float sk[4], sv[4], sz[4] = {0.f, 0.f, 0.f, 0.f};
         {
             const uint2 k2 = *(const uint2*)(sst + col * 4), v2 = *(const uint2*)(sst + 64 + col * 4);
-            const uint2 z2 = *(const uint2*)(sst + 128 + col * 4);
             sk[0] = h2f(k2.x & 0xFFFFu); sk[1] = h2f(k2.x >> 16); sk[2] = h2f(k2.y & 0xFFFFu); sk[3] = h2f(k2.y >> 16);
             sv[0] = h2f(v2.x & 0xFFFFu); sv[1] = h2f(v2.x >> 16); sv[2] = h2f(v2.y & 0xFFFFu); sv[3] = h2f(v2.y >> 16);
-            sz[0] = h2f(z2.x & 0xFFFFu); sz[1] = h2f(z2.x >> 16); sz[2] = h2f(z2.y & 0xFFFFu); sz[3] = h2f(z2.y >> 16);
-        }
-        float z[4][2], tmax[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const bool valid = t * TILE + 16 * g + col < n_packed;
-            // scales of tokens past the end are never written: keep them out of the arithmetic
-            sv[g] = valid ? sv[g] : 0.f;
-            sz[g] = valid ? sz[g] : 0.f;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                z[g][hh] = valid ? sk[g] * (c[g][2 * hh] + c[g][2 * hh + 1]) : -INFINITY;
-                tmax[hh] = fmaxf(tmax[hh], z[g][hh]);
+            if (vaff) {
+                const uint2 z2 = *(const uint2*)(sst + 128 + col * 4);
+                sz[0] = h2f(z2.x & 0xFFFFu); sz[1] = h2f(z2.x >> 16); sz[2] = h2f(z2.y & 0xFFFFu); sz[3] = h2f(z2.y >> 16);
             }
         }
+        float z[4][2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) z[g][hh] = sk[g] * (c[g][2 * hh] + c[g][2 * hh + 1]);
+        if ((t + 1) * TILE > n_packed) {  // the sequence ends inside this tile
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                // scales of tokens past the end are never written: keep them out of the arithmetic
+                if (t * TILE + 16 * g + col >= n_packed) {
+                    sv[g] = 0.f;
+                    sz[g] = 0.f;
+                    z[g][0] = z[g][1] = -INFINITY;
+                }
+            }
+        }
+        float tmax[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) tmax[hh] = fmaxf(fmaxf(z[0][hh], z[1][hh]), fmaxf(z[2][hh], z[3][hh]));
         if (__ballot(tmax[0] > m[0] || tmax[1] > m[1])) {
             float alpha[2];
 #pragma unroll
@@ -1188,7 +1209,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
             for (int hh = 0; hh < 2; ++hh) {
                 const float p = __builtin_amdgcn_exp2f(z[g][hh] - m[hh]);
                 l[hh] += p;
-                zs[hh] += p * sz[g];
+                if (vaff) zs[hh] += p * sz[g];
                 wh[g][hh] = f2h(p * sv[g]);
             }
         }
