@@ -301,6 +301,7 @@ __device__ __forceinline__ void merge_waves4(const float* red, float* sc, float*
             sc[wv * G + h] = f;
             L += f * red[(wv * G + h) * PART + 129];
         }
+        // partials are read once, by the split merge: stream them past the caches
         float* dst = part + ((size_t)h * n_parts + split) * PART;
         dst[128] = M;
         dst[129] = L;
@@ -848,8 +849,7 @@ __device__ __forceinline__ half8_t as_h8(uint32_t a, uint32_t b, uint32_t c, uin
 __device__ __forceinline__ f32x4_t mfma16(half8_t a, half8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-// Column descriptor of one stream slot (one dword, built in the prologue; a lane reads the four of
-// its k-step with one 16-byte LDS read):
+// Column descriptor of one stream slot (one dword, built in the prologue, held in VGPRs):
 //   bits 0..4   alignbit shift that moves the field (pair) or the first code (coordinates) to bit
 //               2 (pair) or bit 1 (coordinates) of the 64-bit window
 //   bits 5..9   field width: 2w for a pair column, w for a coordinate column (0: empty slot)
@@ -913,7 +913,7 @@ __device__ __forceinline__ void col_coord(uint32_t (&P)[16], const uint8_t* lds,
 // k-step KS with its first A columns read per coordinate and the rest as pairs.
 template <int KS, int A>
 __device__ __forceinline__ void mx_kstep(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
-                                         const u32x4_t* sd, uint32_t lb) {
+                                         const u32x4_t (&sd)[4], uint32_t lb) {
     uint32_t P[16];
     const u32x4_t dk = sd[KS];
     if constexpr (A > 0) col_coord<0>(P, lds, dk[0], lb); else col_pair<0>(P, lds, dk[0], lb);
@@ -931,7 +931,7 @@ __device__ __forceinline__ void mx_kstep(f32x4_t (&c)[4], const uint8_t* lds, co
 // k-step KS of a tile; ncc (wave-uniform) = number of coordinate columns of the whole record.
 template <int KS>
 __device__ __forceinline__ void mx_kstep_any(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
-                                             const u32x4_t* sd, uint32_t lb, int ncc) {
+                                             const u32x4_t (&sd)[4], uint32_t lb, int ncc) {
     const int a = ncc - 4 * KS;
     if (a <= 0) mx_kstep<KS, 0>(c, lds, qa, lane, sd, lb);
     else if (a == 1) mx_kstep<KS, 1>(c, lds, qa, lane, sd, lb);
@@ -1094,7 +1094,9 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     const int nnz_pad = (int)__builtin_amdgcn_readfirstlane(s_nnz[0]);  // nonzero slots rounded up to 4
     const int nks = (nnz_pad + 15) >> 4;
     const int ncc = (int)__builtin_amdgcn_readfirstlane(s_nnz[1]);      // coordinate columns
-    const u32x4_t* sd = (const u32x4_t*)(lds + LD::DESC) + 4 * row;  // this lane row's descriptors
+    u32x4_t sd[4];  // this lane row's column descriptors, k-step by k-step
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sd[k] = ((const u32x4_t*)(lds + LD::DESC))[4 * row + k];
 
     // Query operands: lane (col = head part, row u), element e: coordinate e % 2 of stream slot
     // 16 ks + 4 (e / 2) + u, head col / 2, fp16 high part (col even) or low part (col odd).  Wave w
