@@ -593,7 +593,8 @@ __device__ __forceinline__ PrepIn<G> prep_load(const void* q, int dtype, const u
 }
 
 template <int G, bool SORTED, int KG>
-__device__ void prep_store(const PrepIn<G>& in, int lane, float* qp, uint16_t* dsc16, uint32_t* nnz_pad, float* qs) {
+__device__ void prep_store(const PrepIn<G>& in, int lane, float* qp, uint16_t* dsc16, uint32_t* nnz_pad, float* qs,
+                           int3* order = nullptr) {
     float q0[G], q1[G];
     if (in.dtype == BGTQ_F32) {
 #pragma unroll
@@ -625,6 +626,7 @@ __device__ void prep_store(const PrepIn<G>& in, int lane, float* qp, uint16_t* d
         const float sg = in.sg;
         int rank, pos, nnz;
         block_order(w, lane, rank, pos, nnz);
+        if (order) *order = int3{rank, pos, nnz};
         if (w > 0) {
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
@@ -1031,6 +1033,8 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     // Prologue.  Global loads of the tables and the query go out first, then the
     // first tile's prefetch; loads retire in order, so the LDS writes below do not wait for HBM.
     // Loads are unconditional (clamped indices) so that no branch forces an early wait.
+    // The query comes first: wave 0's preparation waits only for it.
+    const PrepIn<G> pin = prep_load<G, true>(a.q, a.q_dtype, a.bits, a.sigma, b, h, a.Hq, lane);
     constexpr int TAB4 = BGTQ_CB_MX_WORDS / 4;
     const u32x4_t* tab4 = (const u32x4_t*)c_mxtab;
     u32x4_t tv[(TAB4 + 255) / 256];
@@ -1039,7 +1043,6 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         tv[k] = tab4[threadIdx.x + 256 * k < TAB4 ? threadIdx.x + 256 * k : 0];
     const uint32_t vca = threadIdx.x & ((1 << VB) - 1), vcb = (threadIdx.x >> VB) & ((1 << VB) - 1);
     const uint32_t vla = c_cent16[cent_base(VB) + vca], vlb = c_cent16[cent_base(VB) + vcb];
-    const PrepIn<G> pin = prep_load<G, true>(a.q, a.q_dtype, a.bits, a.sigma, b, h, a.Hq, lane);
 
     // Tile data: K chunks and one dword of scales per lane (lanes 0..31: K scales of tokens 2l,
     // 2l+1; lanes 32..63: V scales; V zeros in a second dword for affine values) are prefetched one
@@ -1076,13 +1079,13 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     for (int i = threadIdx.x; i < 4 * 16 * 32 / 4; i += 256) ((u32x4_t*)(lds + LD::WX))[i] = u32x4_t{0u, 0u, 0u, 0u};
     float* s_qp = (float*)(lds + LD::QP);
     if (wave == 0) {
-        prep_store<G, true, 0>(pin, lane, s_qp, (uint16_t*)(lds + LD::DSC), s_nnz, nullptr);
+        int3 ord;
+        prep_store<G, true, 0>(pin, lane, s_qp, (uint16_t*)(lds + LD::DSC), s_nnz, nullptr, &ord);
         // Column descriptors: stream slot r sits in column r / 4, lane row r % 4; a column is read
         // per coordinate when its first slot is wider than 5 bits (slots are in width order).
         const int bw = (int)((pin.w4 >> (8 * (lane & 3))) & 0xFFu);
         const int w = bw < 8 ? bw : 8;
-        int rank, pos, nnz;
-        block_order(w, lane, rank, pos, nnz);
+        const int rank = ord.x, pos = ord.y, nnz = ord.z;
         const int ncc_w = (__popcll(__ballot(w > 5)) + 3) >> 2;
         uint32_t* s_desc = (uint32_t*)(lds + LD::DESC);
         if (w > 0) s_desc[(rank & 3) * 16 + (rank >> 2)] = mx_desc(pos, w, (rank >> 2) < ncc_w);
