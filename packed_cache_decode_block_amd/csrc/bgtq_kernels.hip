@@ -832,11 +832,11 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
 //    the fp16 low part of q' = q * sigma * log2(e)/sqrt(d) (hi + lo carries ~22 bits).  Centroids
 //    are fp16 values exactly, so the products lose nothing and the MFMA sums in fp32.
 //  * B = K^ (32 K x 16 tokens): lane (token j, row u) builds its own operand: K index 8u + e is
-//    coordinate e % 2 of stream slot 16 ks + 4 (e / 2) + u, so the four slots of a column (one
-//    per lane row) are consecutive in the record.  Per column and token group the lane reads a
-//    64-bit window of the staged record at its own slot's row, shifts it and ANDs/ORs it into a
-//    table address (pair tables for widths <= 5, fp16 coordinate tables for wider columns).  The
-//    one-dword column descriptors are built once per workgroup; no transposes.
+//    coordinate e % 2 of stream slot 16 ks + 8 (e / 4) + 2u + (e / 2) % 2, so a lane row reads two
+//    adjacent slots of the record from one 64-bit window of the staged record (per token group),
+//    shifts it and ANDs/ORs the field into a table address (pair tables for widths <= 5, fp16
+//    coordinate tables for wider columns).  The one-dword slot descriptors are built once per
+//    workgroup; no transposes.
 //  * C (16 x 16 tokens): lane (token 16g + r, row group u) holds heads 2u, 2u + 1 as (hi, lo).
 //  * P·V: A = V^T (16 dims x 32 tokens) straight from the lane-stream value fields, B = W (32 tokens
 //    x 16 heads) through LDS in pair order (t, t + 32); O^T accumulates per 16-dim block.
@@ -851,20 +851,27 @@ __device__ __forceinline__ half8_t as_h8(uint32_t a, uint32_t b, uint32_t c, uin
 __device__ __forceinline__ f32x4_t mfma16(half8_t a, half8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-// Column descriptor of one stream slot (one dword, built in the prologue, held in VGPRs):
-//   bits 0..4   alignbit shift that moves the field (pair) or the first code (coordinates) to bit
-//               2 (pair) or bit 1 (coordinates) of the 64-bit window
-//   bits 5..9   field width: 2w for a pair column, w for a coordinate column (0: empty slot)
-//   bits 10..15 64-bit shift that moves the second code to bit 1 (coordinate columns)
-//   bits 16..31 byte offset of the window's first stage row
-__device__ __forceinline__ uint32_t mx_desc(int pos, int w, bool coord) {
-    const int k = coord ? 1 : 2;
-    const int u = pos - k;                       // >= -2
-    const int rr = u >= 0 ? u >> 5 : -1;         // window row (-1: the spare row)
-    const uint32_t sh = (uint32_t)(u - 32 * rr);
+// Column descriptor of one stream slot (one dword, built in the prologue; a lane reads the four of a
+// k-step with one 16-byte LDS read).  A lane
+// row reads the two adjacent slots A = 2i, B = 2i + 1 of a column pair from one 64-bit window
+// that starts at a stage row boundary below A's field:
+//   bits 0..5   64-bit shift that moves the slot's field (pair) or first code (coordinates) to bit
+//               2 (pair) or bit 1 (coordinates)
+//   bits 6..11  64-bit shift that moves the second code to bit 1 (coordinate columns)
+//   bits 12..16 field width: 2w for a pair column, w for a coordinate column (0: empty slot)
+//   bits 17..31 byte offset of the window's first stage row (slot A's descriptor)
+// posA/coordA: slot A's record position and column mode; pos/w/coord: this slot's.  Every shift
+// stays below 64 and every field inside the window: A's offset is below 32 and A and B together
+// span at most 32 bits.
+__device__ __forceinline__ uint32_t mx_desc(int posA, bool coordA, int pos, int w, bool coord) {
+    const int uA = posA - (coordA ? 1 : 2);       // >= -2
+    const int rr = uA >= 0 ? uA >> 5 : -1;        // window row (-1: the spare row)
+    const int base = 32 * rr;
+    const int s0 = pos - (coord ? 1 : 2) - base;
+    const uint32_t sh0 = (uint32_t)(s0 < 0 ? 0 : s0);  // < 0 only for empty slots
+    const uint32_t sh1 = coord ? sh0 + (uint32_t)w : 0u;
     const uint32_t fw = (uint32_t)(w == 0 ? 0 : (coord ? w : 2 * w));
-    const uint32_t sh1 = coord ? sh + (uint32_t)w : 0u;
-    return sh | (fw << 5) | (sh1 << 10) | ((uint32_t)(rr + 1) * BGTQ_KST_ROW_BYTES << 16);
+    return sh0 | (sh1 << 6) | (fw << 12) | ((uint32_t)(rr + 1) * BGTQ_KST_ROW_BYTES << 17);
 }
 
 // ((1 << (width & 31)) - 1) << OFF in one v_bfm_b32.
@@ -875,53 +882,52 @@ __device__ __forceinline__ uint32_t bfm(uint32_t width) {
     return r;
 }
 
-// One column of a k-step read as coordinate pairs: per token group g a 64-bit window of two stage
-// rows, alignbit, and_or into the pair table of the slot's width, one 4-byte read.  lb: this lane's
-// token column in the wave's K stage.
-template <int M>
-__device__ __forceinline__ void col_pair(uint32_t (&P)[16], const uint8_t* lds, uint32_t dsc, uint32_t lb) {
-    const uint32_t ad = (dsc >> 16) + lb;
-    const uint32_t mask = bfm<2>(dsc >> 5);
-    const uint32_t base = mask + BGTQ_CB_MX_PAIR_BIAS;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const uint32_t lo = *(const uint32_t*)(lds + ad + 64 * g);
-        const uint32_t hi = *(const uint32_t*)(lds + ad + 64 * g + BGTQ_KST_ROW_BYTES);
-        const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, dsc);
-        P[4 * g + M] = *(const uint32_t*)(lds + ((x & mask) | base));
-    }
+// Slot of a column read as a coordinate pair: 64-bit shift, and_or into the pair table of the
+// slot's width, one 4-byte read.
+__device__ __forceinline__ uint32_t slot_pair(const uint8_t* lds, uint64_t win, uint32_t dsc, uint32_t mask,
+                                              uint32_t base) {
+    const uint32_t x = (uint32_t)(win >> (dsc & 63u));
+    return *(const uint32_t*)(lds + ((x & mask) | base));
+}
+// Slot of a column read per coordinate (the column's first slot is wider than 5 bits): two
+// shifts, two 2-byte reads from the fp16 centroid table of the slot's width.
+__device__ __forceinline__ uint32_t slot_coord(const uint8_t* lds, uint64_t win, uint32_t dsc, uint32_t mask,
+                                               uint32_t base) {
+    const uint32_t x0 = (uint32_t)(win >> (dsc & 63u));
+    const uint32_t x1 = (uint32_t)(win >> ((dsc >> 6) & 63u));
+    const uint32_t c0 = *(const uint16_t*)(lds + ((x0 & mask) | base));
+    const uint32_t c1 = *(const uint16_t*)(lds + ((x1 & mask) | base));
+    return c0 | (c1 << 16);
 }
 
-// One column read per coordinate (its first slot is wider than 5 bits): one window, the first code
-// by alignbit and the second by a 64-bit shift, two 2-byte reads from the fp16 centroid table.
-template <int M>
-__device__ __forceinline__ void col_coord(uint32_t (&P)[16], const uint8_t* lds, uint32_t dsc, uint32_t lb) {
-    const uint32_t ad = (dsc >> 16) + lb;
-    const uint32_t mask = bfm<1>(dsc >> 5);
-    const uint32_t base = mask + BGTQ_CB_MX_COORD_BIAS;
-    const uint32_t sh1 = (dsc >> 10) & 63u;
+// Column pair M (element pairs 2M, 2M + 1) of a k-step: per token group g one window of two stage
+// rows shared by the lane row's two slots.  CA / CB: whether columns 2M / 2M + 1 are read per
+// coordinate.  lb: this lane's token column in the wave's K stage.
+template <int M, bool CA, bool CB>
+__device__ __forceinline__ void col_pair2(uint32_t (&P)[16], const uint8_t* lds, uint32_t dA, uint32_t dB, uint32_t lb) {
+    const uint32_t ad = (dA >> 17) + lb;
+    const uint32_t mA = CA ? bfm<1>(dA >> 12) : bfm<2>(dA >> 12);
+    const uint32_t mB = CB ? bfm<1>(dB >> 12) : bfm<2>(dB >> 12);
+    const uint32_t bA = mA + (CA ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
+    const uint32_t bB = mB + (CB ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const uint32_t lo = *(const uint32_t*)(lds + ad + 64 * g);
         const uint32_t hi = *(const uint32_t*)(lds + ad + 64 * g + BGTQ_KST_ROW_BYTES);
-        const uint32_t x0 = __builtin_amdgcn_alignbit(hi, lo, dsc);
-        const uint32_t x1 = (uint32_t)((((uint64_t)hi << 32) | lo) >> sh1);
-        const uint32_t c0 = *(const uint16_t*)(lds + ((x0 & mask) | base));
-        const uint32_t c1 = *(const uint16_t*)(lds + ((x1 & mask) | base));
-        P[4 * g + M] = c0 | (c1 << 16);
+        const uint64_t win = ((uint64_t)hi << 32) | lo;
+        P[4 * g + 2 * M] = CA ? slot_coord(lds, win, dA, mA, bA) : slot_pair(lds, win, dA, mA, bA);
+        P[4 * g + 2 * M + 1] = CB ? slot_coord(lds, win, dB, mB, bB) : slot_pair(lds, win, dB, mB, bB);
     }
 }
 
 // k-step KS with its first A columns read per coordinate and the rest as pairs.
 template <int KS, int A>
 __device__ __forceinline__ void mx_kstep(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
-                                         const u32x4_t (&sd)[4], uint32_t lb) {
+                                         const u32x4_t* sd, uint32_t lb) {
     uint32_t P[16];
     const u32x4_t dk = sd[KS];
-    if constexpr (A > 0) col_coord<0>(P, lds, dk[0], lb); else col_pair<0>(P, lds, dk[0], lb);
-    if constexpr (A > 1) col_coord<1>(P, lds, dk[1], lb); else col_pair<1>(P, lds, dk[1], lb);
-    if constexpr (A > 2) col_coord<2>(P, lds, dk[2], lb); else col_pair<2>(P, lds, dk[2], lb);
-    if constexpr (A > 3) col_coord<3>(P, lds, dk[3], lb); else col_pair<3>(P, lds, dk[3], lb);
+    col_pair2<0, (A > 0), (A > 1)>(P, lds, dk[0], dk[1], lb);
+    col_pair2<1, (A > 2), (A > 3)>(P, lds, dk[2], dk[3], lb);
     const half8_t q = __builtin_bit_cast(half8_t, qa[KS * 64 + lane]);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -933,7 +939,7 @@ __device__ __forceinline__ void mx_kstep(f32x4_t (&c)[4], const uint8_t* lds, co
 // k-step KS of a tile; ncc (wave-uniform) = number of coordinate columns of the whole record.
 template <int KS>
 __device__ __forceinline__ void mx_kstep_any(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
-                                             const u32x4_t (&sd)[4], uint32_t lb, int ncc) {
+                                             const u32x4_t* sd, uint32_t lb, int ncc) {
     const int a = ncc - 4 * KS;
     if (a <= 0) mx_kstep<KS, 0>(c, lds, qa, lane, sd, lb);
     else if (a == 1) mx_kstep<KS, 1>(c, lds, qa, lane, sd, lb);
@@ -996,9 +1002,9 @@ template <int G, int R, int VB> struct MxLds {
     static constexpr int KST_W = (R + 2) * BGTQ_KST_ROW_BYTES;
     static constexpr int SST = KST + 4 * KST_W;                       // per wave: K scales, V scales, V zeros
     static constexpr int SST_W = 3 * 64 * 2;
-    static constexpr int QP = KST;                                    // prologue: f32 [128 G]
+    static constexpr int QP = KST;                                    // prologue: f32 [128 G], then i32 [2][64]
     static constexpr int RED = KST;                                   // epilogue: f32 [4 G PART + 4 G]
-    static constexpr int SIZE = cmax(cmax(SST + 4 * SST_W, QP + 512 * G), RED + 4 * (4 * G * PART + 4 * G));
+    static constexpr int SIZE = cmax(cmax(SST + 4 * SST_W, QP + 512 * G + 512), RED + 4 * (4 * G * PART + 4 * G));
 };
 
 template <int G, int R, int VB>
@@ -1086,30 +1092,45 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         const int bw = (int)((pin.w4 >> (8 * (lane & 3))) & 0xFFu);
         const int w = bw < 8 ? bw : 8;
         const int rank = ord.x, pos = ord.y, nnz = ord.z;
-        const int ncc_w = (__popcll(__ballot(w > 5)) + 3) >> 2;
+        const int n_wide = __popcll(__ballot(w > 5));
+        // stream-ordered widths and positions, then lane = stream slot
+        int* s_sw = (int*)(lds + LD::QP + 512 * G);
+        int* s_sp = s_sw + 64;
+        if (w > 0) { s_sw[rank] = w; s_sp[rank] = pos; }
+        if (lane >= nnz) { s_sw[lane] = 0; s_sp[lane] = 0; }
+        wave_lds_fence();
+        // slot r: k-step r / 16, column pair (r % 16) / 8, lane row (r % 8) / 2, second of the pair if odd;
+        // a column is read per coordinate when its first slot is wider than 5 bits
+        const int r = lane, ks = r >> 4, mp = (r >> 3) & 1, kq = (r >> 1) & 3, odd = r & 1;
+        auto coord_of = [&](int first) { return first < n_wide; };
+        const int ra = r & ~1;
+        const bool ca = coord_of(16 * ks + 8 * mp), cs = coord_of(16 * ks + 8 * mp + odd);
         uint32_t* s_desc = (uint32_t*)(lds + LD::DESC);
-        if (w > 0) s_desc[(rank & 3) * 16 + (rank >> 2)] = mx_desc(pos, w, (rank >> 2) < ncc_w);
-        if (lane >= nnz) s_desc[(lane & 3) * 16 + (lane >> 2)] = mx_desc(0, 0, (lane >> 2) < ncc_w);
-        if (lane == 0) s_nnz[1] = (uint32_t)ncc_w;
+        s_desc[kq * 16 + 4 * ks + 2 * mp + odd] = mx_desc(s_sp[ra], ca, s_sp[r], s_sw[r], cs);
+        // coordinate columns, counted in k-step order (columns 2M, 2M + 1 of a k-step start at
+        // slots 16 ks + 8 M and 16 ks + 8 M + 1)
+        if (lane == 0) {
+            int a = 0;
+            for (int c = 0; c < 16; ++c) a += coord_of(16 * (c >> 2) + 8 * ((c >> 1) & 1) + (c & 1)) ? 1 : 0;
+            s_nnz[1] = (uint32_t)a;
+        }
     }
     __syncthreads();
 
     const int nnz_pad = (int)__builtin_amdgcn_readfirstlane(s_nnz[0]);  // nonzero slots rounded up to 4
     const int nks = (nnz_pad + 15) >> 4;
     const int ncc = (int)__builtin_amdgcn_readfirstlane(s_nnz[1]);      // coordinate columns
-    u32x4_t sd[4];  // this lane row's column descriptors, k-step by k-step
-#pragma unroll
-    for (int k = 0; k < 4; ++k) sd[k] = ((const u32x4_t*)(lds + LD::DESC))[4 * row + k];
+    const u32x4_t* sd = (const u32x4_t*)(lds + LD::DESC) + 4 * row;  // this lane row's descriptors
 
     // Query operands: lane (col = head part, row u), element e: coordinate e % 2 of stream slot
-    // 16 ks + 4 (e / 2) + u, head col / 2, fp16 high part (col even) or low part (col odd).  Wave w
-    // builds k-step w.
+    // 16 ks + 8 (e / 4) + 2 u + (e / 2) % 2, head col / 2, fp16 high part (col even) or low part
+    // (col odd).  Wave w builds k-step w.
     {
         const int ks = wave;
         half8_t qa;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int sl = 16 * ks + 4 * (e >> 1) + row, hd = col >> 1;
+            const int sl = 16 * ks + 8 * (e >> 2) + 2 * row + ((e >> 1) & 1), hd = col >> 1;
             const float qv = hd < G ? s_qp[sl * 2 * G + (e & 1) * G + hd] : 0.f;
             const _Float16 hi = (_Float16)qv;
             const _Float16 lo = (_Float16)(qv - (float)hi);
