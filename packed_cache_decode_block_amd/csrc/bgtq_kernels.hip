@@ -1318,68 +1318,69 @@ __global__ __launch_bounds__(256, 2) void k_decode_fp16(const Fp16Args a) {
 // Merge split partials (o, m, l) of one (batch, query head) by log-sum-exp.  Grid: (row, slice of
 // 16 dims); thread s takes splits s, s + 256, ...  The first split's record is loaded together with
 // the maxima so one memory round trip covers the common case (at most 256 splits).
-constexpr int CMB_DIMS = 16;
-__global__ __launch_bounds__(256) void k_combine(const CombineArgs a) {
-    __shared__ float s_r[4];
-    __shared__ float s_acc[4][CMB_DIMS + 1];
-    const int row = blockIdx.x, d0 = blockIdx.y * CMB_DIMS, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+constexpr int CMB_DIMS = 8;
+// Sum / max over all 64 lanes, returned wave-uniform: DPP rotations within each row of 16, then
+// row_bcast:15 and row_bcast:31 fold the rows into the last row, and lane 63 is read out.
+__device__ __forceinline__ float wave_total_sum(float v) {
+    v = row_sum16(v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_total_max(float v) {
+    constexpr int NEG_INF = (int)0xFF800000u;
+    v = row_max16(v);
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(NEG_INF, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(NEG_INF, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false)));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Split merge: one wave per (query head row, 8 dims).  Lane l folds partials l, l + 64, ... with
+// an online log-sum-exp, four partials per round with their loads issued together, then the 64
+// lane states merge across the wave.
+__global__ __launch_bounds__(64) void k_combine(const CombineArgs a) {
+    constexpr int U = 4;
+    const int row = blockIdx.x, d0 = blockIdx.y * CMB_DIMS, lane = threadIdx.x;
     const float* pr = a.part + (size_t)row * a.n_parts * PART;
-    const bool has0 = tid < a.n_parts;
-    float4 o0[CMB_DIMS / 4];
-    float m0 = -INFINITY, l0 = 0.f;
-    if (has0) {
-        const float* r = pr + (size_t)tid * PART;
-        m0 = r[128];
-        l0 = r[129];
-#pragma unroll
-        for (int u = 0; u < CMB_DIMS / 4; ++u) o0[u] = *(const float4*)(r + d0 + 4 * u);
-    }
-    float mloc = m0;
-    for (int s = tid + 256; s < a.n_parts; s += 256) mloc = fmaxf(mloc, pr[(size_t)s * PART + 128]);
-    mloc = wave_max(mloc);
-    if (lane == 0) s_r[wave] = mloc;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(s_r[0], s_r[1]), fmaxf(s_r[2], s_r[3]));
-    float acc[CMB_DIMS + 1];
+    float m = -INFINITY, acc[CMB_DIMS + 1];
 #pragma unroll
     for (int j = 0; j <= CMB_DIMS; ++j) acc[j] = 0.f;
-    if (has0 && m0 != -INFINITY) {
-        const float sc = __builtin_amdgcn_exp2f(m0 - M);
+    for (int s0 = 0; s0 < a.n_parts; s0 += 64 * U) {
+        float2 ml[U];
+        f32x4_t o4[U][CMB_DIMS / 4];
 #pragma unroll
-        for (int u = 0; u < CMB_DIMS / 4; ++u) {
-            acc[4 * u] = sc * o0[u].x;
-            acc[4 * u + 1] = sc * o0[u].y;
-            acc[4 * u + 2] = sc * o0[u].z;
-            acc[4 * u + 3] = sc * o0[u].w;
+        for (int u = 0; u < U; ++u) {
+            const int sp = s0 + 64 * u + lane;
+            const float* r = pr + (size_t)(sp < a.n_parts ? sp : 0) * PART;
+            ml[u] = *(const float2*)(r + 128);
+#pragma unroll
+            for (int k = 0; k < CMB_DIMS / 4; ++k) o4[u][k] = *(const f32x4_t*)(r + d0 + 4 * k);
+            if (sp >= a.n_parts) ml[u].x = -INFINITY;
         }
-        acc[CMB_DIMS] = sc * l0;
-    }
-    for (int s = tid + 256; s < a.n_parts; s += 256) {
-        const float* r = pr + (size_t)s * PART;
-        const float m = r[128];
-        if (m == -INFINITY) continue;
-        const float sc = __builtin_amdgcn_exp2f(m - M);
 #pragma unroll
-        for (int u = 0; u < CMB_DIMS / 4; ++u) {
-            const float4 o = *(const float4*)(r + d0 + 4 * u);
-            acc[4 * u] += sc * o.x;
-            acc[4 * u + 1] += sc * o.y;
-            acc[4 * u + 2] += sc * o.z;
-            acc[4 * u + 3] += sc * o.w;
+        for (int u = 0; u < U; ++u) {
+            if (ml[u].x == -INFINITY) continue;  // past the end, or a split without tokens
+            const float mn = fmaxf(m, ml[u].x);
+            const float fo = __builtin_amdgcn_exp2f(m - mn), fn = __builtin_amdgcn_exp2f(ml[u].x - mn);
+            m = mn;
+#pragma unroll
+            for (int k = 0; k < CMB_DIMS / 4; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[4 * k + e] = acc[4 * k + e] * fo + fn * o4[u][k][e];
+            acc[CMB_DIMS] = acc[CMB_DIMS] * fo + fn * ml[u].y;
         }
-        acc[CMB_DIMS] += sc * r[129];
     }
+    const float M = wave_total_max(m);
+    const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
 #pragma unroll
-    for (int j = 0; j <= CMB_DIMS; ++j) acc[j] = wave_sum(acc[j]);
+    for (int j = 0; j <= CMB_DIMS; ++j) acc[j] = wave_total_sum(acc[j] * f);
     if (lane == 0) {
+        const float inv = 1.f / acc[CMB_DIMS];
+        float* dst = a.out + (size_t)row * D + d0;
 #pragma unroll
-        for (int j = 0; j <= CMB_DIMS; ++j) s_acc[wave][j] = acc[j];
-    }
-    __syncthreads();
-    if (tid < CMB_DIMS) {
-        const float L = (s_acc[0][CMB_DIMS] + s_acc[1][CMB_DIMS]) + (s_acc[2][CMB_DIMS] + s_acc[3][CMB_DIMS]);
-        const float o = (s_acc[0][tid] + s_acc[1][tid]) + (s_acc[2][tid] + s_acc[3][tid]);
-        a.out[(size_t)row * D + d0 + tid] = o / L;
+        for (int k = 0; k < CMB_DIMS / 4; ++k)
+            *(f32x4_t*)(dst + 4 * k) = f32x4_t{acc[4 * k] * inv, acc[4 * k + 1] * inv, acc[4 * k + 2] * inv,
+                                               acc[4 * k + 3] * inv};
     }
 }
 
@@ -1641,7 +1642,7 @@ static hipError_t launch_main(K kernel, dim3 grid, dim3 block, hipStream_t s, co
 
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s) {
     if (!a.part || !a.out || a.n_parts < 1 || a.n_parts > BGTQ_MAX_PARTS) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_combine, dim3(rows, D / CMB_DIMS), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_combine, dim3(rows, D / CMB_DIMS), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
