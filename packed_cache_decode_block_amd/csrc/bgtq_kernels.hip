@@ -982,11 +982,58 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
+// Query operands of the matrix-core decode, written by one wave (lane = RoPE block): q' = q *
+// sigma * log2(e)/sqrt(d) of block i (stream slot r = its rank) goes, split into an fp16 high part
+// and an fp16 low part, to k-step r / 16, lane row (r % 8) / 2, element pair 2 ((r % 16) / 8) +
+// r % 2 of the operand lanes of its heads (column 2h: high part, 2h + 1: low part).  Slots past
+// the nonzero blocks, and the columns of absent heads, get zeros.  s_nnz[0] = nonzero blocks
+// rounded up to 4.
+template <int G>
+__device__ void mx_prep_q(const PrepIn<G>& in, int w, int lane, uint8_t* qa, uint32_t* s_nnz) {
+    float q0[G], q1[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        if (in.dtype == BGTQ_F32) {
+            q0[hh] = __builtin_bit_cast(float, in.r0[hh]);
+            q1[hh] = __builtin_bit_cast(float, in.r1[hh]);
+        } else if (in.dtype == BGTQ_F16) {
+            q0[hh] = h2f(in.r0[hh] & 0xFFFFu);
+            q1[hh] = h2f(in.r0[hh] >> 16);
+        } else {
+            q0[hh] = bf2f(in.r0[hh] & 0xFFFFu);
+            q1[hh] = bf2f(in.r0[hh] >> 16);
+        }
+        q0[hh] = q0[hh] * kLog2eOverSqrtD * in.sg;
+        q1[hh] = q1[hh] * kLog2eOverSqrtD * in.sg;
+    }
+    int rank, pos, nnz;
+    block_order(w, lane, rank, pos, nnz);
+    auto put = [&](int r, bool zero) {
+        const int ks = r >> 4, rr = r & 15, urow = (rr >> 1) & 3, mpair = 2 * (rr >> 3) + (rr & 1);
+        uint8_t* base = qa + (size_t)(ks * 64 + 16 * urow) * 16 + 4 * mpair;
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+            uint32_t hi2 = 0u, lo2 = 0u;
+            if (hh < G && !zero) {
+                const _Float16 h0 = (_Float16)q0[hh], h1 = (_Float16)q1[hh];
+                const _Float16 l0 = (_Float16)(q0[hh] - (float)h0), l1 = (_Float16)(q1[hh] - (float)h1);
+                hi2 = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                lo2 = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+            }
+            *(uint32_t*)(base + (2 * hh) * 16) = hi2;
+            *(uint32_t*)(base + (2 * hh + 1) * 16) = lo2;
+        }
+    };
+    if (w > 0) put(rank, false);
+    if (lane >= nnz) put(lane, true);
+    if (lane == 0) s_nnz[0] = (uint32_t)((nnz + 3) & ~3);
+}
+
 // LDS arena of the matrix-core decode (byte offsets).  Loop-time regions: tables (at offset 0,
 // the arena being 8192-aligned, so table offsets are LDS addresses), column descriptors, value
 // centroid pairs, query operands, weight exchange, softmax rescale factors, and per wave the stage
-// of the tile in flight (K record rows -1 .. R at BGTQ_KST_ROW_BYTES stride, scales).  The query
-// prep output and the epilogue records alias the stages.
+// of the tile in flight (K record rows -1 .. R at BGTQ_KST_ROW_BYTES stride, scales).  The
+// prologue's block order and the epilogue records alias the stages.
 constexpr int a16(int x) { return (x + 15) & ~15; }
 constexpr int cmax(int x, int y) { return x > y ? x : y; }
 template <int G, int R, int VB> struct MxLds {
@@ -996,15 +1043,14 @@ template <int G, int R, int VB> struct MxLds {
     static constexpr int QA = a16(VLUT + 4 * (1 << (2 * VB)));        // u32x4 [4 k-steps][64 lanes]
     static constexpr int WX = QA + 4 * 64 * 16;                       // u32 [4 waves][16 heads][32 pairs]
     static constexpr int ALPHA = WX + 4 * 16 * 32 * 4;                // f32 [4 waves][16]
-    static constexpr int NNZ = ALPHA + 4 * 16 * 4;                    // u32 [4]: padded nonzero slots, wide slots
-    static constexpr int DSC = NNZ + 16;                              // u16 [64] (prep output, unused)
-    static constexpr int KST = a16(DSC + 128);                        // per wave: R + 2 rows
+    static constexpr int NNZ = ALPHA + 4 * 16 * 4;                    // u32 [4]: padded nonzero slots, coordinate columns
+    static constexpr int KST = a16(NNZ + 16);                         // per wave: R + 2 rows
     static constexpr int KST_W = (R + 2) * BGTQ_KST_ROW_BYTES;
     static constexpr int SST = KST + 4 * KST_W;                       // per wave: K scales, V scales, V zeros
     static constexpr int SST_W = 3 * 64 * 2;
-    static constexpr int QP = KST;                                    // prologue: f32 [128 G], then i32 [2][64]
+    static constexpr int QP = KST;                                    // prologue: i32 [2][64] block order
     static constexpr int RED = KST;                                   // epilogue: f32 [4 G PART + 4 G]
-    static constexpr int SIZE = cmax(cmax(SST + 4 * SST_W, QP + 512 * G + 512), RED + 4 * (4 * G * PART + 4 * G));
+    static constexpr int SIZE = cmax(cmax(SST + 4 * SST_W, QP + 512), RED + 4 * (4 * G * PART + 4 * G));
 };
 
 template <int G, int R, int VB>
@@ -1083,62 +1129,41 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         s_vlut[threadIdx.x] = a.v_affine ? (uint32_t)f2h((float)vca) | ((uint32_t)f2h((float)vcb) << 16) : vla | (vlb << 16);
 #pragma unroll
     for (int i = threadIdx.x; i < 4 * 16 * 32 / 4; i += 256) ((u32x4_t*)(lds + LD::WX))[i] = u32x4_t{0u, 0u, 0u, 0u};
-    float* s_qp = (float*)(lds + LD::QP);
-    if (wave == 0) {
-        int3 ord;
-        prep_store<G, true, 0>(pin, lane, s_qp, (uint16_t*)(lds + LD::DSC), s_nnz, nullptr, &ord);
-        // Column descriptors: stream slot r sits in column r / 4, lane row r % 4; a column is read
-        // per coordinate when its first slot is wider than 5 bits (slots are in width order).
-        const int bw = (int)((pin.w4 >> (8 * (lane & 3))) & 0xFFu);
-        const int w = bw < 8 ? bw : 8;
-        const int rank = ord.x, pos = ord.y, nnz = ord.z;
+    const int bw = (int)((pin.w4 >> (8 * (lane & 3))) & 0xFFu);
+    const int w = bw < 8 ? bw : 8;  // widths above 8 are invalid; clamp
+    if (wave == 0) mx_prep_q<G>(pin, w, lane, lds + LD::QA, s_nnz);
+    if (wave == 1) {
+        // Slot descriptors: stream slot r is k-step r / 16, column pair (r % 16) / 8, lane row
+        // (r % 8) / 2, second of its pair if odd; a column is read per coordinate when its first
+        // slot is wider than 5 bits (slots are in width order).
+        int rank, pos, nnz;
+        block_order(w, lane, rank, pos, nnz);
         const int n_wide = __popcll(__ballot(w > 5));
-        // stream-ordered widths and positions, then lane = stream slot
-        int* s_sw = (int*)(lds + LD::QP + 512 * G);
+        int* s_sw = (int*)(lds + LD::QP);  // stream-ordered widths and positions
         int* s_sp = s_sw + 64;
         if (w > 0) { s_sw[rank] = w; s_sp[rank] = pos; }
         if (lane >= nnz) { s_sw[lane] = 0; s_sp[lane] = 0; }
         wave_lds_fence();
-        // slot r: k-step r / 16, column pair (r % 16) / 8, lane row (r % 8) / 2, second of the pair if odd;
-        // a column is read per coordinate when its first slot is wider than 5 bits
         const int r = lane, ks = r >> 4, mp = (r >> 3) & 1, kq = (r >> 1) & 3, odd = r & 1;
         auto coord_of = [&](int first) { return first < n_wide; };
-        const int ra = r & ~1;
         const bool ca = coord_of(16 * ks + 8 * mp), cs = coord_of(16 * ks + 8 * mp + odd);
         uint32_t* s_desc = (uint32_t*)(lds + LD::DESC);
-        s_desc[kq * 16 + 4 * ks + 2 * mp + odd] = mx_desc(s_sp[ra], ca, s_sp[r], s_sw[r], cs);
+        s_desc[kq * 16 + 4 * ks + 2 * mp + odd] = mx_desc(s_sp[r & ~1], ca, s_sp[r], s_sw[r], cs);
         // coordinate columns, counted in k-step order (columns 2M, 2M + 1 of a k-step start at
         // slots 16 ks + 8 M and 16 ks + 8 M + 1)
         if (lane == 0) {
-            int a = 0;
-            for (int c = 0; c < 16; ++c) a += coord_of(16 * (c >> 2) + 8 * ((c >> 1) & 1) + (c & 1)) ? 1 : 0;
-            s_nnz[1] = (uint32_t)a;
+            int nc = 0;
+            for (int c = 0; c < 16; ++c) nc += coord_of(16 * (c >> 2) + 8 * ((c >> 1) & 1) + (c & 1)) ? 1 : 0;
+            s_nnz[1] = (uint32_t)nc;
         }
     }
-    __syncthreads();
+    __syncthreads();  // tables, descriptors and query operands are in place; the scratch above is
+                      // reused as the tile stages below
 
     const int nnz_pad = (int)__builtin_amdgcn_readfirstlane(s_nnz[0]);  // nonzero slots rounded up to 4
     const int nks = (nnz_pad + 15) >> 4;
     const int ncc = (int)__builtin_amdgcn_readfirstlane(s_nnz[1]);      // coordinate columns
     const u32x4_t* sd = (const u32x4_t*)(lds + LD::DESC) + 4 * row;  // this lane row's descriptors
-
-    // Query operands: lane (col = head part, row u), element e: coordinate e % 2 of stream slot
-    // 16 ks + 8 (e / 4) + 2 u + (e / 2) % 2, head col / 2, fp16 high part (col even) or low part
-    // (col odd).  Wave w builds k-step w.
-    {
-        const int ks = wave;
-        half8_t qa;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int sl = 16 * ks + 8 * (e >> 2) + 2 * row + ((e >> 1) & 1), hd = col >> 1;
-            const float qv = hd < G ? s_qp[sl * 2 * G + (e & 1) * G + hd] : 0.f;
-            const _Float16 hi = (_Float16)qv;
-            const _Float16 lo = (_Float16)(qv - (float)hi);
-            qa[e] = (col & 1) ? lo : hi;
-        }
-        s_qa[ks * 64 + lane] = __builtin_bit_cast(u32x4_t, qa);
-    }
-    __syncthreads();  // the query prep area is reused as the tile stages below
 
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, zs[2] = {0.f, 0.f};
     f32x4_t o[8];
@@ -1318,7 +1343,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_fp16(const Fp16Args a) {
 // Merge split partials (o, m, l) of one (batch, query head) by log-sum-exp.  Grid: (row, slice of
 // 16 dims); thread s takes splits s, s + 256, ...  The first split's record is loaded together with
 // the maxima so one memory round trip covers the common case (at most 256 splits).
-constexpr int CMB_DIMS = 8;
+constexpr int CMB_DIMS = 4;
 // Sum / max over all 64 lanes, returned wave-uniform: DPP rotations within each row of 16, then
 // row_bcast:15 and row_bcast:31 fold the rows into the last row, and lane 63 is read out.
 __device__ __forceinline__ float wave_total_sum(float v) {
@@ -1335,7 +1360,7 @@ __device__ __forceinline__ float wave_total_max(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-// Split merge: one wave per (query head row, 8 dims).  Lane l folds partials l, l + 64, ... with
+// Split merge: one wave per (query head row, 4 dims).  Lane l folds partials l, l + 64, ... with
 // an online log-sum-exp, four partials per round with their loads issued together, then the 64
 // lane states merge across the wave.
 __global__ __launch_bounds__(64) void k_combine(const CombineArgs a) {
