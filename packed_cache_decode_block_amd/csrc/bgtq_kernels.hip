@@ -6,18 +6,18 @@
 // "Quantize What Counts" summary (Results: group-size sensitivity); the fp16 recent ring and the
 // order-free concatenation follow the "LogQuant" summary (Method 2 and Method 4).
 //
-// Decode mapping (one workgroup = 4 waves = one split of one (batch, kv head)):
-//  * q·k: lane = token.  The tile's K records are staged dword-major in LDS; each nonzero RoPE
-//    block (sorted by width) is one static "slot": a 64-bit LDS window, alignbit, two bit-field
-//    extracts, two centroid reads from an LDS table, then 2g FMAs whose query operand is
-//    broadcast from VGPRs with DPP row_newbcast (q' = q * sigma * log2(e)/sqrt(d), 16 values per
-//    VGPR, replicated in the 4 rows).  No MFMA: per (token, kv head) the work is a g-row GEMV.
-//  * online softmax in base 2, wave-uniform running max per head.
-//  * p·v: lane = (token quad slot, 8-dim group); the 2*v_bits-bit pair field indexes an LDS table
-//    of fp16 centroid pairs and v_dot2_f32_f16 accumulates w(t, t+1)·c(t, t+1) in fp32, with
-//    w = p * scale rounded to fp16 (as flash attention rounds P before P·V).
-//  * epilogue: cross-lane + cross-wave log-sum-exp merge, one (m, l, o) partial per split;
-//    a second kernel merges the splits.
+// Two decode kernels, both one workgroup = 4 waves = one split of one (batch, kv head), each
+// emitting one (o, m, l) partial per query head that k_combine merges across splits:
+//  * k_decode_mx (Block-GTQ keys, g >= 4 query heads per kv head): q·K^T and P·V of each 64-token
+//    tile run on the matrix cores (v_mfma_f32_16x16x32_f16); the vector ALUs only unpack codes and
+//    run the online softmax.  Its design notes sit next to it below.
+//  * k_decode (g <= 2, or affine keys): lane = token.  The tile's K records are staged dword-major
+//    in LDS; each nonzero RoPE block (sorted by width) is one slot: a 64-bit LDS window, alignbit,
+//    two bit-field extracts, two centroid reads from an LDS table, then 2g FMAs whose query
+//    operand is broadcast from VGPRs with DPP.  P·V: the 2*v_bits-bit pair field indexes an LDS
+//    table of fp16 centroid pairs and v_dot2_f32_f16 accumulates w(t, t+1)·c(t, t+1) in fp32,
+//    with w = p * scale rounded to fp16 (as flash attention rounds P before P·V).
+// Both use an online softmax in base 2 with the exact running maximum per head.
 #include "bgtq_internal.h"
 
 #include <hip/hip_ext.h>
