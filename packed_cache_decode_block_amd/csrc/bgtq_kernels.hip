@@ -948,19 +948,41 @@ __device__ __forceinline__ void mx_kstep_any(f32x4_t (&c)[4], const uint8_t* lds
     else mx_kstep<KS, 4>(c, lds, qa, lane, sd, lb);
 }
 
+// The matrix-core decode's value table holds VLUT_COPIES interleaved copies (entry e of copy c at
+// dword e * copies + c) and lane l reads copy l % copies, so lanes looking up different entries
+// rarely meet in one LDS bank.
+template <int VB> struct VLutGeom {
+    static constexpr int LOG2_COPIES = VB <= 3 ? 4 : 2;
+    static constexpr int COPIES = 1 << LOG2_COPIES;
+    static constexpr int BYTES = 4 * COPIES * (1 << (2 * VB));
+};
+// Field F of this lane's value stream scaled to a byte offset in the replicated table, OR-ed with
+// the lane's copy offset (one shift, one and_or).
+template <int VB, int F>
+__device__ __forceinline__ uint32_t vfield_rep(const uint32_t* r, uint32_t lane_copy) {
+    constexpr int bit = 2 * VB * F, w = bit / 32, sh = bit % 32, nb = 2 * VB;
+    constexpr int S = 2 + VLutGeom<VB>::LOG2_COPIES;
+    constexpr uint32_t m = ((1u << nb) - 1u) << S;
+    uint32_t x;
+    if constexpr (sh + nb > 32) x = __builtin_amdgcn_alignbit(r[w + 1], r[w], sh - S);
+    else if constexpr (sh >= S) x = r[w] >> (sh - S);
+    else x = r[w] << (S - sh);
+    return (x & m) | lane_copy;
+}
+
 // P·V of one 32-token half S: B = W rows of this lane's head column, A = value fields (S, db, m).
 template <int VB, int F>
-__device__ __forceinline__ uint32_t vpair(const uint32_t* vs, const uint32_t* vlut) {
-    return *(const uint32_t*)((const uint8_t*)vlut + vfield4<VB, F>(vs));
+__device__ __forceinline__ uint32_t vpair(const uint32_t* vs, const uint32_t* vlut, uint32_t lane_copy) {
+    return *(const uint32_t*)((const uint8_t*)vlut + vfield_rep<VB, F>(vs, lane_copy));
 }
 template <int VB, int S>
 __device__ __forceinline__ void mx_pv(f32x4_t (&o)[8], const uint32_t* vs, const uint32_t* vlut, const uint32_t* wx,
-                                      int lane) {
+                                      int lane, uint32_t lc) {
     const u32x4_t wq = *(const u32x4_t*)(wx + (lane & 15) * 32 + 16 * S + 4 * (lane >> 4));
     const half8_t wb = __builtin_bit_cast(half8_t, wq);
 #define BGTQ_PV(DB)                                                                                          \
-    o[DB] = mfma16(as_h8(vpair<VB, (S * 8 + DB) * 4>(vs, vlut), vpair<VB, (S * 8 + DB) * 4 + 1>(vs, vlut),      \
-                         vpair<VB, (S * 8 + DB) * 4 + 2>(vs, vlut), vpair<VB, (S * 8 + DB) * 4 + 3>(vs, vlut)), \
+    o[DB] = mfma16(as_h8(vpair<VB, (S * 8 + DB) * 4>(vs, vlut, lc), vpair<VB, (S * 8 + DB) * 4 + 1>(vs, vlut, lc), \
+                         vpair<VB, (S * 8 + DB) * 4 + 2>(vs, vlut, lc), vpair<VB, (S * 8 + DB) * 4 + 3>(vs, vlut, lc)), \
                    wb, o[DB])
     BGTQ_PV(0); BGTQ_PV(1); BGTQ_PV(2); BGTQ_PV(3); BGTQ_PV(4); BGTQ_PV(5); BGTQ_PV(6); BGTQ_PV(7);
 #undef BGTQ_PV
@@ -1039,8 +1061,8 @@ constexpr int cmax(int x, int y) { return x > y ? x : y; }
 template <int G, int R, int VB> struct MxLds {
     static constexpr int TAB = 0;                                     // BGTQ_CB_MX_BYTES
     static constexpr int DESC = a16(TAB + BGTQ_CB_MX_BYTES);          // u32 [4 lane rows][16 columns]
-    static constexpr int VLUT = DESC + 64 * 4;                        // u32 [4^VB]
-    static constexpr int QA = a16(VLUT + 4 * (1 << (2 * VB)));        // u32x4 [4 k-steps][64 lanes]
+    static constexpr int VLUT = DESC + 64 * 4;                        // u32 [4^VB][copies]
+    static constexpr int QA = a16(VLUT + VLutGeom<VB>::BYTES);        // u32x4 [4 k-steps][64 lanes]
     static constexpr int WX = QA + 4 * 64 * 16;                       // u32 [4 waves][16 heads][32 pairs]
     static constexpr int ALPHA = WX + 4 * 16 * 32 * 4;                // f32 [4 waves][16]
     static constexpr int NNZ = ALPHA + 4 * 16 * 4;                    // u32 [4]: padded nonzero slots, coordinate columns
@@ -1093,8 +1115,16 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < (TAB4 + 255) / 256; ++k)
         tv[k] = tab4[threadIdx.x + 256 * k < TAB4 ? threadIdx.x + 256 * k : 0];
-    const uint32_t vca = threadIdx.x & ((1 << VB) - 1), vcb = (threadIdx.x >> VB) & ((1 << VB) - 1);
-    const uint32_t vla = c_cent16[cent_base(VB) + vca], vlb = c_cent16[cent_base(VB) + vcb];
+    // value pair table entries this thread writes: entry e = threadIdx.x / copies + 256 / copies * k
+    constexpr int VCOP = VLutGeom<VB>::COPIES, VENT = 1 << (2 * VB);
+    constexpr int VROUNDS = (VENT * VCOP + 255) / 256;
+    uint32_t vla[VROUNDS], vlb[VROUNDS];
+#pragma unroll
+    for (int k = 0; k < VROUNDS; ++k) {
+        const uint32_t e = ((threadIdx.x + 256u * k) / VCOP) & (VENT - 1);
+        vla[k] = c_cent16[cent_base(VB) + (e & ((1u << VB) - 1u))];
+        vlb[k] = c_cent16[cent_base(VB) + (e >> VB)];
+    }
 
     // Tile data: K chunks and one dword of scales per lane (lanes 0..31: K scales of tokens 2l,
     // 2l+1; lanes 32..63: V scales; V zeros in a second dword for affine values) are prefetched one
@@ -1115,18 +1145,22 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         for (int c = 0; c < VB; ++c) vn[c] = vt[c * 64 + lane];
     };
     // Unconditional (branch-free prologue); a wave without tiles reads a tile inside the allocation
-    // and never uses it.
-    {
-        const int64_t t0 = t_lo + wave < t_hi ? t_lo + wave : (t_lo < a.n_tiles ? t_lo : 0);
-        fetch_k(t0);
-        fetch_v(t0);
-    }
+    // and never uses it.  Only the keys now: the values of the first tile go out after the
+    // prologue, so the first burst every wave waits on is half as large.
+    const int64_t t_first = t_lo + wave < t_hi ? t_lo + wave : (t_lo < a.n_tiles ? t_lo : 0);
+    fetch_k(t_first);
 
 #pragma unroll
     for (int k = 0; k < (TAB4 + 255) / 256; ++k)
         if (threadIdx.x + 256 * k < TAB4) ((u32x4_t*)(lds + LD::TAB))[threadIdx.x + 256 * k] = tv[k];
-    if (threadIdx.x < (1 << (2 * VB)))
-        s_vlut[threadIdx.x] = a.v_affine ? (uint32_t)f2h((float)vca) | ((uint32_t)f2h((float)vcb) << 16) : vla | (vlb << 16);
+#pragma unroll
+    for (int k = 0; k < VROUNDS; ++k) {
+        const uint32_t i = threadIdx.x + 256u * k;
+        const uint32_t e = (i / VCOP) & (VENT - 1);
+        if (i < (uint32_t)(VENT * VCOP))
+            s_vlut[i] = a.v_affine ? (uint32_t)f2h((float)(e & ((1u << VB) - 1u))) | ((uint32_t)f2h((float)(e >> VB)) << 16)
+                                   : vla[k] | (vlb[k] << 16);
+    }
 #pragma unroll
     for (int i = threadIdx.x; i < 4 * 16 * 32 / 4; i += 256) ((u32x4_t*)(lds + LD::WX))[i] = u32x4_t{0u, 0u, 0u, 0u};
     const int bw = (int)((pin.w4 >> (8 * (lane & 3))) & 0xFFu);
@@ -1164,6 +1198,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     const int nks = (nnz_pad + 15) >> 4;
     const int ncc = (int)__builtin_amdgcn_readfirstlane(s_nnz[1]);      // coordinate columns
     const u32x4_t* sd = (const u32x4_t*)(lds + LD::DESC) + 4 * row;  // this lane row's descriptors
+    fetch_v(t_first);
 
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, zs[2] = {0.f, 0.f};
     f32x4_t o[8];
@@ -1171,6 +1206,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     uint32_t lb = (uint32_t)(LD::KST + wave * LD::KST_W) + 4u * (uint32_t)col;
     asm volatile("" : "+v"(lb));  // keep the stage base inside lb: one add per column address
+    const uint32_t lcopy = 4u * ((uint32_t)lane & (VLutGeom<VB>::COPIES - 1));  // this lane's value-table copy
 
     for (int64_t t = t_lo + wave; t < t_hi; t += 4) {
         // Stage the tile: K rows (row rho of the record at stage row rho + 1), scales (transposed:
@@ -1279,8 +1315,8 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         for (int c = 0; c < VB; ++c) {
             vs[4 * c] = vn[c][0]; vs[4 * c + 1] = vn[c][1]; vs[4 * c + 2] = vn[c][2]; vs[4 * c + 3] = vn[c][3];
         }
-        mx_pv<VB, 0>(o, vs, s_vlut, wx, lane);
-        mx_pv<VB, 1>(o, vs, s_vlut, wx, lane);
+        mx_pv<VB, 0>(o, vs, s_vlut, wx, lane, lcopy);
+        mx_pv<VB, 1>(o, vs, s_vlut, wx, lane, lcopy);
         if (t + 4 < t_hi) fetch_v(t + 4);
     }
 
