@@ -910,42 +910,52 @@ __device__ __forceinline__ void col_pair2(uint32_t (&P)[16], const uint8_t* lds,
     const uint32_t mB = CB ? bfm<1>(dB >> 12) : bfm<2>(dB >> 12);
     const uint32_t bA = mA + (CA ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
     const uint32_t bB = mB + (CB ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
+    // the four windows (stage rows r, r + 1 of token groups g = 0..3) as four ds_read2, each
+    // straight into a register pair; the block waits for them itself.
+    static_assert(BGTQ_KST_ROW_BYTES == 320, "window read offsets assume 80-dword stage rows");
+    uint64_t wv[4];
+    asm volatile("ds_read2_b32 %0, %4 offset1:80\n\t"
+                 "ds_read2_b32 %1, %4 offset0:16 offset1:96\n\t"
+                 "ds_read2_b32 %2, %4 offset0:32 offset1:112\n\t"
+                 "ds_read2_b32 %3, %4 offset0:48 offset1:128\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(wv[0]), "=&v"(wv[1]), "=&v"(wv[2]), "=&v"(wv[3])
+                 : "v"((uint32_t)(uintptr_t)(lds + ad))
+                 : "memory");
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        const uint32_t lo = *(const uint32_t*)(lds + ad + 64 * g);
-        const uint32_t hi = *(const uint32_t*)(lds + ad + 64 * g + BGTQ_KST_ROW_BYTES);
-        const uint64_t win = ((uint64_t)hi << 32) | lo;
+        const uint64_t win = wv[g];
         P[4 * g + 2 * M] = CA ? slot_coord(lds, win, dA, mA, bA) : slot_pair(lds, win, dA, mA, bA);
         P[4 * g + 2 * M + 1] = CB ? slot_coord(lds, win, dB, mB, bB) : slot_pair(lds, win, dB, mB, bB);
     }
 }
 
-// k-step KS with its first A columns read per coordinate and the rest as pairs.
+// k-step KS with its first A columns read per coordinate and the rest as pairs: the operands.
 template <int KS, int A>
-__device__ __forceinline__ void mx_kstep(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
-                                         const u32x4_t* sd, uint32_t lb) {
-    uint32_t P[16];
+__device__ __forceinline__ void mx_kops(uint32_t (&P)[16], const uint8_t* lds, const u32x4_t* sd, uint32_t lb) {
     const u32x4_t dk = sd[KS];
     col_pair2<0, (A > 0), (A > 1)>(P, lds, dk[0], dk[1], lb);
     col_pair2<1, (A > 2), (A > 3)>(P, lds, dk[2], dk[3], lb);
+}
+
+// k-step KS of a tile; ncc (wave-uniform) = number of coordinate columns of the whole record.  The
+// column modes only change how the operands are built; the products sit after the branches.
+template <int KS>
+__device__ __forceinline__ void mx_kstep_any(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
+                                             const u32x4_t* sd, uint32_t lb, int ncc) {
+    uint32_t P[16];
+    const int a = ncc - 4 * KS;
+    if (a <= 0) mx_kops<KS, 0>(P, lds, sd, lb);
+    else if (a == 1) mx_kops<KS, 1>(P, lds, sd, lb);
+    else if (a == 2) mx_kops<KS, 2>(P, lds, sd, lb);
+    else if (a == 3) mx_kops<KS, 3>(P, lds, sd, lb);
+    else mx_kops<KS, 4>(P, lds, sd, lb);
     const half8_t q = __builtin_bit_cast(half8_t, qa[KS * 64 + lane]);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const half8_t kb = as_h8(P[4 * g], P[4 * g + 1], P[4 * g + 2], P[4 * g + 3]);
         c[g] = KS == 0 ? mfma16(q, kb, f32x4_t{0.f, 0.f, 0.f, 0.f}) : mfma16(q, kb, c[g]);
     }
-}
-
-// k-step KS of a tile; ncc (wave-uniform) = number of coordinate columns of the whole record.
-template <int KS>
-__device__ __forceinline__ void mx_kstep_any(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
-                                             const u32x4_t* sd, uint32_t lb, int ncc) {
-    const int a = ncc - 4 * KS;
-    if (a <= 0) mx_kstep<KS, 0>(c, lds, qa, lane, sd, lb);
-    else if (a == 1) mx_kstep<KS, 1>(c, lds, qa, lane, sd, lb);
-    else if (a == 2) mx_kstep<KS, 2>(c, lds, qa, lane, sd, lb);
-    else if (a == 3) mx_kstep<KS, 3>(c, lds, qa, lane, sd, lb);
-    else mx_kstep<KS, 4>(c, lds, qa, lane, sd, lb);
 }
 
 // The matrix-core decode's value table holds VLUT_COPIES interleaved copies (entry e of copy c at
@@ -988,13 +998,32 @@ __device__ __forceinline__ void mx_pv(f32x4_t (&o)[8], const uint32_t* vs, const
 #undef BGTQ_PV
 }
 
-// Max over the 16 lanes of a row (DPP row rotations).
+// Plain v_max_f32 / v_max3_f32: the operands here are never NaN (scores, -inf for masked tokens),
+// so the quieting that fmaxf adds on values of unknown origin is dead work.
+__device__ __forceinline__ float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+// Max over the 16 lanes of a row: four DPP row rotations fused into the max (two wait states
+// before each, as a DPP source written by the previous VALU instruction requires).
 __device__ __forceinline__ float row_max16(float v) {
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false)));
-    return v;
+    float r;
+    asm("s_nop 1\n\t"
+        "v_max_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf"
+        : "=&v"(r) : "v"(v));
+    return r;
 }
 __device__ __forceinline__ float row_sum16(float v) {
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
@@ -1130,7 +1159,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     // 2l+1; lanes 32..63: V scales; V zeros in a second dword for affine values) are prefetched one
     // tile ahead and staged to LDS when their tile starts; the value streams stay in registers
     // (each lane reads its own stream) and are loaded once the previous tile's P·V is done.
-    u32x4_t kn[R / 4], vn[VB];
+    u32x4_t kn[R / 4], vn[VB], vx[VB];
     uint32_t sn, zn;
     auto fetch_k = [&](int64_t t) {
         const u32x4_t* kt = (const u32x4_t*)(kc + t * (a.k_tile_bytes / 4));
@@ -1139,10 +1168,10 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         sn = (lane < 32 ? ks32 : vs32)[t * (TILE / 2) + (lane & 31)];
         zn = vz32 ? vz32[t * (TILE / 2) + (lane & 31)] : 0u;
     };
-    auto fetch_v = [&](int64_t t) {
+    auto fetch_v = [&](u32x4_t (&dst)[VB], int64_t t) {
         const u32x4_t* vt = (const u32x4_t*)(vc + t * (a.v_tile_bytes / 4));
 #pragma unroll
-        for (int c = 0; c < VB; ++c) vn[c] = vt[c * 64 + lane];
+        for (int c = 0; c < VB; ++c) dst[c] = vt[c * 64 + lane];
     };
     // Unconditional (branch-free prologue); a wave without tiles reads a tile inside the allocation
     // and never uses it.  Only the keys now: the values of the first tile go out after the
@@ -1198,7 +1227,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     const int nks = (nnz_pad + 15) >> 4;
     const int ncc = (int)__builtin_amdgcn_readfirstlane(s_nnz[1]);      // coordinate columns
     const u32x4_t* sd = (const u32x4_t*)(lds + LD::DESC) + 4 * row;  // this lane row's descriptors
-    fetch_v(t_first);
+    fetch_v(vn, t_first);
 
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, zs[2] = {0.f, 0.f};
     f32x4_t o[8];
@@ -1208,7 +1237,8 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     asm volatile("" : "+v"(lb));  // keep the stage base inside lb: one add per column address
     const uint32_t lcopy = 4u * ((uint32_t)lane & (VLutGeom<VB>::COPIES - 1));  // this lane's value-table copy
 
-    for (int64_t t = t_lo + wave; t < t_hi; t += 4) {
+    // two tiles per iteration: the value streams of the next tile load into the other buffer
+    auto tile = [&](const int64_t t, u32x4_t (&vcur)[VB], u32x4_t (&vnext)[VB]) __attribute__((always_inline)) {
         // Stage the tile: K rows (row rho of the record at stage row rho + 1), scales (transposed:
         // token u at (u%16)*4 + u/16).
         wave_lds_fence();
@@ -1226,7 +1256,12 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         }
         wave_lds_fence();
         asm volatile("" ::: "memory");
-        if (t + 4 < t_hi) fetch_k(t + 4);
+        {
+            // unconditional, so that no branch merges the wait counts (the last tile re-reads itself)
+            const int64_t tn = t + 4 < t_hi ? t + 4 : t;
+            fetch_k(tn);
+            fetch_v(vnext, tn);
+        }
 
         // q·k on the matrix cores
         f32x4_t c[4];
@@ -1268,12 +1303,16 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         }
         float tmax[2];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) tmax[hh] = fmaxf(fmaxf(z[0][hh], z[1][hh]), fmaxf(z[2][hh], z[3][hh]));
-        if (__ballot(tmax[0] > m[0] || tmax[1] > m[1])) {
+        for (int hh = 0; hh < 2; ++hh) tmax[hh] = vmax(vmax3(z[0][hh], z[1][hh], z[2][hh]), z[3][hh]);
+        if (t == t_lo + wave) {
+            // the wave's first tile: nothing accumulated yet, so no rescale
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) m[hh] = row_max16(tmax[hh]);
+        } else if (__ballot(tmax[0] > m[0] || tmax[1] > m[1])) {
             float alpha[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const float mn = fmaxf(m[hh], row_max16(tmax[hh]));
+                const float mn = vmax(m[hh], row_max16(tmax[hh]));
                 alpha[hh] = __builtin_amdgcn_exp2f(m[hh] - mn);
                 m[hh] = mn;
                 l[hh] *= alpha[hh];
@@ -1313,11 +1352,14 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         uint32_t vs[4 * VB];
 #pragma unroll
         for (int c = 0; c < VB; ++c) {
-            vs[4 * c] = vn[c][0]; vs[4 * c + 1] = vn[c][1]; vs[4 * c + 2] = vn[c][2]; vs[4 * c + 3] = vn[c][3];
+            vs[4 * c] = vcur[c][0]; vs[4 * c + 1] = vcur[c][1]; vs[4 * c + 2] = vcur[c][2]; vs[4 * c + 3] = vcur[c][3];
         }
         mx_pv<VB, 0>(o, vs, s_vlut, wx, lane, lcopy);
         mx_pv<VB, 1>(o, vs, s_vlut, wx, lane, lcopy);
-        if (t + 4 < t_hi) fetch_v(t + 4);
+        };
+    for (int64_t t = t_lo + wave; t < t_hi; t += 8) {
+        tile(t, vn, vx);
+        if (t + 4 < t_hi) tile(t + 4, vx, vn);
     }
 
     // Epilogue: row sums of l and the zero term, O^T to LDS (over the stages), merge the waves.
