@@ -958,11 +958,13 @@ __device__ __forceinline__ void mx_kstep_any(f32x4_t (&c)[4], const uint8_t* lds
     }
 }
 
-// The matrix-core decode's value table holds VLUT_COPIES interleaved copies (entry e of copy c at
-// dword e * copies + c) and lane l reads copy l % copies, so lanes looking up different entries
-// rarely meet in one LDS bank.
+// The matrix-core decode's value table holds interleaved copies (entry e of copy c at dword
+// e * copies + c) and lane l reads copy l % copies.  With 32 copies (values of up to 3 bits, 8 KB
+// at 3 bits) every lane of the 32 that the LDS serves per pass owns one of its 32 banks, so random
+// entries never conflict (measured on gfx950: random reads from a table wider than 32 dwords cost
+// 1.7x to 2.8x a conflict-free read); 4-bit values keep 4 copies (the 256-entry table).
 template <int VB> struct VLutGeom {
-    static constexpr int LOG2_COPIES = VB <= 3 ? 4 : 2;
+    static constexpr int LOG2_COPIES = VB <= 3 ? 5 : 2;
     static constexpr int COPIES = 1 << LOG2_COPIES;
     static constexpr int BYTES = 4 * COPIES * (1 << (2 * VB));
 };
@@ -1237,7 +1239,9 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
     asm volatile("" : "+v"(lb));  // keep the stage base inside lb: one add per column address
     const uint32_t lcopy = 4u * ((uint32_t)lane & (VLutGeom<VB>::COPIES - 1));  // this lane's value-table copy
 
-    // two tiles per iteration: the value streams of the next tile load into the other buffer
+    // two tiles per iteration: the value streams of the next tile load into the other buffer (4-bit
+    // values: one buffer, reloaded after P·V, as a second one would not fit the register budget)
+    constexpr bool VDB = VB <= 3;
     auto tile = [&](const int64_t t, u32x4_t (&vcur)[VB], u32x4_t (&vnext)[VB]) __attribute__((always_inline)) {
         // Stage the tile: K rows (row rho of the record at stage row rho + 1), scales (transposed:
         // token u at (u%16)*4 + u/16).
@@ -1260,7 +1264,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
             // unconditional, so that no branch merges the wait counts (the last tile re-reads itself)
             const int64_t tn = t + 4 < t_hi ? t + 4 : t;
             fetch_k(tn);
-            fetch_v(vnext, tn);
+            if constexpr (VDB) fetch_v(vnext, tn);
         }
 
         // q·k on the matrix cores
@@ -1356,10 +1360,17 @@ __global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
         }
         mx_pv<VB, 0>(o, vs, s_vlut, wx, lane, lcopy);
         mx_pv<VB, 1>(o, vs, s_vlut, wx, lane, lcopy);
+        if constexpr (!VDB) {
+            if (t + 4 < t_hi) fetch_v(vcur, t + 4);
+        }
         };
-    for (int64_t t = t_lo + wave; t < t_hi; t += 8) {
-        tile(t, vn, vx);
-        if (t + 4 < t_hi) tile(t + 4, vx, vn);
+    if constexpr (VDB) {
+        for (int64_t t = t_lo + wave; t < t_hi; t += 8) {
+            tile(t, vn, vx);
+            if (t + 4 < t_hi) tile(t + 4, vx, vn);
+        }
+    } else {
+        for (int64_t t = t_lo + wave; t < t_hi; t += 4) tile(t, vn, vn);
     }
 
     // Epilogue: row sums of l and the zero term, O^T to LDS (over the stages), merge the waves.

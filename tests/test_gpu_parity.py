@@ -51,6 +51,10 @@ CASES = {
     "w4_reduced": (4, {"L": 1, "B": 2}, 2048 + 13, (None,)),
     "w5_reduced": (5, {}, 3000, (1000, 7, None)),
     "w5_all_recent": (5, {}, 200, (None,)),
+    # other matrix-core template shapes: 16-dword key records with 4-bit values (one value buffer),
+    # and 4 query heads per kv head with 12-dword records and 3-bit values
+    "w2_k4v4": (2, {"L": 1, "v_bits": 4, "k_budget_units": 256}, 1500 + 3, (None,)),
+    "w3_k3v3": (3, {"L": 1, "B": 1, "v_bits": 3, "k_budget_units": 192}, 1000 + 9, (700, None)),
 }
 
 
