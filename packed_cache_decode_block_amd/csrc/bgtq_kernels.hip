@@ -1429,6 +1429,259 @@ __global__ __launch_bounds__(256, 2) void k_decode_fp16(const Fp16Args a) {
     write_partial<G>(st, s_red, part, a.n_parts, a.split0 + split, wave, lane);
 }
 
+// Matrix-core decode over fp16 rows [n][128] of one (b, h), for 4 or 8 query heads per kv head
+// (the unquantized comparator, and the fp16 recent ring of a packed cache).  Same split-K
+// structure, softmax and wave merge as the packed matrix-core kernel; only the operands differ:
+//  * q·k: A = Q' (row 4u + e: head 2u + e/2, the fp16 high part of q * log2(e)/sqrt(d) for e
+//    even, the low part for e odd), built per lane in registers; B = K^T straight from HBM: lane
+//    (token column n, lane row u) of k-step ks loads the 16 bytes of dims 32 ks + 8u .. 8u + 7 of
+//    its token, which is exactly its B operand (one instruction reads 16 whole 64-byte segments).
+//  * P·V: A = V^T from the tile staged in LDS.  A 4-byte read gives two adjacent dims of one
+//    token; the even dims feed one product and the odd dims another, so lane (i, u) of dim block
+//    j reads dims 32 j + 2i, 32 j + 2i + 1 of the tokens (p, p + 32), p = 16 S + 4u + e.  The
+//    tile is staged 32 tokens at a time (the two halves S), rows of 272 bytes: the 32 lanes of a
+//    read then hit 32 distinct banks.  B = W through LDS in (p, p + 32) pair order.
+constexpr int F16MX_VROW = 272;  // bytes per staged value row (256 + 16)
+template <int G> struct F16MxLds {
+    static constexpr int VST = 0;                               // per wave: 32 rows
+    static constexpr int VST_W = 32 * F16MX_VROW;
+    static constexpr int WX = VST + 4 * VST_W;                  // u32 [4 waves][16 heads][32 pairs]
+    static constexpr int ALPHA = WX + 4 * 16 * 32 * 4;          // f32 [4 waves][16]
+    static constexpr int RED = VST;                             // epilogue: f32 [4 G PART + 4 G]
+    static constexpr int SIZE = cmax(ALPHA + 4 * 16 * 4, RED + 4 * (4 * G * PART + 4 * G));
+};
+
+template <int G>
+__global__ __launch_bounds__(256, 2) void k_decode_fp16_mx(const Fp16Args a) {
+    static_assert(G == 4 || G == 8, "matrix-core fp16 decode serves 4 or 8 query heads per kv head");
+    using LD = F16MxLds<G>;
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int row = lane >> 4, col = lane & 15;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LD::SIZE];
+    uint8_t* vst = lds + LD::VST + wave * LD::VST_W;
+    uint32_t* wx = (uint32_t*)(lds + LD::WX) + wave * 16 * 32;
+    float* s_alpha = (float*)(lds + LD::ALPHA) + wave * 16;
+
+    const size_t bh = (size_t)b * a.Hkv + h;
+    const int64_t n = a.n_valid[b];
+    const int64_t n_tiles = (n + TILE - 1) / TILE;
+    const int64_t t_lo = (int64_t)split * a.tiles_per_split;
+    const int64_t t_hi = t_lo + a.tiles_per_split < n_tiles ? t_lo + a.tiles_per_split : n_tiles;
+    const uint16_t* K16 = a.k16 + bh * a.rows * D;
+    const uint16_t* V16 = a.v16 + bh * a.rows * D;
+    const int64_t last = n > 0 ? n - 1 : 0;  // rows past the end are never read: loads clamp to it
+
+    // Tile loads: kk[g][ks] is the B operand of token group g, k-step ks; vv[k] is the 16 bytes at
+    // tile offset 1024 k + 16 lane (token 4k + lane / 16, dims 8 (lane % 16) ..).
+    u32x4_t kk[4][4], vv[16];
+    auto fetch_k = [&](int64_t t) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int64_t tok = t * TILE + 16 * g + col;
+            const u32x4_t* r = (const u32x4_t*)(K16 + (tok < last ? tok : last) * D);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) kk[g][ks] = r[4 * ks + row];
+        }
+    };
+    auto fetch_v = [&](int64_t t) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t tok = t * TILE + 4 * k + row;
+            vv[k] = ((const u32x4_t*)(V16 + (tok < last ? tok : last) * D))[col];
+        }
+    };
+    const int64_t t_first = t_lo + wave < t_hi ? t_lo + wave : (t_lo < n_tiles ? t_lo : 0);
+    fetch_k(t_first);
+    fetch_v(t_first);
+
+    // Query operands (lane = A row col, lane row u = row): dims 32 ks + 8 row .. of head qh.
+    u32x4_t qa[4];
+    {
+        const int qh = 2 * (col >> 2) + ((col >> 1) & 1), lo_part = col & 1;
+        const int64_t qrow = ((int64_t)b * a.Hq + (int64_t)h * G + (qh < G ? qh : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            float x[8];
+            const int d0 = 32 * ks + 8 * row;
+            if (a.q_dtype == BGTQ_F32) {
+                const f32x4_t v0 = *(const f32x4_t*)((const float*)a.q + qrow + d0);
+                const f32x4_t v1 = *(const f32x4_t*)((const float*)a.q + qrow + d0 + 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { x[j] = v0[j]; x[4 + j] = v1[j]; }
+            } else {
+                const u32x4_t v = *(const u32x4_t*)((const uint16_t*)a.q + qrow + d0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x[2 * j] = a.q_dtype == BGTQ_F16 ? h2f(v[j] & 0xFFFFu) : bf2f(v[j] & 0xFFFFu);
+                    x[2 * j + 1] = a.q_dtype == BGTQ_F16 ? h2f(v[j] >> 16) : bf2f(v[j] >> 16);
+                }
+            }
+            uint32_t hv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t e2[2];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const float qs = x[2 * j + c] * kLog2eOverSqrtD;
+                    const _Float16 hi = (_Float16)qs;
+                    const _Float16 lo = (_Float16)(qs - (float)hi);
+                    e2[c] = qh < G ? (uint32_t)__builtin_bit_cast(uint16_t, lo_part ? lo : hi) : 0u;
+                }
+                hv[j] = e2[0] | (e2[1] << 16);
+            }
+            qa[ks] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
+        }
+    }
+    // W rows of absent heads stay zero
+#pragma unroll
+    for (int i = threadIdx.x; i < 4 * 16 * 32 / 4; i += 256) ((u32x4_t*)(lds + LD::WX))[i] = u32x4_t{0u, 0u, 0u, 0u};
+    __syncthreads();
+
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    f32x4_t o[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j][0] = o[j][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // value rows of half S: instruction k holds tokens 4k .. 4k + 3; half S holds tokens
+    // 16 S .. 16 S + 15 (stage rows 0..15) and 32 + 16 S .. 47 + 16 S (rows 16..31)
+    auto stage_half = [&](int S) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int tok = 4 * k + row;
+            if (((tok >> 4) & 1) != S) continue;  // compile-time per k (row varies only inside a group of 4)
+            const int srow = (tok & 15) + 16 * (tok >> 5);
+            *(u32x4_t*)(vst + srow * F16MX_VROW + 16 * col) = vv[k];
+        }
+    };
+    auto pv_half = [&](int S) __attribute__((always_inline)) {
+        const u32x4_t wq = *(const u32x4_t*)(wx + col * 32 + 16 * S + 4 * row);
+        const half8_t wb = __builtin_bit_cast(half8_t, wq);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t d0 = *(const uint32_t*)(vst + (4 * row + e) * F16MX_VROW + 4 * (16 * j + col));
+                const uint32_t d1 = *(const uint32_t*)(vst + (16 + 4 * row + e) * F16MX_VROW + 4 * (16 * j + col));
+                lo[e] = __builtin_amdgcn_perm(d1, d0, 0x05040100u);  // (V[p][2i], V[p+32][2i])
+                hi[e] = __builtin_amdgcn_perm(d1, d0, 0x07060302u);  // (V[p][2i+1], V[p+32][2i+1])
+            }
+            o[j][0] = mfma16(as_h8(lo[0], lo[1], lo[2], lo[3]), wb, o[j][0]);
+            o[j][1] = mfma16(as_h8(hi[0], hi[1], hi[2], hi[3]), wb, o[j][1]);
+        }
+    };
+
+    for (int64_t t = t_lo + wave; t < t_hi; t += 4) {
+        // q·k on the matrix cores
+        f32x4_t c[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            c[g] = mfma16(__builtin_bit_cast(half8_t, qa[0]), __builtin_bit_cast(half8_t, kk[g][0]), f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int ks = 1; ks < 4; ++ks)
+                c[g] = mfma16(__builtin_bit_cast(half8_t, qa[ks]), __builtin_bit_cast(half8_t, kk[g][ks]), c[g]);
+        }
+        // the keys of this tile are consumed: the next tile's go out (a wave's last tile requests
+        // itself again, so that no branch joins the wait counts)
+        const int64_t tn = t + 4 < t_hi ? t + 4 : t;
+        fetch_k(tn);
+        // first value half to LDS; the second stays in registers until the first is consumed
+        wave_lds_fence();
+        stage_half(0);
+
+        // softmax over the tile: lane holds tokens 16g + col, heads 2row, 2row + 1
+        float z[4][2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const bool valid = t * TILE + 16 * g + col < n;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) z[g][hh] = valid ? c[g][2 * hh] + c[g][2 * hh + 1] : -INFINITY;
+        }
+        float tmax[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) tmax[hh] = vmax(vmax3(z[0][hh], z[1][hh], z[2][hh]), z[3][hh]);
+        if (t == t_lo + wave) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) m[hh] = row_max16(tmax[hh]);
+        } else if (__ballot(tmax[0] > m[0] || tmax[1] > m[1])) {
+            float alpha[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const float mn = vmax(m[hh], row_max16(tmax[hh]));
+                alpha[hh] = __builtin_amdgcn_exp2f(m[hh] - mn);
+                m[hh] = mn;
+                l[hh] *= alpha[hh];
+            }
+            wave_lds_fence();
+            if (col == 0) {
+                s_alpha[2 * row] = alpha[0];
+                s_alpha[2 * row + 1] = alpha[1];
+            }
+            wave_lds_fence();
+            const float al = s_alpha[col];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                o[j][0] *= al;
+                o[j][1] *= al;
+            }
+        }
+        uint16_t wh[4][2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const float p = __builtin_amdgcn_exp2f(z[g][hh] - m[hh]);
+                l[hh] += p;
+                wh[g][hh] = f2h(p);
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            uint32_t* wr = wx + (2 * row + hh) * 32 + col;
+            wr[0] = (uint32_t)wh[0][hh] | ((uint32_t)wh[2][hh] << 16);
+            wr[16] = (uint32_t)wh[1][hh] | ((uint32_t)wh[3][hh] << 16);
+        }
+        wave_lds_fence();
+        pv_half(0);
+        wave_lds_fence();
+        stage_half(1);
+        wave_lds_fence();
+        fetch_v(tn);  // the values of this tile are all staged
+        pv_half(1);
+    }
+
+    // Epilogue: row sums of l, O^T to LDS (over the stages), merge the waves.
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) l[hh] = row_sum16(l[hh]);
+    __syncthreads();  // every wave is done with its stage
+    float* s_red = (float*)(lds + LD::RED);
+    float* r = s_red + wave * G * PART;
+    if (col < G) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                r[col * PART + 32 * j + 2 * (4 * row + e)] = o[j][0][e];
+                r[col * PART + 32 * j + 2 * (4 * row + e) + 1] = o[j][1][e];
+            }
+    }
+    if (col == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int hd = 2 * row + hh;
+            if (hd < G) {
+                r[hd * PART + 128] = m[hh];
+                r[hd * PART + 129] = l[hh];
+                r[hd * PART + 130] = 0.f;
+            }
+        }
+    }
+    __syncthreads();
+    float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_parts * PART;
+    merge_waves4<G>(s_red, s_red + 4 * G * PART, part, a.n_parts, a.split0 + split);
+}
+
 // Merge split partials (o, m, l) of one (batch, query head) by log-sum-exp.  Grid: (row, slice of
 // 16 dims); thread s takes splits s, s + 256, ...  The first split's record is loaded together with
 // the maxima so one memory round trip covers the common case (at most 256 splits).
@@ -1780,7 +2033,8 @@ hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t s
 
 template <int G>
 static hipError_t launch_fp16_g(const Fp16Args& a, int B, hipStream_t s) {
-    return launch_main(k_decode_fp16<G>, dim3(a.n_splits, a.Hkv, B), dim3(256), s, a);
+    if constexpr (G >= 4) return launch_main(k_decode_fp16_mx<G>, dim3(a.n_splits, a.Hkv, B), dim3(256), s, a);
+    else return launch_main(k_decode_fp16<G>, dim3(a.n_splits, a.Hkv, B), dim3(256), s, a);
 }
 
 hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t s) {

@@ -64,3 +64,19 @@ def test_full_size_layer(wid):
         ref = pipeline.decode_layer(oc, q[b:b + 1, h * g:(h + 1) * g].float().cpu().numpy())
         e = T.assert_close(out[b:b + 1, h * g:(h + 1) * g], ref, f"workload {wid} b={b} h={h}")
         print(f"  pair (b={b}, h={h}): codes exact, max abs err {e:.2e}", flush=True)
+
+
+def test_full_size_fp16_comparator():
+    """The unquantized comparator at the headline shape (Qwen2.5-3B, 131072 tokens, 16 query / 2 kv
+    heads) with the automatic split count the bench uses; every query head against the oracle."""
+    w = synth.reduced(synth.WORKLOADS[2], L=1)
+    N = w.N
+    print(f"[full size] fp16 comparator: N={N} Hq={w.Hq} Hkv={w.Hkv}", flush=True)
+    k16 = torch.stack([sg.keys(w, 0, h, 0, N) for h in range(w.Hkv)])[None].to(torch.float16)  # [1, Hkv, N, d]
+    v16 = torch.stack([sg.values(w, 0, h, 0, N) for h in range(w.Hkv)])[None].to(torch.float16)
+    q = torch.stack([torch.cat([sg.queries(w, 0, h, 0, N) for h in range(w.Hkv)])])
+    import packed_cache_decode_block_amd as P
+    out = P.bgtq_fp16_decode_attention(k16, v16, q, n_splits=0).cpu().numpy()
+    ref = pipeline.fp16_decode(k16.cpu().numpy(), v16.cpu().numpy(), q.float().cpu().numpy())
+    e = T.assert_close(out, ref, "fp16 comparator, full size")
+    print(f"  max abs err {e:.2e}", flush=True)

@@ -130,16 +130,30 @@ def test_errors_on_device_paths():
     assert cache.n_tokens[0, 0] == 0
 
 
-def test_fp16_baseline_decode():
-    w = synth.reduced(synth.WORKLOADS[2], L=1, B=2)
-    N = 3000
+FP16_CASES = {
+    # name: (workload id, overrides, N, n_splits); 4 and 8 query heads per kv head take the
+    # matrix-core kernel, 1 and 2 the vector one
+    "g8_splits5": (2, {"L": 1, "B": 2}, 3000, 5),
+    "g8_auto_ragged": (2, {"L": 1}, 64 * 7 + 13, 0),
+    "g8_one_split_tail": (2, {"L": 1}, 200, 1),
+    "g4_auto": (3, {"L": 1, "B": 2}, 2048 + 5, 0),
+    "g4_fp32_query": (3, {"L": 1, "B": 1, "dtype": "f32"}, 1000, 3),
+    "g1_vector": (1, {}, 1000, 3),
+    "g2_vector": (2, {"L": 1, "Hq": 4, "Hkv": 2}, 777, 0),
+}
+
+
+@pytest.mark.parametrize("name", list(FP16_CASES))
+def test_fp16_baseline_decode(name):
+    wid, ov, N, ns = FP16_CASES[name]
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
     K, V, q = T.inputs(w, 0, N)
     k16 = K.astype(np.float16)
     v16 = V.astype(np.float16)
     ref = pipeline.fp16_decode(k16, v16, q)
     out = P.bgtq_fp16_decode_attention(torch.from_numpy(k16).cuda(), torch.from_numpy(v16).cuda(),
-                                       T.to_dev(q, w.dtype), n_splits=5)
-    T.assert_close(out.cpu().numpy(), ref, "fp16 baseline")
+                                       T.to_dev(q, w.dtype), n_splits=ns)
+    T.assert_close(out.cpu().numpy(), ref, f"fp16 baseline {name}")
 
 
 @pytest.mark.parametrize("wid", [1, 3])
