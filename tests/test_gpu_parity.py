@@ -81,6 +81,60 @@ def test_quantize_and_decode(name):
         print(f"  splits={ns}: max abs err {e:.2e}", flush=True)
 
 
+def _widths(spec, seed):
+    """Fixed allocation: spec = [(width, count), ...] over the 64 blocks (the rest get 0), placed in
+    a seeded block order so that the stream order is not the block order."""
+    bits = np.zeros(64, np.int64)
+    order = np.random.default_rng(seed).permutation(64)
+    i = 0
+    for wd, cnt in spec:
+        bits[order[i:i + cnt]] = wd
+        i += cnt
+    return bits
+
+
+FIXED_CASES = {
+    # name: (workload id, overrides, width spec, N).  The calibrated allocations of the workloads
+    # leave 37..50 nonzero slots, so these shapes exercise what they do not: all 64 slots (four
+    # k-steps), records without coordinate columns, records of coordinate columns only, a single
+    # k-step, and the pair/coordinate boundary between widths 5 and 6 inside one k-step.
+    "uniform_k3_g8": (2, {"L": 1}, [(3, 64)], 1500 + 7),
+    "uniform_k2_g4": (3, {"L": 1, "B": 1, "v_bits": 2, "k_budget_units": 128}, [(2, 64)], 1000 + 3),
+    "uniform_k4_v4_g8": (2, {"L": 1, "v_bits": 4, "k_budget_units": 256}, [(4, 64)], 700 + 11),
+    "wide_only_g8": (2, {"L": 1}, [(8, 24)], 900 + 1),
+    "one_kstep_g4": (3, {"L": 1, "B": 1, "v_bits": 2, "k_budget_units": 128}, [(8, 16)], 500 + 5),
+    "widths_5_6_g8": (2, {"L": 1}, [(6, 16), (5, 16), (2, 8)], 1200 + 9),
+    "widths_1_to_8_g8": (2, {"L": 1}, [(8, 4), (7, 4), (6, 4), (5, 4), (4, 4), (3, 16), (2, 8), (1, 8)], 800 + 2),
+}
+
+
+@pytest.mark.parametrize("name", list(FIXED_CASES))
+def test_fixed_allocation_decode(name):
+    """Uniform (TQ-MSE-style, every block at the same width) and hand-made Block-GTQ allocations
+    through the same quantize and decode kernels, against the oracle."""
+    wid, ov, spec, N = FIXED_CASES[name]
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
+    bits = np.stack([_widths(spec, 17 + h) for h in range(w.Hkv)])
+    assert np.all(bits.sum(axis=1) == w.k_budget_units)
+    print(f"[fixed {name}] N={N} Hq={w.Hq} Hkv={w.Hkv} nonzero={(bits[0] > 0).sum()}", flush=True)
+    cal = T.meta(w, 0)
+    m = pipeline.LayerMeta(bits, cal.sigma, cal.r, cal.scores)
+    n_cap = ((N + 63) // 64) * 64
+    K, V, q = T.inputs(w, 0, N)
+    oc = T.oracle_layer(w, K, V, m, n_cap)
+    cache = T.gpu_cache(w, n_cap)
+    cache.set_metadata(0, m.bits, m.sigma, m.r)
+    T.append_all(cache, 0, K, V, w.dtype)
+    _compare_cache(cache, oc, w)
+    ref = pipeline.decode_layer(oc, q)
+    qd = T.to_dev(q, w.dtype)
+    for ns in (0, 1, 3):
+        out = cache.decode_attention(0, qd, n_splits=ns)
+        torch.cuda.synchronize()
+        e = T.assert_close(out.cpu().numpy(), ref, f"{name} splits={ns}")
+        print(f"  splits={ns}: max abs err {e:.2e}", flush=True)
+
+
 def test_decode_deterministic_and_split_invariant():
     w = synth.reduced(synth.WORKLOADS[2], L=1)
     N = 5000
