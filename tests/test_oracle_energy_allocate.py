@@ -134,3 +134,82 @@ def test_ldexp_exact_ties_lowest_index():
     # s0 * 4^-1 == s1 exactly: the tie must go to block 0
     b = allocate.greedy([4.0, 1.0], 2, 8)
     np.testing.assert_array_equal(b, [2, 0])
+
+
+# --- greedy under a tabulated rate (the realized Lloyd-Max D(b) instead of 4^-b) ---
+
+def _lloyd_rate(bmax=8):
+    from oracle import codebook
+    return [1.0] + [codebook.codebook_mse(b) for b in range(1, bmax + 1)]
+
+
+def test_realized_rate_is_convex_and_above_4_pow_minus_b():
+    """The frozen tables' D(b) falls with shrinking steps (so the rate greedy is optimal) and sits
+    above 4^-b by a factor that grows toward the Panter-Dite constant pi*sqrt(3)/2."""
+    r = _lloyd_rate()
+    gain = np.diff(r) * -1
+    assert np.all(gain > 0) and np.all(np.diff(gain) < 0)
+    ratio = [r[b] * 4.0 ** b for b in range(1, 9)]
+    assert ratio[0] == pytest.approx(4 * (1 - 2 / np.pi), rel=1e-3)   # D(1) = 1 - 2/pi
+    assert np.all(np.diff(ratio) > 0) and ratio[-1] < np.pi * np.sqrt(3) / 2
+
+
+def _brute_rate(s, U, bmax, rate):
+    best, arg, count = None, None, 0
+    for b in itertools.product(range(bmax + 1), repeat=len(s)):
+        if sum(b) != U or any(bi and si == 0 for bi, si in zip(b, s)):
+            continue
+        obj = allocate.objective_rate(s, b, rate)
+        if best is None or obj < best - 1e-13 * best:
+            best, arg, count = obj, b, 1
+        elif abs(obj - best) <= 1e-13 * best:
+            count += 1
+    return best, arg, count
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_greedy_rate_equals_brute_force(seed):
+    rng = np.random.default_rng(500 + seed)
+    n = int(rng.integers(2, 6)); bmax = int(rng.integers(2, 5))
+    U = int(rng.integers(1, min(12, n * bmax) + 1))
+    s = np.exp(rng.uniform(-6, 6, n))
+    rate = _lloyd_rate(bmax)
+    best, arg, count = _brute_rate(list(s), U, bmax, rate)
+    got = allocate.greedy_rate(s, U, rate, bmax)
+    assert got.sum() == U and got.max() <= bmax
+    assert allocate.objective_rate(s, got, rate) == pytest.approx(best, rel=1e-12)
+    if count == 1:
+        assert tuple(got) == arg
+
+
+def test_greedy_rate_with_4_pow_minus_b_matches_greedy():
+    """Under the idealized rate the gains are s_i 4^-b_i (3/4): the same ranking as greedy()."""
+    rate = [4.0 ** -b for b in range(9)]
+    for seed in range(20):
+        rng = np.random.default_rng(900 + seed)
+        s = np.exp(rng.uniform(-10, 10, 64))
+        np.testing.assert_array_equal(allocate.greedy_rate(s, 192, rate), allocate.greedy(s, 192))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_greedy_rate_beats_4_pow_minus_b_on_realized_distortion(seed):
+    """On its own objective the rate greedy is never worse than the 4^-b allocation, and on
+    heterogeneous heads the two allocations differ (the point of the option)."""
+    rng = np.random.default_rng(300 + seed)
+    s = np.exp(rng.uniform(-12, 12, 64))
+    rate = _lloyd_rate()
+    b_r = allocate.greedy_rate(s, 192, rate)
+    b_4 = allocate.greedy(s, 192)
+    assert allocate.objective_rate(s, b_r, rate) <= allocate.objective_rate(s, b_4, rate) * (1 + 1e-12)
+    gain_add = max(s[i] * (rate[b_r[i]] - rate[b_r[i] + 1]) for i in range(64) if b_r[i] < 8)
+    gain_rm = min(s[j] * (rate[b_r[j] - 1] - rate[b_r[j]]) for j in range(64) if b_r[j] > 0)
+    assert gain_add <= gain_rm
+    if seed == 0:
+        assert not np.array_equal(b_r, b_4)
+
+
+def test_greedy_rate_rejects_non_convex_rate():
+    with pytest.raises(ValueError):
+        allocate.greedy_rate([1.0, 2.0], 3, [1.0, 0.5, 0.4, 0.1], 3)   # steps 0.5, 0.1, 0.3
+    with pytest.raises(ValueError):
+        allocate.greedy_rate([1.0, 2.0], 3, [1.0, 0.5, 0.5, 0.4], 3)   # a flat step
