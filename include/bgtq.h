@@ -141,6 +141,20 @@ int bgtq_allocate(const double *scores, int n_heads, int n_blk, int budget_units
                   int b_min, int b_max, uint8_t *bits_out);
 
 /*
+ * The same greedy ranked by a tabulated distortion-rate curve instead of the idealized 4^-b
+ * (host, synchronous).  The review (§3) states the allocation with the TQ-MSE rate 4^-b; the
+ * library's own scalar tables reach D(b) (their exact N(0,1) mean squared error: D(0) = 1,
+ * D(1) = 1 - 2/pi, ...), whose ratios approach 4 only at wide codes.  With block distortion
+ * s_i * D(b_i), each step adds one bit to the block maximizing s_i * (D(b_i) - D(b_i + 1)) among
+ * blocks with b_i < b_max and s_i > 0 (ties: lowest index).  rate: host fp64 [b_max + 1], D(b)
+ * for b = 0..b_max, strictly decreasing with non-increasing steps (a convex curve, for which this
+ * greedy minimizes sum_i s_i D(b_i) exactly).  Other arguments and errors as bgtq_allocate, plus
+ * BGTQ_E_INVALID for a NULL, non-finite, non-decreasing or non-convex rate.
+ */
+int bgtq_allocate_rate(const double *scores, int n_heads, int n_blk, int budget_units,
+                       int b_min, int b_max, const double *rate, uint8_t *bits_out);
+
+/*
  * Calibration energy (device reduction, then a synchronous copy to the host).  Block-GTQ
  * (abstract; review §3) scores each RoPE block from calibration data per layer and KV head:
  * E_k[i] = mean_t ||k_t,(2i,2i+1)||^2, E_q[i] = mean over t and the g query heads of the group of

@@ -16,7 +16,7 @@ V_CODEBOOK, V_AFFINE = 0, 1
  BUF_RECENT_V, BUF_META) = range(9)
 MAX_BATCH = 64
 
-SYMBOLS = ["bgtq_last_error", "bgtq_version", "bgtq_codebook", "bgtq_allocate", "bgtq_block_energy",
+SYMBOLS = ["bgtq_last_error", "bgtq_version", "bgtq_codebook", "bgtq_allocate", "bgtq_allocate_rate", "bgtq_block_energy",
            "bgtq_cache_bytes", "bgtq_quantize_append", "bgtq_decode_workspace_bytes", "bgtq_decode_attention",
            "bgtq_fp16_decode_workspace_bytes", "bgtq_fp16_decode_attention", "bgtq_profile_enable",
            "bgtq_profile_read"]
@@ -50,6 +50,7 @@ def bind(path: str):
         "bgtq_version": (C.c_char_p, []),
         "bgtq_codebook": (I, [I, C.POINTER(C.c_uint16), F]),
         "bgtq_allocate": (I, [D, I, I, I, I, I, C.POINTER(C.c_uint8)]),
+        "bgtq_allocate_rate": (I, [D, I, I, I, I, I, D, C.POINTER(C.c_uint8)]),
         "bgtq_block_energy": (I, [P, P, I, I64, I, I, I, I, D, F, F, P, SZ, P]),
         "bgtq_cache_bytes": (I64, [C.POINTER(CacheDesc), I]),
         "bgtq_quantize_append": (I, [C.POINTER(CacheDesc), I, P, P, I, I64, C.POINTER(C.c_int64), P]),

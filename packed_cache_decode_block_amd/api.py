@@ -55,14 +55,22 @@ def bgtq_codebook(bits: int):
     return c.view(np.float16), t[: n - 1]
 
 
-def bgtq_allocate(scores, budget_units: int, b_min: int = 0, b_max: int = 8) -> np.ndarray:
-    """Greedy widths: scores [n_heads, n_blk] fp64 -> uint8 [n_heads, n_blk] (host)."""
+def bgtq_allocate(scores, budget_units: int, b_min: int = 0, b_max: int = 8, rate=None) -> np.ndarray:
+    """Greedy widths: scores [n_heads, n_blk] fp64 -> uint8 [n_heads, n_blk] (host).  rate: None
+    ranks gains by 4^-b; else D(b) for b = 0..b_max (bgtq_allocate_rate)."""
     s = np.ascontiguousarray(scores, dtype=np.float64)
     if s.ndim == 1:
         s = s[None]
     out = np.zeros(s.shape, np.uint8)
-    check(lib.bgtq_allocate(s.ctypes.data_as(C.POINTER(C.c_double)), s.shape[0], s.shape[1], budget_units, b_min,
-                            b_max, out.ctypes.data_as(C.POINTER(C.c_uint8))))
+    sp, op = s.ctypes.data_as(C.POINTER(C.c_double)), out.ctypes.data_as(C.POINTER(C.c_uint8))
+    if rate is None:
+        check(lib.bgtq_allocate(sp, s.shape[0], s.shape[1], budget_units, b_min, b_max, op))
+    else:
+        r = np.ascontiguousarray(rate, dtype=np.float64)
+        if r.ndim != 1 or r.shape[0] < b_max + 1:
+            raise ValueError("rate needs b_max + 1 entries")
+        check(lib.bgtq_allocate_rate(sp, s.shape[0], s.shape[1], budget_units, b_min, b_max,
+                                     r.ctypes.data_as(C.POINTER(C.c_double)), op))
     return out
 
 

@@ -210,15 +210,14 @@ int bgtq_codebook(int bits, uint16_t* centroids_f16, float* thresholds) {
     return ok();
 }
 
-int bgtq_allocate(const double* scores, int n_heads, int n_blk, int budget_units, int b_min, int b_max,
-                  uint8_t* bits_out) {
-    if (!scores || !bits_out) return fail(BGTQ_E_INVALID, "NULL pointer");
-    if (n_heads < 1 || n_blk < 1 || n_blk > 256) return fail(BGTQ_E_INVALID, "bad n_heads/n_blk");
-    if (b_max < 1 || b_max > 8 || b_min < 0 || b_min > b_max) return fail(BGTQ_E_INVALID, "bad b_min/b_max");
-    if (budget_units < 0) return fail(BGTQ_E_INVALID, "negative budget");
-    for (int64_t i = 0; i < (int64_t)n_heads * n_blk; ++i)
-        if (!(scores[i] >= 0.0) || !std::isfinite(scores[i]))
-            return fail(BGTQ_E_INVALID, "score %lld is negative or not finite", (long long)i);
+extern "C++" {
+namespace {
+// The greedy of both allocators: from b_min on every live block (positive score), repeatedly add
+// one bit to the live block below b_max with the largest key(score, width); ties go to the
+// lowest index.  Arguments are validated by the callers.
+template <typename Key>
+int greedy_widths(const double* scores, int n_heads, int n_blk, int budget_units, int b_min, int b_max,
+                  uint8_t* bits_out, Key key_of) {
     std::vector<uint8_t> out((size_t)n_heads * n_blk);
     for (int hd = 0; hd < n_heads; ++hd) {
         const double* s = scores + (size_t)hd * n_blk;
@@ -234,7 +233,7 @@ int bgtq_allocate(const double* scores, int n_heads, int n_blk, int budget_units
             double best_key = 0.0;
             for (int i = 0; i < n_blk; ++i) {
                 if (b[i] >= b_max || !(s[i] > 0.0)) continue;
-                const double key = std::ldexp(s[i], -2 * (int)b[i]);  // exact: s * 4^-b
+                const double key = key_of(s[i], (int)b[i]);
                 if (best < 0 || key > best_key) {
                     best = i;
                     best_key = key;
@@ -246,6 +245,45 @@ int bgtq_allocate(const double* scores, int n_heads, int n_blk, int budget_units
     }
     std::memcpy(bits_out, out.data(), out.size());
     return ok();
+}
+
+int check_allocate_args(const double* scores, int n_heads, int n_blk, int budget_units, int b_min, int b_max,
+                        const uint8_t* bits_out) {
+    if (!scores || !bits_out) return fail(BGTQ_E_INVALID, "NULL pointer");
+    if (n_heads < 1 || n_blk < 1 || n_blk > 256) return fail(BGTQ_E_INVALID, "bad n_heads/n_blk");
+    if (b_max < 1 || b_max > 8 || b_min < 0 || b_min > b_max) return fail(BGTQ_E_INVALID, "bad b_min/b_max");
+    if (budget_units < 0) return fail(BGTQ_E_INVALID, "negative budget");
+    for (int64_t i = 0; i < (int64_t)n_heads * n_blk; ++i)
+        if (!(scores[i] >= 0.0) || !std::isfinite(scores[i]))
+            return fail(BGTQ_E_INVALID, "score %lld is negative or not finite", (long long)i);
+    return 0;
+}
+}  // namespace
+}  // extern "C++"
+
+int bgtq_allocate(const double* scores, int n_heads, int n_blk, int budget_units, int b_min, int b_max,
+                  uint8_t* bits_out) {
+    if (int rc = check_allocate_args(scores, n_heads, n_blk, budget_units, b_min, b_max, bits_out)) return rc;
+    // s * 4^-b exactly
+    return greedy_widths(scores, n_heads, n_blk, budget_units, b_min, b_max, bits_out,
+                         [](double s, int b) { return std::ldexp(s, -2 * b); });
+}
+
+int bgtq_allocate_rate(const double* scores, int n_heads, int n_blk, int budget_units, int b_min, int b_max,
+                       const double* rate, uint8_t* bits_out) {
+    if (int rc = check_allocate_args(scores, n_heads, n_blk, budget_units, b_min, b_max, bits_out)) return rc;
+    if (!rate) return fail(BGTQ_E_INVALID, "NULL rate");
+    double gain[8];
+    for (int b = 0; b < b_max; ++b) {
+        if (!std::isfinite(rate[b]) || !std::isfinite(rate[b + 1])) return fail(BGTQ_E_INVALID, "rate not finite");
+        gain[b] = rate[b] - rate[b + 1];
+        if (!(gain[b] > 0.0)) return fail(BGTQ_E_INVALID, "rate does not decrease at width %d", b);
+        if (b > 0 && gain[b] > gain[b - 1])
+            return fail(BGTQ_E_INVALID, "rate steps grow at width %d (the curve must be convex)", b);
+    }
+    // marginal gain of one more bit: s * (D(b) - D(b + 1))
+    return greedy_widths(scores, n_heads, n_blk, budget_units, b_min, b_max, bits_out,
+                         [&gain](double s, int b) { return s * gain[b]; });
 }
 
 int bgtq_block_energy(const void* k_cal, const void* q_cal, int dtype, int64_t T_cal, int Hkv, int g, int d,

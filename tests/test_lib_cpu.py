@@ -51,6 +51,41 @@ def test_allocate_bit_exact_vs_oracle(seed):
         np.testing.assert_array_equal(got[h], oalloc.greedy(s[h], U, 8).astype(np.uint8))
 
 
+def _lloyd_rate():
+    return [1.0] + [ocb.codebook_mse(b) for b in range(1, 9)]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_allocate_rate_bit_exact_vs_oracle(seed):
+    rng = np.random.default_rng(700 + seed)
+    n_heads = int(rng.integers(1, 4))
+    s = np.exp(rng.uniform(-12, 12, (n_heads, 64)))
+    if seed % 3 == 0:
+        s[:, rng.integers(0, 64, 10)] = 0.0                      # dead blocks
+    if seed % 4 == 0:
+        s = np.round(s, 0) + 1.0                                 # ties
+    U = int(rng.choice([64, 128, 192, 256]))
+    b_min = 1 if seed % 5 == 0 else 0
+    rate = _lloyd_rate()
+    got = P.bgtq_allocate(s, U, b_min=b_min, rate=rate)
+    for h in range(n_heads):
+        np.testing.assert_array_equal(got[h], oalloc.greedy_rate(s[h], U, rate, 8, b_min).astype(np.uint8))
+
+
+def test_allocate_rate_errors():
+    s = np.array([[1.0, 2.0, 3.0]])
+    for bad in ([1.0, 0.5, 0.4, 0.1], [1.0, 0.5, 0.5, 0.4], [1.0, 0.5, np.nan, 0.1]):
+        with pytest.raises(P.BgtqError) as e:
+            P.bgtq_allocate(s, 3, b_max=3, rate=bad)
+        assert e.value.code == P.E_INVALID
+    with pytest.raises(P.BgtqError) as e:
+        P.bgtq_allocate(s, 10, b_max=3, rate=[1.0, 0.4, 0.1, 0.05])   # 3 blocks x 3 bits < 10
+    assert e.value.code == P.E_BUDGET
+    rc = P.lib.bgtq_allocate_rate(s.ctypes.data_as(C.POINTER(C.c_double)), 1, 3, 3, 0, 3, None,
+                                  np.zeros(3, np.uint8).ctypes.data_as(C.POINTER(C.c_uint8)))
+    assert rc == P.E_INVALID
+
+
 def test_allocate_b_min_and_errors():
     s = np.array([[1.0, 2.0, 0.0, 4.0]])
     got = P.bgtq_allocate(s, 9, b_min=2, b_max=4)
