@@ -217,7 +217,10 @@ def main():
         w = synth.reduced(w, L=args.layers)
     log(f"[bench] workload {w.wid}: {w.name}")
     t0 = time.perf_counter()
+    P.bgtq_profile_enable(4 * w.L)   # time the quantize-append launches of the cache build
     cache, qs = build_packed(w)
+    nq, totq, _, _ = P.bgtq_profile_read(P.PROF_QUANTIZE)
+    P.bgtq_profile_enable(0)
     log(f"[bench] packed cache built in {time.perf_counter() - t0:.1f}s")
     outs = [torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda") for _ in range(w.L)]
     ws = cache.workspace(args.n_splits)
@@ -275,6 +278,16 @@ def main():
                      "kernel": decode_kernel_name(w), "kernel_avg_us": round(kern_ms * 1e3, 3),
                      "bytes_per_launch": lb, "launches_timed": n_k},
     }
+    if nq:
+        # write path: every packed (token, kv head) reads its K and V rows and writes its record
+        es = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+        n_pk = w.N - min(w.N, w.n_recent)
+        qbytes = w.B * w.Hkv * n_pk * (2 * w.d * es + bytes_per_token_head(w))
+        q_ms = totq / nq
+        result["quantize_append"] = {"kernel": "k_quant", "launches": nq, "kernel_avg_us": round(q_ms * 1e3, 2),
+                                     "tokens_per_launch": w.B * w.Hkv * n_pk, "bytes_per_launch": qbytes,
+                                     "GB/s": round(qbytes / (q_ms * 1e-3) / 1e9, 1)}
+        log(f"[bench] quantize-append {q_ms * 1e3:.1f} us per layer -> {qbytes / (q_ms * 1e-3) / 1e9:.0f} GB/s")
     del ws
     if not args.no_fp16:
         del cache

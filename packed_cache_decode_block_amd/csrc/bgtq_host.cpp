@@ -416,6 +416,7 @@ int bgtq_quantize_append(bgtq_cache* c, int layer, const void* k, const void* v,
             q.tile0[b] = lo[b] / TILE;
             if (hi[b] > lo[b]) max_tiles = std::max(max_tiles, (hi[b] - 1) / TILE - lo[b] / TILE + 1);
         }
+        if (max_tiles == 0) return hipSuccess;  // nothing in range: no launch, and no profiler slot
         ProfScope ps(BGTQ_PROF_QUANTIZE, s);
         return bgtq::launch_quant(q, c->B, max_tiles, s);
     };

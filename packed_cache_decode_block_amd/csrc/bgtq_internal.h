@@ -105,6 +105,7 @@ struct QuantArgs {
     int k_mode, R, k_bits, k_group;
     int v_mode, v_bits;
     int which;                  // bit 0: keys, bit 1: values
+    int vec16;                  // set by the launcher: rows and strides allow 16-byte row loads
     int64_t tile0[BGTQ_MAXB];   // first tile touched per sequence
     int64_t pos_lo[BGTQ_MAXB], pos_hi[BGTQ_MAXB], off[BGTQ_MAXB];
 };

@@ -1797,7 +1797,20 @@ __device__ __forceinline__ uint32_t tq_code(float x, float t, int w, const float
     return code;
 }
 
-__device__ __forceinline__ float rms_scale16(const float* x /*LDS row, stride 1*/, const float* r /*per block or null*/,
+// One token's row in LDS, in the activation's own format (fp32, or the fp16 / bf16 bits, which
+// convert to fp32 exactly).
+template <typename XT> struct XRow {
+    const XT* p;
+    int dtype;
+    __device__ __forceinline__ float operator[](int j) const {
+        if constexpr (sizeof(XT) == 4) return p[j];
+        else return dtype == BGTQ_F16 ? h2f(p[j]) : bf2f(p[j]);
+    }
+    __device__ __forceinline__ XRow operator+(int j) const { return XRow{p + j, dtype}; }
+};
+
+template <typename X>
+__device__ __forceinline__ float rms_scale16(const X& x /*one token's row*/, const float* r /*per block or null*/,
                                              uint16_t* s16) {
 #pragma clang fp contract(off)
     float acc = 0.f;
@@ -1811,7 +1824,8 @@ __device__ __forceinline__ float rms_scale16(const float* x /*LDS row, stride 1*
     return h2f(h);
 }
 
-__device__ __forceinline__ void affine_group(const float* x, int n, int bits, uint16_t* sc16, uint16_t* z16,
+template <typename X>
+__device__ __forceinline__ void affine_group(const X& x, int n, int bits, uint16_t* sc16, uint16_t* z16,
                                              uint32_t* codes) {
 #pragma clang fp contract(off)
     float mn = x[0], mx = x[0];
@@ -1836,18 +1850,28 @@ __device__ __forceinline__ void affine_group(const float* x, int n, int bits, ui
     }
 }
 
+// One workgroup = one tile of 64 positions of one (b, h); lane = token for the per-token steps.
+// The tile's rows are first staged in LDS by the whole wave: with 16-byte aligned rows
+// (QuantArgs::vec16) each instruction moves whole 64-byte row segments, otherwise one element
+// per lane and instruction.  Rows are kept in the activation's format (XT = float for fp32,
+// uint16_t bits for fp16 / bf16), padded to an odd number of dwords so that the per-lane row
+// reads of the quantizer hit distinct banks.  Value codes overwrite their own row in place (code
+// j lands in bytes the row's elements 0..j already vacated).
+template <typename XT>
 __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
+    constexpr int XS = sizeof(XT) == 4 ? D + 1 : D + 2;  // row stride in elements (129 dwords / 65 dwords)
+    constexpr int EPC = 16 / sizeof(XT);                 // elements per 16-byte chunk
+    constexpr int CPR = D / EPC;                         // chunks per row
     const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
     const int64_t tile = a.tile0[b] + blockIdx.x;
     if (tile * TILE >= a.pos_hi[b]) return;  // whole workgroup beyond this sequence's range
     const int64_t pos = tile * TILE + lane;
     const bool active = pos >= a.pos_lo[b] && pos < a.pos_hi[b];
     __shared__ float s_thr[BGTQ_CB_THRESHOLDS];
-    __shared__ float s_x[64][D + 1];
+    __shared__ __attribute__((aligned(16))) XT s_x[64 * XS];
     __shared__ int s_order[64];
     __shared__ int s_wid[64];
     __shared__ float s_r[64], s_sig[64];
-    __shared__ uint8_t s_code[64][D];
     for (int i = lane; i < BGTQ_CB_THRESHOLDS; i += 64) s_thr[i] = __builtin_bit_cast(float, c_thr32[i]);
     const size_t bh = (size_t)b * a.Hkv + h;
     const bool do_k = a.which & 1, do_v = (a.which >> 1) & 1;
@@ -1867,18 +1891,45 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
         if (w > 0) s_order[rank] = lane;
     }
     __syncthreads();
-    int64_t row = 0;
-    if (active) {
-        row = pos - a.off[b];
-        if (a.mod_n) row %= a.mod_n;
-    }
-    const int64_t base = (int64_t)b * a.sB + row * a.sT + (int64_t)h * a.sH;
+    // source element offset of the row of tile position u (inactive positions read nothing)
+    auto row_base = [&](int u, bool& act) -> int64_t {
+        const int64_t p = tile * TILE + u;
+        act = p >= a.pos_lo[b] && p < a.pos_hi[b];
+        int64_t row = 0;
+        if (act) {
+            row = p - a.off[b];
+            if (a.mod_n) row %= a.mod_n;
+        }
+        return (int64_t)b * a.sB + row * a.sT + (int64_t)h * a.sH;
+    };
     for (int pass = 0; pass < 2; ++pass) {
         if ((pass == 0 && !do_k) || (pass == 1 && !do_v)) continue;
         const void* src = pass == 0 ? a.src_k : a.src_v;
-        const int64_t off = base;
-        float* x = s_x[lane];
-        for (int j = 0; j < D; ++j) x[j] = active ? load_act(src, off + j, a.dtype) : 0.f;
+        __syncthreads();  // the previous pass is done with the rows
+        if (a.vec16) {
+            // 16-byte chunks: instruction k covers rows (64 / CPR) * k + lane / CPR
+#pragma unroll 4
+            for (int k = 0; k < CPR; ++k) {
+                const int u = (64 / CPR) * k + lane / CPR, c = lane % CPR;
+                bool act;
+                const int64_t off = row_base(u, act);
+                u32x4_t v = {0u, 0u, 0u, 0u};
+                if (act) v = *(const u32x4_t*)((const XT*)src + off + EPC * c);
+                uint32_t* dst = (uint32_t*)(s_x + u * XS + EPC * c);
+                dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+            }
+        } else {
+            // one element per lane: instruction j covers element j of every row
+            bool act;
+            const int64_t off = row_base(lane, act);
+            for (int j = 0; j < D; ++j) {
+                XT v = 0;
+                if (act) v = ((const XT*)src)[off + j];
+                s_x[lane * XS + j] = v;
+            }
+        }
+        __syncthreads();
+        const XRow<XT> x{s_x + lane * XS, a.dtype};
         if (pass == 0) {
             // ---- keys
             uint32_t* kt = (uint32_t*)(a.k_codes + (bh * a.n_tiles + tile) * a.k_tile_bytes);
@@ -1925,16 +1976,19 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
                 }
             }
         } else {
-            // ---- values: lane-stream layout.  Codes of the 64 tokens go through LDS; thread L then
-            // assembles stream L (4*vb dwords).  Bits of tokens before pos_lo are kept (read-modify-
-            // write); tokens at or past pos_hi get zero codes (never written before, appends are
-            // in order).
+            // ---- values: lane-stream layout.  Codes of the 64 tokens go through LDS (over their own
+            // rows); thread L then assembles stream L (4*vb dwords).  Bits of tokens before pos_lo
+            // are kept (read-modify-write); tokens at or past pos_hi get zero codes (never written
+            // before, appends are in order).
             const int vb = a.v_bits;
             uint16_t s16 = 0, z16 = 0;
-            uint8_t* cr = s_code[lane];
+            uint8_t* cr = (uint8_t*)(s_x + lane * XS);
             if (a.v_mode == BGTQ_V_CODEBOOK) {
                 const float S = rms_scale16(x, nullptr, &s16);
-                for (int j = 0; j < D; ++j) cr[j] = active ? (uint8_t)tq_code(x[j], S, vb, s_thr) : (uint8_t)0;
+                for (int j = 0; j < D; ++j) {
+                    const uint8_t cj = active ? (uint8_t)tq_code(x[j], S, vb, s_thr) : (uint8_t)0;
+                    cr[j] = cj;  // byte j lies in elements 0..j of this row, already read
+                }
             } else {
                 uint32_t codes[D];
                 affine_group(x, D, vb, &s16, &z16, codes);
@@ -1945,6 +1999,7 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
                 if (a.v_mode == BGTQ_V_AFFINE) a.v_zero[bh * a.n_cap + pos] = z16;
             }
             __syncthreads();
+            auto code_at = [&](int p, int dim) -> uint32_t { return ((const uint8_t*)(s_x + p * XS))[dim]; };
             const int64_t t0 = tile * TILE;
             const int lo = a.pos_lo[b] > t0 ? (int)(a.pos_lo[b] - t0) : 0;
             const int dd = lane & 15, jj = lane >> 4;
@@ -1956,7 +2011,7 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
                 for (int phi = phi0; phi <= phi1 && phi < 64; ++phi) {
                     const int m = phi & 3, db = (phi >> 2) & 7, sh = phi >> 5;
                     const int p = 16 * sh + 4 * jj + m, dim = 16 * db + dd;
-                    const uint64_t f = (uint64_t)(s_code[p][dim] | ((uint32_t)s_code[p + 32][dim] << vb));
+                    const uint64_t f = (uint64_t)(code_at(p, dim) | (code_at(p + 32, dim) << vb));
                     const uint64_t fm = (uint64_t)((p >= lo ? cm : 0u) | (p + 32 >= lo ? cm << vb : 0u));
                     const int bit = 2 * vb * phi - 32 * c;   // field position relative to dword c
                     if (bit >= 0) {
@@ -2022,7 +2077,12 @@ hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_
     if (max_tiles <= 0) return hipSuccess;
     if ((a.which & 1) && a.k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma || !a.inv_sigma))
         return hipErrorInvalidValue;
-    return launch_main(k_quant, dim3((unsigned)max_tiles, a.Hkv, B), dim3(64), s, a);
+    QuantArgs q = a;
+    const int es = a.dtype == BGTQ_F32 ? 4 : 2;
+    q.vec16 = ((uintptr_t)a.src_k % 16 == 0) && ((uintptr_t)a.src_v % 16 == 0) && (a.sB * es) % 16 == 0 &&
+              (a.sT * es) % 16 == 0 && (a.sH * es) % 16 == 0;
+    if (a.dtype == BGTQ_F32) return launch_main(k_quant<float>, dim3((unsigned)max_tiles, a.Hkv, B), dim3(64), s, q);
+    return launch_main(k_quant<uint16_t>, dim3((unsigned)max_tiles, a.Hkv, B), dim3(64), s, q);
 }
 
 hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t s) {
