@@ -1475,25 +1475,27 @@ __global__ __launch_bounds__(256, 2) void k_decode_fp16_mx(const Fp16Args a) {
     // Tile loads: kk[g][ks] is the B operand of token group g, k-step ks; vv[k] is the 16 bytes at
     // tile offset 1024 k + 16 lane (token 4k + lane / 16, dims 8 (lane % 16) ..).
     u32x4_t kk[4][4], vv[16];
-    auto fetch_k = [&](int64_t t) {
+    // idle = true (a wave's prefetch past its last tile): every lane reads row 0, one cached row,
+    // instead of a whole tile; the loads stay unconditional so that no branch joins the wait counts.
+    auto fetch_k = [&](int64_t t, bool idle) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const int64_t tok = t * TILE + 16 * g + col;
+            const int64_t tok = idle ? 0 : t * TILE + 16 * g + col;
             const u32x4_t* r = (const u32x4_t*)(K16 + (tok < last ? tok : last) * D);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) kk[g][ks] = r[4 * ks + row];
         }
     };
-    auto fetch_v = [&](int64_t t) {
+    auto fetch_v = [&](int64_t t, bool idle) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-            const int64_t tok = t * TILE + 4 * k + row;
+            const int64_t tok = idle ? 0 : t * TILE + 4 * k + row;
             vv[k] = ((const u32x4_t*)(V16 + (tok < last ? tok : last) * D))[col];
         }
     };
     const int64_t t_first = t_lo + wave < t_hi ? t_lo + wave : (t_lo < n_tiles ? t_lo : 0);
-    fetch_k(t_first);
-    fetch_v(t_first);
+    fetch_k(t_first, false);
+    fetch_v(t_first, false);
 
     // Query operands (lane = A row col, lane row u = row): dims 32 ks + 8 row .. of head qh.
     u32x4_t qa[4];
@@ -1582,10 +1584,10 @@ __global__ __launch_bounds__(256, 2) void k_decode_fp16_mx(const Fp16Args a) {
             for (int ks = 1; ks < 4; ++ks)
                 c[g] = mfma16(__builtin_bit_cast(half8_t, qa[ks]), __builtin_bit_cast(half8_t, kk[g][ks]), c[g]);
         }
-        // the keys of this tile are consumed: the next tile's go out (a wave's last tile requests
-        // itself again, so that no branch joins the wait counts)
-        const int64_t tn = t + 4 < t_hi ? t + 4 : t;
-        fetch_k(tn);
+        // the keys of this tile are consumed: the next tile's go out
+        const bool last_tile = t + 4 >= t_hi;
+        const int64_t tn = last_tile ? t : t + 4;
+        fetch_k(tn, last_tile);
         // first value half to LDS; the second stays in registers until the first is consumed
         wave_lds_fence();
         stage_half(0);
@@ -1647,7 +1649,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_fp16_mx(const Fp16Args a) {
         wave_lds_fence();
         stage_half(1);
         wave_lds_fence();
-        fetch_v(tn);  // the values of this tile are all staged
+        fetch_v(tn, last_tile);  // the values of this tile are all staged
         pv_half(1);
     }
 
