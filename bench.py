@@ -55,13 +55,13 @@ def decode_kernel_name(w) -> str:
     return "k_decode_mx" if (w.k_mode == "gtq" and w.Hq // w.Hkv >= 4) else "k_decode"
 
 
-def measured_traffic(wid: int):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary of this workload
-    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None when there is none or
-    the kernel source has changed since the counters were taken."""
+def measured_traffic(wid: int, kernel: str = "k_decode_mx"):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary of this
+    workload (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None when there is
+    none or the kernel source has changed since the counters were taken."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", {2: "k_decode_mx_qwen2.5-3b_128k_hbm_counters.md"}.get(wid, "-"))
+    path = os.path.join(ROOT, "profiles", {2: f"{kernel}_qwen2.5-3b_128k_hbm_counters.md"}.get(wid, "-"))
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -74,7 +74,7 @@ def measured_traffic(wid: int):
     return int(t.group(1))
 
 
-def build_packed(w, device="cuda"):
+def build_packed(w, device="cuda", uniform_keys=False):
     import torch
 
     import packed_cache_decode_block_amd as P
@@ -97,6 +97,8 @@ def build_packed(w, device="cuda"):
                 np.concatenate([np.transpose(c[1], (1, 0, 2)) for c in cal], axis=1))).to(device).to(td)
             scores, sigma, inv_sigma = P.bgtq_block_energy(kc, qc)
             bits = P.bgtq_allocate(scores, w.k_budget_units)
+            if uniform_keys:  # uniform TQ-MSE keys: every block at the average width
+                bits = np.full_like(bits, w.k_budget_units // 64)
             cache.set_metadata(layer, bits, sigma, inv_sigma)
         for b in range(w.B):
             k = torch.stack([sg.keys(w, layer, h, b, w.N, device) for h in range(w.Hkv)], dim=1)[None]
@@ -188,6 +190,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--uniform-keys", action="store_true",
+                    help="Block-GTQ keys with every block at the average width (the uniform comparator)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -218,7 +222,7 @@ def main():
     log(f"[bench] workload {w.wid}: {w.name}")
     t0 = time.perf_counter()
     P.bgtq_profile_enable(4 * w.L)   # time the quantize-append launches of the cache build
-    cache, qs = build_packed(w)
+    cache, qs = build_packed(w, uniform_keys=args.uniform_keys)
     nq, totq, _, _ = P.bgtq_profile_read(P.PROF_QUANTIZE)
     P.bgtq_profile_enable(0)
     log(f"[bench] packed cache built in {time.perf_counter() - t0:.1f}s")
@@ -269,6 +273,7 @@ def main():
                    "kv_heads": w.Hkv, "head_dim": w.d, "k_format": "blockgtq" if w.k_mode == "gtq" else "affine",
                    "k_bits_per_dim": (w.k_budget_units / 64) if w.k_mode == "gtq" else w.k_bits,
                    "v_bits": w.v_bits, "n_recent_fp16": w.n_recent, "activations": w.dtype,
+                   "key_widths": "uniform" if args.uniform_keys else "greedy",
                    "n_splits": args.n_splits or "auto"},
         "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "launch": "hipgraph" if graph_ok else "eager", "ms_per_step_eager": round(sec_eager * 1e3, 4),
@@ -309,6 +314,8 @@ def main():
         result["fp16_baseline"] = {
             "ms_per_step": round(sec16 * 1e3, 4), "value": round(w.L * b16 / sec16 / 1e9, 2), "unit": "GB/s",
             "kernel_avg_us": round(tot16 / max(n16, 1) * 1e3, 3),
+            "kernel": "k_decode_fp16_mx" if w.Hq // w.Hkv >= 4 else "k_decode_fp16",
+            "traffic": measured_traffic(w.wid, "k_decode_fp16_mx") if w.Hq // w.Hkv >= 4 else None,
             "speedup_packed_vs_fp16": round(sec16 / sec, 3)}
         log(f"[bench] fp16 comparator step {sec16 * 1e3:.3f} ms, speedup {sec16 / sec:.2f}x")
         del ks, vs
