@@ -70,3 +70,16 @@ def merge(parts):
 def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     m, l, o = partial(q, K, V)
     return o / l[:, None]
+
+
+def hadamard_matrix(d: int = 128) -> np.ndarray:
+    """Sylvester Hadamard matrix: H[i, j] = (-1)^popcount(i & j)."""
+    i = np.arange(d)
+    par = np.array([[bin(a & b).count("1") & 1 for b in i] for a in i])
+    return np.where(par == 0, 1.0, -1.0)
+
+
+def unrotate_keys(k_rot: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """Inverse of the key rotation y = H (s * x) / 16 in float64: x = s * (H y) / 8 (H H = 128 I)."""
+    H = hadamard_matrix(k_rot.shape[-1])
+    return np.asarray(signs, np.float64) * (np.asarray(k_rot, np.float64) @ H.T) / 8.0

@@ -59,12 +59,17 @@ class LayerCache:
     k_bits: int
     k_group: int
     meta: LayerMeta | None
+    k_rot: np.ndarray | None = None   # +-1 [Hkv, d]: affine keys stored rotated (y = H (s * k) / 16)
 
 
 def build_layer(k_rows, v_rows, *, k_mode: str, v_mode: str, v_bits: int, n_cap: int,
                 meta: LayerMeta | None = None, k_bits: int = 4, k_group: int = 32,
-                n_recent: int = 0) -> LayerCache:
-    """k_rows, v_rows: float32 [B, Hkv, N, d] (dtype-exact values), all N tokens appended."""
+                n_recent: int = 0, k_rot=None) -> LayerCache:
+    """k_rows, v_rows: float32 [B, Hkv, N, d] (dtype-exact values), all N tokens appended.
+    k_rot: optional +-1 signs [Hkv, d]; affine keys are then rotated before quantization (the
+    fp16 recent buffer keeps the rows as they came)."""
+    if k_rot is not None and k_mode != "affine":
+        raise ValueError("the key rotation applies to affine keys")
     k_rows = np.asarray(k_rows, np.float32)
     v_rows = np.asarray(v_rows, np.float32)
     B, H, N, d = k_rows.shape
@@ -96,6 +101,8 @@ def build_layer(k_rows, v_rows, *, k_mode: str, v_mode: str, v_bits: int, n_cap:
                 words = layout.k_gtq_words(codes, meta.bits[h])
                 k_scale[b, h, :n_packed] = S
             else:
+                if k_rot is not None:
+                    xk = quantize.hadamard_rotate_f32(xk, k_rot[h])
                 codes, sc, zr = quantize.quantize_affine(xk, k_bits, k_group)
                 words = layout.k_affine_words(codes, k_bits)
                 k_scale[b, h, :n_packed] = sc
@@ -113,7 +120,8 @@ def build_layer(k_rows, v_rows, *, k_mode: str, v_mode: str, v_bits: int, n_cap:
                 recent_k[b, h, pos % n_recent] = k_rows[b, h, pos].astype(np.float16)
                 recent_v[b, h, pos % n_recent] = v_rows[b, h, pos].astype(np.float16)
     return LayerCache(k_mode, v_mode, n_packed, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero,
-                      recent_k, recent_v, n_rec, v_bits, k_bits, k_group, meta)
+                      recent_k, recent_v, n_rec, v_bits, k_bits, k_group, meta,
+                      None if k_rot is None else np.asarray(k_rot, np.float64))
 
 
 def dequant_head(c: LayerCache, b: int, h: int):
@@ -129,6 +137,8 @@ def dequant_head(c: LayerCache, b: int, h: int):
         R = c.k_bits * 128 // 32
         codes = layout.k_affine_codes(layout.untile_records(c.k_codes[b, h], n, R), c.k_bits)
         K = attention.dequant_affine(codes, c.k_scale[b, h, :n], c.k_zero[b, h, :n], c.k_group)
+        if c.k_rot is not None:
+            K = attention.unrotate_keys(K, c.k_rot[h])   # back to the original key space, exactly
     vc = layout.v_codes(c.v_codes[b, h], c.v_bits, n)
     if c.v_mode == "codebook":
         V = attention.dequant_codebook(vc, c.v_scale[b, h, :n], c.v_bits)

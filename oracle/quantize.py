@@ -108,3 +108,28 @@ def quantize_affine(x: np.ndarray, b: int, group: int):
     code = np.clip(np.rint(q), 0, 2 ** b - 1)
     code = np.where(s32 == 0, 0, code)
     return code.reshape(n, d).astype(np.int64), scale16, zero16
+
+
+def hadamard_rotate_f32(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """Key rotation before affine quantization: y = H (s * x) / 16 in float32.
+
+    The "Quantize What Counts" summary (Results, rotation integration) reports that rotating the
+    keys alone, in the K4V2 setting, brings accuracy close to K4V4 (rotation spreads key outlier
+    channels over a group), while rotating values alone helps little; it names no rotation.
+    Reading: a randomized Hadamard rotation, H the 128x128 Sylvester Hadamard matrix, s a
+    caller-given +-1 sign per coordinate.  H (s * x) is computed by the fast transform with stages
+    h = 1, 2, 4, ..., 64 in that order; at stage h each pair (j, j + h) with bit h of j clear
+    becomes (a + b, a - b), one float32 addition or subtraction each; the final 1/16 is exact.
+    """
+    y = np.asarray(x, F32) * np.asarray(signs, F32)
+    d = y.shape[-1]
+    h = 1
+    while h < d:
+        y = y.copy()
+        for i0 in range(0, d, 2 * h):
+            a = y[..., i0:i0 + h].copy()
+            b = y[..., i0 + h:i0 + 2 * h].copy()
+            y[..., i0:i0 + h] = a + b
+            y[..., i0 + h:i0 + 2 * h] = a - b
+        h *= 2
+    return (y * F32(1.0 / 16.0)).astype(F32)

@@ -133,6 +133,12 @@ class PackedCache:
     def set_metadata(self, layer: int, bits, sigma, inv_sigma):
         """Upload per-(kv head, block) widths and key scales of one layer (host arrays [Hkv, 64])."""
         torch = _torch()
+        b = np.asarray(bits)
+        d = self.desc
+        if b.shape != (d.Hkv, 64) or b.min() < 0 or b.max() > 8:
+            raise ValueError("bits must be [Hkv, 64] widths in 0..8")
+        if d.k_mode == _lib.K_BLOCKGTQ and np.any(b.sum(axis=1) != d.budget_units):
+            raise ValueError(f"the widths of every kv head must sum to budget_units ({d.budget_units})")
         self.bits[layer].copy_(torch.from_numpy(np.ascontiguousarray(bits, np.uint8)))
         self.sigma[layer].copy_(torch.from_numpy(np.ascontiguousarray(sigma, np.float32)))
         self.inv_sigma[layer].copy_(torch.from_numpy(np.ascontiguousarray(inv_sigma, np.float32)))

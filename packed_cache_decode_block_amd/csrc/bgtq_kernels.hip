@@ -1952,7 +1952,8 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
                     buf |= (uint64_t)(ca | (cb << w)) << nb;
                     nb += 2 * w;
                     if (nb >= 32) {
-                        if (active) kt[k * TILE + lane] = (uint32_t)buf;
+                        // widths summing past the budget (invalid metadata) never write past the record
+                        if (active && k < a.R) kt[k * TILE + lane] = (uint32_t)buf;
                         buf >>= 32;
                         nb -= 32;
                         ++k;

@@ -184,6 +184,31 @@ def test_errors_on_device_paths():
     assert cache.n_tokens[0, 0] == 0
 
 
+def test_metadata_widths_validated_and_bounded():
+    """set_metadata rejects widths that do not sum to the budget; widths written to the device
+    buffer directly (bypassing the binding) never make the quantizer write past a token's record:
+    the later tiles of a three-tile cache stay untouched while the first is appended.  (Three
+    tiles hold 8 KB per (b, h), so even an unbounded write of 32-dword records would stay inside
+    the buffer.)"""
+    w = synth.reduced(synth.WORKLOADS[2], L=1)
+    cache = T.gpu_cache(w, 192)
+    m = T.meta(w, 0)
+    bad = m.bits.copy()
+    bad[0, int(np.argmax(bad[0] < 8))] += 1                      # one bit over the budget
+    with pytest.raises(ValueError):
+        cache.set_metadata(0, bad, m.sigma, m.r)
+    with pytest.raises(ValueError):
+        cache.set_metadata(0, np.full_like(m.bits, 9), m.sigma, m.r)
+    cache.set_metadata(0, m.bits, m.sigma, m.r)
+    over = np.full((w.Hkv, 64), 8, np.uint8)                      # 1024 bits: far past the 384-bit record
+    cache.bits[0].copy_(torch.from_numpy(over))
+    K, V, _ = T.inputs(w, 0, 64)
+    T.append_all(cache, 0, K, V, w.dtype)
+    kc = T.layer_view(cache.k_codes, 1, 0, (w.B, w.Hkv, 3, -1)).cpu().numpy()
+    assert np.all(kc[:, :, 1:] == 0), "the quantizer wrote past the first tile"
+    assert np.any(kc[:, :, 0] != 0)
+
+
 FP16_CASES = {
     # name: (workload id, overrides, N, n_splits); 4 and 8 query heads per kv head take the
     # matrix-core kernel, 1 and 2 the vector one

@@ -134,3 +134,86 @@ def test_affine_pipeline_matches_direct():
         ref = _softmax_attention(q[0, 4 * h:4 * h + 4].astype(np.float64),
                                  attention.dequant_affine(kc, ks, kz, 32), attention.dequant_affine(vc, vs, vz, 128))
         np.testing.assert_allclose(o[0, 4 * h:4 * h + 4], ref, rtol=1e-12, atol=1e-12)
+
+
+# --- key rotation (affine keys) ---
+
+def _signs(seed, d=128):
+    return np.where(np.random.default_rng(seed).random(d) < 0.5, -1.0, 1.0)
+
+
+def test_hadamard_matrix_and_fast_transform():
+    """The fast transform's stages compute the Sylvester matrix: exact on integer inputs (no
+    rounding), H H = 128 I, and the fp32 transform stays within its rounding bound."""
+    from oracle import quantize
+    H = attention.hadamard_matrix(128)
+    np.testing.assert_array_equal(H @ H, 128 * np.eye(128))
+    assert np.all(np.abs(H) == 1) and np.all(H[0] == 1) and np.all(H[:, 0] == 1)
+    rng = np.random.default_rng(3)
+    s = _signs(4)
+    xi = rng.integers(-100, 100, (5, 128)).astype(np.float32)        # exact in fp32 throughout
+    np.testing.assert_array_equal(quantize.hadamard_rotate_f32(xi, s), (xi * s) @ H.T / 16)
+    x = rng.standard_normal((50, 128)).astype(np.float32)
+    y = quantize.hadamard_rotate_f32(x, s).astype(np.float64)
+    exact = (x.astype(np.float64) * s) @ H.T / 16
+    bound = 7 * 2.0 ** -24 * (np.abs(x).astype(np.float64) @ np.abs(H).T) / 16
+    assert np.all(np.abs(y - exact) <= bound)
+
+
+def test_key_rotation_round_trip_and_logit_invariance():
+    from oracle import quantize
+    rng = np.random.default_rng(5)
+    s = _signs(6)
+    k = rng.standard_normal((20, 128))
+    y = (k * s) @ attention.hadamard_matrix().T / 16                 # fp64 rotation
+    np.testing.assert_allclose(attention.unrotate_keys(y, s), k, atol=1e-12)
+    q = rng.standard_normal(128)
+    qr = attention.hadamard_matrix() @ (q * s) / 8                   # the decode's query rotation
+    np.testing.assert_allclose(y @ qr, k @ q, rtol=1e-12, atol=1e-12)
+    yf = quantize.hadamard_rotate_f32(k.astype(np.float32), s)
+    np.testing.assert_allclose(attention.unrotate_keys(yf, s), k.astype(np.float32), atol=1e-5)
+
+
+def test_key_rotation_spreads_outlier_channels():
+    """Soft check of the direction the summary reports: keys with a few large channels quantize
+    with a lower error under 4-bit, group-32 affine groups once rotated (measured in the original
+    key space after the exact inverse)."""
+    from oracle import quantize
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal((2000, 128)).astype(np.float32)
+    k[:, [5, 77]] *= 20.0
+    s = _signs(12)
+    c0, s0, z0 = quantize.quantize_affine(k, 4, 32)
+    e0 = np.mean((attention.dequant_affine(c0, s0, z0, 32) - k) ** 2)
+    y = quantize.hadamard_rotate_f32(k, s)
+    c1, s1, z1 = quantize.quantize_affine(y, 4, 32)
+    e1 = np.mean((attention.unrotate_keys(attention.dequant_affine(c1, s1, z1, 32), s) - k) ** 2)
+    assert e1 < 0.5 * e0
+
+
+def test_rotated_affine_pipeline_matches_direct():
+    """A rotated affine layer decodes to the same output as attention over its keys dequantized
+    and rotated back by hand; ring tokens stay unrotated."""
+    import synth
+    from oracle import pipeline
+    w = synth.reduced(synth.WORKLOADS[4], L=1, B=1, Hkv=2, Hq=8)
+    N = 300
+    K = np.stack([synth.keys(w, 0, h, 0, N) for h in range(2)])[None]
+    V = np.stack([synth.values(w, 0, h, 0, N) for h in range(2)])[None]
+    q = np.concatenate([synth.queries(w, 0, h, 0, N) for h in range(2)])[None]
+    rot = np.stack([_signs(20 + h) for h in range(2)])
+    oc = pipeline.build_layer(K, V, k_mode="affine", v_mode=w.v_mode, v_bits=w.v_bits, n_cap=320, k_bits=4,
+                              k_group=32, n_recent=40, k_rot=rot)
+    out = pipeline.decode_layer(oc, q)
+    from oracle import layout, quantize
+    for h in range(2):
+        n = oc.n_packed
+        codes = layout.k_affine_codes(layout.untile_records(oc.k_codes[0, h], n, 16), 4)
+        Kr = attention.dequant_affine(codes, oc.k_scale[0, h, :n], oc.k_zero[0, h, :n], 32)
+        y = quantize.hadamard_rotate_f32(K[0, h, :n], rot[h])
+        c2, s2, z2 = quantize.quantize_affine(y, 4, 32)
+        np.testing.assert_array_equal(codes, c2)
+        Kx = np.concatenate([attention.unrotate_keys(Kr, rot[h]), oc.recent_k[0, h, :oc.n_recent_valid]])
+        Vx = pipeline.dequant_head(oc, 0, h)[1]
+        ref = attention.attend(q[0, 4 * h:4 * (h + 1)].astype(np.float64), Kx, Vx)
+        np.testing.assert_allclose(out[0, 4 * h:4 * (h + 1)], ref, rtol=1e-12, atol=1e-12)
