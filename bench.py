@@ -74,7 +74,7 @@ def measured_traffic(wid: int, kernel: str = "k_decode_mx"):
     return int(t.group(1))
 
 
-def build_packed(w, device="cuda", uniform_keys=False):
+def build_packed(w, device="cuda", uniform_keys=False, k_rotation=False):
     import torch
 
     import packed_cache_decode_block_amd as P
@@ -86,10 +86,13 @@ def build_packed(w, device="cuda", uniform_keys=False):
                           k_mode=P.K_BLOCKGTQ if w.k_mode == "gtq" else P.K_AFFINE,
                           budget_units=w.k_budget_units or 128, k_bits=w.k_bits or 4, k_group=w.k_group or 32,
                           v_mode=P.V_CODEBOOK if w.v_mode == "codebook" else P.V_AFFINE, v_bits=w.v_bits,
-                          n_recent=w.n_recent, zero=False)
+                          n_recent=w.n_recent, k_rotation=k_rotation, zero=False)
     td = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     qs = []
     for layer in range(w.L):
+        if k_rotation:  # seeded +-1 signs of the key rotation, per (layer, kv head)
+            rs = np.random.default_rng([w.wid, layer, 7]).random((w.Hkv, 128))
+            cache.set_key_rotation(layer, np.where(rs < 0.5, -1.0, 1.0))
         if w.k_mode == "gtq":
             cal = [synth.calibration(w, layer, h) for h in range(w.Hkv)]
             kc = torch.from_numpy(np.ascontiguousarray(np.stack([c[0] for c in cal], axis=1))).to(device).to(td)
@@ -190,6 +193,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--k-rotation", action="store_true",
+                    help="affine keys stored under the randomized Hadamard rotation (affine-key workloads)")
     ap.add_argument("--uniform-keys", action="store_true",
                     help="Block-GTQ keys with every block at the average width (the uniform comparator)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
@@ -222,7 +227,10 @@ def main():
     log(f"[bench] workload {w.wid}: {w.name}")
     t0 = time.perf_counter()
     P.bgtq_profile_enable(4 * w.L)   # time the quantize-append launches of the cache build
-    cache, qs = build_packed(w, uniform_keys=args.uniform_keys)
+    if args.k_rotation and w.k_mode != "affine":
+        print("--k-rotation applies to affine-key workloads (4)", file=sys.stderr)
+        sys.exit(2)
+    cache, qs = build_packed(w, uniform_keys=args.uniform_keys, k_rotation=args.k_rotation)
     nq, totq, _, _ = P.bgtq_profile_read(P.PROF_QUANTIZE)
     P.bgtq_profile_enable(0)
     log(f"[bench] packed cache built in {time.perf_counter() - t0:.1f}s")
@@ -273,7 +281,7 @@ def main():
                    "kv_heads": w.Hkv, "head_dim": w.d, "k_format": "blockgtq" if w.k_mode == "gtq" else "affine",
                    "k_bits_per_dim": (w.k_budget_units / 64) if w.k_mode == "gtq" else w.k_bits,
                    "v_bits": w.v_bits, "n_recent_fp16": w.n_recent, "activations": w.dtype,
-                   "key_widths": "uniform" if args.uniform_keys else "greedy",
+                   "key_widths": "uniform" if args.uniform_keys else "greedy", "key_rotation": args.k_rotation,
                    "n_splits": args.n_splits or "auto"},
         "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "launch": "hipgraph" if graph_ok else "eager", "ms_per_step_eager": round(sec_eager * 1e3, 4),

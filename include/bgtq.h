@@ -86,6 +86,13 @@ enum {
  *   bits      uint8 [L][Hkv][64]   widths (BLOCKGTQ), from bgtq_allocate
  *   sigma     fp32  [L][Hkv][64]   per-block key scale sigma_i = sqrt(E_k[i]/2)
  *   inv_sigma fp32  [L][Hkv][64]   fp32(1/sigma_i), 0 for a dead block
+ *   k_rot     uint8 [L][Hkv][16] or NULL: affine keys only.  Sign bits s_j (bit j % 8 of byte
+ *     j / 8 set means s_j = -1) of a randomized Hadamard key rotation ("Quantize What Counts"
+ *     summary, Results: rotating the keys alone recovers most of K4V4's accuracy at K4V2): each
+ *     appended key row is stored as y = H (s * k) / 16 (H the 128x128 Sylvester Hadamard
+ *     matrix, fast transform in stages 1, 2, ..., 64, fp32), and decode rotates the query to
+ *     H (s * q) / 8 so that the logits are unchanged; the fp16 recent ring keeps rows unrotated.
+ *     NULL disables it.  With Block-GTQ keys it is BGTQ_E_UNSUPPORTED.
  * Host state:
  *   n_tokens  int64 [L][B] host array: tokens appended so far per (layer, sequence) (packed +
  *     recent).  bgtq_quantize_append advances it on success only.
@@ -111,6 +118,7 @@ typedef struct bgtq_cache {
     const uint8_t *bits;
     const float *sigma, *inv_sigma;
     int64_t *n_tokens;
+    const uint8_t *k_rot;
 } bgtq_cache;
 
 /* Thread-local text describing the last non-OK status of this thread ("" if none). */

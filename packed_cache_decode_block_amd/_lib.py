@@ -37,7 +37,7 @@ class CacheDesc(C.Structure):
                 ("k_codes", C.c_void_p), ("v_codes", C.c_void_p), ("k_scale", C.c_void_p), ("k_zero", C.c_void_p),
                 ("v_scale", C.c_void_p), ("v_zero", C.c_void_p), ("recent_k", C.c_void_p), ("recent_v", C.c_void_p),
                 ("bits", C.c_void_p), ("sigma", C.c_void_p), ("inv_sigma", C.c_void_p),
-                ("n_tokens", C.POINTER(C.c_int64))]
+                ("n_tokens", C.POINTER(C.c_int64)), ("k_rot", C.c_void_p)]
 
 
 def bind(path: str):

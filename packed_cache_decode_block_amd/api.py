@@ -96,7 +96,7 @@ class PackedCache:
     """
 
     def __init__(self, *, L, B, Hq, Hkv, n_cap, k_mode=_lib.K_BLOCKGTQ, budget_units=128, k_bits=4, k_group=32,
-                 v_mode=_lib.V_CODEBOOK, v_bits=2, n_recent=0, device="cuda", zero=True):
+                 v_mode=_lib.V_CODEBOOK, v_bits=2, n_recent=0, k_rotation=False, device="cuda", zero=True):
         torch = _torch()
         self.desc = _lib.CacheDesc()
         d = self.desc
@@ -125,10 +125,25 @@ class PackedCache:
         self.bits = torch.zeros((L, Hkv, 64), dtype=torch.uint8, device=device)
         self.sigma = torch.zeros((L, Hkv, 64), dtype=torch.float32, device=device)
         self.inv_sigma = torch.zeros((L, Hkv, 64), dtype=torch.float32, device=device)
+        # sign bits of the randomized Hadamard key rotation (affine keys), [L, Hkv, 16]; see
+        # set_key_rotation.  All signs +1 until set.
+        self.k_rot = torch.zeros((L, Hkv, 16), dtype=torch.uint8, device=device) if k_rotation else None
         for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "recent_k", "recent_v",
-                     "bits", "sigma", "inv_sigma"):
+                     "bits", "sigma", "inv_sigma", "k_rot"):
             setattr(d, name, _ptr(getattr(self, name)))
         self._ws = None
+
+    def set_key_rotation(self, layer: int, signs):
+        """Signs s [Hkv, 128] (+1 / -1, host) of the key rotation of one layer: affine keys are
+        stored as H (s * k) / 16 and the query is rotated to H (s * q) / 8 at decode."""
+        torch = _torch()
+        if self.k_rot is None:
+            raise ValueError("the cache was created without k_rotation")
+        sg = np.asarray(signs)
+        if sg.shape != (self.desc.Hkv, 128) or not np.all(np.abs(sg) == 1):
+            raise ValueError("signs must be [Hkv, 128] of +1 / -1")
+        packed = np.packbits((sg < 0).astype(np.uint8), axis=1, bitorder="little")
+        self.k_rot[layer].copy_(torch.from_numpy(packed))
 
     def set_metadata(self, layer: int, bits, sigma, inv_sigma):
         """Upload per-(kv head, block) widths and key scales of one layer (host arrays [Hkv, 64])."""

@@ -74,6 +74,8 @@ int geometry(const bgtq_cache* c, bgtq::Geometry& g) {
     } else {
         return fail(BGTQ_E_INVALID, "unknown k_mode %d", c->k_mode);
     }
+    if (c->k_rot && c->k_mode != BGTQ_K_AFFINE)
+        return fail(BGTQ_E_UNSUPPORTED, "the key rotation applies to affine keys only");
     if (c->v_mode != BGTQ_V_CODEBOOK && c->v_mode != BGTQ_V_AFFINE) return fail(BGTQ_E_INVALID, "unknown v_mode");
     if (c->v_bits < 1 || c->v_bits > 4) return fail(BGTQ_E_INVALID, "v_bits must be in 1..4");
     g.v_mode = c->v_mode;
@@ -387,6 +389,7 @@ int bgtq_quantize_append(bgtq_cache* c, int layer, const void* k, const void* v,
         q.sigma = c->sigma + (size_t)layer * g.Hkv * 64;
         q.inv_sigma = c->inv_sigma + (size_t)layer * g.Hkv * 64;
     }
+    q.k_rot = c->k_rot ? c->k_rot + (size_t)layer * g.Hkv * 16 : nullptr;
     q.Hkv = g.Hkv;
     q.n_cap = g.n_cap;
     q.n_tiles = g.n_tiles;
@@ -538,6 +541,7 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
     a.q_dtype = dtype;
     a.bits = c->k_mode == BGTQ_K_BLOCKGTQ ? c->bits + (size_t)layer * g.Hkv * 64 : nullptr;
     a.sigma = c->k_mode == BGTQ_K_BLOCKGTQ ? c->sigma + (size_t)layer * g.Hkv * 64 : nullptr;
+    a.k_rot = c->k_rot ? c->k_rot + (size_t)layer * g.Hkv * 16 : nullptr;
     bgtq::Fp16Args ra{};
     if (c->n_recent > 0) {
         ra.k16 = (const uint16_t*)c->recent_k + (size_t)layer * bh * c->n_recent * D;

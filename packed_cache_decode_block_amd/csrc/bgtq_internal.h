@@ -37,6 +37,7 @@ struct DecodeArgs {
     const void* q;              // [B][Hq][128] in q_dtype
     const uint8_t* bits;        // [Hkv][64] this layer's widths (Block-GTQ)
     const float* sigma;         // [Hkv][64]
+    const uint8_t* k_rot;       // [Hkv][16] sign bits of the key rotation (affine keys), or null
     float* part;                // [B][Hq][n_parts][132]
     int q_dtype;
     int Hkv, Hq, G;
@@ -100,6 +101,7 @@ struct QuantArgs {
     const uint8_t* bits;        // [Hkv][64]
     const float* sigma;
     const float* inv_sigma;
+    const uint8_t* k_rot;       // [Hkv][16] sign bits of the key rotation (affine keys), or null
     int Hkv;
     int64_t n_cap, n_tiles, k_tile_bytes, v_tile_bytes;
     int k_mode, R, k_bits, k_group;

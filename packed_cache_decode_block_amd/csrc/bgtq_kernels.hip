@@ -594,7 +594,7 @@ __device__ __forceinline__ PrepIn<G> prep_load(const void* q, int dtype, const u
 
 template <int G, bool SORTED, int KG>
 __device__ void prep_store(const PrepIn<G>& in, int lane, float* qp, uint16_t* dsc16, uint32_t* nnz_pad, float* qs,
-                           int3* order = nullptr) {
+                           int3* order = nullptr, const uint8_t* rot = nullptr) {
     float q0[G], q1[G];
     if (in.dtype == BGTQ_F32) {
 #pragma unroll
@@ -613,6 +613,26 @@ __device__ void prep_store(const PrepIn<G>& in, int lane, float* qp, uint16_t* d
         for (int hh = 0; hh < G; ++hh) {
             q0[hh] = bf2f(in.r0[hh] & 0xFFFFu);
             q1[hh] = bf2f(in.r0[hh] >> 16);
+        }
+    }
+    if (rot) {
+        // keys stored rotated (y = H (s * k) / 16): the query goes to H (s * q) / 8, so q'.y = q.k.
+        // Coordinates 2 lane + e; stage 1 pairs them inside the lane, stages 2..64 pair lane
+        // with lane ^ m (m = 1..32): the lower lane keeps a + b, the upper one takes a - b.
+        const uint32_t sbits = (uint32_t)rot[lane >> 2] >> (2 * (lane & 3));
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            const float a0 = (sbits & 1u) ? -q0[hh] : q0[hh], a1 = (sbits & 2u) ? -q1[hh] : q1[hh];
+            float u = a0 + a1, v = a0 - a1;
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) {
+                const float pu = __shfl_xor(u, m, 64), pv = __shfl_xor(v, m, 64);
+                const bool upper = (lane & m) != 0;
+                u = upper ? pu - u : u + pu;
+                v = upper ? pv - v : v + pv;
+            }
+            q0[hh] = u * 0.125f;
+            q1[hh] = v * 0.125f;
         }
     }
 #pragma unroll
@@ -662,8 +682,10 @@ __device__ void prep_store(const PrepIn<G>& in, int lane, float* qp, uint16_t* d
 
 template <int G, bool SORTED, int KG>
 __device__ void prep_wave(const void* q, int dtype, const uint8_t* bits, const float* sigma, int b, int h,
-                          int Hq, int lane, float* qp, uint16_t* dsc16, uint32_t* nnz_pad, float* qs) {
-    prep_store<G, SORTED, KG>(prep_load<G, SORTED>(q, dtype, bits, sigma, b, h, Hq, lane), lane, qp, dsc16, nnz_pad, qs);
+                          int Hq, int lane, float* qp, uint16_t* dsc16, uint32_t* nnz_pad, float* qs,
+                          const uint8_t* rot = nullptr) {
+    prep_store<G, SORTED, KG>(prep_load<G, SORTED>(q, dtype, bits, sigma, b, h, Hq, lane), lane, qp, dsc16, nnz_pad, qs,
+                              nullptr, rot);
 }
 
 template <int G>
@@ -743,7 +765,8 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
         s_vlut[i] = ha | (hb << 16);
     }
     if (wave == 0)
-        prep_wave<G, !AFFINE_K, KG>(a.q, a.q_dtype, a.bits, a.sigma, b, h, a.Hq, lane, s_qp, s_dsc, &s_nnz, s_qs);
+        prep_wave<G, !AFFINE_K, KG>(a.q, a.q_dtype, a.bits, a.sigma, b, h, a.Hq, lane, s_qp, s_dsc, &s_nnz, s_qs,
+                                    AFFINE_K && a.k_rot ? a.k_rot + h * 16 : nullptr);
     __syncthreads();
 
     float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_parts * PART;
@@ -1859,7 +1882,10 @@ __device__ __forceinline__ void affine_group(const X& x, int n, int bits, uint16
 // uint16_t bits for fp16 / bf16), padded to an odd number of dwords so that the per-lane row
 // reads of the quantizer hit distinct banks.  Value codes overwrite their own row in place (code
 // j lands in bytes the row's elements 0..j already vacated).
-template <typename XT>
+// ROT: affine keys stored rotated, y = H (s * k) / 16 (s from QuantArgs::k_rot): the row is
+// rotated in registers by the fast transform (stages 1, 2, ..., 64, one fp32 addition or
+// subtraction per output, the final 1/16 exact) and staged as fp32 for the affine groups.
+template <typename XT, bool ROT>
 __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
     constexpr int XS = sizeof(XT) == 4 ? D + 1 : D + 2;  // row stride in elements (129 dwords / 65 dwords)
     constexpr int EPC = 16 / sizeof(XT);                 // elements per 16-byte chunk
@@ -1871,6 +1897,7 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
     const bool active = pos >= a.pos_lo[b] && pos < a.pos_hi[b];
     __shared__ float s_thr[BGTQ_CB_THRESHOLDS];
     __shared__ __attribute__((aligned(16))) XT s_x[64 * XS];
+    __shared__ float s_y[ROT ? 64 * (D + 1) : 1];  // rotated key rows (ROT only)
     __shared__ int s_order[64];
     __shared__ int s_wid[64];
     __shared__ float s_r[64], s_sig[64];
@@ -1963,13 +1990,43 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
             } else {
                 const int ng = D / a.k_group;
                 uint32_t codes[D];
-                for (int gi = 0; gi < ng; ++gi) {
-                    uint16_t sc, zz;
-                    affine_group(x + gi * a.k_group, a.k_group, a.k_bits, &sc, &zz, codes + gi * a.k_group);
-                    if (active) {
-                        a.k_scale[(bh * a.n_cap + pos) * ng + gi] = sc;
-                        a.k_zero[(bh * a.n_cap + pos) * ng + gi] = zz;
+                auto groups = [&](const auto& xr) {
+                    for (int gi = 0; gi < ng; ++gi) {
+                        uint16_t sc, zz;
+                        affine_group(xr + gi * a.k_group, a.k_group, a.k_bits, &sc, &zz, codes + gi * a.k_group);
+                        if (active) {
+                            a.k_scale[(bh * a.n_cap + pos) * ng + gi] = sc;
+                            a.k_zero[(bh * a.n_cap + pos) * ng + gi] = zz;
+                        }
                     }
+                };
+                if constexpr (ROT) {
+                    const uint8_t* sg = a.k_rot + h * 16;
+                    float y[D];
+#pragma unroll
+                    for (int j = 0; j < D; ++j) {
+                        const float v = x[j];
+                        y[j] = ((sg[j >> 3] >> (j & 7)) & 1u) ? -v : v;
+                    }
+#pragma unroll
+                    for (int hs = 1; hs < D; hs <<= 1) {
+#pragma unroll
+                        for (int i0 = 0; i0 < D; i0 += 2 * hs) {
+#pragma unroll
+                            for (int j = i0; j < i0 + hs; ++j) {
+#pragma clang fp contract(off)
+                                const float p = y[j], r = y[j + hs];
+                                y[j] = p + r;
+                                y[j + hs] = p - r;
+                            }
+                        }
+                    }
+                    float* yr = s_y + lane * (D + 1);
+#pragma unroll
+                    for (int j = 0; j < D; ++j) yr[j] = y[j] * 0.0625f;
+                    groups(XRow<float>{yr, BGTQ_F32});
+                } else {
+                    groups(x);
                 }
                 const int per = 32 / a.k_bits;
                 for (int k = 0; k < a.R; ++k) {
@@ -2084,8 +2141,13 @@ hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_
     const int es = a.dtype == BGTQ_F32 ? 4 : 2;
     q.vec16 = ((uintptr_t)a.src_k % 16 == 0) && ((uintptr_t)a.src_v % 16 == 0) && (a.sB * es) % 16 == 0 &&
               (a.sT * es) % 16 == 0 && (a.sH * es) % 16 == 0;
-    if (a.dtype == BGTQ_F32) return launch_main(k_quant<float>, dim3((unsigned)max_tiles, a.Hkv, B), dim3(64), s, q);
-    return launch_main(k_quant<uint16_t>, dim3((unsigned)max_tiles, a.Hkv, B), dim3(64), s, q);
+    const dim3 grid((unsigned)max_tiles, a.Hkv, B);
+    if (a.k_rot && a.k_mode == BGTQ_K_AFFINE && (a.which & 1)) {
+        if (a.dtype == BGTQ_F32) return launch_main(k_quant<float, true>, grid, dim3(64), s, q);
+        return launch_main(k_quant<uint16_t, true>, grid, dim3(64), s, q);
+    }
+    if (a.dtype == BGTQ_F32) return launch_main(k_quant<float, false>, grid, dim3(64), s, q);
+    return launch_main(k_quant<uint16_t, false>, grid, dim3(64), s, q);
 }
 
 hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t s) {

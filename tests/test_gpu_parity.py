@@ -135,6 +135,40 @@ def test_fixed_allocation_decode(name):
         print(f"  splits={ns}: max abs err {e:.2e}", flush=True)
 
 
+ROT_CASES = {
+    # affine K4 keys stored rotated (QWC summary, Results: key-only rotation at K4V2); with and
+    # without the fp16 recent ring (ring rows are evicted through the rotated quantizer, the ring
+    # split itself attends with the unrotated query)
+    "w4_rotated": (4, {"L": 1, "B": 2}, 2048 + 13, (None,)),
+    "w4_rotated_ring": (4, {"L": 1, "B": 1, "n_recent": 64}, 1000 + 7, (300, 1, 64, None)),
+}
+
+
+@pytest.mark.parametrize("name", list(ROT_CASES))
+def test_rotated_affine_keys(name):
+    wid, ov, N, chunks = ROT_CASES[name]
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
+    print(f"[rotated {name}] N={N} B={w.B} Hq={w.Hq} Hkv={w.Hkv} n_recent={w.n_recent}", flush=True)
+    n_cap = ((N + 63) // 64 + 1) * 64
+    signs = np.where(np.random.default_rng(31).random((w.Hkv, 128)) < 0.5, -1.0, 1.0)
+    K, V, q = T.inputs(w, 0, N)
+    oc = pipeline.build_layer(K, V, k_mode=w.k_mode, v_mode=w.v_mode, v_bits=w.v_bits, n_cap=n_cap, k_bits=w.k_bits,
+                              k_group=w.k_group, n_recent=w.n_recent, k_rot=signs)
+    cache = P.PackedCache(L=1, B=w.B, Hq=w.Hq, Hkv=w.Hkv, n_cap=n_cap, k_mode=P.K_AFFINE, k_bits=w.k_bits,
+                          k_group=w.k_group, v_mode=P.V_CODEBOOK if w.v_mode == "codebook" else P.V_AFFINE,
+                          v_bits=w.v_bits, n_recent=w.n_recent, k_rotation=True)
+    cache.set_key_rotation(0, signs)
+    T.append_all(cache, 0, K, V, w.dtype, chunks)
+    _compare_cache(cache, oc, w)
+    ref = pipeline.decode_layer(oc, q)
+    qd = T.to_dev(q, w.dtype)
+    for ns in (0, 1, 3):
+        out = cache.decode_attention(0, qd, n_splits=ns)
+        torch.cuda.synchronize()
+        e = T.assert_close(out.cpu().numpy(), ref, f"{name} splits={ns}")
+        print(f"  splits={ns}: max abs err {e:.2e}", flush=True)
+
+
 def test_decode_deterministic_and_split_invariant():
     w = synth.reduced(synth.WORKLOADS[2], L=1)
     N = 5000

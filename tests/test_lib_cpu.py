@@ -132,11 +132,17 @@ def test_cache_bytes_geometry():
     (dict(d=64), P.E_UNSUPPORTED), (dict(Hq=15), P.E_INVALID), (dict(Hq=32, Hkv=2), P.E_UNSUPPORTED),
     (dict(n_cap=100), P.E_INVALID), (dict(budget_units=100), P.E_INVALID), (dict(v_bits=5), P.E_INVALID),
     (dict(k_mode=1, k_bits=3), P.E_INVALID), (dict(k_mode=1, k_group=48), P.E_INVALID), (dict(B=65), P.E_UNSUPPORTED),
-    (dict(k_mode=7), P.E_INVALID), (dict(n_recent=-1), P.E_INVALID)])
+    (dict(k_mode=7), P.E_INVALID), (dict(n_recent=-1), P.E_INVALID),
+    (dict(k_rot=0x1000), P.E_UNSUPPORTED)])                        # key rotation needs affine keys
 def test_descriptor_validation(kw, code):
     d = _desc(**kw)
     assert P.lib.bgtq_cache_bytes(C.byref(d), _lib.BUF_K_CODES) == code
     assert P.lib.bgtq_last_error()
+
+
+def test_key_rotation_accepted_with_affine_keys():
+    d = _desc(k_mode=1, k_bits=4, k_group=32, k_rot=0x1000)
+    assert P.lib.bgtq_cache_bytes(C.byref(d), _lib.BUF_K_CODES) == 2 * 3 * 2 * 4096 * 64
 
 
 def test_append_and_decode_validate_before_launch():
