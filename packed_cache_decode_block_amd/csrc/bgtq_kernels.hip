@@ -923,33 +923,41 @@ __device__ __forceinline__ uint32_t slot_coord(const uint8_t* lds, uint64_t win,
     return c0 | (c1 << 16);
 }
 
-// Column pair M (element pairs 2M, 2M + 1) of a k-step: per token group g one window of two stage
-// rows shared by the lane row's two slots.  CA / CB: whether columns 2M / 2M + 1 are read per
-// coordinate.  lb: this lane's token column in the wave's K stage.
-template <int M, bool CA, bool CB>
-__device__ __forceinline__ void col_pair2(uint32_t (&P)[16], const uint8_t* lds, uint32_t dA, uint32_t dB, uint32_t lb) {
-    const uint32_t ad = (dA >> 17) + lb;
-    const uint32_t mA = CA ? bfm<1>(dA >> 12) : bfm<2>(dA >> 12);
-    const uint32_t mB = CB ? bfm<1>(dB >> 12) : bfm<2>(dB >> 12);
-    const uint32_t bA = mA + (CA ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
-    const uint32_t bB = mB + (CB ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
-    // the four windows (stage rows r, r + 1 of token groups g = 0..3) as four ds_read2, each
-    // straight into a register pair; the block waits for them itself.
+// Both column pairs of a k-step: the eight windows (two column pairs x four token groups) as one
+// batch of ds_read2, then the sixteen slot lookups, so that a k-step waits on two LDS round trips
+// rather than three.  CA0/CB0, CA1/CB1: coordinate mode of columns 0..3.
+template <bool CA0, bool CB0, bool CA1, bool CB1>
+__device__ __forceinline__ void col_pairs_both(uint32_t (&P)[16], const uint8_t* lds, const u32x4_t dk, uint32_t lb) {
+    const uint32_t ad0 = (dk[0] >> 17) + lb, ad1 = (dk[2] >> 17) + lb;
+    const uint32_t m0 = CA0 ? bfm<1>(dk[0] >> 12) : bfm<2>(dk[0] >> 12);
+    const uint32_t m1 = CB0 ? bfm<1>(dk[1] >> 12) : bfm<2>(dk[1] >> 12);
+    const uint32_t m2 = CA1 ? bfm<1>(dk[2] >> 12) : bfm<2>(dk[2] >> 12);
+    const uint32_t m3 = CB1 ? bfm<1>(dk[3] >> 12) : bfm<2>(dk[3] >> 12);
+    const uint32_t b0 = m0 + (CA0 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
+    const uint32_t b1 = m1 + (CB0 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
+    const uint32_t b2 = m2 + (CA1 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
+    const uint32_t b3 = m3 + (CB1 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
     static_assert(BGTQ_KST_ROW_BYTES == 320, "window read offsets assume 80-dword stage rows");
-    uint64_t wv[4];
-    asm volatile("ds_read2_b32 %0, %4 offset1:80\n\t"
-                 "ds_read2_b32 %1, %4 offset0:16 offset1:96\n\t"
-                 "ds_read2_b32 %2, %4 offset0:32 offset1:112\n\t"
-                 "ds_read2_b32 %3, %4 offset0:48 offset1:128\n\t"
+    uint64_t wa[4], wb[4];
+    asm volatile("ds_read2_b32 %0, %8 offset1:80\n\t"
+                 "ds_read2_b32 %1, %8 offset0:16 offset1:96\n\t"
+                 "ds_read2_b32 %2, %8 offset0:32 offset1:112\n\t"
+                 "ds_read2_b32 %3, %8 offset0:48 offset1:128\n\t"
+                 "ds_read2_b32 %4, %9 offset1:80\n\t"
+                 "ds_read2_b32 %5, %9 offset0:16 offset1:96\n\t"
+                 "ds_read2_b32 %6, %9 offset0:32 offset1:112\n\t"
+                 "ds_read2_b32 %7, %9 offset0:48 offset1:128\n\t"
                  "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(wv[0]), "=&v"(wv[1]), "=&v"(wv[2]), "=&v"(wv[3])
-                 : "v"((uint32_t)(uintptr_t)(lds + ad))
+                 : "=&v"(wa[0]), "=&v"(wa[1]), "=&v"(wa[2]), "=&v"(wa[3]),
+                   "=&v"(wb[0]), "=&v"(wb[1]), "=&v"(wb[2]), "=&v"(wb[3])
+                 : "v"((uint32_t)(uintptr_t)(lds + ad0)), "v"((uint32_t)(uintptr_t)(lds + ad1))
                  : "memory");
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        const uint64_t win = wv[g];
-        P[4 * g + 2 * M] = CA ? slot_coord(lds, win, dA, mA, bA) : slot_pair(lds, win, dA, mA, bA);
-        P[4 * g + 2 * M + 1] = CB ? slot_coord(lds, win, dB, mB, bB) : slot_pair(lds, win, dB, mB, bB);
+        P[4 * g + 0] = CA0 ? slot_coord(lds, wa[g], dk[0], m0, b0) : slot_pair(lds, wa[g], dk[0], m0, b0);
+        P[4 * g + 1] = CB0 ? slot_coord(lds, wa[g], dk[1], m1, b1) : slot_pair(lds, wa[g], dk[1], m1, b1);
+        P[4 * g + 2] = CA1 ? slot_coord(lds, wb[g], dk[2], m2, b2) : slot_pair(lds, wb[g], dk[2], m2, b2);
+        P[4 * g + 3] = CB1 ? slot_coord(lds, wb[g], dk[3], m3, b3) : slot_pair(lds, wb[g], dk[3], m3, b3);
     }
 }
 
@@ -957,8 +965,7 @@ __device__ __forceinline__ void col_pair2(uint32_t (&P)[16], const uint8_t* lds,
 template <int KS, int A>
 __device__ __forceinline__ void mx_kops(uint32_t (&P)[16], const uint8_t* lds, const u32x4_t* sd, uint32_t lb) {
     const u32x4_t dk = sd[KS];
-    col_pair2<0, (A > 0), (A > 1)>(P, lds, dk[0], dk[1], lb);
-    col_pair2<1, (A > 2), (A > 3)>(P, lds, dk[2], dk[3], lb);
+    col_pairs_both<(A > 0), (A > 1), (A > 2), (A > 3)>(P, lds, dk, lb);
 }
 
 // k-step KS of a tile; ncc (wave-uniform) = number of coordinate columns of the whole record.  The
@@ -1129,8 +1136,12 @@ template <int G, int R, int VB> struct MxLds {
     static constexpr int SIZE = cmax(cmax(SST + 4 * SST_W, QP + 512), RED + 4 * (4 * G * PART + 4 * G));
 };
 
+// 3-bit values (the headline K3V3 shapes) take two resident workgroups per CU and the register
+// room that buys (both column pairs' windows of a k-step in flight); the others three.
+template <int VB> constexpr int mx_wgs_per_cu() { return VB == 3 ? 2 : 3; }
+
 template <int G, int R, int VB>
-__global__ __launch_bounds__(256, 3) void k_decode_mx(const DecodeArgs a) {
+__global__ __launch_bounds__(256, mx_wgs_per_cu<VB>()) void k_decode_mx(const DecodeArgs a) {
     static_assert(G == 4 || G == 8, "matrix-core decode serves 4 or 8 query heads per kv head");
     static_assert(R % 4 == 0, "K records are staged in 16-byte chunks");
     using LD = MxLds<G, R, VB>;
@@ -2240,7 +2251,10 @@ void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
 }
 void disarm_launch_events() { t_ev_start = t_ev_stop = nullptr; }
 
-int decode_wgs_per_cu(int k_mode, int G) { return (k_mode == BGTQ_K_BLOCKGTQ && G >= 4) ? 3 : 2; }
+int decode_wgs_per_cu(int k_mode, int G, int v_bits) {
+    if (k_mode == BGTQ_K_BLOCKGTQ && G >= 4) return v_bits == 3 ? mx_wgs_per_cu<3>() : mx_wgs_per_cu<2>();
+    return 2;
+}
 
 bool decode_supported(int k_mode, int R, int k_bits, int k_group, int v_bits, int G) {
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return false;
