@@ -169,6 +169,38 @@ def test_rotated_affine_keys(name):
         print(f"  splits={ns}: max abs err {e:.2e}", flush=True)
 
 
+EDGE_CASES = {
+    # name: (workload id, overrides, N, n_splits)
+    "max_batch_64": (3, {"L": 1, "B": 64, "Hkv": 1, "Hq": 4}, 70, 0),
+    "splits_far_beyond_tiles": (2, {"L": 1}, 5 * 64 - 3, 40),
+    "one_token_mx": (2, {"L": 1}, 1, 0),
+    "one_token_vector": (1, {}, 1, 0),
+    "one_token_affine": (4, {"L": 1, "B": 1, "Hkv": 1, "Hq": 4}, 1, 3),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE_CASES))
+def test_decode_edge_cases(name):
+    """The largest batch the library takes, splits that own no tile (their partials carry no
+    weight in the merge), and a context of a single token (the output is that token's value)."""
+    wid, ov, N, ns = EDGE_CASES[name]
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
+    print(f"[edge {name}] N={N} B={w.B} Hq={w.Hq} Hkv={w.Hkv} splits={ns}", flush=True)
+    n_cap = ((N + 63) // 64) * 64
+    m = T.meta(w, 0)
+    K, V, q = T.inputs(w, 0, N)
+    oc = T.oracle_layer(w, K, V, m, n_cap)
+    cache = T.gpu_cache(w, n_cap)
+    if m is not None:
+        cache.set_metadata(0, m.bits, m.sigma, m.r)
+    T.append_all(cache, 0, K, V, w.dtype)
+    _compare_cache(cache, oc, w)
+    ref = pipeline.decode_layer(oc, q)
+    out = cache.decode_attention(0, T.to_dev(q, w.dtype), n_splits=ns).cpu().numpy()
+    e = T.assert_close(out, ref, name)
+    print(f"  max abs err {e:.2e}", flush=True)
+
+
 def test_decode_deterministic_and_split_invariant():
     w = synth.reduced(synth.WORKLOADS[2], L=1)
     N = 5000
