@@ -1860,6 +1860,35 @@ __device__ __forceinline__ float rms_scale16(const X& x /*one token's row*/, con
     return h2f(h);
 }
 
+// Value codes of one token (codebook width VB): the thresholds scaled by the token's scale are
+// formed once (the same fp32 products the search forms), and each code is the number of them at
+// or below the coordinate, which is the search's result since the products ascend (S >= 0).  The
+// 128 codes collect in registers, one byte each, and are stored after every element is read.
+template <int VB, typename X>
+__device__ __forceinline__ void v_codes_row(const X& x, float S, bool active, uint8_t* cr, const float* thr) {
+    constexpr int NT = (1 << VB) - 1;
+    float th[NT];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+#pragma clang fp contract(off)
+        th[m] = S * thr[thr_base(VB) + m];
+    }
+    uint32_t pk[D / 4];
+#pragma unroll
+    for (int k = 0; k < D / 4; ++k) pk[k] = 0u;
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        const float v = x[j];
+        uint32_t c = 0;
+#pragma unroll
+        for (int m = 0; m < NT; ++m) c += v >= th[m] ? 1u : 0u;
+        pk[j >> 2] |= c << (8 * (j & 3));
+    }
+    uint32_t* dst = (uint32_t*)cr;
+#pragma unroll
+    for (int k = 0; k < D / 4; ++k) dst[k] = active ? pk[k] : 0u;
+}
+
 template <typename X>
 __device__ __forceinline__ void affine_group(const X& x, int n, int bits, uint16_t* sc16, uint16_t* z16,
                                              uint32_t* codes) {
@@ -2056,9 +2085,11 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
             uint8_t* cr = (uint8_t*)(s_x + lane * XS);
             if (a.v_mode == BGTQ_V_CODEBOOK) {
                 const float S = rms_scale16(x, nullptr, &s16);
-                for (int j = 0; j < D; ++j) {
-                    const uint8_t cj = active ? (uint8_t)tq_code(x[j], S, vb, s_thr) : (uint8_t)0;
-                    cr[j] = cj;  // byte j lies in elements 0..j of this row, already read
+                switch (vb) {
+                    case 1: v_codes_row<1>(x, S, active, cr, s_thr); break;
+                    case 2: v_codes_row<2>(x, S, active, cr, s_thr); break;
+                    case 3: v_codes_row<3>(x, S, active, cr, s_thr); break;
+                    default: v_codes_row<4>(x, S, active, cr, s_thr); break;
                 }
             } else {
                 uint32_t codes[D];
