@@ -2007,6 +2007,8 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
                 const float S = rms_scale16(x, s_r, &s16);
                 uint64_t buf = 0;
                 int nb = 0, k = 0;
+                // the slots' threshold searches are independent: unrolled so that they interleave
+#pragma unroll 4
                 for (int s = 0; s < nnz; ++s) {
                     const int i = s_order[s], w = s_wid[i];
                     float t;
