@@ -58,6 +58,7 @@ enum {
 #define BGTQ_N_BLOCKS 64
 #define BGTQ_TILE 64
 #define BGTQ_MAX_BATCH 64
+#define BGTQ_ENERGY_CHUNK 16   /* calibration tokens per workgroup of bgtq_block_energy */
 
 /*
  * Packed KV cache descriptor (plain data; the caller fills it and owns every buffer).
@@ -170,7 +171,10 @@ int bgtq_allocate_rate(const double *scores, int n_heads, int n_blk, int budget_
  * inv_sigma_i = fp32(1/sigma_i) (0 if sigma_i = 0).  Sums run in fp64 on the device.
  * k_cal: device [T_cal][Hkv][128], q_cal: device [T_cal][Hkv*g][128], contiguous, dtype.
  * Outputs (host, [Hkv][64]; any may be NULL): scores fp64, sigma fp32, inv_sigma fp32.
- * ws: device scratch of at least Hkv*64*16 bytes (caller-owned).  Synchronizes `stream`.
+ * ws: device scratch of at least Hkv*64*16 bytes (caller-owned).  The tokens are reduced in
+ * chunks of BGTQ_ENERGY_CHUNK, one workgroup each, as many as ws holds (Hkv*64*16 bytes per
+ * chunk; ceil(T_cal / BGTQ_ENERGY_CHUNK) chunks use the whole GPU); the host adds the chunk sums
+ * in order, so equal calls give equal results.  Synchronizes `stream`.
  * Errors: BGTQ_E_INVALID (NULL inputs, T_cal < 1, bad dtype, small ws), BGTQ_E_UNSUPPORTED (d).
  */
 int bgtq_block_energy(const void *k_cal, const void *q_cal, int dtype, int64_t T_cal,

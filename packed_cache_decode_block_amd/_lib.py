@@ -15,6 +15,7 @@ V_CODEBOOK, V_AFFINE = 0, 1
 (BUF_K_CODES, BUF_V_CODES, BUF_K_SCALE, BUF_K_ZERO, BUF_V_SCALE, BUF_V_ZERO, BUF_RECENT_K,
  BUF_RECENT_V, BUF_META) = range(9)
 MAX_BATCH = 64
+ENERGY_CHUNK = 16  # BGTQ_ENERGY_CHUNK: calibration tokens per workgroup of bgtq_block_energy
 
 SYMBOLS = ["bgtq_last_error", "bgtq_version", "bgtq_codebook", "bgtq_allocate", "bgtq_allocate_rate", "bgtq_block_energy",
            "bgtq_cache_bytes", "bgtq_quantize_append", "bgtq_decode_workspace_bytes", "bgtq_decode_attention",

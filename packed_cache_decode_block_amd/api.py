@@ -81,7 +81,8 @@ def bgtq_block_energy(k_cal, q_cal, score_mode: int = _lib.SCORE_QK, stream=None
     _require_cuda(k_cal, q_cal)
     T, Hkv, d = k_cal.shape
     g = q_cal.shape[1] // Hkv
-    ws = torch.empty(Hkv * 64 * 2, dtype=torch.float64, device=k_cal.device)
+    chunks = (T + _lib.ENERGY_CHUNK - 1) // _lib.ENERGY_CHUNK
+    ws = torch.empty(chunks * Hkv * 64 * 2, dtype=torch.float64, device=k_cal.device)
     sc = np.zeros((Hkv, 64)); sg = np.zeros((Hkv, 64), np.float32); rs = np.zeros((Hkv, 64), np.float32)
     check(lib.bgtq_block_energy(_ptr(k_cal), _ptr(q_cal), _dtype_code(k_cal), T, Hkv, g, d, score_mode,
                                 sc.ctypes.data_as(C.POINTER(C.c_double)), sg.ctypes.data_as(C.POINTER(C.c_float)),

@@ -296,20 +296,29 @@ int bgtq_block_energy(const void* k_cal, const void* q_cal, int dtype, int64_t T
     if (d != D) return fail(BGTQ_E_UNSUPPORTED, "head dim must be 128");
     if (T_cal < 1 || Hkv < 1 || g < 1) return fail(BGTQ_E_INVALID, "bad sizes");
     if (score_mode != BGTQ_SCORE_QK && score_mode != BGTQ_SCORE_K) return fail(BGTQ_E_INVALID, "bad score mode");
-    const size_t need = (size_t)Hkv * 64 * 2 * sizeof(double);
-    if (ws_bytes < need) return fail(BGTQ_E_INVALID, "workspace too small (%zu < %zu)", ws_bytes, need);
+    const size_t per_chunk = (size_t)Hkv * 64 * 2 * sizeof(double);
+    if (ws_bytes < per_chunk) return fail(BGTQ_E_INVALID, "workspace too small (%zu < %zu)", ws_bytes, per_chunk);
+    // tokens in chunks of BGTQ_ENERGY_CHUNK, one workgroup each, as far as the workspace holds them
+    const int64_t want = (T_cal + BGTQ_ENERGY_CHUNK - 1) / BGTQ_ENERGY_CHUNK;
+    const int64_t n_chunks = std::max<int64_t>(1, std::min<int64_t>({want, (int64_t)(ws_bytes / per_chunk), 65535}));
+    const int64_t tc = (T_cal + n_chunks - 1) / n_chunks;
     hipStream_t s = (hipStream_t)stream;
-    bgtq::EnergyArgs a{k_cal, q_cal, dtype, T_cal, Hkv, g, (double*)ws};
+    bgtq::EnergyArgs a{k_cal, q_cal, dtype, T_cal, Hkv, g, (double*)ws, (int)n_chunks, tc};
     hipError_t e = bgtq::launch_energy(a, s);
     if (e != hipSuccess) return hip_fail(e, "energy launch");
-    std::vector<double> host((size_t)Hkv * 128);
-    e = hipMemcpyAsync(host.data(), ws, need, hipMemcpyDeviceToHost, s);
+    std::vector<double> host((size_t)n_chunks * Hkv * 128);
+    e = hipMemcpyAsync(host.data(), ws, (size_t)n_chunks * per_chunk, hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "energy copy");
     for (int h = 0; h < Hkv; ++h)
         for (int i = 0; i < 64; ++i) {
-            const double ek = host[(h * 64 + i) * 2] / (double)T_cal;
-            const double eq = host[(h * 64 + i) * 2 + 1] / ((double)T_cal * g);
+            double sk = 0.0, sq = 0.0;  // chunks in order: the same sums for the same chunk count
+            for (int64_t c = 0; c < n_chunks; ++c) {
+                sk += host[((c * Hkv + h) * 64 + i) * 2];
+                sq += host[((c * Hkv + h) * 64 + i) * 2 + 1];
+            }
+            const double ek = sk / (double)T_cal;
+            const double eq = sq / ((double)T_cal * g);
             const float sg = (float)std::sqrt(ek / 2.0);
             if (scores) scores[h * 64 + i] = score_mode == BGTQ_SCORE_QK ? eq * ek : ek;
             if (sigma) sigma[h * 64 + i] = sg;

@@ -79,7 +79,9 @@ struct EnergyArgs {
     int dtype;
     int64_t T;
     int Hkv, G;
-    double* out;                // [Hkv][64][2]: sum_t |k_blk|^2, sum_{t,h} |q_blk|^2
+    double* out;                // [n_chunks][Hkv][64][2]: sum_t |k_blk|^2, sum_{t,h} |q_blk|^2 per chunk
+    int n_chunks;               // token chunks (grid y)
+    int64_t tc;                 // tokens per chunk
 };
 
 // One quantize launch writes tokens [pos_lo[b], pos_hi[b]) of every sequence b; the row of

@@ -1788,11 +1788,14 @@ __global__ __launch_bounds__(64) void k_combine(const CombineArgs a) {
 }
 
 // Calibration energy sums in fp64: out[h][i] = (sum_t |k_t,blk i|^2, sum_{t,g} |q_t,g,blk i|^2).
+// Grid (kv head, token chunk): chunk c sums tokens [c*tc, (c+1)*tc) into out[c][h][i] (fp64);
+// the host adds the chunks in order, so the sums are deterministic for a given chunk count.
 __global__ __launch_bounds__(256) void k_energy(const EnergyArgs a) {
-    const int h = blockIdx.x, blk = threadIdx.x & 63, part = threadIdx.x >> 6;
+    const int h = blockIdx.x, chunk = blockIdx.y, blk = threadIdx.x & 63, part = threadIdx.x >> 6;
     const int Hq = a.Hkv * a.G;
+    const int64_t t0 = (int64_t)chunk * a.tc, t1 = t0 + a.tc < a.T ? t0 + a.tc : a.T;
     double ek = 0.0, eq = 0.0;
-    for (int64_t t = part; t < a.T; t += 4) {
+    for (int64_t t = t0 + part; t < t1; t += 4) {
         const int64_t kb = (t * a.Hkv + h) * D + 2 * blk;
         const double k0 = load_act(a.k, kb, a.dtype), k1 = load_act(a.k, kb + 1, a.dtype);
         ek += k0 * k0 + k1 * k1;
@@ -1812,8 +1815,9 @@ __global__ __launch_bounds__(256) void k_energy(const EnergyArgs a) {
             sk += s_e[p][blk][0];
             sq += s_e[p][blk][1];
         }
-        a.out[(h * 64 + blk) * 2 + 0] = sk;
-        a.out[(h * 64 + blk) * 2 + 1] = sq;
+        double* o = a.out + (((size_t)chunk * a.Hkv + h) * 64 + blk) * 2;
+        o[0] = sk;
+        o[1] = sq;
     }
 }
 
@@ -2173,7 +2177,7 @@ hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s) {
 }
 
 hipError_t launch_energy(const EnergyArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(k_energy, dim3(a.Hkv), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_energy, dim3(a.Hkv, a.n_chunks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
