@@ -336,9 +336,12 @@ def main():
         n16, tot16, _, _ = P.bgtq_profile_read(P.PROF_FP16_DECODE)
         P.bgtq_profile_enable(0)
         b16 = w.B * w.Hkv * w.N * 512 + w.B * w.Hq * w.d * 6
+        k16_ms = tot16 / max(n16, 1)
         result["fp16_baseline"] = {
             "ms_per_step": round(sec16 * 1e3, 4), "value": round(w.L * b16 / sec16 / 1e9, 2), "unit": "GB/s",
-            "kernel_avg_us": round(tot16 / max(n16, 1) * 1e3, 3),
+            "kernel_avg_us": round(k16_ms * 1e3, 3),
+            "kernel_GB/s": round(b16 / (k16_ms * 1e-3) / 1e9, 1),
+            "kernel_frac": round(b16 / (k16_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "kernel": "k_decode_fp16_mx" if w.Hq // w.Hkv >= 4 else "k_decode_fp16",
             "traffic": measured_traffic(w.wid, "k_decode_fp16_mx") if w.Hq // w.Hkv >= 4 else None,
             "speedup_packed_vs_fp16": round(sec16 / sec, 3)}
