@@ -486,7 +486,7 @@ int64_t bgtq_decode_workspace_bytes(const bgtq_cache* c, int n_splits) {
     if (n_splits < 0) return fail(BGTQ_E_INVALID, "n_splits < 0");
     const int64_t max_tiles = g.n_tiles;
     const int ns = n_splits ? n_splits
-                            : default_splits(max_tiles, g.B * g.Hkv, cu_count(), bgtq::decode_wgs_per_cu(c->k_mode, g.G, c->v_bits));
+                            : default_splits(max_tiles, g.B * g.Hkv, cu_count(), bgtq::decode_wgs_per_cu(c->k_mode, g.G, c->v_bits, c->k_group));
     const int parts = ns + (g.n_recent > 0 ? 1 : 0);
     if (parts > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS - 1);
     return (int64_t)g.B * g.Hq * parts * PART * 4;
@@ -527,7 +527,7 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
         any_recent |= rec > 0;
     }
     // Default splits follow the current length; never more than the capacity-sized workspace holds.
-    const int per_cu = bgtq::decode_wgs_per_cu(c->k_mode, g.G, c->v_bits);
+    const int per_cu = bgtq::decode_wgs_per_cu(c->k_mode, g.G, c->v_bits, c->k_group);
     const int ns = n_splits ? n_splits
                             : std::min(default_splits(std::max<int64_t>(max_tiles, 1), g.B * g.Hkv, cu_count(), per_cu),
                                        default_splits(g.n_tiles, g.B * g.Hkv, cu_count(), per_cu));

@@ -138,6 +138,6 @@ bool decode_supported(int k_mode, int R, int k_bits, int k_group, int v_bits, in
 // `start` and `stop` around the kernel itself (hipExtLaunchKernelGGL); disarm drops an unused pair.
 void arm_launch_events(hipEvent_t start, hipEvent_t stop);
 void disarm_launch_events();
-int decode_wgs_per_cu(int k_mode, int G, int v_bits);  // resident decode workgroups per CU the split heuristic aims for
+int decode_wgs_per_cu(int k_mode, int G, int v_bits, int k_group);  // resident decode workgroups per CU the split heuristic aims for
 
 }  // namespace bgtq

@@ -592,6 +592,28 @@ __device__ __forceinline__ PrepIn<G> prep_load(const void* q, int dtype, const u
     return in;
 }
 
+// Keys stored rotated (y = H (s * k) / 16): the query goes to H (s * q) / 8, so q'.y = q.k.  A
+// wave holds coordinates 2 lane + e (q0: e = 0, q1: e = 1); stage 1 pairs them inside the lane,
+// stages 2..64 pair lane with lane ^ m (m = 1..32): the lower lane keeps a + b, the upper one a - b.
+template <int G>
+__device__ __forceinline__ void rotate_query(float (&q0)[G], float (&q1)[G], const uint8_t* rot, int lane) {
+    const uint32_t sbits = (uint32_t)rot[lane >> 2] >> (2 * (lane & 3));
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        const float a0 = (sbits & 1u) ? -q0[hh] : q0[hh], a1 = (sbits & 2u) ? -q1[hh] : q1[hh];
+        float u = a0 + a1, v = a0 - a1;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            const float pu = __shfl_xor(u, m, 64), pv = __shfl_xor(v, m, 64);
+            const bool upper = (lane & m) != 0;
+            u = upper ? pu - u : u + pu;
+            v = upper ? pv - v : v + pv;
+        }
+        q0[hh] = u * 0.125f;
+        q1[hh] = v * 0.125f;
+    }
+}
+
 template <int G, bool SORTED, int KG>
 __device__ void prep_store(const PrepIn<G>& in, int lane, float* qp, uint16_t* dsc16, uint32_t* nnz_pad, float* qs,
                            int3* order = nullptr, const uint8_t* rot = nullptr) {
@@ -615,26 +637,7 @@ __device__ void prep_store(const PrepIn<G>& in, int lane, float* qp, uint16_t* d
             q1[hh] = bf2f(in.r0[hh] >> 16);
         }
     }
-    if (rot) {
-        // keys stored rotated (y = H (s * k) / 16): the query goes to H (s * q) / 8, so q'.y = q.k.
-        // Coordinates 2 lane + e; stage 1 pairs them inside the lane, stages 2..64 pair lane
-        // with lane ^ m (m = 1..32): the lower lane keeps a + b, the upper one takes a - b.
-        const uint32_t sbits = (uint32_t)rot[lane >> 2] >> (2 * (lane & 3));
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const float a0 = (sbits & 1u) ? -q0[hh] : q0[hh], a1 = (sbits & 2u) ? -q1[hh] : q1[hh];
-            float u = a0 + a1, v = a0 - a1;
-#pragma unroll
-            for (int m = 1; m < 64; m <<= 1) {
-                const float pu = __shfl_xor(u, m, 64), pv = __shfl_xor(v, m, 64);
-                const bool upper = (lane & m) != 0;
-                u = upper ? pu - u : u + pu;
-                v = upper ? pv - v : v + pv;
-            }
-            q0[hh] = u * 0.125f;
-            q1[hh] = v * 0.125f;
-        }
-    }
+    if (rot) rotate_query<G>(q0, q1, rot, lane);
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
         q0[hh] *= kLog2eOverSqrtD;
@@ -1414,6 +1417,329 @@ __global__ __launch_bounds__(256, mx_wgs_per_cu<VB>()) void k_decode_mx(const De
         zs[hh] = row_sum16(zs[hh]);
     }
     __syncthreads();  // every wave is done with its stages
+    float* s_red = (float*)(lds + LD::RED);
+    float* r = s_red + wave * G * PART;
+    if (col < G) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) *(f32x4_t*)(r + col * PART + 16 * db + 4 * row) = o[db];
+    }
+    if (col == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int hd = 2 * row + hh;
+            if (hd < G) {
+                r[hd * PART + 128] = m[hh];
+                r[hd * PART + 129] = l[hh];
+                r[hd * PART + 130] = zs[hh];
+            }
+        }
+    }
+    __syncthreads();
+    float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_parts * PART;
+    merge_waves4<G>(s_red, s_red + 4 * G * PART, part, a.n_parts, split);
+}
+
+// Matrix-core decode over affine 4-bit keys in groups of 32 dims (the "Quantize What Counts" K4V2
+// configuration), for 4 or 8 query heads per kv head.  k-step ks of q·k is key group ks: a lane's
+// B operand is one record dword (dims 32 ks + 8u .. 8u + 7 of its token, nibble i at bits 4i),
+// turned into fp16 by OR-ing the nibble pairs (i, i + 4) into 1024 + n and one packed fp16
+// subtraction of 1024, both exact; the A operand holds the query in the matching order (dims
+// 32 ks + 8u + {0, 4, 1, 5, 2, 6, 3, 7}), split into fp16 high and low parts.  Each k-step's
+// product takes its group's scale and zero: z += scale * (q'.codes) + zero * sum(q' over the
+// group).  Softmax, P·V (codebook or affine values) and the wave merge are those of k_decode_mx;
+// keys need no windows or tables.
+template <int G, int VB> struct MxaLds {
+    static constexpr int VLUT = 0;
+    static constexpr int WX = a16(VLUT + VLutGeom<VB>::BYTES);    // u32 [4 waves][16 heads][32 pairs]
+    static constexpr int ALPHA = WX + 4 * 16 * 32 * 4;           // f32 [4 waves][16]
+    static constexpr int QSUM = ALPHA + 4 * 16 * 4;              // f32 [8 heads][4 groups]
+    static constexpr int QS = QSUM + 8 * 4 * 4;                  // f32 [8 heads][128]: the scaled query
+    static constexpr int SST = QS + 8 * 128 * 4;                 // per wave: V scales, V zeros (fp16 [2][64])
+    static constexpr int SST_W = 2 * 64 * 2;
+    static constexpr int RED = a16(SST + 4 * SST_W);              // epilogue: f32 [4 G PART + 4 G]
+    static constexpr int SIZE = RED + 4 * (4 * G * PART + 4 * G);
+};
+
+// Two resident workgroups per CU for every value width: the record dwords, group scales and query
+// operands held per lane need the registers.
+constexpr int kMxaWgsPerCu = 2;
+
+template <int G, int VB>
+__global__ __launch_bounds__(256, kMxaWgsPerCu) void k_decode_mxa(const DecodeArgs a) {
+    static_assert(G == 4 || G == 8, "matrix-core decode serves 4 or 8 query heads per kv head");
+    using LD = MxaLds<G, VB>;
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int row = lane >> 4, col = lane & 15;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LD::SIZE];
+    uint32_t* s_vlut = (uint32_t*)(lds + LD::VLUT);
+    float* s_alpha = (float*)(lds + LD::ALPHA) + wave * 16;
+    float* s_qsum = (float*)(lds + LD::QSUM);
+    float* s_q = (float*)(lds + LD::QS);
+    uint16_t* sst = (uint16_t*)(lds + LD::SST + wave * LD::SST_W);
+    uint32_t* wx = (uint32_t*)(lds + LD::WX) + wave * 16 * 32;
+
+    const size_t bh = (size_t)b * a.Hkv + h;
+    const int64_t n_packed = a.n_packed[b];
+    const int64_t n_tiles_b = (n_packed + TILE - 1) / TILE;
+    const int64_t t_lo = (int64_t)split * a.tiles_per_split;
+    const int64_t t_hi = t_lo + a.tiles_per_split < n_tiles_b ? t_lo + a.tiles_per_split : n_tiles_b;
+    const uint32_t* kc = (const uint32_t*)(a.k_codes + bh * a.n_tiles * a.k_tile_bytes);
+    const uint32_t* vc = (const uint32_t*)(a.v_codes + bh * a.n_tiles * a.v_tile_bytes);
+    const uint2* ksc = (const uint2*)(a.k_scale + bh * a.n_cap * 4);  // the 4 group scales of a token
+    const uint2* kzr = (const uint2*)(a.k_zero + bh * a.n_cap * 4);   // and its 4 group zeros
+    const uint32_t* vs32 = (const uint32_t*)(a.v_scale + bh * a.n_cap);  // fp16 pairs (token 2i, 2i + 1)
+    const uint32_t* vz32 = a.v_affine ? (const uint32_t*)(a.v_zero + bh * a.n_cap) : nullptr;
+    const bool vaff = a.v_affine != 0;
+
+    // Prologue: the query (wave 0), the value table and the first tile's keys go out first.
+    const PrepIn<G> pin = prep_load<G, false>(a.q, a.q_dtype, nullptr, nullptr, b, h, a.Hq, lane);
+    constexpr int VCOP = VLutGeom<VB>::COPIES, VENT = 1 << (2 * VB);
+    constexpr int VROUNDS = (VENT * VCOP + 255) / 256;
+    uint32_t vla[VROUNDS], vlb[VROUNDS];
+#pragma unroll
+    for (int k = 0; k < VROUNDS; ++k) {
+        const uint32_t e = ((threadIdx.x + 256u * k) / VCOP) & (VENT - 1);
+        vla[k] = c_cent16[cent_base(VB) + (e & ((1u << VB) - 1u))];
+        vlb[k] = c_cent16[cent_base(VB) + (e >> VB)];
+    }
+    // Tile data per lane: the record dword of k-step ks for token group g (kd[ks][g]), the group
+    // scales and zeros of its four tokens, and one dword of value scales (lanes 0..31, tokens 2l and
+    // 2l + 1) or value zeros (lanes 32..63); the value streams as in k_decode_mx.
+    uint32_t kd[4][4], vsd;
+    uint2 kss[4], kzz[4];
+    u32x4_t vn[VB], vx[VB];
+    auto fetch_k = [&](int64_t t) {
+        const uint32_t* kt = kc + t * (a.k_tile_bytes / 4);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) kd[ks][g] = kt[(4 * ks + row) * 64 + 16 * g + col];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            kss[g] = ksc[t * TILE + 16 * g + col];
+            kzz[g] = kzr[t * TILE + 16 * g + col];
+        }
+        vsd = lane < 32 ? vs32[t * (TILE / 2) + lane] : (vz32 ? vz32[t * (TILE / 2) + (lane & 31)] : 0u);
+    };
+    auto fetch_v = [&](u32x4_t (&dst)[VB], int64_t t) {
+        const u32x4_t* vt = (const u32x4_t*)(vc + t * (a.v_tile_bytes / 4));
+#pragma unroll
+        for (int c = 0; c < VB; ++c) dst[c] = vt[c * 64 + lane];
+    };
+    const int64_t t_first = t_lo + wave < t_hi ? t_lo + wave : (t_lo < a.n_tiles ? t_lo : 0);
+    fetch_k(t_first);
+
+#pragma unroll
+    for (int k = 0; k < VROUNDS; ++k) {
+        const uint32_t i = threadIdx.x + 256u * k;
+        const uint32_t e = (i / VCOP) & (VENT - 1);
+        if (i < (uint32_t)(VENT * VCOP))
+            s_vlut[i] = a.v_affine ? (uint32_t)f2h((float)(e & ((1u << VB) - 1u))) | ((uint32_t)f2h((float)(e >> VB)) << 16)
+                                   : vla[k] | (vlb[k] << 16);
+    }
+#pragma unroll
+    for (int i = threadIdx.x; i < 4 * 16 * 32 / 4; i += 256) ((u32x4_t*)(lds + LD::WX))[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (wave == 0) {
+        // lane = RoPE block: q' = (rotated) q * log2(e)/sqrt(d) of heads 0..G-1 to LDS, then the
+        // per-group sums of q' (lanes 0 .. 4G-1: head lane / 4, group lane % 4)
+        float q0[G], q1[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            if (pin.dtype == BGTQ_F32) {
+                q0[hh] = __builtin_bit_cast(float, pin.r0[hh]);
+                q1[hh] = __builtin_bit_cast(float, pin.r1[hh]);
+            } else if (pin.dtype == BGTQ_F16) {
+                q0[hh] = h2f(pin.r0[hh] & 0xFFFFu);
+                q1[hh] = h2f(pin.r0[hh] >> 16);
+            } else {
+                q0[hh] = bf2f(pin.r0[hh] & 0xFFFFu);
+                q1[hh] = bf2f(pin.r0[hh] >> 16);
+            }
+        }
+        if (a.k_rot) rotate_query<G>(q0, q1, a.k_rot + h * 16, lane);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            s_q[hh * 128 + 2 * lane] = q0[hh] * kLog2eOverSqrtD;
+            s_q[hh * 128 + 2 * lane + 1] = q1[hh] * kLog2eOverSqrtD;
+        }
+        wave_lds_fence();
+        if (lane < 4 * G) {
+            const float* qg = s_q + (lane >> 2) * 128 + 32 * (lane & 3);
+            float acc = 0.f;
+            for (int j = 0; j < 32; ++j) acc += qg[j];
+            s_qsum[lane] = acc;
+        }
+    }
+    __syncthreads();
+    // A operands: lane = A row col (head 2 (col / 4) + (col / 2) % 2; fp16 high part for col even,
+    // low part for col odd), lane row u = row: dims 32 ks + 8 row + {j, j + 4} in dword j
+    u32x4_t qa[4];
+    float qsg[2][4];
+    {
+        const int qh = 2 * (col >> 2) + ((col >> 1) & 1), lo_part = col & 1;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            uint32_t hv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t e2[2];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const float qv = qh < G ? s_q[qh * 128 + 32 * ks + 8 * row + j + 4 * c] : 0.f;
+                    const _Float16 hi = (_Float16)qv;
+                    const _Float16 lo = (_Float16)(qv - (float)hi);
+                    e2[c] = (uint32_t)__builtin_bit_cast(uint16_t, lo_part ? lo : hi);
+                }
+                hv[j] = e2[0] | (e2[1] << 16);
+            }
+            qa[ks] = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) qsg[hh][ks] = 2 * row + hh < G ? s_qsum[(2 * row + hh) * 4 + ks] : 0.f;
+    }
+    fetch_v(vn, t_first);
+
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, zs[2] = {0.f, 0.f};
+    f32x4_t o[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const uint32_t lcopy = 4u * ((uint32_t)lane & (VLutGeom<VB>::COPIES - 1));
+    const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+
+    constexpr bool VDB = VB <= 3;
+    auto tile = [&](const int64_t t, u32x4_t (&vcur)[VB], u32x4_t (&vnext)[VB]) __attribute__((always_inline)) {
+        // value scales / zeros to LDS (transposed: token u at (u % 16) * 4 + u / 16)
+        wave_lds_fence();
+        {
+            const int u0 = 2 * (lane & 31), reg = lane < 32 ? 0 : 64;
+            sst[reg + (u0 & 15) * 4 + (u0 >> 4)] = (uint16_t)(vsd & 0xFFFFu);
+            sst[reg + ((u0 + 1) & 15) * 4 + ((u0 + 1) >> 4)] = (uint16_t)(vsd >> 16);
+        }
+        // q·k on the matrix cores, one key group per k-step
+        float z[4][2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) z[g][0] = z[g][1] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const half8_t q = __builtin_bit_cast(half8_t, qa[ks]);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t x = kd[ks][g];
+                uint32_t e[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t pair = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;  // (1024 + n_j, 1024 + n_j+4)
+                    e[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pair) - k1024);
+                }
+                const f32x4_t d = mfma16(q, as_h8(e[0], e[1], e[2], e[3]), f32x4_t{0.f, 0.f, 0.f, 0.f});
+                const uint32_t sw = ks < 2 ? kss[g].x : kss[g].y, zw = ks < 2 ? kzz[g].x : kzz[g].y;
+                const float sc = h2f((ks & 1) ? sw >> 16 : sw & 0xFFFFu), zr = h2f((ks & 1) ? zw >> 16 : zw & 0xFFFFu);
+                z[g][0] += sc * (d[0] + d[1]) + zr * qsg[0][ks];
+                z[g][1] += sc * (d[2] + d[3]) + zr * qsg[1][ks];
+            }
+        }
+        {
+            // the keys of this tile are consumed: the next tile's go out (a wave's last tile
+            // requests itself again, so that no branch joins the wait counts)
+            const int64_t tn = t + 4 < t_hi ? t + 4 : t;
+            fetch_k(tn);
+            if constexpr (VDB) fetch_v(vnext, tn);
+        }
+        wave_lds_fence();
+        float sv[4], sz[4] = {0.f, 0.f, 0.f, 0.f};
+        {
+            const uint2 v2 = *(const uint2*)(sst + col * 4);
+            sv[0] = h2f(v2.x & 0xFFFFu); sv[1] = h2f(v2.x >> 16); sv[2] = h2f(v2.y & 0xFFFFu); sv[3] = h2f(v2.y >> 16);
+            if (vaff) {
+                const uint2 z2 = *(const uint2*)(sst + 64 + col * 4);
+                sz[0] = h2f(z2.x & 0xFFFFu); sz[1] = h2f(z2.x >> 16); sz[2] = h2f(z2.y & 0xFFFFu); sz[3] = h2f(z2.y >> 16);
+            }
+        }
+        if ((t + 1) * TILE > n_packed) {  // the sequence ends inside this tile
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                if (t * TILE + 16 * g + col >= n_packed) {
+                    sv[g] = 0.f;
+                    sz[g] = 0.f;
+                    z[g][0] = z[g][1] = -INFINITY;
+                }
+            }
+        }
+        float tmax[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) tmax[hh] = vmax(vmax3(z[0][hh], z[1][hh], z[2][hh]), z[3][hh]);
+        if (t == t_lo + wave) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) m[hh] = row_max16(tmax[hh]);
+        } else if (__ballot(tmax[0] > m[0] || tmax[1] > m[1])) {
+            float alpha[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const float mn = vmax(m[hh], row_max16(tmax[hh]));
+                alpha[hh] = __builtin_amdgcn_exp2f(m[hh] - mn);
+                m[hh] = mn;
+                l[hh] *= alpha[hh];
+                zs[hh] *= alpha[hh];
+            }
+            wave_lds_fence();
+            if (col == 0) {
+                s_alpha[2 * row] = alpha[0];
+                s_alpha[2 * row + 1] = alpha[1];
+            }
+            wave_lds_fence();
+            const float al = s_alpha[col];
+#pragma unroll
+            for (int db = 0; db < 8; ++db) o[db] *= al;
+        }
+        uint16_t wh[4][2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const float p = __builtin_amdgcn_exp2f(z[g][hh] - m[hh]);
+                l[hh] += p;
+                if (vaff) zs[hh] += p * sz[g];
+                wh[g][hh] = f2h(p * sv[g]);
+            }
+        }
+        wave_lds_fence();
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            uint32_t* wr = wx + (2 * row + hh) * 32 + col;
+            wr[0] = (uint32_t)wh[0][hh] | ((uint32_t)wh[2][hh] << 16);
+            wr[16] = (uint32_t)wh[1][hh] | ((uint32_t)wh[3][hh] << 16);
+        }
+        wave_lds_fence();
+        uint32_t vs[4 * VB];
+#pragma unroll
+        for (int c = 0; c < VB; ++c) {
+            vs[4 * c] = vcur[c][0]; vs[4 * c + 1] = vcur[c][1]; vs[4 * c + 2] = vcur[c][2]; vs[4 * c + 3] = vcur[c][3];
+        }
+        mx_pv<VB, 0>(o, vs, s_vlut, wx, lane, lcopy);
+        mx_pv<VB, 1>(o, vs, s_vlut, wx, lane, lcopy);
+        if constexpr (!VDB) {
+            if (t + 4 < t_hi) fetch_v(vcur, t + 4);
+        }
+    };
+    if constexpr (VDB) {
+        for (int64_t t = t_lo + wave; t < t_hi; t += 8) {
+            tile(t, vn, vx);
+            if (t + 4 < t_hi) tile(t + 4, vx, vn);
+        }
+    } else {
+        for (int64_t t = t_lo + wave; t < t_hi; t += 4) tile(t, vn, vn);
+    }
+
+    // Epilogue: row sums of l and the zero term, O^T to LDS, merge the waves.
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        l[hh] = row_sum16(l[hh]);
+        zs[hh] = row_sum16(zs[hh]);
+    }
+    __syncthreads();
     float* s_red = (float*)(lds + LD::RED);
     float* r = s_red + wave * G * PART;
     if (col < G) {
@@ -2234,6 +2560,10 @@ static hipError_t launch_dec_mx(const DecodeArgs& a, int B, hipStream_t s) {
 template <int G, int VB>
 static hipError_t launch_dec_gv(const DecodeArgs& a, int B, int k_mode, int R, hipStream_t s) {
     if (k_mode == BGTQ_K_AFFINE) {
+        if constexpr (G >= 4) {
+            if (a.k_group == 32)
+                return launch_main(k_decode_mxa<G, VB>, dim3(a.n_splits, a.Hkv, B), dim3(256), s, a);
+        }
         switch (a.k_group) {
             case 32: return launch_dec<G, 16, VB, 32>(a, B, s);
             case 64: return launch_dec<G, 16, VB, 64>(a, B, s);
@@ -2288,8 +2618,9 @@ void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
 }
 void disarm_launch_events() { t_ev_start = t_ev_stop = nullptr; }
 
-int decode_wgs_per_cu(int k_mode, int G, int v_bits) {
-    if (k_mode == BGTQ_K_BLOCKGTQ && G >= 4) return v_bits == 3 ? mx_wgs_per_cu<3>() : mx_wgs_per_cu<2>();
+int decode_wgs_per_cu(int k_mode, int G, int v_bits, int k_group) {
+    if (G >= 4 && k_mode == BGTQ_K_BLOCKGTQ) return v_bits == 3 ? mx_wgs_per_cu<3>() : mx_wgs_per_cu<2>();
+    if (G >= 4 && k_mode == BGTQ_K_AFFINE && k_group == 32) return kMxaWgsPerCu;
     return 2;
 }
 

@@ -104,7 +104,11 @@ hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t) 
 void arm_launch_events(hipEvent_t, hipEvent_t) {}
 void disarm_launch_events() {}
 
-int decode_wgs_per_cu(int k_mode, int G, int v_bits) { return (k_mode == BGTQ_K_BLOCKGTQ && G >= 4) ? (v_bits == 3 ? 2 : 3) : 2; }
+int decode_wgs_per_cu(int k_mode, int G, int v_bits, int k_group) {
+    if (G >= 4 && k_mode == BGTQ_K_BLOCKGTQ) return v_bits == 3 ? 2 : 3;
+    (void)k_group;
+    return 2;
+}
 
 bool decode_supported(int k_mode, int R, int k_bits, int k_group, int v_bits, int G) {
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return false;
