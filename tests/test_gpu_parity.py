@@ -55,6 +55,11 @@ CASES = {
     # and 4 query heads per kv head with 12-dword records and 3-bit values
     "w2_k4v4": (2, {"L": 1, "v_bits": 4, "k_budget_units": 256}, 1500 + 3, (None,)),
     "w3_k3v3": (3, {"L": 1, "B": 1, "v_bits": 3, "k_budget_units": 192}, 1000 + 9, (700, None)),
+    # affine group-32 keys on the matrix cores at 8 query heads per kv head, with affine values and
+    # with codebook values; affine groups of 64 (the vector kernel at 4 heads per kv head)
+    "w4_g8": (4, {"L": 1, "B": 1, "Hq": 16, "Hkv": 2}, 777, (None,)),
+    "w4_g8_codebook_v3": (4, {"L": 1, "B": 1, "Hq": 16, "Hkv": 2, "v_mode": "codebook", "v_bits": 3}, 1000 + 3, (None,)),
+    "w4_group64": (4, {"L": 1, "B": 1, "k_group": 64}, 600 + 1, (None,)),
 }
 
 
