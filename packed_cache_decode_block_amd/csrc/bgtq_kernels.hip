@@ -1439,14 +1439,15 @@ __global__ __launch_bounds__(256, mx_wgs_per_cu<VB>()) void k_decode_mx(const De
     merge_waves4<G>(s_red, s_red + 4 * G * PART, part, a.n_parts, split);
 }
 
-// Matrix-core decode over affine 4-bit keys in groups of 32 dims (the "Quantize What Counts" K4V2
-// configuration), for 4 or 8 query heads per kv head.  k-step ks of q·k is key group ks: a lane's
-// B operand is one record dword (dims 32 ks + 8u .. 8u + 7 of its token, nibble i at bits 4i),
+// Matrix-core decode over affine 4-bit keys in groups of KG = 32, 64 or 128 dims (the "Quantize
+// What Counts" K4V2 configuration uses 32), for 4 or 8 query heads per kv head.  A key group spans
+// KG / 32 k-steps of q·k: a lane's B operand is one record dword (dims 32 ks + 8u .. 8u + 7 of
+// its token, nibble i at bits 4i),
 // turned into fp16 by OR-ing the nibble pairs (i, i + 4) into 1024 + n and one packed fp16
 // subtraction of 1024, both exact; the A operand holds the query in the matching order (dims
-// 32 ks + 8u + {0, 4, 1, 5, 2, 6, 3, 7}), split into fp16 high and low parts.  Each k-step's
-// product takes its group's scale and zero: z += scale * (q'.codes) + zero * sum(q' over the
-// group).  Softmax, P·V (codebook or affine values) and the wave merge are those of k_decode_mx;
+// 32 ks + 8u + {0, 4, 1, 5, 2, 6, 3, 7}), split into fp16 high and low parts.  The products of a
+// group's k-steps accumulate on the matrix cores, then take the group's scale and zero:
+// z += scale * (q'.codes) + zero * sum(q' over the group).  Softmax, P·V (codebook or affine values) and the wave merge are those of k_decode_mx;
 // keys need no windows or tables.
 template <int G, int VB> struct MxaLds {
     static constexpr int VLUT = 0;
@@ -1464,9 +1465,11 @@ template <int G, int VB> struct MxaLds {
 // operands held per lane need the registers.
 constexpr int kMxaWgsPerCu = 2;
 
-template <int G, int VB>
+template <int G, int VB, int KG>
 __global__ __launch_bounds__(256, kMxaWgsPerCu) void k_decode_mxa(const DecodeArgs a) {
     static_assert(G == 4 || G == 8, "matrix-core decode serves 4 or 8 query heads per kv head");
+    static_assert(KG == 32 || KG == 64 || KG == 128, "key groups of 32, 64 or 128 dims");
+    constexpr int NG = D / KG, KPG = KG / 32;  // key groups; k-steps per group
     using LD = MxaLds<G, VB>;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1486,8 +1489,8 @@ __global__ __launch_bounds__(256, kMxaWgsPerCu) void k_decode_mxa(const DecodeAr
     const int64_t t_hi = t_lo + a.tiles_per_split < n_tiles_b ? t_lo + a.tiles_per_split : n_tiles_b;
     const uint32_t* kc = (const uint32_t*)(a.k_codes + bh * a.n_tiles * a.k_tile_bytes);
     const uint32_t* vc = (const uint32_t*)(a.v_codes + bh * a.n_tiles * a.v_tile_bytes);
-    const uint2* ksc = (const uint2*)(a.k_scale + bh * a.n_cap * 4);  // the 4 group scales of a token
-    const uint2* kzr = (const uint2*)(a.k_zero + bh * a.n_cap * 4);   // and its 4 group zeros
+    const uint16_t* ksc = a.k_scale + bh * a.n_cap * NG;  // the NG group scales of a token
+    const uint16_t* kzr = a.k_zero + bh * a.n_cap * NG;   // and its NG group zeros
     const uint32_t* vs32 = (const uint32_t*)(a.v_scale + bh * a.n_cap);  // fp16 pairs (token 2i, 2i + 1)
     const uint32_t* vz32 = a.v_affine ? (const uint32_t*)(a.v_zero + bh * a.n_cap) : nullptr;
     const bool vaff = a.v_affine != 0;
@@ -1507,7 +1510,7 @@ __global__ __launch_bounds__(256, kMxaWgsPerCu) void k_decode_mxa(const DecodeAr
     // scales and zeros of its four tokens, and one dword of value scales (lanes 0..31, tokens 2l and
     // 2l + 1) or value zeros (lanes 32..63); the value streams as in k_decode_mx.
     uint32_t kd[4][4], vsd;
-    uint2 kss[4], kzz[4];
+    float kss[4][NG], kzz[4][NG];  // [token group][key group]
     u32x4_t vn[VB], vx[VB];
     auto fetch_k = [&](int64_t t) {
         const uint32_t* kt = kc + t * (a.k_tile_bytes / 4);
@@ -1517,8 +1520,21 @@ __global__ __launch_bounds__(256, kMxaWgsPerCu) void k_decode_mxa(const DecodeAr
             for (int g = 0; g < 4; ++g) kd[ks][g] = kt[(4 * ks + row) * 64 + 16 * g + col];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            kss[g] = ksc[t * TILE + 16 * g + col];
-            kzz[g] = kzr[t * TILE + 16 * g + col];
+            const int64_t tok = t * TILE + 16 * g + col;
+            if constexpr (NG == 4) {
+                const uint2 sw = *(const uint2*)(ksc + tok * 4), zw = *(const uint2*)(kzr + tok * 4);
+                kss[g][0] = h2f(sw.x & 0xFFFFu); kss[g][1] = h2f(sw.x >> 16);
+                kss[g][2] = h2f(sw.y & 0xFFFFu); kss[g][3] = h2f(sw.y >> 16);
+                kzz[g][0] = h2f(zw.x & 0xFFFFu); kzz[g][1] = h2f(zw.x >> 16);
+                kzz[g][2] = h2f(zw.y & 0xFFFFu); kzz[g][3] = h2f(zw.y >> 16);
+            } else if constexpr (NG == 2) {
+                const uint32_t sw = *(const uint32_t*)(ksc + tok * 2), zw = *(const uint32_t*)(kzr + tok * 2);
+                kss[g][0] = h2f(sw & 0xFFFFu); kss[g][1] = h2f(sw >> 16);
+                kzz[g][0] = h2f(zw & 0xFFFFu); kzz[g][1] = h2f(zw >> 16);
+            } else {
+                kss[g][0] = h2f(ksc[tok]);
+                kzz[g][0] = h2f(kzr[tok]);
+            }
         }
         vsd = lane < 32 ? vs32[t * (TILE / 2) + lane] : (vz32 ? vz32[t * (TILE / 2) + (lane & 31)] : 0u);
     };
@@ -1564,10 +1580,10 @@ __global__ __launch_bounds__(256, kMxaWgsPerCu) void k_decode_mxa(const DecodeAr
             s_q[hh * 128 + 2 * lane + 1] = q1[hh] * kLog2eOverSqrtD;
         }
         wave_lds_fence();
-        if (lane < 4 * G) {
-            const float* qg = s_q + (lane >> 2) * 128 + 32 * (lane & 3);
+        if (lane < NG * G) {
+            const float* qg = s_q + (lane / NG) * 128 + KG * (lane % NG);
             float acc = 0.f;
-            for (int j = 0; j < 32; ++j) acc += qg[j];
+            for (int j = 0; j < KG; ++j) acc += qg[j];
             s_qsum[lane] = acc;
         }
     }
@@ -1575,7 +1591,7 @@ __global__ __launch_bounds__(256, kMxaWgsPerCu) void k_decode_mxa(const DecodeAr
     // A operands: lane = A row col (head 2 (col / 4) + (col / 2) % 2; fp16 high part for col even,
     // low part for col odd), lane row u = row: dims 32 ks + 8 row + {j, j + 4} in dword j
     u32x4_t qa[4];
-    float qsg[2][4];
+    float qsg[2][NG];
     {
         const int qh = 2 * (col >> 2) + ((col >> 1) & 1), lo_part = col & 1;
 #pragma unroll
@@ -1598,7 +1614,7 @@ __global__ __launch_bounds__(256, kMxaWgsPerCu) void k_decode_mxa(const DecodeAr
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) qsg[hh][ks] = 2 * row + hh < G ? s_qsum[(2 * row + hh) * 4 + ks] : 0.f;
+            for (int gi = 0; gi < NG; ++gi) qsg[hh][gi] = 2 * row + hh < G ? s_qsum[(2 * row + hh) * NG + gi] : 0.f;
     }
     fetch_v(vn, t_first);
 
@@ -1618,27 +1634,30 @@ __global__ __launch_bounds__(256, kMxaWgsPerCu) void k_decode_mxa(const DecodeAr
             sst[reg + (u0 & 15) * 4 + (u0 >> 4)] = (uint16_t)(vsd & 0xFFFFu);
             sst[reg + ((u0 + 1) & 15) * 4 + ((u0 + 1) >> 4)] = (uint16_t)(vsd >> 16);
         }
-        // q·k on the matrix cores, one key group per k-step
+        // q·k on the matrix cores: the k-steps of a key group accumulate, then the group's scale
+        // and zero apply
         float z[4][2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) z[g][0] = z[g][1] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const half8_t q = __builtin_bit_cast(half8_t, qa[ks]);
+        for (int gi = 0; gi < NG; ++gi) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const uint32_t x = kd[ks][g];
-                uint32_t e[4];
+                f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t pair = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;  // (1024 + n_j, 1024 + n_j+4)
-                    e[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pair) - k1024);
+                for (int kk = 0; kk < KPG; ++kk) {
+                    const int ks = gi * KPG + kk;
+                    const uint32_t x = kd[ks][g];
+                    uint32_t e[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t pair = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;  // (1024 + n_j, 1024 + n_j+4)
+                        e[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pair) - k1024);
+                    }
+                    d = mfma16(__builtin_bit_cast(half8_t, qa[ks]), as_h8(e[0], e[1], e[2], e[3]), d);
                 }
-                const f32x4_t d = mfma16(q, as_h8(e[0], e[1], e[2], e[3]), f32x4_t{0.f, 0.f, 0.f, 0.f});
-                const uint32_t sw = ks < 2 ? kss[g].x : kss[g].y, zw = ks < 2 ? kzz[g].x : kzz[g].y;
-                const float sc = h2f((ks & 1) ? sw >> 16 : sw & 0xFFFFu), zr = h2f((ks & 1) ? zw >> 16 : zw & 0xFFFFu);
-                z[g][0] += sc * (d[0] + d[1]) + zr * qsg[0][ks];
-                z[g][1] += sc * (d[2] + d[3]) + zr * qsg[1][ks];
+                z[g][0] += kss[g][gi] * (d[0] + d[1]) + kzz[g][gi] * qsg[0][gi];
+                z[g][1] += kss[g][gi] * (d[2] + d[3]) + kzz[g][gi] * qsg[1][gi];
             }
         }
         {
@@ -2561,8 +2580,12 @@ template <int G, int VB>
 static hipError_t launch_dec_gv(const DecodeArgs& a, int B, int k_mode, int R, hipStream_t s) {
     if (k_mode == BGTQ_K_AFFINE) {
         if constexpr (G >= 4) {
-            if (a.k_group == 32)
-                return launch_main(k_decode_mxa<G, VB>, dim3(a.n_splits, a.Hkv, B), dim3(256), s, a);
+            const dim3 grid(a.n_splits, a.Hkv, B);
+            switch (a.k_group) {
+                case 32: return launch_main(k_decode_mxa<G, VB, 32>, grid, dim3(256), s, a);
+                case 64: return launch_main(k_decode_mxa<G, VB, 64>, grid, dim3(256), s, a);
+                case 128: return launch_main(k_decode_mxa<G, VB, 128>, grid, dim3(256), s, a);
+            }
         }
         switch (a.k_group) {
             case 32: return launch_dec<G, 16, VB, 32>(a, B, s);
@@ -2620,7 +2643,7 @@ void disarm_launch_events() { t_ev_start = t_ev_stop = nullptr; }
 
 int decode_wgs_per_cu(int k_mode, int G, int v_bits, int k_group) {
     if (G >= 4 && k_mode == BGTQ_K_BLOCKGTQ) return v_bits == 3 ? mx_wgs_per_cu<3>() : mx_wgs_per_cu<2>();
-    if (G >= 4 && k_mode == BGTQ_K_AFFINE && k_group == 32) return kMxaWgsPerCu;
+    if (G >= 4 && k_mode == BGTQ_K_AFFINE && (k_group == 32 || k_group == 64 || k_group == 128)) return kMxaWgsPerCu;
     return 2;
 }
 

@@ -55,11 +55,14 @@ CASES = {
     # and 4 query heads per kv head with 12-dword records and 3-bit values
     "w2_k4v4": (2, {"L": 1, "v_bits": 4, "k_budget_units": 256}, 1500 + 3, (None,)),
     "w3_k3v3": (3, {"L": 1, "B": 1, "v_bits": 3, "k_budget_units": 192}, 1000 + 9, (700, None)),
-    # affine group-32 keys on the matrix cores at 8 query heads per kv head, with affine values and
-    # with codebook values; affine groups of 64 (the vector kernel at 4 heads per kv head)
+    # affine keys on the matrix cores: groups of 32 at 8 query heads per kv head with affine and with
+    # codebook values; groups of 64 and 128 (k-steps accumulate within a group); groups of 64 at 2
+    # query heads per kv head (the vector kernel)
     "w4_g8": (4, {"L": 1, "B": 1, "Hq": 16, "Hkv": 2}, 777, (None,)),
     "w4_g8_codebook_v3": (4, {"L": 1, "B": 1, "Hq": 16, "Hkv": 2, "v_mode": "codebook", "v_bits": 3}, 1000 + 3, (None,)),
     "w4_group64": (4, {"L": 1, "B": 1, "k_group": 64}, 600 + 1, (None,)),
+    "w4_group128_g8": (4, {"L": 1, "B": 1, "k_group": 128, "Hq": 16, "Hkv": 2}, 500 + 7, (None,)),
+    "w4_group64_g2_vector": (4, {"L": 1, "B": 1, "k_group": 64, "Hq": 4, "Hkv": 2}, 300 + 9, (None,)),
 }
 
 
