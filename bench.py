@@ -203,6 +203,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--no-step", action="store_true", help="skip the append-then-attend decode step timing")
     ap.add_argument("--k-rotation", action="store_true",
                     help="affine keys stored under the randomized Hadamard rotation (affine-key workloads)")
     ap.add_argument("--uniform-keys", action="store_true",
@@ -318,6 +319,35 @@ def main():
                                      "tokens_per_launch": w.B * w.Hkv * n_pk, "bytes_per_launch": qbytes,
                                      "GB/s": round(qbytes / (q_ms * 1e-3) / 1e9, 1)}
         log(f"[bench] quantize-append {q_ms * 1e3:.1f} us per layer -> {qbytes / (q_ms * 1e-3) / 1e9:.0f} GB/s")
+    if not args.no_step:
+        # One decode step per layer: append one token per sequence, then attend over the grown
+        # context (bgtq_decode_step), replayed from a HIP graph like the decode-only step.  The
+        # step re-appends position N - 1 (the lengths are set back by one before capture), so the
+        # attended context is the same N tokens; every replay rewrites that slot.  (With an fp16
+        # window the slot the step evicts from already holds the newest row: other bytes, the
+        # same work.)
+        cache.n_tokens -= 1
+        gen = torch.Generator(device="cuda").manual_seed(11)
+        td = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        kn = [torch.randn((w.B, 1, w.Hkv, w.d), generator=gen, device="cuda").to(td) for _ in range(w.L)]
+        vn = [torch.randn((w.B, 1, w.Hkv, w.d), generator=gen, device="cuda").to(td) for _ in range(w.L)]
+        qd = [x.to(td) for x in qs]
+
+        def step_append():
+            for layer in range(w.L):
+                cache.decode_step(layer, kn[layer], vn[layer], qd[layer], outs[layer], n_splits=args.n_splits, ws=ws)
+
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gs):
+            step_append()
+        sec_s = timed(gs.replay, args.steps, args.warmup)
+        result["decode_step"] = {
+            "entry": "bgtq_decode_step", "tokens_appended_per_sequence": 1, "ms_per_step": round(sec_s * 1e3, 4),
+            "us_per_layer": round(sec_s * 1e6 / w.L, 2),
+            "append_us_per_layer": round((sec_s - sec) * 1e6 / w.L, 2)}
+        log(f"[bench] decode step (append 1 token + attend) {sec_s * 1e3:.3f} ms, "
+            f"{sec_s * 1e6 / w.L:.2f} us per layer ({(sec_s - sec) * 1e6 / w.L:.2f} us for the append)")
+        del gs
     del ws
     if not args.no_fp16:
         del cache

@@ -218,6 +218,22 @@ int64_t bgtq_decode_workspace_bytes(const bgtq_cache *c, int n_splits);
 int bgtq_decode_attention(const bgtq_cache *c, int layer, const void *q, int dtype, float *out,
                           void *ws, size_t ws_bytes, int n_splits, void *stream);
 
+/*
+ * One decode step: quantize-append then attend, in one call (device, asynchronous).  The fusion of
+ * the append into the attention step is the operator fusion LogQuant names as future work
+ * (LogQuant summary, Conclusion); the packed path it serves is the one above (review §1
+ * Packed-Cache).  Appends k, v (as bgtq_quantize_append: n_new rows per sequence, same strides
+ * convention) and then computes bgtq_decode_attention for q over the grown context, all on
+ * `stream`; k, v and q share `dtype`.  The result equals the two calls made in turn.
+ * Both halves are validated against the post-append lengths before anything is enqueued: an
+ * error other than BGTQ_E_HIP leaves the cache and n_tokens untouched.  BGTQ_E_HIP from the
+ * attention half is reported after the append was enqueued (n_tokens then includes the new rows).
+ * ws, ws_bytes, n_splits and out as bgtq_decode_attention.  Errors: those of the two calls.
+ */
+int bgtq_decode_step(bgtq_cache *c, int layer, const void *k, const void *v, const void *q,
+                     int dtype, int64_t n_new, const int64_t *strides, float *out, void *ws,
+                     size_t ws_bytes, int n_splits, void *stream);
+
 /* Workspace bytes for bgtq_fp16_decode_attention. */
 int64_t bgtq_fp16_decode_workspace_bytes(int64_t N, int B, int Hq, int Hkv, int n_splits);
 

@@ -159,17 +159,36 @@ class PackedCache:
         self.sigma[layer].copy_(torch.from_numpy(np.ascontiguousarray(sigma, np.float32)))
         self.inv_sigma[layer].copy_(torch.from_numpy(np.ascontiguousarray(inv_sigma, np.float32)))
 
-    def quantize_append(self, layer: int, k, v, stream=None):
-        """Append rows k, v [B, n_new, Hkv, 128] (any strides in B/token/head, dim contiguous)."""
+    @staticmethod
+    def _kv_strides(k, v):
         if not (k.is_cuda and v.is_cuda):
             raise ValueError("k and v must be on the GPU")
         if k.shape != v.shape or k.dtype != v.dtype or k.stride() != v.stride():
             raise ValueError("k and v must have the same shape, dtype and strides")
-        if k.stride(-1) != 1:
-            raise ValueError("head_dim must be contiguous")
-        strides = (C.c_int64 * 3)(k.stride(0), k.stride(1), k.stride(2))
+        if k.dim() != 4 or k.stride(-1) != 1:
+            raise ValueError("k and v must be [B, n_new, Hkv, 128] with head_dim contiguous")
+        return (C.c_int64 * 3)(k.stride(0), k.stride(1), k.stride(2))
+
+    def quantize_append(self, layer: int, k, v, stream=None):
+        """Append rows k, v [B, n_new, Hkv, 128] (any strides in B/token/head, dim contiguous)."""
+        strides = self._kv_strides(k, v)
         check(lib.bgtq_quantize_append(C.byref(self.desc), layer, _ptr(k), _ptr(v), _dtype_code(k), k.shape[1],
                                        strides, _stream(stream)))
+
+    def decode_step(self, layer: int, k, v, q, out=None, n_splits: int = 0, ws=None, stream=None):
+        """Append k, v [B, n_new, Hkv, 128], then attend q [B, Hq, 128] over the grown context -> fp32 out."""
+        torch = _torch()
+        strides = self._kv_strides(k, v)
+        _require_cuda(q)
+        if q.dtype != k.dtype:
+            raise ValueError("q, k and v must share a dtype")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if ws is None:
+            ws = self.workspace(n_splits, q.device)
+        check(lib.bgtq_decode_step(C.byref(self.desc), layer, _ptr(k), _ptr(v), _ptr(q), _dtype_code(q), k.shape[1],
+                                   strides, _ptr(out), _ptr(ws), ws.numel(), n_splits, _stream(stream)))
+        return out
 
     def workspace_bytes(self, n_splits: int = 0) -> int:
         return check(lib.bgtq_decode_workspace_bytes(C.byref(self.desc), n_splits))

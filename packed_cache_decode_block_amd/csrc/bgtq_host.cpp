@@ -346,8 +346,14 @@ int64_t bgtq_cache_bytes(const bgtq_cache* c, int which) {
     return fail(BGTQ_E_INVALID, "unknown buffer selector %d", which);
 }
 
-int bgtq_quantize_append(bgtq_cache* c, int layer, const void* k, const void* v, int dtype, int64_t n_new,
-                         const int64_t* strides, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Quantize-append body.  With dry_run the call validates and plans only: nothing is launched and
+// n_tokens is untouched, so a caller can check both halves of a combined step before either runs.
+int quantize_append_impl(bgtq_cache* c, int layer, const void* k, const void* v, int dtype, int64_t n_new,
+                         const int64_t* strides, void* stream, bool dry_run) {
     bgtq::Geometry g;
     int rc = geometry(c, g);
     if (rc) return rc;
@@ -382,7 +388,7 @@ int bgtq_quantize_append(bgtq_cache* c, int layer, const void* k, const void* v,
             return fail(BGTQ_E_CAPACITY, "sequence %d: %lld packed tokens exceed n_cap %lld", b,
                         (long long)packed_new[b], (long long)c->n_cap);
     }
-    if (n_new == 0) return ok();
+    if (n_new == 0 || dry_run) return ok();
     hipStream_t s = (hipStream_t)stream;
     const size_t bh = (size_t)g.B * g.Hkv;
     bgtq::QuantArgs q{};
@@ -479,6 +485,15 @@ int bgtq_quantize_append(bgtq_cache* c, int layer, const void* k, const void* v,
     return ok();
 }
 
+}  // namespace
+
+extern "C" {
+
+int bgtq_quantize_append(bgtq_cache* c, int layer, const void* k, const void* v, int dtype, int64_t n_new,
+                         const int64_t* strides, void* stream) {
+    return quantize_append_impl(c, layer, k, v, dtype, n_new, strides, stream, false);
+}
+
 int64_t bgtq_decode_workspace_bytes(const bgtq_cache* c, int n_splits) {
     bgtq::Geometry g;
     int rc = geometry(c, g);
@@ -492,8 +507,14 @@ int64_t bgtq_decode_workspace_bytes(const bgtq_cache* c, int n_splits) {
     return (int64_t)g.B * g.Hq * parts * PART * 4;
 }
 
-int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dtype, float* out, void* ws,
-                          size_t ws_bytes, int n_splits, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode body over the context lengths `lens` ([B]; the descriptor's n_tokens row, or the lengths a
+// pending append will leave).  With dry_run the call validates only and launches nothing.
+int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dtype, float* out, void* ws,
+                          size_t ws_bytes, int n_splits, void* stream, const int64_t* lens, bool dry_run) {
     bgtq::Geometry g;
     int rc = geometry(c, g);
     if (rc) return rc;
@@ -501,7 +522,7 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
     if (!q || !out || !ws) return fail(BGTQ_E_INVALID, "NULL q/out/ws");
     if (((uintptr_t)ws) & 255) return fail(BGTQ_E_INVALID, "workspace must be 256-byte aligned");
     if (!dtype_ok(dtype)) return fail(BGTQ_E_INVALID, "bad dtype");
-    if (!c->n_tokens) return fail(BGTQ_E_INVALID, "n_tokens is NULL");
+    if (!c->n_tokens || !lens) return fail(BGTQ_E_INVALID, "n_tokens is NULL");
     if (n_splits < 0) return fail(BGTQ_E_INVALID, "n_splits < 0");
     if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale) return fail(BGTQ_E_INVALID, "NULL cache buffer");
     if (c->k_mode == BGTQ_K_BLOCKGTQ && (!c->bits || !c->sigma))
@@ -512,7 +533,7 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
     if (!bgtq::decode_supported(c->k_mode, g.R, c->k_bits, c->k_group, c->v_bits, g.G))
         return fail(BGTQ_E_UNSUPPORTED, "no decode kernel for this format (k_mode %d, R %d, k_bits %d, k_group %d, "
                     "v_bits %d, g %d)", c->k_mode, g.R, c->k_bits, c->k_group, c->v_bits, g.G);
-    const int64_t* nt = c->n_tokens + (size_t)layer * c->B;
+    const int64_t* nt = lens;
     bgtq::DecodeArgs a{};
     int32_t n_rec[BGTQ_MAX_BATCH] = {};
     int64_t max_tiles = 0;
@@ -536,6 +557,7 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
     const size_t need = (size_t)g.B * g.Hq * parts * PART * 4;
     if (ws_bytes < need) return fail(BGTQ_E_INVALID, "workspace too small (%zu < %zu)", ws_bytes, need);
     (void)any_recent;
+    if (dry_run) return ok();
     hipStream_t s = (hipStream_t)stream;
     float* part = (float*)ws;
     hipError_t e;
@@ -596,6 +618,34 @@ int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dty
     e = bgtq::launch_combine(ca, g.B * g.Hq, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int bgtq_decode_attention(const bgtq_cache* c, int layer, const void* q, int dtype, float* out, void* ws,
+                          size_t ws_bytes, int n_splits, void* stream) {
+    if (c && c->n_tokens && layer >= 0 && layer < c->L && c->B >= 1)
+        return decode_attention_impl(c, layer, q, dtype, out, ws, ws_bytes, n_splits, stream,
+                                     c->n_tokens + (size_t)layer * c->B, false);
+    return decode_attention_impl(c, layer, q, dtype, out, ws, ws_bytes, n_splits, stream, nullptr, false);
+}
+
+int bgtq_decode_step(bgtq_cache* c, int layer, const void* k, const void* v, const void* q, int dtype,
+                     int64_t n_new, const int64_t* strides, float* out, void* ws, size_t ws_bytes, int n_splits,
+                     void* stream) {
+    // Both halves are validated against the post-append lengths before anything is enqueued.
+    int rc = quantize_append_impl(c, layer, k, v, dtype, n_new, strides, stream, true);
+    if (rc) return rc;
+    int64_t lens[BGTQ_MAX_BATCH];
+    const int64_t* nt = c->n_tokens + (size_t)layer * c->B;
+    for (int b = 0; b < c->B; ++b) lens[b] = nt[b] + n_new;
+    rc = decode_attention_impl(c, layer, q, dtype, out, ws, ws_bytes, n_splits, stream, lens, true);
+    if (rc) return rc;
+    rc = quantize_append_impl(c, layer, k, v, dtype, n_new, strides, stream, false);
+    if (rc) return rc;
+    return decode_attention_impl(c, layer, q, dtype, out, ws, ws_bytes, n_splits, stream, nt, false);
 }
 
 int64_t bgtq_fp16_decode_workspace_bytes(int64_t N, int B, int Hq, int Hkv, int n_splits) {

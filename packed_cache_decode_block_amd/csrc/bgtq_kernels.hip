@@ -31,6 +31,7 @@ namespace {
 constexpr int TILE = 64;
 constexpr int D = 128;
 constexpr int PART = 132;                       // floats per partial record: o[128], m, l
+constexpr int kAppendFewMax = 16;               // appends of at most this many positions per sequence take k_append
 constexpr float kLog2eOverSqrtD = 0.12751743074233076f;  // log2(e) / sqrt(128)
 
 __constant__ uint32_t c_cent32[BGTQ_CB_CENTROIDS] = BGTQ_CB_CENTROID_F32_INIT;
@@ -2484,6 +2485,222 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
     }
 }
 
+__device__ __forceinline__ float lane_f(float v, int i) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i));
+}
+
+// The per-token fp16 RMS scale of a row spread over the wave (lane i holds elements 2i, 2i+1 and
+// the block's 1/sigma r): the same IEEE steps as rms_scale16, u = x*r, u*u, summed in element
+// order, each term read across lanes so the sequential sum waits on no memory.
+__device__ __forceinline__ float wave_rms16(float x0, float x1, float r, bool use_r, uint16_t* s16) {
+#pragma clang fp contract(off)
+    const float u0 = use_r ? x0 * r : x0, u1 = use_r ? x1 * r : x1;
+    const float q0 = u0 * u0, q1 = u1 * u1;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        acc = acc + lane_f(q0, i);
+        acc = acc + lane_f(q1, i);
+    }
+    const float ms = acc / 128.0f;
+    const uint16_t h = f2h(sqrtf(ms));
+    *s16 = h;
+    return h2f(h);
+}
+
+// min and max of elements [j0, j0 + n) of a row spread over the wave, folded in element order
+// from element j0 (the order affine_group takes); j0 and n are wave-uniform, n even.
+__device__ __forceinline__ void wave_minmax(float x0, float x1, int j0, int n, float& mn, float& mx) {
+    mn = mx = lane_f(x0, j0 >> 1);
+    mx = fmaxf(mx, lane_f(x1, j0 >> 1));
+    mn = fminf(mn, lane_f(x1, j0 >> 1));
+    for (int i = (j0 >> 1) + 1; i < ((j0 + n) >> 1); ++i) {
+        const float a = lane_f(x0, i), c = lane_f(x1, i);
+        mn = fminf(mn, a);
+        mx = fmaxf(mx, a);
+        mn = fminf(mn, c);
+        mx = fmaxf(mx, c);
+    }
+}
+
+// Quantize-append of a few tokens: one workgroup (one wave) per (tile, kv head, sequence) takes
+// the tile's new tokens one after another, the whole wave on each token (lane i holds RoPE block i,
+// dims 2i and 2i+1), so one new token costs a few short chains instead of one lane's full
+// sequential pass.  Every float step is the one k_quant takes (rows convert to fp32 exactly from
+// all three activation formats): the same scale sum in the same order, the same threshold
+// products and searches, the same affine min/max order.  Key records and value streams
+// are assembled in LDS (atomicOr of each lane's fields) and written once; value dwords keep the
+// bits of other positions (read-modify-write; the tile belongs to this workgroup alone).
+__global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
+    const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const int64_t tile = a.tile0[b] + blockIdx.x;
+    const int64_t t0 = tile * TILE;
+    if (t0 >= a.pos_hi[b]) return;  // whole workgroup beyond this sequence's range
+    const int u_lo = a.pos_lo[b] > t0 ? (int)(a.pos_lo[b] - t0) : 0;
+    const int u_hi = a.pos_hi[b] - t0 < TILE ? (int)(a.pos_hi[b] - t0) : TILE;
+    __shared__ float s_thr[BGTQ_CB_THRESHOLDS];
+    __shared__ int s_wid[64];
+    __shared__ float s_r[64], s_sig[64];
+    __shared__ uint32_t s_rec[32];
+    __shared__ uint32_t s_vv[64 * 16], s_vm[64 * 16];  // value streams of the tile: bits and written mask
+    for (int i = lane; i < BGTQ_CB_THRESHOLDS; i += 64) s_thr[i] = __builtin_bit_cast(float, c_thr32[i]);
+    for (int i = lane; i < 64 * 16; i += 64) s_vv[i] = s_vm[i] = 0u;
+    if (lane < 32) s_rec[lane] = 0u;
+    const size_t bh = (size_t)b * a.Hkv + h;
+    const bool do_k = a.which & 1, do_v = (a.which >> 1) & 1;
+    const bool gtq = a.k_mode == BGTQ_K_BLOCKGTQ;
+    int w = 0, off = 0;  // this lane's block: width and bit offset in the key record
+    if (do_k && gtq) {
+        w = a.bits[h * 64 + lane] < 8 ? a.bits[h * 64 + lane] : 8;  // widths above 8 are invalid; clamp
+        s_wid[lane] = w;
+        s_r[lane] = a.inv_sigma[h * 64 + lane];
+        s_sig[lane] = a.sigma[h * 64 + lane];
+    }
+    __syncthreads();
+    if (do_k && gtq)  // slots in descending width, ties by block index: the fields stored before this one
+        for (int j = 0; j < 64; ++j) {
+            const int wj = s_wid[j];
+            off += (wj > w || (wj == w && j < lane)) ? 2 * wj : 0;
+        }
+    const int vb = a.v_bits;
+    for (int u = u_lo; u < u_hi; ++u) {
+        const int64_t pos = t0 + u;
+        int64_t row = pos - a.off[b];
+        if (a.mod_n) row %= a.mod_n;
+        const int64_t src = (int64_t)b * a.sB + row * a.sT + (int64_t)h * a.sH + 2 * lane;
+        // both rows' loads in flight together
+        const float kx0 = do_k ? load_act(a.src_k, src, a.dtype) : 0.f;
+        const float kx1 = do_k ? load_act(a.src_k, src + 1, a.dtype) : 0.f;
+        const float vx0 = do_v ? load_act(a.src_v, src, a.dtype) : 0.f;
+        const float vx1 = do_v ? load_act(a.src_v, src + 1, a.dtype) : 0.f;
+        for (int pass = 0; pass < 2; ++pass) {
+            if ((pass == 0 && !do_k) || (pass == 1 && !do_v)) continue;
+            const float x0 = pass == 0 ? kx0 : vx0, x1 = pass == 0 ? kx1 : vx1;
+            __syncthreads();  // the previous token or pass is done with the record and streams
+            if (pass == 0) {
+                uint32_t* kt = (uint32_t*)(a.k_codes + (bh * a.n_tiles + tile) * a.k_tile_bytes);
+                if (gtq) {
+                    uint16_t s16;
+                    const float S = wave_rms16(x0, x1, s_r[lane], true, &s16);
+                    if (w > 0) {
+                        float t;
+                        {
+#pragma clang fp contract(off)
+                            t = S * s_sig[lane];
+                        }
+                        const uint32_t f = tq_code(x0, t, w, s_thr) | (tq_code(x1, t, w, s_thr) << w);
+                        const int k = off >> 5, sh = off & 31;
+                        if (k < a.R) atomicOr(&s_rec[k], f << sh);
+                        if (sh + 2 * w > 32 && k + 1 < a.R) atomicOr(&s_rec[k + 1], f >> (32 - sh));
+                    }
+                    if (lane == 0) a.k_scale[bh * a.n_cap + pos] = s16;
+                } else {
+#pragma clang fp contract(off)
+                    const int kg = a.k_group, gi = (2 * lane) / kg, ng = D / kg;
+                    float mn = 0.f, mx = 0.f;
+                    for (int g2 = 0; g2 < ng; ++g2) {  // every group on every lane; keep this lane's
+                        float gmn, gmx;
+                        wave_minmax(x0, x1, g2 * kg, kg, gmn, gmx);
+                        if (g2 == gi) {
+                            mn = gmn;
+                            mx = gmx;
+                        }
+                    }
+                    const float scale = (mx - mn) / (float)((1 << a.k_bits) - 1);
+                    const uint16_t sc16 = f2h(scale), zz16 = f2h(mn);
+                    const float s32 = h2f(sc16), z32 = h2f(zz16), top = (float)((1 << a.k_bits) - 1);
+                    float c0 = 0.f, c1 = 0.f;
+                    if (s32 != 0.f) {
+                        c0 = fminf(fmaxf(rintf((x0 - z32) / s32), 0.f), top);
+                        c1 = fminf(fmaxf(rintf((x1 - z32) / s32), 0.f), top);
+                    }
+                    const int per = 32 / a.k_bits, sh = ((2 * lane) % per) * a.k_bits;
+                    atomicOr(&s_rec[(2 * lane) / per], ((uint32_t)c0 << sh) | ((uint32_t)c1 << (sh + a.k_bits)));
+                    if ((2 * lane) % kg == 0) {
+                        a.k_scale[(bh * a.n_cap + pos) * ng + gi] = sc16;
+                        a.k_zero[(bh * a.n_cap + pos) * ng + gi] = zz16;
+                    }
+                }
+                __syncthreads();
+                if (lane < a.R) {
+                    kt[lane * TILE + u] = s_rec[lane];
+                    s_rec[lane] = 0u;
+                }
+            } else {
+                uint32_t c0, c1;
+                uint16_t s16 = 0, z16 = 0;
+                if (a.v_mode == BGTQ_V_CODEBOOK) {
+                    const float S = wave_rms16(x0, x1, 1.f, false, &s16);
+                    c0 = c1 = 0u;
+                    for (int m = 0; m < (1 << vb) - 1; ++m) {
+                        float th;
+                        {
+#pragma clang fp contract(off)
+                            th = S * s_thr[thr_base(vb) + m];
+                        }
+                        c0 += x0 >= th ? 1u : 0u;
+                        c1 += x1 >= th ? 1u : 0u;
+                    }
+                } else {
+#pragma clang fp contract(off)
+                    float mn, mx;
+                    wave_minmax(x0, x1, 0, D, mn, mx);
+                    const float scale = (mx - mn) / (float)((1 << vb) - 1);
+                    s16 = f2h(scale);
+                    z16 = f2h(mn);
+                    const float s32 = h2f(s16), z32 = h2f(z16), top = (float)((1 << vb) - 1);
+                    float f0 = 0.f, f1 = 0.f;
+                    if (s32 != 0.f) {
+                        f0 = fminf(fmaxf(rintf((x0 - z32) / s32), 0.f), top);
+                        f1 = fminf(fmaxf(rintf((x1 - z32) / s32), 0.f), top);
+                    }
+                    c0 = (uint32_t)f0;
+                    c1 = (uint32_t)f1;
+                }
+                if (lane == 0) {
+                    a.v_scale[bh * a.n_cap + pos] = s16;
+                    if (a.v_mode == BGTQ_V_AFFINE) a.v_zero[bh * a.n_cap + pos] = z16;
+                }
+                // lane-stream position of (token u, dim): stream dd + 16*jj, pair field phi, the
+                // token's half of it chosen by u >= 32 (the layout k_quant assembles per stream)
+                const int p = u & 31, hi = u >> 5;
+                const int sh = p >> 4, jj = (p >> 2) & 3, m = p & 3;
+                const uint32_t cm = (1u << vb) - 1u;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int dim = 2 * lane + e;
+                    const int L = (dim & 15) + 16 * jj, phi = m + 4 * (dim >> 4) + 32 * sh;
+                    const int bit = 2 * vb * phi + vb * hi, c = bit >> 5, o = bit & 31;
+                    const uint32_t code = e ? c1 : c0;
+                    atomicOr(&s_vv[L * 16 + c], code << o);
+                    atomicOr(&s_vm[L * 16 + c], cm << o);
+                    if (o + vb > 32) {
+                        atomicOr(&s_vv[L * 16 + c + 1], code >> (32 - o));
+                        atomicOr(&s_vm[L * 16 + c + 1], cm >> (32 - o));
+                    }
+                }
+            }
+        }
+    }
+    if (!do_v) return;
+    __syncthreads();
+    // this lane's stream: every partly written dword is read first (the loads in flight together),
+    // then merged and stored
+    uint32_t* vt = (uint32_t*)(a.v_codes + (bh * a.n_tiles + tile) * a.v_tile_bytes);
+    uint32_t old[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        old[c] = 0u;
+        const uint32_t m32 = c < 4 * vb ? s_vm[lane * 16 + c] : 0u;
+        if (m32 != 0u && m32 != 0xFFFFFFFFu) old[c] = vt[((c >> 2) * 64 + lane) * 4 + (c & 3)];
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const uint32_t m32 = c < 4 * vb ? s_vm[lane * 16 + c] : 0u, v32 = s_vv[lane * 16 + c];
+        if (m32) vt[((c >> 2) * 64 + lane) * 4 + (c & 3)] = (old[c] & ~m32) | (v32 & m32);
+    }
+}
+
 // Copy rows into the fp16 ring (slot = position % n_recent).
 __global__ __launch_bounds__(128) void k_ring(const RingArgs a) {
     const int h = blockIdx.y, b = blockIdx.z, j = threadIdx.x;
@@ -2535,7 +2752,11 @@ hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_
     q.vec16 = ((uintptr_t)a.src_k % 16 == 0) && ((uintptr_t)a.src_v % 16 == 0) && (a.sB * es) % 16 == 0 &&
               (a.sT * es) % 16 == 0 && (a.sH * es) % 16 == 0;
     const dim3 grid((unsigned)max_tiles, a.Hkv, B);
-    if (a.k_rot && a.k_mode == BGTQ_K_AFFINE && (a.which & 1)) {
+    const bool rot = a.k_rot && a.k_mode == BGTQ_K_AFFINE && (a.which & 1);
+    int64_t most = 0;  // the most positions any sequence appends
+    for (int b = 0; b < B; ++b) most = std::max<int64_t>(most, a.pos_hi[b] - a.pos_lo[b]);
+    if (!rot && most <= kAppendFewMax) return launch_main(k_append, grid, dim3(64), s, q);
+    if (rot) {
         if (a.dtype == BGTQ_F32) return launch_main(k_quant<float, true>, grid, dim3(64), s, q);
         return launch_main(k_quant<uint16_t, true>, grid, dim3(64), s, q);
     }

@@ -322,3 +322,82 @@ def test_block_energy(wid):
         np.testing.assert_allclose(sc[h], energy.scores(ek, eq), rtol=1e-12)
         s_o, r_o = energy.sigma_hat(ek)
         assert np.max(np.abs(sg[h].astype(np.float64) / s_o - 1)) <= 2 ** -23
+
+
+STEP_CASES = {
+    # name: (workload id, overrides, prefill tokens, tokens appended per decode step)
+    "w2_steps_cross_tile": (2, {"L": 1}, 1022, (1, 1, 1, 3, 1)),
+    "w1_from_empty": (1, {}, 0, (1, 1, 62, 1, 1)),
+    "w5_ring_evicts": (5, {}, 300, (1, 1, 2, 1)),
+    "w4_affine_steps": (4, {"L": 1, "B": 2}, 500 + 11, (1, 1, 1)),
+}
+
+
+@pytest.mark.parametrize("name", list(STEP_CASES))
+def test_decode_step_matches_append_then_attend(name):
+    """bgtq_decode_step: each step appends its rows and attends the step's query over the grown
+    context; every output matches the oracle over the same prefix, and the cache ends bit-exact."""
+    wid, ov, n0, steps = STEP_CASES[name]
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
+    N = n0 + sum(steps)
+    print(f"[step case {name}] prefill={n0} steps={steps} B={w.B} Hq={w.Hq} Hkv={w.Hkv}", flush=True)
+    n_cap = ((N + 63) // 64 + 1) * 64
+    m = T.meta(w, 0)
+    K, V, _ = T.inputs(w, 0, N)
+    cache = T.gpu_cache(w, n_cap)
+    if m is not None:
+        cache.set_metadata(0, m.bits, m.sigma, m.r)
+    if n0:
+        T.append_all(cache, 0, K[:, :, :n0], V[:, :, :n0], w.dtype)
+    kd = T.to_dev(np.transpose(K, (0, 2, 1, 3)), w.dtype)        # [B, N, Hkv, d]
+    vd = T.to_dev(np.transpose(V, (0, 2, 1, 3)), w.dtype)
+    pos = n0
+    for i, n in enumerate(steps):
+        q = np.stack([np.concatenate([synth.queries(w, 0, h, b, pos + n) for h in range(w.Hkv)])
+                      for b in range(w.B)])
+        out = cache.decode_step(0, kd[:, pos:pos + n], vd[:, pos:pos + n], T.to_dev(q, w.dtype),
+                                n_splits=(0, 3)[i % 2])
+        torch.cuda.synchronize()
+        pos += n
+        assert (cache.n_tokens[0] == pos).all()
+        oc = T.oracle_layer(w, K[:, :, :pos], V[:, :, :pos], m, n_cap)
+        e = T.assert_close(out.cpu().numpy(), pipeline.decode_layer(oc, q), f"{name} step {i} (context {pos})")
+        print(f"  step {i}: context {pos}, max abs err {e:.2e}", flush=True)
+    _compare_cache(cache, oc, w)
+
+
+FEW_CASES = {
+    # name: (workload id, overrides, N, chunk sizes).  Appends of at most 16 positions per sequence
+    # take the one-token-per-wave kernel; every format it covers, appended a few tokens at a time
+    # (including chunks that straddle a tile boundary and one of 17, which takes the tile kernel).
+    "gtq_v3_g8": (2, {"L": 1}, 150, (1, 1, 5, 16, 17, 1, 60, 1, 3, 40, 1)),
+    "gtq_v2_b2": (3, {"L": 1, "B": 2}, 90, (1, 2, 3, 16, 1, 7, 60)),
+    "gtq_v4_k4": (2, {"L": 1, "v_bits": 4, "k_budget_units": 256}, 70, (1, 13, 1, 16, 39)),
+    "gtq_v1": (1, {"v_bits": 1}, 66, (1, 1, 62, 2)),
+    "affine_g32_v2": (4, {"L": 1, "B": 2}, 80, (1, 1, 14, 48, 16)),
+    "affine_g64_codebook_v3": (4, {"L": 1, "B": 1, "k_group": 64, "v_mode": "codebook", "v_bits": 3}, 70,
+                               (2, 16, 16, 16, 20)),
+    "affine_g128_k8": (4, {"L": 1, "B": 1, "k_group": 128, "k_bits": 8}, 40, (1, 3, 36)),
+    "ring_evicts_few": (5, {}, 300, (100, 156, 1, 1, 16, 2, 24)),
+}
+
+
+@pytest.mark.parametrize("name", list(FEW_CASES))
+def test_few_token_appends_bit_exact(name):
+    wid, ov, N, chunks = FEW_CASES[name]
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
+    print(f"[few case {name}] N={N} chunks={chunks}", flush=True)
+    n_cap = ((N + 63) // 64 + 1) * 64
+    m = T.meta(w, 0)
+    K, V, q = T.inputs(w, 0, N)
+    oc = T.oracle_layer(w, K, V, m, n_cap)
+    cache = T.gpu_cache(w, n_cap)
+    if m is not None:
+        cache.set_metadata(0, m.bits, m.sigma, m.r)
+    T.append_all(cache, 0, K, V, w.dtype, chunks)
+    _compare_cache(cache, oc, w)
+    if name in ("gtq_v1", "affine_g128_k8"):   # formats the quantizer writes but no decode kernel reads
+        return
+    out = cache.decode_attention(0, T.to_dev(q, w.dtype))
+    torch.cuda.synchronize()
+    T.assert_close(out.cpu().numpy(), pipeline.decode_layer(oc, q), name)

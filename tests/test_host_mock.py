@@ -101,3 +101,53 @@ def test_fp16_comparator_arguments(mock):
         need = mock.bgtq_fp16_decode_workspace_bytes(N, B, Hq, Hkv, ns)
         _call_ok(mock, mock.bgtq_fp16_decode_attention(q, q, N, B, Hq, Hkv, 128, q, 2, q, ws, need, ns, None))
         assert mock.bgtq_mock_launches() == 2
+
+
+@pytest.mark.parametrize("fmt", range(len(FORMATS)))
+def test_decode_step_appends_then_attends(mock, fmt):
+    """The combined step enqueues the append's launches before the attention's and matches the lengths
+    that the two separate calls leave."""
+    nt = np.zeros((2, 2), np.int64)
+    d = _desc(nt, **FORMATS[fmt])
+    q = C.c_void_p(FAKE + 0x50000000)
+    ws = C.c_void_p(FAKE + 0x60000000)
+    need = mock.bgtq_decode_workspace_bytes(C.byref(d), 0)
+    total = 0
+    for n_new in (1, 1, 63, 200, 1):
+        mock.bgtq_mock_reset()
+        log = _call_ok(mock, mock.bgtq_decode_step(C.byref(d), 1, q, q, q, 2, n_new, None, q, ws, need, 0, None))
+        total += n_new
+        assert log.count("decode") == 1 and log.count("combine") == 1
+        first_decode = log.index("decode")
+        for tag in ("quant", "ring"):
+            if tag in log:
+                assert log.index(tag) < first_decode, log
+        assert "quant" in log or "ring" in log
+        assert (nt[1] == total).all() and (nt[0] == 0).all()
+
+
+def test_decode_step_failure_leaves_state(mock):
+    """Errors found in either half come back before anything is enqueued or counted."""
+    nt = np.zeros((2, 2), np.int64)
+    d = _desc(nt, n_cap=128)
+    q = C.c_void_p(FAKE + 0x50000000)
+    ws = C.c_void_p(FAKE + 0x60000000)
+    need = mock.bgtq_decode_workspace_bytes(C.byref(d), 0)
+    step = lambda n_new, ws_bytes, ws_=ws, n_splits=0: mock.bgtq_decode_step(
+        C.byref(d), 0, q, q, q, 2, n_new, None, q, ws_, ws_bytes, n_splits, None)
+    cases = [(lambda: step(129, need), _lib.E_CAPACITY),          # append half: capacity
+             (lambda: step(1, 16), _lib.E_INVALID),               # attention half: workspace too small
+             (lambda: step(1, need, C.c_void_p(FAKE + 0x60000010)), _lib.E_INVALID),   # misaligned workspace
+             (lambda: step(0, need), _lib.E_INVALID),             # nothing appended to an empty context
+             (lambda: step(1, need, ws, 1 << 20), _lib.E_UNSUPPORTED)]                  # too many splits
+    for call, code in cases:
+        mock.bgtq_mock_reset()
+        assert call() == code, mock.bgtq_last_error()
+        assert mock.bgtq_mock_launches() == 0
+        assert (nt == 0).all()
+    mock.bgtq_mock_reset()
+    _call_ok(mock, step(5, need))
+    assert (nt[0] == 5).all() and (nt[1] == 0).all()
+    mock.bgtq_mock_reset()
+    _call_ok(mock, step(0, need))                                 # n_new = 0 attends without appending
+    assert "quant" not in mock.bgtq_mock_log().decode() and (nt[0] == 5).all()
