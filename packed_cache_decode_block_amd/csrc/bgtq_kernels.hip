@@ -2538,6 +2538,34 @@ __global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
     if (t0 >= a.pos_hi[b]) return;  // whole workgroup beyond this sequence's range
     const int u_lo = a.pos_lo[b] > t0 ? (int)(a.pos_lo[b] - t0) : 0;
     const int u_hi = a.pos_hi[b] - t0 < TILE ? (int)(a.pos_hi[b] - t0) : TILE;
+    const size_t bh = (size_t)b * a.Hkv + h;
+    const bool do_k = a.which & 1, do_v = (a.which >> 1) & 1;
+    const int vb = a.v_bits;
+    // Every load the first token needs is issued here, before the first barrier, so that one
+    // memory round trip covers the rows, this lane's value-stream dwords, the metadata and the
+    // thresholds (the tile's value dwords are this workgroup's alone until it ends).
+    auto row_src = [&](int u) -> int64_t {
+        int64_t row = t0 + u - a.off[b];
+        if (a.mod_n) row %= a.mod_n;
+        return (int64_t)b * a.sB + row * a.sT + (int64_t)h * a.sH + 2 * lane;
+    };
+    float kx0 = 0.f, kx1 = 0.f, vx0 = 0.f, vx1 = 0.f;
+    auto load_rows = [&](int u) {
+        const int64_t src = row_src(u);
+        if (do_k) {
+            kx0 = load_act(a.src_k, src, a.dtype);
+            kx1 = load_act(a.src_k, src + 1, a.dtype);
+        }
+        if (do_v) {
+            vx0 = load_act(a.src_v, src, a.dtype);
+            vx1 = load_act(a.src_v, src + 1, a.dtype);
+        }
+    };
+    if (u_lo < u_hi) load_rows(u_lo);
+    uint32_t* vt = (uint32_t*)(a.v_codes + (bh * a.n_tiles + tile) * a.v_tile_bytes);
+    uint32_t old[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) old[c] = (do_v && c < 4 * vb) ? vt[((c >> 2) * 64 + lane) * 4 + (c & 3)] : 0u;
     __shared__ float s_thr[BGTQ_CB_THRESHOLDS];
     __shared__ int s_wid[64];
     __shared__ float s_r[64], s_sig[64];
@@ -2546,8 +2574,6 @@ __global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
     for (int i = lane; i < BGTQ_CB_THRESHOLDS; i += 64) s_thr[i] = __builtin_bit_cast(float, c_thr32[i]);
     for (int i = lane; i < 64 * 16; i += 64) s_vv[i] = s_vm[i] = 0u;
     if (lane < 32) s_rec[lane] = 0u;
-    const size_t bh = (size_t)b * a.Hkv + h;
-    const bool do_k = a.which & 1, do_v = (a.which >> 1) & 1;
     const bool gtq = a.k_mode == BGTQ_K_BLOCKGTQ;
     int w = 0, off = 0;  // this lane's block: width and bit offset in the key record
     if (do_k && gtq) {
@@ -2562,17 +2588,9 @@ __global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
             const int wj = s_wid[j];
             off += (wj > w || (wj == w && j < lane)) ? 2 * wj : 0;
         }
-    const int vb = a.v_bits;
     for (int u = u_lo; u < u_hi; ++u) {
         const int64_t pos = t0 + u;
-        int64_t row = pos - a.off[b];
-        if (a.mod_n) row %= a.mod_n;
-        const int64_t src = (int64_t)b * a.sB + row * a.sT + (int64_t)h * a.sH + 2 * lane;
-        // both rows' loads in flight together
-        const float kx0 = do_k ? load_act(a.src_k, src, a.dtype) : 0.f;
-        const float kx1 = do_k ? load_act(a.src_k, src + 1, a.dtype) : 0.f;
-        const float vx0 = do_v ? load_act(a.src_v, src, a.dtype) : 0.f;
-        const float vx1 = do_v ? load_act(a.src_v, src + 1, a.dtype) : 0.f;
+        if (u > u_lo) load_rows(u);
         for (int pass = 0; pass < 2; ++pass) {
             if ((pass == 0 && !do_k) || (pass == 1 && !do_v)) continue;
             const float x0 = pass == 0 ? kx0 : vx0, x1 = pass == 0 ? kx1 : vx1;
@@ -2684,16 +2702,7 @@ __global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
     }
     if (!do_v) return;
     __syncthreads();
-    // this lane's stream: every partly written dword is read first (the loads in flight together),
-    // then merged and stored
-    uint32_t* vt = (uint32_t*)(a.v_codes + (bh * a.n_tiles + tile) * a.v_tile_bytes);
-    uint32_t old[16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        old[c] = 0u;
-        const uint32_t m32 = c < 4 * vb ? s_vm[lane * 16 + c] : 0u;
-        if (m32 != 0u && m32 != 0xFFFFFFFFu) old[c] = vt[((c >> 2) * 64 + lane) * 4 + (c & 3)];
-    }
+    // this lane's stream: the written fields merged into the dwords read at the start
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
         const uint32_t m32 = c < 4 * vb ? s_vm[lane * 16 + c] : 0u, v32 = s_vv[lane * 16 + c];
