@@ -2567,8 +2567,6 @@ __global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
 #pragma unroll
     for (int c = 0; c < 16; ++c) old[c] = (do_v && c < 4 * vb) ? vt[((c >> 2) * 64 + lane) * 4 + (c & 3)] : 0u;
     __shared__ float s_thr[BGTQ_CB_THRESHOLDS];
-    __shared__ int s_wid[64];
-    __shared__ float s_r[64], s_sig[64];
     __shared__ uint32_t s_rec[32];
     __shared__ uint32_t s_vv[64 * 16], s_vm[64 * 16];  // value streams of the tile: bits and written mask
     for (int i = lane; i < BGTQ_CB_THRESHOLDS; i += 64) s_thr[i] = __builtin_bit_cast(float, c_thr32[i]);
@@ -2576,18 +2574,19 @@ __global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
     if (lane < 32) s_rec[lane] = 0u;
     const bool gtq = a.k_mode == BGTQ_K_BLOCKGTQ;
     int w = 0, off = 0;  // this lane's block: width and bit offset in the key record
+    float r_blk = 1.f, sig_blk = 1.f;
     if (do_k && gtq) {
         w = a.bits[h * 64 + lane] < 8 ? a.bits[h * 64 + lane] : 8;  // widths above 8 are invalid; clamp
-        s_wid[lane] = w;
-        s_r[lane] = a.inv_sigma[h * 64 + lane];
-        s_sig[lane] = a.sigma[h * 64 + lane];
-    }
-    __syncthreads();
-    if (do_k && gtq)  // slots in descending width, ties by block index: the fields stored before this one
+        r_blk = a.inv_sigma[h * 64 + lane];
+        sig_blk = a.sigma[h * 64 + lane];
+        // slots in descending width, ties by block index: the fields stored before this one
+#pragma unroll
         for (int j = 0; j < 64; ++j) {
-            const int wj = s_wid[j];
+            const int wj = __builtin_amdgcn_readlane(w, j);
             off += (wj > w || (wj == w && j < lane)) ? 2 * wj : 0;
         }
+    }
+    __syncthreads();
     for (int u = u_lo; u < u_hi; ++u) {
         const int64_t pos = t0 + u;
         if (u > u_lo) load_rows(u);
@@ -2599,12 +2598,12 @@ __global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
                 uint32_t* kt = (uint32_t*)(a.k_codes + (bh * a.n_tiles + tile) * a.k_tile_bytes);
                 if (gtq) {
                     uint16_t s16;
-                    const float S = wave_rms16(x0, x1, s_r[lane], true, &s16);
+                    const float S = wave_rms16(x0, x1, r_blk, true, &s16);
                     if (w > 0) {
                         float t;
                         {
 #pragma clang fp contract(off)
-                            t = S * s_sig[lane];
+                            t = S * sig_blk;
                         }
                         const uint32_t f = tq_code(x0, t, w, s_thr) | (tq_code(x1, t, w, s_thr) << w);
                         const int k = off >> 5, sh = off & 31;

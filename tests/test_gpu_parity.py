@@ -401,3 +401,30 @@ def test_few_token_appends_bit_exact(name):
     out = cache.decode_attention(0, T.to_dev(q, w.dtype))
     torch.cuda.synchronize()
     T.assert_close(out.cpu().numpy(), pipeline.decode_layer(oc, q), name)
+
+
+def test_decode_step_ragged_lengths():
+    """Decode steps on sequences of different lengths: each sequence appends at its own position
+    (other tiles, over bits of an earlier, longer fill that the decode must ignore)."""
+    w = synth.reduced(synth.WORKLOADS[3], L=1, B=3)
+    N = 700
+    m = T.meta(w, 0)
+    K, V, _ = T.inputs(w, 0, N)
+    cache = T.gpu_cache(w, 768)
+    cache.set_metadata(0, m.bits, m.sigma, m.r)
+    T.append_all(cache, 0, K, V, w.dtype)
+    lens = np.array([640, 1, 333])
+    cache.n_tokens[0, :] = lens
+    for step in range(3):
+        kn = np.stack([K[b, :, lens[b]] for b in range(w.B)])[:, None]      # [B, 1, Hkv, d]
+        vn = np.stack([V[b, :, lens[b]] for b in range(w.B)])[:, None]
+        q = np.stack([np.concatenate([synth.queries(w, 0, h, b, int(lens[b]) + 1) for h in range(w.Hkv)])
+                      for b in range(w.B)])
+        out = cache.decode_step(0, T.to_dev(kn, w.dtype), T.to_dev(vn, w.dtype), T.to_dev(q, w.dtype),
+                                n_splits=(0, 2, 5)[step]).cpu().numpy()
+        lens = lens + 1
+        assert (cache.n_tokens[0] == lens).all()
+        for b in range(w.B):
+            wb = synth.reduced(w, B=1)
+            oc = T.oracle_layer(wb, K[b:b + 1, :, :lens[b]], V[b:b + 1, :, :lens[b]], m, 768)
+            T.assert_close(out[b:b + 1], pipeline.decode_layer(oc, q[b:b + 1]), f"step {step} b={b} n={lens[b]}")
