@@ -325,8 +325,7 @@ def main():
         # step re-appends position N - 1 (the lengths are set back by one before capture), so the
         # attended context is the same N tokens; every replay rewrites that slot.  (With an fp16
         # window the slot the step evicts from already holds the newest row: other bytes, the
-        # same work.)
-        cache.n_tokens -= 1
+        # same work.)  Eager launches set the lengths back before every call.
         gen = torch.Generator(device="cuda").manual_seed(11)
         td = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
         kn = [torch.randn((w.B, 1, w.Hkv, w.d), generator=gen, device="cuda").to(td) for _ in range(w.L)]
@@ -335,6 +334,7 @@ def main():
 
         def step_append():
             for layer in range(w.L):
+                cache.n_tokens[layer] -= 1
                 cache.decode_step(layer, kn[layer], vn[layer], qd[layer], outs[layer], n_splits=args.n_splits, ws=ws)
 
         if graph_ok:
@@ -345,6 +345,7 @@ def main():
             del gs
         else:  # eager launches, like the decode-only figure it is compared with
             sec_s = timed(step_append, args.steps, args.warmup)
+        assert (cache.n_tokens == w.N).all()
         result["decode_step"] = {
             "entry": "bgtq_decode_step", "tokens_appended_per_sequence": 1, "ms_per_step": round(sec_s * 1e3, 4),
             "launch": "hipgraph" if graph_ok else "eager",
