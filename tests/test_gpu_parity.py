@@ -428,3 +428,51 @@ def test_decode_step_ragged_lengths():
             wb = synth.reduced(w, B=1)
             oc = T.oracle_layer(wb, K[b:b + 1, :, :lens[b]], V[b:b + 1, :, :lens[b]], m, 768)
             T.assert_close(out[b:b + 1], pipeline.decode_layer(oc, q[b:b + 1]), f"step {step} b={b} n={lens[b]}")
+
+
+@pytest.mark.parametrize("wid,N", [(2, 1500 + 7), (5, 200)])
+def test_graph_replays_match_eager(wid, N):
+    """Decode and the append-then-attend step captured in a HIP graph: every replay (eager work and
+    synchronizations between replays) equals the eager result bit for bit, and the cache bytes
+    stay those the eager step wrote.  (A replayed step rewrites its position with the same row; with
+    the fp16 window the context stays inside it, since a step that evicts reads the ring slot it
+    then overwrites and so is not the same step twice.)"""
+    w = synth.reduced(synth.WORKLOADS[wid], L=1) if wid != 5 else synth.WORKLOADS[5]
+    m = T.meta(w, 0)
+    K, V, q = T.inputs(w, 0, N)
+    cache = T.gpu_cache(w, ((N + 63) // 64 + 1) * 64)
+    cache.set_metadata(0, m.bits, m.sigma, m.r)
+    T.append_all(cache, 0, K[:, :, :N - 1], V[:, :, :N - 1], w.dtype)
+    kd = T.to_dev(np.transpose(K[:, :, N - 1:], (0, 2, 1, 3)), w.dtype)
+    vd = T.to_dev(np.transpose(V[:, :, N - 1:], (0, 2, 1, 3)), w.dtype)
+    qd = T.to_dev(q, w.dtype)
+    ws = cache.workspace()
+    out_step = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    cache.decode_step(0, kd, vd, qd, out=out_step, ws=ws)
+    eager_step = out_step.clone()
+    eager_dec = cache.decode_attention(0, qd, ws=ws).clone()
+    bufs = lambda: [t for t in (cache.k_codes, cache.v_codes, cache.k_scale, cache.v_scale, cache.recent_k,
+                                cache.recent_v) if t is not None]
+    snap = [t.clone() for t in bufs()]
+    torch.cuda.synchronize()
+    out_dec = torch.empty_like(out_step)
+    g_dec, g_step = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_dec):
+        cache.decode_attention(0, qd, out=out_dec, ws=ws)
+    cache.n_tokens[0] -= 1                       # the captured step re-appends position N - 1
+    with torch.cuda.graph(g_step):
+        cache.decode_step(0, kd, vd, qd, out=out_step, ws=ws)
+    assert (cache.n_tokens[0] == N).all()
+    for r in range(3):
+        out_step.zero_()
+        out_dec.zero_()
+        g_step.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out_step.cpu().numpy(), eager_step.cpu().numpy(), f"step replay {r}")
+        other = cache.decode_attention(0, qd * 0.5, ws=torch.empty_like(ws))   # eager work between replays
+        g_dec.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out_dec.cpu().numpy(), eager_dec.cpu().numpy(), f"decode replay {r}")
+        assert torch.isfinite(other).all()
+        for a, b in zip(snap, bufs()):
+            assert torch.equal(a, b), f"cache bytes changed on replay {r}"
