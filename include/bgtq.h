@@ -181,6 +181,28 @@ int bgtq_block_energy(const void *k_cal, const void *q_cal, int dtype, int64_t T
                       int Hkv, int g, int d, int score_mode, double *scores, float *sigma,
                       float *inv_sigma, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * LogQuant's log-based filter for one sequence (host, synchronous; LogQuant summary, Method 2):
+ * at most 3W tokens stay at high precision, and when the set is full the density of its older
+ * part is halved.  Reading: when a token arrives and the set holds 3W, the 2W oldest members
+ * (by position) are halved, the 2nd, 4th, ... oldest leaving for the low-bit store; then the
+ * new token joins.
+ * State: a high-precision store of 3W row slots, of which slots 0..*n_hp-1 are filled;
+ * hp_pos[slot] (capacity 3W) is the token position the row holds, in any slot order.
+ * Planning the append of the token at position `pos` (above every held position):
+ * - when *n_hp == 3W, the W leaving rows' slots are written to evict[0..W-1], oldest first.
+ *   Their rows are to be quantized in that order.  The store is then compacted into slots
+ *   0..2W-1 by copying row move_src[i] to slot move_dst[i], i < *n_moves, after the leaving
+ *   rows were read.  No move reads a slot that another move writes.  evict, move_src and
+ *   move_dst each hold W entries;
+ * - the new token's row goes to slot *new_slot.
+ * hp_pos and *n_hp are left as after the append.  Returns the number of leaving rows (0 or W),
+ * or BGTQ_E_INVALID (W outside [1, 2^20], NULL pointers, *n_hp outside [0, 3W], pos not above a
+ * held position, a repeated position) with nothing changed.
+ */
+int bgtq_logquant_plan(int W, int64_t *hp_pos, int *n_hp, int64_t pos, int32_t *evict,
+                       int32_t *move_src, int32_t *move_dst, int *n_moves, int *new_slot);
+
 /* Bytes of one cache buffer (all L layers) for the descriptor's geometry; <0 on error. */
 int64_t bgtq_cache_bytes(const bgtq_cache *c, int which);
 

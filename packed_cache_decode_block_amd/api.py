@@ -74,6 +74,31 @@ def bgtq_allocate(scores, budget_units: int, b_min: int = 0, b_max: int = 8, rat
     return out
 
 
+class LogQuantPlanner:
+    """Host bookkeeping of one sequence's high-precision store under LogQuant's log-based filter
+    (bgtq_logquant_plan): which store rows leave for the low-bit store, how the store compacts,
+    and where the new token's row goes."""
+
+    def __init__(self, W: int):
+        self.W = int(W)
+        self.hp_pos = np.zeros(3 * self.W, np.int64)
+        self.n_hp = 0
+
+    def append(self, pos: int):
+        """-> (evict_slots, moves [(src, dst)], new_slot) for the token at position pos."""
+        n = C.c_int(self.n_hp)
+        ev = np.zeros(self.W, np.int32)
+        ms = np.zeros(self.W, np.int32)
+        md = np.zeros(self.W, np.int32)
+        nm, ns = C.c_int(0), C.c_int(0)
+        p32 = C.POINTER(C.c_int32)
+        k = check(lib.bgtq_logquant_plan(self.W, self.hp_pos.ctypes.data_as(C.POINTER(C.c_int64)), C.byref(n), pos,
+                                         ev.ctypes.data_as(p32), ms.ctypes.data_as(p32), md.ctypes.data_as(p32),
+                                         C.byref(nm), C.byref(ns)))
+        self.n_hp = n.value
+        return ev[:k].copy(), list(zip(ms[:nm.value].tolist(), md[:nm.value].tolist())), ns.value
+
+
 def bgtq_block_energy(k_cal, q_cal, score_mode: int = _lib.SCORE_QK, stream=None):
     """k_cal [T, Hkv, 128], q_cal [T, Hq, 128] device tensors -> (scores fp64, sigma fp32, inv_sigma fp32)
     host arrays [Hkv, 64].  Synchronizes the stream."""

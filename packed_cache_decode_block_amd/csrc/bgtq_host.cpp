@@ -288,6 +288,51 @@ int bgtq_allocate_rate(const double* scores, int n_heads, int n_blk, int budget_
                          [&gain](double s, int b) { return s * gain[b]; });
 }
 
+int bgtq_logquant_plan(int W, int64_t* hp_pos, int* n_hp, int64_t pos, int32_t* evict, int32_t* move_src,
+                       int32_t* move_dst, int* n_moves, int* new_slot) {
+    if (W < 1 || W > (1 << 20)) return fail(BGTQ_E_INVALID, "W=%d out of range", W);
+    if (!hp_pos || !n_hp || !n_moves || !new_slot) return fail(BGTQ_E_INVALID, "NULL argument");
+    const int n = *n_hp;
+    if (n < 0 || n > 3 * W) return fail(BGTQ_E_INVALID, "n_hp=%d outside [0, 3W]", n);
+    for (int i = 0; i < n; ++i)
+        if (hp_pos[i] >= pos) return fail(BGTQ_E_INVALID, "position %lld not above held position %lld", (long long)pos,
+                                          (long long)hp_pos[i]);
+    int kept = n, n_ev = 0;
+    *n_moves = 0;
+    if (n == 3 * W) {
+        if (!evict || !move_src || !move_dst) return fail(BGTQ_E_INVALID, "NULL evict or move arrays");
+        std::vector<int> order(n);
+        for (int i = 0; i < n; ++i) order[i] = i;
+        std::sort(order.begin(), order.end(), [&](int a, int b) { return hp_pos[a] < hp_pos[b]; });
+        for (int i = 1; i < n; ++i)
+            if (hp_pos[order[i]] == hp_pos[order[i - 1]]) return fail(BGTQ_E_INVALID, "repeated position");
+        // the 2W oldest rows are halved: the 2nd, 4th, ... oldest leave, oldest first
+        std::vector<char> gone(n, 0);
+        for (int i = 1; i < 2 * W; i += 2) {
+            evict[n_ev++] = order[i];
+            gone[order[i]] = 1;
+        }
+        // compaction into slots [0, 2W): kept rows above 2W fill the vacated slots below it, in
+        // ascending slot order on both sides (a vacated slot is never a source)
+        int h = 0, m = 0;
+        for (int src = 2 * W; src < n; ++src) {
+            if (gone[src]) continue;
+            while (!gone[h]) ++h;
+            move_src[m] = src;
+            move_dst[m] = h;
+            hp_pos[h] = hp_pos[src];
+            ++m;
+            ++h;
+        }
+        *n_moves = m;
+        kept = 2 * W;
+    }
+    hp_pos[kept] = pos;
+    *new_slot = kept;
+    *n_hp = kept + 1;
+    return n_ev;
+}
+
 int bgtq_block_energy(const void* k_cal, const void* q_cal, int dtype, int64_t T_cal, int Hkv, int g, int d,
                       int score_mode, double* scores, float* sigma, float* inv_sigma, void* ws, size_t ws_bytes,
                       void* stream) {
