@@ -476,3 +476,30 @@ def test_graph_replays_match_eager(wid, N):
         assert torch.isfinite(other).all()
         for a, b in zip(snap, bufs()):
             assert torch.equal(a, b), f"cache bytes changed on replay {r}"
+
+
+def test_decode_step_rotated_keys():
+    """Decode steps with rotated affine keys (their appends take the tile kernel): every step's
+    output matches the oracle over the same prefix, and the cache ends bit-exact."""
+    w = synth.reduced(synth.WORKLOADS[4], L=1, B=2)
+    n0, steps = 300 + 5, (1, 2, 1)
+    N = n0 + sum(steps)
+    n_cap = ((N + 63) // 64 + 1) * 64
+    signs = np.where(np.random.default_rng(47).random((w.Hkv, 128)) < 0.5, -1.0, 1.0)
+    K, V, _ = T.inputs(w, 0, N)
+    cache = P.PackedCache(L=1, B=w.B, Hq=w.Hq, Hkv=w.Hkv, n_cap=n_cap, k_mode=P.K_AFFINE, k_bits=w.k_bits,
+                          k_group=w.k_group, v_mode=P.V_AFFINE, v_bits=w.v_bits, k_rotation=True)
+    cache.set_key_rotation(0, signs)
+    T.append_all(cache, 0, K[:, :, :n0], V[:, :, :n0], w.dtype)
+    kd = T.to_dev(np.transpose(K, (0, 2, 1, 3)), w.dtype)
+    vd = T.to_dev(np.transpose(V, (0, 2, 1, 3)), w.dtype)
+    pos = n0
+    for i, n in enumerate(steps):
+        q = np.stack([np.concatenate([synth.queries(w, 0, h, b, pos + n) for h in range(w.Hkv)])
+                      for b in range(w.B)])
+        out = cache.decode_step(0, kd[:, pos:pos + n], vd[:, pos:pos + n], T.to_dev(q, w.dtype)).cpu().numpy()
+        pos += n
+        oc = pipeline.build_layer(K[:, :, :pos], V[:, :, :pos], k_mode="affine", v_mode="affine", v_bits=w.v_bits,
+                                  n_cap=n_cap, k_bits=w.k_bits, k_group=w.k_group, k_rot=signs)
+        T.assert_close(out, pipeline.decode_layer(oc, q), f"rotated step {i} (context {pos})")
+    _compare_cache(cache, oc, w)
