@@ -97,6 +97,12 @@ enum {
  * Host state:
  *   n_tokens  int64 [L][B] host array: tokens appended so far per (layer, sequence) (packed +
  *     recent).  bgtq_quantize_append advances it on success only.
+ *   n_hp      int32 [L][B] host array or NULL.  Non-NULL selects LogQuant's log-based filter
+ *     for the recent buffers: they then hold n_hp[layer][b] high-precision rows in slots
+ *     0..n_hp-1, in any order, and the other n_tokens - n_hp tokens are packed.  Appends go
+ *     through bgtq_logquant_append; bgtq_quantize_append and bgtq_decode_step refuse such a cache.
+ *     NULL keeps the positional ring: min(n_tokens, n_recent) recent rows, slot = position mod
+ *     n_recent.
  *
  * Tile layout (64 consecutive tokens of one (batch, kv head)):
  *   K record = little-endian bit stream of R = 2U/32 dwords (affine: 4*k_bits dwords).  Block-GTQ
@@ -120,6 +126,7 @@ typedef struct bgtq_cache {
     const float *sigma, *inv_sigma;
     int64_t *n_tokens;
     const uint8_t *k_rot;
+    int32_t *n_hp;
 } bgtq_cache;
 
 /* Thread-local text describing the last non-OK status of this thread ("" if none). */
@@ -202,6 +209,22 @@ int bgtq_block_energy(const void *k_cal, const void *q_cal, int dtype, int64_t T
  */
 int bgtq_logquant_plan(int W, int64_t *hp_pos, int *n_hp, int64_t pos, int32_t *evict,
                        int32_t *move_src, int32_t *move_dst, int *n_moves, int *new_slot);
+
+/*
+ * Append one token per sequence under LogQuant's log-based filter (device, asynchronous; host
+ * bookkeeping synchronous).  LogQuant summary, Method 2; the filter is bgtq_logquant_plan's,
+ * with W = n_recent / 3.  Needs c->n_hp, n_recent a multiple of 3 in [3, 512], and
+ * B * n_recent <= 1536.  For each sequence the new token's row enters the high-precision store.
+ * When the store already holds 3W rows, the rows that leave are quantized first, oldest first,
+ * and appended to the packed cache.  The store is then compacted, as the plan describes.
+ * k, v: device rows [B][1][Hkv][128] in `dtype` (strides as bgtq_quantize_append, n_new = 1).
+ * hp_pos: host int64 [B][n_recent], the token position each store row holds; maintained here.
+ * On success n_tokens, n_hp and hp_pos advance.  Errors (nothing changed): those of
+ * bgtq_quantize_append, BGTQ_E_INVALID (no n_hp, bad n_recent, inconsistent counts),
+ * BGTQ_E_UNSUPPORTED (B * n_recent above 1536).
+ */
+int bgtq_logquant_append(bgtq_cache *c, int layer, const void *k, const void *v, int dtype,
+                         const int64_t *strides, int64_t *hp_pos, void *stream);
 
 /* Bytes of one cache buffer (all L layers) for the descriptor's geometry; <0 on error. */
 int64_t bgtq_cache_bytes(const bgtq_cache *c, int which);

@@ -17,8 +17,8 @@ V_CODEBOOK, V_AFFINE = 0, 1
 MAX_BATCH = 64
 ENERGY_CHUNK = 16  # BGTQ_ENERGY_CHUNK: calibration tokens per workgroup of bgtq_block_energy
 
-SYMBOLS = ["bgtq_last_error", "bgtq_version", "bgtq_codebook", "bgtq_allocate", "bgtq_allocate_rate", "bgtq_logquant_plan", "bgtq_block_energy",
-           "bgtq_cache_bytes", "bgtq_quantize_append", "bgtq_decode_workspace_bytes", "bgtq_decode_attention",
+SYMBOLS = ["bgtq_last_error", "bgtq_version", "bgtq_codebook", "bgtq_allocate", "bgtq_allocate_rate",
+           "bgtq_logquant_plan", "bgtq_logquant_append", "bgtq_block_energy", "bgtq_cache_bytes", "bgtq_quantize_append", "bgtq_decode_workspace_bytes", "bgtq_decode_attention",
            "bgtq_decode_step", "bgtq_fp16_decode_workspace_bytes", "bgtq_fp16_decode_attention", "bgtq_profile_enable",
            "bgtq_profile_read"]
 PROF_DECODE, PROF_FP16_DECODE, PROF_QUANTIZE = 0, 1, 2
@@ -38,7 +38,8 @@ class CacheDesc(C.Structure):
                 ("k_codes", C.c_void_p), ("v_codes", C.c_void_p), ("k_scale", C.c_void_p), ("k_zero", C.c_void_p),
                 ("v_scale", C.c_void_p), ("v_zero", C.c_void_p), ("recent_k", C.c_void_p), ("recent_v", C.c_void_p),
                 ("bits", C.c_void_p), ("sigma", C.c_void_p), ("inv_sigma", C.c_void_p),
-                ("n_tokens", C.POINTER(C.c_int64)), ("k_rot", C.c_void_p)]
+                ("n_tokens", C.POINTER(C.c_int64)), ("k_rot", C.c_void_p),
+                ("n_hp", C.POINTER(C.c_int32))]
 
 
 def bind(path: str):
@@ -59,6 +60,7 @@ def bind(path: str):
         "bgtq_decode_attention": (I, [C.POINTER(CacheDesc), I, P, I, P, P, SZ, I, P]),
         "bgtq_logquant_plan": (I, [I, C.POINTER(C.c_int64), C.POINTER(C.c_int), I64, C.POINTER(C.c_int32),
                                    C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int), C.POINTER(C.c_int)]),
+        "bgtq_logquant_append": (I, [C.POINTER(CacheDesc), I, P, P, I, C.POINTER(C.c_int64), C.POINTER(C.c_int64), P]),
         "bgtq_decode_step": (I, [C.POINTER(CacheDesc), I, P, P, P, I, I64, C.POINTER(C.c_int64), P, P, SZ, I, P]),
         "bgtq_fp16_decode_workspace_bytes": (I64, [I64, I, I, I, I]),
         "bgtq_fp16_decode_attention": (I, [P, P, I64, I, I, I, I, P, I, P, P, SZ, I, P]),

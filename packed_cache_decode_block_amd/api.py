@@ -122,8 +122,13 @@ class PackedCache:
     """
 
     def __init__(self, *, L, B, Hq, Hkv, n_cap, k_mode=_lib.K_BLOCKGTQ, budget_units=128, k_bits=4, k_group=32,
-                 v_mode=_lib.V_CODEBOOK, v_bits=2, n_recent=0, k_rotation=False, device="cuda", zero=True):
+                 v_mode=_lib.V_CODEBOOK, v_bits=2, n_recent=0, k_rotation=False, logquant_w=None, device="cuda",
+                 zero=True):
+        """logquant_w: base window W of LogQuant's log-based filter; the recent buffers then hold the
+        3W-row high-precision store (n_recent = 3W) and appends go through logquant_append."""
         torch = _torch()
+        if logquant_w is not None:
+            n_recent = 3 * int(logquant_w)
         self.desc = _lib.CacheDesc()
         d = self.desc
         d.L, d.B, d.Hq, d.Hkv, d.d = L, B, Hq, Hkv, 128
@@ -132,6 +137,11 @@ class PackedCache:
         d.v_mode, d.v_bits, d.n_recent = v_mode, v_bits, n_recent
         self.n_tokens = np.zeros((L, B), np.int64)
         d.n_tokens = self.n_tokens.ctypes.data_as(C.POINTER(C.c_int64))
+        self.n_hp = self.hp_pos = None
+        if logquant_w is not None:
+            self.n_hp = np.zeros((L, B), np.int32)
+            self.hp_pos = np.zeros((L, B, n_recent), np.int64)
+            d.n_hp = self.n_hp.ctypes.data_as(C.POINTER(C.c_int32))
         alloc = torch.zeros if zero else torch.empty
 
         def buf(which, dtype):
@@ -199,6 +209,16 @@ class PackedCache:
         strides = self._kv_strides(k, v)
         check(lib.bgtq_quantize_append(C.byref(self.desc), layer, _ptr(k), _ptr(v), _dtype_code(k), k.shape[1],
                                        strides, _stream(stream)))
+
+    def logquant_append(self, layer: int, k, v, stream=None):
+        """Append one token per sequence, k, v [B, 1, Hkv, 128], under the log-based filter."""
+        if self.n_hp is None:
+            raise ValueError("the cache was built without logquant_w")
+        strides = self._kv_strides(k, v)
+        if k.shape[1] != 1:
+            raise ValueError("the log-based filter appends one token per call")
+        check(lib.bgtq_logquant_append(C.byref(self.desc), layer, _ptr(k), _ptr(v), _dtype_code(k), strides,
+                                       self.hp_pos[layer].ctypes.data_as(C.POINTER(C.c_int64)), _stream(stream)))
 
     def decode_step(self, layer: int, k, v, q, out=None, n_splits: int = 0, ws=None, stream=None):
         """Append k, v [B, n_new, Hkv, 128], then attend q [B, Hq, 128] over the grown context -> fp32 out."""

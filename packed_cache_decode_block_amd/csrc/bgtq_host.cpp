@@ -395,6 +395,34 @@ int64_t bgtq_cache_bytes(const bgtq_cache* c, int which) {
 
 namespace {
 
+// Per-layer destination and format fields of the quantize-append arguments.
+void fill_quant_layer(const bgtq_cache* c, const bgtq::Geometry& g, int layer, bgtq::QuantArgs& q) {
+    q.k_codes = (uint8_t*)c->k_codes + (size_t)layer * g.k_codes_layer;
+    q.v_codes = (uint8_t*)c->v_codes + (size_t)layer * g.v_codes_layer;
+    q.k_scale = (uint16_t*)((uint8_t*)c->k_scale + (size_t)layer * g.k_scale_layer);
+    q.k_zero = c->k_zero ? (uint16_t*)((uint8_t*)c->k_zero + (size_t)layer * g.k_scale_layer) : nullptr;
+    q.v_scale = (uint16_t*)((uint8_t*)c->v_scale + (size_t)layer * g.v_scale_layer);
+    q.v_zero = c->v_zero ? (uint16_t*)((uint8_t*)c->v_zero + (size_t)layer * g.v_scale_layer) : nullptr;
+    if (c->k_mode == BGTQ_K_BLOCKGTQ) {
+        q.bits = c->bits + (size_t)layer * g.Hkv * 64;
+        q.sigma = c->sigma + (size_t)layer * g.Hkv * 64;
+        q.inv_sigma = c->inv_sigma + (size_t)layer * g.Hkv * 64;
+    }
+    q.k_rot = c->k_rot ? c->k_rot + (size_t)layer * g.Hkv * 16 : nullptr;
+    q.Hkv = g.Hkv;
+    q.n_cap = g.n_cap;
+    q.n_tiles = g.n_tiles;
+    q.k_tile_bytes = g.k_tile_bytes;
+    q.v_tile_bytes = g.v_tile_bytes;
+    q.k_mode = c->k_mode;
+    q.R = g.R;
+    q.k_bits = c->k_bits;
+    q.k_group = c->k_group;
+    q.v_mode = c->v_mode;
+    q.v_bits = c->v_bits;
+    q.which = 3;
+}
+
 // Quantize-append body.  With dry_run the call validates and plans only: nothing is launched and
 // n_tokens is untouched, so a caller can check both halves of a combined step before either runs.
 int quantize_append_impl(bgtq_cache* c, int layer, const void* k, const void* v, int dtype, int64_t n_new,
@@ -403,6 +431,7 @@ int quantize_append_impl(bgtq_cache* c, int layer, const void* k, const void* v,
     int rc = geometry(c, g);
     if (rc) return rc;
     if (layer < 0 || layer >= c->L) return fail(BGTQ_E_INVALID, "layer %d out of range", layer);
+    if (c->n_hp) return fail(BGTQ_E_INVALID, "the cache uses the log-based filter: append with bgtq_logquant_append");
     if (!k || !v) return fail(BGTQ_E_INVALID, "NULL k/v");
     if (!dtype_ok(dtype)) return fail(BGTQ_E_INVALID, "bad dtype");
     if (n_new < 0) return fail(BGTQ_E_INVALID, "n_new < 0");
@@ -437,31 +466,8 @@ int quantize_append_impl(bgtq_cache* c, int layer, const void* k, const void* v,
     hipStream_t s = (hipStream_t)stream;
     const size_t bh = (size_t)g.B * g.Hkv;
     bgtq::QuantArgs q{};
+    fill_quant_layer(c, g, layer, q);
     q.dtype = dtype;
-    q.k_codes = (uint8_t*)c->k_codes + (size_t)layer * g.k_codes_layer;
-    q.v_codes = (uint8_t*)c->v_codes + (size_t)layer * g.v_codes_layer;
-    q.k_scale = (uint16_t*)((uint8_t*)c->k_scale + (size_t)layer * g.k_scale_layer);
-    q.k_zero = c->k_zero ? (uint16_t*)((uint8_t*)c->k_zero + (size_t)layer * g.k_scale_layer) : nullptr;
-    q.v_scale = (uint16_t*)((uint8_t*)c->v_scale + (size_t)layer * g.v_scale_layer);
-    q.v_zero = c->v_zero ? (uint16_t*)((uint8_t*)c->v_zero + (size_t)layer * g.v_scale_layer) : nullptr;
-    if (c->k_mode == BGTQ_K_BLOCKGTQ) {
-        q.bits = c->bits + (size_t)layer * g.Hkv * 64;
-        q.sigma = c->sigma + (size_t)layer * g.Hkv * 64;
-        q.inv_sigma = c->inv_sigma + (size_t)layer * g.Hkv * 64;
-    }
-    q.k_rot = c->k_rot ? c->k_rot + (size_t)layer * g.Hkv * 16 : nullptr;
-    q.Hkv = g.Hkv;
-    q.n_cap = g.n_cap;
-    q.n_tiles = g.n_tiles;
-    q.k_tile_bytes = g.k_tile_bytes;
-    q.v_tile_bytes = g.v_tile_bytes;
-    q.k_mode = c->k_mode;
-    q.R = g.R;
-    q.k_bits = c->k_bits;
-    q.k_group = c->k_group;
-    q.v_mode = c->v_mode;
-    q.v_bits = c->v_bits;
-    q.which = 3;
     hipError_t e;
     auto run = [&](const void* sk, const void* sv, int dt, int64_t b_, int64_t t_, int64_t h_, int64_t mod_n,
                    const std::vector<int64_t>& lo, const std::vector<int64_t>& hi,
@@ -539,6 +545,128 @@ int bgtq_quantize_append(bgtq_cache* c, int layer, const void* k, const void* v,
     return quantize_append_impl(c, layer, k, v, dtype, n_new, strides, stream, false);
 }
 
+int bgtq_logquant_append(bgtq_cache* c, int layer, const void* k, const void* v, int dtype, const int64_t* strides,
+                         int64_t* hp_pos, void* stream) {
+    bgtq::Geometry g;
+    int rc = geometry(c, g);
+    if (rc) return rc;
+    if (layer < 0 || layer >= c->L) return fail(BGTQ_E_INVALID, "layer %d out of range", layer);
+    if (!c->n_hp) return fail(BGTQ_E_INVALID, "the log-based filter needs n_hp");
+    const int R = c->n_recent;
+    if (R < 3 || R % 3 || R > bgtq::BGTQ_HP_ROWS_MAX)
+        return fail(BGTQ_E_INVALID, "n_recent=%d must be a multiple of 3 in [3, %d]", R, bgtq::BGTQ_HP_ROWS_MAX);
+    if ((int64_t)c->B * R > bgtq::BGTQ_PERM_MAX)
+        return fail(BGTQ_E_UNSUPPORTED, "B * n_recent above %d", bgtq::BGTQ_PERM_MAX);
+    if (!k || !v || !hp_pos) return fail(BGTQ_E_INVALID, "NULL k/v/hp_pos");
+    if (!dtype_ok(dtype)) return fail(BGTQ_E_INVALID, "bad dtype");
+    if (!c->n_tokens) return fail(BGTQ_E_INVALID, "n_tokens is NULL");
+    if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale || !c->recent_k || !c->recent_v)
+        return fail(BGTQ_E_INVALID, "NULL cache buffer");
+    if (c->k_mode == BGTQ_K_BLOCKGTQ && (!c->bits || !c->sigma || !c->inv_sigma))
+        return fail(BGTQ_E_INVALID, "Block-GTQ keys need bits, sigma and inv_sigma");
+    if (c->k_mode == BGTQ_K_AFFINE && !c->k_zero) return fail(BGTQ_E_INVALID, "affine keys need k_zero");
+    if (c->v_mode == BGTQ_V_AFFINE && !c->v_zero) return fail(BGTQ_E_INVALID, "affine values need v_zero");
+    const int W = R / 3;
+    int64_t sB, sT, sH;
+    if (strides) {
+        sB = strides[0]; sT = strides[1]; sH = strides[2];
+    } else {
+        sH = D; sT = (int64_t)g.Hkv * D; sB = sT;
+    }
+    int64_t* nt = c->n_tokens + (size_t)layer * c->B;
+    int32_t* nhp = c->n_hp + (size_t)layer * c->B;
+    // Plan every sequence on copies of the bookkeeping: nothing changes unless all plans succeed.
+    std::vector<int64_t> pos(hp_pos, hp_pos + (size_t)c->B * R);
+    std::vector<int> nh(c->B), slot(c->B), leaving(c->B);
+    std::vector<int32_t> ev(W), ms(W), md(W);
+    bgtq::PermuteArgs pa{};
+    pa.Hkv = g.Hkv;
+    pa.n_recent = R;
+    int n_perm = 0, n_thin = 0;
+    for (int b = 0; b < c->B; ++b) {
+        pa.seq_first[b] = -1;
+        if (nhp[b] < 0 || nhp[b] > R || nhp[b] > nt[b])
+            return fail(BGTQ_E_INVALID, "sequence %d: n_hp %d inconsistent with n_tokens", b, nhp[b]);
+        const int64_t packed = nt[b] - nhp[b];
+        nh[b] = nhp[b];
+        int n_moves = 0;
+        rc = bgtq_logquant_plan(W, pos.data() + (size_t)b * R, &nh[b], nt[b], ev.data(), ms.data(), md.data(), &n_moves,
+                                &slot[b]);
+        if (rc < 0) return rc;
+        leaving[b] = rc;
+        if (rc == 0) continue;
+        if (packed + W > c->n_cap)
+            return fail(BGTQ_E_CAPACITY, "sequence %d: %lld packed tokens exceed n_cap %lld", b,
+                        (long long)(packed + W), (long long)c->n_cap);
+        // kept rows stay or fill the vacated slots below 2W; the leaving rows go to [2W, 3W) in order
+        int16_t* perm = pa.perm + n_perm;
+        for (int j = 0; j < R; ++j) perm[j] = (int16_t)j;
+        for (int m = 0; m < n_moves; ++m) perm[md[m]] = (int16_t)ms[m];
+        for (int i = 0; i < W; ++i) perm[2 * W + i] = (int16_t)ev[i];
+        pa.seq_first[b] = (int16_t)n_perm;
+        n_perm += R;
+        ++n_thin;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const size_t bh = (size_t)g.B * g.Hkv;
+    uint16_t* rk = (uint16_t*)c->recent_k + (size_t)layer * bh * R * D;
+    uint16_t* rv = (uint16_t*)c->recent_v + (size_t)layer * bh * R * D;
+    hipError_t e;
+    if (n_thin) {
+        pa.rows_k = rk;
+        pa.rows_v = rv;
+        e = bgtq::launch_permute(pa, c->B, s);
+        if (e != hipSuccess) return hip_fail(e, "store reorder");
+        // the leaving rows, now in store slots [2W, 3W), become packed positions [packed, packed + W)
+        bgtq::QuantArgs q{};
+        fill_quant_layer(c, g, layer, q);
+        q.src_k = rk;
+        q.src_v = rv;
+        q.dtype = BGTQ_F16;
+        q.sB = (int64_t)g.Hkv * R * D;
+        q.sT = D;
+        q.sH = (int64_t)R * D;
+        q.mod_n = 0;
+        int64_t max_tiles = 0;
+        for (int b = 0; b < c->B; ++b) {
+            const int64_t packed = nt[b] - nhp[b];
+            q.pos_lo[b] = packed;
+            q.pos_hi[b] = packed + leaving[b];
+            q.off[b] = packed - 2 * W;
+            q.tile0[b] = packed / TILE;
+            if (leaving[b]) max_tiles = std::max(max_tiles, (packed + leaving[b] - 1) / TILE - packed / TILE + 1);
+        }
+        {
+            ProfScope ps(BGTQ_PROF_QUANTIZE, s);
+            e = bgtq::launch_quant(q, c->B, max_tiles, s);
+        }
+        if (e != hipSuccess) return hip_fail(e, "quantize (leaving rows)");
+    }
+    // the new token's row enters its store slot (slot = position mod n_recent with position = slot)
+    bgtq::RingArgs ra{};
+    ra.k = k;
+    ra.v = v;
+    ra.dtype = dtype;
+    ra.sB = sB; ra.sT = sT; ra.sH = sH;
+    ra.ring_k = rk;
+    ra.ring_v = rv;
+    ra.Hkv = g.Hkv;
+    ra.n_recent = R;
+    for (int b = 0; b < c->B; ++b) {
+        ra.pos_lo[b] = slot[b];
+        ra.pos_hi[b] = slot[b] + 1;
+        ra.off[b] = slot[b];
+    }
+    e = bgtq::launch_ring(ra, c->B, 1, s);
+    if (e != hipSuccess) return hip_fail(e, "store write");
+    std::copy(pos.begin(), pos.end(), hp_pos);
+    for (int b = 0; b < c->B; ++b) {
+        nhp[b] = nh[b];
+        nt[b] += 1;
+    }
+    return ok();
+}
+
 int64_t bgtq_decode_workspace_bytes(const bgtq_cache* c, int n_splits) {
     bgtq::Geometry g;
     int rc = geometry(c, g);
@@ -585,7 +713,10 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
     bool any_recent = false;
     for (int b = 0; b < c->B; ++b) {
         if (nt[b] <= 0) return fail(BGTQ_E_INVALID, "sequence %d has an empty context", b);
-        const int64_t rec = c->n_recent > 0 ? std::min<int64_t>(nt[b], c->n_recent) : 0;
+        const int64_t rec = c->n_hp ? (int64_t)c->n_hp[(size_t)layer * c->B + b]
+                                    : (c->n_recent > 0 ? std::min<int64_t>(nt[b], c->n_recent) : 0);
+        if (rec < 0 || rec > c->n_recent || rec > nt[b])
+            return fail(BGTQ_E_INVALID, "sequence %d: %lld high-precision rows do not fit", b, (long long)rec);
         a.n_packed[b] = (int32_t)(nt[b] - rec);
         n_rec[b] = (int32_t)rec;
         if (a.n_packed[b] > c->n_cap) return fail(BGTQ_E_INVALID, "sequence %d exceeds n_cap", b);

@@ -126,7 +126,21 @@ struct RingArgs {
     int64_t pos_lo[BGTQ_MAXB], pos_hi[BGTQ_MAXB], off[BGTQ_MAXB];
 };
 
-// Launchers (bgtq_kernels.hip).  Return hipSuccess or the launch error.
+// Reorder the rows of the high-precision store (log-based filter): for a sequence b with
+// seq_first[b] >= 0, new row j of every kv head is old row perm[seq_first[b] + j], j < n_recent.
+constexpr int BGTQ_PERM_MAX = 1536;   // permutation entries carried in the kernel arguments
+constexpr int BGTQ_HP_ROWS_MAX = 512; // store rows a permutation workgroup stages in LDS
+struct PermuteArgs {
+    uint16_t* rows_k;           // [B][Hkv][n_recent][128] for this layer
+    uint16_t* rows_v;
+    int Hkv, n_recent;
+    int16_t seq_first[BGTQ_MAXB];
+    int16_t perm[BGTQ_PERM_MAX];
+};
+
+// Launchers (bgtq_kernels.hip; launch_permute in bgtq_logquant.hip).  Return hipSuccess or the
+// launch error.
+hipError_t launch_permute(const PermuteArgs& a, int B, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s);
 hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t s);

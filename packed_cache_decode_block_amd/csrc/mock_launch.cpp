@@ -101,6 +101,23 @@ hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t) 
     return hipSuccess;
 }
 
+hipError_t launch_permute(const PermuteArgs& a, int B, hipStream_t) {
+    if (!a.rows_k || !a.rows_v || a.n_recent < 1 || a.n_recent > BGTQ_HP_ROWS_MAX) return bad("permute: args");
+    for (int b = 0; b < B; ++b) {
+        const int f = a.seq_first[b];
+        if (f < 0) continue;
+        if (f + a.n_recent > BGTQ_PERM_MAX) return bad("permute: range");
+        std::string seen(a.n_recent, 0);
+        for (int j = 0; j < a.n_recent; ++j) {
+            const int r = a.perm[f + j];
+            if (r < 0 || r >= a.n_recent || seen[r]) return bad("permute: not a permutation");
+            seen[r] = 1;
+        }
+    }
+    note("permute");
+    return hipSuccess;
+}
+
 void arm_launch_events(hipEvent_t, hipEvent_t) {}
 void disarm_launch_events() {}
 

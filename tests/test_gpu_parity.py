@@ -503,3 +503,52 @@ def test_decode_step_rotated_keys():
                                   n_cap=n_cap, k_bits=w.k_bits, k_group=w.k_group, k_rot=signs)
         T.assert_close(out, pipeline.decode_layer(oc, q), f"rotated step {i} (context {pos})")
     _compare_cache(cache, oc, w)
+
+
+@pytest.mark.parametrize("wid,W,N", [(2, 4, 70), (3, 8, 100), (1, 2, 40)])
+def test_logquant_appends_match_oracle(wid, W, N):
+    """LogQuant's log-based filter through the device: after token-by-token appends, the packed
+    store equals the oracle's store of the leaving tokens in leaving order (bit-exact), the
+    high-precision store holds exactly the kept positions' fp16 rows, and decode matches the
+    oracle over the union of both."""
+    from oracle import logquant as lq
+    ov = {"L": 1, "B": 2} if wid == 3 else ({} if wid == 1 else {"L": 1})
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
+    print(f"[logquant {wid}] W={W} N={N} B={w.B} Hq={w.Hq} Hkv={w.Hkv}", flush=True)
+    n_cap, R = 128, 3 * W
+    m = T.meta(w, 0)
+    K, V, _ = T.inputs(w, 0, N)
+    cache = P.PackedCache(L=1, B=w.B, Hq=w.Hq, Hkv=w.Hkv, n_cap=n_cap, budget_units=w.k_budget_units,
+                          v_bits=w.v_bits, logquant_w=W)
+    cache.set_metadata(0, m.bits, m.sigma, m.r)
+    kd = T.to_dev(np.transpose(K, (0, 2, 1, 3)), w.dtype)
+    vd = T.to_dev(np.transpose(V, (0, 2, 1, 3)), w.dtype)
+    checks = {3 * W + 1, 3 * W + W // 2 + 7, N}
+    for p in range(N):
+        cache.logquant_append(0, kd[:, p:p + 1], vd[:, p:p + 1])
+        if p + 1 not in checks:
+            continue
+        torch.cuda.synchronize()
+        kept, left = lq.select(p + 1, W)
+        assert (cache.n_tokens[0] == p + 1).all() and (cache.n_hp[0] == len(kept)).all()
+        # every token passes through the fp16 store first, so the packed rows are its fp16 values
+        k16 = K[:, :, left].astype(np.float16).astype(np.float32)
+        v16 = V[:, :, left].astype(np.float16).astype(np.float32)
+        oc = pipeline.build_layer(k16, v16, k_mode="gtq", v_mode="codebook", v_bits=w.v_bits, n_cap=n_cap, meta=m)
+        _compare_cache(cache, oc, w)
+        rk = T.layer_view(cache.recent_k, 1, 0, (w.B, w.Hkv, R, 128)).cpu().numpy()
+        rv = T.layer_view(cache.recent_v, 1, 0, (w.B, w.Hkv, R, 128)).cpu().numpy()
+        for b in range(w.B):
+            held = cache.hp_pos[0, b, :len(kept)]
+            assert sorted(held.tolist()) == kept
+            np.testing.assert_array_equal(rk[b, :, :len(kept)].view(np.uint16),
+                                          K[b][:, held].astype(np.float16).view(np.uint16), f"store k b={b}")
+            np.testing.assert_array_equal(rv[b, :, :len(kept)].view(np.uint16),
+                                          V[b][:, held].astype(np.float16).view(np.uint16), f"store v b={b}")
+        oc.recent_k = K[:, :, kept].astype(np.float16)
+        oc.recent_v = V[:, :, kept].astype(np.float16)
+        oc.n_recent_valid = len(kept)
+        q = np.stack([np.concatenate([synth.queries(w, 0, h, b, p + 1) for h in range(w.Hkv)]) for b in range(w.B)])
+        out = cache.decode_attention(0, T.to_dev(q, w.dtype)).cpu().numpy()
+        e = T.assert_close(out, pipeline.decode_layer(oc, q), f"logquant context {p + 1}")
+        print(f"  context {p + 1}: {len(left)} packed + {len(kept)} fp16, max abs err {e:.2e}", flush=True)

@@ -151,3 +151,43 @@ def test_decode_step_failure_leaves_state(mock):
     mock.bgtq_mock_reset()
     _call_ok(mock, step(0, need))                                 # n_new = 0 attends without appending
     assert "quant" not in mock.bgtq_mock_log().decode() and (nt[0] == 5).all()
+
+
+def test_logquant_append_plan_and_failures(mock):
+    """The log-based filter's appends: below the 3W ceiling only the store write; at it, the store
+    reorder (a permutation), the quantize of the W leaving rows, then the write; the packed/high-
+    precision split follows the oracle's counts; errors change nothing."""
+    from oracle import logquant as lq
+    W = 4
+    nt = np.zeros((1, 2), np.int64)
+    d = _desc(nt, L=1, n_recent=3 * W)
+    n_hp = np.zeros((1, 2), np.int32)
+    d.n_hp = n_hp.ctypes.data_as(C.POINTER(C.c_int32))
+    hp = np.zeros((2, 3 * W), np.int64)
+    q = C.c_void_p(FAKE + 0x50000000)
+    p64 = C.POINTER(C.c_int64)
+    for p in range(40):
+        mock.bgtq_mock_reset()
+        log = _call_ok(mock, mock.bgtq_logquant_append(C.byref(d), 0, q, q, 2, None, hp.ctypes.data_as(p64), None))
+        steps = [ln for ln in log.splitlines() if ln]
+        kept, left = lq.select(p + 1, W)
+        thinned = len(left) > len(lq.select(p, W)[1])          # the oracle halved at this token
+        assert steps == (["permute", "quant", "ring"] if thinned else ["ring"]), (p, steps)
+        assert (nt[0] == p + 1).all() and (n_hp[0] == len(kept)).all()
+        assert sorted(hp[0, :n_hp[0, 0]]) == kept
+    # the positional-ring entry points refuse a cache under the log-based filter
+    assert mock.bgtq_quantize_append(C.byref(d), 0, q, q, 2, 1, None, None) == _lib.E_INVALID
+    # errors: no store positions array, an inconsistent count, capacity; nothing changes
+    snap = (nt.copy(), n_hp.copy(), hp.copy())
+    assert mock.bgtq_logquant_append(C.byref(d), 0, q, q, 2, None, None, None) == _lib.E_INVALID
+    n_hp[0, 1] = 3 * W + 1
+    assert mock.bgtq_logquant_append(C.byref(d), 0, q, q, 2, None, hp.ctypes.data_as(p64), None) == _lib.E_INVALID
+    n_hp[0, 1] = snap[1][0, 1]
+    d2 = _desc(nt, L=1, n_recent=3 * W, n_cap=64)
+    d2.n_hp = d.n_hp
+    while n_hp[0, 0] < 3 * W:                                   # fill to the ceiling, then overflow n_cap
+        _call_ok(mock, mock.bgtq_logquant_append(C.byref(d2), 0, q, q, 2, None, hp.ctypes.data_as(p64), None))
+    nt[0] = 100
+    pre = (nt.copy(), n_hp.copy(), hp.copy())
+    assert mock.bgtq_logquant_append(C.byref(d2), 0, q, q, 2, None, hp.ctypes.data_as(p64), None) == _lib.E_CAPACITY
+    assert (nt == pre[0]).all() and (n_hp == pre[1]).all() and (hp == pre[2]).all()
