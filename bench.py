@@ -204,6 +204,7 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--no-step", action="store_true", help="skip the append-then-attend decode step timing")
+    ap.add_argument("--no-logquant", action="store_true", help="skip the log-based filter append timing")
     ap.add_argument("--k-rotation", action="store_true",
                     help="affine keys stored under the randomized Hadamard rotation (affine-key workloads)")
     ap.add_argument("--uniform-keys", action="store_true",
@@ -353,6 +354,38 @@ def main():
             "append_us_per_layer": round((sec_s - sec) * 1e6 / w.L, 2)}
         log(f"[bench] decode step (append 1 token + attend) {sec_s * 1e3:.3f} ms, "
             f"{sec_s * 1e6 / w.L:.2f} us per layer ({(sec_s - sec) * 1e6 / w.L:.2f} us for the append)")
+    if not args.no_logquant and w.k_mode == "gtq":
+        # LogQuant's log-based filter (bgtq_logquant_append): 2048 one-token appends per kv head into
+        # a W = 64 store (192 fp16 rows) of this workload's format, a halving every 64 tokens; the
+        # wall time per call includes the host plan, the leaving-row quantize is also event-timed.
+        W_lq, n_lq = 64, 2048
+        lqc = P.PackedCache(L=1, B=1, Hq=w.Hq, Hkv=w.Hkv, n_cap=n_lq, budget_units=w.k_budget_units,
+                            v_bits=w.v_bits, logquant_w=W_lq)
+        lqc.set_metadata(0, np.full((w.Hkv, 64), w.k_budget_units // 64, np.uint8),
+                         np.ones((w.Hkv, 64), np.float32), np.ones((w.Hkv, 64), np.float32))
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        td = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        rows = [torch.randn((1, n_lq, w.Hkv, w.d), generator=gen, device="cuda").to(td) for _ in range(2)]
+        for p in range(3 * W_lq):   # fill the store (no timing)
+            lqc.logquant_append(0, rows[0][:, p:p + 1], rows[1][:, p:p + 1])
+        torch.cuda.synchronize()
+        P.bgtq_profile_enable(n_lq)
+        t0 = time.perf_counter()
+        for p in range(3 * W_lq, n_lq):
+            lqc.logquant_append(0, rows[0][:, p:p + 1], rows[1][:, p:p + 1])
+        torch.cuda.synchronize()
+        t_lq = time.perf_counter() - t0
+        nq_lq, tq_lq, _, _ = P.bgtq_profile_read(P.PROF_QUANTIZE)
+        P.bgtq_profile_enable(0)
+        n_calls = n_lq - 3 * W_lq
+        result["logquant_append"] = {
+            "entry": "bgtq_logquant_append", "W": W_lq, "store_rows": 3 * W_lq, "calls": n_calls,
+            "halvings": nq_lq, "us_per_call": round(t_lq * 1e6 / n_calls, 2),
+            "leaving_quantize_us": round(tq_lq * 1e3 / max(nq_lq, 1), 2),
+            "packed_after": int(lqc.n_tokens[0, 0] - lqc.n_hp[0, 0]), "fp16_after": int(lqc.n_hp[0, 0])}
+        log(f"[bench] log-based filter: {t_lq * 1e6 / n_calls:.1f} us per one-token append (host plan included), "
+            f"{nq_lq} halvings, leaving-row quantize {tq_lq * 1e3 / max(nq_lq, 1):.1f} us each")
+        del lqc, rows
     del ws
     if not args.no_fp16:
         del cache
