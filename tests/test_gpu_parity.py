@@ -505,22 +505,26 @@ def test_decode_step_rotated_keys():
     _compare_cache(cache, oc, w)
 
 
-@pytest.mark.parametrize("wid,W,N", [(2, 4, 70), (3, 8, 100), (1, 2, 40)])
+@pytest.mark.parametrize("wid,W,N", [(2, 4, 70), (3, 8, 100), (1, 2, 40), (4, 4, 60)])
 def test_logquant_appends_match_oracle(wid, W, N):
     """LogQuant's log-based filter through the device: after token-by-token appends, the packed
     store equals the oracle's store of the leaving tokens in leaving order (bit-exact), the
     high-precision store holds exactly the kept positions' fp16 rows, and decode matches the
     oracle over the union of both."""
     from oracle import logquant as lq
-    ov = {"L": 1, "B": 2} if wid == 3 else ({} if wid == 1 else {"L": 1})
+    ov = {"L": 1, "B": 2} if wid == 3 else ({} if wid == 1 else {"L": 1, "B": 1})
     w = synth.reduced(synth.WORKLOADS[wid], **ov)
-    print(f"[logquant {wid}] W={W} N={N} B={w.B} Hq={w.Hq} Hkv={w.Hkv}", flush=True)
+    print(f"[logquant {wid}] W={W} N={N} B={w.B} Hq={w.Hq} Hkv={w.Hkv} keys={w.k_mode}", flush=True)
     n_cap, R = 128, 3 * W
     m = T.meta(w, 0)
     K, V, _ = T.inputs(w, 0, N)
-    cache = P.PackedCache(L=1, B=w.B, Hq=w.Hq, Hkv=w.Hkv, n_cap=n_cap, budget_units=w.k_budget_units,
-                          v_bits=w.v_bits, logquant_w=W)
-    cache.set_metadata(0, m.bits, m.sigma, m.r)
+    cache = P.PackedCache(L=1, B=w.B, Hq=w.Hq, Hkv=w.Hkv, n_cap=n_cap,
+                          k_mode=P.K_BLOCKGTQ if w.k_mode == "gtq" else P.K_AFFINE,
+                          budget_units=w.k_budget_units or 128, k_bits=w.k_bits or 4, k_group=w.k_group or 32,
+                          v_mode=P.V_CODEBOOK if w.v_mode == "codebook" else P.V_AFFINE, v_bits=w.v_bits,
+                          logquant_w=W)
+    if m is not None:
+        cache.set_metadata(0, m.bits, m.sigma, m.r)
     kd = T.to_dev(np.transpose(K, (0, 2, 1, 3)), w.dtype)
     vd = T.to_dev(np.transpose(V, (0, 2, 1, 3)), w.dtype)
     checks = {3 * W + 1, 3 * W + W // 2 + 7, N}
@@ -534,7 +538,8 @@ def test_logquant_appends_match_oracle(wid, W, N):
         # every token passes through the fp16 store first, so the packed rows are its fp16 values
         k16 = K[:, :, left].astype(np.float16).astype(np.float32)
         v16 = V[:, :, left].astype(np.float16).astype(np.float32)
-        oc = pipeline.build_layer(k16, v16, k_mode="gtq", v_mode="codebook", v_bits=w.v_bits, n_cap=n_cap, meta=m)
+        oc = pipeline.build_layer(k16, v16, k_mode=w.k_mode, v_mode=w.v_mode, v_bits=w.v_bits, n_cap=n_cap, meta=m,
+                                  k_bits=w.k_bits or 4, k_group=w.k_group or 32)
         _compare_cache(cache, oc, w)
         rk = T.layer_view(cache.recent_k, 1, 0, (w.B, w.Hkv, R, 128)).cpu().numpy()
         rv = T.layer_view(cache.recent_v, 1, 0, (w.B, w.Hkv, R, 128)).cpu().numpy()
