@@ -219,9 +219,11 @@ int bgtq_logquant_plan(int W, int64_t *hp_pos, int *n_hp, int64_t pos, int32_t *
  * and appended to the packed cache.  The store is then compacted, as the plan describes.
  * k, v: device rows [B][1][Hkv][128] in `dtype` (strides as bgtq_quantize_append, n_new = 1).
  * hp_pos: host int64 [B][n_recent], the token position each store row holds; maintained here.
- * On success n_tokens, n_hp and hp_pos advance.  Errors (nothing changed): those of
- * bgtq_quantize_append, BGTQ_E_INVALID (no n_hp, bad n_recent, inconsistent counts),
- * BGTQ_E_UNSUPPORTED (B * n_recent above 1536).
+ * On success n_tokens, n_hp and hp_pos advance.  Errors found before any launch change nothing:
+ * those of bgtq_quantize_append, BGTQ_E_INVALID (no n_hp, bad n_recent, inconsistent counts),
+ * BGTQ_E_UNSUPPORTED (B * n_recent above 1536).  BGTQ_E_HIP (a launch failed after an earlier
+ * one of the same call was enqueued) leaves the host bookkeeping unchanged and the layer's
+ * device store and packed tail unspecified.
  */
 int bgtq_logquant_append(bgtq_cache *c, int layer, const void *k, const void *v, int dtype,
                          const int64_t *strides, int64_t *hp_pos, void *stream);

@@ -215,8 +215,8 @@ class PackedCache:
         if self.n_hp is None:
             raise ValueError("the cache was built without logquant_w")
         strides = self._kv_strides(k, v)
-        if k.shape[1] != 1:
-            raise ValueError("the log-based filter appends one token per call")
+        if tuple(k.shape) != (self.desc.B, 1, self.desc.Hkv, 128):
+            raise ValueError(f"k and v must be [{self.desc.B}, 1, {self.desc.Hkv}, 128]: one token per sequence")
         check(lib.bgtq_logquant_append(C.byref(self.desc), layer, _ptr(k), _ptr(v), _dtype_code(k), strides,
                                        self.hp_pos[layer].ctypes.data_as(C.POINTER(C.c_int64)), _stream(stream)))
 
