@@ -213,8 +213,8 @@ def main():
                     help="only run a plain device copy of MB megabytes 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU part "
-              "in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the decode path runs on one GPU's "
+              "share of the heads and context", file=sys.stderr)
         sys.exit(2)
 
     import torch
