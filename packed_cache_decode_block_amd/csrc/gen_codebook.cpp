@@ -2,87 +2,122 @@
 //
 // TQ-MSE (review page §1 Key Terms; abstract of "RoPE-Aware Bit Allocation for KV-Cache
 // Quantization") quantizes each coordinate with a distortion-optimal scalar quantizer whose
-// error falls as 4^-b.  The table used by this library for b = 1..8: the Lloyd-Max quantizer
-// of N(0,1) (every centroid the mean of its cell, every threshold the midpoint of its two
-// centroids), centroids rounded to the nearest fp16, thresholds = exact midpoints of the
-// rounded centroids (exact in fp32).  The fixed point is solved with Newton's method on the
-// symmetric positive half (tridiagonal Jacobian).
+// error falls as 4^-b.  The table used by this library for b = 1..8: the minimum-MSE scalar
+// quantizer of N(0,1) with 2^b levels (every centroid the mean of its cell, every threshold the
+// midpoint of its two centroids), centroids rounded to the nearest fp16, thresholds = exact
+// midpoints of the rounded centroids (exact in fp32).
+//
+// Method: Max's shooting procedure (J. Max, "Quantizing for minimum distortion", 1960, §III).
+// The quantizer is symmetric, so with an even level count the positive half starts at the
+// threshold 0.  A trial first centroid c_0 fixes the whole positive half by marching outward:
+// the next threshold t_{k+1} is the point where the mean of the cell [t_k, t_{k+1}] equals c_k
+// (found by bisection; the cell mean grows with its right end), and the next centroid is the
+// mirror c_{k+1} = 2 t_{k+1} - c_k.  The last cell [t_{h-1}, inf) must then have mean c_{h-1};
+// c_0 is bisected on the sign of that mismatch (a march that cannot place a threshold means c_0
+// was too large).  Cell means of finite cells are ratios of two 32-point Gauss-Legendre sums of
+// x phi(x) and phi(x) over the cell; the tail cell's mean is phi(a) / Q(a).  Long double
+// throughout; bisections run until the interval stops shrinking.
 //
 // Usage: gen_codebook <out.h>   writes constant tables consumed by host and device code.
 #include <cinttypes>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
 namespace {
 
-const double kInvSqrt2Pi = 0.3989422804014327;  // 1/sqrt(2*pi)
+typedef long double ld;
 
-double pdf(double x) { return std::exp(-0.5 * x * x) * kInvSqrt2Pi; }
-double upper_tail(double x) { return 0.5 * std::erfc(x / std::sqrt(2.0)); }
+const ld kPi = 3.14159265358979323846264338327950288L;
 
-// Inverse normal CDF by bisection on the upper tail (only used for the starting point).
-double probit(double p) {
-    double lo = -40, hi = 40;
-    for (int i = 0; i < 200; ++i) {
-        double mid = 0.5 * (lo + hi);
-        if (1.0 - upper_tail(mid) < p) lo = mid; else hi = mid;
+ld pdf(ld x) { return std::exp(-0.5L * x * x) / std::sqrt(2.0L * kPi); }
+
+// Nodes and weights of n-point Gauss-Legendre quadrature on [-1, 1]: roots of P_n by Newton's
+// method from the Chebyshev-like first guesses, weights 2 / ((1 - x^2) P_n'(x)^2).
+struct GaussLegendre {
+    std::vector<ld> x, w;
+    explicit GaussLegendre(int n) : x(n), w(n) {
+        for (int i = 0; i < n; ++i) {
+            ld z = std::cos(kPi * (i + 0.75L) / (n + 0.5L)), dp = 0;
+            for (int it = 0; it < 100; ++it) {
+                ld p0 = 1, p1 = z;
+                for (int k = 2; k <= n; ++k) {
+                    const ld p2 = ((2 * k - 1) * z * p1 - (k - 1) * p0) / k;
+                    p0 = p1;
+                    p1 = p2;
+                }
+                dp = n * (z * p1 - p0) / (z * z - 1);
+                const ld dz = p1 / dp;
+                z -= dz;
+                if (std::fabs(dz) < 1e-19L) break;
+            }
+            x[i] = z;
+            w[i] = 2 / ((1 - z * z) * dp * dp);
+        }
     }
-    return 0.5 * (lo + hi);
+};
+
+const GaussLegendre& gl() {
+    static const GaussLegendre q(32);
+    return q;
 }
 
-// Positive-half centroids c[0..h-1] of the 2^b-level Lloyd-Max quantizer.
-std::vector<double> solve(int b) {
-    const int n = 1 << b, h = n / 2;
-    std::vector<double> c(h), t(h + 1), mu(h), da(h), db(h);
-    for (int k = 0; k < h; ++k) c[k] = probit((k + 0.5) / n + 0.5);
-    for (int it = 0; it < 100; ++it) {
-        t[0] = 0.0;
-        for (int k = 1; k < h; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
-        for (int k = 0; k < h; ++k) {
-            const double a = t[k];
-            const bool last = (k == h - 1);
-            const double fa = pdf(a);
-            double num, mass, fb = 0.0, bb = 0.0;
-            if (last) {
-                num = fa;
-                mass = upper_tail(a);
-            } else {
-                bb = t[k + 1];
-                fb = pdf(bb);
-                num = -fa * std::expm1(-0.5 * (bb - a) * (bb + a));
-                mass = upper_tail(a) - upper_tail(bb);
-            }
-            mu[k] = num / mass;
-            da[k] = fa / mass * (mu[k] - a);
-            db[k] = last ? 0.0 : fb / mass * (bb - mu[k]);
-        }
-        // (I - J) x = mu - c with J tridiagonal: J[k][k-1] = da/2, J[k][k] = (da+db)/2, J[k][k+1] = db/2
-        std::vector<double> sub(h, 0.0), dia(h, 1.0), sup(h, 0.0), rhs(h), cp(h), dp(h), x(h);
-        for (int k = 0; k < h; ++k) {
-            if (k >= 1) { sub[k] = -0.5 * da[k]; dia[k] -= 0.5 * da[k]; }
-            if (k + 1 < h) { sup[k] = -0.5 * db[k]; dia[k] -= 0.5 * db[k]; }
-            rhs[k] = mu[k] - c[k];
-        }
-        cp[0] = sup[0] / dia[0];
-        dp[0] = rhs[0] / dia[0];
-        for (int k = 1; k < h; ++k) {
-            const double m = dia[k] - sub[k] * cp[k - 1];
-            cp[k] = sup[k] / m;
-            dp[k] = (rhs[k] - sub[k] * dp[k - 1]) / m;
-        }
-        x[h - 1] = dp[h - 1];
-        for (int k = h - 2; k >= 0; --k) x[k] = dp[k] - cp[k] * x[k + 1];
-        double step = 0.0;
-        for (int k = 0; k < h; ++k) {
-            c[k] += x[k];
-            step = std::fmax(step, std::fabs(x[k]));
-        }
-        if (step < 1e-13) break;
+// Mean of N(0,1) restricted to [a, b] (b may be +inf).
+ld cell_mean(ld a, ld b) {
+    if (std::isinf(b)) return pdf(a) / (0.5L * std::erfc(a / std::sqrt(2.0L)));
+    const ld mid = 0.5L * (a + b), half = 0.5L * (b - a);
+    ld m0 = 0, m1 = 0;
+    for (size_t i = 0; i < gl().x.size(); ++i) {
+        const ld x = mid + half * gl().x[i], f = gl().w[i] * pdf(x);
+        m0 += f;
+        m1 += f * x;
     }
-    return c;
+    return m1 / m0;
+}
+
+// March the positive half from first centroid c0 (h centroids).  Returns false when some
+// threshold cannot be placed (c0 too large); else fills c and the tail mismatch
+// mean(last cell) - c[h-1].
+bool march(ld c0, int h, std::vector<ld>& c, ld& mismatch) {
+    c.assign(1, c0);
+    ld t = 0;
+    for (int k = 0; k + 1 < h; ++k) {
+        const ld ck = c.back();
+        if (!(ck < cell_mean(t, INFINITY))) return false;
+        ld lo = t, hi = t + 1;
+        while (cell_mean(t, hi) < ck) hi = t + 2 * (hi - t);
+        for (;;) {
+            const ld mid = 0.5L * (lo + hi);
+            if (mid <= lo || mid >= hi) break;
+            (cell_mean(t, mid) < ck ? lo : hi) = mid;
+        }
+        t = 0.5L * (lo + hi);
+        c.push_back(2 * t - ck);
+    }
+    mismatch = cell_mean(t, INFINITY) - c.back();
+    return true;
+}
+
+// Positive-half centroids c[0..h-1] of the 2^b-level quantizer.
+std::vector<double> solve(int b) {
+    const int h = (1 << b) / 2;
+    ld lo = 0, hi = std::sqrt(2.0L / kPi);  // c0 lies below the mean of the whole half line
+    std::vector<ld> c;
+    ld mis = 0;
+    for (;;) {
+        const ld mid = 0.5L * (lo + hi);
+        if (mid <= lo || mid >= hi) break;
+        const bool ok = march(mid, h, c, mis);
+        (ok && mis >= 0 ? lo : hi) = mid;
+    }
+    if (!march(lo, h, c, mis)) {
+        std::fprintf(stderr, "march failed at the converged first centroid (b=%d)\n", b);
+        std::exit(1);
+    }
+    return std::vector<double>(c.begin(), c.end());
 }
 
 // Round a double to the nearest fp16 (ties to even) directly, without passing through float.
@@ -131,6 +166,11 @@ int main(int argc, char** argv) {
         const int h = (int)pos.size();
         std::vector<uint16_t> ch(2 * h);
         for (int k = 0; k < h; ++k) {
+            // the fp16 rounding must not depend on the solver's last digits
+            if (to_half(pos[k] * (1 + 1e-10)) != to_half(pos[k]) || to_half(pos[k] * (1 - 1e-10)) != to_half(pos[k])) {
+                std::fprintf(stderr, "centroid %d of width %d lies within 1e-10 of an fp16 rounding tie\n", k, b);
+                return 1;
+            }
             ch[h + k] = to_half(pos[k]);
             ch[h - 1 - k] = to_half(-pos[k]);
         }

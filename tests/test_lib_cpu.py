@@ -1,5 +1,6 @@
 """Host-side checks of the C ABI that need no GPU: exports, tables, allocator, sizes, validation."""
 import ctypes as C
+import math
 import re
 import os
 
@@ -28,6 +29,55 @@ def test_codebook_tables_match_oracle(b):
     oc, ot = ocb.codebook(b)
     np.testing.assert_array_equal(c16.view(np.uint16), oc.view(np.uint16))
     np.testing.assert_array_equal(thr.view(np.uint32), ot.view(np.uint32))
+
+
+def _golden_rows():
+    rows = {}
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "lloyd_max_gaussian.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        b, cents, thr, _ = [f.strip() for f in line.split("|")]
+        rows[int(b)] = ([float(x) for x in cents.split()], [float(x) for x in thr.split()])
+    return rows
+
+
+def _fp16_ulp(x):
+    return float(np.spacing(np.float16(abs(x))))
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_library_codebook_matches_textbook(b):
+    """The library's own table against Max (1960), Table I: each printed centroid and threshold
+    within half a unit of its 4th digit plus half an fp16 ulp (the table is fp16-rounded)."""
+    cents, thr = _golden_rows()[b]
+    c16, t32 = P.bgtq_codebook(b)
+    c = c16.astype(np.float64)
+    h = len(c) // 2
+    np.testing.assert_array_equal(c[:h], -c[::-1][:h])  # symmetric
+    for got, want in zip(c[h:], cents):
+        assert abs(got - want) <= 0.5 * 10 ** (math.floor(math.log10(want)) - 3) + 0.5 * _fp16_ulp(want), (got, want)
+    for got, want in zip(t32.astype(np.float64)[h:], thr):
+        assert abs(got - want) <= 0.5 * 10 ** (math.floor(math.log10(want)) - 3) + 0.5 * _fp16_ulp(want), (got, want)
+
+
+@pytest.mark.parametrize("b", range(1, 9))
+def test_library_codebook_centroid_condition(b):
+    """Every library centroid is the mean of N(0,1) over its own cell (cell ends = the library's
+    thresholds), up to the fp16 rounding of the centroids: within 1.5 fp16 ulps.  Thresholds are
+    the exact midpoints of adjacent centroids.  Cell means by adaptive quadrature."""
+    from scipy import integrate
+    c16, t32 = P.bgtq_codebook(b)
+    c = c16.astype(np.float64)
+    t = t32.astype(np.float64)
+    np.testing.assert_array_equal(t, 0.5 * (c[:-1] + c[1:]))
+    assert np.all(np.diff(c) > 0)
+    edges = np.concatenate([[-np.inf], t, [np.inf]])
+    pdf = lambda x: math.exp(-0.5 * x * x) / math.sqrt(2 * math.pi)
+    for m in range(len(c) // 2, len(c)):
+        lo, hi = edges[m], edges[m + 1]
+        mass = integrate.quad(pdf, lo, hi, epsabs=0, epsrel=1e-12)[0]
+        first = integrate.quad(lambda x: x * pdf(x), lo, hi, epsabs=0, epsrel=1e-12)[0]
+        assert abs(first / mass - c[m]) <= 1.5 * _fp16_ulp(c[m]), (m, first / mass, c[m])
 
 
 def test_codebook_rejects_bad_width():

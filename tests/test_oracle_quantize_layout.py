@@ -142,6 +142,36 @@ def test_k_record_hand_worked():
     assert w.shape == (1, 1) and int(w[0, 0]) == want
 
 
+@pytest.mark.parametrize("b", [2, 4, 8])
+def test_affine_k_record_hand_worked(b):
+    """Affine key record: coordinate j at bits [b*j, b*j + b) of a little-endian stream of b*4
+    dwords, so dword k holds coordinates 32k/b .. 32(k+1)/b - 1, coordinate j at bit (b*j) % 32.
+    Hand-built dwords: the codes 1, 2, 3, 0, ... (repeating mod 2^b) over the first dword, the top
+    code 2^b - 1 in the last coordinate, zeros elsewhere except coordinate 32/b (the first of
+    dword 1) set to 1."""
+    per = 32 // b
+    codes = np.zeros((1, 128), int)
+    first = [(j + 1) % (1 << b) for j in range(per)]   # 1, 2, 3, 0 for b = 2; 1..8 for b = 4; 1..4 for b = 8
+    codes[0, :per] = first
+    codes[0, per] = 1
+    codes[0, 127] = (1 << b) - 1
+    w = layout.k_affine_words(codes, b)
+    assert w.shape == (1, 4 * b)
+    want0 = sum(v << (b * j) for j, v in enumerate(first))
+    assert int(w[0, 0]) == want0
+    assert int(w[0, 1]) == 1                            # coordinate 32/b at bit 0 of dword 1
+    assert int(w[0, -1]) == ((1 << b) - 1) << (32 - b)  # coordinate 127 in the top bits
+    assert not np.any(w[0, 2:-1])
+    # spelled out per width
+    if b == 2:
+        assert int(w[0, 0]) == 0b00_11_10_01_00_11_10_01_00_11_10_01_00_11_10_01
+    if b == 4:
+        assert int(w[0, 0]) == 0x87654321
+    if b == 8:
+        assert int(w[0, 0]) == 0x04030201
+    np.testing.assert_array_equal(layout.k_affine_codes(w, b), codes)
+
+
 def test_straddling_field_round_trip():
     rng = np.random.default_rng(11)
     for _ in range(20):
