@@ -55,6 +55,16 @@ def decode_kernel_name(w) -> str:
     return "k_decode_mx" if (w.k_mode == "gtq" and w.Hq // w.Hkv >= 4) else "k_decode"
 
 
+def arithmetic(w):
+    """(dtype, description) of the arithmetic the workload's decode kernel runs."""
+    if decode_kernel_name(w) == "k_decode_mx" or (w.k_mode != "gtq" and w.Hq // w.Hkv >= 4):
+        return "f16", (f"{w.dtype} activations in; q.k and P.V on the matrix cores with fp16 operands "
+                       "(key centroids exact in fp16, the scaled query as fp16 high + low parts, softmax "
+                       "weights rounded to fp16) accumulated in fp32; softmax and output in fp32")
+    return "f32", (f"{w.dtype} activations in; q.k as fp32 FMAs on the vector ALUs; P.V as fp16 dot products "
+                   "(fp16 centroids times softmax weights rounded to fp16) accumulated in fp32")
+
+
 def measured_traffic(wid: int, kernel: str = "k_decode_mx"):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary of this
     workload (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None when there is
@@ -295,7 +305,7 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": arithmetic(w)[0], "arithmetic": arithmetic(w)[1], "data": "synthetic",
         "config": {"workload": w.name, "layers": w.L, "batch": w.B, "context": w.N, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.d, "k_format": "blockgtq" if w.k_mode == "gtq" else "affine",
                    "k_bits_per_dim": (w.k_budget_units / 64) if w.k_mode == "gtq" else w.k_bits,
