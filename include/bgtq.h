@@ -281,6 +281,22 @@ int bgtq_decode_step(bgtq_cache *c, int layer, const void *k, const void *v, con
                      int dtype, int64_t n_new, const int64_t *strides, float *out, void *ws,
                      size_t ws_bytes, int n_splits, void *stream);
 
+/*
+ * bgtq_decode_attention without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The split-K partials go to a fixed array of BGTQ_NOALLOC_SCRATCH_BYTES bytes that the library
+ * keeps on each GPU it runs on until the process ends (looked up on the first call on a device);
+ * the call itself allocates nothing.  Every call on one GPU shares that GPU's array, so calls that
+ * overlap on one GPU (other streams, other threads) race; calls in order on one stream do not.
+ * n_splits = 0 takes the library's split count, reduced so that the partials
+ * (B * Hq * (splits + 1 if n_recent > 0) * 528 bytes) fit the array; an explicit n_splits whose
+ * partials do not fit is BGTQ_E_UNSUPPORTED, as is a geometry for which one split does not fit.
+ * Other arguments, results and errors as bgtq_decode_attention.
+ */
+#define BGTQ_NOALLOC_SCRATCH_BYTES (4 << 20)
+int bgtq_decode_attention_noalloc(const bgtq_cache *c, int layer, const void *q, int dtype, float *out,
+                                  int n_splits, void *stream);
+
 /* Workspace bytes for bgtq_fp16_decode_attention. */
 int64_t bgtq_fp16_decode_workspace_bytes(int64_t N, int B, int Hq, int Hkv, int n_splits);
 

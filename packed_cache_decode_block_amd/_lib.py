@@ -20,7 +20,8 @@ ENERGY_CHUNK = 16  # BGTQ_ENERGY_CHUNK: calibration tokens per workgroup of bgtq
 SYMBOLS = ["bgtq_last_error", "bgtq_version", "bgtq_codebook", "bgtq_allocate", "bgtq_allocate_rate",
            "bgtq_logquant_plan", "bgtq_logquant_append", "bgtq_block_energy", "bgtq_cache_bytes", "bgtq_quantize_append", "bgtq_decode_workspace_bytes", "bgtq_decode_attention",
            "bgtq_decode_step", "bgtq_fp16_decode_workspace_bytes", "bgtq_fp16_decode_attention", "bgtq_profile_enable",
-           "bgtq_profile_read"]
+           "bgtq_profile_read", "bgtq_decode_attention_noalloc"]
+NOALLOC_SCRATCH_BYTES = 4 << 20  # BGTQ_NOALLOC_SCRATCH_BYTES
 PROF_DECODE, PROF_FP16_DECODE, PROF_QUANTIZE = 0, 1, 2
 
 
@@ -42,8 +43,9 @@ class CacheDesc(C.Structure):
                 ("n_hp", C.POINTER(C.c_int32))]
 
 
-def bind(path: str):
-    """Load a library exporting the C ABI of include/bgtq.h and declare its prototypes."""
+def bind(path: str, optional=()):
+    """Load a library exporting the C ABI of include/bgtq.h and declare its prototypes (names in
+    `optional` may be absent, e.g. from the host-only test library)."""
     lib = C.CDLL(path)
     P, I, I64, SZ, D = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.POINTER(C.c_double)
     F = C.POINTER(C.c_float)
@@ -58,6 +60,7 @@ def bind(path: str):
         "bgtq_quantize_append": (I, [C.POINTER(CacheDesc), I, P, P, I, I64, C.POINTER(C.c_int64), P]),
         "bgtq_decode_workspace_bytes": (I64, [C.POINTER(CacheDesc), I]),
         "bgtq_decode_attention": (I, [C.POINTER(CacheDesc), I, P, I, P, P, SZ, I, P]),
+        "bgtq_decode_attention_noalloc": (I, [C.POINTER(CacheDesc), I, P, I, P, I, P]),
         "bgtq_logquant_plan": (I, [I, C.POINTER(C.c_int64), C.POINTER(C.c_int), I64, C.POINTER(C.c_int32),
                                    C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int), C.POINTER(C.c_int)]),
         "bgtq_logquant_append": (I, [C.POINTER(CacheDesc), I, P, P, I, C.POINTER(C.c_int64), C.POINTER(C.c_int64), P]),
@@ -68,6 +71,8 @@ def bind(path: str):
         "bgtq_profile_read": (I, [I, C.POINTER(C.c_int), D, D, D]),
     }
     for name, (res, args) in sig.items():
+        if name in optional and not hasattr(lib, name):
+            continue
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = res, args
     return lib

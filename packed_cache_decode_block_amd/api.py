@@ -258,6 +258,15 @@ class PackedCache:
         return out
 
 
+    def decode_attention_noalloc(self, layer: int, q, out, n_splits: int = 0, stream=None):
+        """As decode_attention, with the partials in the library's fixed per-GPU scratch (no workspace;
+        out must be given, so the call allocates nothing)."""
+        _require_cuda(q, out)
+        check(lib.bgtq_decode_attention_noalloc(C.byref(self.desc), layer, _ptr(q), _dtype_code(q), _ptr(out),
+                                                n_splits, _stream(stream)))
+        return out
+
+
 def bgtq_fp16_decode_attention(k16, v16, q, out=None, n_splits: int = 0, ws=None, stream=None):
     """Unquantized comparator: k16, v16 fp16 [B, Hkv, N, 128]; q [B, Hq, 128] -> fp32 [B, Hq, 128]."""
     torch = _torch()

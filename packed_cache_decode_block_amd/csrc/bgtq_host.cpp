@@ -687,7 +687,8 @@ namespace {
 // Decode body over the context lengths `lens` ([B]; the descriptor's n_tokens row, or the lengths a
 // pending append will leave).  With dry_run the call validates only and launches nothing.
 int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dtype, float* out, void* ws,
-                          size_t ws_bytes, int n_splits, void* stream, const int64_t* lens, bool dry_run) {
+                          size_t ws_bytes, int n_splits, void* stream, const int64_t* lens, bool dry_run,
+                          bool cap_to_ws = false) {
     bgtq::Geometry g;
     int rc = geometry(c, g);
     if (rc) return rc;
@@ -725,13 +726,25 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
     }
     // Default splits follow the current length; never more than the capacity-sized workspace holds.
     const int per_cu = bgtq::decode_wgs_per_cu(c->k_mode, g.G, c->v_bits, c->k_group);
-    const int ns = n_splits ? n_splits
-                            : std::min(default_splits(std::max<int64_t>(max_tiles, 1), g.B * g.Hkv, cu_count(), per_cu),
-                                       default_splits(g.n_tiles, g.B * g.Hkv, cu_count(), per_cu));
-    const int parts = ns + (c->n_recent > 0 ? 1 : 0);
+    int ns = n_splits ? n_splits
+                      : std::min(default_splits(std::max<int64_t>(max_tiles, 1), g.B * g.Hkv, cu_count(), per_cu),
+                                 default_splits(g.n_tiles, g.B * g.Hkv, cu_count(), per_cu));
+    int parts = ns + (c->n_recent > 0 ? 1 : 0);
+    const size_t per_part = (size_t)g.B * g.Hq * PART * 4;
+    if (cap_to_ws && n_splits == 0 && ws_bytes < parts * per_part) {
+        // the library's choice, reduced to what the fixed workspace holds
+        const int64_t fit = (int64_t)(ws_bytes / per_part) - (c->n_recent > 0 ? 1 : 0);
+        if (fit < 1)
+            return fail(BGTQ_E_UNSUPPORTED, "B*Hq = %d needs %zu bytes of partials per split, above the %zu-byte "
+                        "scratch", g.B * g.Hq, per_part * (c->n_recent > 0 ? 2 : 1), ws_bytes);
+        ns = (int)fit;
+        parts = ns + (c->n_recent > 0 ? 1 : 0);
+    }
     if (parts > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS - 1);
-    const size_t need = (size_t)g.B * g.Hq * parts * PART * 4;
-    if (ws_bytes < need) return fail(BGTQ_E_INVALID, "workspace too small (%zu < %zu)", ws_bytes, need);
+    const size_t need = parts * per_part;
+    if (ws_bytes < need)
+        return fail(cap_to_ws ? BGTQ_E_UNSUPPORTED : BGTQ_E_INVALID, "%s too small (%zu < %zu bytes for %d splits)",
+                    cap_to_ws ? "scratch" : "workspace", ws_bytes, need, ns);
     (void)any_recent;
     if (dry_run) return ok();
     hipStream_t s = (hipStream_t)stream;
@@ -797,6 +810,28 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
 }
 
 }  // namespace
+
+namespace bgtq {
+
+int decode_capped(const bgtq_cache* c, int layer, const void* q, int dtype, float* out, void* ws, size_t ws_bytes,
+                  int n_splits, void* stream) {
+    const int64_t* lens = (c && c->n_tokens && layer >= 0 && layer < c->L && c->B >= 1)
+                              ? c->n_tokens + (size_t)layer * c->B
+                              : nullptr;
+    return decode_attention_impl(c, layer, q, dtype, out, ws, ws_bytes, n_splits, stream, lens, false, true);
+}
+
+int set_error(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+}  // namespace bgtq
 
 extern "C" {
 

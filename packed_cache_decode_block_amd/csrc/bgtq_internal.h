@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/bgtq.h"
+
 #define BGTQ_MAXB 64         // sequences per call carried in kernel arguments
 #define BGTQ_MAX_PARTS 8192  // split partials per query head merged by the combine kernel
 #define BGTQ_KST_ROW_BYTES 320  // stride of the K-record rows staged in LDS by the matrix-core decode
@@ -153,5 +155,12 @@ bool decode_supported(int k_mode, int R, int k_bits, int k_group, int v_bits, in
 void arm_launch_events(hipEvent_t start, hipEvent_t stop);
 void disarm_launch_events();
 int decode_wgs_per_cu(int k_mode, int G, int v_bits, int k_group);  // resident decode workgroups per CU the split heuristic aims for
+// Decode into a workspace the caller did not size (bgtq_decode_attention_noalloc): with
+// n_splits == 0 the library's split choice is capped so that the partials fit ws_bytes; an explicit
+// n_splits must fit.  Same validation, kernels and error reporting as bgtq_decode_attention.
+int decode_capped(const bgtq_cache* c, int layer, const void* q, int dtype, float* out, void* ws, size_t ws_bytes,
+                  int n_splits, void* stream);
+// Sets the thread's error text (bgtq_last_error) and returns code.
+int set_error(int code, const char* fmt, ...);
 
 }  // namespace bgtq

@@ -12,7 +12,7 @@ FAKE = 0x7F0000000000  # never dereferenced: the mocks only inspect argument blo
 
 @pytest.fixture(scope="module")
 def mock():
-    lib = _lib.bind(build_lib.build_mock())
+    lib = _lib.bind(build_lib.build_mock(), optional=("bgtq_decode_attention_noalloc",))
     lib.bgtq_mock_log.restype = C.c_char_p
     return lib
 
