@@ -51,13 +51,13 @@ def layer_bytes(w, N: int) -> float:
 
 def decode_kernel_name(w) -> str:
     """The decode kernel a workload dispatches to: Block-GTQ keys with at least four query heads
-    per kv head take the matrix-core kernel, everything else the vector-ALU one."""
-    return "k_decode_mx" if (w.k_mode == "gtq" and w.Hq // w.Hkv >= 4) else "k_decode"
+    per kv head take the plan-driven matrix-core kernel, everything else the vector-ALU one."""
+    return "k_decode_gtq" if (w.k_mode == "gtq" and w.Hq // w.Hkv >= 4) else "k_decode"
 
 
 def arithmetic(w):
     """(dtype, description) of the arithmetic the workload's decode kernel runs."""
-    if decode_kernel_name(w) == "k_decode_mx" or (w.k_mode != "gtq" and w.Hq // w.Hkv >= 4):
+    if decode_kernel_name(w) == "k_decode_gtq" or (w.k_mode != "gtq" and w.Hq // w.Hkv >= 4):
         return "f16", (f"{w.dtype} activations in; q.k and P.V on the matrix cores with fp16 operands "
                        "(key centroids exact in fp16, the scaled query as fp16 high + low parts, softmax "
                        "weights rounded to fp16) accumulated in fp32; softmax and output in fp32")
@@ -65,11 +65,26 @@ def arithmetic(w):
                    "(fp16 centroids times softmax weights rounded to fp16) accumulated in fp32")
 
 
-def measured_traffic(wid: int, kernel: str = "k_decode_mx"):
+# Source files each decode kernel is built from; a counter summary holds for the sha256 of these.
+KERNEL_SOURCES = {
+    "k_decode_gtq": ("bgtq_decode_gtq.hip", "bgtq_device.h"),
+    "k_decode": ("bgtq_kernels.hip", "bgtq_device.h"),
+    "k_decode_fp16_mx": ("bgtq_kernels.hip", "bgtq_device.h"),
+}
+
+
+def kernel_source_sha(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, "packed_cache_decode_block_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(wid: int, kernel: str = "k_decode_gtq"):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary of this
     workload (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None when there is
     none or the kernel source has changed since the counters were taken."""
-    import hashlib
     import re
     path = os.path.join(ROOT, "profiles", {2: f"{kernel}_qwen2.5-3b_128k_hbm_counters.md"}.get(wid, "-"))
     if not os.path.exists(path):
@@ -77,9 +92,7 @@ def measured_traffic(wid: int, kernel: str = "k_decode_mx"):
     text = open(path).read()
     h = re.search(r"sha256\s+`([0-9a-f]{64})`", text)
     t = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
-    src = os.path.join(ROOT, "packed_cache_decode_block_amd", "csrc", "bgtq_kernels.hip")
-    cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if not h or not t or h.group(1) != cur:
+    if not h or not t or h.group(1) != kernel_source_sha(kernel):
         return None
     return int(t.group(1))
 

@@ -51,7 +51,8 @@ enum { BGTQ_V_CODEBOOK = 0, BGTQ_V_AFFINE = 1 };            /* value formats */
 enum {
     BGTQ_BUF_K_CODES = 0, BGTQ_BUF_V_CODES = 1, BGTQ_BUF_K_SCALE = 2, BGTQ_BUF_K_ZERO = 3,
     BGTQ_BUF_V_SCALE = 4, BGTQ_BUF_V_ZERO = 5, BGTQ_BUF_RECENT_K = 6, BGTQ_BUF_RECENT_V = 7,
-    BGTQ_BUF_META = 8         /* bits + sigma + inv_sigma, for reference */
+    BGTQ_BUF_META = 8,        /* bits + sigma + inv_sigma, for reference */
+    BGTQ_BUF_PLAN = 9         /* decode plan: BGTQ_PLAN_BYTES per (layer, kv head), Block-GTQ keys */
 };
 
 #define BGTQ_HEAD_DIM 128
@@ -59,6 +60,7 @@ enum {
 #define BGTQ_TILE 64
 #define BGTQ_MAX_BATCH 64
 #define BGTQ_ENERGY_CHUNK 16   /* calibration tokens per workgroup of bgtq_block_energy */
+#define BGTQ_PLAN_BYTES 512    /* decode plan bytes per (layer, kv head) */
 
 /*
  * Packed KV cache descriptor (plain data; the caller fills it and owns every buffer).
@@ -87,6 +89,9 @@ enum {
  *   bits      uint8 [L][Hkv][64]   widths (BLOCKGTQ), from bgtq_allocate
  *   sigma     fp32  [L][Hkv][64]   per-block key scale sigma_i = sqrt(E_k[i]/2)
  *   inv_sigma fp32  [L][Hkv][64]   fp32(1/sigma_i), 0 for a dead block
+ *   plan      uint8 [L][Hkv][BGTQ_PLAN_BYTES]: Block-GTQ keys only (else NULL).  What the decode needs
+ *     that depends only on a layer's widths (block order, operand positions), written by
+ *     bgtq_prepare_metadata after the layer's bits are set; its contents are the library's own.
  *   k_rot     uint8 [L][Hkv][16] or NULL: affine keys only.  Sign bits s_j (bit j % 8 of byte
  *     j / 8 set means s_j = -1) of a randomized Hadamard key rotation ("Quantize What Counts"
  *     summary, Results: rotating the keys alone recovers most of K4V4's accuracy at K4V2): each
@@ -127,6 +132,7 @@ typedef struct bgtq_cache {
     int64_t *n_tokens;
     const uint8_t *k_rot;
     int32_t *n_hp;
+    void *plan;
 } bgtq_cache;
 
 /* Thread-local text describing the last non-OK status of this thread ("" if none). */
@@ -227,6 +233,16 @@ int bgtq_logquant_plan(int W, int64_t *hp_pos, int *n_hp, int64_t pos, int32_t *
  */
 int bgtq_logquant_append(bgtq_cache *c, int layer, const void *k, const void *v, int dtype,
                          const int64_t *strides, int64_t *hp_pos, void *stream);
+
+/*
+ * Prepare a layer's decode plan (device, asynchronous) from its widths c->bits[layer]: the block
+ * order of the Block-GTQ records (review §3: widths per RoPE block and KV head), where each block's
+ * codes sit in the record and where its query coordinates go in the decode's operands.  Call it
+ * after writing a layer's bits (and before decoding that layer); the decode of a Block-GTQ cache
+ * reads the plan instead of deriving it in every workgroup.  Writes c->plan[layer] only.
+ * Errors: BGTQ_E_INVALID (NULL descriptor, bits or plan, layer out of range, affine keys).
+ */
+int bgtq_prepare_metadata(const bgtq_cache *c, int layer, void *stream);
 
 /* Bytes of one cache buffer (all L layers) for the descriptor's geometry; <0 on error. */
 int64_t bgtq_cache_bytes(const bgtq_cache *c, int which);

@@ -13,14 +13,15 @@ SCORE_QK, SCORE_K = 0, 1
 K_BLOCKGTQ, K_AFFINE = 0, 1
 V_CODEBOOK, V_AFFINE = 0, 1
 (BUF_K_CODES, BUF_V_CODES, BUF_K_SCALE, BUF_K_ZERO, BUF_V_SCALE, BUF_V_ZERO, BUF_RECENT_K,
- BUF_RECENT_V, BUF_META) = range(9)
+ BUF_RECENT_V, BUF_META, BUF_PLAN) = range(10)
+PLAN_BYTES = 512  # BGTQ_PLAN_BYTES
 MAX_BATCH = 64
 ENERGY_CHUNK = 16  # BGTQ_ENERGY_CHUNK: calibration tokens per workgroup of bgtq_block_energy
 
 SYMBOLS = ["bgtq_last_error", "bgtq_version", "bgtq_codebook", "bgtq_allocate", "bgtq_allocate_rate",
            "bgtq_logquant_plan", "bgtq_logquant_append", "bgtq_block_energy", "bgtq_cache_bytes", "bgtq_quantize_append", "bgtq_decode_workspace_bytes", "bgtq_decode_attention",
            "bgtq_decode_step", "bgtq_fp16_decode_workspace_bytes", "bgtq_fp16_decode_attention", "bgtq_profile_enable",
-           "bgtq_profile_read", "bgtq_decode_attention_noalloc"]
+           "bgtq_profile_read", "bgtq_decode_attention_noalloc", "bgtq_prepare_metadata"]
 NOALLOC_SCRATCH_BYTES = 4 << 20  # BGTQ_NOALLOC_SCRATCH_BYTES
 PROF_DECODE, PROF_FP16_DECODE, PROF_QUANTIZE = 0, 1, 2
 
@@ -40,7 +41,7 @@ class CacheDesc(C.Structure):
                 ("v_scale", C.c_void_p), ("v_zero", C.c_void_p), ("recent_k", C.c_void_p), ("recent_v", C.c_void_p),
                 ("bits", C.c_void_p), ("sigma", C.c_void_p), ("inv_sigma", C.c_void_p),
                 ("n_tokens", C.POINTER(C.c_int64)), ("k_rot", C.c_void_p),
-                ("n_hp", C.POINTER(C.c_int32))]
+                ("n_hp", C.POINTER(C.c_int32)), ("plan", C.c_void_p)]
 
 
 def bind(path: str, optional=()):
@@ -61,6 +62,7 @@ def bind(path: str, optional=()):
         "bgtq_decode_workspace_bytes": (I64, [C.POINTER(CacheDesc), I]),
         "bgtq_decode_attention": (I, [C.POINTER(CacheDesc), I, P, I, P, P, SZ, I, P]),
         "bgtq_decode_attention_noalloc": (I, [C.POINTER(CacheDesc), I, P, I, P, I, P]),
+        "bgtq_prepare_metadata": (I, [C.POINTER(CacheDesc), I, P]),
         "bgtq_logquant_plan": (I, [I, C.POINTER(C.c_int64), C.POINTER(C.c_int), I64, C.POINTER(C.c_int32),
                                    C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int), C.POINTER(C.c_int)]),
         "bgtq_logquant_append": (I, [C.POINTER(CacheDesc), I, P, P, I, C.POINTER(C.c_int64), C.POINTER(C.c_int64), P]),

@@ -164,8 +164,10 @@ class PackedCache:
         # sign bits of the randomized Hadamard key rotation (affine keys), [L, Hkv, 16]; see
         # set_key_rotation.  All signs +1 until set.
         self.k_rot = torch.zeros((L, Hkv, 16), dtype=torch.uint8, device=device) if k_rotation else None
+        # decode plan of each layer (Block-GTQ keys), written by bgtq_prepare_metadata in set_metadata
+        self.plan = buf(_lib.BUF_PLAN, torch.uint8)
         for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "recent_k", "recent_v",
-                     "bits", "sigma", "inv_sigma", "k_rot"):
+                     "bits", "sigma", "inv_sigma", "k_rot", "plan"):
             setattr(d, name, _ptr(getattr(self, name)))
         self._ws = None
 
@@ -193,6 +195,8 @@ class PackedCache:
         self.bits[layer].copy_(torch.from_numpy(np.ascontiguousarray(bits, np.uint8)))
         self.sigma[layer].copy_(torch.from_numpy(np.ascontiguousarray(sigma, np.float32)))
         self.inv_sigma[layer].copy_(torch.from_numpy(np.ascontiguousarray(inv_sigma, np.float32)))
+        if d.k_mode == _lib.K_BLOCKGTQ:
+            check(lib.bgtq_prepare_metadata(C.byref(d), layer, _stream()))
 
     @staticmethod
     def _kv_strides(k, v):

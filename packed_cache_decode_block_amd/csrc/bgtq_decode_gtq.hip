@@ -1,0 +1,650 @@
+// Packed-cache decode over Block-GTQ keys on the matrix cores, one workgroup of eight waves per
+// compute unit ("RoPE-Aware Bit Allocation for KV-Cache Quantization": abstract; review §1
+// Packed-Cache, Figure 2: attention computed straight from the packed codes).
+//
+// The g query heads of a kv head share every dequantized key and value, so per 64-token tile q·K^T
+// is a (g x 128) x (128 x 64) product and P·V a (g x 64) x (64 x 128) product, both on
+// v_mfma_f32_16x16x32_f16; the vector ALUs unpack codes and run the online softmax.  Operand
+// assembly is the one of the bgtq_device.h helpers: key records staged in LDS, per-column 64-bit
+// windows, pair tables for widths up to 5 and fp16 coordinate tables above; values looked up from
+// the lane-stream fields through a replicated pair table.
+//
+// What depends only on the widths of a (layer, kv head) — the block order, the column descriptors
+// of the operand assembly and the per-block operand position of the query — is computed once by
+// k_plan into a small plan record; every workgroup of every decode loads it instead of rebuilding
+// it.  One workgroup per compute unit merges its eight waves into one (o, m, l) partial per query
+// head, so a split-K launch writes one partial per compute unit and kv head.
+#include <hip/hip_ext.h>
+
+#include "bgtq_device.h"
+
+namespace bgtq {
+namespace {
+
+
+// Plan record of one (layer, kv head): u32 desc[64] (column descriptors, index kq*16 + 4ks + 2mp +
+// odd as mx_desc builds them), u8 rank[64] (stream slot of block i, 0xFF for width 0), then u32
+// nnz_pad (nonzero slots rounded up to 4), ncc (coordinate columns), nnz.
+constexpr int kPlanDesc = 0, kPlanRank = 256, kPlanCounts = 320;
+static_assert(kPlanCounts + 12 <= BGTQ_PLAN_BYTES, "plan record size");
+
+// One wave per kv head, lane = RoPE block.
+__global__ __launch_bounds__(64) void k_plan(const uint8_t* bits, uint8_t* plan) {
+    const int h = blockIdx.x, lane = threadIdx.x;
+    const int bw = bits[h * 64 + lane];
+    const int w = bw < 8 ? bw : 8;  // widths above 8 are invalid; clamp
+    int rank, pos, nnz;
+    block_order(w, lane, rank, pos, nnz);
+    const int n_wide = __popcll(__ballot(w > 5));
+    __shared__ int s_sw[64], s_sp[64];
+    if (w > 0) {
+        s_sw[rank] = w;
+        s_sp[rank] = pos;
+    }
+    if (lane >= nnz) {
+        s_sw[lane] = 0;
+        s_sp[lane] = 0;
+    }
+    __syncthreads();
+    uint8_t* p = plan + (size_t)h * BGTQ_PLAN_BYTES;
+    // stream slot r is k-step r / 16, column pair (r % 16) / 8, lane row (r % 8) / 2, second of its
+    // pair if odd; a column is read per coordinate when its first slot is wider than 5 bits
+    const int r = lane, ks = r >> 4, mp = (r >> 3) & 1, kq = (r >> 1) & 3, odd = r & 1;
+    auto coord_of = [&](int first) { return first < n_wide; };
+    const bool ca = coord_of(16 * ks + 8 * mp), cs = coord_of(16 * ks + 8 * mp + odd);
+    ((uint32_t*)(p + kPlanDesc))[kq * 16 + 4 * ks + 2 * mp + odd] = mx_desc(s_sp[r & ~1], ca, s_sp[r], s_sw[r], cs);
+    p[kPlanRank + lane] = (uint8_t)(w > 0 ? rank : 0xFF);
+    if (lane == 0) {
+        int nc = 0;
+        for (int c = 0; c < 16; ++c) nc += coord_of(16 * (c >> 2) + 8 * ((c >> 1) & 1) + (c & 1)) ? 1 : 0;
+        uint32_t* cnt = (uint32_t*)(p + kPlanCounts);
+        cnt[0] = (uint32_t)((nnz + 3) & ~3);
+        cnt[1] = (uint32_t)nc;
+        cnt[2] = (uint32_t)nnz;
+    }
+}
+
+// Query operands from the plan, one (head, block) item per thread (threads 0 .. 511: head hh =
+// thread / 64, block = thread % 64).  The item's coordinates q' = q * sigma * log2(e)/sqrt(d) go to
+// stream slot rank of the operand image as fp16 high and low parts (rows 2hh and 2hh + 1); the item
+// also clears its head's rows of slot `block` when that slot is past the nonzero blocks, and heads
+// beyond G clear their rows of every slot.  Layout of mx_prep_q.
+struct QItem {
+    uint32_t r0, r1;  // the item's two coordinates (fp32 bits, or the packed 16-bit pair in r0)
+    float sg;         // sigma of the block
+    int rank;         // stream slot of the block (0xFF: width 0)
+};
+
+template <int G>
+__device__ __forceinline__ QItem gtq_q_item_load(const void* q, int dtype, const float* sigma, const uint8_t* plan_rank,
+                                                 int b, int h, int Hq) {
+    const int i = threadIdx.x < 512 ? threadIdx.x : 0;
+    const int hh = i >> 6, blk = i & 63;
+    const int64_t at = ((int64_t)b * Hq + (int64_t)h * G + (hh < G ? hh : 0)) * D + 2 * blk;
+    QItem it;
+    if (dtype == BGTQ_F32) {
+        const uint2 v = *(const uint2*)((const float*)q + at);
+        it.r0 = v.x;
+        it.r1 = v.y;
+    } else {
+        it.r0 = *(const uint32_t*)((const uint16_t*)q + at);
+        it.r1 = 0u;
+    }
+    it.sg = sigma[h * 64 + blk];
+    it.rank = plan_rank[blk];
+    return it;
+}
+
+template <int G>
+__device__ void gtq_q_item_store(const QItem& it, int dtype, int nnz, uint8_t* qa) {
+    const int i = threadIdx.x;
+    if (i >= 512) return;
+    const int hh = i >> 6, blk = i & 63;
+    auto slot_base = [&](int r) {
+        const int ks = r >> 4, rr = r & 15, urow = (rr >> 1) & 3, mpair = 2 * (rr >> 3) + (rr & 1);
+        return qa + (size_t)(ks * 64 + 16 * urow) * 16 + 4 * mpair;
+    };
+    if (hh < G && it.rank != 0xFF) {
+        float q0, q1;
+        if (dtype == BGTQ_F32) {
+            q0 = __builtin_bit_cast(float, it.r0);
+            q1 = __builtin_bit_cast(float, it.r1);
+        } else {
+            q0 = dtype == BGTQ_F16 ? h2f(it.r0 & 0xFFFFu) : bf2f(it.r0 & 0xFFFFu);
+            q1 = dtype == BGTQ_F16 ? h2f(it.r0 >> 16) : bf2f(it.r0 >> 16);
+        }
+        const float sg = it.sg * kLog2eOverSqrtD;
+        q0 *= sg;
+        q1 *= sg;
+        const _Float16 h0 = (_Float16)q0, h1 = (_Float16)q1;
+        const _Float16 l0 = (_Float16)(q0 - (float)h0), l1 = (_Float16)(q1 - (float)h1);
+        uint8_t* base = slot_base(it.rank);
+        *(uint32_t*)(base + (2 * hh) * 16) =
+            (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        *(uint32_t*)(base + (2 * hh + 1) * 16) =
+            (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+    if (hh >= G || blk >= nnz) {
+        uint8_t* base = slot_base(blk);
+        *(uint32_t*)(base + (2 * hh) * 16) = 0u;
+        *(uint32_t*)(base + (2 * hh + 1) * 16) = 0u;
+    }
+}
+
+// Query operands from the plan (wave 0, lane = RoPE block): q' = q * sigma * log2(e)/sqrt(d) of
+// block i goes to stream slot rank_i of the operand image (layout of mx_prep_q); slots past the
+// nonzero blocks get zeros.
+template <int G>
+__device__ void gtq_prep_q(const PrepIn<G>& in, int rank, int nnz, int lane, uint8_t* qa) {
+    float q0[G], q1[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        if (in.dtype == BGTQ_F32) {
+            q0[hh] = __builtin_bit_cast(float, in.r0[hh]);
+            q1[hh] = __builtin_bit_cast(float, in.r1[hh]);
+        } else if (in.dtype == BGTQ_F16) {
+            q0[hh] = h2f(in.r0[hh] & 0xFFFFu);
+            q1[hh] = h2f(in.r0[hh] >> 16);
+        } else {
+            q0[hh] = bf2f(in.r0[hh] & 0xFFFFu);
+            q1[hh] = bf2f(in.r0[hh] >> 16);
+        }
+        q0[hh] = q0[hh] * kLog2eOverSqrtD * in.sg;
+        q1[hh] = q1[hh] * kLog2eOverSqrtD * in.sg;
+    }
+    auto put = [&](int r, bool zero) {
+        const int ks = r >> 4, rr = r & 15, urow = (rr >> 1) & 3, mpair = 2 * (rr >> 3) + (rr & 1);
+        uint8_t* base = qa + (size_t)(ks * 64 + 16 * urow) * 16 + 4 * mpair;
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+            uint32_t hi2 = 0u, lo2 = 0u;
+            if (hh < G && !zero) {
+                const _Float16 h0 = (_Float16)q0[hh], h1 = (_Float16)q1[hh];
+                const _Float16 l0 = (_Float16)(q0[hh] - (float)h0), l1 = (_Float16)(q1[hh] - (float)h1);
+                hi2 = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                lo2 = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+            }
+            *(uint32_t*)(base + (2 * hh) * 16) = hi2;
+            *(uint32_t*)(base + (2 * hh + 1) * 16) = lo2;
+        }
+    };
+    if (rank != 0xFF) put(rank, false);
+    if (lane >= nnz) put(lane, true);
+}
+
+// One k-step of q·k: the eight windows of the lane row (two column pairs x four token groups) as
+// one batch of ds_read2 (each lands in a register pair), then token group by token group the four
+// slot lookups and one product, so that only one group's operands are live.  Column modes
+// CA0/CB0/CA1/CB1 as in col_pairs_both; dk holds the four column descriptors of this lane row, qk
+// the query operand of the k-step.
+template <bool CA0, bool CB0, bool CA1, bool CB1, bool FIRST>
+__device__ __forceinline__ void kstep_lean(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t dk, uint32_t lb,
+                                           const half8_t qk) {
+    const uint32_t ad0 = (dk[0] >> 17) + lb, ad1 = (dk[2] >> 17) + lb;
+    const uint32_t m0 = CA0 ? bfm<1>(dk[0] >> 12) : bfm<2>(dk[0] >> 12);
+    const uint32_t m1 = CB0 ? bfm<1>(dk[1] >> 12) : bfm<2>(dk[1] >> 12);
+    const uint32_t m2 = CA1 ? bfm<1>(dk[2] >> 12) : bfm<2>(dk[2] >> 12);
+    const uint32_t m3 = CB1 ? bfm<1>(dk[3] >> 12) : bfm<2>(dk[3] >> 12);
+    const uint32_t b0 = m0 + (CA0 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
+    const uint32_t b1 = m1 + (CB0 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
+    const uint32_t b2 = m2 + (CA1 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
+    const uint32_t b3 = m3 + (CB1 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
+    static_assert(BGTQ_KST_ROW_BYTES == 320, "window read offsets assume 80-dword stage rows");
+    uint64_t wa[4], wb[4];
+    asm volatile("ds_read2_b32 %0, %8 offset1:80\n\t"
+                 "ds_read2_b32 %1, %8 offset0:16 offset1:96\n\t"
+                 "ds_read2_b32 %2, %8 offset0:32 offset1:112\n\t"
+                 "ds_read2_b32 %3, %8 offset0:48 offset1:128\n\t"
+                 "ds_read2_b32 %4, %9 offset1:80\n\t"
+                 "ds_read2_b32 %5, %9 offset0:16 offset1:96\n\t"
+                 "ds_read2_b32 %6, %9 offset0:32 offset1:112\n\t"
+                 "ds_read2_b32 %7, %9 offset0:48 offset1:128\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(wa[0]), "=&v"(wa[1]), "=&v"(wa[2]), "=&v"(wa[3]),
+                   "=&v"(wb[0]), "=&v"(wb[1]), "=&v"(wb[2]), "=&v"(wb[3])
+                 : "v"((uint32_t)(uintptr_t)(lds + ad0)), "v"((uint32_t)(uintptr_t)(lds + ad1))
+                 : "memory");
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t p0 = CA0 ? slot_coord(lds, wa[g], dk[0], m0, b0) : slot_pair(lds, wa[g], dk[0], m0, b0);
+        const uint32_t p1 = CB0 ? slot_coord(lds, wa[g], dk[1], m1, b1) : slot_pair(lds, wa[g], dk[1], m1, b1);
+        const uint32_t p2 = CA1 ? slot_coord(lds, wb[g], dk[2], m2, b2) : slot_pair(lds, wb[g], dk[2], m2, b2);
+        const uint32_t p3 = CB1 ? slot_coord(lds, wb[g], dk[3], m3, b3) : slot_pair(lds, wb[g], dk[3], m3, b3);
+        c[g] = mfma16(qk, as_h8(p0, p1, p2, p3), FIRST ? f32x4_t{0.f, 0.f, 0.f, 0.f} : c[g]);
+    }
+}
+
+// k-step KS; ncc (wave-uniform) = number of coordinate columns of the whole record.
+template <int KS>
+__device__ __forceinline__ void kstep_lean_any(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
+                                               const u32x4_t* sd, uint32_t lb, int ncc) {
+    const u32x4_t dk = sd[KS];
+    const half8_t qk = __builtin_bit_cast(half8_t, qa[KS * 64 + lane]);
+    constexpr bool F = KS == 0;
+    const int a = ncc - 4 * KS;
+    if (a <= 0) kstep_lean<false, false, false, false, F>(c, lds, dk, lb, qk);
+    else if (a == 1) kstep_lean<true, false, false, false, F>(c, lds, dk, lb, qk);
+    else if (a == 2) kstep_lean<true, true, false, false, F>(c, lds, dk, lb, qk);
+    else if (a == 3) kstep_lean<true, true, true, false, F>(c, lds, dk, lb, qk);
+    else kstep_lean<true, true, true, true, F>(c, lds, dk, lb, qk);
+}
+
+// Workgroup barrier that orders LDS only: the waves' LDS writes complete first, global loads still
+// in flight stay in flight (__syncthreads also waits for every outstanding global access).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Merge the NW waves' (o, m, l, zero term) records in red[wave][h] into one partial per head:
+// thread (h, quad of dims) reads the NW maxima of its head (broadcast reads), forms its own scale
+// factors and folds 4 dims of the NW records; the first of a head's threads also writes M and L.
+// No LDS writes between the reads (no serial chain), and the global stores come after the last
+// barrier.
+template <int G, int NW>
+__device__ __forceinline__ void merge_waves_n(const float* red, float* part, int n_parts, int split) {
+    for (int idx = threadIdx.x; idx < G * 32; idx += blockDim.x) {
+        const int h = idx >> 5, j = 4 * (idx & 31);
+        float mw[NW];
+        float M = -INFINITY;
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) {
+            mw[wv] = red[(wv * G + h) * PART + 128];
+            M = fmaxf(M, mw[wv]);
+        }
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        float L = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) {
+            const float* rw = red + (wv * G + h) * PART;
+            const float f = mw[wv] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[wv] - M);
+            acc += f * (*(const f32x4_t*)(rw + j) + rw[130]);
+            L += f * rw[129];
+        }
+        // partials are read once, by the split merge: stream them past the caches
+        float* dst = part + ((size_t)h * n_parts + split) * PART;
+        __builtin_nontemporal_store(acc, (f32x4_t*)(dst + j));
+        if (j == 0) {
+            __builtin_nontemporal_store(M, dst + 128);
+            __builtin_nontemporal_store(L, dst + 129);
+        }
+    }
+}
+
+// LDS arena (byte offsets): tables at offset 0 (the arena is 8192-aligned, so table offsets are
+// LDS addresses), column descriptors, value pair table, query operands, weight exchange, softmax
+// rescale factors, counts, then per wave the stage of the tile in flight (K record rows -1 .. R at
+// BGTQ_KST_ROW_BYTES stride, then its scales).  The epilogue records alias the stages.
+template <int G, int R, int VB, int NW> struct GtqLds {
+    static constexpr int TAB = 0;
+    static constexpr int DESC = a16(TAB + BGTQ_CB_MX_BYTES);          // u32 [4 lane rows][16 columns]
+    static constexpr int VLUT = DESC + 64 * 4;                        // u32 [4^VB][copies]
+    static constexpr int QA = a16(VLUT + VLutGeom<VB>::BYTES);        // u32x4 [4 k-steps][64 lanes]
+    static constexpr int WX = QA + 4 * 64 * 16;                       // u32 [NW waves][16 heads][32 pairs]
+    static constexpr int ALPHA = WX + NW * 16 * 32 * 4;               // f32 [NW waves][16]
+    static constexpr int NNZ = ALPHA + NW * 16 * 4;                   // u32 [4]: nnz_pad, ncc, nnz
+    static constexpr int KST = a16(NNZ + 16);                         // per wave: R + 2 rows
+    static constexpr int KST_W = (R + 2) * BGTQ_KST_ROW_BYTES;
+    static constexpr int SST = KST + NW * KST_W;                      // per wave: K scales, V scales, V zeros
+    static constexpr int SST_W = 3 * 64 * 2;
+    static constexpr int RED = KST;                                   // epilogue: f32 [NW G PART + NW G]
+    static constexpr int SIZE = cmax(SST + NW * SST_W, RED + 4 * NW * G * PART);
+};
+
+template <int G, int R, int VB, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_decode_gtq(const DecodeArgs a) {
+    static_assert(G == 4 || G == 8, "matrix-core decode serves 4 or 8 query heads per kv head");
+    static_assert(R % 4 == 0, "K records are staged in 16-byte chunks");
+    using LD = GtqLds<G, R, VB, NW>;
+    static_assert(LD::SIZE <= 160 * 1024, "LDS budget");
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int row = lane >> 4, col = lane & 15;
+    __shared__ __attribute__((aligned(8192))) uint8_t lds[LD::SIZE];
+    uint32_t* s_vlut = (uint32_t*)(lds + LD::VLUT);
+    u32x4_t* s_qa = (u32x4_t*)(lds + LD::QA);
+    float* s_alpha = (float*)(lds + LD::ALPHA) + wave * 16;
+    uint32_t* s_nnz = (uint32_t*)(lds + LD::NNZ);
+    uint8_t* kst = lds + LD::KST + wave * LD::KST_W;
+    uint16_t* sst = (uint16_t*)(lds + LD::SST + wave * LD::SST_W);
+    uint32_t* wx = (uint32_t*)(lds + LD::WX) + wave * 16 * 32;
+
+    const size_t bh = (size_t)b * a.Hkv + h;
+    const int64_t n_packed = a.n_packed[b];
+    const int64_t n_tiles_b = (n_packed + TILE - 1) / TILE;
+    const int64_t t_lo = (int64_t)split * a.tiles_per_split;
+    const int64_t t_hi = t_lo + a.tiles_per_split < n_tiles_b ? t_lo + a.tiles_per_split : n_tiles_b;
+    const uint32_t* kc = (const uint32_t*)(a.k_codes + bh * a.n_tiles * a.k_tile_bytes);
+    const uint32_t* vc = (const uint32_t*)(a.v_codes + bh * a.n_tiles * a.v_tile_bytes);
+    const uint32_t* ks32 = (const uint32_t*)(a.k_scale + bh * a.n_cap);  // fp16 pairs (token 2i, 2i + 1)
+    const uint32_t* vs32 = (const uint32_t*)(a.v_scale + bh * a.n_cap);
+    const uint32_t* vz32 = a.v_affine ? (const uint32_t*)(a.v_zero + bh * a.n_cap) : nullptr;
+    const bool vaff = a.v_affine != 0;
+    const uint8_t* plan = a.plan + (size_t)h * BGTQ_PLAN_BYTES;
+
+    // Prologue.  Global loads first: the query and this lane's block of the plan (wave 0), the
+    // plan's descriptors and counts, the table image and the value centroids, then the first tile's
+    // keys; loads retire in order, so the LDS writes below do not wait for HBM.  Loads are
+    // unconditional (clamped indices) so that no branch forces an early wait.
+    PrepIn<G> pin;
+    int prank = 0;
+    QItem qit;
+    if constexpr (NW > 8) {
+        qit = gtq_q_item_load<G>(a.q, a.q_dtype, a.sigma, plan + kPlanRank, b, h, a.Hq);
+    } else {
+        pin = prep_load<G, true>(a.q, a.q_dtype, a.bits, a.sigma, b, h, a.Hq, lane);
+        prank = plan[kPlanRank + lane];
+    }
+    const uint32_t pdesc = threadIdx.x < 64 ? ((const uint32_t*)(plan + kPlanDesc))[threadIdx.x] : 0u;
+    const uint32_t pcnt = threadIdx.x < 3 ? ((const uint32_t*)(plan + kPlanCounts))[threadIdx.x] : 0u;
+    constexpr int TAB4 = BGTQ_CB_MX_WORDS / 4;
+    const u32x4_t* tab4 = (const u32x4_t*)c_mxtab;
+    constexpr int NT = 64 * NW;
+    u32x4_t tv[(TAB4 + NT - 1) / NT];
+#pragma unroll
+    for (int k = 0; k < (TAB4 + NT - 1) / NT; ++k)
+        tv[k] = tab4[threadIdx.x + NT * k < TAB4 ? threadIdx.x + NT * k : 0];
+    constexpr int VCOP = VLutGeom<VB>::COPIES, VENT = 1 << (2 * VB);
+    constexpr int VROUNDS = (VENT * VCOP + NT - 1) / NT;
+    uint32_t vla[VROUNDS], vlb[VROUNDS];
+#pragma unroll
+    for (int k = 0; k < VROUNDS; ++k) {
+        const uint32_t e = ((threadIdx.x + (uint32_t)NT * k) / VCOP) & (VENT - 1);
+        vla[k] = c_cent16[cent_base(VB) + (e & ((1u << VB) - 1u))];
+        vlb[k] = c_cent16[cent_base(VB) + (e >> VB)];
+    }
+
+    // Tile data: K chunks and one dword of scales per lane (lanes 0..31: K scales of tokens 2l,
+    // 2l+1; lanes 32..63: V scales; V zeros in a second dword for affine values) are prefetched one
+    // tile ahead and staged to LDS when their tile starts; the value streams stay in registers
+    // (each lane reads its own stream).
+    u32x4_t kn[R / 4], vn[VB], vx[VB];
+    uint32_t sn, zn;
+    auto fetch_k = [&](int64_t t) {
+        const u32x4_t* kt = (const u32x4_t*)(kc + t * (a.k_tile_bytes / 4));
+#pragma unroll
+        for (int c = 0; c < R / 4; ++c) kn[c] = kt[c * 64 + lane];
+        sn = (lane < 32 ? ks32 : vs32)[t * (TILE / 2) + (lane & 31)];
+        zn = vz32 ? vz32[t * (TILE / 2) + (lane & 31)] : 0u;
+    };
+    auto fetch_v = [&](u32x4_t (&dst)[VB], int64_t t) {
+        const u32x4_t* vt = (const u32x4_t*)(vc + t * (a.v_tile_bytes / 4));
+#pragma unroll
+        for (int c = 0; c < VB; ++c) dst[c] = vt[c * 64 + lane];
+    };
+    // Unconditional (branch-free prologue); a wave without tiles reads a tile inside the allocation
+    // and never uses it.  The small loads above go out first (the scheduling fence keeps the tile
+    // loads behind them), so they do not queue behind every compute unit's tile burst.
+    const int64_t t_first = t_lo + wave < t_hi ? t_lo + wave : (t_lo < a.n_tiles ? t_lo : 0);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_k(t_first);
+    if constexpr (NW > 8) fetch_v(vn, t_first);
+
+#pragma unroll
+    for (int k = 0; k < (TAB4 + NT - 1) / NT; ++k)
+        if (threadIdx.x + NT * k < TAB4) ((u32x4_t*)(lds + LD::TAB))[threadIdx.x + NT * k] = tv[k];
+#pragma unroll
+    for (int k = 0; k < VROUNDS; ++k) {
+        const uint32_t i = threadIdx.x + (uint32_t)NT * k;
+        const uint32_t e = (i / VCOP) & (VENT - 1);
+        if (i < (uint32_t)(VENT * VCOP))
+            s_vlut[i] = a.v_affine ? (uint32_t)f2h((float)(e & ((1u << VB) - 1u))) | ((uint32_t)f2h((float)(e >> VB)) << 16)
+                                   : vla[k] | (vlb[k] << 16);
+    }
+#pragma unroll
+    for (int i = threadIdx.x; i < NW * 16 * 32 / 4; i += NT) ((u32x4_t*)(lds + LD::WX))[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (threadIdx.x < 64) ((uint32_t*)(lds + LD::DESC))[threadIdx.x] = pdesc;
+    if (threadIdx.x < 3) s_nnz[threadIdx.x] = pcnt;
+    if constexpr (NW > 8) {
+        const int nnz = (int)__builtin_amdgcn_readfirstlane(((const uint32_t*)(plan + kPlanCounts))[2]);
+        gtq_q_item_store<G>(qit, a.q_dtype, nnz, lds + LD::QA);
+    } else if (wave == 0) {
+        const int nnz = (int)__builtin_amdgcn_readfirstlane(((const uint32_t*)(plan + kPlanCounts))[2]);
+        gtq_prep_q<G>(pin, prank, nnz, lane, lds + LD::QA);
+    }
+    lds_barrier();  // tables, descriptors and query operands are in place
+
+    const int nnz_pad = (int)__builtin_amdgcn_readfirstlane(s_nnz[0]);  // nonzero slots rounded up to 4
+    const int nks = (nnz_pad + 15) >> 4;
+    const int ncc = (int)__builtin_amdgcn_readfirstlane(s_nnz[1]);      // coordinate columns
+    const u32x4_t* sd = (const u32x4_t*)(lds + LD::DESC) + 4 * row;  // this lane row's descriptors
+    if constexpr (NW <= 8) fetch_v(vn, t_first);
+
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, zs[2] = {0.f, 0.f};
+    f32x4_t o[8];
+    if constexpr (NW <= 8) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    uint32_t lb = (uint32_t)(LD::KST + wave * LD::KST_W) + 4u * (uint32_t)col;
+    asm volatile("" : "+v"(lb));  // keep the stage base inside lb: one add per column address
+    const uint32_t lcopy = 4u * ((uint32_t)lane & (VLutGeom<VB>::COPIES - 1));  // this lane's value-table copy
+
+    // With eight waves, two tiles per iteration: the value streams of the next tile load into the
+    // other buffer (4-bit values: one buffer, reloaded after P·V).  With sixteen waves one buffer: the
+    // other waves of the SIMD cover the reload.
+    constexpr bool VDB = VB <= 3 && NW <= 8;
+    auto tile = [&](const int64_t t, u32x4_t (&vcur)[VB], u32x4_t (&vnext)[VB]) __attribute__((always_inline)) {
+        // Stage the tile: K rows (row rho of the record at stage row rho + 1), scales (transposed:
+        // token u at (u%16)*4 + u/16).
+        wave_lds_fence();
+#pragma unroll
+        for (int c = 0; c < R / 4; ++c)
+            *(u32x4_t*)(kst + (4 * c + row + 1) * BGTQ_KST_ROW_BYTES + 16 * col) = kn[c];
+        {
+            const int u0 = 2 * (lane & 31), reg = lane < 32 ? 0 : 64;
+            sst[reg + (u0 & 15) * 4 + (u0 >> 4)] = (uint16_t)(sn & 0xFFFFu);
+            sst[reg + ((u0 + 1) & 15) * 4 + ((u0 + 1) >> 4)] = (uint16_t)(sn >> 16);
+            if (lane < 32) {
+                sst[128 + (u0 & 15) * 4 + (u0 >> 4)] = (uint16_t)(zn & 0xFFFFu);
+                sst[128 + ((u0 + 1) & 15) * 4 + ((u0 + 1) >> 4)] = (uint16_t)(zn >> 16);
+            }
+        }
+        wave_lds_fence();
+        asm volatile("" ::: "memory");
+        if constexpr (NW <= 8) {
+            // unconditional, so that no branch merges the wait counts (the last tile re-reads itself)
+            const int64_t tn = t + NW < t_hi ? t + NW : t;
+            fetch_k(tn);
+            if constexpr (VDB) fetch_v(vnext, tn);
+        }
+
+        // q·k on the matrix cores
+        f32x4_t c[4];
+        if (nks == 0) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) c[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        if constexpr (NW > 8) {
+            if (nks > 0) kstep_lean_any<0>(c, lds, s_qa, lane, sd, lb, ncc);
+            if (nks > 1) kstep_lean_any<1>(c, lds, s_qa, lane, sd, lb, ncc);
+            if (nks > 2) kstep_lean_any<2>(c, lds, s_qa, lane, sd, lb, ncc);
+            if (nks > 3) kstep_lean_any<3>(c, lds, s_qa, lane, sd, lb, ncc);
+        } else {
+            if (nks > 0) mx_kstep_any<0>(c, lds, s_qa, lane, sd, lb, ncc);
+            if (nks > 1) mx_kstep_any<1>(c, lds, s_qa, lane, sd, lb, ncc);
+            if (nks > 2) mx_kstep_any<2>(c, lds, s_qa, lane, sd, lb, ncc);
+            if (nks > 3) mx_kstep_any<3>(c, lds, s_qa, lane, sd, lb, ncc);
+        }
+
+        // softmax over the tile: lane holds tokens 16g + col, heads 2row, 2row + 1
+        float sk[4], sv[4], sz[4] = {0.f, 0.f, 0.f, 0.f};
+        {
+            const uint2 k2 = *(const uint2*)(sst + col * 4), v2 = *(const uint2*)(sst + 64 + col * 4);
+            sk[0] = h2f(k2.x & 0xFFFFu); sk[1] = h2f(k2.x >> 16); sk[2] = h2f(k2.y & 0xFFFFu); sk[3] = h2f(k2.y >> 16);
+            sv[0] = h2f(v2.x & 0xFFFFu); sv[1] = h2f(v2.x >> 16); sv[2] = h2f(v2.y & 0xFFFFu); sv[3] = h2f(v2.y >> 16);
+            if (vaff) {
+                const uint2 z2 = *(const uint2*)(sst + 128 + col * 4);
+                sz[0] = h2f(z2.x & 0xFFFFu); sz[1] = h2f(z2.x >> 16); sz[2] = h2f(z2.y & 0xFFFFu); sz[3] = h2f(z2.y >> 16);
+            }
+        }
+        float z[4][2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) z[g][hh] = sk[g] * (c[g][2 * hh] + c[g][2 * hh + 1]);
+        if ((t + 1) * TILE > n_packed) {  // the sequence ends inside this tile
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                // scales of tokens past the end are never written: keep them out of the arithmetic
+                if (t * TILE + 16 * g + col >= n_packed) {
+                    sv[g] = 0.f;
+                    sz[g] = 0.f;
+                    z[g][0] = z[g][1] = -INFINITY;
+                }
+            }
+        }
+        float tmax[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) tmax[hh] = vmax(vmax3(z[0][hh], z[1][hh], z[2][hh]), z[3][hh]);
+        if (t == t_lo + wave) {
+            // the wave's first tile: nothing accumulated yet, so no rescale
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) m[hh] = row_max16(tmax[hh]);
+        } else if (__ballot(tmax[0] > m[0] || tmax[1] > m[1])) {
+            float alpha[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const float mn = vmax(m[hh], row_max16(tmax[hh]));
+                alpha[hh] = __builtin_amdgcn_exp2f(m[hh] - mn);
+                m[hh] = mn;
+                l[hh] *= alpha[hh];
+                zs[hh] *= alpha[hh];
+            }
+            wave_lds_fence();
+            if (col == 0) {
+                s_alpha[2 * row] = alpha[0];
+                s_alpha[2 * row + 1] = alpha[1];
+            }
+            wave_lds_fence();
+            const float al = s_alpha[col];
+#pragma unroll
+            for (int db = 0; db < 8; ++db) o[db] *= al;
+        }
+        uint16_t wh[4][2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const float p = __builtin_amdgcn_exp2f(z[g][hh] - m[hh]);
+                l[hh] += p;
+                if (vaff) zs[hh] += p * sz[g];
+                wh[g][hh] = f2h(p * sv[g]);
+            }
+        }
+        wave_lds_fence();
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            uint32_t* wr = wx + (2 * row + hh) * 32 + col;
+            wr[0] = (uint32_t)wh[0][hh] | ((uint32_t)wh[2][hh] << 16);
+            wr[16] = (uint32_t)wh[1][hh] | ((uint32_t)wh[3][hh] << 16);
+        }
+        wave_lds_fence();
+
+        // P·V on the matrix cores from this lane's value stream
+        uint32_t vs[4 * VB];
+#pragma unroll
+        for (int cc = 0; cc < VB; ++cc) {
+            vs[4 * cc] = vcur[cc][0]; vs[4 * cc + 1] = vcur[cc][1]; vs[4 * cc + 2] = vcur[cc][2]; vs[4 * cc + 3] = vcur[cc][3];
+        }
+        if constexpr (NW > 8) {
+            mx_pv<VB, 0, true>(o, vs, s_vlut, wx, lane, lcopy);  // the wave's only tile: start from zero
+        } else {
+            mx_pv<VB, 0>(o, vs, s_vlut, wx, lane, lcopy);
+        }
+        mx_pv<VB, 1>(o, vs, s_vlut, wx, lane, lcopy);
+        if constexpr (NW <= 8 && !VDB) {
+            if (t + NW < t_hi) fetch_v(vcur, t + NW);
+        }
+    };
+    if constexpr (VDB) {
+        for (int64_t t = t_lo + wave; t < t_hi; t += 2 * NW) {
+            tile(t, vn, vx);
+            if (t + NW < t_hi) tile(t + NW, vx, vn);
+        }
+    } else if constexpr (NW > 8) {
+        // one tile per wave (the host sizes the splits so): straight-line code, its loads issued in
+        // the prologue; its P·V starts the accumulators, a wave without a tile clears them
+        if (t_lo + wave < t_hi) {
+            tile(t_lo + wave, vn, vn);
+        } else {
+#pragma unroll
+            for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    } else {
+        for (int64_t t = t_lo + wave; t < t_hi; t += NW) tile(t, vn, vn);
+    }
+
+    // Epilogue: row sums of l and the zero term, O^T to LDS (over the stages), merge the waves.
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        l[hh] = row_sum16(l[hh]);
+        zs[hh] = row_sum16(zs[hh]);
+    }
+    lds_barrier();  // every wave is done with its stages
+    float* s_red = (float*)(lds + LD::RED);
+    float* r = s_red + wave * G * PART;
+    if (col < G) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) *(f32x4_t*)(r + col * PART + 16 * db + 4 * row) = o[db];
+    }
+    if (col == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int hd = 2 * row + hh;
+            if (hd < G) {
+                r[hd * PART + 128] = m[hh];
+                r[hd * PART + 129] = l[hh];
+                r[hd * PART + 130] = zs[hh];
+            }
+        }
+    }
+    lds_barrier();
+    float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_parts * PART;
+    merge_waves_n<G, NW>(s_red, part, a.n_parts, split);
+}
+
+template <int G, int VB, int NW>
+hipError_t launch_gtq_gvw(const DecodeArgs& a, int B, int R, hipStream_t s) {
+    const dim3 grid(a.n_splits, a.Hkv, B), block(64 * NW);
+    switch (R) {
+        case 8: return launch_main(k_decode_gtq<G, 8, VB, NW>, grid, block, s, a);
+        case 12: return launch_main(k_decode_gtq<G, 12, VB, NW>, grid, block, s, a);
+        case 16: return launch_main(k_decode_gtq<G, 16, VB, NW>, grid, block, s, a);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Splits of at most kGtqWavesOneTile tiles take the sixteen-wave kernel (one tile per wave,
+// straight-line), longer splits the eight-wave kernel that loops over its tiles.
+template <int G, int VB>
+hipError_t launch_gtq_gv(const DecodeArgs& a, int B, int R, hipStream_t s) {
+    if (a.tiles_per_split <= kGtqWavesOneTile) return launch_gtq_gvw<G, VB, kGtqWavesOneTile>(a, B, R, s);
+    return launch_gtq_gvw<G, VB, kGtqWavesLoop>(a, B, R, s);
+}
+
+template <int G>
+hipError_t launch_gtq_g(const DecodeArgs& a, int B, int R, int v_bits, hipStream_t s) {
+    switch (v_bits) {
+        case 2: return launch_gtq_gv<G, 2>(a, B, R, s);
+        case 3: return launch_gtq_gv<G, 3>(a, B, R, s);
+        case 4: return launch_gtq_gv<G, 4>(a, B, R, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_plan(const uint8_t* bits, uint8_t* plan, int Hkv, hipStream_t s) {
+    if (!bits || !plan || Hkv < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_plan, dim3(Hkv), dim3(64), 0, s, bits, plan);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_gtq(const DecodeArgs& a, int B, int R, int v_bits, hipStream_t s) {
+    if (!a.plan || B < 1 || B > BGTQ_MAXB) return hipErrorInvalidValue;
+    switch (a.G) {
+        case 4: return launch_gtq_g<4>(a, B, R, v_bits, s);
+        case 8: return launch_gtq_g<8>(a, B, R, v_bits, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace bgtq

@@ -92,14 +92,15 @@ int geometry(const bgtq_cache* c, bgtq::Geometry& g) {
     return BGTQ_OK;
 }
 
-int default_splits(int64_t max_tiles, int bh, int n_cu, int per_cu) {
+int default_splits(int64_t max_tiles, int bh, int n_cu, int per_cu, int waves = 4) {
     // One round of workgroups (per_cu resident per CU), each with a whole number of tiles per wave
-    // (a multiple of 4, at least 8) so that the waves of a split finish together.
+    // (a multiple of the wave count; at least two tiles per wave with four waves, one with more) so
+    // that the waves of a split finish together.
     const int64_t target = (int64_t)per_cu * n_cu;
     int64_t s = (target + bh - 1) / bh;
     if (s < 1) s = 1;
     int64_t tps = (max_tiles + s - 1) / s;
-    tps = (tps + 3) / 4 * 4;
+    tps = (tps + waves - 1) / waves * waves;
     if (tps < 8) tps = 8;
     s = (max_tiles + tps - 1) / tps;
     return (int)(s < 1 ? 1 : s);
@@ -117,6 +118,24 @@ int cu_count() {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Block-GTQ keys with 4 or 8 query heads per kv head take the plan-driven matrix-core decode, one
+// workgroup per compute unit.
+bool uses_gtq_kernel(const bgtq_cache* c, int G) { return c->k_mode == BGTQ_K_BLOCKGTQ && G >= 4; }
+
+// The library's split count for a context of max_tiles tiles per (batch, kv head).  Block-GTQ at
+// g >= 4: one tile per wave of a sixteen-wave workgroup when one round of workgroups covers the
+// context, else one round of eight-wave workgroups that loop over their tiles.  Other formats: the
+// per-CU heuristic of their kernel.
+int auto_splits(const bgtq_cache* c, int G, int64_t max_tiles, int bh) {
+    const int n_cu = cu_count();
+    if (uses_gtq_kernel(c, G)) {
+        const int64_t one = (max_tiles + bgtq::kGtqWavesOneTile - 1) / bgtq::kGtqWavesOneTile;
+        if (one * bh <= n_cu) return (int)std::max<int64_t>(one, 1);
+        return default_splits(max_tiles, bh, n_cu, 1, bgtq::kGtqWavesLoop);
+    }
+    return default_splits(max_tiles, bh, n_cu, bgtq::decode_wgs_per_cu(c->k_mode, G, c->v_bits, c->k_group));
+}
 
 // Event pairs around main-kernel launches (tracing aid, see bgtq_profile_enable).
 struct Profiler {
@@ -372,6 +391,20 @@ int bgtq_block_energy(const void* k_cal, const void* q_cal, int dtype, int64_t T
     return ok();
 }
 
+int bgtq_prepare_metadata(const bgtq_cache* c, int layer, void* stream) {
+    bgtq::Geometry g;
+    int rc = geometry(c, g);
+    if (rc) return rc;
+    if (layer < 0 || layer >= c->L) return fail(BGTQ_E_INVALID, "layer %d out of range", layer);
+    if (c->k_mode != BGTQ_K_BLOCKGTQ) return fail(BGTQ_E_INVALID, "the decode plan is for Block-GTQ keys");
+    if (!c->bits || !c->plan) return fail(BGTQ_E_INVALID, "NULL bits or plan");
+    hipError_t e = bgtq::launch_plan(c->bits + (size_t)layer * g.Hkv * 64,
+                                     (uint8_t*)c->plan + (size_t)layer * g.Hkv * BGTQ_PLAN_BYTES, g.Hkv,
+                                     (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "plan launch");
+    return ok();
+}
+
 int64_t bgtq_cache_bytes(const bgtq_cache* c, int which) {
     bgtq::Geometry g;
     int rc = geometry(c, g);
@@ -387,6 +420,7 @@ int64_t bgtq_cache_bytes(const bgtq_cache* c, int which) {
         case BGTQ_BUF_RECENT_K:
         case BGTQ_BUF_RECENT_V: return L * g.recent_layer;
         case BGTQ_BUF_META: return L * g.Hkv * 64 * (1 + 4 + 4);
+        case BGTQ_BUF_PLAN: return c->k_mode == BGTQ_K_BLOCKGTQ ? L * g.Hkv * BGTQ_PLAN_BYTES : 0;
     }
     return fail(BGTQ_E_INVALID, "unknown buffer selector %d", which);
 }
@@ -673,8 +707,13 @@ int64_t bgtq_decode_workspace_bytes(const bgtq_cache* c, int n_splits) {
     if (rc) return rc;
     if (n_splits < 0) return fail(BGTQ_E_INVALID, "n_splits < 0");
     const int64_t max_tiles = g.n_tiles;
-    const int ns = n_splits ? n_splits
-                            : default_splits(max_tiles, g.B * g.Hkv, cu_count(), bgtq::decode_wgs_per_cu(c->k_mode, g.G, c->v_bits, c->k_group));
+    // the largest count the library picks for any length up to the capacity
+    int ns = n_splits;
+    if (!ns) {
+        const int bh = g.B * g.Hkv;
+        ns = auto_splits(c, g.G, max_tiles, bh);
+        if (uses_gtq_kernel(c, g.G)) ns = std::max(ns, std::max(1, cu_count() / bh));
+    }
     const int parts = ns + (g.n_recent > 0 ? 1 : 0);
     if (parts > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS - 1);
     return (int64_t)g.B * g.Hq * parts * PART * 4;
@@ -701,6 +740,8 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
     if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale) return fail(BGTQ_E_INVALID, "NULL cache buffer");
     if (c->k_mode == BGTQ_K_BLOCKGTQ && (!c->bits || !c->sigma))
         return fail(BGTQ_E_INVALID, "NULL key metadata");
+    if (uses_gtq_kernel(c, g.G) && !c->plan)
+        return fail(BGTQ_E_INVALID, "NULL decode plan (Block-GTQ keys need bgtq_prepare_metadata)");
     if (c->k_mode == BGTQ_K_AFFINE && !c->k_zero) return fail(BGTQ_E_INVALID, "affine keys need k_zero");
     if (c->v_mode == BGTQ_V_AFFINE && !c->v_zero) return fail(BGTQ_E_INVALID, "affine values need v_zero");
     if (c->n_recent > 0 && (!c->recent_k || !c->recent_v)) return fail(BGTQ_E_INVALID, "recent ring buffers are NULL");
@@ -725,10 +766,7 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
         any_recent |= rec > 0;
     }
     // Default splits follow the current length; never more than the capacity-sized workspace holds.
-    const int per_cu = bgtq::decode_wgs_per_cu(c->k_mode, g.G, c->v_bits, c->k_group);
-    int ns = n_splits ? n_splits
-                      : std::min(default_splits(std::max<int64_t>(max_tiles, 1), g.B * g.Hkv, cu_count(), per_cu),
-                                 default_splits(g.n_tiles, g.B * g.Hkv, cu_count(), per_cu));
+    int ns = n_splits ? n_splits : auto_splits(c, g.G, std::max<int64_t>(max_tiles, 1), g.B * g.Hkv);
     int parts = ns + (c->n_recent > 0 ? 1 : 0);
     const size_t per_part = (size_t)g.B * g.Hq * PART * 4;
     if (cap_to_ws && n_splits == 0 && ws_bytes < parts * per_part) {
@@ -762,6 +800,7 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
     a.bits = c->k_mode == BGTQ_K_BLOCKGTQ ? c->bits + (size_t)layer * g.Hkv * 64 : nullptr;
     a.sigma = c->k_mode == BGTQ_K_BLOCKGTQ ? c->sigma + (size_t)layer * g.Hkv * 64 : nullptr;
     a.k_rot = c->k_rot ? c->k_rot + (size_t)layer * g.Hkv * 16 : nullptr;
+    a.plan = uses_gtq_kernel(c, g.G) ? (const uint8_t*)c->plan + (size_t)layer * g.Hkv * BGTQ_PLAN_BYTES : nullptr;
     bgtq::Fp16Args ra{};
     if (c->n_recent > 0) {
         ra.k16 = (const uint16_t*)c->recent_k + (size_t)layer * bh * c->n_recent * D;
@@ -796,7 +835,8 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
     a.v_affine = c->v_mode == BGTQ_V_AFFINE;
     {
         ProfScope ps(BGTQ_PROF_DECODE, s);
-        e = bgtq::launch_decode(a, g.B, c->k_mode, g.R, c->v_bits, s);
+        e = uses_gtq_kernel(c, g.G) ? bgtq::launch_decode_gtq(a, g.B, g.R, c->v_bits, s)
+                                    : bgtq::launch_decode(a, g.B, c->k_mode, g.R, c->v_bits, s);
     }
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     if (c->n_recent > 0) {

@@ -40,6 +40,7 @@ struct DecodeArgs {
     const uint8_t* bits;        // [Hkv][64] this layer's widths (Block-GTQ)
     const float* sigma;         // [Hkv][64]
     const uint8_t* k_rot;       // [Hkv][16] sign bits of the key rotation (affine keys), or null
+    const uint8_t* plan;        // [Hkv][BGTQ_PLAN_BYTES] this layer's decode plan (Block-GTQ keys)
     float* part;                // [B][Hq][n_parts][132]
     int q_dtype;
     int Hkv, Hq, G;
@@ -144,6 +145,15 @@ struct PermuteArgs {
 // launch error.
 hipError_t launch_permute(const PermuteArgs& a, int B, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t s);
+// Block-GTQ keys at g = 4 or 8 (bgtq_decode_gtq.hip): one workgroup of kGtqWaves waves per split.
+hipError_t launch_decode_gtq(const DecodeArgs& a, int B, int R, int v_bits, hipStream_t s);
+hipError_t launch_plan(const uint8_t* bits, uint8_t* plan, int Hkv, hipStream_t s);
+// Waves per workgroup of the Block-GTQ matrix-core decode (one workgroup per compute unit): splits
+// of at most kGtqWavesOneTile tiles run one tile per wave, longer ones loop on kGtqWavesLoop waves.
+constexpr int kGtqWavesOneTile = 16;
+constexpr int kGtqWavesLoop = 8;
+// Event pair armed for the next main-kernel launch of this thread (see arm_launch_events).
+extern thread_local hipEvent_t t_ev_start, t_ev_stop;
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s);
 hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t s);
 hipError_t launch_energy(const EnergyArgs& a, hipStream_t s);

@@ -23,61 +23,12 @@
 #include <hip/hip_ext.h>
 
 #include "../../include/bgtq.h"
+#include "bgtq_device.h"
 #include "generated/bgtq_codebook_data.h"
 
 namespace bgtq {
 namespace {
 
-constexpr int TILE = 64;
-constexpr int D = 128;
-constexpr int PART = 132;                       // floats per partial record: o[128], m, l
-constexpr int kAppendFewMax = 16;               // appends of at most this many positions per sequence take k_append
-constexpr float kLog2eOverSqrtD = 0.12751743074233076f;  // log2(e) / sqrt(128)
-
-__constant__ uint32_t c_cent32[BGTQ_CB_CENTROIDS] = BGTQ_CB_CENTROID_F32_INIT;
-__constant__ uint16_t c_cent16[BGTQ_CB_CENTROIDS] = BGTQ_CB_CENTROID_F16_INIT;
-__constant__ uint32_t c_thr32[BGTQ_CB_THRESHOLDS] = BGTQ_CB_THRESHOLD_F32_INIT;
-// LDS image of the matrix-core decode's tables: pair tables of widths 5..1, then the fp16
-// centroid tables of widths 8..1, each at a multiple of its size (offsets BGTQ_CB_MX_*_OFFSETS).
-__constant__ __attribute__((aligned(16))) uint32_t c_mxtab[BGTQ_CB_MX_WORDS] = BGTQ_CB_MX_INIT;
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-// Read-only global data the kernel never writes, read through the constant address space so
-// uniform loads become scalar loads.
-typedef __attribute__((address_space(4))) uint32_t cu32_t;
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ int cent_base(int w) { return (1 << w) - 2; }
-__device__ __forceinline__ int thr_base(int w) { return (1 << w) - w - 1; }
-__device__ __forceinline__ float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
-__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
-__device__ __forceinline__ float bf2f(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
-
-__device__ __forceinline__ float load_act(const void* p, int64_t i, int dtype) {
-    if (dtype == BGTQ_F32) return ((const float*)p)[i];
-    const uint32_t u = ((const uint16_t*)p)[i];
-    return dtype == BGTQ_F16 ? h2f(u) : bf2f(u);
-}
-
-// Orders LDS traffic of one wave: lanes exchange data through LDS without a workgroup barrier.
-__device__ __forceinline__ void wave_lds_fence() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
 
 // ---------------------------------------------------------------------------------------------
 // acc[h] += bcast(q, lane BASE + h) * va ; acc[h] += bcast(q, lane BASE + G + h) * vb
@@ -286,40 +237,6 @@ __device__ __forceinline__ void merge_waves(const float* red, float* sc, float* 
     }
 }
 
-// merge_waves for four waves with 16-byte accesses: thread (h, quad of dims) handles 4 dims.
-template <int G>
-__device__ __forceinline__ void merge_waves4(const float* red, float* sc, float* part, int n_parts, int split) {
-    if (threadIdx.x < G) {
-        const int h = threadIdx.x;
-        float M = -INFINITY;
-#pragma unroll
-        for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, red[(wv * G + h) * PART + 128]);
-        float L = 0.f;
-#pragma unroll
-        for (int wv = 0; wv < 4; ++wv) {
-            const float m = red[(wv * G + h) * PART + 128];
-            const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-            sc[wv * G + h] = f;
-            L += f * red[(wv * G + h) * PART + 129];
-        }
-        // partials are read once, by the split merge: stream them past the caches
-        float* dst = part + ((size_t)h * n_parts + split) * PART;
-        dst[128] = M;
-        dst[129] = L;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * 32; idx += blockDim.x) {
-        const int h = idx >> 5, j = 4 * (idx & 31);
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int wv = 0; wv < 4; ++wv) {
-            const float* rw = red + (wv * G + h) * PART;
-            const float f = sc[wv * G + h];
-            acc += f * (*(const f32x4_t*)(rw + j) + rw[130]);
-        }
-        *(f32x4_t*)(part + ((size_t)h * n_parts + split) * PART + j) = acc;
-    }
-}
 
 // Epilogue: merge lanes and waves, write one (o[128], m, l) partial per query head.
 // STRIDE16: o[h][j] holds dim 16j + lane (lanes 0..15 after the merge); else dim 8*lane + j.
@@ -531,67 +448,6 @@ __device__ void fp16_tiles(WaveState<G>& st, const uint16_t* K16, const uint16_t
 //  dsc16[s]: slot descriptor (start dword | bit offset << 5 | width << 10); padding = width 1 at 0.
 //  qs[g*G + h]: per-key-group sums of the natural scaled query (affine keys).
 // The block order comes from nine wave ballots (one per width) instead of a sort.
-// Stream order of the RoPE blocks (lane = block, w = its width): rank among the nonzero blocks by
-// width descending (ties: lower block first), bit position of its 2w-bit field in the K record,
-// and the number of nonzero blocks.  Nine wave ballots, one per width.
-__device__ __forceinline__ void block_order(int w, int lane, int& rank, int& pos, int& nnz) {
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    rank = 0;
-    pos = 0;
-    nnz = 0;
-#pragma unroll
-    for (int v = 0; v <= 8; ++v) {
-        const uint64_t mk = __ballot(w == v);
-        const int c = __popcll(mk);
-        if (v == 0) nnz = 64 - c;
-        if (v > w) {
-            rank += c;
-            pos += 2 * v * c;
-        } else if (v == w) {
-            const int cl = __popcll(mk & lt);
-            rank += cl;
-            pos += 2 * v * cl;
-        }
-    }
-}
-
-// Global inputs of the preparation (lane = RoPE block), loaded raw and converted later so a kernel
-// can issue them, then its tile prefetch, before anything waits on them.
-template <int G> struct PrepIn {
-    uint32_t r0[G], r1[G];  // fp32 bits of (q_2i, q_2i+1), or the packed 16-bit pair in r0
-    float sg;
-    uint32_t w4;  // the dword of the width array holding this block's width (byte lane & 3)
-    int dtype;
-};
-
-template <int G, bool SORTED>
-__device__ __forceinline__ PrepIn<G> prep_load(const void* q, int dtype, const uint8_t* bits, const float* sigma, int b,
-                                               int h, int Hq, int lane) {
-    PrepIn<G> in;
-    in.dtype = dtype;
-    in.w4 = 0u;
-    in.sg = 0.f;
-    if constexpr (SORTED) {
-        in.w4 = ((const uint32_t*)(bits + h * 64))[lane >> 2];
-        in.sg = sigma[h * 64 + lane];
-    }
-    const int64_t row0 = ((int64_t)b * Hq + (int64_t)h * G) * D + 2 * lane;
-    if (dtype == BGTQ_F32) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const uint2 v = *(const uint2*)((const float*)q + row0 + (int64_t)hh * D);
-            in.r0[hh] = v.x;
-            in.r1[hh] = v.y;
-        }
-    } else {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            in.r0[hh] = *(const uint32_t*)((const uint16_t*)q + row0 + (int64_t)hh * D);
-            in.r1[hh] = 0u;
-        }
-    }
-    return in;
-}
 
 // Keys stored rotated (y = H (s * k) / 16): the query goes to H (s * q) / 8, so q'.y = q.k.  A
 // wave holds coordinates 2 lane + e (q0: e = 0, q1: e = 1); stage 1 pairs them inside the lane,
@@ -871,277 +727,6 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
 //    largest weight of a split is fp16(scale) exactly, whatever the split boundaries.
 
 
-__device__ __forceinline__ half8_t as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    const u32x4_t v = {a, b, c, d};
-    return __builtin_bit_cast(half8_t, v);
-}
-__device__ __forceinline__ f32x4_t mfma16(half8_t a, half8_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-// Column descriptor of one stream slot (one dword, built in the prologue; a lane reads the four of a
-// k-step with one 16-byte LDS read).  A lane
-// row reads the two adjacent slots A = 2i, B = 2i + 1 of a column pair from one 64-bit window
-// that starts at a stage row boundary below A's field:
-//   bits 0..5   64-bit shift that moves the slot's field (pair) or first code (coordinates) to bit
-//               2 (pair) or bit 1 (coordinates)
-//   bits 6..11  64-bit shift that moves the second code to bit 1 (coordinate columns)
-//   bits 12..16 field width: 2w for a pair column, w for a coordinate column (0: empty slot)
-//   bits 17..31 byte offset of the window's first stage row (slot A's descriptor)
-// posA/coordA: slot A's record position and column mode; pos/w/coord: this slot's.  Every shift
-// stays below 64 and every field inside the window: A's offset is below 32 and A and B together
-// span at most 32 bits.
-__device__ __forceinline__ uint32_t mx_desc(int posA, bool coordA, int pos, int w, bool coord) {
-    const int uA = posA - (coordA ? 1 : 2);       // >= -2
-    const int rr = uA >= 0 ? uA >> 5 : -1;        // window row (-1: the spare row)
-    const int base = 32 * rr;
-    const int s0 = pos - (coord ? 1 : 2) - base;
-    const uint32_t sh0 = (uint32_t)(s0 < 0 ? 0 : s0);  // < 0 only for empty slots
-    const uint32_t sh1 = coord ? sh0 + (uint32_t)w : 0u;
-    const uint32_t fw = (uint32_t)(w == 0 ? 0 : (coord ? w : 2 * w));
-    return sh0 | (sh1 << 6) | (fw << 12) | ((uint32_t)(rr + 1) * BGTQ_KST_ROW_BYTES << 17);
-}
-
-// ((1 << (width & 31)) - 1) << OFF in one v_bfm_b32.
-template <int OFF>
-__device__ __forceinline__ uint32_t bfm(uint32_t width) {
-    uint32_t r;
-    asm("v_bfm_b32 %0, %1, %2" : "=v"(r) : "v"(width), "n"(OFF));
-    return r;
-}
-
-// Slot of a column read as a coordinate pair: 64-bit shift, and_or into the pair table of the
-// slot's width, one 4-byte read.
-__device__ __forceinline__ uint32_t slot_pair(const uint8_t* lds, uint64_t win, uint32_t dsc, uint32_t mask,
-                                              uint32_t base) {
-    const uint32_t x = (uint32_t)(win >> (dsc & 63u));
-    return *(const uint32_t*)(lds + ((x & mask) | base));
-}
-// Slot of a column read per coordinate (the column's first slot is wider than 5 bits): two
-// shifts, two 2-byte reads from the fp16 centroid table of the slot's width.
-__device__ __forceinline__ uint32_t slot_coord(const uint8_t* lds, uint64_t win, uint32_t dsc, uint32_t mask,
-                                               uint32_t base) {
-    const uint32_t x0 = (uint32_t)(win >> (dsc & 63u));
-    const uint32_t x1 = (uint32_t)(win >> ((dsc >> 6) & 63u));
-    const uint32_t c0 = *(const uint16_t*)(lds + ((x0 & mask) | base));
-    const uint32_t c1 = *(const uint16_t*)(lds + ((x1 & mask) | base));
-    return c0 | (c1 << 16);
-}
-
-// Both column pairs of a k-step: the eight windows (two column pairs x four token groups) as one
-// batch of ds_read2, then the sixteen slot lookups, so that a k-step waits on two LDS round trips
-// rather than three.  CA0/CB0, CA1/CB1: coordinate mode of columns 0..3.
-template <bool CA0, bool CB0, bool CA1, bool CB1>
-__device__ __forceinline__ void col_pairs_both(uint32_t (&P)[16], const uint8_t* lds, const u32x4_t dk, uint32_t lb) {
-    const uint32_t ad0 = (dk[0] >> 17) + lb, ad1 = (dk[2] >> 17) + lb;
-    const uint32_t m0 = CA0 ? bfm<1>(dk[0] >> 12) : bfm<2>(dk[0] >> 12);
-    const uint32_t m1 = CB0 ? bfm<1>(dk[1] >> 12) : bfm<2>(dk[1] >> 12);
-    const uint32_t m2 = CA1 ? bfm<1>(dk[2] >> 12) : bfm<2>(dk[2] >> 12);
-    const uint32_t m3 = CB1 ? bfm<1>(dk[3] >> 12) : bfm<2>(dk[3] >> 12);
-    const uint32_t b0 = m0 + (CA0 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
-    const uint32_t b1 = m1 + (CB0 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
-    const uint32_t b2 = m2 + (CA1 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
-    const uint32_t b3 = m3 + (CB1 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
-    static_assert(BGTQ_KST_ROW_BYTES == 320, "window read offsets assume 80-dword stage rows");
-    uint64_t wa[4], wb[4];
-    asm volatile("ds_read2_b32 %0, %8 offset1:80\n\t"
-                 "ds_read2_b32 %1, %8 offset0:16 offset1:96\n\t"
-                 "ds_read2_b32 %2, %8 offset0:32 offset1:112\n\t"
-                 "ds_read2_b32 %3, %8 offset0:48 offset1:128\n\t"
-                 "ds_read2_b32 %4, %9 offset1:80\n\t"
-                 "ds_read2_b32 %5, %9 offset0:16 offset1:96\n\t"
-                 "ds_read2_b32 %6, %9 offset0:32 offset1:112\n\t"
-                 "ds_read2_b32 %7, %9 offset0:48 offset1:128\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(wa[0]), "=&v"(wa[1]), "=&v"(wa[2]), "=&v"(wa[3]),
-                   "=&v"(wb[0]), "=&v"(wb[1]), "=&v"(wb[2]), "=&v"(wb[3])
-                 : "v"((uint32_t)(uintptr_t)(lds + ad0)), "v"((uint32_t)(uintptr_t)(lds + ad1))
-                 : "memory");
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        P[4 * g + 0] = CA0 ? slot_coord(lds, wa[g], dk[0], m0, b0) : slot_pair(lds, wa[g], dk[0], m0, b0);
-        P[4 * g + 1] = CB0 ? slot_coord(lds, wa[g], dk[1], m1, b1) : slot_pair(lds, wa[g], dk[1], m1, b1);
-        P[4 * g + 2] = CA1 ? slot_coord(lds, wb[g], dk[2], m2, b2) : slot_pair(lds, wb[g], dk[2], m2, b2);
-        P[4 * g + 3] = CB1 ? slot_coord(lds, wb[g], dk[3], m3, b3) : slot_pair(lds, wb[g], dk[3], m3, b3);
-    }
-}
-
-// k-step KS with its first A columns read per coordinate and the rest as pairs: the operands.
-template <int KS, int A>
-__device__ __forceinline__ void mx_kops(uint32_t (&P)[16], const uint8_t* lds, const u32x4_t* sd, uint32_t lb) {
-    const u32x4_t dk = sd[KS];
-    col_pairs_both<(A > 0), (A > 1), (A > 2), (A > 3)>(P, lds, dk, lb);
-}
-
-// k-step KS of a tile; ncc (wave-uniform) = number of coordinate columns of the whole record.  The
-// column modes only change how the operands are built; the products sit after the branches.
-template <int KS>
-__device__ __forceinline__ void mx_kstep_any(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
-                                             const u32x4_t* sd, uint32_t lb, int ncc) {
-    uint32_t P[16];
-    const int a = ncc - 4 * KS;
-    if (a <= 0) mx_kops<KS, 0>(P, lds, sd, lb);
-    else if (a == 1) mx_kops<KS, 1>(P, lds, sd, lb);
-    else if (a == 2) mx_kops<KS, 2>(P, lds, sd, lb);
-    else if (a == 3) mx_kops<KS, 3>(P, lds, sd, lb);
-    else mx_kops<KS, 4>(P, lds, sd, lb);
-    const half8_t q = __builtin_bit_cast(half8_t, qa[KS * 64 + lane]);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const half8_t kb = as_h8(P[4 * g], P[4 * g + 1], P[4 * g + 2], P[4 * g + 3]);
-        c[g] = KS == 0 ? mfma16(q, kb, f32x4_t{0.f, 0.f, 0.f, 0.f}) : mfma16(q, kb, c[g]);
-    }
-}
-
-// The matrix-core decode's value table holds interleaved copies (entry e of copy c at dword
-// e * copies + c) and lane l reads copy l % copies.  With 32 copies (values of up to 3 bits, 8 KB
-// at 3 bits) every lane of the 32 that the LDS serves per pass owns one of its 32 banks, so random
-// entries never conflict (measured on gfx950: random reads from a table wider than 32 dwords cost
-// 1.7x to 2.8x a conflict-free read); 4-bit values keep 4 copies (the 256-entry table).
-template <int VB> struct VLutGeom {
-    static constexpr int LOG2_COPIES = VB <= 3 ? 5 : 2;
-    static constexpr int COPIES = 1 << LOG2_COPIES;
-    static constexpr int BYTES = 4 * COPIES * (1 << (2 * VB));
-};
-// Field F of this lane's value stream scaled to a byte offset in the replicated table, OR-ed with
-// the lane's copy offset (one shift, one and_or).
-template <int VB, int F>
-__device__ __forceinline__ uint32_t vfield_rep(const uint32_t* r, uint32_t lane_copy) {
-    constexpr int bit = 2 * VB * F, w = bit / 32, sh = bit % 32, nb = 2 * VB;
-    constexpr int S = 2 + VLutGeom<VB>::LOG2_COPIES;
-    constexpr uint32_t m = ((1u << nb) - 1u) << S;
-    uint32_t x;
-    if constexpr (sh + nb > 32) x = __builtin_amdgcn_alignbit(r[w + 1], r[w], sh - S);
-    else if constexpr (sh >= S) x = r[w] >> (sh - S);
-    else x = r[w] << (S - sh);
-    return (x & m) | lane_copy;
-}
-
-// P·V of one 32-token half S: B = W rows of this lane's head column, A = value fields (S, db, m).
-template <int VB, int F>
-__device__ __forceinline__ uint32_t vpair(const uint32_t* vs, const uint32_t* vlut, uint32_t lane_copy) {
-    return *(const uint32_t*)((const uint8_t*)vlut + vfield_rep<VB, F>(vs, lane_copy));
-}
-template <int VB, int S>
-__device__ __forceinline__ void mx_pv(f32x4_t (&o)[8], const uint32_t* vs, const uint32_t* vlut, const uint32_t* wx,
-                                      int lane, uint32_t lc) {
-    const u32x4_t wq = *(const u32x4_t*)(wx + (lane & 15) * 32 + 16 * S + 4 * (lane >> 4));
-    const half8_t wb = __builtin_bit_cast(half8_t, wq);
-#define BGTQ_PV(DB)                                                                                          \
-    o[DB] = mfma16(as_h8(vpair<VB, (S * 8 + DB) * 4>(vs, vlut, lc), vpair<VB, (S * 8 + DB) * 4 + 1>(vs, vlut, lc), \
-                         vpair<VB, (S * 8 + DB) * 4 + 2>(vs, vlut, lc), vpair<VB, (S * 8 + DB) * 4 + 3>(vs, vlut, lc)), \
-                   wb, o[DB])
-    BGTQ_PV(0); BGTQ_PV(1); BGTQ_PV(2); BGTQ_PV(3); BGTQ_PV(4); BGTQ_PV(5); BGTQ_PV(6); BGTQ_PV(7);
-#undef BGTQ_PV
-}
-
-// Plain v_max_f32 / v_max3_f32: the operands here are never NaN (scores, -inf for masked tokens),
-// so the quieting that fmaxf adds on values of unknown origin is dead work.
-__device__ __forceinline__ float vmax(float a, float b) {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-// Max over the 16 lanes of a row: four DPP row rotations fused into the max (two wait states
-// before each, as a DPP source written by the previous VALU instruction requires).
-__device__ __forceinline__ float row_max16(float v) {
-    float r;
-    asm("s_nop 1\n\t"
-        "v_max_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 1\n\t"
-        "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 1\n\t"
-        "v_max_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 1\n\t"
-        "v_max_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf"
-        : "=&v"(r) : "v"(v));
-    return r;
-}
-__device__ __forceinline__ float row_sum16(float v) {
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false));
-    return v;
-}
-
-// Query operands of the matrix-core decode, written by one wave (lane = RoPE block): q' = q *
-// sigma * log2(e)/sqrt(d) of block i (stream slot r = its rank) goes, split into an fp16 high part
-// and an fp16 low part, to k-step r / 16, lane row (r % 8) / 2, element pair 2 ((r % 16) / 8) +
-// r % 2 of the operand lanes of its heads (column 2h: high part, 2h + 1: low part).  Slots past
-// the nonzero blocks, and the columns of absent heads, get zeros.  s_nnz[0] = nonzero blocks
-// rounded up to 4.
-template <int G>
-__device__ void mx_prep_q(const PrepIn<G>& in, int w, int lane, uint8_t* qa, uint32_t* s_nnz) {
-    float q0[G], q1[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        if (in.dtype == BGTQ_F32) {
-            q0[hh] = __builtin_bit_cast(float, in.r0[hh]);
-            q1[hh] = __builtin_bit_cast(float, in.r1[hh]);
-        } else if (in.dtype == BGTQ_F16) {
-            q0[hh] = h2f(in.r0[hh] & 0xFFFFu);
-            q1[hh] = h2f(in.r0[hh] >> 16);
-        } else {
-            q0[hh] = bf2f(in.r0[hh] & 0xFFFFu);
-            q1[hh] = bf2f(in.r0[hh] >> 16);
-        }
-        q0[hh] = q0[hh] * kLog2eOverSqrtD * in.sg;
-        q1[hh] = q1[hh] * kLog2eOverSqrtD * in.sg;
-    }
-    int rank, pos, nnz;
-    block_order(w, lane, rank, pos, nnz);
-    auto put = [&](int r, bool zero) {
-        const int ks = r >> 4, rr = r & 15, urow = (rr >> 1) & 3, mpair = 2 * (rr >> 3) + (rr & 1);
-        uint8_t* base = qa + (size_t)(ks * 64 + 16 * urow) * 16 + 4 * mpair;
-#pragma unroll
-        for (int hh = 0; hh < 8; ++hh) {
-            uint32_t hi2 = 0u, lo2 = 0u;
-            if (hh < G && !zero) {
-                const _Float16 h0 = (_Float16)q0[hh], h1 = (_Float16)q1[hh];
-                const _Float16 l0 = (_Float16)(q0[hh] - (float)h0), l1 = (_Float16)(q1[hh] - (float)h1);
-                hi2 = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                lo2 = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
-            }
-            *(uint32_t*)(base + (2 * hh) * 16) = hi2;
-            *(uint32_t*)(base + (2 * hh + 1) * 16) = lo2;
-        }
-    };
-    if (w > 0) put(rank, false);
-    if (lane >= nnz) put(lane, true);
-    if (lane == 0) s_nnz[0] = (uint32_t)((nnz + 3) & ~3);
-}
-
-// LDS arena of the matrix-core decode (byte offsets).  Loop-time regions: tables (at offset 0,
-// the arena being 8192-aligned, so table offsets are LDS addresses), column descriptors, value
-// centroid pairs, query operands, weight exchange, softmax rescale factors, and per wave the stage
-// of the tile in flight (K record rows -1 .. R at BGTQ_KST_ROW_BYTES stride, scales).  The
-// prologue's block order and the epilogue records alias the stages.
-constexpr int a16(int x) { return (x + 15) & ~15; }
-constexpr int cmax(int x, int y) { return x > y ? x : y; }
-template <int G, int R, int VB> struct MxLds {
-    static constexpr int TAB = 0;                                     // BGTQ_CB_MX_BYTES
-    static constexpr int DESC = a16(TAB + BGTQ_CB_MX_BYTES);          // u32 [4 lane rows][16 columns]
-    static constexpr int VLUT = DESC + 64 * 4;                        // u32 [4^VB][copies]
-    static constexpr int QA = a16(VLUT + VLutGeom<VB>::BYTES);        // u32x4 [4 k-steps][64 lanes]
-    static constexpr int WX = QA + 4 * 64 * 16;                       // u32 [4 waves][16 heads][32 pairs]
-    static constexpr int ALPHA = WX + 4 * 16 * 32 * 4;                // f32 [4 waves][16]
-    static constexpr int NNZ = ALPHA + 4 * 16 * 4;                    // u32 [4]: padded nonzero slots, coordinate columns
-    static constexpr int KST = a16(NNZ + 16);                         // per wave: R + 2 rows
-    static constexpr int KST_W = (R + 2) * BGTQ_KST_ROW_BYTES;
-    static constexpr int SST = KST + 4 * KST_W;                       // per wave: K scales, V scales, V zeros
-    static constexpr int SST_W = 3 * 64 * 2;
-    static constexpr int QP = KST;                                    // prologue: i32 [2][64] block order
-    static constexpr int RED = KST;                                   // epilogue: f32 [4 G PART + 4 G]
-    static constexpr int SIZE = cmax(cmax(SST + 4 * SST_W, QP + 512), RED + 4 * (4 * G * PART + 4 * G));
-};
-
-// 3-bit values (the headline K3V3 shapes) take two resident workgroups per CU and the register
-// room that buys (both column pairs' windows of a k-step in flight); the others three.
 template <int VB> constexpr int mx_wgs_per_cu() { return VB == 3 ? 2 : 3; }
 
 template <int G, int R, int VB>
@@ -2085,10 +1670,10 @@ __device__ __forceinline__ float wave_total_max(float v) {
 }
 
 // Split merge: one wave per (query head row, 4 dims).  Lane l folds partials l, l + 64, ... with
-// an online log-sum-exp, four partials per round with their loads issued together, then the 64
+// an online log-sum-exp, U partials per round with their loads issued together, then the 64
 // lane states merge across the wave.
+template <int U>
 __global__ __launch_bounds__(64) void k_combine(const CombineArgs a) {
-    constexpr int U = 4;
     const int row = blockIdx.x, d0 = blockIdx.y * CMB_DIMS, lane = threadIdx.x;
     const float* pr = a.part + (size_t)row * a.n_parts * PART;
     float m = -INFINITY, acc[CMB_DIMS + 1];
@@ -2727,22 +2312,13 @@ __global__ __launch_bounds__(128) void k_ring(const RingArgs a) {
 // Launchers
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 
-// Launch with the armed event pair, if any (consumed), else plainly.
-template <typename K, typename A>
-static hipError_t launch_main(K kernel, dim3 grid, dim3 block, hipStream_t s, const A& a) {
-    if (t_ev_start) {
-        hipEvent_t e0 = t_ev_start, e1 = t_ev_stop;
-        t_ev_start = t_ev_stop = nullptr;
-        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, a);
-    } else {
-        hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
-    }
-    return hipGetLastError();
-}
-
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s) {
     if (!a.part || !a.out || a.n_parts < 1 || a.n_parts > BGTQ_MAX_PARTS) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_combine, dim3(rows, D / CMB_DIMS), dim3(64), 0, s, a);
+    // partials per lane per round: no more loads than there are partials
+    const dim3 grid(rows, D / CMB_DIMS);
+    if (a.n_parts <= 64) hipLaunchKernelGGL(k_combine<1>, grid, dim3(64), 0, s, a);
+    else if (a.n_parts <= 128) hipLaunchKernelGGL(k_combine<2>, grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL(k_combine<4>, grid, dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

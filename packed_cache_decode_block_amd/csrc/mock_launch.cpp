@@ -31,6 +31,8 @@ extern "C" void bgtq_mock_reset(void) {
 
 namespace bgtq {
 
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
 hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t) {
     if (!a.k_codes || !a.v_codes || !a.k_scale || !a.v_scale || !a.q || !a.part) return bad("decode: null pointer");
     if (k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma)) return bad("decode: null key metadata");
@@ -48,6 +50,18 @@ hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bi
     }
     if (a.n_tiles * 64 != a.n_cap) return bad("decode: n_tiles");
     note("decode");
+    return hipSuccess;
+}
+
+hipError_t launch_decode_gtq(const DecodeArgs& a, int B, int R, int v_bits, hipStream_t s) {
+    if (!a.plan) return bad("decode: null plan");
+    if (a.G != 4 && a.G != 8) return bad("decode: group size of the plan-driven decode");
+    return launch_decode(a, B, BGTQ_K_BLOCKGTQ, R, v_bits, s);
+}
+
+hipError_t launch_plan(const uint8_t* bits, uint8_t* plan, int Hkv, hipStream_t) {
+    if (!bits || !plan || Hkv < 1) return bad("plan");
+    note("plan");
     return hipSuccess;
 }
 

@@ -27,6 +27,8 @@ def _desc(nt, **kw):
     ptrs = ["k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma"]
     if base["k_mode"] == 1:
         ptrs.append("k_zero")
+    else:
+        ptrs.append("plan")
     if base["v_mode"] == 1:
         ptrs.append("v_zero")
     if base["n_recent"]:
@@ -191,3 +193,24 @@ def test_logquant_append_plan_and_failures(mock):
     pre = (nt.copy(), n_hp.copy(), hp.copy())
     assert mock.bgtq_logquant_append(C.byref(d2), 0, q, q, 2, None, hp.ctypes.data_as(p64), None) == _lib.E_CAPACITY
     assert (nt == pre[0]).all() and (n_hp == pre[1]).all() and (hp == pre[2]).all()
+
+
+def test_prepare_metadata_and_plan_requirement(mock):
+    """The Block-GTQ decode needs the layer's plan: bgtq_prepare_metadata launches one plan kernel
+    per layer; a descriptor without a plan is refused before any launch; affine keys have none."""
+    nt = np.full((2, 2), 500, np.int64)
+    d = _desc(nt)
+    mock.bgtq_mock_reset()
+    _call_ok(mock, mock.bgtq_prepare_metadata(C.byref(d), 1, None))
+    assert mock.bgtq_mock_log().decode().split() == ["plan"]
+    assert mock.bgtq_prepare_metadata(C.byref(d), 2, None) == _lib.E_INVALID
+    assert mock.bgtq_cache_bytes(C.byref(d), _lib.BUF_PLAN) == 2 * 2 * _lib.PLAN_BYTES
+    q = C.c_void_p(FAKE + 0x50000000)
+    ws = C.c_void_p(FAKE + 0x60000000)
+    d.plan = None
+    mock.bgtq_mock_reset()
+    assert mock.bgtq_decode_attention(C.byref(d), 0, q, 2, q, ws, 1 << 30, 0, None) == _lib.E_INVALID
+    assert b"plan" in mock.bgtq_last_error() and mock.bgtq_mock_launches() == 0
+    da = _desc(nt, k_mode=1, k_bits=4, k_group=32, v_mode=1, v_bits=2)
+    assert mock.bgtq_cache_bytes(C.byref(da), _lib.BUF_PLAN) == 0
+    assert mock.bgtq_prepare_metadata(C.byref(da), 0, None) == _lib.E_INVALID

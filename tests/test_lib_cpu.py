@@ -207,7 +207,7 @@ def test_append_and_decode_validate_before_launch():
         setattr(d, name, 0x1000)
     assert P.lib.bgtq_quantize_append(C.byref(d), 0, fake, fake, 2, 10, None, None) == P.E_INVALID
     assert b"inv_sigma" in P.lib.bgtq_last_error()
-    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma"):
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma", "plan"):
         setattr(d, name, 0x1000)
     assert P.lib.bgtq_quantize_append(C.byref(d), 5, fake, fake, 2, 10, None, None) == P.E_INVALID  # layer
     assert P.lib.bgtq_quantize_append(C.byref(d), 0, fake, fake, 9, 10, None, None) == P.E_INVALID  # dtype
@@ -223,7 +223,7 @@ def test_append_and_decode_validate_before_launch():
     assert P.lib.bgtq_decode_attention(C.byref(d), 0, fake, 2, out, ws, 16, 4, None) == P.E_INVALID
     # unsupported decode format (budget 208 -> 13-dword records has no kernel)
     d2 = _desc(budget_units=208)
-    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma"):
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "bits", "sigma", "inv_sigma", "plan"):
         setattr(d2, name, 0x1000)
     d2.n_tokens = nt.ctypes.data_as(C.POINTER(C.c_int64))
     assert P.lib.bgtq_decode_attention(C.byref(d2), 0, fake, 2, out, ws, 1 << 30, 4, None) == P.E_UNSUPPORTED
