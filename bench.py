@@ -5,8 +5,10 @@ One step = decode attention for every layer of the workload (prep + split-K deco
 layer, through the C ABI) with the packed cache, queries and outputs resident in HBM.  Prints one
 JSON line: effective HBM GB/s over algorithmic bytes (codes, scales/zeros, fp16 recent tokens, q,
 out), the decode kernel's roofline (HIP events recorded around every decode kernel's own
-execution over a second pass of the timed steps), the unquantized fp16 comparator, and the CPU
-oracle timed on a bounded sample.
+execution over a second pass of the timed steps, queued behind a GPU-side wait so that the host's
+launch latency stays outside them), the unquantized fp16 comparator, and the CPU
+oracle timed on a bounded sample.  The default run adds the same decode with every product on the
+vector ALUs (vector_alu_decode) and the decode line of each other workload (per_workload).
 
 Default workload: Qwen2.5-3B-shaped decode, 36 layers, 16 query / 2 KV heads, 131072 tokens,
 batch 1, Block-GTQ K3 keys and 3-bit values, bf16 activations (synthetic inputs).
@@ -49,15 +51,18 @@ def layer_bytes(w, N: int) -> float:
             + w.B * w.Hq * w.d * (act + 4))
 
 
-def decode_kernel_name(w) -> str:
-    """The decode kernel a workload dispatches to: Block-GTQ keys with at least four query heads
-    per kv head take the plan-driven matrix-core kernel, everything else the vector-ALU one."""
-    return "k_decode_gtq" if (w.k_mode == "gtq" and w.Hq // w.Hkv >= 4) else "k_decode"
+def decode_kernel_name(w, path: str = "auto") -> str:
+    """The decode kernel a workload dispatches to: with at least four query heads per kv head the
+    matrix-core kernels (plan-driven for Block-GTQ keys, the affine one for affine keys), everything
+    else and the vector path the vector-ALU one."""
+    if path == "auto" and w.Hq // w.Hkv >= 4:
+        return "k_decode_gtq" if w.k_mode == "gtq" else "k_decode_mxa"
+    return "k_decode"
 
 
-def arithmetic(w):
+def arithmetic(w, path: str = "auto"):
     """(dtype, description) of the arithmetic the workload's decode kernel runs."""
-    if decode_kernel_name(w) == "k_decode_gtq" or (w.k_mode != "gtq" and w.Hq // w.Hkv >= 4):
+    if decode_kernel_name(w, path) != "k_decode":
         return "f16", (f"{w.dtype} activations in; q.k and P.V on the matrix cores with fp16 operands "
                        "(key centroids exact in fp16, the scaled query as fp16 high + low parts, softmax "
                        "weights rounded to fp16) accumulated in fp32; softmax and output in fp32")
@@ -65,10 +70,15 @@ def arithmetic(w):
                    "(fp16 centroids times softmax weights rounded to fp16) accumulated in fp32")
 
 
+# Short names of the workloads in profile file names.
+WORKLOAD_TAGS = {1: "1layer_4k", 2: "qwen2.5-3b_128k", 3: "llama3.1-8b_32k_b8", 4: "llama3.1-8b_64k_b2_affine",
+                 5: "qwen2.5-3b_512k"}
+
 # Source files each decode kernel is built from; a counter summary holds for the sha256 of these.
 KERNEL_SOURCES = {
     "k_decode_gtq": ("bgtq_decode_gtq.hip", "bgtq_device.h"),
     "k_decode": ("bgtq_kernels.hip", "bgtq_device.h"),
+    "k_decode_mxa": ("bgtq_kernels.hip", "bgtq_device.h"),
     "k_decode_fp16_mx": ("bgtq_kernels.hip", "bgtq_device.h"),
 }
 
@@ -86,7 +96,7 @@ def measured_traffic(wid: int, kernel: str = "k_decode_gtq"):
     workload (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None when there is
     none or the kernel source has changed since the counters were taken."""
     import re
-    path = os.path.join(ROOT, "profiles", {2: f"{kernel}_qwen2.5-3b_128k_hbm_counters.md"}.get(wid, "-"))
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{WORKLOAD_TAGS.get(wid, '-')}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -169,6 +179,117 @@ def timed(run_step, steps: int, warmup: int):
     return (time.perf_counter() - t0) / steps
 
 
+def queued(torch, run_step, steps: int, host_s: float):
+    """Run the steps behind a GPU-side wait longer than the host needs to enqueue them, so that
+    the GPU meets every launch already queued: events recorded around each kernel then time the
+    kernel, not the host's launch latency.  host_s: the host's time for the steps (eager)."""
+    if not hasattr(queued, "rate"):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record()
+        torch.cuda._sleep(1_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        queued.rate = 1_000_000 / max(e0.elapsed_time(e1) * 1e-3, 1e-6)  # sleep cycles per second
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(queued.rate * (1.5 * host_s + 0.005)))
+    for _ in range(steps):
+        run_step()
+    torch.cuda.synchronize()
+
+
+def time_decode(P, torch, cache, qs, outs, w, args, graph: bool = True):
+    """Decode step over every layer: eager step time, the decode kernel's event-timed duration over
+    a second pass of the steps, and the step replayed from a HIP graph (every layer's prep, decode
+    and merge; no host launch overhead between them; eager if capture fails)."""
+    ws = cache.workspace(args.n_splits)
+
+    def step():
+        for layer in range(w.L):
+            cache.decode_attention(layer, qs[layer], outs[layer], n_splits=args.n_splits, ws=ws)
+
+    sec_eager = timed(step, args.steps, args.warmup)       # eager launches, no tracing
+    P.bgtq_profile_enable(w.L * args.steps)
+    queued(torch, step, args.steps, sec_eager * args.steps)
+    n_k, tot_ms, min_ms, max_ms = P.bgtq_profile_read(P.PROF_DECODE)
+    P.bgtq_profile_enable(0)
+    r = {"sec": sec_eager, "sec_eager": sec_eager, "graph_ok": False, "n_k": n_k,
+         "kern_ms": tot_ms / max(n_k, 1), "min_ms": min_ms, "max_ms": max_ms, "step": step, "ws": ws}
+    if graph and not args.eager:
+        try:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            with torch.cuda.graph(g):
+                step()
+            r["sec"] = timed(g.replay, args.steps, args.warmup)
+            r["graph_ok"] = True
+            del g
+        except Exception as e:  # capture unsupported: keep the eager number
+            log(f"[bench] graph capture failed ({e}); reporting eager launches")
+    return r
+
+
+def time_fp16(P, torch, w, qs, outs, args, sec_packed):
+    """The unquantized comparator: the same rows in fp16, decoded by the library's fp16 kernel."""
+    ks, vs = build_fp16(w)
+    ws16 = torch.empty(P.lib.bgtq_fp16_decode_workspace_bytes(w.N, w.B, w.Hq, w.Hkv, args.n_splits),
+                       dtype=torch.uint8, device="cuda")
+
+    def step16():
+        for layer in range(w.L):
+            P.bgtq_fp16_decode_attention(ks[layer], vs[layer], qs[layer], outs[layer], args.n_splits, ws16)
+
+    sec16 = timed(step16, args.steps, args.warmup)
+    P.bgtq_profile_enable(w.L * args.steps)
+    queued(torch, step16, args.steps, sec16 * args.steps)
+    n16, tot16, _, _ = P.bgtq_profile_read(P.PROF_FP16_DECODE)
+    P.bgtq_profile_enable(0)
+    del ks, vs, ws16
+    b16 = w.B * w.Hkv * w.N * 512 + w.B * w.Hq * w.d * 6
+    k16_ms = tot16 / max(n16, 1)
+    mx = w.Hq // w.Hkv >= 4
+    return {"ms_per_step": round(sec16 * 1e3, 4), "value": round(w.L * b16 / sec16 / 1e9, 2), "unit": "GB/s",
+            "kernel_avg_us": round(k16_ms * 1e3, 3),
+            "kernel_GB/s": round(b16 / (k16_ms * 1e-3) / 1e9, 1),
+            "kernel_frac": round(b16 / (k16_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "kernel": "k_decode_fp16_mx" if mx else "k_decode_fp16",
+            "traffic": measured_traffic(w.wid, "k_decode_fp16_mx") if mx else None,
+            "speedup_packed_vs_fp16": round(sec16 / sec_packed, 3)}
+
+
+def per_workload(wid, args, P, torch, synth):
+    """One workload's decode at its own shape.  Every layer of a workload has the same shape, so
+    enough layers are timed for a step to stream more than the 256 MB Infinity Cache (copies of the
+    layer when the workload has fewer); the one-layer 4K workload (279 KB) is timed as it is."""
+    w = synth.WORKLOADS[wid]
+    lb = layer_bytes(w, w.N)
+    if wid != 1:
+        w = synth.reduced(w, L=max(1, int(np.ceil(320e6 / lb))))
+    cache, qs = build_packed(w)
+    outs = [torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda") for _ in range(w.L)]
+    r = time_decode(P, torch, cache, qs, outs, w, args)
+    del cache
+    torch.cuda.empty_cache()
+    kname = decode_kernel_name(w)
+    ach = lb / (r["kern_ms"] * 1e-3) / 1e9
+    e = {"workload": w.name, "layers_timed": w.L, "launch": "hipgraph" if r["graph_ok"] else "eager",
+         "ms_per_step": round(r["sec"] * 1e3, 4), "GB/s": round(w.L * lb / r["sec"] / 1e9, 2),
+         "tokens_heads_per_s": round(w.B * w.N * w.Hq * w.L / r["sec"], 1),
+         "kernel": kname, "kernel_avg_us": round(r["kern_ms"] * 1e3, 3), "bytes_per_launch": lb,
+         "kernel_GB/s": round(ach, 1), "frac": round(ach / PEAK_HBM_GBS, 4),
+         "traffic": measured_traffic(wid, kname), "dtype": arithmetic(w)[0]}
+    if not args.no_fp16:
+        e["fp16_baseline"] = time_fp16(P, torch, w, qs, outs, args, r["sec"])
+    torch.cuda.empty_cache()
+    log(f"[bench] workload {wid}: {kname} {r['kern_ms'] * 1e3:.2f} us per layer ({ach:.0f} GB/s, "
+        f"frac {ach / PEAK_HBM_GBS:.3f}), step {r['sec'] * 1e3:.3f} ms over {w.L} layers")
+    return e
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The oracle (numpy, fp64) decoding a bounded sample: layer 0, the first N_s tokens of every
     (batch, kv head) of the first sequence, all query heads; repeated until ~budget_s seconds."""
@@ -232,6 +353,11 @@ def main():
                     help="affine keys stored under the randomized Hadamard rotation (affine-key workloads)")
     ap.add_argument("--uniform-keys", action="store_true",
                     help="Block-GTQ keys with every block at the average width (the uniform comparator)")
+    ap.add_argument("--decode-path", choices=("auto", "vector"), default="auto",
+                    help="auto: the library's kernels; vector: every product on the vector ALUs (k_decode)")
+    ap.add_argument("--no-vector", action="store_true", help="skip the vector-ALU decode leg of the default run")
+    ap.add_argument("--no-per-workload", action="store_true",
+                    help="skip the other workloads' decode lines of the default run")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -277,37 +403,11 @@ def main():
     P.bgtq_profile_enable(0)
     log(f"[bench] packed cache built in {time.perf_counter() - t0:.1f}s")
     outs = [torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda") for _ in range(w.L)]
-    ws = cache.workspace(args.n_splits)
-
-    def step():
-        for layer in range(w.L):
-            cache.decode_attention(layer, qs[layer], outs[layer], n_splits=args.n_splits, ws=ws)
-
-    sec_eager = timed(step, args.steps, args.warmup)       # eager launches, no tracing
-    # Decode-kernel durations: HIP events recorded around each kernel's own execution.
-    P.bgtq_profile_enable(w.L * args.steps)
-    timed(step, args.steps, 0)
-    n_k, tot_ms, min_ms, max_ms = P.bgtq_profile_read(P.PROF_DECODE)
-    P.bgtq_profile_enable(0)
-    kern_ms = tot_ms / max(n_k, 1)
-    sec = sec_eager
-    # Replay the whole step (every layer's prep + decode + combine) from a HIP graph: no host launch
-    # overhead between the 3*L kernels.  Falls back to eager timing if capture fails.
-    graph_ok = False
-    if not args.eager:
-        try:
-            g = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                step()
-            torch.cuda.current_stream().wait_stream(side)
-            with torch.cuda.graph(g):
-                step()
-            sec = timed(g.replay, args.steps, args.warmup)
-            graph_ok = True
-        except Exception as e:  # capture unsupported: keep the eager number
-            log(f"[bench] graph capture failed ({e}); reporting eager launches")
+    if args.decode_path == "vector":
+        cache.decode_path = P.DECODE_VECTOR
+    r = time_decode(P, torch, cache, qs, outs, w, args)
+    sec, sec_eager, graph_ok, ws = r["sec"], r["sec_eager"], r["graph_ok"], r["ws"]
+    n_k, kern_ms, min_ms, max_ms = r["n_k"], r["kern_ms"], r["min_ms"], r["max_ms"]
     lb = layer_bytes(w, w.N)
     value = w.L * lb / sec / 1e9
     achieved = lb / (kern_ms * 1e-3) / 1e9
@@ -318,21 +418,42 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": arithmetic(w)[0], "arithmetic": arithmetic(w)[1], "data": "synthetic",
+        "vs_baseline": None, "dtype": arithmetic(w, args.decode_path)[0],
+        "arithmetic": arithmetic(w, args.decode_path)[1], "data": "synthetic",
         "config": {"workload": w.name, "layers": w.L, "batch": w.B, "context": w.N, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.d, "k_format": "blockgtq" if w.k_mode == "gtq" else "affine",
                    "k_bits_per_dim": (w.k_budget_units / 64) if w.k_mode == "gtq" else w.k_bits,
                    "v_bits": w.v_bits, "n_recent_fp16": w.n_recent, "activations": w.dtype,
                    "key_widths": "uniform" if args.uniform_keys else "greedy", "key_rotation": args.k_rotation,
-                   "n_splits": args.n_splits or "auto", "layer_copies_cycled": copies},
+                   "n_splits": args.n_splits or "auto", "layer_copies_cycled": copies,
+                   "decode_path": args.decode_path},
         "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "launch": "hipgraph" if graph_ok else "eager", "ms_per_step_eager": round(sec_eager * 1e3, 4),
         "tokens_heads_per_s": round(w.B * w.N * w.Hq * w.L / sec, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.wid),
-                     "kernel": decode_kernel_name(w), "kernel_avg_us": round(kern_ms * 1e3, 3),
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(w.wid, decode_kernel_name(w, args.decode_path)),
+                     "kernel": decode_kernel_name(w, args.decode_path), "kernel_avg_us": round(kern_ms * 1e3, 3),
                      "bytes_per_launch": lb, "launches_timed": n_k},
     }
+    if args.decode_path == "auto" and not args.no_vector and decode_kernel_name(w) != "k_decode":
+        # The same cache and queries with every product on the vector ALUs (no matrix-core
+        # instructions): the kernel the library takes below four query heads per kv head.
+        cache.decode_path = P.DECODE_VECTOR
+        rv = time_decode(P, torch, cache, qs, outs, w, args)
+        cache.decode_path = P.DECODE_AUTO
+        ws = cache.workspace(args.n_splits)
+        av = lb / (rv["kern_ms"] * 1e-3) / 1e9
+        result["vector_alu_decode"] = {
+            "decode_path": "vector", "kernel": "k_decode", "kernel_avg_us": round(rv["kern_ms"] * 1e3, 3),
+            "bytes_per_launch": lb, "kernel_GB/s": round(av, 1), "frac": round(av / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(w.wid, "k_decode"), "launches_timed": rv["n_k"],
+            "ms_per_step": round(rv["sec"] * 1e3, 4), "launch": "hipgraph" if rv["graph_ok"] else "eager",
+            "GB/s": round(w.L * lb / rv["sec"] / 1e9, 2), "dtype": arithmetic(w, "vector")[0],
+            "arithmetic": arithmetic(w, "vector")[1],
+            "matrix_core_speedup": round(rv["kern_ms"] / kern_ms, 3)}
+        log(f"[bench] vector-ALU decode: k_decode {rv['kern_ms'] * 1e3:.2f} us per layer ({av:.0f} GB/s), "
+            f"step {rv['sec'] * 1e3:.3f} ms")
     if nq:
         # write path: every packed (token, kv head) reads its K and V rows and writes its record
         es = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
@@ -413,31 +534,15 @@ def main():
     if not args.no_fp16:
         del cache
         torch.cuda.empty_cache()
-        ks, vs = build_fp16(w)
-        ws16 = torch.empty(P.lib.bgtq_fp16_decode_workspace_bytes(w.N, w.B, w.Hq, w.Hkv, args.n_splits),
-                           dtype=torch.uint8, device="cuda")
-
-        def step16():
-            for layer in range(w.L):
-                P.bgtq_fp16_decode_attention(ks[layer], vs[layer], qs[layer], outs[layer], args.n_splits, ws16)
-
-        sec16 = timed(step16, args.steps, args.warmup)
-        P.bgtq_profile_enable(w.L * args.steps)
-        timed(step16, args.steps, 0)
-        n16, tot16, _, _ = P.bgtq_profile_read(P.PROF_FP16_DECODE)
-        P.bgtq_profile_enable(0)
-        b16 = w.B * w.Hkv * w.N * 512 + w.B * w.Hq * w.d * 6
-        k16_ms = tot16 / max(n16, 1)
-        result["fp16_baseline"] = {
-            "ms_per_step": round(sec16 * 1e3, 4), "value": round(w.L * b16 / sec16 / 1e9, 2), "unit": "GB/s",
-            "kernel_avg_us": round(k16_ms * 1e3, 3),
-            "kernel_GB/s": round(b16 / (k16_ms * 1e-3) / 1e9, 1),
-            "kernel_frac": round(b16 / (k16_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "kernel": "k_decode_fp16_mx" if w.Hq // w.Hkv >= 4 else "k_decode_fp16",
-            "traffic": measured_traffic(w.wid, "k_decode_fp16_mx") if w.Hq // w.Hkv >= 4 else None,
-            "speedup_packed_vs_fp16": round(sec16 / sec, 3)}
-        log(f"[bench] fp16 comparator step {sec16 * 1e3:.3f} ms, speedup {sec16 / sec:.2f}x")
-        del ks, vs
+        result["fp16_baseline"] = time_fp16(P, torch, w, qs, outs, args, sec)
+        log(f"[bench] fp16 comparator step {result['fp16_baseline']['ms_per_step']:.3f} ms, "
+            f"speedup {result['fp16_baseline']['speedup_packed_vs_fp16']:.2f}x")
+    else:
+        del cache
+    del qs, outs
+    torch.cuda.empty_cache()
+    if args.workload == 2 and not args.layers and not args.no_per_workload and args.decode_path == "auto":
+        result["per_workload"] = {str(i): per_workload(i, args, P, torch, synth) for i in (1, 3, 4, 5)}
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w)

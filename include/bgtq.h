@@ -62,6 +62,12 @@ enum {
 #define BGTQ_ENERGY_CHUNK 16   /* calibration tokens per workgroup of bgtq_block_energy */
 #define BGTQ_PLAN_BYTES 512    /* decode plan bytes per (layer, kv head) */
 
+/* Decode kernel family of a cache (bgtq_cache.decode_path). */
+enum {
+    BGTQ_DECODE_AUTO = 0,   /* the library's choice: matrix cores for g >= 4, vector ALUs below */
+    BGTQ_DECODE_VECTOR = 1  /* q·k and P·V on the vector ALUs for every format and head ratio */
+};
+
 /*
  * Packed KV cache descriptor (plain data; the caller fills it and owns every buffer).
  *
@@ -99,6 +105,10 @@ enum {
  *     matrix, fast transform in stages 1, 2, ..., 64, fp32), and decode rotates the query to
  *     H (s * q) / 8 so that the logits are unchanged; the fp16 recent ring keeps rows unrotated.
  *     NULL disables it.  With Block-GTQ keys it is BGTQ_E_UNSUPPORTED.
+ *   decode_path  BGTQ_DECODE_AUTO or BGTQ_DECODE_VECTOR (plain value, not a buffer): which decode
+ *     kernels bgtq_decode_attention runs.  Both compute the same attention to the same tolerance;
+ *     VECTOR keeps every product on the vector ALUs (no matrix-core instructions), for comparison
+ *     and measurement.  Other values: BGTQ_E_INVALID from the decode calls.
  * Host state:
  *   n_tokens  int64 [L][B] host array: tokens appended so far per (layer, sequence) (packed +
  *     recent).  bgtq_quantize_append advances it on success only.
@@ -133,6 +143,7 @@ typedef struct bgtq_cache {
     const uint8_t *k_rot;
     int32_t *n_hp;
     void *plan;
+    int32_t decode_path;
 } bgtq_cache;
 
 /* Thread-local text describing the last non-OK status of this thread ("" if none). */

@@ -15,6 +15,7 @@ V_CODEBOOK, V_AFFINE = 0, 1
 (BUF_K_CODES, BUF_V_CODES, BUF_K_SCALE, BUF_K_ZERO, BUF_V_SCALE, BUF_V_ZERO, BUF_RECENT_K,
  BUF_RECENT_V, BUF_META, BUF_PLAN) = range(10)
 PLAN_BYTES = 512  # BGTQ_PLAN_BYTES
+DECODE_AUTO, DECODE_VECTOR = 0, 1  # bgtq_cache.decode_path
 MAX_BATCH = 64
 ENERGY_CHUNK = 16  # BGTQ_ENERGY_CHUNK: calibration tokens per workgroup of bgtq_block_energy
 
@@ -41,7 +42,7 @@ class CacheDesc(C.Structure):
                 ("v_scale", C.c_void_p), ("v_zero", C.c_void_p), ("recent_k", C.c_void_p), ("recent_v", C.c_void_p),
                 ("bits", C.c_void_p), ("sigma", C.c_void_p), ("inv_sigma", C.c_void_p),
                 ("n_tokens", C.POINTER(C.c_int64)), ("k_rot", C.c_void_p),
-                ("n_hp", C.POINTER(C.c_int32)), ("plan", C.c_void_p)]
+                ("n_hp", C.POINTER(C.c_int32)), ("plan", C.c_void_p), ("decode_path", C.c_int32)]
 
 
 def bind(path: str, optional=()):

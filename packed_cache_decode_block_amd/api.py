@@ -123,9 +123,11 @@ class PackedCache:
 
     def __init__(self, *, L, B, Hq, Hkv, n_cap, k_mode=_lib.K_BLOCKGTQ, budget_units=128, k_bits=4, k_group=32,
                  v_mode=_lib.V_CODEBOOK, v_bits=2, n_recent=0, k_rotation=False, logquant_w=None, device="cuda",
-                 zero=True):
+                 zero=True, decode_path=_lib.DECODE_AUTO):
         """logquant_w: base window W of LogQuant's log-based filter; the recent buffers then hold the
-        3W-row high-precision store (n_recent = 3W) and appends go through logquant_append."""
+        3W-row high-precision store (n_recent = 3W) and appends go through logquant_append.
+        decode_path: DECODE_AUTO (the library's kernel choice) or DECODE_VECTOR (every product on the
+        vector ALUs); also settable later through the attribute of the same name."""
         torch = _torch()
         if logquant_w is not None:
             n_recent = 3 * int(logquant_w)
@@ -135,6 +137,7 @@ class PackedCache:
         d.n_cap = n_cap
         d.k_mode, d.budget_units, d.k_bits, d.k_group = k_mode, budget_units, k_bits, k_group
         d.v_mode, d.v_bits, d.n_recent = v_mode, v_bits, n_recent
+        d.decode_path = decode_path
         self.n_tokens = np.zeros((L, B), np.int64)
         d.n_tokens = self.n_tokens.ctypes.data_as(C.POINTER(C.c_int64))
         self.n_hp = self.hp_pos = None
@@ -238,6 +241,14 @@ class PackedCache:
         check(lib.bgtq_decode_step(C.byref(self.desc), layer, _ptr(k), _ptr(v), _ptr(q), _dtype_code(q), k.shape[1],
                                    strides, _ptr(out), _ptr(ws), ws.numel(), n_splits, _stream(stream)))
         return out
+
+    @property
+    def decode_path(self) -> int:
+        return self.desc.decode_path
+
+    @decode_path.setter
+    def decode_path(self, path: int):
+        self.desc.decode_path = int(path)
 
     def workspace_bytes(self, n_splits: int = 0) -> int:
         return check(lib.bgtq_decode_workspace_bytes(C.byref(self.desc), n_splits))

@@ -1,19 +1,31 @@
-// Packed-cache decode over Block-GTQ keys on the matrix cores, one workgroup of eight waves per
-// compute unit ("RoPE-Aware Bit Allocation for KV-Cache Quantization": abstract; review §1
-// Packed-Cache, Figure 2: attention computed straight from the packed codes).
+// Packed-cache decode over Block-GTQ keys on the matrix cores, one workgroup per compute unit
+// ("RoPE-Aware Bit Allocation for KV-Cache Quantization": abstract; review §1 Packed-Cache,
+// Figure 2: attention computed straight from the packed codes).
 //
 // The g query heads of a kv head share every dequantized key and value, so per 64-token tile q·K^T
 // is a (g x 128) x (128 x 64) product and P·V a (g x 64) x (64 x 128) product, both on
-// v_mfma_f32_16x16x32_f16; the vector ALUs unpack codes and run the online softmax.  Operand
-// assembly is the one of the bgtq_device.h helpers: key records staged in LDS, per-column 64-bit
-// windows, pair tables for widths up to 5 and fp16 coordinate tables above; values looked up from
-// the lane-stream fields through a replicated pair table.
+// v_mfma_f32_16x16x32_f16; the vector ALUs unpack codes and run the online softmax.
+//  * A = Q' (16 rows x 32 K): row 4u + e is head 2u + e/2, with e even the fp16 high part and e odd
+//    the fp16 low part of q' = q * sigma * log2(e)/sqrt(d) (hi + lo carries ~22 bits).  Centroids
+//    are fp16 values exactly, so the products lose nothing and the matrix cores sum in fp32.
+//  * B = K^ (32 K x 16 tokens): lane (token j, row u) builds its own operand: K index 8u + e is
+//    coordinate e % 2 of stream slot 16 ks + 8 (e / 4) + 2u + (e / 2) % 2, so a lane row reads two
+//    adjacent slots of the record from one 64-bit window of the staged record (per token group),
+//    shifts it and ANDs/ORs the field into a table address (pair tables for widths <= 5, fp16
+//    coordinate tables for wider columns).  No transposes.
+//  * C (16 x 16 tokens): lane (token 16g + r, row group u) holds heads 2u, 2u + 1 as (hi, lo).
+//  * P·V: A = V^T (16 dims x 32 tokens) straight from the lane-stream value fields through a
+//    replicated pair table, B = W (32 tokens x 16 heads) through LDS in pair order (t, t + 32);
+//    O^T accumulates per 16-dim block.
+//  * Online softmax with the exact running max per head (a wave-uniform branch raises it), so the
+//    largest weight of a split is fp16(scale) exactly, whatever the split boundaries.
 //
 // What depends only on the widths of a (layer, kv head) — the block order, the column descriptors
 // of the operand assembly and the per-block operand position of the query — is computed once by
 // k_plan into a small plan record; every workgroup of every decode loads it instead of rebuilding
-// it.  One workgroup per compute unit merges its eight waves into one (o, m, l) partial per query
-// head, so a split-K launch writes one partial per compute unit and kv head.
+// it.  One workgroup per compute unit (sixteen waves with one tile each, or eight waves looping over
+// their tiles) merges its waves into one (o, m, l) partial per query head, so a split-K launch
+// writes one partial per compute unit and kv head.
 #include <hip/hip_ext.h>
 
 #include "bgtq_device.h"
@@ -64,11 +76,17 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* bits, uint8_t* plan)
     }
 }
 
+// Query operand image (LDS, u32x4 [4 k-steps][64 lanes]): q' = q * sigma * log2(e)/sqrt(d) of the
+// block in stream slot r (its rank), split into an fp16 high part and an fp16 low part, sits at
+// k-step r / 16, lane row (r % 8) / 2, element pair 2 ((r % 16) / 8) + r % 2 of the operand lanes
+// of its head (column 2h: high part, 2h + 1: low part).  Slots past the nonzero blocks, and the
+// columns of absent heads, hold zeros.
+//
 // Query operands from the plan, one (head, block) item per thread (threads 0 .. 511: head hh =
-// thread / 64, block = thread % 64).  The item's coordinates q' = q * sigma * log2(e)/sqrt(d) go to
-// stream slot rank of the operand image as fp16 high and low parts (rows 2hh and 2hh + 1); the item
-// also clears its head's rows of slot `block` when that slot is past the nonzero blocks, and heads
-// beyond G clear their rows of every slot.  Layout of mx_prep_q.
+// thread / 64, block = thread % 64).  The item's coordinates go to stream slot rank of the image as
+// fp16 high and low parts (rows 2hh and 2hh + 1); the item also clears its head's rows of slot
+// `block` when that slot is past the nonzero blocks, and heads beyond G clear their rows of every
+// slot.
 struct QItem {
     uint32_t r0, r1;  // the item's two coordinates (fp32 bits, or the packed 16-bit pair in r0)
     float sg;         // sigma of the block
@@ -132,7 +150,7 @@ __device__ void gtq_q_item_store(const QItem& it, int dtype, int nnz, uint8_t* q
 }
 
 // Query operands from the plan (wave 0, lane = RoPE block): q' = q * sigma * log2(e)/sqrt(d) of
-// block i goes to stream slot rank_i of the operand image (layout of mx_prep_q); slots past the
+// block i goes to stream slot rank_i of the operand image (layout above); slots past the
 // nonzero blocks get zeros.
 template <int G>
 __device__ void gtq_prep_q(const PrepIn<G>& in, int rank, int nnz, int lane, uint8_t* qa) {
@@ -170,63 +188,6 @@ __device__ void gtq_prep_q(const PrepIn<G>& in, int rank, int nnz, int lane, uin
     };
     if (rank != 0xFF) put(rank, false);
     if (lane >= nnz) put(lane, true);
-}
-
-// One k-step of q·k: the eight windows of the lane row (two column pairs x four token groups) as
-// one batch of ds_read2 (each lands in a register pair), then token group by token group the four
-// slot lookups and one product, so that only one group's operands are live.  Column modes
-// CA0/CB0/CA1/CB1 as in col_pairs_both; dk holds the four column descriptors of this lane row, qk
-// the query operand of the k-step.
-template <bool CA0, bool CB0, bool CA1, bool CB1, bool FIRST>
-__device__ __forceinline__ void kstep_lean(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t dk, uint32_t lb,
-                                           const half8_t qk) {
-    const uint32_t ad0 = (dk[0] >> 17) + lb, ad1 = (dk[2] >> 17) + lb;
-    const uint32_t m0 = CA0 ? bfm<1>(dk[0] >> 12) : bfm<2>(dk[0] >> 12);
-    const uint32_t m1 = CB0 ? bfm<1>(dk[1] >> 12) : bfm<2>(dk[1] >> 12);
-    const uint32_t m2 = CA1 ? bfm<1>(dk[2] >> 12) : bfm<2>(dk[2] >> 12);
-    const uint32_t m3 = CB1 ? bfm<1>(dk[3] >> 12) : bfm<2>(dk[3] >> 12);
-    const uint32_t b0 = m0 + (CA0 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
-    const uint32_t b1 = m1 + (CB0 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
-    const uint32_t b2 = m2 + (CA1 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
-    const uint32_t b3 = m3 + (CB1 ? BGTQ_CB_MX_COORD_BIAS : BGTQ_CB_MX_PAIR_BIAS);
-    static_assert(BGTQ_KST_ROW_BYTES == 320, "window read offsets assume 80-dword stage rows");
-    uint64_t wa[4], wb[4];
-    asm volatile("ds_read2_b32 %0, %8 offset1:80\n\t"
-                 "ds_read2_b32 %1, %8 offset0:16 offset1:96\n\t"
-                 "ds_read2_b32 %2, %8 offset0:32 offset1:112\n\t"
-                 "ds_read2_b32 %3, %8 offset0:48 offset1:128\n\t"
-                 "ds_read2_b32 %4, %9 offset1:80\n\t"
-                 "ds_read2_b32 %5, %9 offset0:16 offset1:96\n\t"
-                 "ds_read2_b32 %6, %9 offset0:32 offset1:112\n\t"
-                 "ds_read2_b32 %7, %9 offset0:48 offset1:128\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(wa[0]), "=&v"(wa[1]), "=&v"(wa[2]), "=&v"(wa[3]),
-                   "=&v"(wb[0]), "=&v"(wb[1]), "=&v"(wb[2]), "=&v"(wb[3])
-                 : "v"((uint32_t)(uintptr_t)(lds + ad0)), "v"((uint32_t)(uintptr_t)(lds + ad1))
-                 : "memory");
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const uint32_t p0 = CA0 ? slot_coord(lds, wa[g], dk[0], m0, b0) : slot_pair(lds, wa[g], dk[0], m0, b0);
-        const uint32_t p1 = CB0 ? slot_coord(lds, wa[g], dk[1], m1, b1) : slot_pair(lds, wa[g], dk[1], m1, b1);
-        const uint32_t p2 = CA1 ? slot_coord(lds, wb[g], dk[2], m2, b2) : slot_pair(lds, wb[g], dk[2], m2, b2);
-        const uint32_t p3 = CB1 ? slot_coord(lds, wb[g], dk[3], m3, b3) : slot_pair(lds, wb[g], dk[3], m3, b3);
-        c[g] = mfma16(qk, as_h8(p0, p1, p2, p3), FIRST ? f32x4_t{0.f, 0.f, 0.f, 0.f} : c[g]);
-    }
-}
-
-// k-step KS; ncc (wave-uniform) = number of coordinate columns of the whole record.
-template <int KS>
-__device__ __forceinline__ void kstep_lean_any(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
-                                               const u32x4_t* sd, uint32_t lb, int ncc) {
-    const u32x4_t dk = sd[KS];
-    const half8_t qk = __builtin_bit_cast(half8_t, qa[KS * 64 + lane]);
-    constexpr bool F = KS == 0;
-    const int a = ncc - 4 * KS;
-    if (a <= 0) kstep_lean<false, false, false, false, F>(c, lds, dk, lb, qk);
-    else if (a == 1) kstep_lean<true, false, false, false, F>(c, lds, dk, lb, qk);
-    else if (a == 2) kstep_lean<true, true, false, false, F>(c, lds, dk, lb, qk);
-    else if (a == 3) kstep_lean<true, true, true, false, F>(c, lds, dk, lb, qk);
-    else kstep_lean<true, true, true, true, F>(c, lds, dk, lb, qk);
 }
 
 // Workgroup barrier that orders LDS only: the waves' LDS writes complete first, global loads still
@@ -370,12 +331,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_gtq(const DecodeArgs a) {
         for (int c = 0; c < VB; ++c) dst[c] = vt[c * 64 + lane];
     };
     // Unconditional (branch-free prologue); a wave without tiles reads a tile inside the allocation
-    // and never uses it.  The small loads above go out first (the scheduling fence keeps the tile
-    // loads behind them), so they do not queue behind every compute unit's tile burst.
+    // and never uses it.  With eight waves the first keys go out right behind the small loads above
+    // (the scheduling fence keeps them behind); with sixteen they wait for the barrier below.
     const int64_t t_first = t_lo + wave < t_hi ? t_lo + wave : (t_lo < a.n_tiles ? t_lo : 0);
     __builtin_amdgcn_sched_barrier(0);
-    fetch_k(t_first);
-    if constexpr (NW > 8) fetch_v(vn, t_first);
+    if constexpr (NW <= 8) fetch_k(t_first);
 
 #pragma unroll
     for (int k = 0; k < (TAB4 + NT - 1) / NT; ++k)
@@ -400,11 +360,27 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_gtq(const DecodeArgs a) {
         gtq_prep_q<G>(pin, prank, nnz, lane, lds + LD::QA);
     }
     lds_barrier();  // tables, descriptors and query operands are in place
+    if constexpr (NW > 8) {
+        // One tile per wave, issued in four groups of one wave per SIMD, a barrier between groups.
+        // Each compute unit's requests then reach memory group by group, so the first group's
+        // tiles land first and are worked on while the later groups' tiles stream in; issued all
+        // at once, every wave's last bytes would arrive at the end of the burst.  The small loads
+        // were waited for before the barrier above, so no wave's prologue queues behind the
+        // tile bursts of the whole chip.
+        const int grp = wave >> 2;
+        for (int k = 0; k < grp; ++k) asm volatile("s_barrier" ::: "memory");
+        fetch_k(t_first);
+        fetch_v(vn, t_first);
+        for (int k = grp; k < NW / 4 - 1; ++k) asm volatile("s_barrier" ::: "memory");
+    }
 
     const int nnz_pad = (int)__builtin_amdgcn_readfirstlane(s_nnz[0]);  // nonzero slots rounded up to 4
     const int nks = (nnz_pad + 15) >> 4;
     const int ncc = (int)__builtin_amdgcn_readfirstlane(s_nnz[1]);      // coordinate columns
-    const u32x4_t* sd = (const u32x4_t*)(lds + LD::DESC) + 4 * row;  // this lane row's descriptors
+    // This lane row's column descriptors of the four k-steps, read while the tile data is in flight.
+    u32x4_t dks[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) dks[ks] = ((const u32x4_t*)(lds + LD::DESC))[4 * row + ks];
     if constexpr (NW <= 8) fetch_v(vn, t_first);
 
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, zs[2] = {0.f, 0.f};
@@ -452,17 +428,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_gtq(const DecodeArgs a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) c[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        if constexpr (NW > 8) {
-            if (nks > 0) kstep_lean_any<0>(c, lds, s_qa, lane, sd, lb, ncc);
-            if (nks > 1) kstep_lean_any<1>(c, lds, s_qa, lane, sd, lb, ncc);
-            if (nks > 2) kstep_lean_any<2>(c, lds, s_qa, lane, sd, lb, ncc);
-            if (nks > 3) kstep_lean_any<3>(c, lds, s_qa, lane, sd, lb, ncc);
-        } else {
-            if (nks > 0) mx_kstep_any<0>(c, lds, s_qa, lane, sd, lb, ncc);
-            if (nks > 1) mx_kstep_any<1>(c, lds, s_qa, lane, sd, lb, ncc);
-            if (nks > 2) mx_kstep_any<2>(c, lds, s_qa, lane, sd, lb, ncc);
-            if (nks > 3) mx_kstep_any<3>(c, lds, s_qa, lane, sd, lb, ncc);
-        }
+        if (nks > 0) mx_kstep_any<0>(c, lds, s_qa, lane, dks[0], lb, ncc);
+        if (nks > 1) mx_kstep_any<1>(c, lds, s_qa, lane, dks[1], lb, ncc);
+        if (nks > 2) mx_kstep_any<2>(c, lds, s_qa, lane, dks[2], lb, ncc);
+        if (nks > 3) mx_kstep_any<3>(c, lds, s_qa, lane, dks[3], lb, ncc);
 
         // softmax over the tile: lane holds tokens 16g + col, heads 2row, 2row + 1
         float sk[4], sv[4], sz[4] = {0.f, 0.f, 0.f, 0.f};

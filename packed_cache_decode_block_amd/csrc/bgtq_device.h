@@ -256,27 +256,27 @@ __device__ __forceinline__ void col_pairs_both(uint32_t (&P)[16], const uint8_t*
         P[4 * g + 2] = CA1 ? slot_coord(lds, wb[g], dk[2], m2, b2) : slot_pair(lds, wb[g], dk[2], m2, b2);
         P[4 * g + 3] = CB1 ? slot_coord(lds, wb[g], dk[3], m3, b3) : slot_pair(lds, wb[g], dk[3], m3, b3);
     }
+    // Every lookup address first, then every lookup, then the halves joined: one LDS round trip for
+    // the k-step's sixteen operands instead of one per token group.
+    __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 32, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
 }
 
-// k-step KS with its first A columns read per coordinate and the rest as pairs: the operands.
-template <int KS, int A>
-__device__ __forceinline__ void mx_kops(uint32_t (&P)[16], const uint8_t* lds, const u32x4_t* sd, uint32_t lb) {
-    const u32x4_t dk = sd[KS];
-    col_pairs_both<(A > 0), (A > 1), (A > 2), (A > 3)>(P, lds, dk, lb);
-}
-
-// k-step KS of a tile; ncc (wave-uniform) = number of coordinate columns of the whole record.  The
-// column modes only change how the operands are built; the products sit after the branches.
+// k-step KS of a tile; dk = the lane row's four column descriptors of this k-step, ncc
+// (wave-uniform) = number of coordinate columns of the whole record (the first ncc columns are
+// read per coordinate, the rest as pairs).  The column modes only change how the operands are
+// built; the products sit after the branches.
 template <int KS>
 __device__ __forceinline__ void mx_kstep_any(f32x4_t (&c)[4], const uint8_t* lds, const u32x4_t* qa, int lane,
-                                             const u32x4_t* sd, uint32_t lb, int ncc) {
+                                             const u32x4_t dk, uint32_t lb, int ncc) {
     uint32_t P[16];
     const int a = ncc - 4 * KS;
-    if (a <= 0) mx_kops<KS, 0>(P, lds, sd, lb);
-    else if (a == 1) mx_kops<KS, 1>(P, lds, sd, lb);
-    else if (a == 2) mx_kops<KS, 2>(P, lds, sd, lb);
-    else if (a == 3) mx_kops<KS, 3>(P, lds, sd, lb);
-    else mx_kops<KS, 4>(P, lds, sd, lb);
+    if (a <= 0) col_pairs_both<false, false, false, false>(P, lds, dk, lb);
+    else if (a == 1) col_pairs_both<true, false, false, false>(P, lds, dk, lb);
+    else if (a == 2) col_pairs_both<true, true, false, false>(P, lds, dk, lb);
+    else if (a == 3) col_pairs_both<true, true, true, false>(P, lds, dk, lb);
+    else col_pairs_both<true, true, true, true>(P, lds, dk, lb);
     const half8_t q = __builtin_bit_cast(half8_t, qa[KS * 64 + lane]);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -363,79 +363,8 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
-// Query operands of the matrix-core decode, written by one wave (lane = RoPE block): q' = q *
-// sigma * log2(e)/sqrt(d) of block i (stream slot r = its rank) goes, split into an fp16 high part
-// and an fp16 low part, to k-step r / 16, lane row (r % 8) / 2, element pair 2 ((r % 16) / 8) +
-// r % 2 of the operand lanes of its heads (column 2h: high part, 2h + 1: low part).  Slots past
-// the nonzero blocks, and the columns of absent heads, get zeros.  s_nnz[0] = nonzero blocks
-// rounded up to 4.
-template <int G>
-__device__ void mx_prep_q(const PrepIn<G>& in, int w, int lane, uint8_t* qa, uint32_t* s_nnz) {
-    float q0[G], q1[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        if (in.dtype == BGTQ_F32) {
-            q0[hh] = __builtin_bit_cast(float, in.r0[hh]);
-            q1[hh] = __builtin_bit_cast(float, in.r1[hh]);
-        } else if (in.dtype == BGTQ_F16) {
-            q0[hh] = h2f(in.r0[hh] & 0xFFFFu);
-            q1[hh] = h2f(in.r0[hh] >> 16);
-        } else {
-            q0[hh] = bf2f(in.r0[hh] & 0xFFFFu);
-            q1[hh] = bf2f(in.r0[hh] >> 16);
-        }
-        q0[hh] = q0[hh] * kLog2eOverSqrtD * in.sg;
-        q1[hh] = q1[hh] * kLog2eOverSqrtD * in.sg;
-    }
-    int rank, pos, nnz;
-    block_order(w, lane, rank, pos, nnz);
-    auto put = [&](int r, bool zero) {
-        const int ks = r >> 4, rr = r & 15, urow = (rr >> 1) & 3, mpair = 2 * (rr >> 3) + (rr & 1);
-        uint8_t* base = qa + (size_t)(ks * 64 + 16 * urow) * 16 + 4 * mpair;
-#pragma unroll
-        for (int hh = 0; hh < 8; ++hh) {
-            uint32_t hi2 = 0u, lo2 = 0u;
-            if (hh < G && !zero) {
-                const _Float16 h0 = (_Float16)q0[hh], h1 = (_Float16)q1[hh];
-                const _Float16 l0 = (_Float16)(q0[hh] - (float)h0), l1 = (_Float16)(q1[hh] - (float)h1);
-                hi2 = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                lo2 = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
-            }
-            *(uint32_t*)(base + (2 * hh) * 16) = hi2;
-            *(uint32_t*)(base + (2 * hh + 1) * 16) = lo2;
-        }
-    };
-    if (w > 0) put(rank, false);
-    if (lane >= nnz) put(lane, true);
-    if (lane == 0) s_nnz[0] = (uint32_t)((nnz + 3) & ~3);
-}
-
-// LDS arena of the matrix-core decode (byte offsets).  Loop-time regions: tables (at offset 0,
-// the arena being 8192-aligned, so table offsets are LDS addresses), column descriptors, value
-// centroid pairs, query operands, weight exchange, softmax rescale factors, and per wave the stage
-// of the tile in flight (K record rows -1 .. R at BGTQ_KST_ROW_BYTES stride, scales).  The
-// prologue's block order and the epilogue records alias the stages.
 constexpr int a16(int x) { return (x + 15) & ~15; }
 constexpr int cmax(int x, int y) { return x > y ? x : y; }
-template <int G, int R, int VB> struct MxLds {
-    static constexpr int TAB = 0;                                     // BGTQ_CB_MX_BYTES
-    static constexpr int DESC = a16(TAB + BGTQ_CB_MX_BYTES);          // u32 [4 lane rows][16 columns]
-    static constexpr int VLUT = DESC + 64 * 4;                        // u32 [4^VB][copies]
-    static constexpr int QA = a16(VLUT + VLutGeom<VB>::BYTES);        // u32x4 [4 k-steps][64 lanes]
-    static constexpr int WX = QA + 4 * 64 * 16;                       // u32 [4 waves][16 heads][32 pairs]
-    static constexpr int ALPHA = WX + 4 * 16 * 32 * 4;                // f32 [4 waves][16]
-    static constexpr int NNZ = ALPHA + 4 * 16 * 4;                    // u32 [4]: padded nonzero slots, coordinate columns
-    static constexpr int KST = a16(NNZ + 16);                         // per wave: R + 2 rows
-    static constexpr int KST_W = (R + 2) * BGTQ_KST_ROW_BYTES;
-    static constexpr int SST = KST + 4 * KST_W;                       // per wave: K scales, V scales, V zeros
-    static constexpr int SST_W = 3 * 64 * 2;
-    static constexpr int QP = KST;                                    // prologue: i32 [2][64] block order
-    static constexpr int RED = KST;                                   // epilogue: f32 [4 G PART + 4 G]
-    static constexpr int SIZE = cmax(cmax(SST + 4 * SST_W, QP + 512), RED + 4 * (4 * G * PART + 4 * G));
-};
-
-// 3-bit values (the headline K3V3 shapes) take two resident workgroups per CU and the register
-// room that buys (both column pairs' windows of a k-step in flight); the others three.
 
 // Launch with the armed event pair, if any (consumed), else plainly.
 template <typename K, typename A>

@@ -121,7 +121,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Block-GTQ keys with 4 or 8 query heads per kv head take the plan-driven matrix-core decode, one
 // workgroup per compute unit.
-bool uses_gtq_kernel(const bgtq_cache* c, int G) { return c->k_mode == BGTQ_K_BLOCKGTQ && G >= 4; }
+bool vector_only(const bgtq_cache* c) { return c->decode_path == BGTQ_DECODE_VECTOR; }
+bool uses_gtq_kernel(const bgtq_cache* c, int G) { return c->k_mode == BGTQ_K_BLOCKGTQ && G >= 4 && !vector_only(c); }
 
 // The library's split count for a context of max_tiles tiles per (batch, kv head).  Block-GTQ at
 // g >= 4: one tile per wave of a sixteen-wave workgroup when one round of workgroups covers the
@@ -134,7 +135,7 @@ int auto_splits(const bgtq_cache* c, int G, int64_t max_tiles, int bh) {
         if (one * bh <= n_cu) return (int)std::max<int64_t>(one, 1);
         return default_splits(max_tiles, bh, n_cu, 1, bgtq::kGtqWavesLoop);
     }
-    return default_splits(max_tiles, bh, n_cu, bgtq::decode_wgs_per_cu(c->k_mode, G, c->v_bits, c->k_group));
+    return default_splits(max_tiles, bh, n_cu, bgtq::decode_wgs_per_cu(c->k_mode, G, c->v_bits, c->k_group, vector_only(c)));
 }
 
 // Event pairs around main-kernel launches (tracing aid, see bgtq_profile_enable).
@@ -740,6 +741,8 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
     if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale) return fail(BGTQ_E_INVALID, "NULL cache buffer");
     if (c->k_mode == BGTQ_K_BLOCKGTQ && (!c->bits || !c->sigma))
         return fail(BGTQ_E_INVALID, "NULL key metadata");
+    if (c->decode_path != BGTQ_DECODE_AUTO && c->decode_path != BGTQ_DECODE_VECTOR)
+        return fail(BGTQ_E_INVALID, "decode_path %d is neither BGTQ_DECODE_AUTO nor BGTQ_DECODE_VECTOR", c->decode_path);
     if (uses_gtq_kernel(c, g.G) && !c->plan)
         return fail(BGTQ_E_INVALID, "NULL decode plan (Block-GTQ keys need bgtq_prepare_metadata)");
     if (c->k_mode == BGTQ_K_AFFINE && !c->k_zero) return fail(BGTQ_E_INVALID, "affine keys need k_zero");
@@ -836,7 +839,7 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
     {
         ProfScope ps(BGTQ_PROF_DECODE, s);
         e = uses_gtq_kernel(c, g.G) ? bgtq::launch_decode_gtq(a, g.B, g.R, c->v_bits, s)
-                                    : bgtq::launch_decode(a, g.B, c->k_mode, g.R, c->v_bits, s);
+                                    : bgtq::launch_decode(a, g.B, c->k_mode, g.R, c->v_bits, vector_only(c), s);
     }
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     if (c->n_recent > 0) {

@@ -144,7 +144,7 @@ struct PermuteArgs {
 // Launchers (bgtq_kernels.hip; launch_permute in bgtq_logquant.hip).  Return hipSuccess or the
 // launch error.
 hipError_t launch_permute(const PermuteArgs& a, int B, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, bool vector_only, hipStream_t s);
 // Block-GTQ keys at g = 4 or 8 (bgtq_decode_gtq.hip): one workgroup of kGtqWaves waves per split.
 hipError_t launch_decode_gtq(const DecodeArgs& a, int B, int R, int v_bits, hipStream_t s);
 hipError_t launch_plan(const uint8_t* bits, uint8_t* plan, int Hkv, hipStream_t s);
@@ -164,7 +164,7 @@ bool decode_supported(int k_mode, int R, int k_bits, int k_group, int v_bits, in
 // `start` and `stop` around the kernel itself (hipExtLaunchKernelGGL); disarm drops an unused pair.
 void arm_launch_events(hipEvent_t start, hipEvent_t stop);
 void disarm_launch_events();
-int decode_wgs_per_cu(int k_mode, int G, int v_bits, int k_group);  // resident decode workgroups per CU the split heuristic aims for
+int decode_wgs_per_cu(int k_mode, int G, int v_bits, int k_group, bool vector_only);  // resident decode workgroups per CU the split heuristic aims for
 // Decode into a workspace the caller did not size (bgtq_decode_attention_noalloc): with
 // n_splits == 0 the library's split choice is capped so that the partials fit ws_bytes; an explicit
 // n_splits must fit.  Same validation, kernels and error reporting as bgtq_decode_attention.

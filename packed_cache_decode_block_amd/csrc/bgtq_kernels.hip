@@ -6,17 +6,19 @@
 // "Quantize What Counts" summary (Results: group-size sensitivity); the fp16 recent ring and the
 // order-free concatenation follow the "LogQuant" summary (Method 2 and Method 4).
 //
-// Two decode kernels, both one workgroup = 4 waves = one split of one (batch, kv head), each
-// emitting one (o, m, l) partial per query head that k_combine merges across splits:
-//  * k_decode_mx (Block-GTQ keys, g >= 4 query heads per kv head): q·K^T and P·V of each 64-token
-//    tile run on the matrix cores (v_mfma_f32_16x16x32_f16); the vector ALUs only unpack codes and
-//    run the online softmax.  Its design notes sit next to it below.
-//  * k_decode (g <= 2, or affine keys): lane = token.  The tile's K records are staged dword-major
-//    in LDS; each nonzero RoPE block (sorted by width) is one slot: a 64-bit LDS window, alignbit,
-//    two bit-field extracts, two centroid reads from an LDS table, then 2g FMAs whose query
-//    operand is broadcast from VGPRs with DPP.  P·V: the 2*v_bits-bit pair field indexes an LDS
-//    table of fp16 centroid pairs and v_dot2_f32_f16 accumulates w(t, t+1)·c(t, t+1) in fp32,
-//    with w = p * scale rounded to fp16 (as flash attention rounds P before P·V).
+// Decode kernels here, each one workgroup = 4 waves = one split of one (batch, kv head), emitting
+// one (o, m, l) partial per query head that k_combine merges across splits:
+//  * k_decode (vector ALUs only; every format and head ratio): lane = token.  The tile's K records
+//    are staged dword-major in LDS; each nonzero RoPE block (sorted by width) is one slot: a 64-bit
+//    LDS window, alignbit, two bit-field extracts, two centroid reads from an LDS table, then 2g
+//    FMAs whose query operand is broadcast from VGPRs with DPP.  P·V: the 2*v_bits-bit pair field
+//    indexes an LDS table of fp16 centroid pairs and v_dot2_f32_f16 accumulates
+//    w(t, t+1)·c(t, t+1) in fp32, with w = p * scale rounded to fp16 (as flash attention rounds P
+//    before P·V).  The library takes it for g <= 2, and for any g when a cache asks for the
+//    vector path.
+//  * k_decode_mxa (affine keys, g >= 4): q·k and P·V on the matrix cores.
+//  * k_decode_fp16 / k_decode_fp16_mx: fp16 rows (the unquantized comparator and the recent ring).
+// Block-GTQ keys with g >= 4 take the matrix-core kernel of bgtq_decode_gtq.hip.
 // Both use an online softmax in base 2 with the exact running maximum per head.
 #include "bgtq_internal.h"
 
@@ -706,325 +708,6 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
 }
 
 
-// ---------------------------------------------------------------------------------------------
-// Matrix-core decode for g >= 4 query heads per kv head.  The g heads share every dequantized key
-// and value, so per 64-token tile q·K^T is a (g x 128) x (128 x 64) product and P·V a
-// (g x 64) x (64 x 128) product: v_mfma_f32_16x16x32_f16 takes both and the vector ALUs only
-// unpack codes and run the softmax.
-//  * A = Q' (16 rows x 32 K): row 4u + e is head 2u + e/2, with e even the fp16 high part and e odd
-//    the fp16 low part of q' = q * sigma * log2(e)/sqrt(d) (hi + lo carries ~22 bits).  Centroids
-//    are fp16 values exactly, so the products lose nothing and the MFMA sums in fp32.
-//  * B = K^ (32 K x 16 tokens): lane (token j, row u) builds its own operand: K index 8u + e is
-//    coordinate e % 2 of stream slot 16 ks + 8 (e / 4) + 2u + (e / 2) % 2, so a lane row reads two
-//    adjacent slots of the record from one 64-bit window of the staged record (per token group),
-//    shifts it and ANDs/ORs the field into a table address (pair tables for widths <= 5, fp16
-//    coordinate tables for wider columns).  The one-dword slot descriptors are built once per
-//    workgroup; no transposes.
-//  * C (16 x 16 tokens): lane (token 16g + r, row group u) holds heads 2u, 2u + 1 as (hi, lo).
-//  * P·V: A = V^T (16 dims x 32 tokens) straight from the lane-stream value fields, B = W (32 tokens
-//    x 16 heads) through LDS in pair order (t, t + 32); O^T accumulates per 16-dim block.
-//  * online softmax with the exact running max per head (a wave-uniform branch raises it), so the
-//    largest weight of a split is fp16(scale) exactly, whatever the split boundaries.
-
-
-template <int VB> constexpr int mx_wgs_per_cu() { return VB == 3 ? 2 : 3; }
-
-template <int G, int R, int VB>
-__global__ __launch_bounds__(256, mx_wgs_per_cu<VB>()) void k_decode_mx(const DecodeArgs a) {
-    static_assert(G == 4 || G == 8, "matrix-core decode serves 4 or 8 query heads per kv head");
-    static_assert(R % 4 == 0, "K records are staged in 16-byte chunks");
-    using LD = MxLds<G, R, VB>;
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int row = lane >> 4, col = lane & 15;
-    __shared__ __attribute__((aligned(8192))) uint8_t lds[LD::SIZE];
-    uint32_t* s_vlut = (uint32_t*)(lds + LD::VLUT);
-    u32x4_t* s_qa = (u32x4_t*)(lds + LD::QA);
-    float* s_alpha = (float*)(lds + LD::ALPHA) + wave * 16;
-    uint32_t* s_nnz = (uint32_t*)(lds + LD::NNZ);
-    uint8_t* kst = lds + LD::KST + wave * LD::KST_W;
-    uint16_t* sst = (uint16_t*)(lds + LD::SST + wave * LD::SST_W);
-    uint32_t* wx = (uint32_t*)(lds + LD::WX) + wave * 16 * 32;
-
-    const size_t bh = (size_t)b * a.Hkv + h;
-    const int64_t n_packed = a.n_packed[b];
-    const int64_t n_tiles_b = (n_packed + TILE - 1) / TILE;
-    const int64_t t_lo = (int64_t)split * a.tiles_per_split;
-    const int64_t t_hi = t_lo + a.tiles_per_split < n_tiles_b ? t_lo + a.tiles_per_split : n_tiles_b;
-    const uint32_t* kc = (const uint32_t*)(a.k_codes + bh * a.n_tiles * a.k_tile_bytes);
-    const uint32_t* vc = (const uint32_t*)(a.v_codes + bh * a.n_tiles * a.v_tile_bytes);
-    const uint32_t* ks32 = (const uint32_t*)(a.k_scale + bh * a.n_cap);  // fp16 pairs (token 2i, 2i + 1)
-    const uint32_t* vs32 = (const uint32_t*)(a.v_scale + bh * a.n_cap);
-    const uint32_t* vz32 = a.v_affine ? (const uint32_t*)(a.v_zero + bh * a.n_cap) : nullptr;
-    const bool vaff = a.v_affine != 0;
-
-    // Prologue.  Global loads of the tables and the query go out first, then the
-    // first tile's prefetch; loads retire in order, so the LDS writes below do not wait for HBM.
-    // Loads are unconditional (clamped indices) so that no branch forces an early wait.
-    // The query comes first: wave 0's preparation waits only for it.
-    const PrepIn<G> pin = prep_load<G, true>(a.q, a.q_dtype, a.bits, a.sigma, b, h, a.Hq, lane);
-    constexpr int TAB4 = BGTQ_CB_MX_WORDS / 4;
-    const u32x4_t* tab4 = (const u32x4_t*)c_mxtab;
-    u32x4_t tv[(TAB4 + 255) / 256];
-#pragma unroll
-    for (int k = 0; k < (TAB4 + 255) / 256; ++k)
-        tv[k] = tab4[threadIdx.x + 256 * k < TAB4 ? threadIdx.x + 256 * k : 0];
-    // value pair table entries this thread writes: entry e = threadIdx.x / copies + 256 / copies * k
-    constexpr int VCOP = VLutGeom<VB>::COPIES, VENT = 1 << (2 * VB);
-    constexpr int VROUNDS = (VENT * VCOP + 255) / 256;
-    uint32_t vla[VROUNDS], vlb[VROUNDS];
-#pragma unroll
-    for (int k = 0; k < VROUNDS; ++k) {
-        const uint32_t e = ((threadIdx.x + 256u * k) / VCOP) & (VENT - 1);
-        vla[k] = c_cent16[cent_base(VB) + (e & ((1u << VB) - 1u))];
-        vlb[k] = c_cent16[cent_base(VB) + (e >> VB)];
-    }
-
-    // Tile data: K chunks and one dword of scales per lane (lanes 0..31: K scales of tokens 2l,
-    // 2l+1; lanes 32..63: V scales; V zeros in a second dword for affine values) are prefetched one
-    // tile ahead and staged to LDS when their tile starts; the value streams stay in registers
-    // (each lane reads its own stream) and are loaded once the previous tile's P·V is done.
-    u32x4_t kn[R / 4], vn[VB], vx[VB];
-    uint32_t sn, zn;
-    auto fetch_k = [&](int64_t t) {
-        const u32x4_t* kt = (const u32x4_t*)(kc + t * (a.k_tile_bytes / 4));
-#pragma unroll
-        for (int c = 0; c < R / 4; ++c) kn[c] = kt[c * 64 + lane];
-        sn = (lane < 32 ? ks32 : vs32)[t * (TILE / 2) + (lane & 31)];
-        zn = vz32 ? vz32[t * (TILE / 2) + (lane & 31)] : 0u;
-    };
-    auto fetch_v = [&](u32x4_t (&dst)[VB], int64_t t) {
-        const u32x4_t* vt = (const u32x4_t*)(vc + t * (a.v_tile_bytes / 4));
-#pragma unroll
-        for (int c = 0; c < VB; ++c) dst[c] = vt[c * 64 + lane];
-    };
-    // Unconditional (branch-free prologue); a wave without tiles reads a tile inside the allocation
-    // and never uses it.  Only the keys now: the values of the first tile go out after the
-    // prologue, so the first burst every wave waits on is half as large.
-    const int64_t t_first = t_lo + wave < t_hi ? t_lo + wave : (t_lo < a.n_tiles ? t_lo : 0);
-    fetch_k(t_first);
-
-#pragma unroll
-    for (int k = 0; k < (TAB4 + 255) / 256; ++k)
-        if (threadIdx.x + 256 * k < TAB4) ((u32x4_t*)(lds + LD::TAB))[threadIdx.x + 256 * k] = tv[k];
-#pragma unroll
-    for (int k = 0; k < VROUNDS; ++k) {
-        const uint32_t i = threadIdx.x + 256u * k;
-        const uint32_t e = (i / VCOP) & (VENT - 1);
-        if (i < (uint32_t)(VENT * VCOP))
-            s_vlut[i] = a.v_affine ? (uint32_t)f2h((float)(e & ((1u << VB) - 1u))) | ((uint32_t)f2h((float)(e >> VB)) << 16)
-                                   : vla[k] | (vlb[k] << 16);
-    }
-#pragma unroll
-    for (int i = threadIdx.x; i < 4 * 16 * 32 / 4; i += 256) ((u32x4_t*)(lds + LD::WX))[i] = u32x4_t{0u, 0u, 0u, 0u};
-    const int bw = (int)((pin.w4 >> (8 * (lane & 3))) & 0xFFu);
-    const int w = bw < 8 ? bw : 8;  // widths above 8 are invalid; clamp
-    if (wave == 0) mx_prep_q<G>(pin, w, lane, lds + LD::QA, s_nnz);
-    if (wave == 1) {
-        // Slot descriptors: stream slot r is k-step r / 16, column pair (r % 16) / 8, lane row
-        // (r % 8) / 2, second of its pair if odd; a column is read per coordinate when its first
-        // slot is wider than 5 bits (slots are in width order).
-        int rank, pos, nnz;
-        block_order(w, lane, rank, pos, nnz);
-        const int n_wide = __popcll(__ballot(w > 5));
-        int* s_sw = (int*)(lds + LD::QP);  // stream-ordered widths and positions
-        int* s_sp = s_sw + 64;
-        if (w > 0) { s_sw[rank] = w; s_sp[rank] = pos; }
-        if (lane >= nnz) { s_sw[lane] = 0; s_sp[lane] = 0; }
-        wave_lds_fence();
-        const int r = lane, ks = r >> 4, mp = (r >> 3) & 1, kq = (r >> 1) & 3, odd = r & 1;
-        auto coord_of = [&](int first) { return first < n_wide; };
-        const bool ca = coord_of(16 * ks + 8 * mp), cs = coord_of(16 * ks + 8 * mp + odd);
-        uint32_t* s_desc = (uint32_t*)(lds + LD::DESC);
-        s_desc[kq * 16 + 4 * ks + 2 * mp + odd] = mx_desc(s_sp[r & ~1], ca, s_sp[r], s_sw[r], cs);
-        // coordinate columns, counted in k-step order (columns 2M, 2M + 1 of a k-step start at
-        // slots 16 ks + 8 M and 16 ks + 8 M + 1)
-        if (lane == 0) {
-            int nc = 0;
-            for (int c = 0; c < 16; ++c) nc += coord_of(16 * (c >> 2) + 8 * ((c >> 1) & 1) + (c & 1)) ? 1 : 0;
-            s_nnz[1] = (uint32_t)nc;
-        }
-    }
-    __syncthreads();  // tables, descriptors and query operands are in place; the scratch above is
-                      // reused as the tile stages below
-
-    const int nnz_pad = (int)__builtin_amdgcn_readfirstlane(s_nnz[0]);  // nonzero slots rounded up to 4
-    const int nks = (nnz_pad + 15) >> 4;
-    const int ncc = (int)__builtin_amdgcn_readfirstlane(s_nnz[1]);      // coordinate columns
-    const u32x4_t* sd = (const u32x4_t*)(lds + LD::DESC) + 4 * row;  // this lane row's descriptors
-    fetch_v(vn, t_first);
-
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, zs[2] = {0.f, 0.f};
-    f32x4_t o[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    uint32_t lb = (uint32_t)(LD::KST + wave * LD::KST_W) + 4u * (uint32_t)col;
-    asm volatile("" : "+v"(lb));  // keep the stage base inside lb: one add per column address
-    const uint32_t lcopy = 4u * ((uint32_t)lane & (VLutGeom<VB>::COPIES - 1));  // this lane's value-table copy
-
-    // two tiles per iteration: the value streams of the next tile load into the other buffer (4-bit
-    // values: one buffer, reloaded after P·V, as a second one would not fit the register budget)
-    constexpr bool VDB = VB <= 3;
-    auto tile = [&](const int64_t t, u32x4_t (&vcur)[VB], u32x4_t (&vnext)[VB]) __attribute__((always_inline)) {
-        // Stage the tile: K rows (row rho of the record at stage row rho + 1), scales (transposed:
-        // token u at (u%16)*4 + u/16).
-        wave_lds_fence();
-#pragma unroll
-        for (int c = 0; c < R / 4; ++c)
-            *(u32x4_t*)(kst + (4 * c + row + 1) * BGTQ_KST_ROW_BYTES + 16 * col) = kn[c];
-        {
-            const int u0 = 2 * (lane & 31), reg = lane < 32 ? 0 : 64;
-            sst[reg + (u0 & 15) * 4 + (u0 >> 4)] = (uint16_t)(sn & 0xFFFFu);
-            sst[reg + ((u0 + 1) & 15) * 4 + ((u0 + 1) >> 4)] = (uint16_t)(sn >> 16);
-            if (lane < 32) {
-                sst[128 + (u0 & 15) * 4 + (u0 >> 4)] = (uint16_t)(zn & 0xFFFFu);
-                sst[128 + ((u0 + 1) & 15) * 4 + ((u0 + 1) >> 4)] = (uint16_t)(zn >> 16);
-            }
-        }
-        wave_lds_fence();
-        asm volatile("" ::: "memory");
-        {
-            // unconditional, so that no branch merges the wait counts (the last tile re-reads itself)
-            const int64_t tn = t + 4 < t_hi ? t + 4 : t;
-            fetch_k(tn);
-            if constexpr (VDB) fetch_v(vnext, tn);
-        }
-
-        // q·k on the matrix cores
-        f32x4_t c[4];
-        if (nks == 0) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) c[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        if (nks > 0) mx_kstep_any<0>(c, lds, s_qa, lane, sd, lb, ncc);
-        if (nks > 1) mx_kstep_any<1>(c, lds, s_qa, lane, sd, lb, ncc);
-        if (nks > 2) mx_kstep_any<2>(c, lds, s_qa, lane, sd, lb, ncc);
-        if (nks > 3) mx_kstep_any<3>(c, lds, s_qa, lane, sd, lb, ncc);
-
-        // softmax over the tile: lane holds tokens 16g + col, heads 2row, 2row + 1
-        float sk[4], sv[4], sz[4] = {0.f, 0.f, 0.f, 0.f};
-        {
-            const uint2 k2 = *(const uint2*)(sst + col * 4), v2 = *(const uint2*)(sst + 64 + col * 4);
-            sk[0] = h2f(k2.x & 0xFFFFu); sk[1] = h2f(k2.x >> 16); sk[2] = h2f(k2.y & 0xFFFFu); sk[3] = h2f(k2.y >> 16);
-            sv[0] = h2f(v2.x & 0xFFFFu); sv[1] = h2f(v2.x >> 16); sv[2] = h2f(v2.y & 0xFFFFu); sv[3] = h2f(v2.y >> 16);
-            if (vaff) {
-                const uint2 z2 = *(const uint2*)(sst + 128 + col * 4);
-                sz[0] = h2f(z2.x & 0xFFFFu); sz[1] = h2f(z2.x >> 16); sz[2] = h2f(z2.y & 0xFFFFu); sz[3] = h2f(z2.y >> 16);
-            }
-        }
-        float z[4][2];
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) z[g][hh] = sk[g] * (c[g][2 * hh] + c[g][2 * hh + 1]);
-        if ((t + 1) * TILE > n_packed) {  // the sequence ends inside this tile
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                // scales of tokens past the end are never written: keep them out of the arithmetic
-                if (t * TILE + 16 * g + col >= n_packed) {
-                    sv[g] = 0.f;
-                    sz[g] = 0.f;
-                    z[g][0] = z[g][1] = -INFINITY;
-                }
-            }
-        }
-        float tmax[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) tmax[hh] = vmax(vmax3(z[0][hh], z[1][hh], z[2][hh]), z[3][hh]);
-        if (t == t_lo + wave) {
-            // the wave's first tile: nothing accumulated yet, so no rescale
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) m[hh] = row_max16(tmax[hh]);
-        } else if (__ballot(tmax[0] > m[0] || tmax[1] > m[1])) {
-            float alpha[2];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const float mn = vmax(m[hh], row_max16(tmax[hh]));
-                alpha[hh] = __builtin_amdgcn_exp2f(m[hh] - mn);
-                m[hh] = mn;
-                l[hh] *= alpha[hh];
-                zs[hh] *= alpha[hh];
-            }
-            wave_lds_fence();
-            if (col == 0) {
-                s_alpha[2 * row] = alpha[0];
-                s_alpha[2 * row + 1] = alpha[1];
-            }
-            wave_lds_fence();
-            const float al = s_alpha[col];
-#pragma unroll
-            for (int db = 0; db < 8; ++db) o[db] *= al;
-        }
-        uint16_t wh[4][2];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const float p = __builtin_amdgcn_exp2f(z[g][hh] - m[hh]);
-                l[hh] += p;
-                if (vaff) zs[hh] += p * sz[g];
-                wh[g][hh] = f2h(p * sv[g]);
-            }
-        }
-        wave_lds_fence();
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            uint32_t* wr = wx + (2 * row + hh) * 32 + col;
-            wr[0] = (uint32_t)wh[0][hh] | ((uint32_t)wh[2][hh] << 16);
-            wr[16] = (uint32_t)wh[1][hh] | ((uint32_t)wh[3][hh] << 16);
-        }
-        wave_lds_fence();
-
-        // P·V on the matrix cores from this lane's value stream, then the next tile's streams
-        uint32_t vs[4 * VB];
-#pragma unroll
-        for (int c = 0; c < VB; ++c) {
-            vs[4 * c] = vcur[c][0]; vs[4 * c + 1] = vcur[c][1]; vs[4 * c + 2] = vcur[c][2]; vs[4 * c + 3] = vcur[c][3];
-        }
-        mx_pv<VB, 0>(o, vs, s_vlut, wx, lane, lcopy);
-        mx_pv<VB, 1>(o, vs, s_vlut, wx, lane, lcopy);
-        if constexpr (!VDB) {
-            if (t + 4 < t_hi) fetch_v(vcur, t + 4);
-        }
-        };
-    if constexpr (VDB) {
-        for (int64_t t = t_lo + wave; t < t_hi; t += 8) {
-            tile(t, vn, vx);
-            if (t + 4 < t_hi) tile(t + 4, vx, vn);
-        }
-    } else {
-        for (int64_t t = t_lo + wave; t < t_hi; t += 4) tile(t, vn, vn);
-    }
-
-    // Epilogue: row sums of l and the zero term, O^T to LDS (over the stages), merge the waves.
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        l[hh] = row_sum16(l[hh]);
-        zs[hh] = row_sum16(zs[hh]);
-    }
-    __syncthreads();  // every wave is done with its stages
-    float* s_red = (float*)(lds + LD::RED);
-    float* r = s_red + wave * G * PART;
-    if (col < G) {
-#pragma unroll
-        for (int db = 0; db < 8; ++db) *(f32x4_t*)(r + col * PART + 16 * db + 4 * row) = o[db];
-    }
-    if (col == 0) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int hd = 2 * row + hh;
-            if (hd < G) {
-                r[hd * PART + 128] = m[hh];
-                r[hd * PART + 129] = l[hh];
-                r[hd * PART + 130] = zs[hh];
-            }
-        }
-    }
-    __syncthreads();
-    float* part = a.part + ((size_t)b * a.Hq + (size_t)h * G) * a.n_parts * PART;
-    merge_waves4<G>(s_red, s_red + 4 * G * PART, part, a.n_parts, split);
-}
-
 // Matrix-core decode over affine 4-bit keys in groups of KG = 32, 64 or 128 dims (the "Quantize
 // What Counts" K4V2 configuration uses 32), for 4 or 8 query heads per kv head.  A key group spans
 // KG / 32 k-steps of q·k: a lane's B operand is one record dword (dims 32 ks + 8u .. 8u + 7 of
@@ -1033,8 +716,8 @@ __global__ __launch_bounds__(256, mx_wgs_per_cu<VB>()) void k_decode_mx(const De
 // subtraction of 1024, both exact; the A operand holds the query in the matching order (dims
 // 32 ks + 8u + {0, 4, 1, 5, 2, 6, 3, 7}), split into fp16 high and low parts.  The products of a
 // group's k-steps accumulate on the matrix cores, then take the group's scale and zero:
-// z += scale * (q'.codes) + zero * sum(q' over the group).  Softmax, P·V (codebook or affine values) and the wave merge are those of k_decode_mx;
-// keys need no windows or tables.
+// z += scale * (q'.codes) + zero * sum(q' over the group).  Softmax, P·V (codebook or affine values)
+// and the wave merge are those of the Block-GTQ matrix-core decode; keys need no windows or tables.
 template <int G, int VB> struct MxaLds {
     static constexpr int VLUT = 0;
     static constexpr int WX = a16(VLUT + VLutGeom<VB>::BYTES);    // u32 [4 waves][16 heads][32 pairs]
@@ -1094,7 +777,7 @@ __global__ __launch_bounds__(256, kMxaWgsPerCu) void k_decode_mxa(const DecodeAr
     }
     // Tile data per lane: the record dword of k-step ks for token group g (kd[ks][g]), the group
     // scales and zeros of its four tokens, and one dword of value scales (lanes 0..31, tokens 2l and
-    // 2l + 1) or value zeros (lanes 32..63); the value streams as in k_decode_mx.
+    // 2l + 1) or value zeros (lanes 32..63); the value streams as in the Block-GTQ matrix-core decode.
     uint32_t kd[4][4], vsd;
     float kss[4][NG], kzz[4][NG];  // [token group][key group]
     u32x4_t vn[VB], vx[VB];
@@ -2376,15 +2059,10 @@ static hipError_t launch_dec(const DecodeArgs& a, int B, hipStream_t s) {
     return launch_main(k_decode<G, R, VB, KG>, dim3(a.n_splits, a.Hkv, B), dim3(256), s, a);
 }
 
-template <int G, int R, int VB>
-static hipError_t launch_dec_mx(const DecodeArgs& a, int B, hipStream_t s) {
-    return launch_main(k_decode_mx<G, R, VB>, dim3(a.n_splits, a.Hkv, B), dim3(256), s, a);
-}
-
 template <int G, int VB>
-static hipError_t launch_dec_gv(const DecodeArgs& a, int B, int k_mode, int R, hipStream_t s) {
+static hipError_t launch_dec_gv(const DecodeArgs& a, int B, int k_mode, int R, bool vector_only, hipStream_t s) {
     if (k_mode == BGTQ_K_AFFINE) {
-        if constexpr (G >= 4) {
+        if constexpr (G >= 4) if (!vector_only) {
             const dim3 grid(a.n_splits, a.Hkv, B);
             switch (a.k_group) {
                 case 32: return launch_main(k_decode_mxa<G, VB, 32>, grid, dim3(256), s, a);
@@ -2399,14 +2077,6 @@ static hipError_t launch_dec_gv(const DecodeArgs& a, int B, int k_mode, int R, h
         }
         return hipErrorInvalidValue;
     }
-    if constexpr (G >= 4) {
-        switch (R) {
-            case 8: return launch_dec_mx<G, 8, VB>(a, B, s);
-            case 12: return launch_dec_mx<G, 12, VB>(a, B, s);
-            case 16: return launch_dec_mx<G, 16, VB>(a, B, s);
-        }
-        return hipErrorInvalidValue;
-    }
     switch (R) {
         case 8: return launch_dec<G, 8, VB, 0>(a, B, s);
         case 12: return launch_dec<G, 12, VB, 0>(a, B, s);
@@ -2416,26 +2086,29 @@ static hipError_t launch_dec_gv(const DecodeArgs& a, int B, int k_mode, int R, h
 }
 
 template <int G>
-static hipError_t launch_dec_g(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t s) {
+static hipError_t launch_dec_g(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, bool vector_only,
+                               hipStream_t s) {
     switch (v_bits) {
-        case 2: return launch_dec_gv<G, 2>(a, B, k_mode, R, s);
-        case 3: return launch_dec_gv<G, 3>(a, B, k_mode, R, s);
-        case 4: return launch_dec_gv<G, 4>(a, B, k_mode, R, s);
+        case 2: return launch_dec_gv<G, 2>(a, B, k_mode, R, vector_only, s);
+        case 3: return launch_dec_gv<G, 3>(a, B, k_mode, R, vector_only, s);
+        case 4: return launch_dec_gv<G, 4>(a, B, k_mode, R, vector_only, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t s) {
+// Vector-ALU decode (k_decode) for every format, or the affine matrix-core kernel for affine keys at
+// g >= 4 unless vector_only.  Block-GTQ keys at g >= 4 come here only on the vector path.
+hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, bool vector_only, hipStream_t s) {
     if (!a.k_codes || !a.v_codes || !a.k_scale || !a.v_scale || !a.q || !a.part || B < 1 || B > BGTQ_MAXB)
         return hipErrorInvalidValue;
     if (k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma)) return hipErrorInvalidValue;
     if (k_mode == BGTQ_K_AFFINE && !a.k_zero) return hipErrorInvalidValue;
     if (a.v_affine && !a.v_zero) return hipErrorInvalidValue;
     switch (a.G) {
-        case 1: return launch_dec_g<1>(a, B, k_mode, R, v_bits, s);
-        case 2: return launch_dec_g<2>(a, B, k_mode, R, v_bits, s);
-        case 4: return launch_dec_g<4>(a, B, k_mode, R, v_bits, s);
-        case 8: return launch_dec_g<8>(a, B, k_mode, R, v_bits, s);
+        case 1: return launch_dec_g<1>(a, B, k_mode, R, v_bits, vector_only, s);
+        case 2: return launch_dec_g<2>(a, B, k_mode, R, v_bits, vector_only, s);
+        case 4: return launch_dec_g<4>(a, B, k_mode, R, v_bits, vector_only, s);
+        case 8: return launch_dec_g<8>(a, B, k_mode, R, v_bits, vector_only, s);
     }
     return hipErrorInvalidValue;
 }
@@ -2446,9 +2119,8 @@ void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
 }
 void disarm_launch_events() { t_ev_start = t_ev_stop = nullptr; }
 
-int decode_wgs_per_cu(int k_mode, int G, int v_bits, int k_group) {
-    if (G >= 4 && k_mode == BGTQ_K_BLOCKGTQ) return v_bits == 3 ? mx_wgs_per_cu<3>() : mx_wgs_per_cu<2>();
-    if (G >= 4 && k_mode == BGTQ_K_AFFINE && (k_group == 32 || k_group == 64 || k_group == 128)) return kMxaWgsPerCu;
+int decode_wgs_per_cu(int k_mode, int G, int v_bits, int k_group, bool vector_only) {
+    if (!vector_only && G >= 4 && k_mode == BGTQ_K_AFFINE && (k_group == 32 || k_group == 64 || k_group == 128)) return kMxaWgsPerCu;
     return 2;
 }
 

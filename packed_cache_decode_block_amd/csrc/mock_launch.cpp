@@ -33,7 +33,7 @@ namespace bgtq {
 
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 
-hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, hipStream_t) {
+static hipError_t check_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits) {
     if (!a.k_codes || !a.v_codes || !a.k_scale || !a.v_scale || !a.q || !a.part) return bad("decode: null pointer");
     if (k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma)) return bad("decode: null key metadata");
     if (k_mode == BGTQ_K_AFFINE && !a.k_zero) return bad("decode: null k_zero");
@@ -49,14 +49,21 @@ hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bi
         if (tiles > (int64_t)a.n_splits * a.tiles_per_split) return bad("decode: splits do not cover the context");
     }
     if (a.n_tiles * 64 != a.n_cap) return bad("decode: n_tiles");
-    note("decode");
     return hipSuccess;
 }
 
-hipError_t launch_decode_gtq(const DecodeArgs& a, int B, int R, int v_bits, hipStream_t s) {
+hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, bool vector_only, hipStream_t) {
+    if (hipError_t e = check_decode(a, B, k_mode, R, v_bits)) return e;
+    note(vector_only ? "decode_vector" : "decode");
+    return hipSuccess;
+}
+
+hipError_t launch_decode_gtq(const DecodeArgs& a, int B, int R, int v_bits, hipStream_t) {
     if (!a.plan) return bad("decode: null plan");
     if (a.G != 4 && a.G != 8) return bad("decode: group size of the plan-driven decode");
-    return launch_decode(a, B, BGTQ_K_BLOCKGTQ, R, v_bits, s);
+    if (hipError_t e = check_decode(a, B, BGTQ_K_BLOCKGTQ, R, v_bits)) return e;
+    note("decode_gtq");
+    return hipSuccess;
 }
 
 hipError_t launch_plan(const uint8_t* bits, uint8_t* plan, int Hkv, hipStream_t) {
@@ -135,7 +142,7 @@ hipError_t launch_permute(const PermuteArgs& a, int B, hipStream_t) {
 void arm_launch_events(hipEvent_t, hipEvent_t) {}
 void disarm_launch_events() {}
 
-int decode_wgs_per_cu(int k_mode, int G, int v_bits, int k_group) {
+int decode_wgs_per_cu(int k_mode, int G, int v_bits, int k_group, bool) {
     if (G >= 4 && k_mode == BGTQ_K_BLOCKGTQ) return v_bits == 3 ? 2 : 3;
     (void)k_group;
     return 2;

@@ -89,6 +89,37 @@ def test_quantize_and_decode(name):
         print(f"  splits={ns}: max abs err {e:.2e}", flush=True)
 
 
+VECTOR_CASES = ["w2_reduced", "w3_k3v3", "w2_k4v4", "w4_g8", "w5_reduced"]
+
+
+@pytest.mark.parametrize("name", VECTOR_CASES)
+def test_vector_decode_path(name):
+    """The cache's vector-ALU decode path (no matrix-core instructions) against the oracle, at the
+    head ratios where the library otherwise takes the matrix cores; the matrix-core result of the
+    same cache is compared too."""
+    wid, ov, N, chunks = CASES[name]
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
+    print(f"[vector {name}] N={N} B={w.B} Hq={w.Hq} Hkv={w.Hkv}", flush=True)
+    n_cap = ((N + 63) // 64 + 1) * 64
+    m = T.meta(w, 0)
+    K, V, q = T.inputs(w, 0, N)
+    oc = T.oracle_layer(w, K, V, m, n_cap)
+    cache = T.gpu_cache(w, n_cap)
+    if m is not None:
+        cache.set_metadata(0, m.bits, m.sigma, m.r)
+    T.append_all(cache, 0, K, V, w.dtype, chunks)
+    ref = pipeline.decode_layer(oc, q)
+    qd = T.to_dev(q, w.dtype)
+    auto = cache.decode_attention(0, qd).cpu().numpy()
+    cache.decode_path = P.DECODE_VECTOR
+    for ns in (0, 1, 3):
+        out = cache.decode_attention(0, qd, n_splits=ns)
+        torch.cuda.synchronize()
+        e = T.assert_close(out.cpu().numpy(), ref, f"vector {name} splits={ns}")
+        print(f"  splits={ns}: max abs err {e:.2e}", flush=True)
+    T.assert_close(auto, ref, f"auto {name}")
+
+
 def _widths(spec, seed):
     """Fixed allocation: spec = [(width, count), ...] over the 64 blocks (the rest get 0), placed in
     a seeded block order so that the stream order is not the block order."""

@@ -214,3 +214,31 @@ def test_prepare_metadata_and_plan_requirement(mock):
     da = _desc(nt, k_mode=1, k_bits=4, k_group=32, v_mode=1, v_bits=2)
     assert mock.bgtq_cache_bytes(C.byref(da), _lib.BUF_PLAN) == 0
     assert mock.bgtq_prepare_metadata(C.byref(da), 0, None) == _lib.E_INVALID
+
+
+def test_decode_path_routing(mock):
+    """decode_path picks the kernel family: Block-GTQ keys at 8 query heads per kv head take the
+    plan-driven matrix-core kernel by default and the vector-ALU kernel on the vector path (which
+    needs no plan), with workspaces sized for each; other values are refused before any launch."""
+    nt = np.full((2, 2), 3000, np.int64)
+    d = _desc(nt)
+    q = C.c_void_p(FAKE + 0x50000000)
+    ws = C.c_void_p(FAKE + 0x60000000)
+    need = mock.bgtq_decode_workspace_bytes(C.byref(d), 0)
+    mock.bgtq_mock_reset()
+    log = _call_ok(mock, mock.bgtq_decode_attention(C.byref(d), 0, q, 2, q, ws, need, 0, None))
+    assert log.split() == ["decode_gtq", "combine"], log
+    d.decode_path = _lib.DECODE_VECTOR
+    d.plan = None
+    need_v = mock.bgtq_decode_workspace_bytes(C.byref(d), 0)
+    assert need_v > 0
+    for ns in (0, 1, 5):
+        mock.bgtq_mock_reset()
+        log = _call_ok(mock, mock.bgtq_decode_attention(C.byref(d), 0, q, 2, q, ws,
+                                                        mock.bgtq_decode_workspace_bytes(C.byref(d), ns), ns, None))
+        assert log.split() == ["decode_vector", "combine"], log
+    for bad in (2, -1):
+        d.decode_path = bad
+        mock.bgtq_mock_reset()
+        assert mock.bgtq_decode_attention(C.byref(d), 0, q, 2, q, ws, need, 0, None) == _lib.E_INVALID
+        assert b"decode_path" in mock.bgtq_last_error() and mock.bgtq_mock_launches() == 0
