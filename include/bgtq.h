@@ -293,12 +293,17 @@ int bgtq_decode_attention(const bgtq_cache *c, int layer, const void *q, int dty
                           void *ws, size_t ws_bytes, int n_splits, void *stream);
 
 /*
- * One decode step: quantize-append then attend, in one call (device, asynchronous).  The fusion of
- * the append into the attention step is the operator fusion LogQuant names as future work
- * (LogQuant summary, Conclusion); the packed path it serves is the one above (review §1
- * Packed-Cache).  Appends k, v (as bgtq_quantize_append: n_new rows per sequence, same strides
- * convention) and then computes bgtq_decode_attention for q over the grown context, all on
- * `stream`; k, v and q share `dtype`.  The result equals the two calls made in turn.
+ * One decode step: quantize-append then attend, in one call (device, asynchronous).  Appends k, v
+ * (as bgtq_quantize_append: n_new rows per sequence, same strides convention) and computes
+ * bgtq_decode_attention for q over the grown context, all on `stream`; k, v and q share `dtype`.
+ * The codes and scales written are those bgtq_quantize_append writes, and the output equals the
+ * two calls made in turn (to the decode's rounding).
+ * Launches: with one new token per sequence, Block-GTQ keys, g >= 4 on BGTQ_DECODE_AUTO and no
+ * fp16 window (n_recent == 0, no log-based filter), the append is fused into the attention
+ * launch — the operator fusion LogQuant names as future work (LogQuant summary, Conclusion): the
+ * wave whose tile holds the new token quantizes it while its tile is in flight, writes it to the
+ * cache and attends to it with the rest of the tile, so the step is the decode launch plus the
+ * split merge.  Otherwise the append kernels run first, as dependent launches on `stream`.
  * Both halves are validated against the post-append lengths before anything is enqueued: an
  * error other than BGTQ_E_HIP leaves the cache and n_tokens untouched.  BGTQ_E_HIP from the
  * attention half is reported after the append was enqueued (n_tokens then includes the new rows).

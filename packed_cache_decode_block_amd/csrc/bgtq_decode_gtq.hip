@@ -35,10 +35,11 @@ namespace {
 
 
 // Plan record of one (layer, kv head): u32 desc[64] (column descriptors, index kq*16 + 4ks + 2mp +
-// odd as mx_desc builds them), u8 rank[64] (stream slot of block i, 0xFF for width 0), then u32
-// nnz_pad (nonzero slots rounded up to 4), ncc (coordinate columns), nnz.
-constexpr int kPlanDesc = 0, kPlanRank = 256, kPlanCounts = 320;
-static_assert(kPlanCounts + 12 <= BGTQ_PLAN_BYTES, "plan record size");
+// odd as mx_desc builds them), u8 rank[64] (stream slot of block i, 0xFF for width 0), u32 nnz_pad
+// (nonzero slots rounded up to 4), ncc (coordinate columns), nnz, then u16 off[64] (bit offset of
+// block i's field in the key record).
+constexpr int kPlanDesc = 0, kPlanRank = 256, kPlanCounts = 320, kPlanOff = 336;
+static_assert(kPlanOff + 128 <= BGTQ_PLAN_BYTES, "plan record size");
 
 // One wave per kv head, lane = RoPE block.
 __global__ __launch_bounds__(64) void k_plan(const uint8_t* bits, uint8_t* plan) {
@@ -66,6 +67,7 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* bits, uint8_t* plan)
     const bool ca = coord_of(16 * ks + 8 * mp), cs = coord_of(16 * ks + 8 * mp + odd);
     ((uint32_t*)(p + kPlanDesc))[kq * 16 + 4 * ks + 2 * mp + odd] = mx_desc(s_sp[r & ~1], ca, s_sp[r], s_sw[r], cs);
     p[kPlanRank + lane] = (uint8_t)(w > 0 ? rank : 0xFF);
+    ((uint16_t*)(p + kPlanOff))[lane] = (uint16_t)pos;
     if (lane == 0) {
         int nc = 0;
         for (int c = 0; c < 16; ++c) nc += coord_of(16 * (c >> 2) + 8 * ((c >> 1) & 1) + (c & 1)) ? 1 : 0;
@@ -229,9 +231,221 @@ __device__ __forceinline__ void merge_waves_n(const float* red, float* part, int
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// One-token append inside the decode (bgtq_decode_step on this kernel; LogQuant summary,
+// Conclusion: fusing the write into the attention launch).  In the workgroup whose splits hold the
+// appended token (the last packed one of its sequence), wave 0 quantizes it in the prologue, before
+// the barrier that releases the tiles, with the steps of the append kernels (one wave, lane i =
+// RoPE block i with dims 2i and 2i + 1): the key record, fp16 scales and value codes go to the cache
+// and to LDS; the wave that stages the token's tile patches its record column, scales and value
+// fields in, so the token is attended with the rest of its tile.
+
+// The token's key record (R dwords), scales (key, value, value zero), the squares summed for the
+// scales, and its value fields as they go into the streams of lanes 16 jj .. 16 jj + 15 (bits and
+// mask per stream dword; jj from the token's tile position).
+struct AppLds {  // 16-byte aligned (read 16 bytes at a time): the arrays come first
+    float sq[256];  // squares of the scaled key row, then of the value row
+    uint32_t vval[16][16];
+    uint32_t vmsk[16][16];
+    uint32_t rec[16];
+    uint16_t sc[4];
+};
+static_assert(offsetof(AppLds, vval) % 16 == 0 && offsetof(AppLds, vmsk) % 16 == 0, "16-byte rows");
+
+struct AppRow {
+    float kx0, kx1, vx0, vx1;  // the lane's two elements of the key and value rows
+    int w, off;                // width of the lane's block and its bit offset in the record
+    float r, sg;               // 1/sigma and sigma of the lane's block
+    uint32_t thr[(BGTQ_CB_THRESHOLDS + 63) / 64];  // thresholds lane + 64 k
+};
+
+__device__ __forceinline__ AppRow app_load(const DecodeArgs& a, const uint8_t* plan, int b, int h, int lane) {
+    const int64_t src = (int64_t)b * a.app_sB + (int64_t)h * a.app_sH + 2 * lane;
+    AppRow r;
+    r.kx0 = load_act(a.app_k, src, a.app_dtype);
+    r.kx1 = load_act(a.app_k, src + 1, a.app_dtype);
+    r.vx0 = load_act(a.app_v, src, a.app_dtype);
+    r.vx1 = load_act(a.app_v, src + 1, a.app_dtype);
+    const int bw = a.bits[h * 64 + lane];
+    r.w = bw < 8 ? bw : 8;
+    r.off = ((const uint16_t*)(plan + kPlanOff))[lane];
+    r.r = a.inv_sigma[h * 64 + lane];
+    r.sg = a.sigma[h * 64 + lane];
+#pragma unroll
+    for (int k = 0; k < (BGTQ_CB_THRESHOLDS + 63) / 64; ++k)
+        r.thr[k] = c_thr32[lane + 64 * k < BGTQ_CB_THRESHOLDS ? lane + 64 * k : 0];
+    return r;
+}
+
+// Quantize the token at position pos of (batch, kv head) bh and write it to the cache; leave the
+// record, scales and value codes in ap.  thr: LDS for the scalar thresholds.
+template <int R, int VB>
+__device__ void app_quantize(const DecodeArgs& a, const AppRow& in, int lane, size_t bh, int64_t pos, bool vaff,
+                             float* thr, AppLds* ap) {
+#pragma unroll
+    for (int k = 0; k < (BGTQ_CB_THRESHOLDS + 63) / 64; ++k)
+        if (lane + 64 * k < BGTQ_CB_THRESHOLDS) thr[lane + 64 * k] = __builtin_bit_cast(float, in.thr[k]);
+    if (lane < R) ap->rec[lane] = 0u;
+    {
+#pragma clang fp contract(off)
+        const float u0 = in.kx0 * in.r, u1 = in.kx1 * in.r;
+        ap->sq[2 * lane] = u0 * u0;
+        ap->sq[2 * lane + 1] = u1 * u1;
+        ap->sq[128 + 2 * lane] = in.vx0 * in.vx0;
+        ap->sq[128 + 2 * lane + 1] = in.vx1 * in.vx1;
+    }
+    wave_lds_fence();
+    // The per-token scales: squares summed in element order (lane 0: keys, lane 32: values; the
+    // steps of the append kernels), mean, square root, fp16.
+    float acc = 0.f;
+    {
+        const f32x4_t* sq4 = (const f32x4_t*)(ap->sq + (lane >= 32 ? 128 : 0));
+#pragma unroll
+        for (int i0 = 0; i0 < 32; i0 += 8) {  // eight reads in flight, then their 32 additions
+            f32x4_t v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = sq4[i0 + i];
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                acc = acc + v[i][0];
+                acc = acc + v[i][1];
+                acc = acc + v[i][2];
+                acc = acc + v[i][3];
+            }
+        }
+    }
+    const uint16_t ks16 = f2h(sqrtf(lane_f(acc, 0) / 128.0f));
+    const float S = h2f(ks16);
+    if (in.w > 0) {
+        float t;
+        {
+#pragma clang fp contract(off)
+            t = S * in.sg;
+        }
+        // both coordinates' binary searches (tq_code) in one loop, so their reads overlap
+        uint32_t q0 = 0u, q1 = 0u;
+        const float* tb = thr + thr_base(in.w);
+        for (int st = in.w - 1; st >= 0; --st) {
+#pragma clang fp contract(off)
+            const uint32_t a0 = q0 + (1u << st), a1 = q1 + (1u << st);
+            const float th0 = t * tb[a0 - 1], th1 = t * tb[a1 - 1];
+            if (in.kx0 >= th0) q0 = a0;
+            if (in.kx1 >= th1) q1 = a1;
+        }
+        const uint32_t f = q0 | (q1 << in.w);
+        const int k = in.off >> 5, sh = in.off & 31;
+        if (k < R) atomicOr(&ap->rec[k], f << sh);
+        if (sh + 2 * in.w > 32 && k + 1 < R) atomicOr(&ap->rec[k + 1], f >> (32 - sh));
+    }
+    uint32_t c0 = 0u, c1 = 0u;
+    uint16_t vs16 = 0, vz16 = 0;
+    if (!vaff) {
+        vs16 = f2h(sqrtf(lane_f(acc, 32) / 128.0f));
+        const float Sv = h2f(vs16);
+        static_assert(thr_base_c(VB) + (1 << VB) - 1 <= 64, "value thresholds in the first register");
+#pragma unroll
+        for (int m = 0; m < (1 << VB) - 1; ++m) {
+            float th;
+            {
+#pragma clang fp contract(off)
+                th = Sv * __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)in.thr[0], thr_base_c(VB) + m));
+            }
+            c0 += in.vx0 >= th ? 1u : 0u;
+            c1 += in.vx1 >= th ? 1u : 0u;
+        }
+    } else {
+#pragma clang fp contract(off)
+        float mn, mx;
+        wave_minmax(in.vx0, in.vx1, 0, D, mn, mx);
+        const float scale = (mx - mn) / (float)((1 << VB) - 1);
+        vs16 = f2h(scale);
+        vz16 = f2h(mn);
+        const float s32 = h2f(vs16), z32 = h2f(vz16), top = (float)((1 << VB) - 1);
+        float f0 = 0.f, f1 = 0.f;
+        if (s32 != 0.f) {
+            f0 = fminf(fmaxf(rintf((in.vx0 - z32) / s32), 0.f), top);
+            f1 = fminf(fmaxf(rintf((in.vx1 - z32) / s32), 0.f), top);
+        }
+        c0 = (uint32_t)f0;
+        c1 = (uint32_t)f1;
+    }
+    // Value fields: dim 16 db + dd of the token goes to stream dd + 16 jj, field (s * 8 + db) * 4 + m
+    // (p = u % 32 = 16 s + 4 jj + m, the token's half chosen by u >= 32); lane i places dims 2i and
+    // 2i + 1 into the bits and masks of their streams' dwords (rows dd of vval / vmsk).
+    ap->vval[lane >> 2][4 * (lane & 3)] = 0u;  // 64 lanes x 4 = the 256 dwords of each table
+    ap->vval[lane >> 2][4 * (lane & 3) + 1] = 0u;
+    ap->vval[lane >> 2][4 * (lane & 3) + 2] = 0u;
+    ap->vval[lane >> 2][4 * (lane & 3) + 3] = 0u;
+    ap->vmsk[lane >> 2][4 * (lane & 3)] = 0u;
+    ap->vmsk[lane >> 2][4 * (lane & 3) + 1] = 0u;
+    ap->vmsk[lane >> 2][4 * (lane & 3) + 2] = 0u;
+    ap->vmsk[lane >> 2][4 * (lane & 3) + 3] = 0u;
+    wave_lds_fence();
+    {
+        const int u = (int)(pos % TILE), p = u & 31, hi = u >> 5, s = p >> 4, m = p & 3;
+        constexpr uint32_t cm = (1u << VB) - 1u;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int dim = 2 * lane + e, dd = dim & 15, db = dim >> 4;
+            const uint32_t code = e ? c1 : c0;
+            const int bit = 2 * VB * (m + 4 * db + 32 * s) + VB * hi, c = bit >> 5, o = bit & 31;
+            atomicOr(&ap->vval[dd][c], code << o);
+            atomicOr(&ap->vmsk[dd][c], cm << o);
+            if (o + VB > 32) {
+                atomicOr(&ap->vval[dd][c + 1], code >> (32 - o));
+                atomicOr(&ap->vmsk[dd][c + 1], cm >> (32 - o));
+            }
+        }
+    }
+    if (lane == 0) {
+        ap->sc[0] = ks16;
+        ap->sc[1] = vs16;
+        ap->sc[2] = vz16;
+        a.app_k_scale[bh * a.n_cap + pos] = ks16;
+        a.app_v_scale[bh * a.n_cap + pos] = vs16;
+        if (vaff) a.app_v_zero[bh * a.n_cap + pos] = vz16;
+    }
+    wave_lds_fence();
+    if (lane < R) {
+        uint32_t* kt = (uint32_t*)(a.app_k_codes + (bh * a.n_tiles + pos / TILE) * a.k_tile_bytes);
+        kt[lane * TILE + pos % TILE] = ap->rec[lane];
+    }
+}
+
+// Patch the appended token (tile position u) into the staged tile: its record column and scales
+// in LDS, its value fields in the stream registers of lanes 16 jj .. 16 jj + 15; the stream dwords
+// that change are written to the cache (the rest of each dword is as the tile loaded it).
+template <int R, int VB>
+__device__ __forceinline__ void app_patch(const DecodeArgs& a, const AppLds* ap, int lane, int u, size_t bh,
+                                          int64_t tile, uint8_t* kst, uint16_t* sst, bool vaff, u32x4_t (&vcur)[VB]) {
+    if (lane < R) *(uint32_t*)(kst + (lane + 1) * BGTQ_KST_ROW_BYTES + 4 * u) = ap->rec[lane];
+    if (lane == 0) {
+        const int si = (u & 15) * 4 + (u >> 4);
+        sst[si] = ap->sc[0];
+        sst[64 + si] = ap->sc[1];
+        if (vaff) sst[128 + si] = ap->sc[2];
+    }
+    if ((lane >> 4) != ((u >> 2) & 3)) return;
+    uint32_t* vt = (uint32_t*)(a.app_v_codes + (bh * a.n_tiles + tile) * a.v_tile_bytes);
+#pragma unroll
+    for (int c4 = 0; c4 < VB; ++c4) {
+        const u32x4_t mk = *(const u32x4_t*)&ap->vmsk[lane & 15][4 * c4];
+        const u32x4_t vv = *(const u32x4_t*)&ap->vval[lane & 15][4 * c4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (mk[e]) {
+                const uint32_t nv = (vcur[c4][e] & ~mk[e]) | vv[e];
+                vcur[c4][e] = nv;
+                vt[(c4 * 64 + lane) * 4 + e] = nv;
+            }
+        }
+    }
+}
+
 // LDS arena (byte offsets): tables at offset 0 (the arena is 8192-aligned, so table offsets are
 // LDS addresses), column descriptors, value pair table, query operands, weight exchange, softmax
-// rescale factors, counts, then per wave the stage of the tile in flight (K record rows -1 .. R at
+// rescale factors, counts, the append's thresholds and token, then per wave the stage of the tile in flight (K record rows -1 .. R at
 // BGTQ_KST_ROW_BYTES stride, then its scales).  The epilogue records alias the stages.
 template <int G, int R, int VB, int NW> struct GtqLds {
     static constexpr int TAB = 0;
@@ -241,7 +455,9 @@ template <int G, int R, int VB, int NW> struct GtqLds {
     static constexpr int WX = QA + 4 * 64 * 16;                       // u32 [NW waves][16 heads][32 pairs]
     static constexpr int ALPHA = WX + NW * 16 * 32 * 4;               // f32 [NW waves][16]
     static constexpr int NNZ = ALPHA + NW * 16 * 4;                   // u32 [4]: nnz_pad, ncc, nnz
-    static constexpr int KST = a16(NNZ + 16);                         // per wave: R + 2 rows
+    static constexpr int THR = a16(NNZ + 16);                         // f32 [BGTQ_CB_THRESHOLDS] (append)
+    static constexpr int APP = a16(THR + 4 * BGTQ_CB_THRESHOLDS);     // AppLds (append), 16-byte aligned
+    static constexpr int KST = a16(APP + (int)sizeof(AppLds));        // per wave: R + 2 rows
     static constexpr int KST_W = (R + 2) * BGTQ_KST_ROW_BYTES;
     static constexpr int SST = KST + NW * KST_W;                      // per wave: K scales, V scales, V zeros
     static constexpr int SST_W = 3 * 64 * 2;
@@ -279,6 +495,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_gtq(const DecodeArgs a) {
     const uint32_t* vz32 = a.v_affine ? (const uint32_t*)(a.v_zero + bh * a.n_cap) : nullptr;
     const bool vaff = a.v_affine != 0;
     const uint8_t* plan = a.plan + (size_t)h * BGTQ_PLAN_BYTES;
+    // Append in this launch: the sequence's last packed token, at tile t_app, position u_app; the
+    // wave that will stage that tile quantizes it (t_app is -1 without an append).
+    const bool app = a.app_k != nullptr;
+    const int64_t t_app = app ? (n_packed - 1) / TILE : -1;
+    const int u_app = app ? (int)((n_packed - 1) % TILE) : 0;
+    const bool app_here = t_app >= t_lo && t_app < t_hi;  // this workgroup's splits hold the token
+    float* s_thr = (float*)(lds + LD::THR);
+    AppLds* s_app = (AppLds*)(lds + LD::APP);
 
     // Prologue.  Global loads first: the query and this lane's block of the plan (wave 0), the
     // plan's descriptors and counts, the table image and the value centroids, then the first tile's
@@ -293,6 +517,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_gtq(const DecodeArgs a) {
         pin = prep_load<G, true>(a.q, a.q_dtype, a.bits, a.sigma, b, h, a.Hq, lane);
         prank = plan[kPlanRank + lane];
     }
+    AppRow arow{};
+    if (app_here && wave == 0) arow = app_load(a, plan, b, h, lane);
     const uint32_t pdesc = threadIdx.x < 64 ? ((const uint32_t*)(plan + kPlanDesc))[threadIdx.x] : 0u;
     const uint32_t pcnt = threadIdx.x < 3 ? ((const uint32_t*)(plan + kPlanCounts))[threadIdx.x] : 0u;
     constexpr int TAB4 = BGTQ_CB_MX_WORDS / 4;
@@ -359,6 +585,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_gtq(const DecodeArgs a) {
         const int nnz = (int)__builtin_amdgcn_readfirstlane(((const uint32_t*)(plan + kPlanCounts))[2]);
         gtq_prep_q<G>(pin, prank, nnz, lane, lds + LD::QA);
     }
+    if (app_here && wave == 0) {  // ahead of every tile of this workgroup, at raised issue priority
+        __builtin_amdgcn_s_setprio(3);
+        app_quantize<R, VB>(a, arow, lane, bh, n_packed - 1, vaff, s_thr, s_app);
+        __builtin_amdgcn_s_setprio(0);
+    }
     lds_barrier();  // tables, descriptors and query operands are in place
     if constexpr (NW > 8) {
         // One tile per wave, issued in four groups of one wave per SIMD, a barrier between groups.
@@ -414,6 +645,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_gtq(const DecodeArgs a) {
             }
         }
         wave_lds_fence();
+        if (t == t_app) {
+            app_patch<R, VB>(a, s_app, lane, u_app, bh, t, kst, sst, vaff, vcur);
+            wave_lds_fence();
+        }
         asm volatile("" ::: "memory");
         if constexpr (NW <= 8) {
             // unconditional, so that no branch merges the wait counts (the last tile re-reads itself)

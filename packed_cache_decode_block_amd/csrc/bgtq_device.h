@@ -39,6 +39,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int cent_base(int w) { return (1 << w) - 2; }
 __device__ __forceinline__ int thr_base(int w) { return (1 << w) - w - 1; }
+constexpr int thr_base_c(int w) { return (1 << w) - w - 1; }
 __device__ __forceinline__ float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 __device__ __forceinline__ float bf2f(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
@@ -365,6 +366,63 @@ __device__ __forceinline__ float row_sum16(float v) {
 
 constexpr int a16(int x) { return (x + 15) & ~15; }
 constexpr int cmax(int x, int y) { return x > y ? x : y; }
+
+// ---------------------------------------------------------------------------------------------
+// Quantize one token (shared by the append kernels and the decode that appends).  The float32
+// steps are spelled out one IEEE operation at a time (no contraction) so the codes and fp16 scales
+// are reproducible bit for bit.
+// Code of x among the 2^w - 1 scaled thresholds t * thr[thr_base(w) + m] (ascending): the number
+// of thresholds x reaches, by binary search.
+__device__ __forceinline__ uint32_t tq_code(float x, float t, int w, const float* thr) {
+#pragma clang fp contract(off)
+    uint32_t code = 0;
+    const float* tb = thr + thr_base(w);
+    for (int st = w - 1; st >= 0; --st) {
+        const uint32_t cand = code + (1u << st);
+        const float th = t * tb[cand - 1];
+        if (x >= th) code = cand;
+    }
+    return code;
+}
+
+
+__device__ __forceinline__ float lane_f(float v, int i) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i));
+}
+
+// The per-token fp16 RMS scale of a row spread over the wave (lane i holds elements 2i, 2i+1 and
+// the block's 1/sigma r): the same IEEE steps as rms_scale16, u = x*r, u*u, summed in element
+// order, each term read across lanes so the sequential sum waits on no memory.
+__device__ __forceinline__ float wave_rms16(float x0, float x1, float r, bool use_r, uint16_t* s16) {
+#pragma clang fp contract(off)
+    const float u0 = use_r ? x0 * r : x0, u1 = use_r ? x1 * r : x1;
+    const float q0 = u0 * u0, q1 = u1 * u1;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        acc = acc + lane_f(q0, i);
+        acc = acc + lane_f(q1, i);
+    }
+    const float ms = acc / 128.0f;
+    const uint16_t h = f2h(sqrtf(ms));
+    *s16 = h;
+    return h2f(h);
+}
+
+// min and max of elements [j0, j0 + n) of a row spread over the wave, folded in element order
+// from element j0 (the order affine_group takes); j0 and n are wave-uniform, n even.
+__device__ __forceinline__ void wave_minmax(float x0, float x1, int j0, int n, float& mn, float& mx) {
+    mn = mx = lane_f(x0, j0 >> 1);
+    mx = fmaxf(mx, lane_f(x1, j0 >> 1));
+    mn = fminf(mn, lane_f(x1, j0 >> 1));
+    for (int i = (j0 >> 1) + 1; i < ((j0 + n) >> 1); ++i) {
+        const float a = lane_f(x0, i), c = lane_f(x1, i);
+        mn = fminf(mn, a);
+        mx = fmaxf(mx, a);
+        mn = fminf(mn, c);
+        mx = fmaxf(mx, c);
+    }
+}
 
 // Launch with the armed event pair, if any (consumed), else plainly.
 template <typename K, typename A>

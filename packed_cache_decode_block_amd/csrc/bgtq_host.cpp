@@ -726,9 +726,18 @@ namespace {
 
 // Decode body over the context lengths `lens` ([B]; the descriptor's n_tokens row, or the lengths a
 // pending append will leave).  With dry_run the call validates only and launches nothing.
+// Rows of a one-token append that the decode launch quantizes and writes itself (element (b, h, j)
+// at b * sB + h * sH + j).
+struct AppendRows {
+    const void* k;
+    const void* v;
+    int dtype;
+    int64_t sB, sH;
+};
+
 int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dtype, float* out, void* ws,
                           size_t ws_bytes, int n_splits, void* stream, const int64_t* lens, bool dry_run,
-                          bool cap_to_ws = false) {
+                          bool cap_to_ws = false, const AppendRows* app = nullptr) {
     bgtq::Geometry g;
     int rc = geometry(c, g);
     if (rc) return rc;
@@ -836,6 +845,19 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
     a.tiles_per_split = (int)((max_tiles + ns - 1) / ns);
     if (a.tiles_per_split < 1) a.tiles_per_split = 1;
     a.v_affine = c->v_mode == BGTQ_V_AFFINE;
+    if (app) {  // the last packed token of every sequence is written by this launch
+        a.app_k = app->k;
+        a.app_v = app->v;
+        a.app_dtype = app->dtype;
+        a.app_sB = app->sB;
+        a.app_sH = app->sH;
+        a.inv_sigma = c->inv_sigma + (size_t)layer * g.Hkv * 64;
+        a.app_k_codes = (uint8_t*)c->k_codes + (size_t)layer * g.k_codes_layer;
+        a.app_v_codes = (uint8_t*)c->v_codes + (size_t)layer * g.v_codes_layer;
+        a.app_k_scale = (uint16_t*)((uint8_t*)c->k_scale + (size_t)layer * g.k_scale_layer);
+        a.app_v_scale = (uint16_t*)((uint8_t*)c->v_scale + (size_t)layer * g.v_scale_layer);
+        a.app_v_zero = c->v_zero ? (uint16_t*)((uint8_t*)c->v_zero + (size_t)layer * g.v_scale_layer) : nullptr;
+    }
     {
         ProfScope ps(BGTQ_PROF_DECODE, s);
         e = uses_gtq_kernel(c, g.G) ? bgtq::launch_decode_gtq(a, g.B, g.R, c->v_bits, s)
@@ -893,10 +915,21 @@ int bgtq_decode_step(bgtq_cache* c, int layer, const void* k, const void* v, con
     int rc = quantize_append_impl(c, layer, k, v, dtype, n_new, strides, stream, true);
     if (rc) return rc;
     int64_t lens[BGTQ_MAX_BATCH];
-    const int64_t* nt = c->n_tokens + (size_t)layer * c->B;
+    int64_t* nt = c->n_tokens + (size_t)layer * c->B;
     for (int b = 0; b < c->B; ++b) lens[b] = nt[b] + n_new;
     rc = decode_attention_impl(c, layer, q, dtype, out, ws, ws_bytes, n_splits, stream, lens, true);
     if (rc) return rc;
+    // One token per sequence into a cache without an fp16 window, on the plan-driven kernel: the
+    // decode launch quantizes and writes the token itself (the wave whose tile holds it, while the
+    // tile is in flight) and attends to it; otherwise the append kernels run first.
+    if (n_new == 1 && !c->n_hp && c->n_recent == 0 && uses_gtq_kernel(c, c->Hq / c->Hkv)) {
+        const AppendRows rows{k, v, dtype, strides ? strides[0] : (int64_t)c->Hkv * D, strides ? strides[2] : D};
+        rc = decode_attention_impl(c, layer, q, dtype, out, ws, ws_bytes, n_splits, stream, lens, false, false,
+                                   &rows);
+        if (rc) return rc;
+        for (int b = 0; b < c->B; ++b) nt[b] = lens[b];
+        return ok();
+    }
     rc = quantize_append_impl(c, layer, k, v, dtype, n_new, strides, stream, false);
     if (rc) return rc;
     return decode_attention_impl(c, layer, q, dtype, out, ws, ws_bytes, n_splits, stream, nt, false);

@@ -53,6 +53,21 @@ struct DecodeArgs {
     int tiles_per_split;
     int v_affine;
     int32_t n_packed[BGTQ_MAXB];
+    // One-token append in the same launch (the plan-driven kernel, for bgtq_decode_step): with
+    // app_k set, the last packed token of every sequence (position n_packed - 1) is quantized
+    // from the rows app_k / app_v (element (b, h, j) at b * app_sB + h * app_sH + j, app_dtype)
+    // and written to the cache through the app_* pointers (the same buffers as above) by the wave
+    // whose tile holds it, which then attends to it with the rest of its tile.
+    const void* app_k;
+    const void* app_v;
+    int app_dtype;
+    int64_t app_sB, app_sH;
+    const float* inv_sigma;     // [Hkv][64] this layer's 1/sigma
+    uint8_t* app_k_codes;
+    uint8_t* app_v_codes;
+    uint16_t* app_k_scale;
+    uint16_t* app_v_scale;
+    uint16_t* app_v_zero;
 };
 
 struct CombineArgs {

@@ -1332,10 +1332,6 @@ __global__ __launch_bounds__(256, 2) void k_decode_fp16_mx(const Fp16Args a) {
     merge_waves4<G>(s_red, s_red + 4 * G * PART, part, a.n_parts, a.split0 + split);
 }
 
-// Merge split partials (o, m, l) of one (batch, query head) by log-sum-exp.  Grid: (row, slice of
-// 16 dims); thread s takes splits s, s + 256, ...  The first split's record is loaded together with
-// the maxima so one memory round trip covers the common case (at most 256 splits).
-constexpr int CMB_DIMS = 4;
 // Sum / max over all 64 lanes, returned wave-uniform: DPP rotations within each row of 16, then
 // row_bcast:15 and row_bcast:31 fold the rows into the last row, and lane 63 is read out.
 __device__ __forceinline__ float wave_total_sum(float v) {
@@ -1352,52 +1348,59 @@ __device__ __forceinline__ float wave_total_max(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-// Split merge: one wave per (query head row, 4 dims).  Lane l folds partials l, l + 64, ... with
-// an online log-sum-exp, U partials per round with their loads issued together, then the 64
-// lane states merge across the wave.
-template <int U>
-__global__ __launch_bounds__(64) void k_combine(const CombineArgs a) {
-    const int row = blockIdx.x, d0 = blockIdx.y * CMB_DIMS, lane = threadIdx.x;
+// Split merge by log-sum-exp, one workgroup of four waves per (batch, query head) row; lane l holds
+// dims 2l and 2l + 1.  Wave w folds chunks of CMB_CHUNK consecutive partials (chunks w, w + 4, ...):
+// lanes 0..CMB_CHUNK-1 load the chunk's maxima and sums, and every lane loads the chunk's o rows
+// (one coalesced 512-byte read per partial), all issued together; lane j computes the weight
+// e^(m_j - M) of partial j and readlane broadcasts it to the products.  A split without tokens
+// holds m = -inf, l = 0, o = 0 and weighs 0.  The four wave states merge through LDS.
+constexpr int CMB_CHUNK = 32;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void k_combine(const CombineArgs a) {
+    const int row = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const float* pr = a.part + (size_t)row * a.n_parts * PART;
-    float m = -INFINITY, acc[CMB_DIMS + 1];
+    float M = -INFINITY, L = 0.f, ox = 0.f, oy = 0.f;
+    for (int base = wave * CMB_CHUNK; base < a.n_parts; base += 4 * CMB_CHUNK) {
+        const int cnt = a.n_parts - base < CMB_CHUNK ? a.n_parts - base : CMB_CHUNK;
+        const float2 ml = *(const float2*)(pr + (size_t)(base + (lane < cnt ? lane : 0)) * PART + 128);
+        float2 ov[CMB_CHUNK];
 #pragma unroll
-    for (int j = 0; j <= CMB_DIMS; ++j) acc[j] = 0.f;
-    for (int s0 = 0; s0 < a.n_parts; s0 += 64 * U) {
-        float2 ml[U];
-        f32x4_t o4[U][CMB_DIMS / 4];
+        for (int j = 0; j < CMB_CHUNK; ++j)
+            ov[j] = *(const float2*)(pr + (size_t)(base + (j < cnt ? j : 0)) * PART + 2 * lane);
+        const float mj = lane < cnt ? ml.x : -INFINITY;
+        const float mn = fmaxf(M, wave_total_max(mj));  // -inf while every split so far is empty
+        const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+        const float f = mj == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mj - mn);
+        L = L * fo + wave_total_sum(f * ml.y);
+        ox *= fo;
+        oy *= fo;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int sp = s0 + 64 * u + lane;
-            const float* r = pr + (size_t)(sp < a.n_parts ? sp : 0) * PART;
-            ml[u] = *(const float2*)(r + 128);
-#pragma unroll
-            for (int k = 0; k < CMB_DIMS / 4; ++k) o4[u][k] = *(const f32x4_t*)(r + d0 + 4 * k);
-            if (sp >= a.n_parts) ml[u].x = -INFINITY;
+        for (int j = 0; j < CMB_CHUNK; ++j) {  // past cnt, f is 0 and ov[j] repeats the chunk's first row
+            const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+            ox = fmaf(fj, ov[j].x, ox);
+            oy = fmaf(fj, ov[j].y, oy);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (ml[u].x == -INFINITY) continue;  // past the end, or a split without tokens
-            const float mn = fmaxf(m, ml[u].x);
-            const float fo = __builtin_amdgcn_exp2f(m - mn), fn = __builtin_amdgcn_exp2f(ml[u].x - mn);
-            m = mn;
-#pragma unroll
-            for (int k = 0; k < CMB_DIMS / 4; ++k)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[4 * k + e] = acc[4 * k + e] * fo + fn * o4[u][k][e];
-            acc[CMB_DIMS] = acc[CMB_DIMS] * fo + fn * ml[u].y;
-        }
+        M = mn;
     }
-    const float M = wave_total_max(m);
-    const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-#pragma unroll
-    for (int j = 0; j <= CMB_DIMS; ++j) acc[j] = wave_total_sum(acc[j] * f);
+    __shared__ float s_m[4], s_l[4];
+    __shared__ float2 s_o[4][64];
     if (lane == 0) {
-        const float inv = 1.f / acc[CMB_DIMS];
-        float* dst = a.out + (size_t)row * D + d0;
+        s_m[wave] = M;
+        s_l[wave] = L;
+    }
+    s_o[wave][lane] = float2{ox, oy};
+    __syncthreads();
+    if (wave == 0) {
+        const float Mt = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+        float Lt = 0.f, rx = 0.f, ry = 0.f;
 #pragma unroll
-        for (int k = 0; k < CMB_DIMS / 4; ++k)
-            *(f32x4_t*)(dst + 4 * k) = f32x4_t{acc[4 * k] * inv, acc[4 * k + 1] * inv, acc[4 * k + 2] * inv,
-                                               acc[4 * k + 3] * inv};
+        for (int w = 0; w < 4; ++w) {
+            const float f = s_m[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[w] - Mt);
+            Lt += f * s_l[w];
+            rx += f * s_o[w][lane].x;
+            ry += f * s_o[w][lane].y;
+        }
+        const float inv = 1.f / Lt;
+        *(float2*)(a.out + (size_t)row * D + 2 * lane) = float2{rx * inv, ry * inv};
     }
 }
 
@@ -1435,22 +1438,11 @@ __global__ __launch_bounds__(256) void k_energy(const EnergyArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------------------------
+
 // ---------------------------------------------------------------------------------------------
 // Quantize-append.  The float32 steps are spelled out one IEEE operation at a time (no
-// contraction) so the codes and fp16 scales are reproducible bit for bit.
-__device__ __forceinline__ uint32_t tq_code(float x, float t, int w, const float* thr) {
-#pragma clang fp contract(off)
-    uint32_t code = 0;
-    const float* tb = thr + thr_base(w);
-    for (int st = w - 1; st >= 0; --st) {
-        const uint32_t cand = code + (1u << st);
-        const float th = t * tb[cand - 1];
-        if (x >= th) code = cand;
-    }
-    return code;
-}
-
+// contraction) so the codes and fp16 scales are reproducible bit for bit (tq_code and the
+// wave-wide row helpers are in bgtq_device.h).
 // One token's row in LDS, in the activation's own format (fp32, or the fp16 / bf16 bits, which
 // convert to fp32 exactly).
 template <typename XT> struct XRow {
@@ -1753,44 +1745,6 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
     }
 }
 
-__device__ __forceinline__ float lane_f(float v, int i) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i));
-}
-
-// The per-token fp16 RMS scale of a row spread over the wave (lane i holds elements 2i, 2i+1 and
-// the block's 1/sigma r): the same IEEE steps as rms_scale16, u = x*r, u*u, summed in element
-// order, each term read across lanes so the sequential sum waits on no memory.
-__device__ __forceinline__ float wave_rms16(float x0, float x1, float r, bool use_r, uint16_t* s16) {
-#pragma clang fp contract(off)
-    const float u0 = use_r ? x0 * r : x0, u1 = use_r ? x1 * r : x1;
-    const float q0 = u0 * u0, q1 = u1 * u1;
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-        acc = acc + lane_f(q0, i);
-        acc = acc + lane_f(q1, i);
-    }
-    const float ms = acc / 128.0f;
-    const uint16_t h = f2h(sqrtf(ms));
-    *s16 = h;
-    return h2f(h);
-}
-
-// min and max of elements [j0, j0 + n) of a row spread over the wave, folded in element order
-// from element j0 (the order affine_group takes); j0 and n are wave-uniform, n even.
-__device__ __forceinline__ void wave_minmax(float x0, float x1, int j0, int n, float& mn, float& mx) {
-    mn = mx = lane_f(x0, j0 >> 1);
-    mx = fmaxf(mx, lane_f(x1, j0 >> 1));
-    mn = fminf(mn, lane_f(x1, j0 >> 1));
-    for (int i = (j0 >> 1) + 1; i < ((j0 + n) >> 1); ++i) {
-        const float a = lane_f(x0, i), c = lane_f(x1, i);
-        mn = fminf(mn, a);
-        mx = fmaxf(mx, a);
-        mn = fminf(mn, c);
-        mx = fmaxf(mx, c);
-    }
-}
-
 // Quantize-append of a few tokens: one workgroup (one wave) per (tile, kv head, sequence) takes
 // the tile's new tokens one after another, the whole wave on each token (lane i holds RoPE block i,
 // dims 2i and 2i+1), so one new token costs a few short chains instead of one lane's full
@@ -1997,11 +1951,7 @@ thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s) {
     if (!a.part || !a.out || a.n_parts < 1 || a.n_parts > BGTQ_MAX_PARTS) return hipErrorInvalidValue;
-    // partials per lane per round: no more loads than there are partials
-    const dim3 grid(rows, D / CMB_DIMS);
-    if (a.n_parts <= 64) hipLaunchKernelGGL(k_combine<1>, grid, dim3(64), 0, s, a);
-    else if (a.n_parts <= 128) hipLaunchKernelGGL(k_combine<2>, grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL(k_combine<4>, grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_combine, dim3(rows), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -62,6 +62,16 @@ hipError_t launch_decode_gtq(const DecodeArgs& a, int B, int R, int v_bits, hipS
     if (!a.plan) return bad("decode: null plan");
     if (a.G != 4 && a.G != 8) return bad("decode: group size of the plan-driven decode");
     if (hipError_t e = check_decode(a, B, BGTQ_K_BLOCKGTQ, R, v_bits)) return e;
+    if (a.app_k) {
+        if (!a.app_v || !a.inv_sigma || !a.app_k_codes || !a.app_v_codes || !a.app_k_scale || !a.app_v_scale ||
+            (a.v_affine && !a.app_v_zero))
+            return bad("decode: append pointers");
+        if (a.app_dtype < 0 || a.app_dtype > 2) return bad("decode: append dtype");
+        for (int b = 0; b < B; ++b)
+            if (a.n_packed[b] < 1) return bad("decode: append into an empty sequence");
+        note("decode_gtq_append");
+        return hipSuccess;
+    }
     note("decode_gtq");
     return hipSuccess;
 }

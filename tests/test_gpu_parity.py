@@ -397,6 +397,49 @@ def test_decode_step_matches_append_then_attend(name):
     _compare_cache(cache, oc, w)
 
 
+FUSED_CASES = {
+    # name: (workload id, overrides, prefill tokens, one-token steps, n_splits per step).  One token
+    # per sequence on the plan-driven kernel is quantized inside the decode launch; these cover its
+    # eight-wave looping kernel (more than 16 tiles per split), affine and 4-bit values, fp16 rows,
+    # 4 query heads per kv head with two sequences, and tokens at the last position of a tile and at
+    # the first position of a new one.
+    "g8_looping_kernel": (2, {"L": 1}, 2046, 3, (1, 2, 1)),
+    "g8_affine_values": (2, {"L": 1, "v_mode": "affine"}, 127, 3, (0, 1, 3)),
+    "g8_k4v4_f16": (2, {"L": 1, "v_bits": 4, "k_budget_units": 256, "dtype": "f16"}, 190, 3, (0, 2, 1)),
+    "g4_two_sequences": (3, {"L": 1, "B": 2}, 1300, 2, (0, 1)),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED_CASES))
+def test_fused_decode_step(name):
+    """One-token decode steps that the decode launch appends itself: every output matches the
+    oracle over the grown context and the cache ends bit-exact (codes, scales, value streams)."""
+    wid, ov, n0, n_steps, splits = FUSED_CASES[name]
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
+    N = n0 + n_steps
+    print(f"[fused step {name}] prefill={n0} steps={n_steps} B={w.B} Hq={w.Hq} Hkv={w.Hkv}", flush=True)
+    n_cap = ((N + 63) // 64 + 1) * 64
+    m = T.meta(w, 0)
+    K, V, _ = T.inputs(w, 0, N)
+    cache = T.gpu_cache(w, n_cap)
+    cache.set_metadata(0, m.bits, m.sigma, m.r)
+    T.append_all(cache, 0, K[:, :, :n0], V[:, :, :n0], w.dtype)
+    kd = T.to_dev(np.transpose(K, (0, 2, 1, 3)), w.dtype)        # [B, N, Hkv, d]
+    vd = T.to_dev(np.transpose(V, (0, 2, 1, 3)), w.dtype)
+    pos = n0
+    for i in range(n_steps):
+        q = np.stack([np.concatenate([synth.queries(w, 0, h, b, pos + 1) for h in range(w.Hkv)])
+                      for b in range(w.B)])
+        out = cache.decode_step(0, kd[:, pos:pos + 1], vd[:, pos:pos + 1], T.to_dev(q, w.dtype), n_splits=splits[i])
+        torch.cuda.synchronize()
+        pos += 1
+        assert (cache.n_tokens[0] == pos).all()
+        oc = T.oracle_layer(w, K[:, :, :pos], V[:, :, :pos], m, n_cap)
+        e = T.assert_close(out.cpu().numpy(), pipeline.decode_layer(oc, q), f"{name} step {i} (context {pos})")
+        print(f"  step {i}: context {pos}, splits {splits[i]}, max abs err {e:.2e}", flush=True)
+    _compare_cache(cache, oc, w)
+
+
 FEW_CASES = {
     # name: (workload id, overrides, N, chunk sizes).  Appends of at most 16 positions per sequence
     # take the one-token-per-wave kernel; every format it covers, appended a few tokens at a time

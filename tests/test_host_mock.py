@@ -107,24 +107,30 @@ def test_fp16_comparator_arguments(mock):
 
 @pytest.mark.parametrize("fmt", range(len(FORMATS)))
 def test_decode_step_appends_then_attends(mock, fmt):
-    """The combined step enqueues the append's launches before the attention's and matches the lengths
-    that the two separate calls leave."""
+    """The combined step matches the lengths that the two separate calls leave.  One token per
+    sequence on the plan-driven kernel without an fp16 window is written by the decode launch itself
+    (one decode launch and the merge); otherwise the append's launches come before the attention's."""
     nt = np.zeros((2, 2), np.int64)
-    d = _desc(nt, **FORMATS[fmt])
+    f = FORMATS[fmt]
+    d = _desc(nt, **f)
     q = C.c_void_p(FAKE + 0x50000000)
     ws = C.c_void_p(FAKE + 0x60000000)
     need = mock.bgtq_decode_workspace_bytes(C.byref(d), 0)
+    fusable = f.get("k_mode", 0) == 0 and f.get("Hq", 16) // f.get("Hkv", 2) >= 4 and not f.get("n_recent", 0)
     total = 0
     for n_new in (1, 1, 63, 200, 1):
         mock.bgtq_mock_reset()
         log = _call_ok(mock, mock.bgtq_decode_step(C.byref(d), 1, q, q, q, 2, n_new, None, q, ws, need, 0, None))
         total += n_new
-        assert log.count("decode") == 1 and log.count("combine") == 1
-        first_decode = log.index("decode")
-        for tag in ("quant", "ring"):
-            if tag in log:
-                assert log.index(tag) < first_decode, log
-        assert "quant" in log or "ring" in log
+        if fusable and n_new == 1:
+            assert log.split() == ["decode_gtq_append", "combine"], log
+        else:
+            assert log.count("decode") == 1 and log.count("combine") == 1 and "append" not in log
+            first_decode = log.index("decode")
+            for tag in ("quant", "ring"):
+                if tag in log:
+                    assert log.index(tag) < first_decode, log
+            assert "quant" in log or "ring" in log
         assert (nt[1] == total).all() and (nt[0] == 0).all()
 
 
