@@ -83,3 +83,12 @@ def unrotate_keys(k_rot: np.ndarray, signs: np.ndarray) -> np.ndarray:
     """Inverse of the key rotation y = H (s * x) / 16 in float64: x = s * (H y) / 8 (H H = 128 I)."""
     H = hadamard_matrix(k_rot.shape[-1])
     return np.asarray(signs, np.float64) * (np.asarray(k_rot, np.float64) @ H.T) / 8.0
+
+
+def unrotate_output(o_rot: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """Undo the value rotation once, on the attention output ("Quantize What Counts" summary,
+    Results, rotation integration: values rotated before quantization).  With values stored as
+    y_t = H (s * v_t) / 16, the output over them is o' = sum_t p_t y_t / sum_t p_t = H (s * o) / 16
+    by linearity, so o = s * (H o') / 8 (H H = 128 I), in float64."""
+    H = hadamard_matrix(o_rot.shape[-1])
+    return np.asarray(signs, np.float64) * (np.asarray(o_rot, np.float64) @ H.T) / 8.0

@@ -60,16 +60,22 @@ class LayerCache:
     k_group: int
     meta: LayerMeta | None
     k_rot: np.ndarray | None = None   # +-1 [Hkv, d]: affine keys stored rotated (y = H (s * k) / 16)
+    v_rot: np.ndarray | None = None   # +-1 [Hkv, d]: values stored rotated (y = H (s * v) / 16)
 
 
 def build_layer(k_rows, v_rows, *, k_mode: str, v_mode: str, v_bits: int, n_cap: int,
                 meta: LayerMeta | None = None, k_bits: int = 4, k_group: int = 32,
-                n_recent: int = 0, k_rot=None) -> LayerCache:
+                n_recent: int = 0, k_rot=None, v_rot=None) -> LayerCache:
     """k_rows, v_rows: float32 [B, Hkv, N, d] (dtype-exact values), all N tokens appended.
     k_rot: optional +-1 signs [Hkv, d]; affine keys are then rotated before quantization (the
-    fp16 recent buffer keeps the rows as they came)."""
+    fp16 recent buffer keeps the rows as they came).  v_rot: optional +-1 signs [Hkv, d]; values
+    are then rotated the same way before quantization, and decode_layer undoes the rotation once
+    on the output (caches without an fp16 recent buffer only: its rows would sit in the other
+    space)."""
     if k_rot is not None and k_mode != "affine":
         raise ValueError("the key rotation applies to affine keys")
+    if v_rot is not None and n_recent:
+        raise ValueError("the value rotation applies to caches without an fp16 recent buffer")
     k_rows = np.asarray(k_rows, np.float32)
     v_rows = np.asarray(v_rows, np.float32)
     B, H, N, d = k_rows.shape
@@ -96,6 +102,8 @@ def build_layer(k_rows, v_rows, *, k_mode: str, v_mode: str, v_bits: int, n_cap:
         for h in range(H):
             xk = k_rows[b, h, :n_packed]
             xv = v_rows[b, h, :n_packed]
+            if v_rot is not None:
+                xv = quantize.hadamard_rotate_f32(xv, v_rot[h])
             if k_mode == "gtq":
                 codes, S = quantize.quantize_k_gtq(xk, meta.sigma[h], meta.r[h], meta.bits[h])
                 words = layout.k_gtq_words(codes, meta.bits[h])
@@ -121,7 +129,8 @@ def build_layer(k_rows, v_rows, *, k_mode: str, v_mode: str, v_bits: int, n_cap:
                 recent_v[b, h, pos % n_recent] = v_rows[b, h, pos].astype(np.float16)
     return LayerCache(k_mode, v_mode, n_packed, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero,
                       recent_k, recent_v, n_rec, v_bits, k_bits, k_group, meta,
-                      None if k_rot is None else np.asarray(k_rot, np.float64))
+                      None if k_rot is None else np.asarray(k_rot, np.float64),
+                      None if v_rot is None else np.asarray(v_rot, np.float64))
 
 
 def dequant_head(c: LayerCache, b: int, h: int):
@@ -162,7 +171,10 @@ def decode_layer(c: LayerCache, q) -> np.ndarray:
     for b in range(B):
         for h in range(H):
             K, V = dequant_head(c, b, h)
-            out[b, h * g:(h + 1) * g] = attention.attend(q[b, h * g:(h + 1) * g], K, V)
+            o = attention.attend(q[b, h * g:(h + 1) * g], K, V)
+            if c.v_rot is not None:   # V holds rotated values: undo the rotation once, on the output
+                o = attention.unrotate_output(o, c.v_rot[h])
+            out[b, h * g:(h + 1) * g] = o
     return out
 
 

@@ -111,11 +111,12 @@ def quantize_affine(x: np.ndarray, b: int, group: int):
 
 
 def hadamard_rotate_f32(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
-    """Key rotation before affine quantization: y = H (s * x) / 16 in float32.
+    """Rotation of rows before quantization (affine keys, or values): y = H (s * x) / 16 in float32.
 
     The "Quantize What Counts" summary (Results, rotation integration) reports that rotating the
     keys alone, in the K4V2 setting, brings accuracy close to K4V4 (rotation spreads key outlier
-    channels over a group), while rotating values alone helps little; it names no rotation.
+    channels over a group), while rotating the values alone gives marginal or negative results; it
+    names no rotation.
     Reading: a randomized Hadamard rotation, H the 128x128 Sylvester Hadamard matrix, s a
     caller-given +-1 sign per coordinate.  H (s * x) is computed by the fast transform with stages
     h = 1, 2, 4, ..., 64 in that order; at stage h each pair (j, j + h) with bit h of j clear

@@ -217,3 +217,85 @@ def test_rotated_affine_pipeline_matches_direct():
         Vx = pipeline.dequant_head(oc, 0, h)[1]
         ref = attention.attend(q[0, 4 * h:4 * (h + 1)].astype(np.float64), Kx, Vx)
         np.testing.assert_allclose(out[0, 4 * h:4 * (h + 1)], ref, rtol=1e-12, atol=1e-12)
+
+
+# --- value rotation ---
+
+def test_hadamard_matrix_is_sylvester():
+    """The oracle's Hadamard matrix is the Sylvester construction scipy builds."""
+    from scipy.linalg import hadamard
+    np.testing.assert_array_equal(attention.hadamard_matrix(128), hadamard(128))
+
+
+def test_value_rotation_undone_once_on_the_output():
+    """Values stored as y = H (s * v) / 16: attention over y, then s * (H o') / 8, equals attention
+    over v (linearity); the signs go after the transform on the way back (before it, the output
+    is wrong for random signs)."""
+    rng = np.random.default_rng(21)
+    s = _signs(22)
+    H = attention.hadamard_matrix()
+    q = rng.standard_normal((4, 128)) * 2
+    K = rng.standard_normal((70, 128))
+    V = rng.standard_normal((70, 128))
+    Y = (V * s) @ H.T / 16                                            # fp64 rotation of every row
+    o_rot = attention.attend(q, K, Y)
+    np.testing.assert_allclose(attention.unrotate_output(o_rot, s), attention.attend(q, K, V), rtol=1e-12, atol=1e-12)
+    wrong = (o_rot * s) @ H.T / 8
+    assert np.max(np.abs(wrong - attention.attend(q, K, V))) > 1e-2
+    np.testing.assert_allclose(attention.unrotate_output(Y, s), V, atol=1e-12)
+
+
+@pytest.mark.parametrize("v_mode,v_bits", [("codebook", 3), ("affine", 2)])
+def test_value_rotation_pipeline(v_mode, v_bits):
+    """A layer with rotated values stores the codes of the rotated rows (fp32 fast transform) and
+    decodes to attention over those values dequantized, rotated back once on the output."""
+    from oracle import quantize
+    w = synth.reduced(synth.WORKLOADS[2], L=1, v_mode=v_mode, v_bits=v_bits)
+    N = 200
+    m = pipeline.calibrate(*zip(*[synth.calibration(w, 0, h) for h in range(w.Hkv)]), w.k_budget_units)
+    K = np.stack([synth.keys(w, 0, h, 0, N) for h in range(w.Hkv)])[None]
+    V = np.stack([synth.values(w, 0, h, 0, N) for h in range(w.Hkv)])[None]
+    q = np.concatenate([synth.queries(w, 0, h, 0, N) for h in range(w.Hkv)])[None]
+    s = np.stack([_signs(30 + h) for h in range(w.Hkv)])
+    c = pipeline.build_layer(K, V, k_mode="gtq", v_mode=v_mode, v_bits=v_bits, n_cap=256, meta=m, v_rot=s)
+    for h in range(w.Hkv):
+        y = quantize.hadamard_rotate_f32(V[0, h], s[h])
+        if v_mode == "codebook":
+            codes, S = quantize.quantize_v(y, v_bits)
+            np.testing.assert_array_equal(c.v_scale[0, h, :N].view(np.uint16), S.view(np.uint16))
+        else:
+            codes, sc, zr = quantize.quantize_affine(y, v_bits, 128)
+            np.testing.assert_array_equal(c.v_scale[0, h, :N].view(np.uint16), sc[:, 0].view(np.uint16))
+        np.testing.assert_array_equal(layout.v_codes(c.v_codes[0, h], v_bits, N), codes)
+    out = pipeline.decode_layer(c, q)
+    for h in range(w.Hkv):
+        Kh, Yh = pipeline.dequant_head(c, 0, h)
+        g = w.Hq // w.Hkv
+        ref = attention.unrotate_output(attention.attend(q[0, h * g:(h + 1) * g].astype(np.float64), Kh, Yh), s[h])
+        np.testing.assert_allclose(out[0, h * g:(h + 1) * g], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_value_rotation_at_high_width_tracks_exact_attention():
+    """8-bit codebook values under the rotation: the decode stays as close to attention over the
+    unquantized values as the unrotated layer does (the rotation is undone, not left on the
+    output, where the error would be of the output's own size)."""
+    w = synth.reduced(synth.WORKLOADS[2], L=1, Hkv=1, Hq=8, v_bits=8)
+    N = 150
+    m = pipeline.calibrate(*zip(*[synth.calibration(w, 0, 0)]), w.k_budget_units)
+    K = synth.keys(w, 0, 0, 0, N)[None, None]
+    V = synth.values(w, 0, 0, 0, N)[None, None]
+    q = synth.queries(w, 0, 0, 0, N)[None]
+    err = {}
+    for rot in (None, _signs(40)[None]):
+        c = pipeline.build_layer(K, V, k_mode="gtq", v_mode="codebook", v_bits=8, n_cap=192, meta=m, v_rot=rot)
+        Kh, _ = pipeline.dequant_head(c, 0, 0)
+        exact = attention.attend(q[0].astype(np.float64), Kh, V[0, 0].astype(np.float64))
+        err[rot is None] = np.max(np.abs(pipeline.decode_layer(c, q)[0] - exact))
+    assert err[False] < 2 * err[True] and err[False] < 0.1 < np.abs(exact).max()
+
+
+def test_value_rotation_refuses_the_fp16_window():
+    K = np.zeros((1, 1, 10, 128), np.float32)
+    with pytest.raises(ValueError):
+        pipeline.build_layer(K, K, k_mode="affine", v_mode="affine", v_bits=2, n_cap=64, n_recent=4,
+                             v_rot=np.ones((1, 128)))
