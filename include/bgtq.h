@@ -105,6 +105,12 @@ enum {
  *     matrix, fast transform in stages 1, 2, ..., 64, fp32), and decode rotates the query to
  *     H (s * q) / 8 so that the logits are unchanged; the fp16 recent ring keeps rows unrotated.
  *     NULL disables it.  With Block-GTQ keys it is BGTQ_E_UNSUPPORTED.
+ *   v_rot     uint8 [L][Hkv][16] or NULL: sign bits s_j (as k_rot) of a randomized Hadamard
+ *     rotation of the values ("Quantize What Counts" summary, Results: the summary finds rotating
+ *     the values alone marginal or harmful; offered for comparison).  Each appended value row is
+ *     stored as y = H (s * v) / 16 (the transform of k_rot, fp32) and quantized; the split merge
+ *     undoes the rotation once on the output, o = s * (H o') / 8.  Any key format; not with an fp16
+ *     window (n_recent > 0 or a log-based filter): BGTQ_E_UNSUPPORTED.  NULL disables it.
  *   decode_path  BGTQ_DECODE_AUTO or BGTQ_DECODE_VECTOR (plain value, not a buffer): which decode
  *     kernels bgtq_decode_attention runs.  Both compute the same attention to the same tolerance;
  *     VECTOR keeps every product on the vector ALUs (no matrix-core instructions), for comparison
@@ -144,6 +150,7 @@ typedef struct bgtq_cache {
     int32_t *n_hp;
     void *plan;
     int32_t decode_path;
+    const uint8_t *v_rot;
 } bgtq_cache;
 
 /* Thread-local text describing the last non-OK status of this thread ("" if none). */

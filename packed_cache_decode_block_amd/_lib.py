@@ -42,7 +42,8 @@ class CacheDesc(C.Structure):
                 ("v_scale", C.c_void_p), ("v_zero", C.c_void_p), ("recent_k", C.c_void_p), ("recent_v", C.c_void_p),
                 ("bits", C.c_void_p), ("sigma", C.c_void_p), ("inv_sigma", C.c_void_p),
                 ("n_tokens", C.POINTER(C.c_int64)), ("k_rot", C.c_void_p),
-                ("n_hp", C.POINTER(C.c_int32)), ("plan", C.c_void_p), ("decode_path", C.c_int32)]
+                ("n_hp", C.POINTER(C.c_int32)), ("plan", C.c_void_p), ("decode_path", C.c_int32),
+                ("v_rot", C.c_void_p)]
 
 
 def bind(path: str, optional=()):

@@ -123,11 +123,12 @@ class PackedCache:
 
     def __init__(self, *, L, B, Hq, Hkv, n_cap, k_mode=_lib.K_BLOCKGTQ, budget_units=128, k_bits=4, k_group=32,
                  v_mode=_lib.V_CODEBOOK, v_bits=2, n_recent=0, k_rotation=False, logquant_w=None, device="cuda",
-                 zero=True, decode_path=_lib.DECODE_AUTO):
+                 zero=True, decode_path=_lib.DECODE_AUTO, v_rotation=False):
         """logquant_w: base window W of LogQuant's log-based filter; the recent buffers then hold the
         3W-row high-precision store (n_recent = 3W) and appends go through logquant_append.
         decode_path: DECODE_AUTO (the library's kernel choice) or DECODE_VECTOR (every product on the
-        vector ALUs); also settable later through the attribute of the same name."""
+        vector ALUs); also settable later through the attribute of the same name.
+        v_rotation: values stored under a randomized Hadamard rotation (set_value_rotation)."""
         torch = _torch()
         if logquant_w is not None:
             n_recent = 3 * int(logquant_w)
@@ -167,10 +168,12 @@ class PackedCache:
         # sign bits of the randomized Hadamard key rotation (affine keys), [L, Hkv, 16]; see
         # set_key_rotation.  All signs +1 until set.
         self.k_rot = torch.zeros((L, Hkv, 16), dtype=torch.uint8, device=device) if k_rotation else None
+        # sign bits of the value rotation, [L, Hkv, 16]; see set_value_rotation
+        self.v_rot = torch.zeros((L, Hkv, 16), dtype=torch.uint8, device=device) if v_rotation else None
         # decode plan of each layer (Block-GTQ keys), written by bgtq_prepare_metadata in set_metadata
         self.plan = buf(_lib.BUF_PLAN, torch.uint8)
         for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "recent_k", "recent_v",
-                     "bits", "sigma", "inv_sigma", "k_rot", "plan"):
+                     "bits", "sigma", "inv_sigma", "k_rot", "plan", "v_rot"):
             setattr(d, name, _ptr(getattr(self, name)))
         self._ws = None
 
@@ -185,6 +188,18 @@ class PackedCache:
             raise ValueError("signs must be [Hkv, 128] of +1 / -1")
         packed = np.packbits((sg < 0).astype(np.uint8), axis=1, bitorder="little")
         self.k_rot[layer].copy_(torch.from_numpy(packed))
+
+    def set_value_rotation(self, layer: int, signs):
+        """Signs s [Hkv, 128] (+1 / -1, host) of the value rotation of one layer: values are stored
+        as H (s * v) / 16 and the decode output is rotated back to s * (H o') / 8."""
+        torch = _torch()
+        if self.v_rot is None:
+            raise ValueError("the cache was created without v_rotation")
+        sg = np.asarray(signs)
+        if sg.shape != (self.desc.Hkv, 128) or not np.all(np.abs(sg) == 1):
+            raise ValueError("signs must be [Hkv, 128] of +1 / -1")
+        packed = np.packbits((sg < 0).astype(np.uint8), axis=1, bitorder="little")
+        self.v_rot[layer].copy_(torch.from_numpy(packed))
 
     def set_metadata(self, layer: int, bits, sigma, inv_sigma):
         """Upload per-(kv head, block) widths and key scales of one layer (host arrays [Hkv, 64])."""

@@ -76,6 +76,8 @@ int geometry(const bgtq_cache* c, bgtq::Geometry& g) {
     }
     if (c->k_rot && c->k_mode != BGTQ_K_AFFINE)
         return fail(BGTQ_E_UNSUPPORTED, "the key rotation applies to affine keys only");
+    if (c->v_rot && (c->n_recent > 0 || c->n_hp))
+        return fail(BGTQ_E_UNSUPPORTED, "the value rotation applies to caches without an fp16 window");
     if (c->v_mode != BGTQ_V_CODEBOOK && c->v_mode != BGTQ_V_AFFINE) return fail(BGTQ_E_INVALID, "unknown v_mode");
     if (c->v_bits < 1 || c->v_bits > 4) return fail(BGTQ_E_INVALID, "v_bits must be in 1..4");
     g.v_mode = c->v_mode;
@@ -444,6 +446,7 @@ void fill_quant_layer(const bgtq_cache* c, const bgtq::Geometry& g, int layer, b
         q.inv_sigma = c->inv_sigma + (size_t)layer * g.Hkv * 64;
     }
     q.k_rot = c->k_rot ? c->k_rot + (size_t)layer * g.Hkv * 16 : nullptr;
+    q.v_rot = c->v_rot ? c->v_rot + (size_t)layer * g.Hkv * 16 : nullptr;
     q.Hkv = g.Hkv;
     q.n_cap = g.n_cap;
     q.n_tiles = g.n_tiles;
@@ -868,7 +871,7 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
         e = bgtq::launch_fp16(ra, g.B, s);
         if (e != hipSuccess) return hip_fail(e, "recent-ring decode launch");
     }
-    bgtq::CombineArgs ca{part, out, parts};
+    bgtq::CombineArgs ca{part, out, parts, c->v_rot ? c->v_rot + (size_t)layer * g.Hkv * 16 : nullptr, g.Hq, g.G};
     e = bgtq::launch_combine(ca, g.B * g.Hq, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return ok();
@@ -922,7 +925,7 @@ int bgtq_decode_step(bgtq_cache* c, int layer, const void* k, const void* v, con
     // One token per sequence into a cache without an fp16 window, on the plan-driven kernel: the
     // decode launch quantizes and writes the token itself (the wave whose tile holds it, while the
     // tile is in flight) and attends to it; otherwise the append kernels run first.
-    if (n_new == 1 && !c->n_hp && c->n_recent == 0 && uses_gtq_kernel(c, c->Hq / c->Hkv)) {
+    if (n_new == 1 && !c->n_hp && c->n_recent == 0 && !c->v_rot && uses_gtq_kernel(c, c->Hq / c->Hkv)) {
         const AppendRows rows{k, v, dtype, strides ? strides[0] : (int64_t)c->Hkv * D, strides ? strides[2] : D};
         rc = decode_attention_impl(c, layer, q, dtype, out, ws, ws_bytes, n_splits, stream, lens, false, false,
                                    &rows);
@@ -986,7 +989,7 @@ int bgtq_fp16_decode_attention(const void* k16, const void* v16, int64_t N, int 
         e = bgtq::launch_fp16(a, B, s);
     }
     if (e != hipSuccess) return hip_fail(e, "fp16 decode launch");
-    bgtq::CombineArgs ca{part, out, ns};
+    bgtq::CombineArgs ca{part, out, ns, nullptr, Hq, Hq / Hkv};
     e = bgtq::launch_combine(ca, B * Hq, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return ok();

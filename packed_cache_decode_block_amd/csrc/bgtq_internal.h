@@ -74,6 +74,8 @@ struct CombineArgs {
     const float* part;          // [B*Hq][n_parts][132]
     float* out;                 // [B*Hq][128]
     int n_parts;
+    const uint8_t* v_rot;       // [Hkv][16] sign bits of the value rotation of this layer, or null
+    int Hq, G;                  // with v_rot: row r is query head r % Hq of kv head (r % Hq) / G
 };
 
 // fp16 tiles: rows [B][Hkv][rows][128] fp16.  Used for the unquantized comparator (all splits)
@@ -122,6 +124,7 @@ struct QuantArgs {
     const float* sigma;
     const float* inv_sigma;
     const uint8_t* k_rot;       // [Hkv][16] sign bits of the key rotation (affine keys), or null
+    const uint8_t* v_rot;       // [Hkv][16] sign bits of the value rotation, or null
     int Hkv;
     int64_t n_cap, n_tiles, k_tile_bytes, v_tile_bytes;
     int k_mode, R, k_bits, k_group;

@@ -1400,7 +1400,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
             ry += f * s_o[w][lane].y;
         }
         const float inv = 1.f / Lt;
-        *(float2*)(a.out + (size_t)row * D + 2 * lane) = float2{rx * inv, ry * inv};
+        float o0 = rx * inv, o1 = ry * inv;
+        if (a.v_rot) {
+            // values stored as H (s * v) / 16: the output is rotated back once, o = s * (H o') / 8
+            // (lane holds dims 2 lane and 2 lane + 1: stage 1 inside the lane, stages 2..64 with
+            // lane ^ m, the lower lane keeping a + b, the upper one a - b)
+            const int hq = row % a.Hq;
+            const uint32_t sb = (uint32_t)a.v_rot[(hq / a.G) * 16 + (lane >> 2)] >> (2 * (lane & 3));
+            float u = o0 + o1, v = o0 - o1;
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) {
+                const float pu = __shfl_xor(u, m, 64), pv = __shfl_xor(v, m, 64);
+                const bool upper = (lane & m) != 0;
+                u = upper ? pu - u : u + pu;
+                v = upper ? pv - v : v + pv;
+            }
+            o0 = (sb & 1u) ? -(u * 0.125f) : u * 0.125f;
+            o1 = (sb & 2u) ? -(v * 0.125f) : v * 0.125f;
+        }
+        *(float2*)(a.out + (size_t)row * D + 2 * lane) = float2{o0, o1};
     }
 }
 
@@ -1532,9 +1550,9 @@ __device__ __forceinline__ void affine_group(const X& x, int n, int bits, uint16
 // uint16_t bits for fp16 / bf16), padded to an odd number of dwords so that the per-lane row
 // reads of the quantizer hit distinct banks.  Value codes overwrite their own row in place (code
 // j lands in bytes the row's elements 0..j already vacated).
-// ROT: affine keys stored rotated, y = H (s * k) / 16 (s from QuantArgs::k_rot): the row is
-// rotated in registers by the fast transform (stages 1, 2, ..., 64, one fp32 addition or
-// subtraction per output, the final 1/16 exact) and staged as fp32 for the affine groups.
+// ROT: affine keys and / or values stored rotated, y = H (s * x) / 16 (s from QuantArgs::k_rot,
+// v_rot): the row is rotated in registers by the fast transform (stages 1, 2, ..., 64, one fp32
+// addition or subtraction per output, the final 1/16 exact) and staged as fp32 for the quantizer.
 template <typename XT, bool ROT>
 __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
     constexpr int XS = sizeof(XT) == 4 ? D + 1 : D + 2;  // row stride in elements (129 dwords / 65 dwords)
@@ -1547,7 +1565,7 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
     const bool active = pos >= a.pos_lo[b] && pos < a.pos_hi[b];
     __shared__ float s_thr[BGTQ_CB_THRESHOLDS];
     __shared__ __attribute__((aligned(16))) XT s_x[64 * XS];
-    __shared__ float s_y[ROT ? 64 * (D + 1) : 1];  // rotated key rows (ROT only)
+    __shared__ float s_y[ROT ? 64 * (D + 1) : 1];  // rotated rows (ROT only)
     __shared__ int s_order[64];
     __shared__ int s_wid[64];
     __shared__ float s_r[64], s_sig[64];
@@ -1609,6 +1627,34 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
         }
         __syncthreads();
         const XRow<XT> x{s_x + lane * XS, a.dtype};
+        // The row rotated to y = H (s * x) / 16 (fast transform: stages 1, 2, ..., 64, one fp32
+        // addition or subtraction per output, the 1/16 exact), staged as fp32 in this lane's row of
+        // s_y; sg: the (layer, kv head)'s sign bits.
+        auto rotate_row = [&](const uint8_t* sg) -> const float* {
+            float y[D];
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                const float v = x[j];
+                y[j] = ((sg[j >> 3] >> (j & 7)) & 1u) ? -v : v;
+            }
+#pragma unroll
+            for (int hs = 1; hs < D; hs <<= 1) {
+#pragma unroll
+                for (int i0 = 0; i0 < D; i0 += 2 * hs) {
+#pragma unroll
+                    for (int j = i0; j < i0 + hs; ++j) {
+#pragma clang fp contract(off)
+                        const float p = y[j], r = y[j + hs];
+                        y[j] = p + r;
+                        y[j + hs] = p - r;
+                    }
+                }
+            }
+            float* yr = s_y + lane * (D + 1);
+#pragma unroll
+            for (int j = 0; j < D; ++j) yr[j] = y[j] * 0.0625f;
+            return yr;
+        };
         if (pass == 0) {
             // ---- keys
             uint32_t* kt = (uint32_t*)(a.k_codes + (bh * a.n_tiles + tile) * a.k_tile_bytes);
@@ -1653,30 +1699,8 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
                     }
                 };
                 if constexpr (ROT) {
-                    const uint8_t* sg = a.k_rot + h * 16;
-                    float y[D];
-#pragma unroll
-                    for (int j = 0; j < D; ++j) {
-                        const float v = x[j];
-                        y[j] = ((sg[j >> 3] >> (j & 7)) & 1u) ? -v : v;
-                    }
-#pragma unroll
-                    for (int hs = 1; hs < D; hs <<= 1) {
-#pragma unroll
-                        for (int i0 = 0; i0 < D; i0 += 2 * hs) {
-#pragma unroll
-                            for (int j = i0; j < i0 + hs; ++j) {
-#pragma clang fp contract(off)
-                                const float p = y[j], r = y[j + hs];
-                                y[j] = p + r;
-                                y[j + hs] = p - r;
-                            }
-                        }
-                    }
-                    float* yr = s_y + lane * (D + 1);
-#pragma unroll
-                    for (int j = 0; j < D; ++j) yr[j] = y[j] * 0.0625f;
-                    groups(XRow<float>{yr, BGTQ_F32});
+                    if (a.k_rot) groups(XRow<float>{rotate_row(a.k_rot + h * 16), BGTQ_F32});
+                    else groups(x);
                 } else {
                     groups(x);
                 }
@@ -1695,18 +1719,26 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
             const int vb = a.v_bits;
             uint16_t s16 = 0, z16 = 0;
             uint8_t* cr = (uint8_t*)(s_x + lane * XS);
-            if (a.v_mode == BGTQ_V_CODEBOOK) {
-                const float S = rms_scale16(x, nullptr, &s16);
-                switch (vb) {
-                    case 1: v_codes_row<1>(x, S, active, cr, s_thr); break;
-                    case 2: v_codes_row<2>(x, S, active, cr, s_thr); break;
-                    case 3: v_codes_row<3>(x, S, active, cr, s_thr); break;
-                    default: v_codes_row<4>(x, S, active, cr, s_thr); break;
+            auto vquant = [&](const auto& xr) {
+                if (a.v_mode == BGTQ_V_CODEBOOK) {
+                    const float S = rms_scale16(xr, nullptr, &s16);
+                    switch (vb) {
+                        case 1: v_codes_row<1>(xr, S, active, cr, s_thr); break;
+                        case 2: v_codes_row<2>(xr, S, active, cr, s_thr); break;
+                        case 3: v_codes_row<3>(xr, S, active, cr, s_thr); break;
+                        default: v_codes_row<4>(xr, S, active, cr, s_thr); break;
+                    }
+                } else {
+                    uint32_t codes[D];
+                    affine_group(xr, D, vb, &s16, &z16, codes);
+                    for (int j = 0; j < D; ++j) cr[j] = active ? (uint8_t)codes[j] : (uint8_t)0;
                 }
+            };
+            if constexpr (ROT) {
+                if (a.v_rot) vquant(XRow<float>{rotate_row(a.v_rot + h * 16), BGTQ_F32});
+                else vquant(x);
             } else {
-                uint32_t codes[D];
-                affine_group(x, D, vb, &s16, &z16, codes);
-                for (int j = 0; j < D; ++j) cr[j] = active ? (uint8_t)codes[j] : (uint8_t)0;
+                vquant(x);
             }
             if (active) {
                 a.v_scale[bh * a.n_cap + pos] = s16;
@@ -1969,7 +2001,7 @@ hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_
     q.vec16 = ((uintptr_t)a.src_k % 16 == 0) && ((uintptr_t)a.src_v % 16 == 0) && (a.sB * es) % 16 == 0 &&
               (a.sT * es) % 16 == 0 && (a.sH * es) % 16 == 0;
     const dim3 grid((unsigned)max_tiles, a.Hkv, B);
-    const bool rot = a.k_rot && a.k_mode == BGTQ_K_AFFINE && (a.which & 1);
+    const bool rot = (a.k_rot && a.k_mode == BGTQ_K_AFFINE && (a.which & 1)) || (a.v_rot && (a.which & 2));
     int64_t most = 0;  // the most positions any sequence appends
     for (int b = 0; b < B; ++b) most = std::max<int64_t>(most, a.pos_hi[b] - a.pos_lo[b]);
     if (!rot && most <= kAppendFewMax) return launch_main(k_append, grid, dim3(64), s, q);

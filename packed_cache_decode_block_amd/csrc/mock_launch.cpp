@@ -97,6 +97,7 @@ hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t) {
 
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t) {
     if (!a.part || !a.out || a.n_parts < 1 || a.n_parts > BGTQ_MAX_PARTS || rows < 1) return bad("combine");
+    if (a.v_rot && (a.Hq < 1 || a.G < 1 || a.Hq % a.G || rows % a.Hq)) return bad("combine: rotation geometry");
     note("combine");
     return hipSuccess;
 }

@@ -208,6 +208,58 @@ def test_rotated_affine_keys(name):
         print(f"  splits={ns}: max abs err {e:.2e}", flush=True)
 
 
+VROT_CASES = {
+    # values stored rotated (QWC summary, Results: rotation integration; the summary finds the
+    # value-only rotation marginal, built for comparison): codebook values with Block-GTQ keys at 8
+    # and 4 query heads per kv head (the latter with two sequences and chunked appends, including
+    # few-token ones that take the bulk quantizer), affine values with rotated affine keys
+    "gtq_v3_g8": (2, {"L": 1}, 1500 + 7, (None,), False),
+    "gtq_v2_g4_b2": (3, {"L": 1, "B": 2}, 700 + 3, (1, 5, 300, None), False),
+    "affine_k4v2_both_rotated": (4, {"L": 1, "B": 1}, 900 + 1, (None,), True),
+}
+
+
+@pytest.mark.parametrize("name", list(VROT_CASES))
+def test_rotated_values(name):
+    wid, ov, N, chunks, krot = VROT_CASES[name]
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
+    print(f"[rotated values {name}] N={N} B={w.B} Hq={w.Hq} Hkv={w.Hkv} keys rotated {krot}", flush=True)
+    n_cap = ((N + 63) // 64 + 1) * 64
+    vs = np.where(np.random.default_rng(41).random((w.Hkv, 128)) < 0.5, -1.0, 1.0)
+    ks = np.where(np.random.default_rng(43).random((w.Hkv, 128)) < 0.5, -1.0, 1.0) if krot else None
+    m = T.meta(w, 0)
+    K, V, q = T.inputs(w, 0, N)
+    oc = pipeline.build_layer(K, V, k_mode=w.k_mode, v_mode=w.v_mode, v_bits=w.v_bits, n_cap=n_cap, meta=m,
+                              k_bits=w.k_bits or 4, k_group=w.k_group or 32, k_rot=ks, v_rot=vs)
+    cache = P.PackedCache(L=1, B=w.B, Hq=w.Hq, Hkv=w.Hkv, n_cap=n_cap,
+                          k_mode=P.K_BLOCKGTQ if w.k_mode == "gtq" else P.K_AFFINE,
+                          budget_units=w.k_budget_units or 128, k_bits=w.k_bits or 4, k_group=w.k_group or 32,
+                          v_mode=P.V_CODEBOOK if w.v_mode == "codebook" else P.V_AFFINE, v_bits=w.v_bits,
+                          k_rotation=krot, v_rotation=True)
+    if m is not None:
+        cache.set_metadata(0, m.bits, m.sigma, m.r)
+    if krot:
+        cache.set_key_rotation(0, ks)
+    cache.set_value_rotation(0, vs)
+    T.append_all(cache, 0, K, V, w.dtype, chunks)
+    _compare_cache(cache, oc, w)
+    ref = pipeline.decode_layer(oc, q)
+    qd = T.to_dev(q, w.dtype)
+    for ns in (0, 1, 3):
+        out = cache.decode_attention(0, qd, n_splits=ns)
+        torch.cuda.synchronize()
+        e = T.assert_close(out.cpu().numpy(), ref, f"{name} splits={ns}")
+        print(f"  splits={ns}: max abs err {e:.2e}", flush=True)
+    # one decode step on top: the appended token goes through the rotated quantizer
+    kd = T.to_dev(np.transpose(K, (0, 2, 1, 3))[:, -1:], w.dtype)
+    vd = T.to_dev(np.transpose(V, (0, 2, 1, 3))[:, -1:], w.dtype)
+    cache.n_tokens[0] -= 1
+    out = cache.decode_step(0, kd, vd, qd)
+    torch.cuda.synchronize()
+    T.assert_close(out.cpu().numpy(), ref, f"{name} step")
+    _compare_cache(cache, oc, w)
+
+
 EDGE_CASES = {
     # name: (workload id, overrides, N, n_splits)
     "max_batch_64": (3, {"L": 1, "B": 64, "Hkv": 1, "Hq": 4}, 70, 0),

@@ -248,3 +248,27 @@ def test_decode_path_routing(mock):
         mock.bgtq_mock_reset()
         assert mock.bgtq_decode_attention(C.byref(d), 0, q, 2, q, ws, need, 0, None) == _lib.E_INVALID
         assert b"decode_path" in mock.bgtq_last_error() and mock.bgtq_mock_launches() == 0
+
+
+def test_value_rotation_needs_no_fp16_window(mock):
+    """The value rotation is refused, before any launch, with an fp16 window; without one the
+    merge gets the layer's sign bits."""
+    nt = np.full((2, 2), 300, np.int64)
+    d = _desc(nt, budget_units=192, v_bits=2, n_recent=256)
+    d.v_rot = FAKE + 0x7000000
+    q = C.c_void_p(FAKE + 0x50000000)
+    ws = C.c_void_p(FAKE + 0x60000000)
+    mock.bgtq_mock_reset()
+    assert mock.bgtq_decode_attention(C.byref(d), 0, q, 2, q, ws, 1 << 30, 0, None) == _lib.E_UNSUPPORTED
+    assert mock.bgtq_quantize_append(C.byref(d), 0, q, q, 2, 1, None, None) == _lib.E_UNSUPPORTED
+    assert mock.bgtq_mock_launches() == 0
+    d2 = _desc(nt)
+    d2.v_rot = FAKE + 0x7000000
+    need = mock.bgtq_decode_workspace_bytes(C.byref(d2), 0)
+    mock.bgtq_mock_reset()
+    _call_ok(mock, mock.bgtq_decode_attention(C.byref(d2), 1, q, 2, q, ws, need, 0, None))
+    # a one-token step with rotated values keeps the separate append launch (the fused path
+    # quantizes without the rotation)
+    mock.bgtq_mock_reset()
+    log = _call_ok(mock, mock.bgtq_decode_step(C.byref(d2), 1, q, q, q, 2, 1, None, q, ws, need, 0, None))
+    assert "append" not in log and ("quant" in log), log
