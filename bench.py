@@ -107,6 +107,22 @@ def measured_traffic(wid: int, kernel: str = "k_decode_gtq"):
     return int(t.group(1))
 
 
+def calibrate_layer(w, layer: int, device="cuda"):
+    """Block-GTQ metadata of one layer through the library: calibration energy on the device, then
+    the greedy widths (bits, sigma, inv_sigma as host arrays [Hkv, 64])."""
+    import torch
+
+    import packed_cache_decode_block_amd as P
+    import synth
+    td = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    cal = [synth.calibration(w, layer, h) for h in range(w.Hkv)]
+    kc = torch.from_numpy(np.ascontiguousarray(np.stack([c[0] for c in cal], axis=1))).to(device).to(td)
+    qc = torch.from_numpy(np.ascontiguousarray(
+        np.concatenate([np.transpose(c[1], (1, 0, 2)) for c in cal], axis=1))).to(device).to(td)
+    scores, sigma, inv_sigma = P.bgtq_block_energy(kc, qc)
+    return P.bgtq_allocate(scores, w.k_budget_units), sigma, inv_sigma
+
+
 def build_packed(w, device="cuda", uniform_keys=False, k_rotation=False):
     import torch
 
@@ -127,12 +143,7 @@ def build_packed(w, device="cuda", uniform_keys=False, k_rotation=False):
             rs = np.random.default_rng([w.wid, layer, 7]).random((w.Hkv, 128))
             cache.set_key_rotation(layer, np.where(rs < 0.5, -1.0, 1.0))
         if w.k_mode == "gtq":
-            cal = [synth.calibration(w, layer, h) for h in range(w.Hkv)]
-            kc = torch.from_numpy(np.ascontiguousarray(np.stack([c[0] for c in cal], axis=1))).to(device).to(td)
-            qc = torch.from_numpy(np.ascontiguousarray(
-                np.concatenate([np.transpose(c[1], (1, 0, 2)) for c in cal], axis=1))).to(device).to(td)
-            scores, sigma, inv_sigma = P.bgtq_block_energy(kc, qc)
-            bits = P.bgtq_allocate(scores, w.k_budget_units)
+            bits, sigma, inv_sigma = calibrate_layer(w, layer, device)
             if uniform_keys:  # uniform TQ-MSE keys: every block at the average width
                 bits = np.full_like(bits, w.k_budget_units // 64)
             cache.set_metadata(layer, bits, sigma, inv_sigma)
@@ -499,24 +510,28 @@ def main():
         log(f"[bench] decode step (append 1 token + attend) {sec_s * 1e3:.3f} ms, "
             f"{sec_s * 1e6 / w.L:.2f} us per layer ({(sec_s - sec) * 1e6 / w.L:.2f} us for the append)")
     if not args.no_logquant and w.k_mode == "gtq":
-        # LogQuant's log-based filter (bgtq_logquant_append): 2048 one-token appends per kv head into
-        # a W = 64 store (192 fp16 rows) of this workload's format, a halving every 64 tokens; the
-        # wall time per call includes the host plan, the leaving-row quantize is also event-timed.
+        # LogQuant's log-based filter on this workload's format and layer-0 calibration, W = 64 (a
+        # 192-row fp16 store): (1) one-token appends (bgtq_logquant_append), 2048 per kv head, a
+        # halving every 64 tokens; wall time per call includes the host plan; the leaving rows'
+        # quantize is event-timed; (2) a whole prompt of the workload's context in one call
+        # (bgtq_logquant_prefill), event-timed quantize and wall time.
+        from synth import gpu as sg
         W_lq, n_lq = 64, 2048
+        bits0, sig0, inv0 = calibrate_layer(w, 0)
+        td = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
         lqc = P.PackedCache(L=1, B=1, Hq=w.Hq, Hkv=w.Hkv, n_cap=n_lq, budget_units=w.k_budget_units,
                             v_bits=w.v_bits, logquant_w=W_lq)
-        lqc.set_metadata(0, np.full((w.Hkv, 64), w.k_budget_units // 64, np.uint8),
-                         np.ones((w.Hkv, 64), np.float32), np.ones((w.Hkv, 64), np.float32))
-        gen = torch.Generator(device="cuda").manual_seed(5)
-        td = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
-        rows = [torch.randn((1, n_lq, w.Hkv, w.d), generator=gen, device="cuda").to(td) for _ in range(2)]
+        lqc.set_metadata(0, bits0, sig0, inv0)
+        rows = [torch.stack([f(w, 0, h, 0, n_lq) for h in range(w.Hkv)], dim=1)[None].to(td)
+                for f in (sg.keys, sg.values)]
         for p in range(3 * W_lq):   # fill the store (no timing)
             lqc.logquant_append(0, rows[0][:, p:p + 1], rows[1][:, p:p + 1])
+        views = [(rows[0][:, p:p + 1], rows[1][:, p:p + 1]) for p in range(3 * W_lq, n_lq)]
         torch.cuda.synchronize()
         P.bgtq_profile_enable(n_lq)
         t0 = time.perf_counter()
-        for p in range(3 * W_lq, n_lq):
-            lqc.logquant_append(0, rows[0][:, p:p + 1], rows[1][:, p:p + 1])
+        for kv in views:
+            lqc.logquant_append(0, kv[0], kv[1])
         torch.cuda.synchronize()
         t_lq = time.perf_counter() - t0
         nq_lq, tq_lq, _, _ = P.bgtq_profile_read(P.PROF_QUANTIZE)
@@ -524,12 +539,40 @@ def main():
         n_calls = n_lq - 3 * W_lq
         result["logquant_append"] = {
             "entry": "bgtq_logquant_append", "W": W_lq, "store_rows": 3 * W_lq, "calls": n_calls,
+            "metadata": "calibrated (layer 0 of the workload)",
             "halvings": nq_lq, "us_per_call": round(t_lq * 1e6 / n_calls, 2),
             "leaving_quantize_us": round(tq_lq * 1e3 / max(nq_lq, 1), 2),
             "packed_after": int(lqc.n_tokens[0, 0] - lqc.n_hp[0, 0]), "fp16_after": int(lqc.n_hp[0, 0])}
         log(f"[bench] log-based filter: {t_lq * 1e6 / n_calls:.1f} us per one-token append (host plan included), "
             f"{nq_lq} halvings, leaving-row quantize {tq_lq * 1e3 / max(nq_lq, 1):.1f} us each")
-        del lqc, rows
+        del lqc, rows, views
+        # the prompt of the workload's full context, one call
+        N_p = w.N
+        pc = P.PackedCache(L=1, B=w.B, Hq=w.Hq, Hkv=w.Hkv, n_cap=N_p, budget_units=w.k_budget_units,
+                           v_bits=w.v_bits, logquant_w=W_lq)
+        pc.set_metadata(0, bits0, sig0, inv0)
+        kp = torch.stack([torch.stack([sg.keys(w, 0, h, b, N_p) for h in range(w.Hkv)], dim=1) for b in range(w.B)])
+        vp = torch.stack([torch.stack([sg.values(w, 0, h, b, N_p) for h in range(w.Hkv)], dim=1) for b in range(w.B)])
+        pc.logquant_prefill(0, kp, vp)  # warm-up (then the layer is reset and filled again)
+        torch.cuda.synchronize()
+        pc.n_tokens[:] = 0
+        pc.n_hp[:] = 0
+        P.bgtq_profile_enable(4)
+        t0 = time.perf_counter()
+        pc.logquant_prefill(0, kp, vp)
+        torch.cuda.synchronize()
+        t_pf = time.perf_counter() - t0
+        npf, tpf, _, _ = P.bgtq_profile_read(P.PROF_QUANTIZE)
+        P.bgtq_profile_enable(0)
+        n_pk = int(pc.n_tokens[0, 0] - pc.n_hp[0, 0])
+        result["logquant_prefill"] = {
+            "entry": "bgtq_logquant_prefill", "W": W_lq, "prompt_tokens": N_p, "packed": n_pk,
+            "fp16": int(pc.n_hp[0, 0]), "ms_per_call": round(t_pf * 1e3, 3),
+            "quantize_us": round(tpf * 1e3 / max(npf, 1), 1),
+            "tokens_per_s": round(w.B * N_p / t_pf, 1)}
+        log(f"[bench] log-based filter prefill of {N_p} tokens: {t_pf * 1e3:.2f} ms per call "
+            f"(gathered quantize {tpf * 1e3 / max(npf, 1):.1f} us)")
+        del pc, kp, vp
     del ws
     if not args.no_fp16:
         del cache

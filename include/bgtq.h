@@ -235,22 +235,55 @@ int bgtq_logquant_plan(int W, int64_t *hp_pos, int *n_hp, int64_t pos, int32_t *
                        int32_t *move_src, int32_t *move_dst, int *n_moves, int *new_slot);
 
 /*
+ * Device workspace of the log-based filter's calls (host, no side effects): the bytes that
+ * bgtq_logquant_prefill needs for a prompt of n_prompt tokens (its gather indices), or, with
+ * n_prompt = 0, that bgtq_logquant_append needs (the store permutation, once B * n_recent is above
+ * 1536; 0 below, where the permutation travels in the kernel arguments).  <0 on error.
+ */
+int64_t bgtq_logquant_workspace_bytes(const bgtq_cache *c, int64_t n_prompt);
+
+/*
  * Append one token per sequence under LogQuant's log-based filter (device, asynchronous; host
  * bookkeeping synchronous).  LogQuant summary, Method 2; the filter is bgtq_logquant_plan's,
- * with W = n_recent / 3.  Needs c->n_hp, n_recent a multiple of 3 in [3, 512], and
- * B * n_recent <= 1536.  For each sequence the new token's row enters the high-precision store.
- * When the store already holds 3W rows, the rows that leave are quantized first, oldest first,
- * and appended to the packed cache.  The store is then compacted, as the plan describes.
+ * with W = n_recent / 3.  Needs c->n_hp and n_recent a multiple of 3 in [3, 512].  For each
+ * sequence the new token's row enters the high-precision store.  When the store already holds 3W
+ * rows, the rows that leave are quantized first, oldest first, and appended to the packed cache.
+ * The store is then compacted, as the plan describes.
  * k, v: device rows [B][1][Hkv][128] in `dtype` (strides as bgtq_quantize_append, n_new = 1).
  * hp_pos: host int64 [B][n_recent], the token position each store row holds; maintained here.
+ * ws, ws_bytes: device workspace, 256-byte aligned, of bgtq_logquant_workspace_bytes(c, 0) bytes;
+ * may be NULL when that is 0 (B * n_recent <= 1536).  The store permutation is then copied into
+ * it from host memory on `stream`.
  * On success n_tokens, n_hp and hp_pos advance.  Errors found before any launch change nothing:
- * those of bgtq_quantize_append, BGTQ_E_INVALID (no n_hp, bad n_recent, inconsistent counts),
- * BGTQ_E_UNSUPPORTED (B * n_recent above 1536).  BGTQ_E_HIP (a launch failed after an earlier
- * one of the same call was enqueued) leaves the host bookkeeping unchanged and the layer's
- * device store and packed tail unspecified.
+ * those of bgtq_quantize_append, BGTQ_E_INVALID (no n_hp, bad n_recent, inconsistent counts, a
+ * missing or small workspace).  BGTQ_E_HIP (a launch failed after an earlier one of the same call
+ * was enqueued) leaves the host bookkeeping unchanged and the layer's device store and packed tail
+ * unspecified.
  */
 int bgtq_logquant_append(bgtq_cache *c, int layer, const void *k, const void *v, int dtype,
-                         const int64_t *strides, int64_t *hp_pos, void *stream);
+                         const int64_t *strides, int64_t *hp_pos, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/*
+ * LogQuant's filter over a prompt, in one call (device, asynchronous; host planning synchronous;
+ * LogQuant summary, Method 2).  Appends n_prompt tokens to every sequence of a layer whose
+ * sequences are empty (n_tokens and n_hp 0), with the result of n_prompt calls of
+ * bgtq_logquant_append up to the order of the store's slots: the filter's selection over
+ * positions 0..n_prompt-1 decides which tokens stay at high precision (at most 3W = n_recent) and
+ * in which order the others left; the leaving tokens are quantized into packed positions
+ * 0, 1, ... in that order (one gathered quantize launch) and the kept tokens' fp16 rows go to
+ * store slots 0..n_hp-1 in position order.  k, v: device rows [B][n_prompt][Hkv][128] in `dtype`
+ * (strides as bgtq_quantize_append).  hp_pos: host int64 [B][n_recent], written (-1 past n_hp).
+ * ws, ws_bytes: device workspace, 256-byte aligned, of bgtq_logquant_workspace_bytes(c, n_prompt)
+ * bytes (the gather indices, copied from host memory on `stream`).  On success n_tokens = n_prompt
+ * and n_hp = the kept count.  Errors before any launch change nothing: BGTQ_E_INVALID (no n_hp,
+ * bad n_recent or n_prompt, a sequence not empty, NULL pointers, a missing or small workspace),
+ * BGTQ_E_CAPACITY (the leaving tokens exceed n_cap), and the format errors of
+ * bgtq_quantize_append.
+ */
+int bgtq_logquant_prefill(bgtq_cache *c, int layer, const void *k, const void *v, int dtype,
+                          int64_t n_prompt, const int64_t *strides, int64_t *hp_pos, void *ws,
+                          size_t ws_bytes, void *stream);
 
 /*
  * Prepare a layer's decode plan (device, asynchronous) from its widths c->bits[layer]: the block

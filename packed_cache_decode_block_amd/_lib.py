@@ -22,7 +22,8 @@ ENERGY_CHUNK = 16  # BGTQ_ENERGY_CHUNK: calibration tokens per workgroup of bgtq
 SYMBOLS = ["bgtq_last_error", "bgtq_version", "bgtq_codebook", "bgtq_allocate", "bgtq_allocate_rate",
            "bgtq_logquant_plan", "bgtq_logquant_append", "bgtq_block_energy", "bgtq_cache_bytes", "bgtq_quantize_append", "bgtq_decode_workspace_bytes", "bgtq_decode_attention",
            "bgtq_decode_step", "bgtq_fp16_decode_workspace_bytes", "bgtq_fp16_decode_attention", "bgtq_profile_enable",
-           "bgtq_profile_read", "bgtq_decode_attention_noalloc", "bgtq_prepare_metadata"]
+           "bgtq_profile_read", "bgtq_decode_attention_noalloc", "bgtq_prepare_metadata",
+           "bgtq_logquant_workspace_bytes", "bgtq_logquant_prefill"]
 NOALLOC_SCRATCH_BYTES = 4 << 20  # BGTQ_NOALLOC_SCRATCH_BYTES
 PROF_DECODE, PROF_FP16_DECODE, PROF_QUANTIZE = 0, 1, 2
 
@@ -67,7 +68,11 @@ def bind(path: str, optional=()):
         "bgtq_prepare_metadata": (I, [C.POINTER(CacheDesc), I, P]),
         "bgtq_logquant_plan": (I, [I, C.POINTER(C.c_int64), C.POINTER(C.c_int), I64, C.POINTER(C.c_int32),
                                    C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int), C.POINTER(C.c_int)]),
-        "bgtq_logquant_append": (I, [C.POINTER(CacheDesc), I, P, P, I, C.POINTER(C.c_int64), C.POINTER(C.c_int64), P]),
+        "bgtq_logquant_append": (I, [C.POINTER(CacheDesc), I, P, P, I, C.POINTER(C.c_int64), C.POINTER(C.c_int64), P,
+                                     SZ, P]),
+        "bgtq_logquant_workspace_bytes": (I64, [C.POINTER(CacheDesc), I64]),
+        "bgtq_logquant_prefill": (I, [C.POINTER(CacheDesc), I, P, P, I, I64, C.POINTER(C.c_int64), C.POINTER(C.c_int64),
+                                      P, SZ, P]),
         "bgtq_decode_step": (I, [C.POINTER(CacheDesc), I, P, P, P, I, I64, C.POINTER(C.c_int64), P, P, SZ, I, P]),
         "bgtq_fp16_decode_workspace_bytes": (I64, [I64, I, I, I, I]),
         "bgtq_fp16_decode_attention": (I, [P, P, I64, I, I, I, I, P, I, P, P, SZ, I, P]),

@@ -26,8 +26,12 @@ def _dtype_code(t) -> int:
 
 def _stream(stream=None):
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return C.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return C.c_void_p(stream.cuda_stream)
+    try:  # the raw handle of the current stream, without building a Stream object
+        return C.c_void_p(torch._C._cuda_getCurrentRawStream(torch.cuda.current_device()))
+    except AttributeError:
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 def _ptr(t):
@@ -145,6 +149,7 @@ class PackedCache:
         if logquant_w is not None:
             self.n_hp = np.zeros((L, B), np.int32)
             self.hp_pos = np.zeros((L, B, n_recent), np.int64)
+            self._hp_ptr = [self.hp_pos[i].ctypes.data_as(C.POINTER(C.c_int64)) for i in range(L)]
             d.n_hp = self.n_hp.ctypes.data_as(C.POINTER(C.c_int32))
         alloc = torch.zeros if zero else torch.empty
 
@@ -176,6 +181,7 @@ class PackedCache:
                      "bits", "sigma", "inv_sigma", "k_rot", "plan", "v_rot"):
             setattr(d, name, _ptr(getattr(self, name)))
         self._ws = None
+        self._lq_ws = None
 
     def set_key_rotation(self, layer: int, signs):
         """Signs s [Hkv, 128] (+1 / -1, host) of the key rotation of one layer: affine keys are
@@ -232,6 +238,16 @@ class PackedCache:
         check(lib.bgtq_quantize_append(C.byref(self.desc), layer, _ptr(k), _ptr(v), _dtype_code(k), k.shape[1],
                                        strides, _stream(stream)))
 
+    def _lq_workspace(self, n_prompt: int, device):
+        torch = _torch()
+        n = check(lib.bgtq_logquant_workspace_bytes(C.byref(self.desc), n_prompt))
+        if n == 0:
+            return None, 0
+        if self._lq_ws is None or self._lq_ws.numel() < n + 256:
+            self._lq_ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+        p = self._lq_ws.data_ptr()
+        return C.c_void_p((p + 255) // 256 * 256), n
+
     def logquant_append(self, layer: int, k, v, stream=None):
         """Append one token per sequence, k, v [B, 1, Hkv, 128], under the log-based filter."""
         if self.n_hp is None:
@@ -239,8 +255,20 @@ class PackedCache:
         strides = self._kv_strides(k, v)
         if tuple(k.shape) != (self.desc.B, 1, self.desc.Hkv, 128):
             raise ValueError(f"k and v must be [{self.desc.B}, 1, {self.desc.Hkv}, 128]: one token per sequence")
+        ws, n = self._lq_workspace(0, k.device)
         check(lib.bgtq_logquant_append(C.byref(self.desc), layer, _ptr(k), _ptr(v), _dtype_code(k), strides,
-                                       self.hp_pos[layer].ctypes.data_as(C.POINTER(C.c_int64)), _stream(stream)))
+                                       self._hp_ptr[layer], ws, n, _stream(stream)))
+
+    def logquant_prefill(self, layer: int, k, v, stream=None):
+        """Start a layer from a prompt, k, v [B, n_prompt, Hkv, 128], under the log-based filter, in
+        one call: the filter's selection over the prompt, one gathered quantize of the tokens that
+        leave the high-precision store, and the kept rows written to the store."""
+        if self.n_hp is None:
+            raise ValueError("the cache was built without logquant_w")
+        strides = self._kv_strides(k, v)
+        ws, n = self._lq_workspace(k.shape[1], k.device)
+        check(lib.bgtq_logquant_prefill(C.byref(self.desc), layer, _ptr(k), _ptr(v), _dtype_code(k), k.shape[1],
+                                        strides, self._hp_ptr[layer], ws, n, _stream(stream)))
 
     def decode_step(self, layer: int, k, v, q, out=None, n_splits: int = 0, ws=None, stream=None):
         """Append k, v [B, n_new, Hkv, 128], then attend q [B, Hq, 128] over the grown context -> fp32 out."""

@@ -583,8 +583,22 @@ int bgtq_quantize_append(bgtq_cache* c, int layer, const void* k, const void* v,
     return quantize_append_impl(c, layer, k, v, dtype, n_new, strides, stream, false);
 }
 
+int64_t bgtq_logquant_workspace_bytes(const bgtq_cache* c, int64_t n_prompt) {
+    bgtq::Geometry g;
+    int rc = geometry(c, g);
+    if (rc) return rc;
+    if (n_prompt < 0) return fail(BGTQ_E_INVALID, "n_prompt < 0");
+    const int64_t R = c->n_recent;
+    // the store permutation of every sequence (int16), when it does not fit the kernel arguments
+    const int64_t perm = (int64_t)c->B * R > bgtq::BGTQ_PERM_MAX ? (int64_t)c->B * R * 2 : 0;
+    // a prefill's gather indices (int32): the leaving tokens in leaving order, then the kept ones
+    const int64_t gather = n_prompt > 0 ? (n_prompt + R) * 4 : 0;
+    const int64_t need = std::max(perm, gather);
+    return need ? (need + 255) / 256 * 256 : 0;
+}
+
 int bgtq_logquant_append(bgtq_cache* c, int layer, const void* k, const void* v, int dtype, const int64_t* strides,
-                         int64_t* hp_pos, void* stream) {
+                         int64_t* hp_pos, void* ws, size_t ws_bytes, void* stream) {
     bgtq::Geometry g;
     int rc = geometry(c, g);
     if (rc) return rc;
@@ -593,8 +607,10 @@ int bgtq_logquant_append(bgtq_cache* c, int layer, const void* k, const void* v,
     const int R = c->n_recent;
     if (R < 3 || R % 3 || R > bgtq::BGTQ_HP_ROWS_MAX)
         return fail(BGTQ_E_INVALID, "n_recent=%d must be a multiple of 3 in [3, %d]", R, bgtq::BGTQ_HP_ROWS_MAX);
-    if ((int64_t)c->B * R > bgtq::BGTQ_PERM_MAX)
-        return fail(BGTQ_E_UNSUPPORTED, "B * n_recent above %d", bgtq::BGTQ_PERM_MAX);
+    const bool perm_in_ws = (int64_t)c->B * R > bgtq::BGTQ_PERM_MAX;
+    if (perm_in_ws && (!ws || ws_bytes < (size_t)c->B * R * 2 || ((uintptr_t)ws & 255)))
+        return fail(BGTQ_E_INVALID, "B * n_recent above %d: the store permutation needs a 256-byte aligned workspace "
+                    "of bgtq_logquant_workspace_bytes(c, 0) bytes", bgtq::BGTQ_PERM_MAX);
     if (!k || !v || !hp_pos) return fail(BGTQ_E_INVALID, "NULL k/v/hp_pos");
     if (!dtype_ok(dtype)) return fail(BGTQ_E_INVALID, "bad dtype");
     if (!c->n_tokens) return fail(BGTQ_E_INVALID, "n_tokens is NULL");
@@ -617,6 +633,7 @@ int bgtq_logquant_append(bgtq_cache* c, int layer, const void* k, const void* v,
     std::vector<int64_t> pos(hp_pos, hp_pos + (size_t)c->B * R);
     std::vector<int> nh(c->B), slot(c->B), leaving(c->B);
     std::vector<int32_t> ev(W), ms(W), md(W);
+    std::vector<int16_t> perm_host(perm_in_ws ? (size_t)c->B * R : 0);
     bgtq::PermuteArgs pa{};
     pa.Hkv = g.Hkv;
     pa.n_recent = R;
@@ -637,11 +654,11 @@ int bgtq_logquant_append(bgtq_cache* c, int layer, const void* k, const void* v,
             return fail(BGTQ_E_CAPACITY, "sequence %d: %lld packed tokens exceed n_cap %lld", b,
                         (long long)(packed + W), (long long)c->n_cap);
         // kept rows stay or fill the vacated slots below 2W; the leaving rows go to [2W, 3W) in order
-        int16_t* perm = pa.perm + n_perm;
+        int16_t* perm = (perm_in_ws ? perm_host.data() : pa.perm) + n_perm;
         for (int j = 0; j < R; ++j) perm[j] = (int16_t)j;
         for (int m = 0; m < n_moves; ++m) perm[md[m]] = (int16_t)ms[m];
         for (int i = 0; i < W; ++i) perm[2 * W + i] = (int16_t)ev[i];
-        pa.seq_first[b] = (int16_t)n_perm;
+        pa.seq_first[b] = n_perm;
         n_perm += R;
         ++n_thin;
     }
@@ -653,6 +670,11 @@ int bgtq_logquant_append(bgtq_cache* c, int layer, const void* k, const void* v,
     if (n_thin) {
         pa.rows_k = rk;
         pa.rows_v = rv;
+        if (perm_in_ws) {
+            e = bgtq::copy_to_device(ws, perm_host.data(), (size_t)n_perm * 2, s);
+            if (e != hipSuccess) return hip_fail(e, "store permutation copy");
+            pa.perm_dev = (const int16_t*)ws;
+        }
         e = bgtq::launch_permute(pa, c->B, s);
         if (e != hipSuccess) return hip_fail(e, "store reorder");
         // the leaving rows, now in store slots [2W, 3W), become packed positions [packed, packed + W)
@@ -701,6 +723,116 @@ int bgtq_logquant_append(bgtq_cache* c, int layer, const void* k, const void* v,
     for (int b = 0; b < c->B; ++b) {
         nhp[b] = nh[b];
         nt[b] += 1;
+    }
+    return ok();
+}
+
+int bgtq_logquant_prefill(bgtq_cache* c, int layer, const void* k, const void* v, int dtype, int64_t n_prompt,
+                          const int64_t* strides, int64_t* hp_pos, void* ws, size_t ws_bytes, void* stream) {
+    bgtq::Geometry g;
+    int rc = geometry(c, g);
+    if (rc) return rc;
+    if (layer < 0 || layer >= c->L) return fail(BGTQ_E_INVALID, "layer %d out of range", layer);
+    if (!c->n_hp) return fail(BGTQ_E_INVALID, "the log-based filter needs n_hp");
+    const int R = c->n_recent;
+    if (R < 3 || R % 3 || R > bgtq::BGTQ_HP_ROWS_MAX)
+        return fail(BGTQ_E_INVALID, "n_recent=%d must be a multiple of 3 in [3, %d]", R, bgtq::BGTQ_HP_ROWS_MAX);
+    if (!k || !v || !hp_pos) return fail(BGTQ_E_INVALID, "NULL k/v/hp_pos");
+    if (!dtype_ok(dtype)) return fail(BGTQ_E_INVALID, "bad dtype");
+    if (n_prompt < 1 || n_prompt > INT32_MAX) return fail(BGTQ_E_INVALID, "n_prompt must be in [1, 2^31)");
+    if (!c->n_tokens) return fail(BGTQ_E_INVALID, "n_tokens is NULL");
+    if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale || !c->recent_k || !c->recent_v)
+        return fail(BGTQ_E_INVALID, "NULL cache buffer");
+    if (c->k_mode == BGTQ_K_BLOCKGTQ && (!c->bits || !c->sigma || !c->inv_sigma))
+        return fail(BGTQ_E_INVALID, "Block-GTQ keys need bits, sigma and inv_sigma");
+    if (c->k_mode == BGTQ_K_AFFINE && !c->k_zero) return fail(BGTQ_E_INVALID, "affine keys need k_zero");
+    if (c->v_mode == BGTQ_V_AFFINE && !c->v_zero) return fail(BGTQ_E_INVALID, "affine values need v_zero");
+    int64_t* nt = c->n_tokens + (size_t)layer * c->B;
+    int32_t* nhp = c->n_hp + (size_t)layer * c->B;
+    for (int b = 0; b < c->B; ++b)
+        if (nt[b] != 0 || nhp[b] != 0) return fail(BGTQ_E_INVALID, "sequence %d is not empty: prefill starts a layer", b);
+    const int64_t need = bgtq_logquant_workspace_bytes(c, n_prompt);
+    if (!ws || ws_bytes < (size_t)need || ((uintptr_t)ws & 255))
+        return fail(BGTQ_E_INVALID, "workspace must be 256-byte aligned and hold %lld bytes", (long long)need);
+    // The filter's selection over positions 0..n_prompt-1 (the same for every sequence): a store of
+    // at most 3W positions; at 3W, of its 2W oldest the 2nd, 4th, ... leave, oldest first.
+    const int W = R / 3;
+    std::vector<int32_t> hp, leave;
+    hp.reserve(R + 1);
+    leave.reserve((size_t)n_prompt);
+    std::vector<int32_t> keep;
+    keep.reserve(R);
+    for (int64_t p = 0; p < n_prompt; ++p) {
+        if ((int)hp.size() == R) {
+            keep.clear();
+            for (int i = 0; i < 2 * W; ++i) (i % 2 ? leave : keep).push_back(hp[i]);
+            for (int i = 2 * W; i < R; ++i) keep.push_back(hp[i]);
+            hp.swap(keep);
+        }
+        hp.push_back((int32_t)p);
+    }
+    const int64_t n_leave = (int64_t)leave.size(), n_keep = (int64_t)hp.size();
+    if (n_leave > c->n_cap)
+        return fail(BGTQ_E_CAPACITY, "%lld packed tokens exceed n_cap %lld", (long long)n_leave, (long long)c->n_cap);
+    int64_t sB, sT, sH;
+    if (strides) {
+        sB = strides[0]; sT = strides[1]; sH = strides[2];
+    } else {
+        sH = D; sT = (int64_t)g.Hkv * D; sB = n_prompt * sT;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    // gather indices in the workspace: the leaving tokens (packed positions 0..n_leave-1), then the kept
+    std::vector<int32_t> idx(leave);
+    idx.insert(idx.end(), hp.begin(), hp.end());
+    hipError_t e = bgtq::copy_to_device(ws, idx.data(), idx.size() * 4, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill index copy");
+    const int32_t* g_leave = (const int32_t*)ws;
+    const int32_t* g_keep = g_leave + n_leave;
+    if (n_leave > 0) {
+        bgtq::QuantArgs q{};
+        fill_quant_layer(c, g, layer, q);
+        q.src_k = k;
+        q.src_v = v;
+        q.dtype = dtype;
+        q.sB = sB; q.sT = sT; q.sH = sH;
+        q.gather = g_leave;
+        q.gather_stride = 0;
+        q.round16 = 1;  // every leaving token was an fp16 store row first
+        for (int b = 0; b < c->B; ++b) {
+            q.pos_lo[b] = 0;
+            q.pos_hi[b] = n_leave;
+            q.off[b] = 0;
+            q.tile0[b] = 0;
+        }
+        ProfScope ps(BGTQ_PROF_QUANTIZE, s);
+        e = bgtq::launch_quant(q, c->B, (n_leave + TILE - 1) / TILE, s);
+        if (e != hipSuccess) return hip_fail(e, "prefill quantize");
+    }
+    const size_t bh = (size_t)g.B * g.Hkv;
+    bgtq::RingArgs ra{};
+    ra.k = k;
+    ra.v = v;
+    ra.dtype = dtype;
+    ra.sB = sB; ra.sT = sT; ra.sH = sH;
+    ra.ring_k = (uint16_t*)c->recent_k + (size_t)layer * bh * R * D;
+    ra.ring_v = (uint16_t*)c->recent_v + (size_t)layer * bh * R * D;
+    ra.Hkv = g.Hkv;
+    ra.n_recent = R;
+    ra.gather = g_keep;
+    ra.gather_stride = 0;
+    for (int b = 0; b < c->B; ++b) {
+        ra.pos_lo[b] = 0;
+        ra.pos_hi[b] = n_keep;
+        ra.off[b] = 0;
+    }
+    e = bgtq::launch_ring(ra, c->B, n_keep, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill store write");
+    for (int b = 0; b < c->B; ++b) {
+        int64_t* hb = hp_pos + (size_t)b * R;
+        for (int64_t j = 0; j < n_keep; ++j) hb[j] = hp[j];
+        for (int64_t j = n_keep; j < R; ++j) hb[j] = -1;
+        nhp[b] = (int32_t)n_keep;
+        nt[b] = n_prompt;
     }
     return ok();
 }

@@ -133,6 +133,11 @@ struct QuantArgs {
     int vec16;                  // set by the launcher: rows and strides allow 16-byte row loads
     int64_t tile0[BGTQ_MAXB];   // first tile touched per sequence
     int64_t pos_lo[BGTQ_MAXB], pos_hi[BGTQ_MAXB], off[BGTQ_MAXB];
+    // Gathered source rows (device int32, or null): position p of sequence b reads source row
+    // gather[b * gather_stride + p - pos_lo[b]] instead of p - off[b].
+    const int32_t* gather;
+    int64_t gather_stride;
+    int round16;                // rows are rounded to fp16 first (as if they had passed the fp16 store)
 };
 
 // Copy rows into the fp16 ring: position p -> slot p % n_recent, for p in [pos_lo[b], pos_hi[b]).
@@ -145,6 +150,8 @@ struct RingArgs {
     uint16_t* ring_v;
     int Hkv, n_recent;
     int64_t pos_lo[BGTQ_MAXB], pos_hi[BGTQ_MAXB], off[BGTQ_MAXB];
+    const int32_t* gather;      // as QuantArgs::gather (null: row p - off[b])
+    int64_t gather_stride;
 };
 
 // Reorder the rows of the high-precision store (log-based filter): for a sequence b with
@@ -155,13 +162,16 @@ struct PermuteArgs {
     uint16_t* rows_k;           // [B][Hkv][n_recent][128] for this layer
     uint16_t* rows_v;
     int Hkv, n_recent;
-    int16_t seq_first[BGTQ_MAXB];
+    int32_t seq_first[BGTQ_MAXB];
+    const int16_t* perm_dev;    // the permutation in device memory (caller workspace), or null: perm
     int16_t perm[BGTQ_PERM_MAX];
 };
 
 // Launchers (bgtq_kernels.hip; launch_permute in bgtq_logquant.hip).  Return hipSuccess or the
 // launch error.
 hipError_t launch_permute(const PermuteArgs& a, int B, hipStream_t s);
+// Host memory to the device, enqueued on s (the log-based filter's permutations and gather indices).
+hipError_t copy_to_device(void* dst, const void* src, size_t bytes, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int B, int k_mode, int R, int v_bits, bool vector_only, hipStream_t s);
 // Block-GTQ keys at g = 4 or 8 (bgtq_decode_gtq.hip): one workgroup of kGtqWaves waves per split.
 hipError_t launch_decode_gtq(const DecodeArgs& a, int B, int R, int v_bits, hipStream_t s);

@@ -1594,8 +1594,12 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
         act = p >= a.pos_lo[b] && p < a.pos_hi[b];
         int64_t row = 0;
         if (act) {
-            row = p - a.off[b];
-            if (a.mod_n) row %= a.mod_n;
+            if (a.gather) {
+                row = a.gather[b * a.gather_stride + (p - a.pos_lo[b])];
+            } else {
+                row = p - a.off[b];
+                if (a.mod_n) row %= a.mod_n;
+            }
         }
         return (int64_t)b * a.sB + row * a.sT + (int64_t)h * a.sH;
     };
@@ -1625,8 +1629,23 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
                 s_x[lane * XS + j] = v;
             }
         }
+        int xdt = a.dtype;
+        if (a.round16) {
+            // rows as the fp16 store holds them: each lane rounds its own row in place
+            __syncthreads();
+            XT* r = s_x + lane * XS;
+            for (int j = 0; j < D; ++j) {
+                if constexpr (sizeof(XT) == 4) {
+                    r[j] = h2f(f2h(r[j]));
+                } else {
+                    const float f = a.dtype == BGTQ_F16 ? h2f(r[j]) : bf2f(r[j]);
+                    r[j] = f2h(f);
+                }
+            }
+            if constexpr (sizeof(XT) == 2) xdt = BGTQ_F16;
+        }
         __syncthreads();
-        const XRow<XT> x{s_x + lane * XS, a.dtype};
+        const XRow<XT> x{s_x + lane * XS, xdt};
         // The row rotated to y = H (s * x) / 16 (fast transform: stages 1, 2, ..., 64, one fp32
         // addition or subtraction per output, the 1/16 exact), staged as fp32 in this lane's row of
         // s_y; sg: the (layer, kv head)'s sign bits.
@@ -1777,16 +1796,19 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
     }
 }
 
-// Quantize-append of a few tokens: one workgroup (one wave) per (tile, kv head, sequence) takes
-// the tile's new tokens one after another, the whole wave on each token (lane i holds RoPE block i,
-// dims 2i and 2i+1), so one new token costs a few short chains instead of one lane's full
-// sequential pass.  Every float step is the one k_quant takes (rows convert to fp32 exactly from
+// Quantize-append of a few tokens: one workgroup of NW waves per (tile, kv head, sequence); wave w
+// takes the tile's new tokens w, w + NW, ... one after another, the whole wave on each token
+// (lane i holds RoPE block i, dims 2i and 2i+1), so one new token costs a few short chains instead
+// of one lane's full sequential pass, and NW tokens run at once.  Every float step is the one k_quant takes (rows convert to fp32 exactly from
 // all three activation formats): the same scale sum in the same order, the same threshold
 // products and searches, the same affine min/max order.  Key records and value streams
-// are assembled in LDS (atomicOr of each lane's fields) and written once; value dwords keep the
-// bits of other positions (read-modify-write; the tile belongs to this workgroup alone).
-__global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
-    const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+// are assembled in LDS (atomicOr of each lane's fields: a record per wave, the tile's value streams
+// shared) and written once; value dwords keep the bits of other positions (read-modify-write by
+// wave 0 at the end; the tile belongs to this workgroup alone).
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_append(const QuantArgs a) {
+    const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t tile = a.tile0[b] + blockIdx.x;
     const int64_t t0 = tile * TILE;
     if (t0 >= a.pos_hi[b]) return;  // whole workgroup beyond this sequence's range
@@ -1799,32 +1821,40 @@ __global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
     // memory round trip covers the rows, this lane's value-stream dwords, the metadata and the
     // thresholds (the tile's value dwords are this workgroup's alone until it ends).
     auto row_src = [&](int u) -> int64_t {
-        int64_t row = t0 + u - a.off[b];
-        if (a.mod_n) row %= a.mod_n;
+        int64_t row;
+        if (a.gather) {
+            row = a.gather[b * a.gather_stride + (t0 + u - a.pos_lo[b])];
+        } else {
+            row = t0 + u - a.off[b];
+            if (a.mod_n) row %= a.mod_n;
+        }
         return (int64_t)b * a.sB + row * a.sT + (int64_t)h * a.sH + 2 * lane;
     };
     float kx0 = 0.f, kx1 = 0.f, vx0 = 0.f, vx1 = 0.f;
+    auto r16 = [&](float x) { return a.round16 ? h2f(f2h(x)) : x; };  // as the fp16 store holds it
     auto load_rows = [&](int u) {
         const int64_t src = row_src(u);
         if (do_k) {
-            kx0 = load_act(a.src_k, src, a.dtype);
-            kx1 = load_act(a.src_k, src + 1, a.dtype);
+            kx0 = r16(load_act(a.src_k, src, a.dtype));
+            kx1 = r16(load_act(a.src_k, src + 1, a.dtype));
         }
         if (do_v) {
-            vx0 = load_act(a.src_v, src, a.dtype);
-            vx1 = load_act(a.src_v, src + 1, a.dtype);
+            vx0 = r16(load_act(a.src_v, src, a.dtype));
+            vx1 = r16(load_act(a.src_v, src + 1, a.dtype));
         }
     };
-    if (u_lo < u_hi) load_rows(u_lo);
+    if (u_lo + wave < u_hi) load_rows(u_lo + wave);
     uint32_t* vt = (uint32_t*)(a.v_codes + (bh * a.n_tiles + tile) * a.v_tile_bytes);
     uint32_t old[16];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) old[c] = (do_v && c < 4 * vb) ? vt[((c >> 2) * 64 + lane) * 4 + (c & 3)] : 0u;
+    for (int c = 0; c < 16; ++c)
+        old[c] = (wave == 0 && do_v && c < 4 * vb) ? vt[((c >> 2) * 64 + lane) * 4 + (c & 3)] : 0u;
     __shared__ float s_thr[BGTQ_CB_THRESHOLDS];
-    __shared__ uint32_t s_rec[32];
+    __shared__ uint32_t s_recs[NW][32];
     __shared__ uint32_t s_vv[64 * 16], s_vm[64 * 16];  // value streams of the tile: bits and written mask
-    for (int i = lane; i < BGTQ_CB_THRESHOLDS; i += 64) s_thr[i] = __builtin_bit_cast(float, c_thr32[i]);
-    for (int i = lane; i < 64 * 16; i += 64) s_vv[i] = s_vm[i] = 0u;
+    uint32_t* s_rec = s_recs[wave];
+    for (int i = threadIdx.x; i < BGTQ_CB_THRESHOLDS; i += 64 * NW) s_thr[i] = __builtin_bit_cast(float, c_thr32[i]);
+    for (int i = threadIdx.x; i < 64 * 16; i += 64 * NW) s_vv[i] = s_vm[i] = 0u;
     if (lane < 32) s_rec[lane] = 0u;
     const bool gtq = a.k_mode == BGTQ_K_BLOCKGTQ;
     int w = 0, off = 0;  // this lane's block: width and bit offset in the key record
@@ -1841,13 +1871,13 @@ __global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
         }
     }
     __syncthreads();
-    for (int u = u_lo; u < u_hi; ++u) {
+    for (int u = u_lo + wave; u < u_hi; u += NW) {
         const int64_t pos = t0 + u;
-        if (u > u_lo) load_rows(u);
+        if (u > u_lo + wave) load_rows(u);
         for (int pass = 0; pass < 2; ++pass) {
             if ((pass == 0 && !do_k) || (pass == 1 && !do_v)) continue;
             const float x0 = pass == 0 ? kx0 : vx0, x1 = pass == 0 ? kx1 : vx1;
-            __syncthreads();  // the previous token or pass is done with the record and streams
+            wave_lds_fence();  // the wave's previous token or pass is done with its record
             if (pass == 0) {
                 uint32_t* kt = (uint32_t*)(a.k_codes + (bh * a.n_tiles + tile) * a.k_tile_bytes);
                 if (gtq) {
@@ -1892,7 +1922,7 @@ __global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
                         a.k_zero[(bh * a.n_cap + pos) * ng + gi] = zz16;
                     }
                 }
-                __syncthreads();
+                wave_lds_fence();
                 if (lane < a.R) {
                     kt[lane * TILE + u] = s_rec[lane];
                     s_rec[lane] = 0u;
@@ -1955,6 +1985,7 @@ __global__ __launch_bounds__(64) void k_append(const QuantArgs a) {
     }
     if (!do_v) return;
     __syncthreads();
+    if (wave != 0) return;
     // this lane's stream: the written fields merged into the dwords read at the start
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
@@ -1968,7 +1999,7 @@ __global__ __launch_bounds__(128) void k_ring(const RingArgs a) {
     const int h = blockIdx.y, b = blockIdx.z, j = threadIdx.x;
     const int64_t pos = a.pos_lo[b] + blockIdx.x;
     if (pos >= a.pos_hi[b]) return;
-    const int64_t row = pos - a.off[b];
+    const int64_t row = a.gather ? (int64_t)a.gather[b * a.gather_stride + (pos - a.pos_lo[b])] : pos - a.off[b];
     const int64_t src = (int64_t)b * a.sB + row * a.sT + (int64_t)h * a.sH + j;
     const size_t dst = (((size_t)b * a.Hkv + h) * a.n_recent + (size_t)(pos % a.n_recent)) * D + j;
     a.ring_k[dst] = f2h(load_act(a.k, src, a.dtype));
@@ -1980,6 +2011,10 @@ __global__ __launch_bounds__(128) void k_ring(const RingArgs a) {
 // ---------------------------------------------------------------------------------------------
 // Launchers
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+hipError_t copy_to_device(void* dst, const void* src, size_t bytes, hipStream_t s) {
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s);
+}
 
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s) {
     if (!a.part || !a.out || a.n_parts < 1 || a.n_parts > BGTQ_MAX_PARTS) return hipErrorInvalidValue;
@@ -2004,7 +2039,13 @@ hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_
     const bool rot = (a.k_rot && a.k_mode == BGTQ_K_AFFINE && (a.which & 1)) || (a.v_rot && (a.which & 2));
     int64_t most = 0;  // the most positions any sequence appends
     for (int b = 0; b < B; ++b) most = std::max<int64_t>(most, a.pos_hi[b] - a.pos_lo[b]);
-    if (!rot && most <= kAppendFewMax) return launch_main(k_append, grid, dim3(64), s, q);
+    if (!rot && most <= kAppendFewMax) {
+        // one wave per token in flight, up to 16 (each wave takes every NW-th token of its tile)
+        const int per_tile = most < TILE ? (int)most : TILE;
+        if (per_tile <= 1) return launch_main(k_append<1>, grid, dim3(64), s, q);
+        if (per_tile <= 4) return launch_main(k_append<4>, grid, dim3(256), s, q);
+        return launch_main(k_append<16>, grid, dim3(1024), s, q);
+    }
     if (rot) {
         if (a.dtype == BGTQ_F32) return launch_main(k_quant<float, true>, grid, dim3(64), s, q);
         return launch_main(k_quant<uint16_t, true>, grid, dim3(64), s, q);

@@ -12,7 +12,8 @@ constexpr int D = 128;
 constexpr int COLS = 32;  // dims per workgroup
 
 // Grid (D / COLS, kv head, sequence), 256 threads: the workgroup stages its COLS-dim column of
-// every store row in LDS, then writes row j from staged row perm[j]; keys, then values.
+// every store row in LDS, then writes row j from staged row perm[j] (from the arguments, or from
+// device memory when the permutations of all sequences exceed them); keys, then values.
 __global__ __launch_bounds__(256) void k_hp_permute(const PermuteArgs a) {
     const int c0 = blockIdx.x * COLS, h = blockIdx.y, b = blockIdx.z;
     const int first = a.seq_first[b];
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(256) void k_hp_permute(const PermuteArgs a) {
         __syncthreads();
         for (int i = threadIdx.x; i < R * COLS; i += 256) {
             const int r = i / COLS, c = i % COLS;
-            base[r * D + c0 + c] = s_col[a.perm[first + r] * COLS + c];
+            base[r * D + c0 + c] = s_col[(a.perm_dev ? a.perm_dev[first + r] : a.perm[first + r]) * COLS + c];
         }
     }
 }

@@ -12,6 +12,9 @@
 namespace {
 std::string g_log;
 int g_launches = 0;
+// the last host-to-device copy: destination and bytes (stands in for the device memory it filled)
+const void* g_copy_dst = nullptr;
+std::string g_copy;
 hipError_t bad(const char* what) {
     g_log += std::string("BAD ") + what + "\n";
     return hipErrorInvalidValue;
@@ -27,6 +30,14 @@ extern "C" int bgtq_mock_launches(void) { return g_launches; }
 extern "C" void bgtq_mock_reset(void) {
     g_log.clear();
     g_launches = 0;
+    g_copy_dst = nullptr;
+    g_copy.clear();
+}
+// Bytes of the last host-to-device copy (up to max), for tests; returns how many there were.
+extern "C" int64_t bgtq_mock_last_copy(void* out, int64_t max) {
+    const int64_t n = (int64_t)g_copy.size();
+    if (out) std::memcpy(out, g_copy.data(), (size_t)(n < max ? n : max));
+    return n;
 }
 
 namespace bgtq {
@@ -108,8 +119,27 @@ hipError_t launch_energy(const EnergyArgs& a, hipStream_t) {
     return hipSuccess;
 }
 
+hipError_t copy_to_device(void* dst, const void* src, size_t bytes, hipStream_t) {
+    if (!dst || !src || bytes == 0) return bad("copy: args");
+    g_copy_dst = dst;
+    g_copy.assign((const char*)src, bytes);
+    note("copy");
+    return hipSuccess;
+}
+
+// Device int32 indices the host copied just before (the mock's only device memory).
+static bool copied_range(const void* p, int64_t n) {
+    const char* c = (const char*)p;
+    const char* d = (const char*)g_copy_dst;
+    return d && c >= d && c + n * 4 <= d + g_copy.size();
+}
+
 hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_t) {
     if (max_tiles <= 0) return hipSuccess;
+    if (a.gather) {
+        for (int b = 0; b < B; ++b)
+            if (!copied_range(a.gather + b * a.gather_stride, a.pos_hi[b] - a.pos_lo[b])) return bad("quant: gather");
+    }
     if (!a.src_k || !a.src_v || !a.k_codes || !a.v_codes || !a.k_scale || !a.v_scale) return bad("quant: null");
     if (a.k_mode == BGTQ_K_BLOCKGTQ && (!a.bits || !a.sigma || !a.inv_sigma)) return bad("quant: null metadata");
     if (a.k_mode == BGTQ_K_AFFINE && !a.k_zero) return bad("quant: null k_zero");
@@ -118,7 +148,8 @@ hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_
         if (a.pos_lo[b] < 0 || a.pos_hi[b] < a.pos_lo[b] || a.pos_hi[b] > a.n_cap) return bad("quant: range");
         if (a.tile0[b] != a.pos_lo[b] / 64) return bad("quant: tile0");
         if (a.pos_hi[b] > a.pos_lo[b] && (a.pos_hi[b] - 1) / 64 - a.tile0[b] + 1 > max_tiles) return bad("quant: grid");
-        if (a.mod_n == 0 && a.pos_hi[b] > a.pos_lo[b] && a.pos_lo[b] - a.off[b] < 0) return bad("quant: source row");
+        if (!a.gather && a.mod_n == 0 && a.pos_hi[b] > a.pos_lo[b] && a.pos_lo[b] - a.off[b] < 0)
+            return bad("quant: source row");
     }
     note("quant");
     return hipSuccess;
@@ -127,8 +158,11 @@ hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_
 hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t) {
     if (max_rows <= 0) return hipSuccess;
     if (!a.k || !a.v || !a.ring_k || !a.ring_v || a.n_recent < 1) return bad("ring: null");
-    for (int b = 0; b < B; ++b)
-        if (a.pos_hi[b] - a.pos_lo[b] > max_rows || a.pos_lo[b] < a.off[b]) return bad("ring: range");
+    for (int b = 0; b < B; ++b) {
+        if (a.pos_hi[b] - a.pos_lo[b] > max_rows || a.pos_hi[b] > a.n_recent + a.pos_lo[b]) return bad("ring: range");
+        if (a.gather ? !copied_range(a.gather + b * a.gather_stride, a.pos_hi[b] - a.pos_lo[b]) : a.pos_lo[b] < a.off[b])
+            return bad("ring: source rows");
+    }
     note("ring");
     return hipSuccess;
 }
@@ -138,10 +172,17 @@ hipError_t launch_permute(const PermuteArgs& a, int B, hipStream_t) {
     for (int b = 0; b < B; ++b) {
         const int f = a.seq_first[b];
         if (f < 0) continue;
-        if (f + a.n_recent > BGTQ_PERM_MAX) return bad("permute: range");
+        const int16_t* perm = a.perm;
+        if (a.perm_dev) {
+            if (!copied_range(a.perm_dev, 0) || (int64_t)(f + a.n_recent) * 2 > (int64_t)g_copy.size())
+                return bad("permute: device permutation");
+            perm = (const int16_t*)g_copy.data();
+        } else if (f + a.n_recent > BGTQ_PERM_MAX) {
+            return bad("permute: range");
+        }
         std::string seen(a.n_recent, 0);
         for (int j = 0; j < a.n_recent; ++j) {
-            const int r = a.perm[f + j];
+            const int r = perm[f + j];
             if (r < 0 || r >= a.n_recent || seen[r]) return bad("permute: not a permutation");
             seen[r] = 1;
         }

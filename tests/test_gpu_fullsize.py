@@ -80,3 +80,48 @@ def test_full_size_fp16_comparator():
     ref = pipeline.fp16_decode(k16.cpu().numpy(), v16.cpu().numpy(), q.float().cpu().numpy())
     e = T.assert_close(out, ref, "fp16 comparator, full size")
     print(f"  max abs err {e:.2e}", flush=True)
+
+
+def test_full_size_logquant_prefill():
+    """LogQuant's filter over a 131072-token prompt in one call at the headline shape (Qwen2.5-3B:
+    16 query / 2 kv heads, K3V3, W = 64): for kv head 0 the whole packed store equals the oracle's
+    store of the leaving tokens in leaving order (bit-exact), the high-precision store holds the kept
+    rows, and the decode over both matches the oracle."""
+    from oracle import logquant as lq
+    import packed_cache_decode_block_amd as P
+    w = synth.reduced(synth.WORKLOADS[2], L=1)
+    N, W, g = w.N, 64, w.g
+    kept, left = lq.select(N, W)
+    n_cap = (len(left) + 63) // 64 * 64
+    print(f"[full size] log-based filter prefill: N={N} W={W}: {len(left)} packed + {len(kept)} fp16", flush=True)
+    m = T.meta(w, 0)
+    cache = P.PackedCache(L=1, B=1, Hq=w.Hq, Hkv=w.Hkv, n_cap=n_cap, budget_units=w.k_budget_units,
+                          v_bits=w.v_bits, logquant_w=W)
+    cache.set_metadata(0, m.bits, m.sigma, m.r)
+    kk = torch.stack([sg.keys(w, 0, h, 0, N) for h in range(w.Hkv)], dim=1)[None]     # [1, N, Hkv, d]
+    vv = torch.stack([sg.values(w, 0, h, 0, N) for h in range(w.Hkv)], dim=1)[None]
+    q = torch.stack([torch.cat([sg.queries(w, 0, h, 0, N) for h in range(w.Hkv)])])
+    cache.logquant_prefill(0, kk, vv)
+    out = cache.decode_attention(0, q).cpu().numpy()
+    torch.cuda.synchronize()
+    assert cache.n_tokens[0, 0] == N and cache.n_hp[0, 0] == len(kept) and cache.hp_pos[0, 0, :len(kept)].tolist() == kept
+    h = 0
+    K = kk[0, :, h].float().cpu().numpy()
+    V = vv[0, :, h].float().cpu().numpy()
+    k16 = K[left].astype(np.float16).astype(np.float32)[None, None]
+    v16 = V[left].astype(np.float16).astype(np.float32)[None, None]
+    wb = synth.reduced(w, B=1, Hkv=1, Hq=g)
+    oc = pipeline.build_layer(k16, v16, k_mode="gtq", v_mode="codebook", v_bits=w.v_bits, n_cap=n_cap,
+                              meta=_pair_meta(m, h))
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale"):
+        ref = getattr(oc, name)
+        got = T.layer_view(getattr(cache, name), 1, 0, (1, w.Hkv) + ref.shape[2:])[0, h].cpu().numpy()
+        if ref.dtype == np.float16:
+            got, ref = got.view(np.uint16), ref.view(np.uint16)
+        np.testing.assert_array_equal(got, ref[0, 0], f"{name} (h={h})")
+    oc.recent_k = K[kept].astype(np.float16)[None, None]
+    oc.recent_v = V[kept].astype(np.float16)[None, None]
+    oc.n_recent_valid = len(kept)
+    ref = pipeline.decode_layer(oc, q[:, h * g:(h + 1) * g].float().cpu().numpy())
+    e = T.assert_close(out[:, h * g:(h + 1) * g], ref, "prefill full size")
+    print(f"  kv head {h}: packed store exact, max abs err {e:.2e}", flush=True)

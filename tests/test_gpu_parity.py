@@ -631,6 +631,75 @@ def test_decode_step_rotated_keys():
     _compare_cache(cache, oc, w)
 
 
+PREFILL_CASES = {
+    # name: (workload id, overrides, W, prompt tokens): Block-GTQ at 8 and 4 query heads per kv head
+    # (two sequences), fp32 rows at one (their fp16 rounding matters), affine K4V2
+    "g8_w4": (2, {"L": 1, "B": 1}, 4, 700),
+    "g4_b2_w8": (3, {"L": 1, "B": 2}, 8, 1500),
+    "g1_fp32_w2": (1, {}, 2, 300),
+    "affine_b2_w16": (4, {"L": 1, "B": 2}, 16, 1100),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_CASES))
+def test_logquant_prefill_matches_oracle(name):
+    """LogQuant's filter over a whole prompt in one call: the packed store equals the oracle's
+    store of the leaving tokens (fp16-rounded, as they leave the store) in leaving order, bit-exact;
+    the high-precision store holds the kept positions' fp16 rows in position order; decode matches
+    the oracle; and a cache fed the same prompt token by token holds the same packed bytes."""
+    from oracle import logquant as lq
+    wid, ov, W, N = PREFILL_CASES[name]
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
+    print(f"[prefill {name}] W={W} N={N} B={w.B} Hq={w.Hq} Hkv={w.Hkv}", flush=True)
+    kept, left = lq.select(N, W)
+    n_cap, R = (len(left) + 63) // 64 * 64 + 64, 3 * W
+    m = T.meta(w, 0)
+    K, V, _ = T.inputs(w, 0, N)
+    caches = []
+    for _ in range(2):
+        c = P.PackedCache(L=1, B=w.B, Hq=w.Hq, Hkv=w.Hkv, n_cap=n_cap,
+                          k_mode=P.K_BLOCKGTQ if w.k_mode == "gtq" else P.K_AFFINE,
+                          budget_units=w.k_budget_units or 128, k_bits=w.k_bits or 4, k_group=w.k_group or 32,
+                          v_mode=P.V_CODEBOOK if w.v_mode == "codebook" else P.V_AFFINE, v_bits=w.v_bits,
+                          logquant_w=W)
+        if m is not None:
+            c.set_metadata(0, m.bits, m.sigma, m.r)
+        caches.append(c)
+    cache, ref_cache = caches
+    kd = T.to_dev(np.transpose(K, (0, 2, 1, 3)), w.dtype)
+    vd = T.to_dev(np.transpose(V, (0, 2, 1, 3)), w.dtype)
+    cache.logquant_prefill(0, kd, vd)
+    torch.cuda.synchronize()
+    assert (cache.n_tokens[0] == N).all() and (cache.n_hp[0] == len(kept)).all()
+    k16 = K[:, :, left].astype(np.float16).astype(np.float32)
+    v16 = V[:, :, left].astype(np.float16).astype(np.float32)
+    oc = pipeline.build_layer(k16, v16, k_mode=w.k_mode, v_mode=w.v_mode, v_bits=w.v_bits, n_cap=n_cap, meta=m,
+                              k_bits=w.k_bits or 4, k_group=w.k_group or 32)
+    _compare_cache(cache, oc, w)
+    rk = T.layer_view(cache.recent_k, 1, 0, (w.B, w.Hkv, R, 128)).cpu().numpy()
+    rv = T.layer_view(cache.recent_v, 1, 0, (w.B, w.Hkv, R, 128)).cpu().numpy()
+    for b in range(w.B):
+        assert cache.hp_pos[0, b, :len(kept)].tolist() == kept
+        np.testing.assert_array_equal(rk[b, :, :len(kept)].view(np.uint16),
+                                      K[b][:, kept].astype(np.float16).view(np.uint16), f"store k b={b}")
+        np.testing.assert_array_equal(rv[b, :, :len(kept)].view(np.uint16),
+                                      V[b][:, kept].astype(np.float16).view(np.uint16), f"store v b={b}")
+    oc.recent_k = K[:, :, kept].astype(np.float16)
+    oc.recent_v = V[:, :, kept].astype(np.float16)
+    oc.n_recent_valid = len(kept)
+    q = np.stack([np.concatenate([synth.queries(w, 0, h, b, N) for h in range(w.Hkv)]) for b in range(w.B)])
+    out = cache.decode_attention(0, T.to_dev(q, w.dtype)).cpu().numpy()
+    e = T.assert_close(out, pipeline.decode_layer(oc, q), f"prefill {name}")
+    print(f"  {len(left)} packed + {len(kept)} fp16, max abs err {e:.2e}", flush=True)
+    for p in range(N):
+        ref_cache.logquant_append(0, kd[:, p:p + 1], vd[:, p:p + 1])
+    torch.cuda.synchronize()
+    for name_ in ("k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero"):
+        a, r = getattr(cache, name_), getattr(ref_cache, name_)
+        if a is not None:
+            assert torch.equal(a, r), f"{name_}: prefill and token-by-token appends differ"
+
+
 @pytest.mark.parametrize("wid,W,N", [(2, 4, 70), (3, 8, 100), (1, 2, 40), (4, 4, 60)])
 def test_logquant_appends_match_oracle(wid, W, N):
     """LogQuant's log-based filter through the device: after token-by-token appends, the packed

@@ -14,6 +14,8 @@ FAKE = 0x7F0000000000  # never dereferenced: the mocks only inspect argument blo
 def mock():
     lib = _lib.bind(build_lib.build_mock(), optional=("bgtq_decode_attention_noalloc",))
     lib.bgtq_mock_log.restype = C.c_char_p
+    lib.bgtq_mock_last_copy.restype = C.c_int64
+    lib.bgtq_mock_last_copy.argtypes = [C.c_void_p, C.c_int64]
     return lib
 
 
@@ -176,7 +178,7 @@ def test_logquant_append_plan_and_failures(mock):
     p64 = C.POINTER(C.c_int64)
     for p in range(40):
         mock.bgtq_mock_reset()
-        log = _call_ok(mock, mock.bgtq_logquant_append(C.byref(d), 0, q, q, 2, None, hp.ctypes.data_as(p64), None))
+        log = _call_ok(mock, mock.bgtq_logquant_append(C.byref(d), 0, q, q, 2, None, hp.ctypes.data_as(p64), None, 0, None))
         steps = [ln for ln in log.splitlines() if ln]
         kept, left = lq.select(p + 1, W)
         thinned = len(left) > len(lq.select(p, W)[1])          # the oracle halved at this token
@@ -187,17 +189,17 @@ def test_logquant_append_plan_and_failures(mock):
     assert mock.bgtq_quantize_append(C.byref(d), 0, q, q, 2, 1, None, None) == _lib.E_INVALID
     # errors: no store positions array, an inconsistent count, capacity; nothing changes
     snap = (nt.copy(), n_hp.copy(), hp.copy())
-    assert mock.bgtq_logquant_append(C.byref(d), 0, q, q, 2, None, None, None) == _lib.E_INVALID
+    assert mock.bgtq_logquant_append(C.byref(d), 0, q, q, 2, None, None, None, 0, None) == _lib.E_INVALID
     n_hp[0, 1] = 3 * W + 1
-    assert mock.bgtq_logquant_append(C.byref(d), 0, q, q, 2, None, hp.ctypes.data_as(p64), None) == _lib.E_INVALID
+    assert mock.bgtq_logquant_append(C.byref(d), 0, q, q, 2, None, hp.ctypes.data_as(p64), None, 0, None) == _lib.E_INVALID
     n_hp[0, 1] = snap[1][0, 1]
     d2 = _desc(nt, L=1, n_recent=3 * W, n_cap=64)
     d2.n_hp = d.n_hp
     while n_hp[0, 0] < 3 * W:                                   # fill to the ceiling, then overflow n_cap
-        _call_ok(mock, mock.bgtq_logquant_append(C.byref(d2), 0, q, q, 2, None, hp.ctypes.data_as(p64), None))
+        _call_ok(mock, mock.bgtq_logquant_append(C.byref(d2), 0, q, q, 2, None, hp.ctypes.data_as(p64), None, 0, None))
     nt[0] = 100
     pre = (nt.copy(), n_hp.copy(), hp.copy())
-    assert mock.bgtq_logquant_append(C.byref(d2), 0, q, q, 2, None, hp.ctypes.data_as(p64), None) == _lib.E_CAPACITY
+    assert mock.bgtq_logquant_append(C.byref(d2), 0, q, q, 2, None, hp.ctypes.data_as(p64), None, 0, None) == _lib.E_CAPACITY
     assert (nt == pre[0]).all() and (n_hp == pre[1]).all() and (hp == pre[2]).all()
 
 
@@ -272,3 +274,66 @@ def test_value_rotation_needs_no_fp16_window(mock):
     mock.bgtq_mock_reset()
     log = _call_ok(mock, mock.bgtq_decode_step(C.byref(d2), 1, q, q, q, 2, 1, None, q, ws, need, 0, None))
     assert "append" not in log and ("quant" in log), log
+
+
+def test_logquant_permutation_in_workspace(mock):
+    """Above 1536 permutation entries (B * 3W) the store permutation goes through the caller's
+    workspace: refused without one, copied there (a valid permutation per sequence) with one."""
+    from oracle import logquant as lq
+    W = 64
+    B = 9                                                          # 9 * 192 = 1728 entries
+    nt = np.zeros((1, B), np.int64)
+    d = _desc(nt, L=1, B=B, n_recent=3 * W)
+    n_hp = np.zeros((1, B), np.int32)
+    d.n_hp = n_hp.ctypes.data_as(C.POINTER(C.c_int32))
+    hp = np.zeros((B, 3 * W), np.int64)
+    q = C.c_void_p(FAKE + 0x50000000)
+    p64 = C.POINTER(C.c_int64)
+    need = mock.bgtq_logquant_workspace_bytes(C.byref(d), 0)
+    assert need >= B * 3 * W * 2 and need % 256 == 0
+    ws = C.c_void_p(FAKE + 0x60000000)
+    assert mock.bgtq_logquant_append(C.byref(d), 0, q, q, 2, None, hp.ctypes.data_as(p64), None, 0, None) == _lib.E_INVALID
+    assert mock.bgtq_logquant_append(C.byref(d), 0, q, q, 2, None, hp.ctypes.data_as(p64), ws, need - 256, None) == _lib.E_INVALID
+    assert (nt == 0).all()
+    for p in range(3 * W + 1):
+        mock.bgtq_mock_reset()
+        log = _call_ok(mock, mock.bgtq_logquant_append(C.byref(d), 0, q, q, 2, None, hp.ctypes.data_as(p64), ws, need, None))
+    assert log.split() == ["copy", "permute", "quant", "ring"], log
+    kept, _ = lq.select(3 * W + 1, W)
+    assert (n_hp[0] == len(kept)).all() and all(sorted(hp[b, :len(kept)]) == kept for b in range(B))
+
+
+def test_logquant_prefill_gathers_the_oracle_selection(mock):
+    """The one-call prefill: the gather indices it copies are the oracle's leaving tokens in leaving
+    order, then the kept ones; the quantize and the store write read them; the bookkeeping ends as
+    n_prompt one-token appends leave it (slot order aside).  Errors change nothing."""
+    from oracle import logquant as lq
+    W, B, n = 8, 2, 1000
+    nt = np.zeros((1, B), np.int64)
+    d = _desc(nt, L=1, B=B, n_recent=3 * W, n_cap=1024)
+    n_hp = np.zeros((1, B), np.int32)
+    d.n_hp = n_hp.ctypes.data_as(C.POINTER(C.c_int32))
+    hp = np.zeros((B, 3 * W), np.int64)
+    q = C.c_void_p(FAKE + 0x50000000)
+    p64 = C.POINTER(C.c_int64)
+    ws = C.c_void_p(FAKE + 0x60000000)
+    need = mock.bgtq_logquant_workspace_bytes(C.byref(d), n)
+    assert need >= (n + 3 * W) * 4
+    pre = lambda ws_, nb, n_=n: mock.bgtq_logquant_prefill(C.byref(d), 0, q, q, 2, n_, None, hp.ctypes.data_as(p64),
+                                                           ws_, nb, None)
+    for call, code in ((lambda: pre(None, 0), _lib.E_INVALID), (lambda: pre(ws, need - 256), _lib.E_INVALID),
+                       (lambda: pre(ws, need, 0), _lib.E_INVALID),
+                       (lambda: pre(ws, mock.bgtq_logquant_workspace_bytes(C.byref(d), 1100), 1100), _lib.E_CAPACITY)):
+        mock.bgtq_mock_reset()
+        assert call() == code, mock.bgtq_last_error()
+        assert mock.bgtq_mock_launches() == 0 and (nt == 0).all() and (n_hp == 0).all()
+    mock.bgtq_mock_reset()
+    log = _call_ok(mock, pre(ws, need))
+    assert log.split() == ["copy", "quant", "ring"], log
+    kept, left = lq.select(n, W)
+    idx = np.zeros(len(left) + len(kept), np.int32)
+    assert mock.bgtq_mock_last_copy(idx.ctypes.data_as(C.c_void_p), idx.nbytes) == idx.nbytes
+    assert list(idx[:len(left)]) == left and list(idx[len(left):]) == kept
+    assert (nt[0] == n).all() and (n_hp[0] == len(kept)).all()
+    assert all(list(hp[b, :len(kept)]) == kept for b in range(B)) and (hp[:, len(kept):] == -1).all()
+    assert pre(ws, need) == _lib.E_INVALID                         # a started layer is refused
