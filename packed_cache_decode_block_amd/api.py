@@ -83,10 +83,12 @@ class LogQuantPlanner:
     (bgtq_logquant_plan): which store rows leave for the low-bit store, how the store compacts,
     and where the new token's row goes."""
 
-    def __init__(self, W: int):
+    def __init__(self, W: int, library=None):
+        """library: a library exporting bgtq_logquant_plan (default: this package's)."""
         self.W = int(W)
         self.hp_pos = np.zeros(3 * self.W, np.int64)
         self.n_hp = 0
+        self._lib = library if library is not None else lib
 
     def append(self, pos: int):
         """-> (evict_slots, moves [(src, dst)], new_slot) for the token at position pos."""
@@ -96,7 +98,7 @@ class LogQuantPlanner:
         md = np.zeros(self.W, np.int32)
         nm, ns = C.c_int(0), C.c_int(0)
         p32 = C.POINTER(C.c_int32)
-        k = check(lib.bgtq_logquant_plan(self.W, self.hp_pos.ctypes.data_as(C.POINTER(C.c_int64)), C.byref(n), pos,
+        k = check(self._lib.bgtq_logquant_plan(self.W, self.hp_pos.ctypes.data_as(C.POINTER(C.c_int64)), C.byref(n), pos,
                                          ev.ctypes.data_as(p32), ms.ctypes.data_as(p32), md.ctypes.data_as(p32),
                                          C.byref(nm), C.byref(ns)))
         self.n_hp = n.value

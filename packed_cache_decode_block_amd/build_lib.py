@@ -56,10 +56,13 @@ def build(verbose: bool = False) -> str:
 
 
 MOCK = os.path.join(BUILD, "libbgtq_mock.so")
+MOCK_SAN = os.path.join(BUILD, "libbgtq_mock_san.so")
 
 
-def build_mock() -> str:
-    """Host C ABI linked against mock launchers (test-only; checks kernel arguments without a GPU)."""
+def build_mock(sanitize: bool = False) -> str:
+    """Host C ABI linked against mock launchers (test-only; checks kernel arguments without a GPU).
+    sanitize: a separate copy built with AddressSanitizer and UndefinedBehaviorSanitizer (host code
+    only; load it in a process that preloads the ASan runtime)."""
     os.makedirs(BUILD, exist_ok=True)
     gen_dir = os.path.join(CSRC, "generated")
     os.makedirs(gen_dir, exist_ok=True)
@@ -67,15 +70,19 @@ def build_mock() -> str:
     _run(["g++", "-O2", "-std=c++17", "-o", gen_exe, os.path.join(CSRC, "gen_codebook.cpp")])
     _run([gen_exe, os.path.join(gen_dir, "bgtq_codebook_data.h")])
     flags = ["-O1", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+    out = MOCK_SAN if sanitize else MOCK
+    tag = "mock_san_" if sanitize else "mock_"
     objs = []
     for u in ("bgtq_host.cpp", "mock_launch.cpp"):
-        obj = os.path.join(BUILD, "mock_" + u + ".o")
-        _run(["g++", *flags, "-c", os.path.join(CSRC, u), "-o", obj])
+        obj = os.path.join(BUILD, tag + u + ".o")
+        _run(["g++", *flags, *(san if sanitize else []), "-c", os.path.join(CSRC, u), "-o", obj])
         objs.append(obj)
-    tmp = MOCK + ".tmp"
-    _run(["g++", "-shared", "-o", tmp, *objs, "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"])
-    os.replace(tmp, MOCK)
-    return MOCK
+    tmp = out + ".tmp"
+    _run(["g++", "-shared", *(san if sanitize else []), "-o", tmp, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+          "-Wl,-rpath,/opt/rocm/lib"])
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -1,6 +1,7 @@
 """Host logic of the C ABI without a GPU: the real bgtq_host.cpp linked against mock launchers
 that check every kernel argument block (pointers set, ranges consistent) and record launches."""
 import ctypes as C
+import os
 
 import numpy as np
 import pytest
@@ -12,7 +13,10 @@ FAKE = 0x7F0000000000  # never dereferenced: the mocks only inspect argument blo
 
 @pytest.fixture(scope="module")
 def mock():
-    lib = _lib.bind(build_lib.build_mock(), optional=("bgtq_decode_attention_noalloc",))
+    # BGTQ_SANITIZED_MOCK=1: the AddressSanitizer / UBSan build (tests/test_sanitized_host.py runs
+    # this module that way, in a process that preloads the ASan runtime)
+    san = os.environ.get("BGTQ_SANITIZED_MOCK") == "1"
+    lib = _lib.bind(build_lib.build_mock(sanitize=san), optional=("bgtq_decode_attention_noalloc",))
     lib.bgtq_mock_log.restype = C.c_char_p
     lib.bgtq_mock_last_copy.restype = C.c_int64
     lib.bgtq_mock_last_copy.argtypes = [C.c_void_p, C.c_int64]

@@ -2,17 +2,28 @@
 plans on a simulated high-precision store keeps exactly the oracle's positions at every step,
 the leaving rows come out in the oracle's order, and the compaction is conflict-free."""
 import ctypes as C
+import os
 
 import numpy as np
 import pytest
 
 import packed_cache_decode_block_amd as P
 from oracle import logquant as lq
+from packed_cache_decode_block_amd import _lib, build_lib
+
+
+@pytest.fixture(scope="module")
+def plan_lib():
+    """The library's planner, or (BGTQ_SANITIZED_MOCK=1) the AddressSanitizer / UBSan build of the
+    host code, which tests/test_sanitized_host.py runs this module against."""
+    if os.environ.get("BGTQ_SANITIZED_MOCK") == "1":
+        return _lib.bind(build_lib.build_mock(sanitize=True), optional=("bgtq_decode_attention_noalloc",))
+    return P.lib
 
 
 @pytest.mark.parametrize("W", [1, 2, 3, 4, 8, 32])
-def test_plans_replay_to_the_oracle(W):
-    pl = P.LogQuantPlanner(W)
+def test_plans_replay_to_the_oracle(W, plan_lib):
+    pl = P.LogQuantPlanner(W, library=plan_lib)
     store = np.full(3 * W, -1, np.int64)        # the simulated store: token position per slot
     left = []
     n = 30 * W + 5
@@ -33,14 +44,14 @@ def test_plans_replay_to_the_oracle(W):
     assert left == lq.select(n, W)[1]
 
 
-def test_plan_errors_change_nothing():
+def test_plan_errors_change_nothing(plan_lib):
     W = 2
     hp = np.array([0, 1, 2, 3, 4, 5], np.int64)
     n = C.c_int(6)
     ev, ms, md = (np.zeros(W, np.int32) for _ in range(3))
     nm, ns = C.c_int(0), C.c_int(0)
     p64, p32 = C.POINTER(C.c_int64), C.POINTER(C.c_int32)
-    call = lambda W_, pos, n_=n: P.lib.bgtq_logquant_plan(W_, hp.ctypes.data_as(p64), C.byref(n_), pos,
+    call = lambda W_, pos, n_=n: plan_lib.bgtq_logquant_plan(W_, hp.ctypes.data_as(p64), C.byref(n_), pos,
                                                           ev.ctypes.data_as(p32), ms.ctypes.data_as(p32),
                                                           md.ctypes.data_as(p32), C.byref(nm), C.byref(ns))
     assert call(W, 5) == P.E_INVALID                           # not above the held positions
