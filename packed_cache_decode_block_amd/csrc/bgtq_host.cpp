@@ -130,6 +130,10 @@ bool uses_gtq_kernel(const bgtq_cache* c, int G) { return c->k_mode == BGTQ_K_BL
 // g >= 4: one tile per wave of a sixteen-wave workgroup when one round of workgroups covers the
 // context, else one round of eight-wave workgroups that loop over their tiles.  Other formats: the
 // per-CU heuristic of their kernel.
+// A window longer than the merge attends to itself is decoded by a split-K launch of its own, which
+// writes one more partial per query head.
+bool ring_split(int64_t n_recent) { return n_recent > bgtq::kMergeWindowMax; }
+
 int auto_splits(const bgtq_cache* c, int G, int64_t max_tiles, int bh) {
     const int n_cu = cu_count();
     if (uses_gtq_kernel(c, G)) {
@@ -850,7 +854,7 @@ int64_t bgtq_decode_workspace_bytes(const bgtq_cache* c, int n_splits) {
         ns = auto_splits(c, g.G, max_tiles, bh);
         if (uses_gtq_kernel(c, g.G)) ns = std::max(ns, std::max(1, cu_count() / bh));
     }
-    const int parts = ns + (g.n_recent > 0 ? 1 : 0);
+    const int parts = ns + (ring_split(g.n_recent) ? 1 : 0);
     if (parts > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS - 1);
     return (int64_t)g.B * g.Hq * parts * PART * 4;
 }
@@ -914,16 +918,17 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
     }
     // Default splits follow the current length; never more than the capacity-sized workspace holds.
     int ns = n_splits ? n_splits : auto_splits(c, g.G, std::max<int64_t>(max_tiles, 1), g.B * g.Hkv);
-    int parts = ns + (c->n_recent > 0 ? 1 : 0);
+    const int ring = ring_split(c->n_recent) ? 1 : 0;  // the window's own partial, when it has a launch
+    int parts = ns + ring;
     const size_t per_part = (size_t)g.B * g.Hq * PART * 4;
     if (cap_to_ws && n_splits == 0 && ws_bytes < parts * per_part) {
         // the library's choice, reduced to what the fixed workspace holds
-        const int64_t fit = (int64_t)(ws_bytes / per_part) - (c->n_recent > 0 ? 1 : 0);
+        const int64_t fit = (int64_t)(ws_bytes / per_part) - ring;
         if (fit < 1)
             return fail(BGTQ_E_UNSUPPORTED, "B*Hq = %d needs %zu bytes of partials per split, above the %zu-byte "
-                        "scratch", g.B * g.Hq, per_part * (c->n_recent > 0 ? 2 : 1), ws_bytes);
+                        "scratch", g.B * g.Hq, per_part * (1 + ring), ws_bytes);
         ns = (int)fit;
-        parts = ns + (c->n_recent > 0 ? 1 : 0);
+        parts = ns + ring;
     }
     if (parts > BGTQ_MAX_PARTS) return fail(BGTQ_E_UNSUPPORTED, "n_splits above %d", BGTQ_MAX_PARTS - 1);
     const size_t need = parts * per_part;
@@ -949,7 +954,7 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
     a.k_rot = c->k_rot ? c->k_rot + (size_t)layer * g.Hkv * 16 : nullptr;
     a.plan = uses_gtq_kernel(c, g.G) ? (const uint8_t*)c->plan + (size_t)layer * g.Hkv * BGTQ_PLAN_BYTES : nullptr;
     bgtq::Fp16Args ra{};
-    if (c->n_recent > 0) {
+    if (ring) {
         ra.k16 = (const uint16_t*)c->recent_k + (size_t)layer * bh * c->n_recent * D;
         ra.v16 = (const uint16_t*)c->recent_v + (size_t)layer * bh * c->n_recent * D;
         ra.q = q;
@@ -999,11 +1004,19 @@ int decode_attention_impl(const bgtq_cache* c, int layer, const void* q, int dty
                                     : bgtq::launch_decode(a, g.B, c->k_mode, g.R, c->v_bits, vector_only(c), s);
     }
     if (e != hipSuccess) return hip_fail(e, "decode launch");
-    if (c->n_recent > 0) {
+    bgtq::CombineArgs ca{part, out, parts, c->v_rot ? c->v_rot + (size_t)layer * g.Hkv * 16 : nullptr, g.Hq, g.G};
+    if (ring) {
         e = bgtq::launch_fp16(ra, g.B, s);
         if (e != hipSuccess) return hip_fail(e, "recent-ring decode launch");
+    } else if (c->n_recent > 0) {  // the merge attends to the window itself
+        ca.k16 = (const uint16_t*)c->recent_k + (size_t)layer * bh * c->n_recent * D;
+        ca.v16 = (const uint16_t*)c->recent_v + (size_t)layer * bh * c->n_recent * D;
+        ca.q = q;
+        ca.q_dtype = dtype;
+        ca.Hkv = g.Hkv;
+        ca.rows = c->n_recent;
+        for (int b = 0; b < c->B; ++b) ca.n_valid[b] = n_rec[b];
     }
-    bgtq::CombineArgs ca{part, out, parts, c->v_rot ? c->v_rot + (size_t)layer * g.Hkv * 16 : nullptr, g.Hq, g.G};
     e = bgtq::launch_combine(ca, g.B * g.Hq, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return ok();

@@ -75,8 +75,22 @@ struct CombineArgs {
     float* out;                 // [B*Hq][128]
     int n_parts;
     const uint8_t* v_rot;       // [Hkv][16] sign bits of the value rotation of this layer, or null
-    int Hq, G;                  // with v_rot: row r is query head r % Hq of kv head (r % Hq) / G
+    int Hq, G;                  // row r is query head r % Hq of sequence r / Hq, kv head (r % Hq) / G
+    // The fp16 window of a packed cache, attended by the merge itself (k16 null: no window):
+    // rows [B][Hkv][rows][128] fp16, the first n_valid[b] of sequence b valid, at most
+    // kMergeWindowMax; q [B][Hq][128] in q_dtype.
+    const uint16_t* k16;
+    const uint16_t* v16;
+    const void* q;
+    int q_dtype;
+    int Hkv;
+    int64_t rows;
+    int32_t n_valid[BGTQ_MAXB];
 };
+
+// Longest fp16 window the split merge attends to itself; a longer one is decoded by a split-K
+// launch of its own that writes one more partial.
+constexpr int kMergeWindowMax = 512;
 
 // fp16 tiles: rows [B][Hkv][rows][128] fp16.  Used for the unquantized comparator (all splits)
 // and for the fp16 recent ring of a packed cache (one extra split written at part index split0).

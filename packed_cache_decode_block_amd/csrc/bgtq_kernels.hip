@@ -1354,18 +1354,39 @@ __device__ __forceinline__ float wave_total_max(float v) {
 // (one coalesced 512-byte read per partial), all issued together; lane j computes the weight
 // e^(m_j - M) of partial j and readlane broadcasts it to the products.  A split without tokens
 // holds m = -inf, l = 0, o = 0 and weighs 0.  The four wave states merge through LDS.
+//
+// With WIN the merge also attends to the row's fp16 window (the packed cache's recent rows), wave
+// w taking tokens 64 w .. 64 w + 63, then 256 further on, so the window costs no launch of its own:
+// - q.k: lane (u, c) = (lane / 16, lane % 16) loads dims 32 ks + 8 u .. + 7 (ks = 0..3) of tokens
+//   16 g + c (g = 0..3), so one instruction reads 64-byte row segments of 16 tokens; the lane's 32
+//   query values are fp32 registers, and it sums its 32 dims for its 4 tokens in fp32.  Two
+//   butterfly exchanges (lane ^ 32, then lane ^ 16) leave lane l with token l's whole product.
+// - softmax over the block in the base-2 domain of the partials (q.k times log2(e)/sqrt(d));
+// - P.V: lane l loads dims 2l, 2l + 1 of each token's value row (one coalesced 256-byte row per
+//   instruction); the weights, fp32, are broadcast by readlane.
+// The block's (m, l, o) folds into the wave's state as one more partial would.  A wave's first
+// window block and its first chunk of partials are loaded together, before either is used.
 constexpr int CMB_CHUNK = 32;
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void k_combine(const CombineArgs a) {
-    const int row = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+template <bool WIN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, WIN ? 2 : 4))) void k_combine(const CombineArgs a) {
+    const int row = blockIdx.x, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: addresses stay scalar
     const float* pr = a.part + (size_t)row * a.n_parts * PART;
     float M = -INFINITY, L = 0.f, ox = 0.f, oy = 0.f;
-    for (int base = wave * CMB_CHUNK; base < a.n_parts; base += 4 * CMB_CHUNK) {
-        const int cnt = a.n_parts - base < CMB_CHUNK ? a.n_parts - base : CMB_CHUNK;
-        const float2 ml = *(const float2*)(pr + (size_t)(base + (lane < cnt ? lane : 0)) * PART + 128);
-        float2 ov[CMB_CHUNK];
+    float2 ml, ov[CMB_CHUNK];
+    // one chunk of partials from bs on (fewer than CMB_CHUNK at the end; none past it: every read
+    // is then partial 0's, and weighs 0)
+    auto chunk_count = [&](int bs) { return a.n_parts - bs < CMB_CHUNK ? a.n_parts - bs : CMB_CHUNK; };
+    auto chunk_load = [&](int bs) {
+        const int cnt = chunk_count(bs);
+        const int b0 = cnt > 0 ? bs : 0;
+        ml = *(const float2*)(pr + (size_t)(b0 + (lane < cnt ? lane : 0)) * PART + 128);
 #pragma unroll
         for (int j = 0; j < CMB_CHUNK; ++j)
-            ov[j] = *(const float2*)(pr + (size_t)(base + (j < cnt ? j : 0)) * PART + 2 * lane);
+            ov[j] = *(const float2*)(pr + (size_t)(b0 + (j < cnt ? j : 0)) * PART + 2 * lane);
+    };
+    auto chunk_fold = [&](int bs) {
+        const int cnt = chunk_count(bs);
         const float mj = lane < cnt ? ml.x : -INFINITY;
         const float mn = fmaxf(M, wave_total_max(mj));  // -inf while every split so far is empty
         const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
@@ -1380,6 +1401,134 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
             oy = fmaf(fj, ov[j].y, oy);
         }
         M = mn;
+    };
+    if constexpr (!WIN) {
+        for (int base = wave * CMB_CHUNK; base < a.n_parts; base += 4 * CMB_CHUNK) {
+            chunk_load(base);
+            chunk_fold(base);
+        }
+    } else {
+        const int u = lane >> 4, c = lane & 15;
+        const int b = row / a.Hq, h = (row % a.Hq) / a.G;
+        const int wn = a.n_valid[b];
+        const uint16_t* WK = a.k16 + ((size_t)b * a.Hkv + h) * a.rows * D;
+        const uint16_t* WV = a.v16 + ((size_t)b * a.Hkv + h) * a.rows * D;
+        u32x4_t wk[4][4];  // [g][ks]: dims 32 ks + 8 u .. of token 16 g + c
+        uint32_t wv[64];   // dims 2 lane, 2 lane + 1 of token j
+        // rows past the valid ones are never read: every index clamps to the last valid row (row 0
+        // of the window, always allocated, when none is valid)
+        auto win_load = [&](int t0) {
+            const int last = wn > 0 ? wn - 1 : 0;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int tok = t0 + 16 * g + c < last ? t0 + 16 * g + c : last;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) wk[g][ks] = ((const u32x4_t*)(WK + (size_t)tok * D))[4 * ks + u];
+            }
+#pragma unroll
+            for (int j = 0; j < 64; ++j) {
+                const int tok = t0 + j < last ? t0 + j : last;
+                wv[j] = ((const uint32_t*)(WV + (size_t)tok * D))[lane];
+            }
+        };
+        // the window block and the chunk of partials go out first, the query's raw bits last
+        // (fp32: two 16-byte pieces per k-step; fp16/bf16: one); one wait then covers them all
+        int base = wave * CMB_CHUNK;
+        win_load(64 * wave);
+        chunk_load(base);
+        float wq[32];  // query dims 32 ks + 8 u + e at [8 ks + e]
+        const size_t q0 = (size_t)row * D;
+        if (a.q_dtype == BGTQ_F32) {
+            // (loaded as float vectors and read by element: a bit cast of a vector element would
+            // take the vector's first element)
+            f32x4_t qf[8];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                qf[2 * ks] = *(const f32x4_t*)((const float*)a.q + q0 + 32 * ks + 8 * u);
+                qf[2 * ks + 1] = *(const f32x4_t*)((const float*)a.q + q0 + 32 * ks + 8 * u + 4);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    wq[8 * ks + e] = qf[2 * ks][e];
+                    wq[8 * ks + 4 + e] = qf[2 * ks + 1][e];
+                }
+        } else {
+            u32x4_t qr[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) qr[ks] = *(const u32x4_t*)((const uint16_t*)a.q + q0 + 32 * ks + 8 * u);
+            if (a.q_dtype == BGTQ_F16) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        wq[8 * ks + 2 * e] = h2f(qr[ks][e] & 0xFFFFu);
+                        wq[8 * ks + 2 * e + 1] = h2f(qr[ks][e] >> 16);
+                    }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        wq[8 * ks + 2 * e] = bf2f(qr[ks][e] & 0xFFFFu);
+                        wq[8 * ks + 2 * e + 1] = bf2f(qr[ks][e] >> 16);
+                    }
+            }
+        }
+        auto win_fold = [&](int t0) {
+            float s[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float acc = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc = fmaf(wq[8 * ks + 2 * e], h2f(wk[g][ks][e] & 0xFFFFu), acc);
+                        acc = fmaf(wq[8 * ks + 2 * e + 1], h2f(wk[g][ks][e] >> 16), acc);
+                    }
+                s[g] = acc;
+            }
+            // lanes u and u ^ 2 sum groups {0, 1} (kept where u < 2) and {2, 3}; then lanes u and
+            // u ^ 1 sum the group each keeps, u
+            const bool hi = u >= 2, odd = u & 1;
+            float t[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float send = hi ? s[i] : s[2 + i];
+                t[i] = (hi ? s[2 + i] : s[i]) + __shfl_xor(send, 32, 64);
+            }
+            const float zs = (odd ? t[1] : t[0]) + __shfl_xor(odd ? t[0] : t[1], 16, 64);
+            const float z = t0 + lane < wn ? zs * kLog2eOverSqrtD : -INFINITY;
+            const float mw = wave_total_max(z);
+            const float p = z == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z - mw);
+            const float lw = wave_total_sum(p);
+            float wx = 0.f, wy = 0.f;
+#pragma unroll
+            for (int j = 0; j < 64; ++j) {
+                const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j));
+                wx = fmaf(pj, h2f(wv[j] & 0xFFFFu), wx);
+                wy = fmaf(pj, h2f(wv[j] >> 16), wy);
+            }
+            const float mn = fmaxf(M, mw);
+            const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+            const float fw = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mn);
+            L = L * fo + lw * fw;
+            ox = ox * fo + wx * fw;
+            oy = oy * fo + wy * fw;
+            M = mn;
+        };
+        chunk_fold(base);
+        for (base += 4 * CMB_CHUNK; base < a.n_parts; base += 4 * CMB_CHUNK) {
+            chunk_load(base);
+            chunk_fold(base);
+        }
+        win_fold(64 * wave);
+        for (int t0 = 64 * wave + 256; t0 < wn; t0 += 256) {
+            win_load(t0);
+            win_fold(t0);
+        }
     }
     __shared__ float s_m[4], s_l[4];
     __shared__ float2 s_o[4][64];
@@ -2018,7 +2167,14 @@ hipError_t copy_to_device(void* dst, const void* src, size_t bytes, hipStream_t 
 
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s) {
     if (!a.part || !a.out || a.n_parts < 1 || a.n_parts > BGTQ_MAX_PARTS) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_combine, dim3(rows), dim3(256), 0, s, a);
+    if (a.k16) {
+        if (!a.v16 || !a.q || a.rows < 1 || a.Hkv < 1 || a.G < 1 || a.Hq != a.Hkv * a.G) return hipErrorInvalidValue;
+        for (int b = 0; b < rows / a.Hq; ++b)
+            if (a.n_valid[b] < 0 || a.n_valid[b] > a.rows || a.n_valid[b] > kMergeWindowMax) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_combine<true>, dim3(rows), dim3(256), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(k_combine<false>, dim3(rows), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

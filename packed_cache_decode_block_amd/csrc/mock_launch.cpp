@@ -15,6 +15,9 @@ int g_launches = 0;
 // the last host-to-device copy: destination and bytes (stands in for the device memory it filled)
 const void* g_copy_dst = nullptr;
 std::string g_copy;
+// partial records per query head of the last decode launch (0: none since the reset); the merge
+// after it must read exactly these
+int g_decode_parts = 0;
 hipError_t bad(const char* what) {
     g_log += std::string("BAD ") + what + "\n";
     return hipErrorInvalidValue;
@@ -32,6 +35,7 @@ extern "C" void bgtq_mock_reset(void) {
     g_launches = 0;
     g_copy_dst = nullptr;
     g_copy.clear();
+    g_decode_parts = 0;
 }
 // Bytes of the last host-to-device copy (up to max), for tests; returns how many there were.
 extern "C" int64_t bgtq_mock_last_copy(void* out, int64_t max) {
@@ -60,6 +64,7 @@ static hipError_t check_decode(const DecodeArgs& a, int B, int k_mode, int R, in
         if (tiles > (int64_t)a.n_splits * a.tiles_per_split) return bad("decode: splits do not cover the context");
     }
     if (a.n_tiles * 64 != a.n_cap) return bad("decode: n_tiles");
+    g_decode_parts = a.n_parts;
     return hipSuccess;
 }
 
@@ -109,6 +114,18 @@ hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t) {
 hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t) {
     if (!a.part || !a.out || a.n_parts < 1 || a.n_parts > BGTQ_MAX_PARTS || rows < 1) return bad("combine");
     if (a.v_rot && (a.Hq < 1 || a.G < 1 || a.Hq % a.G || rows % a.Hq)) return bad("combine: rotation geometry");
+    if (g_decode_parts && a.n_parts != g_decode_parts) return bad("combine: partial count differs from the decode's");
+    g_decode_parts = 0;
+    if (a.k16) {
+        if (!a.v16 || !a.q || a.rows < 1 || a.Hkv < 1 || a.G < 1 || a.Hq != a.Hkv * a.G || rows % a.Hq)
+            return bad("combine: window geometry");
+        if (a.q_dtype < 0 || a.q_dtype > 2) return bad("combine: q dtype");
+        for (int b = 0; b < rows / a.Hq; ++b)
+            if (a.n_valid[b] < 0 || a.n_valid[b] > a.rows || a.n_valid[b] > kMergeWindowMax)
+                return bad("combine: window rows");
+        note("combine_window");
+        return hipSuccess;
+    }
     note("combine");
     return hipSuccess;
 }

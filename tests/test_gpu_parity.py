@@ -51,6 +51,13 @@ CASES = {
     "w4_reduced": (4, {"L": 1, "B": 2}, 2048 + 13, (None,)),
     "w5_reduced": (5, {}, 3000, (1000, 7, None)),
     "w5_all_recent": (5, {}, 200, (None,)),
+    # fp16 windows: the merge attends to windows of up to 512 rows itself (two token blocks per
+    # wave at 512; one query head per kv head on the vector path; 4 per kv head with a ragged
+    # window), a longer window takes a split-K launch of its own
+    "w5_window_512": (5, {"n_recent": 512}, 1500 + 11, (600, None)),
+    "w1_window_g1": (1, {"n_recent": 100}, 1000 + 1, (None,)),
+    "w3_window_77": (3, {"L": 1, "B": 2, "n_recent": 77}, 500 + 3, (300, None)),
+    "w5_window_600": (5, {"n_recent": 600}, 2000 + 5, (700, None)),
     # other matrix-core template shapes: 16-dword key records with 4-bit values (one value buffer),
     # and 4 query heads per kv head with 12-dword records and 3-bit values
     "w2_k4v4": (2, {"L": 1, "v_bits": 4, "k_budget_units": 256}, 1500 + 3, (None,)),

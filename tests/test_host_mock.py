@@ -53,7 +53,8 @@ def _call_ok(mock, rc):
 
 FORMATS = [dict(), dict(budget_units=128, v_bits=2), dict(k_mode=1, k_bits=4, k_group=32, v_mode=1, v_bits=2),
            dict(budget_units=192, v_bits=2, n_recent=256), dict(budget_units=256, v_bits=4, Hq=8, Hkv=8),
-           dict(k_mode=1, k_group=128, v_bits=4, Hq=4, Hkv=2, n_recent=64)]
+           dict(k_mode=1, k_group=128, v_bits=4, Hq=4, Hkv=2, n_recent=64),
+           dict(budget_units=128, v_bits=2, n_recent=600), dict(Hq=2, Hkv=2, v_bits=2, n_recent=100)]
 
 
 @pytest.mark.parametrize("fmt", range(len(FORMATS)))
@@ -71,7 +72,10 @@ def test_append_then_decode_arguments(mock, fmt):
             assert need > 0
             log = _call_ok(mock, mock.bgtq_decode_attention(C.byref(d), 1, q, 2, q, ws, need, ns, None))
             assert log.count("decode") == 1 and log.count("combine") == 1
-            assert log.count("fp16") == (1 if d.n_recent else 0)
+            # a window of at most 512 rows is attended by the merge itself; a longer one has a
+            # split-K launch of its own
+            assert log.count("fp16") == (1 if d.n_recent > 512 else 0)
+            assert log.count("combine_window") == (1 if 0 < d.n_recent <= 512 else 0)
     assert (nt[1] == 1 + 63 + 64 + 200 + 1000).all() and (nt[0] == 0).all()
 
 
@@ -88,6 +92,17 @@ def test_ring_eviction_plan(mock):
     log = mock.bgtq_mock_log().decode()
     assert "quant" in log and "ring" in log
     assert nt[0, 0] == 400
+
+
+def test_window_partials_in_the_workspace(mock):
+    """A window the merge attends to needs no partial of its own; a longer window's launch needs
+    one more per query head."""
+    nt = np.zeros((2, 2), np.int64)
+    per_part = 2 * 16 * 132 * 4
+    for ns in (0, 1, 7):
+        base = mock.bgtq_decode_workspace_bytes(C.byref(_desc(nt)), ns)
+        assert mock.bgtq_decode_workspace_bytes(C.byref(_desc(nt, n_recent=512)), ns) == base
+        assert mock.bgtq_decode_workspace_bytes(C.byref(_desc(nt, n_recent=513)), ns) == base + per_part
 
 
 def test_capacity_and_failure_leave_state(mock):
