@@ -323,7 +323,9 @@ int64_t bgtq_decode_workspace_bytes(const bgtq_cache *c, int n_splits);
  * copy of K/V, compute z_t = q.k_hat_t/sqrt(128) with k_hat = S*sigma_i*c[code] (affine:
  * scale*code+zero), an online softmax, and o = sum_t p_t v_hat_t / sum_t p_t over the packed
  * tokens and the fp16 recent tokens (order-free concatenation, LogQuant summary Method 4).
- * Split-K over context; partials merged by log-sum-exp.
+ * Split-K over context; partials merged by log-sum-exp.  An fp16 window of at most 512 rows
+ * (n_recent, or the log-based filter's store) is attended by the merge launch itself; a longer one
+ * by a split-K launch of its own, which takes one more partial per query head of workspace.
  * q: device [B][Hq][128] in dtype; out: device fp32 [B][Hq][128]; ws: device scratch of at
  * least bgtq_decode_workspace_bytes(c, n_splits) bytes (256-byte aligned), contents undefined
  * after the call.  Errors: BGTQ_E_INVALID (NULL, layer, empty context, small workspace),
@@ -361,7 +363,7 @@ int bgtq_decode_step(bgtq_cache *c, int layer, const void *k, const void *v, con
  * the call itself allocates nothing.  Every call on one GPU shares that GPU's array, so calls that
  * overlap on one GPU (other streams, other threads) race; calls in order on one stream do not.
  * n_splits = 0 takes the library's split count, reduced so that the partials
- * (B * Hq * (splits + 1 if n_recent > 0) * 528 bytes) fit the array; an explicit n_splits whose
+ * (B * Hq * (splits + 1 if n_recent > 512) * 528 bytes) fit the array; an explicit n_splits whose
  * partials do not fit is BGTQ_E_UNSUPPORTED, as is a geometry for which one split does not fit.
  * Other arguments, results and errors as bgtq_decode_attention.
  */
