@@ -1757,14 +1757,21 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
         const void* src = pass == 0 ? a.src_k : a.src_v;
         __syncthreads();  // the previous pass is done with the rows
         if (a.vec16) {
-            // 16-byte chunks: instruction k covers rows (64 / CPR) * k + lane / CPR
-#pragma unroll 4
+            // 16-byte chunks: instruction k covers rows (64 / CPR) * k + lane / CPR; every load of
+            // the pass is issued before the first LDS write, one round trip for the tile's rows
+            u32x4_t ld[CPR];
+#pragma unroll
             for (int k = 0; k < CPR; ++k) {
                 const int u = (64 / CPR) * k + lane / CPR, c = lane % CPR;
                 bool act;
                 const int64_t off = row_base(u, act);
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (act) v = *(const u32x4_t*)((const XT*)src + off + EPC * c);
+                ld[k] = u32x4_t{0u, 0u, 0u, 0u};
+                if (act) ld[k] = *(const u32x4_t*)((const XT*)src + off + EPC * c);
+            }
+#pragma unroll
+            for (int k = 0; k < CPR; ++k) {
+                const int u = (64 / CPR) * k + lane / CPR, c = lane % CPR;
+                const u32x4_t v = ld[k];
                 uint32_t* dst = (uint32_t*)(s_x + u * XS + EPC * c);
                 dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
             }
