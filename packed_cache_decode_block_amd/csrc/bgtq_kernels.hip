@@ -596,11 +596,12 @@ __global__ __launch_bounds__(256, 2) void k_decode(const DecodeArgs a) {
         const uint32_t* kt = kc + t * (a.k_tile_bytes / 4);
         const uint32_t* vt = vc + t * (a.v_tile_bytes / 4);
 #pragma unroll
-        for (int k = 0; k < RK; ++k) kn[k] = kt[k * TILE + lane];
+        // the packed tiles are read once per step: non-temporal loads
+        for (int k = 0; k < RK; ++k) kn[k] = __builtin_nontemporal_load(kt + k * TILE + lane);
 #pragma unroll
         for (int c4 = 0; c4 < VB; ++c4) {
-            const uint4 v = ((const uint4*)vt)[c4 * 64 + lane];
-            vn[4 * c4] = v.x; vn[4 * c4 + 1] = v.y; vn[4 * c4 + 2] = v.z; vn[4 * c4 + 3] = v.w;
+            const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)vt + c4 * 64 + lane);
+            vn[4 * c4] = v[0]; vn[4 * c4 + 1] = v[1]; vn[4 * c4 + 2] = v[2]; vn[4 * c4 + 3] = v[3];
         }
         const int64_t p = t * TILE + lane < n_packed ? t * TILE + lane : 0;
 #pragma unroll
@@ -786,7 +787,7 @@ __global__ __launch_bounds__(256, kMxaWgsPerCu) void k_decode_mxa(const DecodeAr
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) kd[ks][g] = kt[(4 * ks + row) * 64 + 16 * g + col];
+            for (int g = 0; g < 4; ++g) kd[ks][g] = __builtin_nontemporal_load(kt + (4 * ks + row) * 64 + 16 * g + col);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int64_t tok = t * TILE + 16 * g + col;
@@ -810,7 +811,7 @@ __global__ __launch_bounds__(256, kMxaWgsPerCu) void k_decode_mxa(const DecodeAr
     auto fetch_v = [&](u32x4_t (&dst)[VB], int64_t t) {
         const u32x4_t* vt = (const u32x4_t*)(vc + t * (a.v_tile_bytes / 4));
 #pragma unroll
-        for (int c = 0; c < VB; ++c) dst[c] = vt[c * 64 + lane];
+        for (int c = 0; c < VB; ++c) dst[c] = __builtin_nontemporal_load(vt + c * 64 + lane);
     };
     const int64_t t_first = t_lo + wave < t_hi ? t_lo + wave : (t_lo < a.n_tiles ? t_lo : 0);
     fetch_k(t_first);
@@ -1120,8 +1121,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_fp16_mx(const Fp16Args a) {
     const uint16_t* V16 = a.v16 + bh * a.rows * D;
     const int64_t last = n > 0 ? n - 1 : 0;  // rows past the end are never read: loads clamp to it
 
-    // Tile loads: kk[g][ks] is the B operand of token group g, k-step ks; vv[k] is the 16 bytes at
-    // tile offset 1024 k + 16 lane (token 4k + lane / 16, dims 8 (lane % 16) ..).
+    // Tile loads (non-temporal: the rows are read once per step): kk[g][ks] is the B operand of
+    // token group g, k-step ks; vv[k] is the 16 bytes at tile offset 1024 k + 16 lane (token
+    // 4k + lane / 16, dims 8 (lane % 16) ..).
     u32x4_t kk[4][4], vv[16];
     // idle = true (a wave's prefetch past its last tile): every lane reads row 0, one cached row,
     // instead of a whole tile; the loads stay unconditional so that no branch joins the wait counts.
@@ -1131,14 +1133,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_fp16_mx(const Fp16Args a) {
             const int64_t tok = idle ? 0 : t * TILE + 16 * g + col;
             const u32x4_t* r = (const u32x4_t*)(K16 + (tok < last ? tok : last) * D);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) kk[g][ks] = r[4 * ks + row];
+            for (int ks = 0; ks < 4; ++ks) kk[g][ks] = __builtin_nontemporal_load(r + 4 * ks + row);
         }
     };
     auto fetch_v = [&](int64_t t, bool idle) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const int64_t tok = idle ? 0 : t * TILE + 4 * k + row;
-            vv[k] = ((const u32x4_t*)(V16 + (tok < last ? tok : last) * D))[col];
+            vv[k] = __builtin_nontemporal_load((const u32x4_t*)(V16 + (tok < last ? tok : last) * D) + col);
         }
     };
     const int64_t t_first = t_lo + wave < t_hi ? t_lo + wave : (t_lo < n_tiles ? t_lo : 0);
