@@ -545,14 +545,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_gtq(const DecodeArgs a) {
     // (each lane reads its own stream).
     u32x4_t kn[R / 4], vn[VB], vx[VB];
     uint32_t sn, zn;
-    // The packed tiles are read once per step: non-temporal loads keep them from displacing what
-    // is reused (tables, plan, the partials the merge reads), 2-4% per step in same-box A/B runs.
+    // The packed tiles and their scales are read once per step: non-temporal loads keep them from
+    // displacing what is reused (tables, plan, the partials the merge reads), 2-5% per step in
+    // same-box A/B runs.
     auto fetch_k = [&](int64_t t) {
         const u32x4_t* kt = (const u32x4_t*)(kc + t * (a.k_tile_bytes / 4));
 #pragma unroll
         for (int c = 0; c < R / 4; ++c) kn[c] = __builtin_nontemporal_load(kt + c * 64 + lane);
-        sn = (lane < 32 ? ks32 : vs32)[t * (TILE / 2) + (lane & 31)];
-        zn = vz32 ? vz32[t * (TILE / 2) + (lane & 31)] : 0u;
+        sn = __builtin_nontemporal_load((lane < 32 ? ks32 : vs32) + t * (TILE / 2) + (lane & 31));
+        zn = vz32 ? __builtin_nontemporal_load(vz32 + t * (TILE / 2) + (lane & 31)) : 0u;
     };
     auto fetch_v = [&](u32x4_t (&dst)[VB], int64_t t) {
         const u32x4_t* vt = (const u32x4_t*)(vc + t * (a.v_tile_bytes / 4));
