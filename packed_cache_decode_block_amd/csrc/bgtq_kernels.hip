@@ -1761,6 +1761,7 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
         if (a.vec16) {
             // 16-byte chunks: instruction k covers rows (64 / CPR) * k + lane / CPR; every load of
             // the pass is issued before the first LDS write, one round trip for the tile's rows
+            // (non-temporal, as the key records below: each is touched once here)
             u32x4_t ld[CPR];
 #pragma unroll
             for (int k = 0; k < CPR; ++k) {
@@ -1768,7 +1769,7 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
                 bool act;
                 const int64_t off = row_base(u, act);
                 ld[k] = u32x4_t{0u, 0u, 0u, 0u};
-                if (act) ld[k] = *(const u32x4_t*)((const XT*)src + off + EPC * c);
+                if (act) ld[k] = __builtin_nontemporal_load((const u32x4_t*)((const XT*)src + off + EPC * c));
             }
 #pragma unroll
             for (int k = 0; k < CPR; ++k) {
@@ -1855,7 +1856,7 @@ __global__ __launch_bounds__(64) void k_quant(const QuantArgs a) {
                     nb += 2 * w;
                     if (nb >= 32) {
                         // widths summing past the budget (invalid metadata) never write past the record
-                        if (active && k < a.R) kt[k * TILE + lane] = (uint32_t)buf;
+                        if (active && k < a.R) __builtin_nontemporal_store((uint32_t)buf, kt + k * TILE + lane);
                         buf >>= 32;
                         nb -= 32;
                         ++k;
