@@ -19,7 +19,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
-KERNEL_UNITS = ["bgtq_kernels.hip", "bgtq_decode_gtq.hip", "bgtq_logquant.hip", "bgtq_noalloc.hip"]
+KERNEL_UNITS = ["bgtq_kernels.hip", "bgtq_decode_gtq.hip", "bgtq_quant_rows.hip", "bgtq_logquant.hip",
+                "bgtq_noalloc.hip"]
 HOST_UNITS = ["bgtq_host.cpp"]
 
 

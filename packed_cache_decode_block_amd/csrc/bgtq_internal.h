@@ -200,6 +200,10 @@ hipError_t launch_combine(const CombineArgs& a, int rows, hipStream_t s);
 hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t s);
 hipError_t launch_energy(const EnergyArgs& a, hipStream_t s);
 hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_t s);
+// Bulk quantize with rows held in registers (bgtq_quant_rows.hip): 16-bit rows in 16-byte chunks,
+// Block-GTQ keys and codebook values (either half may be absent).
+bool quant_rows_supported(const QuantArgs& a);
+hipError_t launch_quant_rows(const QuantArgs& a, int B, int64_t max_tiles, hipStream_t s);
 hipError_t launch_ring(const RingArgs& a, int B, int64_t max_rows, hipStream_t s);
 bool decode_supported(int k_mode, int R, int k_bits, int k_group, int v_bits, int G);
 // Tracing aid: the next decode, fp16-decode or quantize kernel launch on this thread records

@@ -2212,6 +2212,7 @@ hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_
         if (per_tile <= 4) return launch_main(k_append<4>, grid, dim3(256), s, q);
         return launch_main(k_append<16>, grid, dim3(1024), s, q);
     }
+    if (!rot && quant_rows_supported(q)) return launch_quant_rows(q, B, max_tiles, s);
     if (rot) {
         if (a.dtype == BGTQ_F32) return launch_main(k_quant<float, true>, grid, dim3(64), s, q);
         return launch_main(k_quant<uint16_t, true>, grid, dim3(64), s, q);

@@ -500,9 +500,9 @@ def test_fused_decode_step(name):
 
 
 FEW_CASES = {
-    # name: (workload id, overrides, N, chunk sizes).  Appends of at most 16 positions per sequence
+    # name: (workload id, overrides, N, chunk sizes).  Appends of at most 64 positions per sequence
     # take the one-token-per-wave kernel; every format it covers, appended a few tokens at a time
-    # (including chunks that straddle a tile boundary and one of 17, which takes the tile kernel).
+    # (including chunks that straddle a tile boundary).
     "gtq_v3_g8": (2, {"L": 1}, 150, (1, 1, 5, 16, 17, 1, 60, 1, 3, 40, 1)),
     "gtq_v2_b2": (3, {"L": 1, "B": 2}, 90, (1, 2, 3, 16, 1, 7, 60)),
     "gtq_v4_k4": (2, {"L": 1, "v_bits": 4, "k_budget_units": 256}, 70, (1, 13, 1, 16, 39)),
@@ -534,6 +534,40 @@ def test_few_token_appends_bit_exact(name):
     out = cache.decode_attention(0, T.to_dev(q, w.dtype))
     torch.cuda.synchronize()
     T.assert_close(out.cpu().numpy(), pipeline.decode_layer(oc, q), name)
+
+
+BULK_CASES = {
+    # name: (workload id, overrides, N, chunk sizes, decoded).  Appends of more than 64 positions
+    # per sequence take the bulk quantizer; 16-bit rows with Block-GTQ keys and codebook values take
+    # the kernels that hold each row in registers.  fp16 and bf16 rows, record sizes from 1 to 32
+    # dwords, value widths 1 to 4, chunks that start inside a tile (the streams of the tile's
+    # earlier tokens keep their bits) and two sequences.  Formats no decode kernel reads compare
+    # the packed store only.
+    "gtq_f16_k3v3": (2, {"L": 1, "dtype": "f16"}, 1000 + 21, (130, 77, None), True),
+    "gtq_bf16_v1_r1": (2, {"L": 1, "v_bits": 1, "k_budget_units": 16}, 700 + 5, (65, 200, None), False),
+    "gtq_bf16_v4_r32": (2, {"L": 1, "v_bits": 4, "k_budget_units": 512}, 600 + 3, (100, None), False),
+    "gtq_f16_v2_r8_b2": (3, {"L": 1, "B": 2, "dtype": "f16"}, 900 + 9, (333, 65, None), True),
+    "gtq_bf16_v3_r16": (2, {"L": 1, "v_bits": 3, "k_budget_units": 256}, 400 + 1, (None,), True),
+}
+
+
+@pytest.mark.parametrize("name", list(BULK_CASES))
+def test_bulk_quantize_bit_exact(name):
+    wid, ov, N, chunks, decoded = BULK_CASES[name]
+    w = synth.reduced(synth.WORKLOADS[wid], **ov)
+    print(f"[bulk case {name}] N={N} chunks={chunks}", flush=True)
+    n_cap = ((N + 63) // 64 + 1) * 64
+    m = T.meta(w, 0)
+    K, V, q = T.inputs(w, 0, N)
+    oc = T.oracle_layer(w, K, V, m, n_cap)
+    cache = T.gpu_cache(w, n_cap)
+    cache.set_metadata(0, m.bits, m.sigma, m.r)
+    T.append_all(cache, 0, K, V, w.dtype, chunks)
+    _compare_cache(cache, oc, w)
+    if decoded:
+        out = cache.decode_attention(0, T.to_dev(q, w.dtype))
+        torch.cuda.synchronize()
+        T.assert_close(out.cpu().numpy(), pipeline.decode_layer(oc, q), name)
 
 
 def test_decode_step_ragged_lengths():
