@@ -80,6 +80,8 @@ KERNEL_SOURCES = {
     "k_decode": ("bgtq_kernels.hip", "bgtq_device.h"),
     "k_decode_mxa": ("bgtq_kernels.hip", "bgtq_device.h"),
     "k_decode_fp16_mx": ("bgtq_kernels.hip", "bgtq_device.h"),
+    "k_quant": ("bgtq_kernels.hip", "bgtq_device.h"),
+    "k_quant_rows": ("bgtq_quant_rows.hip", "bgtq_device.h"),
 }
 
 
@@ -471,7 +473,11 @@ def main():
         n_pk = w.N - min(w.N, w.n_recent)
         qbytes = w.B * w.Hkv * n_pk * (2 * w.d * es + bytes_per_token_head(w))
         q_ms = totq / nq
-        result["quantize_append"] = {"kernel": "k_quant", "launches": nq, "kernel_avg_us": round(q_ms * 1e3, 2),
+        # 16-bit rows with Block-GTQ keys and codebook values take the register-row kernels (keys
+        # then values, one event pair around both), every other format the tile kernel
+        rows_path = w.dtype != "f32" and w.k_mode == "gtq" and w.v_mode == "codebook"
+        qk = "k_quant_rows_keys + k_quant_rows_values" if rows_path else "k_quant"
+        result["quantize_append"] = {"kernel": qk, "launches": nq, "kernel_avg_us": round(q_ms * 1e3, 2),
                                      "tokens_per_launch": w.B * w.Hkv * n_pk, "bytes_per_launch": qbytes,
                                      "GB/s": round(qbytes / (q_ms * 1e-3) / 1e9, 1)}
         log(f"[bench] quantize-append {q_ms * 1e3:.1f} us per layer -> {qbytes / (q_ms * 1e-3) / 1e9:.0f} GB/s")
