@@ -24,7 +24,8 @@
 //    of the wave's half of its stream (whole dwords: fields of dims 64 hw .. 64 hw + 63 fill
 //    dwords VB (2 sh + hw) .. VB (2 sh + hw + 1) - 1 for token halves sh) with shifts known at
 //    compile time.
-// Rows that are not 16-byte aligned, fp32 rows, affine formats and the rotations take k_quant.
+// Rows that are not 16-byte aligned, fp32 rows, affine formats, the rotations and width or sigma
+// arrays off a 4-byte boundary take k_quant.
 #include "bgtq_internal.h"
 
 #include <hip/hip_ext.h>
@@ -403,8 +404,10 @@ hipError_t launch_rows(const QuantArgs& a, dim3 grid, hipStream_t s) {
 }  // namespace
 
 bool quant_rows_supported(const QuantArgs& a) {
+    // the key kernel reads the widths, sigmas and 1/sigmas as scalar dwords: 4-byte aligned arrays
+    const bool meta4 = (uintptr_t)a.bits % 4 == 0 && (uintptr_t)a.sigma % 4 == 0 && (uintptr_t)a.inv_sigma % 4 == 0;
     return a.dtype != BGTQ_F32 && a.vec16 && a.R >= 1 && a.R <= QR_RMAX && a.v_bits >= 1 && a.v_bits <= 4 &&
-           (!(a.which & 1) || a.k_mode == BGTQ_K_BLOCKGTQ) && (!(a.which & 2) || a.v_mode == BGTQ_V_CODEBOOK);
+           (!(a.which & 1) || (a.k_mode == BGTQ_K_BLOCKGTQ && meta4)) && (!(a.which & 2) || a.v_mode == BGTQ_V_CODEBOOK);
 }
 
 hipError_t launch_quant_rows(const QuantArgs& a, int B, int64_t max_tiles, hipStream_t s) {
