@@ -7,9 +7,9 @@
 // k_quant spells out (fp32, one IEEE operation at a time, the per-token sum in element order), so
 // codes and fp16 scales are the same bits.
 //
-// Two kernels, k_quant_rows_keys then k_quant_rows_values (each its own register allocation: one
-// kernel holding both needs the registers of both).  One workgroup of two waves per tile of 64
-// positions of one (sequence, kv head), lane = token; wave hw takes elements 64 hw .. 64 hw + 63
+// One kernel, k_quant_rows: a workgroup of two waves codes either the keys or the values of one
+// tile of 64 positions of one (sequence, kv head) (the role is fixed per workgroup, so each wave
+// runs one of the two paths), lane = token; wave hw takes elements 64 hw .. 64 hw + 63
 // of every row.  A wave reads its 64 half rows with 16-byte loads (eight half rows per
 // instruction) and turns them through LDS in four rounds of 16, so that lane t ends with its
 // token's 64 elements in 32 registers (element pairs, as stored): the per-token chains read
@@ -49,6 +49,8 @@ constexpr int QR_RMAX = 32;                    // key record dwords at most (bud
 // LDS words of the key kernel for R-dword records: thresholds, each wave's staging, the records
 // (an odd stride of R | 1 dwords per token), the partial sums and the scales.
 constexpr int qr_key_words(int R) { return QR_THR + 2 * QR_STAGE + TILE * (R | 1) + 2 * TILE; }
+// LDS words of the value role: each wave's staging and code exchange, the partial sums, the scales.
+constexpr int qr_value_words = 2 * QR_VAREA + 2 * TILE;
 
 // Element formats: bf16 bits, fp16 bits, and bf16 rows first rounded to fp16 (rows that passed
 // an fp16 store).
@@ -205,13 +207,12 @@ __device__ __forceinline__ uint32_t qr_pair(float x0, float x1, float t, int w, 
     return (((uint32_t)(uintptr_t)q0 - a0) >> 2) | ((((uint32_t)(uintptr_t)q1 - a0) >> 2) << w);
 }
 
-// Keys: Block-GTQ records and fp16 scales of one tile.  Dynamic LDS: 4 * qr_key_words(R) bytes.
+// Keys: Block-GTQ records and fp16 scales of tile tile0[b] + tx.  LDS: qr_key_words(R) words.
 template <int MODE>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(MODE == QR_BF16 ? 6 : 4))) void k_quant_rows_keys(const QuantArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];
+__device__ __forceinline__ void qr_keys_tile(const QuantArgs& a, int64_t tx, uint32_t* s_dyn) {
     const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
     const int hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t tile = a.tile0[b] + blockIdx.x;
+    const int64_t tile = a.tile0[b] + tx;
     if (tile * TILE >= a.pos_hi[b]) return;  // whole workgroup beyond this sequence's range
     const int R = a.R;
     float* s_thr = (float*)s_dyn;
@@ -272,18 +273,18 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(MODE == QR_
     }
 }
 
-// Values: codes at width VB, fp16 scales and the tile's lane streams (stream L = dd + 16 jj holds,
+// Values (tile tile0[b] + tx; LDS: qr_value_words words): codes at width VB, fp16 scales and the tile's lane streams (stream L = dd + 16 jj holds,
 // at field phi = 32 sh + 4 db + m, the codes of dim 16 db + dd for tokens p = 16 sh + 4 jj + m and
 // p + 32).  Wave hw holds dims 64 hw .. 64 hw + 63, i.e. db = 4 hw + dbl (dbl 0..3).
 template <int MODE, int VB>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(MODE == QR_BF16 ? 6 : 4))) void k_quant_rows_values(const QuantArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t s_area[2][QR_VAREA];
-    __shared__ float s_acc[TILE], s_S[TILE];
+__device__ __forceinline__ void qr_values_tile(const QuantArgs& a, int64_t tx, uint32_t* s_dyn) {
     const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
     const int hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t tile = a.tile0[b] + blockIdx.x;
+    const int64_t tile = a.tile0[b] + tx;
     if (tile * TILE >= a.pos_hi[b]) return;  // whole workgroup beyond this sequence's range
-    uint32_t* area = s_area[hw];
+    uint32_t* area = s_dyn + hw * QR_VAREA;
+    float* s_acc = (float*)(s_dyn + 2 * QR_VAREA);
+    float* s_S = s_acc + TILE;
     const int64_t pos = tile * TILE + lane;
     const bool active = pos >= a.pos_lo[b] && pos < a.pos_hi[b];
     uint32_t x[QR_HALF];
@@ -379,26 +380,36 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(MODE == QR_
     if (hw == 1 && active) a.v_scale[bh * a.n_cap + pos] = s16;
 }
 
+// One launch for a layer's bulk append: workgroup x codes the keys (even x) or the values (odd x)
+// of tile x / 2 when both are appended, else the one half of tile x.  The two roles interleave in
+// launch order, so the rows of workgroups that start later load while earlier ones code theirs.
+template <int MODE, int VB>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(MODE == QR_BF16 ? 6 : 4))) void k_quant_rows(const QuantArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];
+    const bool both = (a.which & 3) == 3;
+    const int64_t tx = both ? (int64_t)(blockIdx.x >> 1) : (int64_t)blockIdx.x;
+    const bool keys = both ? (blockIdx.x & 1) == 0 : (a.which & 1) != 0;
+    if (keys) qr_keys_tile<MODE>(a, tx, s_dyn);
+    else qr_values_tile<MODE, VB>(a, tx, s_dyn);
+}
+
 template <int MODE>
-hipError_t launch_rows(const QuantArgs& a, dim3 grid, hipStream_t s) {
-    // an armed event pair spans both launches: start with the keys, stop after the values
-    hipEvent_t e0 = t_ev_start, e1 = t_ev_stop;
-    t_ev_start = t_ev_stop = nullptr;
+hipError_t launch_rows(const QuantArgs& a, int64_t max_tiles, int Hkv, int B, hipStream_t s) {
     const bool keys = a.which & 1, values = (a.which >> 1) & 1;
-    if (keys) {
-        hipExtLaunchKernelGGL(k_quant_rows_keys<MODE>, grid, dim3(128), (size_t)(4 * qr_key_words(a.R)), s, e0,
-                              values ? nullptr : e1, 0, a);
-        if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const dim3 grid((unsigned)(max_tiles * (keys && values ? 2 : 1)), Hkv, B);
+    const int words = cmax(keys ? qr_key_words(a.R) : 0, values ? qr_value_words : 0);
+    auto k = a.v_bits == 1 ? k_quant_rows<MODE, 1>
+           : a.v_bits == 2 ? k_quant_rows<MODE, 2>
+           : a.v_bits == 3 ? k_quant_rows<MODE, 3>
+                           : k_quant_rows<MODE, 4>;
+    if (t_ev_start) {
+        hipEvent_t e0 = t_ev_start, e1 = t_ev_stop;
+        t_ev_start = t_ev_stop = nullptr;
+        hipExtLaunchKernelGGL(k, grid, dim3(128), (size_t)(4 * words), s, e0, e1, 0, a);
+    } else {
+        hipLaunchKernelGGL(k, grid, dim3(128), (size_t)(4 * words), s, a);
     }
-    if (values) {
-        auto kv = a.v_bits == 1 ? k_quant_rows_values<MODE, 1>
-                : a.v_bits == 2 ? k_quant_rows_values<MODE, 2>
-                : a.v_bits == 3 ? k_quant_rows_values<MODE, 3>
-                                : k_quant_rows_values<MODE, 4>;
-        hipExtLaunchKernelGGL(kv, grid, dim3(128), 0, s, keys ? nullptr : e0, e1, 0, a);
-        if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -412,10 +423,9 @@ bool quant_rows_supported(const QuantArgs& a) {
 
 hipError_t launch_quant_rows(const QuantArgs& a, int B, int64_t max_tiles, hipStream_t s) {
     if (!quant_rows_supported(a)) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)max_tiles, a.Hkv, B);
-    if (a.dtype == BGTQ_F16) return launch_rows<QR_F16>(a, grid, s);
-    if (a.round16) return launch_rows<QR_BF16_TO_F16>(a, grid, s);
-    return launch_rows<QR_BF16>(a, grid, s);
+    if (a.dtype == BGTQ_F16) return launch_rows<QR_F16>(a, max_tiles, a.Hkv, B, s);
+    if (a.round16) return launch_rows<QR_BF16_TO_F16>(a, max_tiles, a.Hkv, B, s);
+    return launch_rows<QR_BF16>(a, max_tiles, a.Hkv, B, s);
 }
 
 }  // namespace bgtq
