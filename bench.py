@@ -473,10 +473,10 @@ def main():
         n_pk = w.N - min(w.N, w.n_recent)
         qbytes = w.B * w.Hkv * n_pk * (2 * w.d * es + bytes_per_token_head(w))
         q_ms = totq / nq
-        # 16-bit rows with Block-GTQ keys and codebook values take the register-row kernels (keys
-        # then values, one event pair around both), every other format the tile kernel
+        # 16-bit rows with Block-GTQ keys and codebook values take the register-row kernel (one
+        # launch, key and value workgroups interleaved), every other format the tile kernel
         rows_path = w.dtype != "f32" and w.k_mode == "gtq" and w.v_mode == "codebook"
-        qk = "k_quant_rows_keys + k_quant_rows_values" if rows_path else "k_quant"
+        qk = "k_quant_rows" if rows_path else "k_quant"
         result["quantize_append"] = {"kernel": qk, "launches": nq, "kernel_avg_us": round(q_ms * 1e3, 2),
                                      "tokens_per_launch": w.B * w.Hkv * n_pk, "bytes_per_launch": qbytes,
                                      "GB/s": round(qbytes / (q_ms * 1e-3) / 1e9, 1)}
