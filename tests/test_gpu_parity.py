@@ -500,9 +500,10 @@ def test_fused_decode_step(name):
 
 
 FEW_CASES = {
-    # name: (workload id, overrides, N, chunk sizes).  Appends of at most 64 positions per sequence
-    # take the one-token-per-wave kernel; every format it covers, appended a few tokens at a time
-    # (including chunks that straddle a tile boundary).
+    # name: (workload id, overrides, N, chunk sizes).  Short appends take the one-token-per-wave
+    # kernel (at most 16 positions per sequence for 16-bit rows with Block-GTQ keys and codebook
+    # values, at most 64 otherwise); every format it covers, appended a few tokens at a time
+    # (including chunks that straddle a tile boundary, and longer chunks that take the bulk kernel).
     "gtq_v3_g8": (2, {"L": 1}, 150, (1, 1, 5, 16, 17, 1, 60, 1, 3, 40, 1)),
     "gtq_v2_b2": (3, {"L": 1, "B": 2}, 90, (1, 2, 3, 16, 1, 7, 60)),
     "gtq_v4_k4": (2, {"L": 1, "v_bits": 4, "k_budget_units": 256}, 70, (1, 13, 1, 16, 39)),
