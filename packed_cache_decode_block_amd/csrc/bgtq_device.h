@@ -20,7 +20,6 @@ constexpr int TILE = 64;
 constexpr int D = 128;
 constexpr int PART = 132;                       // floats per partial record: o[128], m, l
 constexpr int kAppendFewMax = 64;               // appends of at most this many positions per sequence take k_append
-constexpr int kAppendFewRows = 16;              // ... at most this many when the register-row bulk kernel takes the format
 constexpr float kLog2eOverSqrtD = 0.12751743074233076f;  // log2(e) / sqrt(128)
 
 __constant__ uint32_t c_cent32[BGTQ_CB_CENTROIDS] = BGTQ_CB_CENTROID_F32_INIT;

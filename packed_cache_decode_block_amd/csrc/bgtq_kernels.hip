@@ -2207,6 +2207,7 @@ hipError_t launch_quant(const QuantArgs& a, int B, int64_t max_tiles, hipStream_
     for (int b = 0; b < B; ++b) most = std::max<int64_t>(most, a.pos_hi[b] - a.pos_lo[b]);
     // one wave per token beats a tile launch for short appends; the register-row bulk kernel takes
     // over sooner (a 64-row append: 16 us against 40 us for one wave per token)
+    constexpr int kAppendFewRows = 16;
     if (!rot && most <= (quant_rows_supported(q) ? kAppendFewRows : kAppendFewMax)) {
         // one wave per token in flight, up to 16 (each wave takes every NW-th token of its tile)
         const int per_tile = most < TILE ? (int)most : TILE;
