@@ -89,12 +89,13 @@ __device__ __forceinline__ void qr_load_half(const QuantArgs& a, const uint16_t*
                                              int lane, int hw, uint32_t* stage, uint32_t (&x)[QR_HALF]) {
     // each lane finds its own token's row once; load instruction k reads half rows 8k .. 8k + 7
     // (lane 8 * (row - 8k) + 16-byte chunk) at the offsets their lanes found
-    // (a running workgroup has at least one row in range: rows out of range read the first one's
-    // and are zeroed, so that every load is issued unconditionally)
+    // (rows out of range read the first row in range, or lane 0's row 0 of the sequence when it
+    // appends nothing inside a tile another sequence needs, and are zeroed, so that every load is
+    // issued unconditionally)
     bool act_mine;
     int64_t off_mine = qr_row(a, tile, b, h, lane, act_mine) + 64 * hw;
     const uint64_t am = __ballot(act_mine);
-    const int first = (int)__builtin_ctzll(am);
+    const int first = am ? (int)__builtin_ctzll(am) : 0;
     const int64_t off_first = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(off_mine >> 32), first) << 32) |
                                         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)off_mine, first));
     if (!act_mine) off_mine = off_first;
