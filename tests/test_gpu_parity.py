@@ -742,7 +742,9 @@ def test_logquant_prefill_matches_oracle(name):
             assert torch.equal(a, r), f"{name_}: prefill and token-by-token appends differ"
 
 
-@pytest.mark.parametrize("wid,W,N", [(2, 4, 70), (3, 8, 100), (1, 2, 40), (4, 4, 60)])
+# W > 16 sends a halving's W leaving rows through the bulk quantizer (16-bit store rows, appended
+# mid-tile for W = 24), smaller W through the one-token-per-wave kernel
+@pytest.mark.parametrize("wid,W,N", [(2, 4, 70), (3, 8, 100), (1, 2, 40), (4, 4, 60), (2, 32, 140), (3, 24, 110)])
 def test_logquant_appends_match_oracle(wid, W, N):
     """LogQuant's log-based filter through the device: after token-by-token appends, the packed
     store equals the oracle's store of the leaving tokens in leaving order (bit-exact), the
